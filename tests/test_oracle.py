@@ -1,0 +1,356 @@
+"""Pins for the CPU oracle, checked against what the pages and mathematics fix.
+
+None of these re-types the oracle's loop.  Each pin compares it with
+something independent: a hand-computed example, the pages' own structure
+(scale 1 on the A step, the adapter scale on the B step, a float32
+intermediate: "Compress then Serve", rebuttal pseudocode of
+add_lora_slice_with_sigma), a merged-weight GEMM done by a library
+routine, closed forms, exact-integer constructions, invariances that hold
+exactly in floating point, and a textbook rounding-error bound.  The
+mutation test at the end plants plausible mistakes in a copy of the oracle
+and checks that the pins catch every one.
+"""
+import math
+import os
+import shutil
+import subprocess
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from synth import config, random_case
+from conftest import read_golden
+
+
+def _delta(x, starts, segs, adapters, y_in=None, acc="f32", lib=None):
+    return oracle.lora_delta(x, starts, segs, adapters, y_in, acc=acc, lib=lib)
+
+
+def _rand_adapter(g, r, h_in, h_out, scale=None):
+    a = g.uniform(-1, 1, (r, h_in)).astype(np.float32) / np.float32(math.sqrt(h_in))
+    b = (g.standard_normal((h_out, r)) * 0.02).astype(np.float32)
+    return a, b, float(np.float32(scale if scale is not None else g.uniform(0.25, 4)))
+
+
+# ---------------------------------------------------------------------------
+# Pins written as functions of a library handle, so the mutation test can run
+# the same checks against a deliberately broken oracle.
+# ---------------------------------------------------------------------------
+def pin_hand_example(lib=None):
+    """tests/golden/hand_tiny.txt: a worked example computed by hand."""
+    rows = read_golden("hand_tiny.txt")
+    kv = {}
+    adapters, cur = {}, None
+    x, y_in, expect = [], [], []
+    for k, vals in rows:
+        if k == "adapter":
+            cur = int(vals[0])
+            adapters[cur] = {"A": [], "B": [], "scale": float(vals[4])}
+        elif k in ("A", "B"):
+            adapters[cur][k].append([float(v) for v in vals])
+        elif k == "x":
+            x.append([float(v) for v in vals])
+        elif k == "y_in":
+            y_in.append([float(v) for v in vals])
+        elif k == "expect":
+            expect.append([float(v) for v in vals])
+        else:
+            kv[k] = [int(v) for v in vals]
+    ad = {i: (np.array(d["A"], np.float32), np.array(d["B"], np.float32), d["scale"])
+          for i, d in adapters.items()}
+    for acc in ("f32", "f64"):
+        y = _delta(np.array(x, np.float32), kv["seg_starts"], kv["seg_adapter"], ad,
+                   np.array(y_in, np.float32), acc=acc, lib=lib)
+        assert np.array_equal(y, np.array(expect)), (acc, y)
+
+
+def pin_indicator_adapters(lib=None, seed=5):
+    """Indicator adapters: A_i has a single 1 at [0][0], x[t][0] = 1,
+    B_i[0][0] = id mod 128 and B_i[1][0] = id div 128.  Every product that
+    reaches y is an exact small integer, so the output decodes, exactly, the
+    adapter id each token was served with."""
+    g = np.random.default_rng(seed)
+    T, h_in, h_out, s = 40, 24, 16, 2.0
+    ids = [3, 130, 257, 999, 77]
+    adapters = {}
+    for i in ids:
+        r = int(g.integers(1, 9))
+        a = np.zeros((r, h_in), np.float32)
+        a[0, 0] = 1.0
+        b = (g.standard_normal((h_out, r))).astype(np.float32)   # multiplies exact zeros
+        b[:, 0] = 0.0
+        b[0, 0], b[1, 0] = i % 128, i // 128
+        adapters[i] = (a, b, s)
+    cuts = np.sort(g.choice(np.arange(1, T), 9, replace=False))
+    starts = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    segs = g.choice(ids + [-1], len(starts) - 1).astype(np.int32)
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    x[:, 0] = 1.0
+    y = _delta(x, starts, segs, adapters, lib=lib)
+    expect_id = np.full(T, -1)
+    for si in range(len(segs)):
+        for t in range(starts[si], starts[si + 1]):
+            expect_id[t] = segs[si]
+    for t in range(T):
+        if expect_id[t] == -1:
+            assert np.all(y[t] == 0), t
+        else:
+            got = int(y[t, 0] / s) + 128 * int(y[t, 1] / s)
+            assert got == expect_id[t] and y[t, 0] == s * (expect_id[t] % 128), (t, got)
+            assert np.all(y[t, 2:] == 0), t
+
+
+def pin_merged_weight(lib=None, seed=7):
+    """One adapter for every token: y = W x + s B (A x) must equal the
+    merged-weight product (W + s B A) x, evaluated by numpy in float64.
+    W and x are small integers so y_in = W x is exact in float32."""
+    g = np.random.default_rng(seed)
+    T, h_in, h_out, r, s = 12, 40, 24, 5, 1.5
+    W = g.integers(-3, 4, (h_out, h_in)).astype(np.float64)
+    x = g.integers(-4, 5, (T, h_in)).astype(np.float32)
+    a, b, _ = _rand_adapter(g, r, h_in, h_out)
+    y_in = (x.astype(np.float64) @ W.T).astype(np.float32)
+    starts = np.array([0, 5, 5, T], np.int32)             # includes an empty segment
+    segs = np.array([4, 4, 4], np.int32)
+    merged = (W + s * b.astype(np.float64) @ a.astype(np.float64))
+    ref = x.astype(np.float64) @ merged.T
+    y64 = _delta(x, starts, segs, {4: (a, b, s)}, y_in, acc="f64", lib=lib)
+    y32 = _delta(x, starts, segs, {4: (a, b, s)}, y_in, acc="f32", lib=lib)
+    scale = np.abs(ref).max()
+    assert np.abs(y64 - ref).max() <= 1e-12 * scale
+    assert np.abs(y32 - ref).max() <= 1e-5 * scale
+
+
+def pin_b_zero(lib=None, seed=11):
+    """B = 0 gives a zero delta: y equals y_in, value for value."""
+    w = random_case(seed, T=48, h_in=64, h_out=40)
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((w.num_tokens, 64)).astype(np.float32)
+    y_in = g.standard_normal((w.num_tokens, 40)).astype(np.float32)
+    adapters = {}
+    for i in range(w.pool_size):
+        a, _, s = _rand_adapter(g, int(w.ranks[i]), 64, 40)
+        adapters[i] = (a, np.zeros((40, int(w.ranks[i])), np.float32), s)
+    for acc in ("f32", "f64"):
+        y = _delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, acc=acc, lib=lib)
+        assert np.array_equal(y, y_in)
+
+
+ALL_PINS = (pin_hand_example, pin_indicator_adapters, pin_merged_weight, pin_b_zero)
+
+
+def test_hand_example():
+    pin_hand_example()
+
+
+def test_indicator_adapters():
+    pin_indicator_adapters()
+
+
+def test_merged_weight():
+    pin_merged_weight()
+
+
+def test_b_zero_identity():
+    pin_b_zero()
+
+
+def test_rank1_closed_form():
+    """Rank 1: delta[t] = s * b * (a . x[t]); the dot product is taken with
+    math.fsum (correctly rounded), so the float64 oracle must agree to a few
+    ulps."""
+    g = np.random.default_rng(3)
+    T, h_in, h_out = 9, 200, 33
+    a, b, s = _rand_adapter(g, 1, h_in, h_out)
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    y = _delta(x, [0, T], [0], {0: (a, b, s)}, acc="f64")
+    for t in range(T):
+        dot = math.fsum(float(a[0, k]) * float(x[t, k]) for k in range(h_in))
+        ref = np.array([s * float(b[o, 0]) * dot for o in range(h_out)])
+        assert np.allclose(y[t], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_brute_force_matmul():
+    """Per segment, delta = s * (X_seg A^T) B^T, via numpy float64 matmul, on
+    the tiny fp32 workload and on random heterogeneous batches."""
+    cases = [config(0)] + [random_case(i) for i in range(6)]
+    for w in cases:
+        pr = w.projs[0]
+        x = w.activation(0, pr.x_key)
+        y64 = oracle.workload_call(w, 0, 0, acc="f64")
+        ref = np.zeros((w.num_tokens, pr.h_out))
+        for si in range(w.num_segs):
+            aid = int(w.seg_adapter[si])
+            lo, hi = int(w.seg_starts[si]), int(w.seg_starts[si + 1])
+            if aid < 0 or hi == lo:
+                continue
+            a, b = w.adapter_block(aid, 0, 0)
+            ref[lo:hi] = float(w.scales[aid]) * (
+                (x[lo:hi].astype(np.float64) @ a.T.astype(np.float64)) @ b.T.astype(np.float64))
+        assert np.allclose(y64, ref, rtol=1e-12, atol=1e-14), w.name
+
+
+def test_permutation_invariance():
+    """Reordering segments (with their token rows) changes no token's result,
+    bit for bit."""
+    for seed in range(4):
+        w = random_case(seed, T=60, h_in=96, h_out=48)
+        x = w.activation(0, "x")
+        y = oracle.workload_call(w, 0, 0)
+        perm = np.random.default_rng(seed).permutation(w.num_segs)
+        rows, new_starts = [], [0]
+        for si in perm:
+            rows.extend(range(w.seg_starts[si], w.seg_starts[si + 1]))
+            new_starts.append(new_starts[-1] + w.seg_starts[si + 1] - w.seg_starts[si])
+        ad = {i: (*w.adapter_block(i, 0, 0), float(w.scales[i])) for i in range(w.pool_size)}
+        y2 = _delta(x[rows], new_starts, w.seg_adapter[perm], ad)
+        assert np.array_equal(y2, y[rows])
+
+
+def test_segment_split_invariance():
+    """Cutting a segment in two with the same adapter is bit-identical."""
+    w = random_case(21, T=50, h_in=64, h_out=32, max_seg=20)
+    x = w.activation(0, "x")
+    ad = {i: (*w.adapter_block(i, 0, 0), float(w.scales[i])) for i in range(w.pool_size)}
+    y = _delta(x, w.seg_starts, w.seg_adapter, ad)
+    starts, segs = [0], []
+    for si in range(w.num_segs):
+        lo, hi = int(w.seg_starts[si]), int(w.seg_starts[si + 1])
+        mid = (lo + hi) // 2
+        starts += [mid, hi]
+        segs += [w.seg_adapter[si]] * 2
+    y2 = _delta(x, starts, segs, ad)
+    assert np.array_equal(y, y2)
+
+
+def test_padding_invariance():
+    """An adapter of rank r stored with zero rows of A and zero columns of B
+    up to a larger rank gives the same bits (the extra products are +-0)."""
+    g = np.random.default_rng(8)
+    T, h_in, h_out = 20, 48, 40
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    y_in = g.standard_normal((T, h_out)).astype(np.float32)
+    for r, r_pad in ((1, 8), (5, 8), (12, 16), (33, 64)):
+        a, b, s = _rand_adapter(g, r, h_in, h_out)
+        ap = np.zeros((r_pad, h_in), np.float32)
+        ap[:r] = a
+        bp = np.zeros((h_out, r_pad), np.float32)
+        bp[:, :r] = b
+        y = _delta(x, [0, T], [1], {1: (a, b, s)}, y_in)
+        yp = _delta(x, [0, T], [1], {1: (ap, bp, s)}, y_in)
+        assert np.array_equal(y, yp), (r, r_pad)
+
+
+def test_linearity():
+    """delta(2x) = 2 delta(x) and delta with 2s = 2 delta with s (exact: powers
+    of two); splitting the rank, (A, B) = ([A1; A2], [B1 B2]), adds the two
+    halves' deltas (to rounding)."""
+    g = np.random.default_rng(9)
+    T, h_in, h_out, r = 16, 80, 24, 12
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    a, b, s = _rand_adapter(g, r, h_in, h_out, scale=1.25)
+    y = _delta(x, [0, T], [0], {0: (a, b, s)})
+    assert np.array_equal(_delta(2 * x, [0, T], [0], {0: (a, b, s)}), 2 * y)
+    assert np.array_equal(_delta(x, [0, T], [0], {0: (a, b, 2 * s)}), 2 * y)
+    y64 = _delta(x, [0, T], [0], {0: (a, b, s)}, acc="f64")
+    h1 = _delta(x, [0, T], [0], {0: (a[:5], b[:, :5], s)}, acc="f64")
+    h2 = _delta(x, [0, T], [0], {0: (a[5:], b[:, 5:], s)}, acc="f64")
+    assert np.allclose(h1 + h2, y64, rtol=1e-12, atol=1e-15)
+
+
+def test_f32_within_rounding_bound():
+    """The float32 oracle stays inside the textbook bound for recursive
+    summation (|fl(sum) - sum| <= gamma_n * sum|terms|, gamma_n = n u / (1 - n u),
+    u = 2^-24), propagated through the A step, the B step, the scale and the
+    add, measured against the float64 oracle."""
+    u = 2.0 ** -24
+    gam = lambda n: n * u / (1 - n * u)  # noqa: E731
+    for w in [config(0)] + [random_case(i, has_base=True) for i in (1, 2, 3)]:
+        pr = w.projs[0]
+        x = w.activation(0, pr.x_key).astype(np.float64)
+        g = np.random.default_rng(w.seed)
+        y_in = g.standard_normal((w.num_tokens, pr.h_out)).astype(np.float32)
+        ad = {i: (*w.adapter_block(i, 0, 0), float(w.scales[i])) for i in range(w.pool_size)}
+        y32 = _delta(w.activation(0, pr.x_key), w.seg_starts, w.seg_adapter, ad, y_in)
+        y64 = _delta(w.activation(0, pr.x_key), w.seg_starts, w.seg_adapter, ad, y_in, acc="f64")
+        tok = w.token_adapter()
+        for t in range(w.num_tokens):
+            i = int(tok[t])
+            if i < 0:
+                assert np.array_equal(y32[t], y_in[t])
+                continue
+            a, b, s = ad[i]
+            a, b = a.astype(np.float64), b.astype(np.float64)
+            r = a.shape[0]
+            v = a @ x[t]
+            ev = gam(pr.h_in) * (np.abs(a) @ np.abs(x[t]))            # A-step error
+            d = b @ v
+            ed = gam(r) * (np.abs(b) @ (np.abs(v) + ev)) + np.abs(b) @ ev
+            sd = abs(s) * (np.abs(d) + ed)
+            bound = abs(s) * ed + u * sd + u * (np.abs(y_in[t]) + sd) * 1.0001 + 1e-30
+            assert np.all(np.abs(y32[t] - y64[t]) <= bound), (w.name, t)
+
+
+def test_errors():
+    x = np.zeros((4, 8), np.float32)
+    ad = {1: (np.zeros((2, 8), np.float32), np.zeros((8, 2), np.float32), 1.0)}
+    for starts, segs in (([0, 3], [1]), ([1, 4], [1]), ([0, 3, 2, 4], [1, 1, 1]), ([0, 4], [2])):
+        with pytest.raises(oracle.OracleError):
+            _delta(x, starts, segs, ad)
+
+
+def test_config0_under_one_second():
+    """The tiny fp32 workload's oracle run finishes in under a second."""
+    w = config(0)
+    t0 = time.perf_counter()
+    oracle.workload_call(w, 0, 0)
+    assert time.perf_counter() - t0 < 1.0
+
+
+# ---------------------------------------------------------------------------
+# Mutation test: each planted mistake must make at least one pin fail.
+# ---------------------------------------------------------------------------
+MUTATIONS = {
+    "drop_scale": ("yt[o] = yt[o] + sc * d;", "yt[o] = yt[o] + d;"),
+    "transpose_B": ("const float *bo = B[a] + (int64_t)o * r;\n"
+                    "            float d = 0.0f;", None),
+    "rank_off_by_one": ("for (int32_t j = 0; j < r; ++j) {\n            float acc",
+                        "for (int32_t j = 0; j < r - 1; ++j) {\n            float acc"),
+    "reversed_x": ("acc += aj[k] * xt[k];", "acc += aj[k] * xt[h_in - 1 - k];"),
+    "drop_y_in": ("yt[o] = y_in ? y_in[(int64_t)t * ld_in + o] : 0.0f;", "yt[o] = 0.0f;"),
+    "wrong_lookup": ("if (ids[a] == id) return a;", "if (ids[a] == id) return (a + 1) % n;"),
+    "sign_flip": ("yt[o] = yt[o] + sc * d;", "yt[o] = yt[o] - sc * d;"),
+    "no_adapter_uses_first": ("const int32_t a = tok_a[t];",
+                              "const int32_t a = tok_a[t] < 0 ? 0 : tok_a[t];"),
+}
+
+
+def _mutate(src, name):
+    old, new = MUTATIONS[name]
+    if name == "transpose_B":
+        # read B as if it were stored r x h_out
+        old = "d += bo[j] * v[j];"
+        new = "d += B[a][(int64_t)j * h_out + o] * v[j];"
+    assert src.count(old) >= 1, name
+    return src.replace(old, new, 1)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(oracle_build.SRC).read()
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(_mutate(src, name))
+    lib_path = str(tmp_path / "liboracle_mut.so")
+    oracle_build.build(out=lib_path, src=str(mutated))
+    lib = oracle.load_library(lib_path)
+    failures = 0
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, oracle.OracleError):
+            failures += 1
+    assert failures >= 1, f"no pin caught mutation {name}"
