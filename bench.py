@@ -1,0 +1,284 @@
+"""Benchmark of the multi-adapter LoRA delta on one MI355X.
+
+A step is one pass of the whole delta over one heterogeneous batch: for the
+full Mistral-7B-shaped stack (the default workload) that is 32 layers x 4
+calls (qkv fused through y offsets, o, gate_up fused, down), i.e. all 224
+(layer, projection) deltas y = base_out + s B (A x), with inputs already
+resident in HBM.  The step is captured once in a HIP graph and replayed.
+
+Prints one JSON line: tokens/s over the whole stack, achieved HBM GB/s of
+the algorithmic bytes, the roofline of the dominant kernel (measured with
+HIP events on the launch stream), and the CPU oracle's rate on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0        # dense bf16 MFMA
+METRIC = ("LoRA-delta tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, layers=None):
+    """Bytes and FLOPs the delta must move/do, each counted once: adapter
+    bytes of the distinct (adapter, layer, projection) triples at true rank,
+    each activation read once, y written once and its input (base_out or y)
+    read once."""
+    es = 2 if w.dtype == "bf16" else 4
+    layers = range(w.num_layers) if layers is None else layers
+    tok = w.token_adapter()
+    touched = w.touched()
+    act = int((tok >= 0).sum())
+    per_layer_adapter = sum(int(w.ranks[a]) * (p.h_in + p.h_out) for a in touched
+                            for p in w.projs) * es
+    per_layer_x = sum(w.num_tokens * w.x_width(k) for k in w.x_keys()) * es
+    per_layer_y = sum(w.num_tokens * p.h_out for p in w.projs) * es * 2
+    flops = sum(2 * int(w.ranks[tok[t]]) * (p.h_in + p.h_out) for t in range(w.num_tokens)
+                if tok[t] >= 0 for p in w.projs)
+    n = len(list(layers))
+    return {"adapter": per_layer_adapter * n, "x": per_layer_x * n, "y": per_layer_y * n,
+            "bytes": (per_layer_adapter + per_layer_x + per_layer_y) * n, "flops": flops * n,
+            "active_tokens": act}
+
+
+def kernel_bytes(w, call, kind):
+    """Algorithmic bytes of one shrink or expand launch for one call."""
+    es = 2 if w.dtype == "bf16" else 4
+    touched = w.touched()
+    tok = w.token_adapter()
+    act = int((tok >= 0).sum())
+    r_sum = sum(int(w.ranks[a]) for a in touched)
+    v_bytes = 4 * sum(int(w.ranks[tok[t]]) for t in range(w.num_tokens) if tok[t] >= 0) * len(call)
+    if kind == "shrink":
+        h_in = w.projs[call[0]].h_in
+        return r_sum * h_in * es * len(call) + act * h_in * es + v_bytes
+    h_out = sum(w.projs[p].h_out for p in call)
+    return r_sum * h_out * es + v_bytes + 2 * w.num_tokens * h_out * es
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "lora_sgmv.cpp", "sgmv_internal.h"):
+        with open(os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, blocks, layers, threads):
+    """Time the oracle (as it is) on the host for the sampled layers."""
+    import oracle
+    t_total = 0.0
+    for l in layers:
+        for p, pr in enumerate(w.projs):
+            adapters = {a: (blocks[(a, l, p)][0], blocks[(a, l, p)][1], float(w.scales[a]))
+                        for a in w.touched()}
+            x = w.activation(l, pr.x_key)
+            y_in = w.base_out(l, p) if w.has_base else None
+            t0 = time.perf_counter()
+            oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, threads=threads)
+            t_total += time.perf_counter() - t0
+    frac = len(layers) / w.num_layers
+    return {"value": w.num_tokens * frac / t_total, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(layers)} of {w.num_layers} layers x {len(w.projs)} projections, "
+                      f"all {w.num_tokens} tokens, float32 oracle, {threads} OpenMP threads, "
+                      f"{t_total:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, help="0..4 (default: the full stack)")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--cpu-layers", type=int, default=-1,
+                    help="layers of the CPU-oracle sample (-1: all, 0: skip)")
+    ap.add_argument("--kernel-reps", type=int, default=5,
+                    help="event-timed passes for the per-kernel roofline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the delta shards over GPUs by request without any exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import config, default_threads
+    from synth.device import DeviceWorkload
+
+    hab.load()
+    torch.cuda.set_device(0)
+    w = config(args.workload)
+    threads = min(16, os.cpu_count() or 1)
+    cpu_layers = list(range(w.num_layers)) if args.cpu_layers < 0 else list(
+        range(min(args.cpu_layers, w.num_layers)))
+    keep = {}
+
+    def on_block(aid, l, p, a, b):
+        if l in cpu_layers:
+            keep[(aid, l, p)] = (a, b)
+
+    t0 = time.perf_counter()
+    dw = DeviceWorkload(w, on_block=on_block, threads=default_threads())
+    torch.cuda.synchronize()
+    log(f"[bench] staged {w.name}: {time.perf_counter() - t0:.1f} s, "
+        f"plan {dw.plan.stats()}")
+    alg = algorithmic(w)
+    launches = 2 * len(dw.layers) * len(dw.calls)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            dw.run_fused()
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            dw.run_fused()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                graph.replay()
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            dw.run_fused()
+
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.mode}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms)")
+
+    # eager step time for reference (Python + C launch path, no graph)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        for _ in range(max(3, args.steps // 5)):
+            dw.run_fused()
+        e3.record(stream)
+        torch.cuda.synchronize()
+    eager_ms = e2.elapsed_time(e3) / max(3, args.steps // 5)
+
+    # per-kernel durations: shrink and expand launched separately, each
+    # bracketed by events on the launch stream
+    kt = {"shrink": [0.0, 0], "expand": [0.0, 0]}
+    kb = {"shrink": 0, "expand": 0}
+    v = torch.zeros((w.num_tokens, dw.max_proj * w.r_max), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        for rep in range(args.kernel_reps):
+            evs = []
+            for l in dw.layers:
+                for ci, c in enumerate(dw.calls):
+                    x = dw.x[(l, w.projs[c[0]].x_key)]
+                    y = dw.y[(l, ci)]
+                    if w.has_base:
+                        y.copy_(dw.base[(l, ci)])
+                    ea, eb, ec = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                    ea.record(stream)
+                    hab.sgmv_shrink(dw.pool, dw.plan, l, c, x, v[:, :len(c) * w.r_max])
+                    eb.record(stream)
+                    hab.sgmv_expand(dw.pool, dw.plan, l, c, dw.y_offsets[ci],
+                                    v[:, :len(c) * w.r_max], y)
+                    ec.record(stream)
+                    evs.append((ea, eb, ec))
+                    if rep == 0:
+                        kb["shrink"] += kernel_bytes(w, c, "shrink")
+                        kb["expand"] += kernel_bytes(w, c, "expand")
+            torch.cuda.synchronize()
+            for ea, eb, ec in evs:
+                kt["shrink"][0] += ea.elapsed_time(eb)
+                kt["shrink"][1] += 1
+                kt["expand"][0] += eb.elapsed_time(ec)
+                kt["expand"][1] += 1
+    per_launch = {k: kt[k][0] / kt[k][1] for k in kt}           # ms
+    n_launch = len(dw.layers) * len(dw.calls)
+    bytes_per_launch = {k: kb[k] / n_launch for k in kb}
+    kern = {k: {"avg_us": per_launch[k] * 1e3,
+                "gbs": bytes_per_launch[k] / (per_launch[k] * 1e-3) / 1e9,
+                "alg_bytes_per_launch": bytes_per_launch[k]} for k in kt}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    kname = {"shrink": "k_shrink", "expand": "k_expand"}[dom]
+    traffic = traffic_from_profile(kname, w.name)
+    roof = {"bound": "hbm", "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel": kname,
+            "avg_launch_us": round(kern[dom]["avg_us"], 3),
+            "alg_bytes_per_launch": int(kern[dom]["alg_bytes_per_launch"])}
+    log(f"[bench] kernels: {json.dumps(kern)}")
+
+    cpu = None
+    if args.cpu_layers != 0 and keep:
+        cpu = cpu_baseline(w, keep, cpu_layers, threads)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    tok_s = w.num_tokens / (ms * 1e-3)
+    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description,
+                   "tokens": w.num_tokens, "layers": w.num_layers,
+                   "projections": [p.name for p in w.projs],
+                   "calls_per_layer": len(dw.calls), "kernel_launches_per_step": launches,
+                   "distinct_adapters": int(len(w.touched())), "mode": args.mode},
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tflops": round(tflops, 3), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"],
+        "eager_ms_per_step": round(eager_ms, 5),
+        "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

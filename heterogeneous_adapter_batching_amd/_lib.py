@@ -1,0 +1,91 @@
+"""ctypes declarations of the C ABI in include/lora_sgmv.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhab_lora.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+LORA_MAX_PROJ = 8
+LORA_MAX_RANK = 64
+
+STATUS = {0: "LORA_OK", -1: "LORA_EINVAL", -2: "LORA_ENOSPC", -3: "LORA_ENOENT",
+          -4: "LORA_ERANK", -5: "LORA_EDTYPE", -6: "LORA_ESEG", -7: "LORA_EHIP",
+          -8: "LORA_EEXIST", -9: "LORA_ESTATE"}
+
+
+def status_name(code: int) -> str:
+    return STATUS.get(code, f"status {code}")
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_proj", ctypes.c_int32),
+                ("h_in", ctypes.c_int32 * LORA_MAX_PROJ), ("h_out", ctypes.c_int32 * LORA_MAX_PROJ),
+                ("r_max", ctypes.c_int32), ("rank_granule", ctypes.c_int32),
+                ("max_slots", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_i32, _i64, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+_vp, _i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+_pp = ctypes.POINTER(ctypes.c_void_p)
+
+# name: (restype, argtypes)
+SIGNATURES = {
+    "lora_last_error": (ctypes.c_char_p, []),
+    "lora_adapter_bytes": (_u64, [ctypes.POINTER(PoolDesc), _i32]),
+    "lora_pool_extent_bytes": (_u64, [ctypes.POINTER(PoolDesc), _i32]),
+    "lora_pool_create": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(PoolDesc), _vp, _u64]),
+    "lora_pool_destroy": (_i32, [_vp]),
+    "lora_pool_reserve": (_i32, [_vp, _i32, _i32, _f32]),
+    "lora_pool_upload": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "lora_pool_register": (_i32, [_vp, _i32, _i32, _f32, _pp, _pp, _i32, _vp]),
+    "lora_pool_unregister": (_i32, [_vp, _i32]),
+    "lora_pool_query": (_i32, [_vp, _i32, _i32p, _i32p, ctypes.POINTER(_f32),
+                               ctypes.POINTER(_u64)]),
+    "lora_pool_stats": (_i32, [_vp, _i32p, ctypes.POINTER(_u64)]),
+    "lora_plan_create": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32]),
+    "lora_plan_destroy": (_i32, [_vp]),
+    "lora_plan_workspace_bytes": (_u64, [_vp, _i32]),
+    "lora_plan_upload": (_i32, [_vp, _vp, _u64, _i32, _vp]),
+    "lora_plan_stats": (_i32, [_vp, _i32p, _i32p, _i32p, _i32p]),
+    "lora_plan_export": (_i32, [_vp, _i32p, _i32p, _i32p, _i32p]),
+    "sgmv_shrink": (_i32, [_vp, _vp, _i32, _i32, _i32p, _vp, _i64, _vp, _i64, _vp]),
+    "sgmv_expand": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp]),
+    "sgmv_fused": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp, _i64,
+                          _vp]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libhab_lora.so (built in-tree by __graft_entry__.build()).
+
+    Raises ImportError when the library has not been built: there is no other
+    implementation to fall back to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        msg = load().lora_last_error()
+        raise LoraError(status, msg.decode() if msg else "")

@@ -1,0 +1,303 @@
+"""Pool, Plan and the three sgmv calls over the C ABI (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from ._lib import LORA_BF16, LORA_F32, LORA_MAX_PROJ, PoolDesc, check, load
+
+_DTYPES = {"bf16": LORA_BF16, "f32": LORA_F32}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _torch_dtype(dtype: str):
+    torch = _torch()
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32_array(values) -> ctypes.Array:
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+def make_desc(num_layers: int, h_in: Sequence[int], h_out: Sequence[int], r_max: int,
+              dtype: str = "bf16", max_slots: int = 1024, rank_granule: int = 8) -> PoolDesc:
+    if len(h_in) != len(h_out) or not 1 <= len(h_in) <= LORA_MAX_PROJ:
+        raise ValueError("h_in / h_out must list 1..8 projections")
+    d = PoolDesc()
+    d.num_layers = num_layers
+    d.num_proj = len(h_in)
+    for i, (a, b) in enumerate(zip(h_in, h_out)):
+        d.h_in[i] = a
+        d.h_out[i] = b
+    d.r_max = r_max
+    d.rank_granule = rank_granule
+    d.max_slots = max_slots
+    d.dtype = _DTYPES[dtype]
+    return d
+
+
+def adapter_bytes(desc: PoolDesc, rank: int) -> int:
+    """Bytes of one adapter at its true rank (no device needed)."""
+    return int(load().lora_adapter_bytes(ctypes.byref(desc), rank))
+
+
+def extent_bytes(desc: PoolDesc, rank: int) -> int:
+    """Bytes one adapter occupies in the slab (padded rank, 256-byte rounded)."""
+    return int(load().lora_pool_extent_bytes(ctypes.byref(desc), rank))
+
+
+def _check_dev(t, name, dtype=None, ndim=2):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+
+
+class Pool:
+    """An adapter pool over one HBM slab.
+
+    Either give ``slab`` (a CUDA tensor the pool will use; the caller keeps it
+    alive) or ``slab_bytes`` (a uint8 CUDA tensor is allocated here).
+    ``slab_ptr`` (an integer address) creates a host-metadata-only pool whose
+    slab is never touched; it is for planning without a GPU.
+    """
+
+    def __init__(self, num_layers: int, h_in: Sequence[int], h_out: Sequence[int], r_max: int,
+                 dtype: str = "bf16", max_slots: int = 1024, rank_granule: int = 8,
+                 slab=None, slab_bytes: Optional[int] = None, slab_ptr: Optional[int] = None,
+                 device: str = "cuda"):
+        self.lib = load()
+        self.desc = make_desc(num_layers, h_in, h_out, r_max, dtype, max_slots, rank_granule)
+        self.dtype = dtype
+        self.num_layers, self.h_in, self.h_out = num_layers, list(h_in), list(h_out)
+        self.r_max = r_max
+        self.slab = None
+        if slab_ptr is not None:
+            ptr, nbytes = slab_ptr, int(slab_bytes or 0)
+        else:
+            torch = _torch()
+            if slab is None:
+                if slab_bytes is None:
+                    raise ValueError("give slab, slab_bytes or slab_ptr")
+                slab = torch.empty(int(slab_bytes), dtype=torch.uint8, device=device)
+            self.slab = slab
+            ptr, nbytes = slab.data_ptr(), slab.numel() * slab.element_size()
+        self._h = ctypes.c_void_p()
+        check(self.lib.lora_pool_create(ctypes.byref(self._h), ctypes.byref(self.desc),
+                                        ctypes.c_void_p(ptr), nbytes))
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self.lib.lora_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def extent_bytes(self, rank: int) -> int:
+        return extent_bytes(self.desc, rank)
+
+    def adapter_bytes(self, rank: int) -> int:
+        return adapter_bytes(self.desc, rank)
+
+    def reserve(self, adapter_id: int, rank: int, scale: float):
+        check(self.lib.lora_pool_reserve(self._h, adapter_id, rank, ctypes.c_float(scale)))
+
+    def upload(self, adapter_id: int, layer: int, proj: int, A, B, stream=None):
+        """A: [rank][h_in], B: [h_out][rank], CUDA tensors of the pool dtype or
+        host numpy arrays (float32 values for an f32 pool, uint16 bf16 bits
+        for a bf16 pool)."""
+        on_host = isinstance(A, np.ndarray)
+        if on_host:
+            A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
+            pa, pb = A.ctypes.data, B.ctypes.data
+        else:
+            A, B = A.contiguous(), B.contiguous()
+            pa, pb = A.data_ptr(), B.data_ptr()
+        check(self.lib.lora_pool_upload(self._h, adapter_id, layer, proj, ctypes.c_void_p(pa),
+                                        ctypes.c_void_p(pb), int(on_host), _stream_handle(stream)))
+
+    def register(self, adapter_id: int, rank: int, scale: float, A: Sequence, B: Sequence,
+                 stream=None):
+        """A[p]: [L][rank][h_in_p], B[p]: [L][h_out_p][rank] for every projection,
+        all CUDA tensors or all host numpy arrays (see ``upload``)."""
+        on_host = isinstance(A[0], np.ndarray)
+        keep = []
+        ptrs_a, ptrs_b = [], []
+        for a, b in zip(A, B):
+            if on_host:
+                a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+                ptrs_a.append(a.ctypes.data)
+                ptrs_b.append(b.ctypes.data)
+            else:
+                a, b = a.contiguous(), b.contiguous()
+                ptrs_a.append(a.data_ptr())
+                ptrs_b.append(b.data_ptr())
+            keep += [a, b]
+        arr_a = (ctypes.c_void_p * len(ptrs_a))(*ptrs_a)
+        arr_b = (ctypes.c_void_p * len(ptrs_b))(*ptrs_b)
+        check(self.lib.lora_pool_register(self._h, adapter_id, rank, ctypes.c_float(scale),
+                                          arr_a, arr_b, int(on_host), _stream_handle(stream)))
+
+    def unregister(self, adapter_id: int):
+        check(self.lib.lora_pool_unregister(self._h, adapter_id))
+
+    def query(self, adapter_id: int):
+        r, rp = ctypes.c_int32(), ctypes.c_int32()
+        sc, off = ctypes.c_float(), ctypes.c_uint64()
+        check(self.lib.lora_pool_query(self._h, adapter_id, ctypes.byref(r), ctypes.byref(rp),
+                                       ctypes.byref(sc), ctypes.byref(off)))
+        return {"rank": r.value, "r_pad": rp.value, "scale": sc.value, "offset": off.value}
+
+    def stats(self):
+        n, free = ctypes.c_int32(), ctypes.c_uint64()
+        check(self.lib.lora_pool_stats(self._h, ctypes.byref(n), ctypes.byref(free)))
+        return {"adapters": n.value, "free_bytes": free.value}
+
+
+class Plan:
+    """The gather plan of one heterogeneous batch (built on the host)."""
+
+    def __init__(self, pool: Pool, num_tokens: int, seg_starts, seg_adapter):
+        self.lib = pool.lib
+        self.pool = pool
+        self.num_tokens = int(num_tokens)
+        starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
+        segs = np.ascontiguousarray(seg_adapter, dtype=np.int32)
+        if starts.ndim != 1 or segs.ndim != 1 or starts.shape[0] != segs.shape[0] + 1:
+            raise ValueError("seg_starts must have one more entry than seg_adapter")
+        self._h = ctypes.c_void_p()
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        check(self.lib.lora_plan_create(ctypes.byref(self._h), pool.handle, self.num_tokens,
+                                        starts.ctypes.data_as(i32p), segs.ctypes.data_as(i32p),
+                                        int(segs.shape[0])))
+        self.ws = None
+        self.max_proj = 0
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self.lib.lora_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def workspace_bytes(self, max_proj: int) -> int:
+        return int(self.lib.lora_plan_workspace_bytes(self._h, max_proj))
+
+    def upload(self, max_proj: int = 3, ws=None, stream=None):
+        """Copy the plan into a device workspace (allocated here unless given)."""
+        torch = _torch()
+        need = self.workspace_bytes(max_proj)
+        if ws is None:
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        check(self.lib.lora_plan_upload(self._h, ctypes.c_void_p(ws.data_ptr()),
+                                        ws.numel() * ws.element_size(), max_proj,
+                                        _stream_handle(stream)))
+        self.ws = ws
+        self.max_proj = max_proj
+        return self
+
+    def stats(self):
+        vals = [ctypes.c_int32() for _ in range(4)]
+        check(self.lib.lora_plan_stats(self._h, *[ctypes.byref(v) for v in vals]))
+        return dict(zip(("groups", "blocks", "active_tokens", "max_block_tokens"),
+                        [v.value for v in vals]))
+
+    def export(self):
+        st = self.stats()
+        T, G = self.num_tokens, st["groups"]
+        order = np.zeros(max(T, 1), np.int32)
+        tgroup = np.zeros(max(T, 1), np.int32)
+        gad = np.zeros(max(G, 1), np.int32)
+        grank = np.zeros(max(G, 1), np.int32)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        check(self.lib.lora_plan_export(self._h, order.ctypes.data_as(i32p),
+                                        tgroup.ctypes.data_as(i32p), gad.ctypes.data_as(i32p),
+                                        grank.ctypes.data_as(i32p)))
+        return {"token_order": order[:T], "token_group": tgroup[:T],
+                "group_adapter": gad[:G], "group_rank": grank[:G]}
+
+
+def _projs(projs):
+    projs = [int(p) for p in projs]
+    return len(projs), _i32_array(projs)
+
+
+def sgmv_shrink(pool: Pool, plan: Plan, layer: int, projs, x, v=None, stream=None):
+    """v[:, i*r_max : i*r_max + r_max] = A_i,p x for each listed projection."""
+    torch = _torch()
+    _check_dev(x, "x", _torch_dtype(pool.dtype))
+    n, parr = _projs(projs)
+    if v is None:
+        v = torch.zeros((x.shape[0], n * pool.r_max), dtype=torch.float32, device=x.device)
+    _check_dev(v, "v", torch.float32)
+    check(pool.lib.sgmv_shrink(pool.handle, plan.handle, layer, n, parr,
+                               ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                               ctypes.c_void_p(v.data_ptr()), v.stride(0),
+                               _stream_handle(stream)))
+    return v
+
+
+def sgmv_expand(pool: Pool, plan: Plan, layer: int, projs, y_offsets, v, y, stream=None):
+    """y[:, off_i : off_i + h_out] += s * B_i,p v_i (rounded once)."""
+    torch = _torch()
+    _check_dev(v, "v", torch.float32)
+    _check_dev(y, "y", _torch_dtype(pool.dtype))
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_expand(pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
+                               ctypes.c_void_p(v.data_ptr()), v.stride(0),
+                               ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                               _stream_handle(stream)))
+    return y
+
+
+def sgmv_fused(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=None,
+               stream=None):
+    """y = (base or y) + s * B (A x) for each listed projection's slice of y."""
+    dt = _torch_dtype(pool.dtype)
+    _check_dev(x, "x", dt)
+    _check_dev(y, "y", dt)
+    if base is not None:
+        _check_dev(base, "base", dt)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_fused(pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
+                              ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                              ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                              base.stride(0) if base is not None else 0,
+                              ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                              _stream_handle(stream)))
+    return y

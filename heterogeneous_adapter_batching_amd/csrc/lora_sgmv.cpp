@@ -1,0 +1,720 @@
+// Host side of the multi-adapter LoRA delta library: the adapter pool (slot
+// table and extent allocator over a caller-owned HBM slab), the gather plan
+// of a heterogeneous batch, and the C ABI declared in include/lora_sgmv.h.
+//
+// Nothing here allocates device memory.  Validation happens before anything
+// is enqueued, so an error leaves every object as it was.
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "lora_sgmv.h"
+#include "sgmv_internal.h"
+
+using lora::BlockDesc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lora_status fail(lora_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+lora_status hip_fail(hipError_t e, const char *what) {
+    return fail(LORA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+uint64_t round_up(uint64_t v, uint64_t m) { return (v + m - 1) / m * m; }
+
+int32_t esize(int32_t dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+
+lora_status check_desc(const lora_pool_desc *d) {
+    if (!d) return fail(LORA_EINVAL, "null pool descriptor");
+    if (d->dtype != LORA_F32 && d->dtype != LORA_BF16)
+        return fail(LORA_EDTYPE, "dtype %d is neither LORA_F32 nor LORA_BF16", d->dtype);
+    if (d->num_layers < 1) return fail(LORA_EINVAL, "num_layers %d < 1", d->num_layers);
+    if (d->num_proj < 1 || d->num_proj > LORA_MAX_PROJ)
+        return fail(LORA_EINVAL, "num_proj %d not in 1..%d", d->num_proj, LORA_MAX_PROJ);
+    for (int p = 0; p < d->num_proj; ++p) {
+        if (d->h_in[p] < 8 || d->h_in[p] % 8 || d->h_out[p] < 8 || d->h_out[p] % 8)
+            return fail(LORA_EINVAL, "projection %d: h_in %d / h_out %d must be positive "
+                        "multiples of 8", p, d->h_in[p], d->h_out[p]);
+    }
+    if (d->rank_granule < 8 || d->rank_granule % 8)
+        return fail(LORA_EINVAL, "rank_granule %d must be a positive multiple of 8",
+                    d->rank_granule);
+    if (d->r_max < 1 || d->r_max > LORA_MAX_RANK || d->r_max % d->rank_granule)
+        return fail(LORA_EINVAL, "r_max %d must be a multiple of rank_granule %d and <= %d",
+                    d->r_max, d->rank_granule, LORA_MAX_RANK);
+    if (d->max_slots < 1) return fail(LORA_EINVAL, "max_slots %d < 1", d->max_slots);
+    return LORA_OK;
+}
+
+// sum over projections of (h_in + h_out): the per-rank, per-layer element count
+int64_t row_elems(const lora_pool_desc *d) {
+    int64_t w = 0;
+    for (int p = 0; p < d->num_proj; ++p) w += int64_t(d->h_in[p]) + d->h_out[p];
+    return w;
+}
+
+int32_t pad_rank(const lora_pool_desc *d, int32_t r) {
+    return int32_t(round_up(uint64_t(r), uint64_t(d->rank_granule)));
+}
+
+}  // namespace
+
+struct Slot {
+    int32_t rank;
+    int32_t r_pad;
+    float scale;
+    uint64_t off;
+    uint64_t bytes;
+};
+
+struct lora_pool {
+    lora_pool_desc d;
+    uint8_t *slab;
+    uint64_t slab_bytes;
+    std::unordered_map<int32_t, Slot> slots;
+    std::map<uint64_t, uint64_t> free_list;  // offset -> bytes, coalesced
+    uint64_t generation = 0;                  // bumped by unregister
+    int64_t W = 0;                            // row_elems(d)
+    int64_t pre[LORA_MAX_PROJ + 1] = {};      // prefix of (h_in + h_out) over projections
+
+    // element offset multipliers of the A and B blocks of (layer, proj), in
+    // units of r_pad elements
+    int64_t coef_a(int layer, int p) const { return int64_t(layer) * W + pre[p]; }
+    int64_t coef_b(int layer, int p) const { return coef_a(layer, p) + d.h_in[p]; }
+
+    bool alloc(uint64_t bytes, uint64_t *off) {
+        for (auto it = free_list.begin(); it != free_list.end(); ++it) {
+            if (it->second >= bytes) {
+                *off = it->first;
+                const uint64_t rest = it->second - bytes;
+                const uint64_t roff = it->first + bytes;
+                free_list.erase(it);
+                if (rest) free_list.emplace(roff, rest);
+                return true;
+            }
+        }
+        return false;
+    }
+
+    void release(uint64_t off, uint64_t bytes) {
+        auto it = free_list.emplace(off, bytes).first;
+        auto nx = std::next(it);
+        if (nx != free_list.end() && it->first + it->second == nx->first) {
+            it->second += nx->second;
+            free_list.erase(nx);
+        }
+        if (it != free_list.begin()) {
+            auto pv = std::prev(it);
+            if (pv->first + pv->second == it->first) {
+                pv->second += it->second;
+                free_list.erase(it);
+            }
+        }
+    }
+};
+
+struct lora_plan {
+    const lora_pool *pool = nullptr;
+    uint64_t pool_generation = 0;
+    int32_t T = 0;
+    std::vector<int32_t> token_order;    // plan order: grouped adapter tokens, then the rest
+    std::vector<int32_t> token_group;    // per token row
+    std::vector<int32_t> group_adapter, group_rank;
+    std::vector<BlockDesc> blocks;       // adapter blocks [0, nb_act), no-adapter blocks after
+    std::vector<int32_t> rt_prefix;      // over adapter blocks
+    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1;
+
+    // device image in the caller's workspace
+    void *ws = nullptr;
+    uint64_t ws_bytes = 0;
+    int32_t max_proj = 0;
+    uint64_t off_tok = 0, off_blocks = 0, off_rtp = 0, off_cnt = 0, off_part = 0, off_v = 0;
+    uint64_t image_bytes = 0, part_bytes = 0, v_bytes = 0;
+    void *staging = nullptr;
+    uint64_t staging_bytes = 0;
+    hipEvent_t staged = nullptr;
+
+    int32_t rt_total() const { return rt_prefix.empty() ? 0 : rt_prefix.back(); }
+    int32_t nb_all() const { return int32_t(blocks.size()); }
+
+    void layout(int32_t mp) {
+        const lora_pool_desc &d = pool->d;
+        uint64_t o = 0;
+        off_tok = o;     o = round_up(o + 4ull * std::max(T, 1), 256);
+        off_blocks = o;  o = round_up(o + sizeof(BlockDesc) * std::max(nb_all(), 1), 256);
+        off_rtp = o;     o = round_up(o + 4ull * (nb_act + 1), 256);
+        off_cnt = o;     o = round_up(o + 4ull * LORA_MAX_PROJ * std::max(nb_act, 1), 256);
+        image_bytes = o;
+        // the k-chunk policy keeps units <= kTargetWaves + nproj * rt_total
+        part_bytes = 4ull * (lora::kTargetWaves + uint64_t(mp) * rt_total()) * tt *
+                     lora::kTile * lora::kTile;
+        off_part = o;    o = round_up(o + part_bytes, 256);
+        v_bytes = 4ull * std::max(T, 1) * mp * d.r_max;
+        off_v = o;       o = round_up(o + v_bytes, 256);
+        ws_bytes = o;
+    }
+};
+
+// ------------------------------------------------------------------ C ABI ----
+extern "C" {
+
+const char *lora_last_error(void) { return g_last_error.c_str(); }
+
+uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank) {
+    if (check_desc(d) != LORA_OK || rank < 1) return 0;
+    return uint64_t(rank) * esize(d->dtype) * uint64_t(d->num_layers) * uint64_t(row_elems(d));
+}
+
+uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank) {
+    if (check_desc(d) != LORA_OK || rank < 1 || rank > d->r_max) return 0;
+    return round_up(uint64_t(pad_rank(d, rank)) * esize(d->dtype) * uint64_t(d->num_layers) *
+                    uint64_t(row_elems(d)), 256);
+}
+
+lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d, void *slab,
+                             uint64_t slab_bytes) {
+    if (!out) return fail(LORA_EINVAL, "null output pointer");
+    lora_status st = check_desc(d);
+    if (st != LORA_OK) return st;
+    if (!slab || (reinterpret_cast<uintptr_t>(slab) & 255))
+        return fail(LORA_EINVAL, "slab must be a non-null, 256-byte aligned device pointer");
+    lora_pool *p = new lora_pool();
+    p->d = *d;
+    p->slab = static_cast<uint8_t *>(slab);
+    p->slab_bytes = slab_bytes / 256 * 256;
+    if (p->slab_bytes) p->free_list.emplace(0, p->slab_bytes);
+    p->W = row_elems(d);
+    for (int i = 0; i < d->num_proj; ++i) p->pre[i + 1] = p->pre[i] + d->h_in[i] + d->h_out[i];
+    *out = p;
+    return LORA_OK;
+}
+
+lora_status lora_pool_destroy(lora_pool *p) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    delete p;
+    return LORA_OK;
+}
+
+lora_status lora_pool_reserve(lora_pool *p, int32_t id, int32_t rank, float scale) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (id < 0) return fail(LORA_EINVAL, "adapter id %d < 0", id);
+    if (rank < 1 || rank > p->d.r_max)
+        return fail(LORA_ERANK, "rank %d not in 1..r_max=%d", rank, p->d.r_max);
+    if (p->slots.count(id)) return fail(LORA_EEXIST, "adapter %d already registered", id);
+    if (int32_t(p->slots.size()) >= p->d.max_slots)
+        return fail(LORA_ENOSPC, "all %d slots in use", p->d.max_slots);
+    const uint64_t bytes = lora_pool_extent_bytes(&p->d, rank);
+    uint64_t off = 0;
+    if (!p->alloc(bytes, &off))
+        return fail(LORA_ENOSPC, "no free extent of %llu bytes in the slab",
+                    (unsigned long long)bytes);
+    p->slots.emplace(id, Slot{rank, pad_rank(&p->d, rank), scale, off, bytes});
+    return LORA_OK;
+}
+
+lora_status lora_pool_upload(lora_pool *p, int32_t id, int32_t layer, int32_t proj,
+                             const void *A, const void *B, int32_t src_on_host, void *stream) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    auto it = p->slots.find(id);
+    if (it == p->slots.end()) return fail(LORA_ENOENT, "adapter %d not registered", id);
+    if (layer < 0 || layer >= p->d.num_layers)
+        return fail(LORA_EINVAL, "layer %d not in 0..%d", layer, p->d.num_layers - 1);
+    if (proj < 0 || proj >= p->d.num_proj)
+        return fail(LORA_EINVAL, "projection %d not in 0..%d", proj, p->d.num_proj - 1);
+    if (!A || !B) return fail(LORA_EINVAL, "null weight pointer");
+    const Slot &s = it->second;
+    const uint64_t es = esize(p->d.dtype);
+    const uint64_t h_in = p->d.h_in[proj], h_out = p->d.h_out[proj];
+    uint8_t *a_dst = p->slab + s.off + uint64_t(s.r_pad) * es * p->coef_a(layer, proj);
+    uint8_t *b_dst = p->slab + s.off + uint64_t(s.r_pad) * es * p->coef_b(layer, proj);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipMemcpyKind kind = src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+    hipError_t e = hipMemcpyAsync(a_dst, A, uint64_t(s.rank) * h_in * es, kind, st);
+    if (e != hipSuccess) return hip_fail(e, "A upload");
+    if (s.r_pad > s.rank) {
+        e = hipMemsetAsync(a_dst + uint64_t(s.rank) * h_in * es, 0,
+                           uint64_t(s.r_pad - s.rank) * h_in * es, st);
+        if (e != hipSuccess) return hip_fail(e, "A pad rows");
+        e = hipMemset2DAsync(b_dst + uint64_t(s.rank) * es, uint64_t(s.r_pad) * es, 0,
+                             uint64_t(s.r_pad - s.rank) * es, h_out, st);
+        if (e != hipSuccess) return hip_fail(e, "B pad columns");
+    }
+    e = hipMemcpy2DAsync(b_dst, uint64_t(s.r_pad) * es, B, uint64_t(s.rank) * es,
+                         uint64_t(s.rank) * es, h_out, kind, st);
+    if (e != hipSuccess) return hip_fail(e, "B upload");
+    if (src_on_host) {
+        e = hipStreamSynchronize(st);   // host source must be consumed before returning
+        if (e != hipSuccess) return hip_fail(e, "upload synchronize");
+    }
+    return LORA_OK;
+}
+
+lora_status lora_pool_unregister(lora_pool *p, int32_t id) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    auto it = p->slots.find(id);
+    if (it == p->slots.end()) return fail(LORA_ENOENT, "adapter %d not registered", id);
+    p->release(it->second.off, it->second.bytes);
+    p->slots.erase(it);
+    ++p->generation;
+    return LORA_OK;
+}
+
+lora_status lora_pool_register(lora_pool *p, int32_t id, int32_t rank, float scale,
+                               const void *const *A, const void *const *B,
+                               int32_t src_on_host, void *stream) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (!A || !B) return fail(LORA_EINVAL, "null weight array");
+    for (int i = 0; i < p->d.num_proj; ++i)
+        if (!A[i] || !B[i]) return fail(LORA_EINVAL, "null weights for projection %d", i);
+    lora_status st = lora_pool_reserve(p, id, rank, scale);
+    if (st != LORA_OK) return st;
+    const uint64_t es = esize(p->d.dtype);
+    for (int l = 0; l < p->d.num_layers; ++l) {
+        for (int i = 0; i < p->d.num_proj; ++i) {
+            const uint8_t *a = static_cast<const uint8_t *>(A[i]) +
+                               uint64_t(l) * rank * p->d.h_in[i] * es;
+            const uint8_t *b = static_cast<const uint8_t *>(B[i]) +
+                               uint64_t(l) * p->d.h_out[i] * rank * es;
+            st = lora_pool_upload(p, id, l, i, a, b, src_on_host, stream);
+            if (st != LORA_OK) {
+                std::string msg = g_last_error;
+                auto it = p->slots.find(id);   // undo the reservation (not a generation bump)
+                p->release(it->second.off, it->second.bytes);
+                p->slots.erase(it);
+                g_last_error = msg;
+                return st;
+            }
+        }
+    }
+    return LORA_OK;
+}
+
+lora_status lora_pool_query(const lora_pool *p, int32_t id, int32_t *rank, int32_t *r_pad,
+                            float *scale, uint64_t *off) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    auto it = p->slots.find(id);
+    if (it == p->slots.end()) return fail(LORA_ENOENT, "adapter %d not registered", id);
+    if (rank) *rank = it->second.rank;
+    if (r_pad) *r_pad = it->second.r_pad;
+    if (scale) *scale = it->second.scale;
+    if (off) *off = it->second.off;
+    return LORA_OK;
+}
+
+lora_status lora_pool_stats(const lora_pool *p, int32_t *num, uint64_t *free_bytes) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (num) *num = int32_t(p->slots.size());
+    if (free_bytes) {
+        uint64_t f = 0;
+        for (auto &kv : p->free_list) f += kv.second;
+        *free_bytes = f;
+    }
+    return LORA_OK;
+}
+
+// ------------------------------------------------------------------- plan ----
+lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
+                             const int32_t *seg_starts, const int32_t *seg_adapter, int32_t S) {
+    if (!out) return fail(LORA_EINVAL, "null output pointer");
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (T < 0 || S < 0) return fail(LORA_ESEG, "negative token or segment count");
+    if (!seg_starts || (S > 0 && !seg_adapter)) return fail(LORA_EINVAL, "null segment table");
+    if (seg_starts[0] != 0) return fail(LORA_ESEG, "seg_starts[0] = %d, not 0", seg_starts[0]);
+    if (seg_starts[S] != T)
+        return fail(LORA_ESEG, "seg_starts[%d] = %d, not num_tokens %d", S, seg_starts[S], T);
+    for (int32_t s = 0; s < S; ++s) {
+        if (seg_starts[s + 1] < seg_starts[s])
+            return fail(LORA_ESEG, "seg_starts decreases at segment %d", s);
+        const int32_t id = seg_adapter[s];
+        if (id < -1) return fail(LORA_ENOENT, "segment %d names adapter id %d", s, id);
+        if (id >= 0 && !p->slots.count(id))
+            return fail(LORA_ENOENT, "segment %d names unregistered adapter %d", s, id);
+    }
+
+    lora_plan *pl = new lora_plan();
+    pl->pool = p;
+    pl->pool_generation = p->generation;
+    pl->T = T;
+    pl->token_group.assign(T, -1);
+
+    // groups in first-appearance order (segments with tokens only)
+    std::unordered_map<int32_t, int32_t> gidx;
+    std::vector<std::vector<int32_t>> members;
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t id = seg_adapter[s];
+        if (id < 0 || seg_starts[s + 1] == seg_starts[s]) continue;
+        auto it = gidx.find(id);
+        int32_t g;
+        if (it == gidx.end()) {
+            g = int32_t(members.size());
+            gidx.emplace(id, g);
+            members.emplace_back();
+            pl->group_adapter.push_back(id);
+            pl->group_rank.push_back(p->slots.at(id).rank);
+        } else {
+            g = it->second;
+        }
+        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) {
+            members[g].push_back(t);
+            pl->token_group[t] = g;
+        }
+    }
+    std::vector<int32_t> idle;
+    for (int32_t t = 0; t < T; ++t)
+        if (pl->token_group[t] < 0) idle.push_back(t);
+
+    // blocks: each group cut into near-equal blocks of at most kMaxBlockTokens
+    auto add_blocks = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
+        const int32_t n = int32_t(toks.size());
+        const int32_t nblk = (n + lora::kMaxBlockTokens - 1) / lora::kMaxBlockTokens;
+        int32_t start = 0;
+        for (int32_t i = 0; i < nblk; ++i) {
+            const int32_t cnt = n / nblk + (i < n % nblk ? 1 : 0);
+            BlockDesc bd{};
+            bd.tok_off = int32_t(pl->token_order.size()) + start;
+            bd.n_tok = cnt;
+            bd.r_pad = sl ? sl->r_pad : 0;
+            bd.rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
+            bd.scale = sl ? sl->scale : 0.f;
+            bd.group = g;
+            bd.ext_lo = sl ? uint32_t(sl->off & 0xffffffffu) : 0u;
+            bd.ext_hi = sl ? uint32_t(sl->off >> 32) : 0u;
+            pl->blocks.push_back(bd);
+            pl->max_block = std::max(pl->max_block, cnt);
+            start += cnt;
+        }
+        pl->token_order.insert(pl->token_order.end(), toks.begin(), toks.end());
+    };
+    for (int32_t g = 0; g < int32_t(members.size()); ++g)
+        add_blocks(members[g], g, &p->slots.at(pl->group_adapter[g]));
+    pl->nb_act = int32_t(pl->blocks.size());
+    pl->n_active = int32_t(pl->token_order.size());
+    add_blocks(idle, -1, nullptr);
+
+    pl->rt_prefix.assign(pl->nb_act + 1, 0);
+    for (int32_t b = 0; b < pl->nb_act; ++b)
+        pl->rt_prefix[b + 1] = pl->rt_prefix[b] + pl->blocks[b].rt;
+    const int32_t tiles = (pl->max_block + lora::kTile - 1) / lora::kTile;
+    pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
+    *out = pl;
+    return LORA_OK;
+}
+
+lora_status lora_plan_destroy(lora_plan *pl) {
+    if (!pl) return fail(LORA_EINVAL, "null plan");
+    if (pl->staged) {
+        (void)hipEventSynchronize(pl->staged);
+        (void)hipEventDestroy(pl->staged);
+    }
+    if (pl->staging) (void)hipHostFree(pl->staging);
+    delete pl;
+    return LORA_OK;
+}
+
+uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj) {
+    if (!pl || max_proj < 1 || max_proj > LORA_MAX_PROJ) return 0;
+    lora_plan tmp;   // compute the layout without touching the plan
+    tmp.pool = pl->pool;
+    tmp.T = pl->T;
+    tmp.blocks = pl->blocks;
+    tmp.rt_prefix = pl->rt_prefix;
+    tmp.nb_act = pl->nb_act;
+    tmp.tt = pl->tt;
+    tmp.layout(max_proj);
+    return tmp.ws_bytes;
+}
+
+lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
+                             void *stream) {
+    if (!pl) return fail(LORA_EINVAL, "null plan");
+    if (max_proj < 1 || max_proj > LORA_MAX_PROJ)
+        return fail(LORA_EINVAL, "max_proj %d not in 1..%d", max_proj, LORA_MAX_PROJ);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return fail(LORA_EINVAL, "workspace must be a non-null, 256-byte aligned device pointer");
+    const uint64_t need = lora_plan_workspace_bytes(pl, max_proj);
+    if (ws_bytes < need)
+        return fail(LORA_ESTATE, "workspace of %llu bytes < %llu needed",
+                    (unsigned long long)ws_bytes, (unsigned long long)need);
+    hipError_t e;
+    if (pl->staged) {   // the previous image may still be in flight
+        e = hipEventSynchronize(pl->staged);
+        if (e != hipSuccess) return hip_fail(e, "plan staging wait");
+    }
+    lora_plan probe = lora_plan();   // layout of the new image
+    probe.pool = pl->pool; probe.T = pl->T; probe.blocks = pl->blocks;
+    probe.rt_prefix = pl->rt_prefix; probe.nb_act = pl->nb_act; probe.tt = pl->tt;
+    probe.layout(max_proj);
+    if (pl->staging_bytes < probe.image_bytes) {
+        void *buf = nullptr;
+        e = hipHostMalloc(&buf, probe.image_bytes, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "plan staging buffer");
+        if (pl->staging) (void)hipHostFree(pl->staging);
+        pl->staging = buf;
+        pl->staging_bytes = probe.image_bytes;
+    }
+    if (!pl->staged) {
+        e = hipEventCreateWithFlags(&pl->staged, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "plan staging event");
+    }
+    pl->layout(max_proj);
+    pl->max_proj = max_proj;
+    uint8_t *img = static_cast<uint8_t *>(pl->staging);
+    std::memset(img, 0, pl->image_bytes);   // also zeroes the fix-up counters
+    if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
+    if (!pl->blocks.empty())
+        std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
+    std::memcpy(img + pl->off_rtp, pl->rt_prefix.data(), 4ull * pl->rt_prefix.size());
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(ws, img, pl->image_bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "plan upload");
+    e = hipEventRecord(pl->staged, st);
+    if (e != hipSuccess) return hip_fail(e, "plan staging event record");
+    pl->ws = ws;
+    return LORA_OK;
+}
+
+lora_status lora_plan_stats(const lora_plan *pl, int32_t *ng, int32_t *nb, int32_t *na,
+                            int32_t *mb) {
+    if (!pl) return fail(LORA_EINVAL, "null plan");
+    if (ng) *ng = int32_t(pl->group_adapter.size());
+    if (nb) *nb = pl->nb_all();
+    if (na) *na = pl->n_active;
+    if (mb) *mb = pl->max_block;
+    return LORA_OK;
+}
+
+lora_status lora_plan_export(const lora_plan *pl, int32_t *order, int32_t *tgroup,
+                             int32_t *gad, int32_t *grank) {
+    if (!pl) return fail(LORA_EINVAL, "null plan");
+    if (order && pl->T) std::memcpy(order, pl->token_order.data(), 4ull * pl->T);
+    if (tgroup && pl->T) std::memcpy(tgroup, pl->token_group.data(), 4ull * pl->T);
+    const size_t G = pl->group_adapter.size();
+    if (gad && G) std::memcpy(gad, pl->group_adapter.data(), 4 * G);
+    if (grank && G) std::memcpy(grank, pl->group_rank.data(), 4 * G);
+    return LORA_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------- sgmv ----
+namespace {
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+struct CallCheck {
+    int32_t h_in = 0;
+    int32_t es = 0;
+    int32_t vec = 0;   // elements per 16 bytes
+};
+
+lora_status check_call(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                       const int32_t *projs, CallCheck *cc) {
+    if (!p || !pl) return fail(LORA_EINVAL, "null pool or plan");
+    if (pl->pool != p) return fail(LORA_EINVAL, "plan was built for another pool");
+    if (pl->pool_generation != p->generation)
+        return fail(LORA_ESTATE, "an adapter was unregistered after the plan was built");
+    if (!pl->ws) return fail(LORA_ESTATE, "plan has not been uploaded");
+    if (layer < 0 || layer >= p->d.num_layers)
+        return fail(LORA_EINVAL, "layer %d not in 0..%d", layer, p->d.num_layers - 1);
+    if (nproj < 1 || nproj > pl->max_proj)
+        return fail(LORA_EINVAL, "nproj %d not in 1..%d (plan uploaded for %d)", nproj,
+                    pl->max_proj, pl->max_proj);
+    if (!projs) return fail(LORA_EINVAL, "null projection list");
+    for (int i = 0; i < nproj; ++i) {
+        if (projs[i] < 0 || projs[i] >= p->d.num_proj)
+            return fail(LORA_EINVAL, "projection %d not in 0..%d", projs[i], p->d.num_proj - 1);
+        for (int k = 0; k < i; ++k)
+            if (projs[k] == projs[i]) return fail(LORA_EINVAL, "projection %d listed twice", projs[i]);
+        if (p->d.h_in[projs[i]] != p->d.h_in[projs[0]])
+            return fail(LORA_EINVAL, "projections of one call must share h_in");
+    }
+    cc->h_in = p->d.h_in[projs[0]];
+    cc->es = esize(p->d.dtype);
+    cc->vec = 16 / cc->es;
+    return LORA_OK;
+}
+
+lora_status check_y(const lora_pool *p, int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                    const void *y, int64_t ldy, const char *name, const CallCheck &cc) {
+    if (!yoff) return fail(LORA_EINVAL, "null y_offsets");
+    if (!y || !aligned16(y)) return fail(LORA_EINVAL, "%s must be non-null and 16-byte aligned", name);
+    if (ldy < 1 || ldy % 8 || ldy % cc.vec)
+        return fail(LORA_EINVAL, "ld of %s (%lld) must be a positive multiple of 8", name,
+                    (long long)ldy);
+    for (int i = 0; i < nproj; ++i) {
+        if (yoff[i] < 0 || yoff[i] % 8)
+            return fail(LORA_EINVAL, "y_offsets[%d] = %d must be a non-negative multiple of 8", i,
+                        yoff[i]);
+        if (int64_t(yoff[i]) + p->d.h_out[projs[i]] > ldy)
+            return fail(LORA_EINVAL, "slice of projection %d exceeds ld of %s", projs[i], name);
+    }
+    return LORA_OK;
+}
+
+// k-chunking of the shrink: enough units to fill the GPU, never more than
+// kTargetWaves + nproj * rt_total (the workspace is sized for that).
+void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
+                     int32_t *kc, int32_t *c0) {
+    const int64_t per_chunk = int64_t(nproj) * std::max(pl->rt_total(), 1);
+    const int32_t frags = (h_in + span - 1) / span;
+    int64_t want = (lora::kTargetWaves + per_chunk - 1) / per_chunk;
+    want = std::max<int64_t>(1, std::min<int64_t>(want, frags));
+    const int32_t fper = int32_t((frags + want - 1) / want);
+    *kc = fper * span;
+    *c0 = (h_in + *kc - 1) / *kc;
+}
+
+lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                       const int32_t *projs, const void *x, int64_t ldx, float *v, int64_t ldv,
+                       const CallCheck &cc, hipStream_t st) {
+    if (pl->nb_act == 0) return LORA_OK;
+    lora::ShrinkArgs a{};
+    const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
+    a.slab = p->slab;
+    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
+    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
+    a.counters = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(ws) + pl->off_cnt);
+    a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->off_part);
+    a.x = x;
+    a.v = v;
+    a.ldx = ldx;
+    a.ldv = ldv;
+    for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
+    a.nb = pl->nb_act;
+    a.nproj = nproj;
+    a.h_in = cc.h_in;
+    shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
+    a.units = nproj * pl->rt_total() * a.c0;
+    a.r_max = p->d.r_max;
+    const uint64_t need = 4ull * uint64_t(a.units) * pl->tt * lora::kTile * lora::kTile;
+    if (need > pl->part_bytes)
+        return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
+                    (unsigned long long)need, (unsigned long long)pl->part_bytes);
+    hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, a, st);
+    if (e != hipSuccess) return hip_fail(e, "shrink launch");
+    return LORA_OK;
+}
+
+lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                       const int32_t *projs, const int32_t *yoff, const float *v, int64_t ldv,
+                       void *y, int64_t ldy, const void *base, int64_t ldb, hipStream_t st) {
+    const int32_t nb = base ? pl->nb_all() : pl->nb_act;
+    if (nb == 0) return LORA_OK;
+    lora::ExpandArgs a{};
+    const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
+    a.slab = p->slab;
+    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
+    a.v = v;
+    a.y = y;
+    a.base = base;
+    a.ldv = ldv;
+    a.ldy = ldy;
+    a.ldb = ldb;
+    int64_t rows = 0;
+    for (int i = 0; i < nproj; ++i) {
+        a.coef_b[i] = p->coef_b(layer, projs[i]);
+        a.h_out[i] = p->d.h_out[projs[i]];
+        a.y_off[i] = yoff[i];
+        rows += a.h_out[i];
+    }
+    // o-chunk rows: enough units to fill the GPU, at least one 32-row pair of tiles
+    int64_t oc = (rows * nb + lora::kTargetWaves - 1) / lora::kTargetWaves;
+    oc = std::max<int64_t>(32, std::min<int64_t>(1024, round_up(uint64_t(oc), 32)));
+    a.oc = int32_t(oc);
+    a.oc_prefix[0] = 0;
+    for (int i = 0; i < nproj; ++i)
+        a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + a.oc - 1) / a.oc;
+    for (int i = nproj; i < LORA_MAX_PROJ; ++i) a.oc_prefix[i + 1] = INT32_MAX;
+    a.nb = nb;
+    a.nproj = nproj;
+    a.units = nb * a.oc_prefix[nproj];
+    a.r_max = p->d.r_max;
+    hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, a, st);
+    if (e != hipSuccess) return hip_fail(e, "expand launch");
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                        const int32_t *projs, const void *x, int64_t ldx, float *v, int64_t ldv,
+                        void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    if (pl->T == 0) return LORA_OK;   // empty batch: nothing to read or write
+    if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
+    if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
+                                               (long long)ldx);
+    if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
+    if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
+        return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
+    return run_shrink(p, pl, layer, nproj, projs, x, ldx, v, ldv, cc,
+                      static_cast<hipStream_t>(stream));
+}
+
+lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                        const int32_t *projs, const int32_t *yoff, const float *v, int64_t ldv,
+                        void *y, int64_t ldy, void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    if (pl->T == 0) return LORA_OK;   // empty batch: nothing to read or write
+    if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
+    if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
+        return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
+    st = check_y(p, nproj, projs, yoff, y, ldy, "y", cc);
+    if (st != LORA_OK) return st;
+    return run_expand(p, pl, layer, nproj, projs, yoff, v, ldv, y, ldy, nullptr, 0,
+                      static_cast<hipStream_t>(stream));
+}
+
+lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                       const int32_t *projs, const int32_t *yoff, const void *x, int64_t ldx,
+                       const void *base, int64_t ldb, void *y, int64_t ldy, void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    if (pl->T == 0) return LORA_OK;   // empty batch: nothing to read or write
+    if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
+    if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
+                                               (long long)ldx);
+    st = check_y(p, nproj, projs, yoff, y, ldy, "y", cc);
+    if (st != LORA_OK) return st;
+    if (base) {
+        st = check_y(p, nproj, projs, yoff, base, ldb, "base", cc);
+        if (st != LORA_OK) return st;
+    }
+    float *v = reinterpret_cast<float *>(static_cast<uint8_t *>(pl->ws) + pl->off_v);
+    const int64_t ldv = int64_t(pl->max_proj) * p->d.r_max;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, v, ldv, cc, hs);
+    if (st != LORA_OK) return st;
+    return run_expand(p, pl, layer, nproj, projs, yoff, v, ldv, y, ldy, base, ldb, hs);
+}
+
+}  // extern "C"

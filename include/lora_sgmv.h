@@ -1,0 +1,226 @@
+/*
+ * lora_sgmv.h -- C ABI of the MI355X (gfx950) multi-adapter LoRA delta library.
+ *
+ * The library computes, for a heterogeneous batch of token rows in which each
+ * contiguous segment of tokens names one adapter of an HBM-resident pool,
+ *
+ *     y[t, off_p : off_p + h_out_p] (+)= s_i * B_i,p (A_i,p x[t])       (*)
+ *
+ * where i is the adapter of the segment holding token t and p the adapted
+ * projection.  Sources for the operation:
+ *   - LoRA: the base weight stays frozen and two small trained matrices A and
+ *     B carry the update ("TGI Multi-LoRA: Deploy Once, Serve 30 Models",
+ *     section "Technical Foundation: Low-Rank Adaptation (LoRA)").
+ *   - One request names one adapter, so one batch mixes adapters (same page,
+ *     "How Multi-LoRA Serving Works"); grouping the requests that share an
+ *     adapter is the segmented gather of SGMV ("Compress then Serve", the
+ *     rebuttal paragraph on Punica).
+ *   - The A step runs with scale 1.0 into a float32 buffer of shape
+ *     (tokens, R); the B step applies the scale and updates a slice of y
+ *     given by y_offset and y_slice_size ("Compress then Serve", rebuttal
+ *     pseudocode of add_lora_slice_with_sigma, buffer creation and steps 1
+ *     and 3).
+ *   - Adapters of different ranks in one batch ("how does this differ from
+ *     s-Lora?" issue thread: the multi-rank kernel and the rank caveats).
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are row-major.  A_i,p is r_i x h_in_p and B_i,p is h_out_p x r_i.
+ *   - The caller owns ALL device memory (the pool slab, activations, outputs,
+ *     the intermediate v and the plan workspace).  The library never calls
+ *     hipMalloc or hipFree.  It owns host metadata only, plus one pinned
+ *     host staging buffer per plan.
+ *   - Calls that take `stream` (a hipStream_t, passed as void*) only enqueue
+ *     work on it and do not synchronise; results are valid in stream order.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     A status other than LORA_OK means nothing was enqueued and no library
+ *     state changed; lora_last_error() then holds a message (thread-local).
+ *   - Element type of x, y, base_out and pool weights is the pool's dtype
+ *     (bf16 or f32).  v is always float32.  Device pointers must be 16-byte
+ *     aligned and leading dimensions multiples of 16 bytes' worth of elements
+ *     (8 for bf16, 4 for f32); h_in_p and h_out_p must be multiples of 8.
+ *   - Arithmetic: products of inputs are formed exactly and summed in float32
+ *     (the float32 intermediate of the pseudocode); y is rounded once, to
+ *     nearest-even, to the output type.  Results are deterministic: the same
+ *     call on the same inputs gives the same bits.
+ *   - Thread safety: calls on different pools/plans are independent.  Pool
+ *     mutation must not overlap launches that read the same slots, and one
+ *     plan workspace must not be used by two streams at once.
+ */
+#ifndef LORA_SGMV_H
+#define LORA_SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LORA_OK = 0,
+    LORA_EINVAL = -1,  /* bad argument: null pointer, size, stride, alignment */
+    LORA_ENOSPC = -2,  /* pool slab or slot table full */
+    LORA_ENOENT = -3,  /* adapter id not registered */
+    LORA_ERANK = -4,   /* rank < 1 or rank > r_max */
+    LORA_EDTYPE = -5,  /* unsupported element type */
+    LORA_ESEG = -6,    /* malformed segment table */
+    LORA_EHIP = -7,    /* a HIP runtime call failed */
+    LORA_EEXIST = -8,  /* adapter id already registered */
+    LORA_ESTATE = -9   /* plan not uploaded, or its workspace is too small */
+} lora_status;
+
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+#define LORA_MAX_PROJ 8   /* adapted projections per pool (q, k, v, o, gate, up, down, ...) */
+#define LORA_MAX_RANK 64  /* largest supported r_max */
+
+/* Shape of a pool: every adapter carries A and B for each (layer, projection). */
+typedef struct {
+    int32_t num_layers;             /* L >= 1 */
+    int32_t num_proj;               /* 1 .. LORA_MAX_PROJ */
+    int32_t h_in[LORA_MAX_PROJ];    /* input width of projection p (multiple of 8) */
+    int32_t h_out[LORA_MAX_PROJ];   /* output width of projection p (multiple of 8) */
+    int32_t r_max;                  /* largest rank accepted; multiple of rank_granule, <= 64 */
+    int32_t rank_granule;           /* ranks are zero-padded to a multiple of this (8 or 16) */
+    int32_t max_slots;              /* most adapters resident at once */
+    int32_t dtype;                  /* lora_dtype of weights, activations and outputs */
+} lora_pool_desc;
+
+typedef struct lora_pool lora_pool;
+typedef struct lora_plan lora_plan;
+
+/* Message for the last non-OK status returned on this thread. */
+const char *lora_last_error(void);
+
+/* ---------------------------------------------------------------- pool ---- */
+
+/* Bytes of one adapter at its true rank: sum over layers and projections of
+ * rank * (h_in + h_out) * element size.  This is the adapter size the pages
+ * quote (13.6 MB for a Mistral-7B q,v adapter of rank 16 in 16-bit, "TGI
+ * Multi-LoRA", section "Technical Foundation").  0 on a bad descriptor. */
+uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank);
+
+/* Bytes one adapter occupies in the slab: the same sum at the padded rank,
+ * rounded up to 256 bytes.  0 on a bad descriptor or rank. */
+uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank);
+
+/* Create a pool over a caller-owned device buffer `slab` of `slab_bytes`
+ * (256-byte aligned).  Each adapter occupies one contiguous extent of the
+ * slab; inside it, for layer l and projection p, the A block [r_pad][h_in_p]
+ * is followed by the B block [h_out_p][r_pad], layers outermost.  Pad rows
+ * of A and pad columns of B are zero.  The slab is not touched here and is
+ * not freed by lora_pool_destroy. */
+lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d,
+                             void *slab, uint64_t slab_bytes);
+lora_status lora_pool_destroy(lora_pool *p);
+
+/* Reserve an extent and a slot for `adapter_id` (>= 0) at `rank` with scale
+ * `scale` (the adapter's alpha / r).  The extent's contents are undefined
+ * until uploaded.  Errors: LORA_EEXIST, LORA_ERANK, LORA_ENOSPC, LORA_EINVAL. */
+lora_status lora_pool_reserve(lora_pool *p, int32_t adapter_id, int32_t rank, float scale);
+
+/* Copy the weights of one (layer, proj) of a reserved adapter into its
+ * extent, zero-filling the rank padding.  A: [rank][h_in_p], B: [h_out_p][rank],
+ * both dense row-major in the pool dtype, in host memory (src_on_host = 1) or
+ * device memory (0).  Enqueued on `stream`; host sources are copied before
+ * the call returns. */
+lora_status lora_pool_upload(lora_pool *p, int32_t adapter_id, int32_t layer, int32_t proj,
+                             const void *A, const void *B, int32_t src_on_host, void *stream);
+
+/* Reserve and upload every (layer, proj): A[p] -> [L][rank][h_in_p] and
+ * B[p] -> [L][h_out_p][rank] (arrays of num_proj pointers).  On an upload
+ * error the reservation is released again. */
+lora_status lora_pool_register(lora_pool *p, int32_t adapter_id, int32_t rank, float scale,
+                               const void *const *A, const void *const *B,
+                               int32_t src_on_host, void *stream);
+
+/* Release an adapter's slot and extent.  Plans built earlier that name the
+ * adapter must not be launched afterwards. */
+lora_status lora_pool_unregister(lora_pool *p, int32_t adapter_id);
+
+/* Where an adapter lives: rank, padded rank, scale and extent byte offset in
+ * the slab (any output pointer may be NULL).  LORA_ENOENT if absent. */
+lora_status lora_pool_query(const lora_pool *p, int32_t adapter_id, int32_t *rank,
+                            int32_t *r_pad, float *scale, uint64_t *extent_offset);
+
+/* Number of resident adapters and free slab bytes. */
+lora_status lora_pool_stats(const lora_pool *p, int32_t *num_adapters, uint64_t *free_bytes);
+
+/* ---------------------------------------------------------------- plan ---- */
+
+/* Build the gather plan of one heterogeneous batch (host memory inputs).
+ *   num_tokens T >= 0; seg_starts[S+1] with seg_starts[0] = 0, non-decreasing,
+ *   seg_starts[S] = T; seg_adapter[S] holds adapter ids, -1 = no adapter.
+ *   Empty segments are allowed and ids may repeat.
+ * Segments are grouped by adapter in first-appearance order (the segmented
+ * gather), each group is cut into blocks of at most 64 tokens, and every id
+ * is resolved to its slot, rank and scale.  Errors: LORA_ESEG, LORA_ENOENT.
+ * The plan stays valid while its adapters stay registered. */
+lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_tokens,
+                             const int32_t *seg_starts, const int32_t *seg_adapter,
+                             int32_t num_segs);
+lora_status lora_plan_destroy(lora_plan *pl);   /* waits for its last upload */
+
+/* Device bytes the plan needs: its tables, per-call partial sums and the v
+ * buffer of sgmv_fused, sized for calls of up to `max_proj` projections at
+ * once.  0 on error. */
+uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj);
+
+/* Copy the plan's tables into the caller-owned device workspace `ws`
+ * (256-byte aligned, at least lora_plan_workspace_bytes(pl, max_proj)) and
+ * reset its counters, on `stream`.  Every sgmv call with this plan then uses
+ * `ws`; calls must be ordered after this upload on the same stream. */
+lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
+                             void *stream);
+
+/* Plan summary: groups, blocks, tokens with an adapter, largest block. */
+lora_status lora_plan_stats(const lora_plan *pl, int32_t *num_groups, int32_t *num_blocks,
+                            int32_t *num_active_tokens, int32_t *max_block_tokens);
+
+/* Export the plan's gather tables (host arrays, any may be NULL):
+ *   token_order[T]     token rows in plan order (grouped; no-adapter tokens last)
+ *   token_group[T]     group index of each token row (-1 = no adapter)
+ *   group_adapter[G]   adapter id of each group, first-appearance order
+ *   group_rank[G]      its rank */
+lora_status lora_plan_export(const lora_plan *pl, int32_t *token_order, int32_t *token_group,
+                             int32_t *group_adapter, int32_t *group_rank);
+
+/* ---------------------------------------------------------------- sgmv ---- */
+/* For all three: `projs` lists `nproj` projection indices of the pool that
+ * read the same input x (e.g. q, k, v), so x has width h_in of all of them
+ * (they must agree).  For projection i of the list, its output is the
+ * column slice y[:, y_offsets[i] : y_offsets[i] + h_out] (the pseudocode's
+ * y_offset and y_slice_size), and its v columns are
+ * v[:, i * r_max : i * r_max + r_max].  With num_tokens = 0 the calls
+ * validate the pool, plan and projection list and do nothing else. */
+
+/* Shrink (the A step, scale 1.0): v[t][i*r_max + j] = sum_k A_i,p[j][k] x[t][k]
+ * for every token with an adapter, j < r_max (columns j >= rank are zero).
+ * Rows of tokens without an adapter are not written.
+ * x: [T][ldx] device; v: [T][ldv] float32 device, ldv >= nproj * r_max. */
+lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                        int32_t nproj, const int32_t *projs,
+                        const void *x, int64_t ldx, float *v, int64_t ldv, void *stream);
+
+/* Expand (the B step): y[t][y_offsets[i] + o] += s_i * sum_j B_i,p[o][j] v[t][i*r_max + j]
+ * for every token with an adapter, computed in float32 from the current y
+ * and rounded once.  Rows of tokens without an adapter are not written.
+ * v: [T][ldv] float32 device; y: [T][ldy] device. */
+lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                        int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                        const float *v, int64_t ldv, void *y, int64_t ldy, void *stream);
+
+/* Fused shrink then expand: y = y_in + s_i * B_i,p (A_i,p x), with y_in = base
+ * (base_out of the frozen layer, same column layout as y, [T][ldb]) when base
+ * is non-NULL, else the current y.  Tokens without an adapter get y = base
+ * (or are left untouched when base is NULL).  v lives in the workspace. */
+lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                       int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                       const void *x, int64_t ldx, const void *base, int64_t ldb,
+                       void *y, int64_t ldy, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_SGMV_H */

@@ -1,0 +1,386 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+The contract tolerance is max|y_gpu - y_ref| <= 1e-2 * max|y_ref| + 1e-3 per
+output tensor, for bf16 inputs with float32 accumulation.  On small cases a
+much tighter bound is also enforced: the GPU must be as accurate as float32
+arithmetic itself (a rounding-error bound for the two sums, the scale and the
+add, plus the single rounding of y to bf16), measured against the float64
+oracle.  Gather, segment indexing, padding, permutation and determinism are
+checked bit for bit.
+"""
+import dataclasses
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import config, random_case, Proj
+from synth.device import DeviceWorkload, from_device
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import heterogeneous_adapter_batching_amd as hab
+    hab.load()
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def contract_check(y_gpu, y_ref, what):
+    tol = 1e-2 * float(np.abs(y_ref).max()) + 1e-3
+    err = float(np.abs(y_gpu.astype(np.float64) - y_ref).max()) if y_ref.size else 0.0
+    assert err <= tol, f"{what}: max|diff| {err:.3e} > tol {tol:.3e}"
+    return err, tol
+
+
+def oracle_ref(w, layer, p, acc="f32", threads=8):
+    return oracle.workload_call(w, layer, p, acc=acc, threads=threads)
+
+
+def tight_bound(w, layer, p, out_bf16):
+    """Per-element bound for a float32 evaluation of y_in + s B (A x) in any
+    summation order (|error| <= gamma_n * sum|terms| per sum, with 2u per
+    operation to allow a non-nearest internal rounding), plus the final
+    rounding of y to the output type."""
+    u = 2.0 ** -23
+    pr = w.projs[p]
+    x = w.activation(layer, pr.x_key).astype(np.float64)
+    tok = w.token_adapter()
+    y_in = w.base_out(layer, p).astype(np.float64) if w.has_base else np.zeros(
+        (w.num_tokens, pr.h_out))
+    bound = np.zeros((w.num_tokens, pr.h_out))
+    for t in range(w.num_tokens):
+        i = int(tok[t])
+        if i < 0:
+            continue
+        a, b = (m.astype(np.float64) for m in w.adapter_block(i, layer, p))
+        s = abs(float(w.scales[i]))
+        r = a.shape[0]
+        absv = np.abs(a) @ np.abs(x[t])
+        ga = (pr.h_in + 64) * u
+        gb = (3 * r + 4) * u
+        e = s * (ga * (np.abs(b) @ absv) + gb * (np.abs(b) @ absv)) + u * (
+            np.abs(y_in[t]) + s * (np.abs(b) @ absv))
+        bound[t] = e
+    y64 = oracle_ref(w, layer, p, acc="f64")
+    out_r = (2.0 ** -8 if out_bf16 else 2.0 ** -24) * (np.abs(y64) + bound)
+    return y64, 1.01 * (bound + out_r) + 1e-30
+
+
+def check_workload(dw, tight=False, threads=8):
+    w = dw.w
+    for l in dw.layers:
+        for p in range(len(w.projs)):
+            got = dw.output(l, p)
+            ref = oracle_ref(w, l, p, threads=threads)
+            contract_check(got, ref, f"{w.name} layer {l} proj {w.projs[p].name}")
+            if tight:
+                y64, bnd = tight_bound(w, l, p, w.dtype == "bf16")
+                viol = np.abs(got.astype(np.float64) - y64) > bnd
+                assert not viol.any(), (
+                    f"{w.name} {w.projs[p].name}: {int(viol.sum())} elements outside the "
+                    f"float32 bound, worst {np.max(np.abs(got - y64) - bnd):.3e}")
+
+
+# ------------------------------------------------------------- workloads ----
+@pytest.mark.parametrize("ci", [0, 1, 2, 3])
+def test_workload_parity(ci):
+    w = config(ci)
+    log(f"[parity] workload {ci} {w.name}")
+    dw = DeviceWorkload(w, slab_fill=0xFF if ci == 3 else None)   # NaN over untouched extents
+    dw.zero_outputs()
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=ci in (0, 1))
+
+
+def test_full_stack_parity():
+    """The 32-layer x 7-projection stack, in the launch pattern the benchmark
+    times (4 calls per layer: qkv, o, gate_up, down), every output checked."""
+    w = config(4)
+    log("[parity] full stack (workload 4)")
+    refs = {}
+    pending = {}
+    touched = w.touched()
+
+    def on_block(aid, l, p, a, b):
+        pending.setdefault((l, p), {})[aid] = (a, b, float(w.scales[aid]))
+        if len(pending[(l, p)]) == len(touched):
+            pr = w.projs[p]
+            refs[(l, p)] = oracle.lora_delta(w.activation(l, pr.x_key), w.seg_starts,
+                                             w.seg_adapter, pending.pop((l, p)),
+                                             w.base_out(l, p), threads=16)
+
+    dw = DeviceWorkload(w, on_block=on_block)
+    dw.run_fused()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for (l, p), ref in refs.items():
+        got = dw.output(l, p)
+        err, tol = contract_check(got, ref, f"layer {l} proj {w.projs[p].name}")
+        # the delta alone, to a tolerance scaled by the delta (plus bf16 rounding of y)
+        d_ref = ref - w.base_out(l, p)
+        lim = 1e-2 * np.abs(d_ref).max() + 1e-3 + 2.0 ** -8 * np.abs(ref)
+        assert np.all(np.abs(got - ref) <= lim), f"delta check layer {l} proj {p}"
+        worst = max(worst, err / tol)
+    assert len(refs) == 32 * 7
+    log(f"[parity] full stack worst err/tol {worst:.3f}")
+
+
+# ---------------------------------------------------------- random cases ----
+def multi_proj_case(seed, dtype="bf16", has_base=False, T=None, r_max=64):
+    g = np.random.default_rng(seed)
+    base = random_case(seed, dtype=dtype, has_base=has_base, T=T, r_max=r_max,
+                       h_in=int(g.integers(1, 70)) * 8)
+    nproj = int(g.integers(1, 4))
+    projs = tuple(Proj(f"p{i}", base.projs[0].h_in, int(g.integers(1, 50)) * 8, "x")
+                  for i in range(nproj))
+    return dataclasses.replace(base, projs=projs, calls=(tuple(range(nproj)),))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_heterogeneous(seed):
+    dtype = "f32" if seed % 4 == 3 else "bf16"
+    w = multi_proj_case(seed, dtype=dtype, has_base=seed % 2 == 0)
+    log(f"[parity] random {seed} T={w.num_tokens} S={w.num_segs} projs="
+        f"{[(p.h_in, p.h_out) for p in w.projs]} ranks={list(w.ranks)} {dtype}")
+    dw = DeviceWorkload(w, threads=4)
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_blocks(seed):
+    """Long same-adapter segments: several 64-token blocks per group, ragged tails."""
+    T = [65, 130, 200, 257][seed]
+    w = random_case(100 + seed, T=T, h_in=512, h_out=256, n_adapters=3, max_seg=T,
+                    no_adapter_frac=0.0, r_choices=[8, 16, 32, 64])
+    log(f"[parity] prefill {seed} T={T} segments={list(np.diff(w.seg_starts))}")
+    dw = DeviceWorkload(w, threads=4)
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
+def test_two_step_equals_fused():
+    """sgmv_shrink + sgmv_expand through a v buffer gives the same bits as sgmv_fused."""
+    for w in (config(1), multi_proj_case(3, has_base=True), config(0)):
+        log(f"[parity] two-step vs fused {w.name}")
+        dw = DeviceWorkload(w, threads=4)
+        dw.zero_outputs()
+        dw.run_fused()
+        fused = {k: from_device(v) for k, v in dw.y.items()}
+        dw.zero_outputs()
+        dw.run_two_step()
+        torch.cuda.synchronize()
+        for k, v in dw.y.items():
+            assert np.array_equal(from_device(v), fused[k]), k
+
+
+def test_shrink_output_layout():
+    """v holds A x in columns [i*r_max, i*r_max + rank) and zeros up to r_max;
+    rows of tokens without an adapter are left as they were."""
+    import heterogeneous_adapter_batching_amd as hab
+    w = multi_proj_case(7, T=40, r_max=32)
+    w = dataclasses.replace(w, ranks=np.minimum(w.ranks, 32))
+    dw = DeviceWorkload(w, threads=4)
+    n = len(w.projs)
+    v = torch.full((w.num_tokens, n * 32 + 8), 7.0, device="cuda")
+    hab.sgmv_shrink(dw.pool, dw.plan, 0, tuple(range(n)), dw.x[(0, "x")], v)
+    v = v.cpu().numpy()
+    x = w.activation(0, "x").astype(np.float64)
+    tok = w.token_adapter()
+    for t in range(w.num_tokens):
+        i = int(tok[t])
+        if i < 0:
+            assert np.all(v[t] == 7.0)
+            continue
+        for p in range(n):
+            a, _ = w.adapter_block(i, 0, p)
+            r = a.shape[0]
+            ref = a.astype(np.float64) @ x[t]
+            tol = 1e-5 * (np.abs(a) @ np.abs(x[t])) + 1e-30
+            assert np.all(np.abs(v[t, p * 32:p * 32 + r] - ref) <= tol)
+            assert np.all(v[t, p * 32 + r:(p + 1) * 32] == 0)
+        assert np.all(v[t, n * 32:] == 7.0)
+
+
+# ------------------------------------------------------------ exact pins ----
+def test_b_zero_identity_bitexact():
+    w = multi_proj_case(11, has_base=True, T=50)
+    over = {}
+    for a in range(w.pool_size):
+        for p in range(len(w.projs)):
+            A, B = w.adapter_block(a, 0, p)
+            over[(a, 0, p)] = (A, np.zeros_like(B))
+    w = dataclasses.replace(w, overrides=over)
+    dw = DeviceWorkload(w, threads=4)
+    dw.run_fused()
+    torch.cuda.synchronize()
+    for p in range(len(w.projs)):
+        assert np.array_equal(dw.output(0, p), w.base_out(0, p))
+
+
+def test_indicator_gather_bitexact():
+    """Indicator adapters make every delta an exact integer that encodes the
+    adapter id: the GPU's gather and segment indexing must reproduce the
+    segment table exactly."""
+    T, h_in, h_out, pool = 300, 64, 32, 400
+    g = np.random.default_rng(17)
+    cuts = np.sort(g.choice(np.arange(1, T), 90, replace=False))
+    starts = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    segs = g.integers(-1, pool, len(starts) - 1).astype(np.int32)
+    ranks = g.choice([1, 8, 16, 24, 64], pool).astype(np.int32)
+    base = random_case(0, T=T, h_in=h_in, h_out=h_out)
+    over = {}
+    for i in range(pool):
+        r = int(ranks[i])
+        a = np.zeros((r, h_in), np.float32)
+        a[0, 0] = 1.0
+        b = np.zeros((h_out, r), np.float32)
+        b[0, 0], b[1, 0] = i % 128, i // 128
+        if r > 1:
+            b[2:, 1:] = 0.5          # multiplies exact zeros of v
+        over[(i, 0, 0)] = (a, b)
+    w = dataclasses.replace(base, num_tokens=T, seg_starts=starts, seg_adapter=segs,
+                            pool_size=pool, ranks=ranks,
+                            scales=np.full(pool, 2.0, np.float32), overrides=over,
+                            seed=77)
+    x = w.activation(0, "x")
+    x[:, 0] = 1.0
+    w.activation = lambda layer, key, _x=x: _x      # noqa: E731  (instance override)
+    dw = DeviceWorkload(w, threads=4)
+    dw.zero_outputs()
+    dw.run_fused()
+    torch.cuda.synchronize()
+    y = dw.output(0, 0)
+    tok = w.token_adapter()
+    for t in range(T):
+        i = int(tok[t])
+        if i < 0:
+            assert np.all(y[t] == 0), t
+        else:
+            assert y[t, 0] == 2 * (i % 128) and y[t, 1] == 2 * (i // 128), (t, i, y[t, :2])
+            assert np.all(y[t, 2:] == 0), t
+
+
+def test_padding_invariance_bitexact():
+    """An adapter stored at rank r equals the same adapter zero-padded to a
+    larger rank, bit for bit."""
+    w = random_case(31, T=70, h_in=256, h_out=128, n_adapters=4, r_choices=[3, 5, 12, 20],
+                    no_adapter_frac=0.0)
+    dw = DeviceWorkload(w, threads=4)
+    dw.run_fused()
+    small = dw.output(0, 0)
+    over, ranks = {}, np.full(w.pool_size, 64, np.int32)
+    for a in range(w.pool_size):
+        A, B = w.adapter_block(a, 0, 0)
+        r = A.shape[0]
+        Ap = np.zeros((64, 256), np.float32)
+        Ap[:r] = A
+        Bp = np.zeros((128, 64), np.float32)
+        Bp[:, :r] = B
+        over[(a, 0, 0)] = (Ap, Bp)
+    w2 = dataclasses.replace(w, ranks=ranks, overrides=over)
+    dw2 = DeviceWorkload(w2, threads=4)
+    dw2.run_fused()
+    torch.cuda.synchronize()
+    assert np.array_equal(dw2.output(0, 0), small)
+
+
+def test_permutation_and_split_invariance_bitexact():
+    w = random_case(41, T=120, h_in=384, h_out=200 // 8 * 8, n_adapters=5, max_seg=30,
+                    r_choices=[8, 16, 32])
+    dw = DeviceWorkload(w, threads=4)
+    dw.run_fused()
+    y = dw.output(0, 0)
+    x = w.activation(0, "x")
+    perm = np.random.default_rng(1).permutation(w.num_segs)
+    rows, starts = [], [0]
+    for si in perm:
+        rows.extend(range(w.seg_starts[si], w.seg_starts[si + 1]))
+        starts.append(starts[-1] + w.seg_starts[si + 1] - w.seg_starts[si])
+    wp = dataclasses.replace(w, seg_starts=np.asarray(starts, np.int32),
+                             seg_adapter=w.seg_adapter[perm])
+    wp.activation = lambda layer, key: x[rows]      # noqa: E731
+    dwp = DeviceWorkload(wp, threads=4)
+    dwp.run_fused()
+    assert np.array_equal(dwp.output(0, 0), y[rows])
+    # split every segment in two
+    s2, a2 = [0], []
+    for si in range(w.num_segs):
+        lo, hi = int(w.seg_starts[si]), int(w.seg_starts[si + 1])
+        s2 += [(lo + hi) // 2, hi]
+        a2 += [w.seg_adapter[si]] * 2
+    ws = dataclasses.replace(w, seg_starts=np.asarray(s2, np.int32),
+                             seg_adapter=np.asarray(a2, np.int32))
+    dws = DeviceWorkload(ws, threads=4)
+    dws.run_fused()
+    torch.cuda.synchronize()
+    assert np.array_equal(dws.output(0, 0), y)
+
+
+def test_determinism():
+    w = config(3)
+    dw = DeviceWorkload(w)
+    outs = []
+    for _ in range(2):
+        dw.zero_outputs()
+        dw.run_fused()
+        torch.cuda.synchronize()
+        outs.append({k: from_device(v) for k, v in dw.y.items()})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k])
+
+
+# ------------------------------------------------------------ edge cases ----
+def test_edge_cases():
+    cases = [
+        random_case(51, T=0, h_in=64, h_out=32),                               # empty batch
+        random_case(52, T=1, h_in=64, h_out=32, no_adapter_frac=0.0),          # one token
+        random_case(53, T=64, h_in=64, h_out=32, n_adapters=1, max_seg=64,
+                    no_adapter_frac=0.0),                                      # one full block
+        random_case(54, T=37, h_in=14336, h_out=64, n_adapters=2,
+                    r_choices=[64]),                                           # long h_in, r_max
+        random_case(55, T=20, h_in=4104, h_out=4104, n_adapters=3),            # ragged widths
+        random_case(56, T=30, h_in=64, h_out=32, no_adapter_frac=1.0, has_base=True),
+    ]
+    for w in cases:
+        log(f"[parity] edge {w.name} T={w.num_tokens} h_in={w.projs[0].h_in} "
+            f"h_out={w.projs[0].h_out}")
+        dw = DeviceWorkload(w, threads=4)
+        dw.run_fused()
+        torch.cuda.synchronize()
+        check_workload(dw, tight=w.projs[0].h_in < 10000, threads=4)
+
+
+def test_call_errors_enqueue_nothing():
+    import heterogeneous_adapter_batching_amd as hab
+    w = random_case(61, T=10, h_in=64, h_out=32)
+    dw = DeviceWorkload(w, threads=2)
+    x, y = dw.x[(0, "x")], dw.y[(0, 0)]
+    plan2 = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter)   # not uploaded
+    with pytest.raises(hab.LoraError) as ei:
+        hab.sgmv_fused(dw.pool, plan2, 0, (0,), (0,), x, y)
+    assert ei.value.status == -9
+    for args, code in (((1, (0,), (0,)), -1), ((0, (1,), (0,)), -1), ((0, (0,), (8,)), -1),
+                       ((0, (0,), (4,)), -1)):
+        with pytest.raises(hab.LoraError) as ei:
+            hab.sgmv_fused(dw.pool, dw.plan, args[0], args[1], args[2], x, y)
+        assert ei.value.status == code, args
+    dw.pool.unregister(int(w.touched()[0]) if len(w.touched()) else 0)
+    with pytest.raises(hab.LoraError) as ei:
+        hab.sgmv_fused(dw.pool, dw.plan, 0, (0,), (0,), x, y)
+    assert ei.value.status == -9

@@ -1,0 +1,212 @@
+"""Host-side tests of the C-ABI library (no GPU calls).
+
+- every function include/lora_sgmv.h declares is exported by libhab_lora.so;
+- the pool's byte accounting reproduces the adapter size the pages print
+  ("TGI Multi-LoRA: Deploy Once, Serve 30 Models", "Technical Foundation":
+  13.6 MB adapter, 14.48 GB Mistral-7B base, under a thousandth, 30 adapters
+  about 3% of VRAM);
+- validation rejects malformed input with the documented status and leaves
+  the pool unchanged;
+- the gather plan (first-appearance grouping, token order, blocks) is
+  bit-exact against an independent re-implementation.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import heterogeneous_adapter_batching_amd as hab
+from heterogeneous_adapter_batching_amd.api import make_desc
+from synth import random_case, config
+from conftest import ROOT, read_golden
+
+HEADER = os.path.join(ROOT, "include", "lora_sgmv.h")
+MISTRAL = dict(h=4096, kv=1024, ffn=14336, layers=32)
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert len(names) >= 18, names
+    lib = ctypes.CDLL(hab.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares every one of them
+    from heterogeneous_adapter_batching_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == names
+
+
+def _pool(**kw):
+    args = dict(num_layers=1, h_in=[64], h_out=[32], r_max=64, dtype="bf16",
+                slab_ptr=1 << 20, slab_bytes=1 << 24)
+    args.update(kw)
+    return hab.Pool(**args)
+
+
+def test_pages_adapter_size():
+    fig = {k: float(v[0]) for k, v in read_golden("pages_figures.txt")}
+    h, kv, L = MISTRAL["h"], MISTRAL["kv"], MISTRAL["layers"]
+    # three readings of the 13.6 MB adapter, all exactly 13,631,488 bytes
+    readings = [
+        (make_desc(L, [h, h], [h, kv], 16, "bf16"), 16),          # q, v at r=16, 16-bit
+        (make_desc(L, [h, h], [h, kv], 8, "f32"), 8),             # q, v at r=8, fp32
+        (make_desc(L, [h, h, h, h], [h, kv, kv, h], 8, "bf16"), 8),  # q, k, v, o at r=8
+    ]
+    base = fig["base_gb"] * 1e9
+    for d, r in readings:
+        b = hab.adapter_bytes(d, r)
+        assert b == 13_631_488
+        assert round(b / 1e6, 1) == fig["adapter_mb"]
+        assert b / base < fig["adapter_base_ratio_max"]
+        pct = fig["adapters_loaded"] * b / base * 100
+        assert round(pct) == fig["vram_increase_pct"]          # 2.8% -> "roughly 3%"
+        assert hab.extent_bytes(d, r) == b                      # no padding at these ranks
+    # the full-stack workload's adapter: 7 projections, r=16, bf16
+    w = config(4)
+    d = make_desc(32, [p.h_in for p in w.projs], [p.h_out for p in w.projs], 16, "bf16")
+    assert hab.adapter_bytes(d, 16) == 83_886_080
+
+
+def test_extent_padding_and_alignment():
+    d = make_desc(2, [64, 128], [32, 16], 64, "bf16", rank_granule=8)
+    per_rank = 2 * 2 * (64 + 32 + 128 + 16)      # bytes per rank row over layers, projections
+    assert hab.adapter_bytes(d, 5) == 5 * per_rank
+    assert hab.extent_bytes(d, 5) == -(-8 * per_rank // 256) * 256
+    assert hab.extent_bytes(d, 65) == 0 and hab.adapter_bytes(d, 0) == 0
+    d16 = make_desc(2, [64, 128], [32, 16], 64, "bf16", rank_granule=16)
+    assert hab.extent_bytes(d16, 5) == -(-16 * per_rank // 256) * 256
+
+
+def test_pool_allocator_reuse_and_coalesce():
+    d = make_desc(1, [64], [32], 64, "bf16")
+    e8 = hab.extent_bytes(d, 8)
+    pool = _pool(slab_bytes=4 * e8)
+    for i in range(4):
+        pool.reserve(i, 8, 1.0)
+    with pytest.raises(hab.LoraError) as ei:
+        pool.reserve(9, 8, 1.0)
+    assert ei.value.status == -2                                   # ENOSPC
+    pool.unregister(1)
+    pool.unregister(2)                                             # coalesce 1+2
+    pool.reserve(10, 16, 1.0)                                      # needs 2 * e8
+    assert pool.query(10)["offset"] == e8
+    assert pool.stats() == {"adapters": 3, "free_bytes": 0}
+
+
+def test_pool_validation_leaves_state():
+    pool = _pool(max_slots=2)
+    pool.reserve(1, 8, 2.0)
+    before = pool.stats()
+    cases = [((1, 8, 1.0), -8), ((2, 0, 1.0), -4), ((2, 65, 1.0), -4), ((-3, 8, 1.0), -1)]
+    for args, code in cases:
+        with pytest.raises(hab.LoraError) as ei:
+            pool.reserve(*args)
+        assert ei.value.status == code, args
+        assert pool.stats() == before
+    pool.reserve(2, 8, 1.0)
+    with pytest.raises(hab.LoraError) as ei:
+        pool.reserve(3, 8, 1.0)
+    assert ei.value.status == -2                                   # slots full
+    with pytest.raises(hab.LoraError) as ei:
+        pool.unregister(7)
+    assert ei.value.status == -3
+    with pytest.raises(hab.LoraError) as ei:
+        pool.query(7)
+    assert ei.value.status == -3
+
+
+def test_bad_descriptors():
+    for kw, code in (({"h_in": [60]}, -1), ({"r_max": 12}, -1), ({"r_max": 128}, -1),
+                     ({"dtype": "bf16", "rank_granule": 4}, -1)):
+        with pytest.raises(hab.LoraError) as ei:
+            _pool(**kw)
+        assert ei.value.status == code, kw
+
+
+def test_segment_validation():
+    pool = _pool()
+    pool.reserve(4, 8, 1.0)
+    bad = [
+        (5, [1, 5], [4], -6),            # does not start at 0
+        (5, [0, 4], [4], -6),            # does not end at T
+        (5, [0, 3, 2, 5], [4, 4, 4], -6),  # decreasing
+        (5, [0, 5], [6], -3),            # unknown id
+        (5, [0, 5], [-2], -3),           # ids below -1
+        (-1, [0], [], -6),
+    ]
+    for T, starts, segs, code in bad:
+        with pytest.raises(hab.LoraError) as ei:
+            hab.Plan(pool, T, starts, segs)
+        assert ei.value.status == code, (T, starts, segs)
+    # empty batch, empty segments, only "no adapter" tokens: all valid
+    assert hab.Plan(pool, 0, [0], []).stats()["groups"] == 0
+    assert hab.Plan(pool, 3, [0, 0, 3, 3], [4, -1, 4]).stats() == {
+        "groups": 0, "blocks": 1, "active_tokens": 0, "max_block_tokens": 3}
+
+
+def reference_plan(T, starts, segs, ranks):
+    """Independent re-implementation of the gather: groups in order of first
+    appearance among non-empty segments, each group's tokens in segment order,
+    then every token without an adapter in ascending order."""
+    order_ids, members = [], {}
+    for s in range(len(segs)):
+        a = int(segs[s])
+        if a < 0 or starts[s + 1] == starts[s]:
+            continue
+        if a not in members:
+            order_ids.append(a)
+            members[a] = []
+        members[a].extend(range(starts[s], starts[s + 1]))
+    tok_group = np.full(T, -1, np.int32)
+    order = []
+    for g, a in enumerate(order_ids):
+        order.extend(members[a])
+        tok_group[members[a]] = g
+    order.extend(t for t in range(T) if tok_group[t] < 0)
+    return (np.asarray(order, np.int32), tok_group, np.asarray(order_ids, np.int32),
+            np.asarray([ranks[a] for a in order_ids], np.int32))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_matches_reference(seed):
+    w = random_case(seed, T=int(np.random.default_rng(seed).integers(0, 300)),
+                    h_in=64, h_out=32)
+    pool = _pool(max_slots=w.pool_size)
+    for i in range(w.pool_size):
+        pool.reserve(i, int(w.ranks[i]), float(w.scales[i]))
+    plan = hab.Plan(pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+    got = plan.export()
+    ref = reference_plan(w.num_tokens, w.seg_starts, w.seg_adapter, w.ranks)
+    for k, r in zip(("token_order", "token_group", "group_adapter", "group_rank"), ref):
+        assert np.array_equal(got[k], r), k
+    st = plan.stats()
+    assert st["active_tokens"] == int((ref[1] >= 0).sum())
+    sizes = np.bincount(ref[1][ref[1] >= 0], minlength=len(ref[2]))
+    exp_blocks = int(sum(-(-n // 64) for n in sizes)) + (-(-int((ref[1] < 0).sum()) // 64))
+    assert st["blocks"] == exp_blocks
+
+
+def test_plan_for_workloads():
+    """Groups of the five workloads' segment tables (the gather each launch does)."""
+    expect_groups = {0: None, 1: None, 2: 8, 3: None, 4: None}
+    for i in range(5):
+        w = config(i)
+        pool = hab.Pool(w.num_layers, [p.h_in for p in w.projs], [p.h_out for p in w.projs],
+                        w.r_max, w.dtype, max_slots=w.pool_size, slab_ptr=1 << 20,
+                        slab_bytes=1 << 40)
+        for a in range(w.pool_size):
+            pool.reserve(a, int(w.ranks[a]), float(w.scales[a]))
+        plan = hab.Plan(pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+        st = plan.stats()
+        assert st["groups"] == len(w.touched())
+        if expect_groups[i] is not None:
+            assert st["groups"] == expect_groups[i]
+        assert st["active_tokens"] == w.num_tokens
