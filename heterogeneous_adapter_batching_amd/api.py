@@ -68,7 +68,7 @@ def _check_dev(t, name, dtype=None, ndim=2):
         raise ValueError(f"{name} must be {ndim}-D")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if ndim == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+    if ndim == 2 and t.numel() > 0 and t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} rows must be contiguous")
 
 

@@ -80,29 +80,43 @@ __device__ __forceinline__ uint64_t extent(const BlockDesc &b) {
     return (uint64_t(b.ext_hi) << 32) | b.ext_lo;
 }
 
+// Workgroup g runs on XCD g % kXcds.  Give each XCD a contiguous range of
+// units, so units that share operands (the x chunk of one block, the partials
+// of one block) meet in one L2.
+__device__ __forceinline__ int xcd_unit(int grid) {
+    const int g = blockIdx.x;
+    return (g % kXcds) * (grid / kXcds) + g / kXcds;
+}
+
+// unit -> block: the largest b with rt_prefix[b] <= key (rt_prefix[nb] > key)
+__device__ __forceinline__ int find_block(const int32_t *rt_prefix, int nb, int key) {
+    int lo = 0, hi = nb;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (rt_prefix[mid] <= key) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // ---------------------------------------------------------------- shrink ----
 template <typename T, int TT>
 __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     constexpr int E = Elem<T>::E;        // elements per 16-byte fragment
     constexpr int SPAN = 4 * E;          // K covered by one fragment over 4 lane groups
     constexpr int UNROLL = 4;
+    __shared__ f32x4 red[kWaves][TT][kWaveSize];
+
+    const int u = xcd_unit(a.grid);
+    if (u >= a.units) return;            // whole workgroup: no barrier is skipped
     const int lane = threadIdx.x & 63;
+    const int w = wave_id();
     const int n = lane & 15, q = lane >> 4;
-    const int u = blockIdx.x * kWavesPerGroup + wave_id();
-    if (u >= a.units) return;
 
     // unit -> (block, chunk, rank tile, projection)
     const int per = a.nproj * a.c0;
-    const int key = u / per;
-    int lo = 0, hi = a.nb;               // rt_prefix[lo] <= key < rt_prefix[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.rt_prefix[mid] <= key) lo = mid; else hi = mid;
-    }
-    const int b = lo;
+    const int b = find_block(a.rt_prefix, a.nb, u / per);
     const BlockDesc blk = a.blocks[b];
-    const int ubase = a.rt_prefix[b] * per;
-    int rem = u - ubase;
+    int rem = u - a.rt_prefix[b] * per;
     const int p = rem % a.nproj;
     rem /= a.nproj;
     const int rt = rem % blk.rt;
@@ -125,8 +139,11 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     }
     const int ntiles = (blk.n_tok + kTile - 1) / kTile;   // wave-uniform
 
-    const int k_lo = c * a.kc;
-    const int k_hi = min(a.h_in, k_lo + a.kc);
+    // this wave's quarter of the chunk
+    const int kw = a.kc / kWaves;
+    const int k_chunk_end = min(a.h_in, (c + 1) * a.kc);
+    const int k_lo = c * a.kc + w * kw;
+    const int k_hi = min(k_chunk_end, k_lo + kw);
     f32x4 acc[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -153,60 +170,42 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
         }
     }
 
-    // partial tile of this unit: [token][rank], lane holds ranks 4q..4q+3 of token n
+    // sum the 4 waves in a fixed order; lane holds ranks 4q..4q+3 of token n
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) red[w][tt][lane] = acc[tt];
+    __syncthreads();
     float *pt = a.partial + size_t(u) * (TT * kTile * kTile);
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-        *reinterpret_cast<f32x4 *>(pt + (tt * kTile + n) * kTile + q * 4) = acc[tt];
+    for (int i = threadIdx.x; i < TT * kWaveSize; i += kWaves * kWaveSize) {
+        const int tt = i / kWaveSize, ln = i % kWaveSize;
+        const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
+        *reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4) = s4;
+    }
+}
 
-    // Fix-up: the last unit of (block, projection) to finish reduces all of
-    // its partials in a fixed order, so the result does not depend on timing.
-    __threadfence();
-    uint32_t prev = 0;
-    uint32_t *cnt = a.counters + b * LORA_MAX_PROJ + p;
-    if (lane == 0) prev = atomicAdd(cnt, 1u);
-    prev = __shfl(prev, 0);
-    const uint32_t total = uint32_t(blk.rt) * uint32_t(a.c0);
-    if (prev != total - 1) return;
-    __threadfence();
-
-    for (int rt2 = 0; rt2 < blk.rt; ++rt2) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            if (tt >= ntiles) continue;
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c2 = 0; c2 < a.c0; ++c2) {
-                const int u2 = ubase + (c2 * blk.rt + rt2) * a.nproj + p;
-                const float *p2 = a.partial + size_t(u2) * (TT * kTile * kTile);
-                s += __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4 *>(p2 + (tt * kTile + n) * kTile + q * 4));
-            }
-            if (tv[tt]) {
-                const int t = a.tok[blk.tok_off + tt * kTile + n];
-                float *vr = a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int col = rt2 * kTile + q * 4 + i;
-                    if (col < a.r_max) vr[col] = s[i];
-                }
+// --------------------------------------------------------------- reduce -----
+// One workgroup per (adapter block, projection): v = sum of the chunk partials.
+template <int TT>
+__global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
+    const int bp = blockIdx.x;
+    const int b = bp / a.nproj, p = bp % a.nproj;
+    const BlockDesc blk = a.blocks[b];
+    const int per = a.nproj * a.c0;
+    const int ubase = a.rt_prefix[b] * per;
+    const int quads = a.r_max / 4;
+    for (int i = threadIdx.x; i < blk.n_tok * quads; i += blockDim.x) {
+        const int ti = i / quads, j = (i % quads) * 4;
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j < blk.r_pad) {
+            const int rt = j / kTile, jj = j % kTile;
+            for (int c = 0; c < a.c0; ++c) {
+                const int u = ubase + (c * blk.rt + rt) * a.nproj + p;
+                s4 += *reinterpret_cast<const f32x4 *>(
+                    a.partial + size_t(u) * (TT * kTile * kTile) + ti * kTile + jj);
             }
         }
+        const int t = a.tok[blk.tok_off + ti];
+        *reinterpret_cast<f32x4 *>(a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j) = s4;
     }
-    // columns past the rank tiles, up to r_max, are zero
-    for (int col0 = blk.rt * kTile; col0 < a.r_max; col0 += kTile) {
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            if (tt >= ntiles || !tv[tt]) continue;
-            const int t = a.tok[blk.tok_off + tt * kTile + n];
-            float *vr = a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int col = col0 + q * 4 + i;
-                if (col < a.r_max) vr[col] = 0.f;
-            }
-        }
-    }
-    if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- expand ----
@@ -280,10 +279,14 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     constexpr int SPAN = 4 * E;                      // ranks per K-step
     constexpr int KS = (LORA_MAX_RANK + SPAN - 1) / SPAN;
     constexpr int OT = 2;                            // o-tiles per iteration
+    constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
+    __shared__ float vs[TT * kTile][VS];
+
+    const int u = xcd_unit(a.grid);
+    if (u >= a.units) return;                        // whole workgroup
     const int lane = threadIdx.x & 63;
+    const int w = wave_id();
     const int n = lane & 15, q = lane >> 4;
-    const int u = blockIdx.x * kWavesPerGroup + wave_id();
-    if (u >= a.units) return;
 
     const int upb = a.oc_prefix[a.nproj];
     const int b = u / upb;
@@ -293,8 +296,8 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     const int oc = rem - a.oc_prefix[p];
     const BlockDesc blk = a.blocks[b];
     const int h_out = a.h_out[p];
-    const int o_lo = oc * a.oc;
-    const int o_hi = min(h_out, o_lo + a.oc);
+    const int o_lo = min(h_out, (oc * kWaves + w) * a.ocw);
+    const int o_hi = min(h_out, o_lo + a.ocw);
     const int ntiles = (blk.n_tok + kTile - 1) / kTile;
     const int yoff = a.y_off[p];
 
@@ -323,8 +326,35 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
         return;
     }
 
-    // v operand per (token tile, K-step), built once per unit
-    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;   // wave-uniform
+    // v of the block's tokens into LDS, once per workgroup
+    const int quads = blk.r_pad / 4;
+    if (a.partial) {
+        const int per = a.nproj * a.c0;
+        const int ubase = a.rt_prefix[b] * per;
+        for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
+            const int ti = i / quads, j = (i % quads) * 4;
+            const int rt = j / kTile, jj = j % kTile;
+            f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < a.c0; ++c) {
+                const int uu = ubase + (c * blk.rt + rt) * a.nproj + p;
+                s4 += *reinterpret_cast<const f32x4 *>(
+                    a.partial + size_t(uu) * (TT * kTile * kTile) + ti * kTile + jj);
+            }
+            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = s4;
+        }
+    } else {
+        for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
+            const int ti = i / quads, j = (i % quads) * 4;
+            const int t = a.tok[blk.tok_off + ti];
+            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = *reinterpret_cast<const f32x4 *>(
+                a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j);
+        }
+    }
+    __syncthreads();
+    if (o_lo >= o_hi) return;
+
+    // v operand per (token tile, K-step)
+    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;  // wave-uniform
     VOperand<T> vop[TT][KS];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
@@ -333,12 +363,11 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
             float f[E];
             const int j0 = ks * SPAN + q * E;
             const bool ok = tt < ntiles && tv[tt] && ks < ks_n && j0 < blk.r_pad;
-            const float *vr = a.v + int64_t(trow[tt]) * a.ldv + int64_t(p) * a.r_max + j0;
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
-                f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (ok) w = *reinterpret_cast<const f32x4 *>(vr + e);
-                f[e] = w[0]; f[e + 1] = w[1]; f[e + 2] = w[2]; f[e + 3] = w[3];
+                f32x4 w4 = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (ok) w4 = *reinterpret_cast<const f32x4 *>(&vs[tt * kTile + n][j0 + e]);
+                f[e] = w4[0]; f[e + 1] = w4[1]; f[e + 2] = w4[2]; f[e + 3] = w4[3];
             }
             vop[tt][ks].set(f);
         }
@@ -394,7 +423,7 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
 
 template <typename T>
 hipError_t shrink_dispatch(int tt, const ShrinkArgs &a, hipStream_t s) {
-    const dim3 grid((a.units + kWavesPerGroup - 1) / kWavesPerGroup), block(256);
+    const dim3 grid(a.grid), block(kWaves * kWaveSize);
     switch (tt) {
     case 1: hipLaunchKernelGGL((k_shrink<T, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_shrink<T, 2>), grid, block, 0, s, a); break;
@@ -406,7 +435,7 @@ hipError_t shrink_dispatch(int tt, const ShrinkArgs &a, hipStream_t s) {
 
 template <typename T>
 hipError_t expand_dispatch(int tt, const ExpandArgs &a, hipStream_t s) {
-    const dim3 grid((a.units + kWavesPerGroup - 1) / kWavesPerGroup), block(256);
+    const dim3 grid(a.grid), block(kWaves * kWaveSize);
     switch (tt) {
     case 1: hipLaunchKernelGGL((k_expand<T, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_expand<T, 2>), grid, block, 0, s, a); break;
@@ -422,6 +451,18 @@ hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s) 
     if (a.units <= 0) return hipSuccess;
     return dtype == LORA_BF16 ? shrink_dispatch<uint16_t>(tt, a, s)
                               : shrink_dispatch<float>(tt, a, s);
+}
+
+hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
+    if (a.nb <= 0) return hipSuccess;
+    const dim3 grid(a.nb * a.nproj), block(kWaves * kWaveSize);
+    switch (tt) {
+    case 1: hipLaunchKernelGGL((k_reduce<1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_reduce<2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_reduce<4>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_expand(int dtype, int tt, const ExpandArgs &a, hipStream_t s) {

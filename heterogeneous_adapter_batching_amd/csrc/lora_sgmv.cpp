@@ -148,8 +148,8 @@ struct lora_plan {
     void *ws = nullptr;
     uint64_t ws_bytes = 0;
     int32_t max_proj = 0;
-    uint64_t off_tok = 0, off_blocks = 0, off_rtp = 0, off_cnt = 0, off_part = 0, off_v = 0;
-    uint64_t image_bytes = 0, part_bytes = 0, v_bytes = 0;
+    uint64_t off_tok = 0, off_blocks = 0, off_rtp = 0, off_part = 0;
+    uint64_t image_bytes = 0, part_bytes = 0;
     void *staging = nullptr;
     uint64_t staging_bytes = 0;
     hipEvent_t staged = nullptr;
@@ -158,19 +158,15 @@ struct lora_plan {
     int32_t nb_all() const { return int32_t(blocks.size()); }
 
     void layout(int32_t mp) {
-        const lora_pool_desc &d = pool->d;
         uint64_t o = 0;
         off_tok = o;     o = round_up(o + 4ull * std::max(T, 1), 256);
         off_blocks = o;  o = round_up(o + sizeof(BlockDesc) * std::max(nb_all(), 1), 256);
         off_rtp = o;     o = round_up(o + 4ull * (nb_act + 1), 256);
-        off_cnt = o;     o = round_up(o + 4ull * LORA_MAX_PROJ * std::max(nb_act, 1), 256);
         image_bytes = o;
-        // the k-chunk policy keeps units <= kTargetWaves + nproj * rt_total
-        part_bytes = 4ull * (lora::kTargetWaves + uint64_t(mp) * rt_total()) * tt *
+        // the k-chunk policy keeps shrink units <= kTargetGroups + nproj * rt_total
+        part_bytes = 4ull * (lora::kTargetGroups + uint64_t(mp) * rt_total()) * tt *
                      lora::kTile * lora::kTile;
         off_part = o;    o = round_up(o + part_bytes, 256);
-        v_bytes = 4ull * std::max(T, 1) * mp * d.r_max;
-        off_v = o;       o = round_up(o + v_bytes, 256);
         ws_bytes = o;
     }
 };
@@ -255,15 +251,27 @@ lora_status lora_pool_upload(lora_pool *p, int32_t id, int32_t layer, int32_t pr
         e = hipMemsetAsync(a_dst + uint64_t(s.rank) * h_in * es, 0,
                            uint64_t(s.r_pad - s.rank) * h_in * es, st);
         if (e != hipSuccess) return hip_fail(e, "A pad rows");
+    }
+    const uint64_t b_bytes = h_out * uint64_t(s.r_pad) * es;
+    std::vector<uint8_t> padded;   // host source with padding: widen rows on the host
+    if (s.r_pad == s.rank) {
+        e = hipMemcpyAsync(b_dst, B, b_bytes, kind, st);
+    } else if (src_on_host) {
+        padded.assign(b_bytes, 0);
+        const uint8_t *src = static_cast<const uint8_t *>(B);
+        for (uint64_t o = 0; o < h_out; ++o)
+            std::memcpy(padded.data() + o * s.r_pad * es, src + o * s.rank * es, s.rank * es);
+        e = hipMemcpyAsync(b_dst, padded.data(), b_bytes, kind, st);
+    } else {
         e = hipMemset2DAsync(b_dst + uint64_t(s.rank) * es, uint64_t(s.r_pad) * es, 0,
                              uint64_t(s.r_pad - s.rank) * es, h_out, st);
         if (e != hipSuccess) return hip_fail(e, "B pad columns");
+        e = hipMemcpy2DAsync(b_dst, uint64_t(s.r_pad) * es, B, uint64_t(s.rank) * es,
+                             uint64_t(s.rank) * es, h_out, kind, st);
     }
-    e = hipMemcpy2DAsync(b_dst, uint64_t(s.r_pad) * es, B, uint64_t(s.rank) * es,
-                         uint64_t(s.rank) * es, h_out, kind, st);
     if (e != hipSuccess) return hip_fail(e, "B upload");
     if (src_on_host) {
-        e = hipStreamSynchronize(st);   // host source must be consumed before returning
+        e = hipStreamSynchronize(st);   // host sources must be consumed before returning
         if (e != hipSuccess) return hip_fail(e, "upload synchronize");
     }
     return LORA_OK;
@@ -479,7 +487,7 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     pl->layout(max_proj);
     pl->max_proj = max_proj;
     uint8_t *img = static_cast<uint8_t *>(pl->staging);
-    std::memset(img, 0, pl->image_bytes);   // also zeroes the fix-up counters
+    std::memset(img, 0, pl->image_bytes);
     if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
     if (!pl->blocks.empty())
         std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
@@ -571,22 +579,28 @@ lora_status check_y(const lora_pool *p, int32_t nproj, const int32_t *projs, con
     return LORA_OK;
 }
 
-// k-chunking of the shrink: enough units to fill the GPU, never more than
-// kTargetWaves + nproj * rt_total (the workspace is sized for that).
+// k-chunking of the shrink: about kTargetGroups workgroups per launch, never
+// more than kTargetGroups + nproj * rt_total (the workspace is sized for that);
+// every chunk is a multiple of 4 fragment spans so the 4 waves split it evenly.
 void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
                      int32_t *kc, int32_t *c0) {
     const int64_t per_chunk = int64_t(nproj) * std::max(pl->rt_total(), 1);
-    const int32_t frags = (h_in + span - 1) / span;
-    int64_t want = (lora::kTargetWaves + per_chunk - 1) / per_chunk;
-    want = std::max<int64_t>(1, std::min<int64_t>(want, frags));
-    const int32_t fper = int32_t((frags + want - 1) / want);
-    *kc = fper * span;
+    const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
+    int64_t want = (lora::kTargetGroups + per_chunk - 1) / per_chunk;
+    want = std::max<int64_t>(1, std::min<int64_t>(want, steps));
+    const int32_t sper = int32_t((steps + want - 1) / want);
+    *kc = sper * lora::kWaves * span;
     *c0 = (h_in + *kc - 1) / *kc;
 }
 
+int32_t grid_for(int32_t units) {
+    return int32_t(round_up(uint64_t(std::max(units, 0)), lora::kXcds));
+}
+
 lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
-                       const int32_t *projs, const void *x, int64_t ldx, float *v, int64_t ldv,
-                       const CallCheck &cc, hipStream_t st) {
+                       const int32_t *projs, const void *x, int64_t ldx, const CallCheck &cc,
+                       hipStream_t st, int32_t *c0_out) {
+    *c0_out = 0;
     if (pl->nb_act == 0) return LORA_OK;
     lora::ShrinkArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
@@ -594,31 +608,52 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
     a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
-    a.counters = reinterpret_cast<uint32_t *>(const_cast<uint8_t *>(ws) + pl->off_cnt);
     a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->off_part);
     a.x = x;
-    a.v = v;
     a.ldx = ldx;
-    a.ldv = ldv;
     for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
     a.nb = pl->nb_act;
     a.nproj = nproj;
     a.h_in = cc.h_in;
     shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
     a.units = nproj * pl->rt_total() * a.c0;
-    a.r_max = p->d.r_max;
+    a.grid = grid_for(a.units);
     const uint64_t need = 4ull * uint64_t(a.units) * pl->tt * lora::kTile * lora::kTile;
     if (need > pl->part_bytes)
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
                     (unsigned long long)need, (unsigned long long)pl->part_bytes);
     hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
+    *c0_out = a.c0;
     return LORA_OK;
 }
 
+lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, int32_t c0,
+                       float *v, int64_t ldv, hipStream_t st) {
+    if (pl->nb_act == 0) return LORA_OK;
+    lora::ReduceArgs a{};
+    const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
+    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
+    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
+    a.partial = reinterpret_cast<const float *>(ws + pl->off_part);
+    a.v = v;
+    a.ldv = ldv;
+    a.nb = pl->nb_act;
+    a.nproj = nproj;
+    a.c0 = c0;
+    a.r_max = p->d.r_max;
+    hipError_t e = lora::launch_reduce(pl->tt, a, st);
+    if (e != hipSuccess) return hip_fail(e, "reduce launch");
+    return LORA_OK;
+}
+
+// v source of the expand: the shrink partials of this call (c0 > 0), or a
+// caller's v buffer
 lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
-                       const int32_t *projs, const int32_t *yoff, const float *v, int64_t ldv,
-                       void *y, int64_t ldy, const void *base, int64_t ldb, hipStream_t st) {
+                       const int32_t *projs, const int32_t *yoff, int32_t c0, const float *v,
+                       int64_t ldv, void *y, int64_t ldy, const void *base, int64_t ldb,
+                       hipStream_t st) {
     const int32_t nb = base ? pl->nb_all() : pl->nb_act;
     if (nb == 0) return LORA_OK;
     lora::ExpandArgs a{};
@@ -626,6 +661,9 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.slab = p->slab;
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
+    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
+    a.partial = c0 > 0 ? reinterpret_cast<const float *>(ws + pl->off_part) : nullptr;
+    a.c0 = c0;
     a.v = v;
     a.y = y;
     a.base = base;
@@ -639,17 +677,20 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         a.y_off[i] = yoff[i];
         rows += a.h_out[i];
     }
-    // o-chunk rows: enough units to fill the GPU, at least one 32-row pair of tiles
-    int64_t oc = (rows * nb + lora::kTargetWaves - 1) / lora::kTargetWaves;
-    oc = std::max<int64_t>(32, std::min<int64_t>(1024, round_up(uint64_t(oc), 32)));
-    a.oc = int32_t(oc);
+    // rows per wave: about kTargetGroups workgroups, 32 .. 512 rows per wave
+    int64_t ocw = (rows * nb + int64_t(lora::kTargetGroups) * lora::kWaves - 1) /
+                  (int64_t(lora::kTargetGroups) * lora::kWaves);
+    ocw = std::max<int64_t>(32, std::min<int64_t>(512, round_up(uint64_t(ocw), 32)));
+    a.ocw = int32_t(ocw);
+    const int32_t rows_per_group = a.ocw * lora::kWaves;
     a.oc_prefix[0] = 0;
     for (int i = 0; i < nproj; ++i)
-        a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + a.oc - 1) / a.oc;
+        a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
     for (int i = nproj; i < LORA_MAX_PROJ; ++i) a.oc_prefix[i + 1] = INT32_MAX;
     a.nb = nb;
     a.nproj = nproj;
     a.units = nb * a.oc_prefix[nproj];
+    a.grid = grid_for(a.units);
     a.r_max = p->d.r_max;
     hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, a, st);
     if (e != hipSuccess) return hip_fail(e, "expand launch");
@@ -673,8 +714,11 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
     if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
-    return run_shrink(p, pl, layer, nproj, projs, x, ldx, v, ldv, cc,
-                      static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t c0 = 0;
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0);
+    if (st != LORA_OK) return st;
+    return run_reduce(p, pl, nproj, c0, v, ldv, hs);
 }
 
 lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
@@ -689,7 +733,7 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
     st = check_y(p, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, v, ldv, y, ldy, nullptr, 0,
+    return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -709,12 +753,11 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         st = check_y(p, nproj, projs, yoff, base, ldb, "base", cc);
         if (st != LORA_OK) return st;
     }
-    float *v = reinterpret_cast<float *>(static_cast<uint8_t *>(pl->ws) + pl->off_v);
-    const int64_t ldv = int64_t(pl->max_proj) * p->d.r_max;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, v, ldv, cc, hs);
+    int32_t c0 = 0;
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0);
     if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, v, ldv, y, ldy, base, ldb, hs);
+    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs);
 }
 
 }  // extern "C"

@@ -11,10 +11,11 @@
 namespace lora {
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerGroup = 4;            // 256-thread workgroups of independent waves
+constexpr int kWaves = 4;                    // waves per 256-thread workgroup
 constexpr int kTile = 16;                    // MFMA tile edge (rows, tokens)
 constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 token tiles
-constexpr int kTargetWaves = 4096;           // work units aimed for per launch (16 per CU)
+constexpr int kTargetGroups = 1024;          // workgroups aimed for per launch (4 per CU)
+constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 
 // One token block of one adapter group (or of the tokens without an adapter).
 struct BlockDesc {
@@ -29,38 +30,57 @@ struct BlockDesc {
 };
 static_assert(sizeof(BlockDesc) == 32, "BlockDesc is 32 bytes");
 
-// Shrink: one wave per unit (block b, k-chunk c, rank tile rt, projection p),
-// units of one block ordered with c outermost so the waves that share an x
-// chunk are adjacent.  The last wave to finish a (block, projection) sums the
-// k-chunk partials in a fixed order and writes v.
+// Shrink: one workgroup per unit (block b, k-chunk c, rank tile rt,
+// projection i).  Units of a block are ordered with c outermost, so the units
+// that read the same x chunk are consecutive; consecutive units are placed on
+// one XCD.  The 4 waves split the chunk's K range and are summed through LDS
+// in a fixed order; the unit writes one float32 partial tile
+// [16 * TT token slots][16 ranks] at partial + unit * TT * 256.
 struct ShrinkArgs {
     const uint8_t *slab;
     const int32_t *tok;          // plan token order
     const BlockDesc *blocks;
     const int32_t *rt_prefix;    // [nb + 1] prefix sums of BlockDesc::rt
-    uint32_t *counters;          // [nb][LORA_MAX_PROJ], zero between launches
-    float *partial;              // [units][16 * TT tokens][16 ranks]
+    float *partial;
     const void *x;
-    float *v;
     int64_t ldx;
-    int64_t ldv;
     int64_t coef_a[LORA_MAX_PROJ];  // A block offset = extent + r_pad * esize * coef_a[i]
     int32_t nb;                  // adapter blocks
     int32_t nproj;
     int32_t h_in;
-    int32_t kc;                  // k-chunk length (elements, multiple of the fragment span)
+    int32_t kc;                  // k-chunk (elements, multiple of 4 fragment spans)
     int32_t c0;                  // number of k-chunks
     int32_t units;
-    int32_t r_max;               // v column stride per projection
+    int32_t grid;                // workgroups launched: units rounded up to kXcds
 };
 
-// Expand: one wave per unit (block b, projection i, o-chunk).  Reads v, streams
-// the B rows of the chunk and writes y = y_in + s * (B v), rounded once.
+// v from the shrink's partials, for the standalone shrink:
+// v[t][i * r_max + j] = sum over chunks (j < r_pad), 0 for r_pad <= j < r_max.
+struct ReduceArgs {
+    const int32_t *tok;
+    const BlockDesc *blocks;
+    const int32_t *rt_prefix;
+    const float *partial;
+    float *v;
+    int64_t ldv;
+    int32_t nb;
+    int32_t nproj;
+    int32_t c0;
+    int32_t r_max;
+};
+
+// Expand: one workgroup per unit (block b, projection i, chunk of 4 * ocw
+// output rows).  The workgroup gathers its tokens' v into LDS once (summing
+// the shrink partials in a fixed order, or reading a caller's v), then each
+// wave streams the B rows of its ocw rows and writes y = y_in + s * (B v),
+// rounded once.
 struct ExpandArgs {
     const uint8_t *slab;
     const int32_t *tok;
     const BlockDesc *blocks;
-    const float *v;
+    const int32_t *rt_prefix;
+    const float *partial;        // non-null: v = sum of partials
+    const float *v;              // else: caller's v [T][ldv]
     void *y;
     const void *base;            // nullable: y_in = base, else y_in = y
     int64_t ldv;
@@ -69,17 +89,20 @@ struct ExpandArgs {
     int64_t coef_b[LORA_MAX_PROJ];  // B block offset = extent + r_pad * esize * coef_b[i]
     int32_t h_out[LORA_MAX_PROJ];
     int32_t y_off[LORA_MAX_PROJ];
-    int32_t oc_prefix[LORA_MAX_PROJ + 1];  // o-chunks of projections before i
+    int32_t oc_prefix[LORA_MAX_PROJ + 1];  // row chunks of projections before i
     int32_t nb;                  // blocks launched over
     int32_t nproj;
-    int32_t oc;                  // rows per o-chunk (multiple of 16)
+    int32_t ocw;                 // output rows per wave (multiple of 32)
+    int32_t c0;                  // partial chunks (when partial != null)
     int32_t units;
+    int32_t grid;
     int32_t r_max;
 };
 
 // Kernel launchers (kernels.hip).  dtype is a lora_dtype; tt is the number of
 // 16-token tiles of the largest block (1, 2 or 4).
 hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s);
+hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 hipError_t launch_expand(int dtype, int tt, const ExpandArgs &a, hipStream_t s);
 
 }  // namespace lora

@@ -161,15 +161,16 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_to
                              int32_t num_segs);
 lora_status lora_plan_destroy(lora_plan *pl);   /* waits for its last upload */
 
-/* Device bytes the plan needs: its tables, per-call partial sums and the v
- * buffer of sgmv_fused, sized for calls of up to `max_proj` projections at
- * once.  0 on error. */
+/* Device bytes the plan needs: its tables and the per-call partial sums of
+ * the shrink, sized for calls of up to `max_proj` projections at once.
+ * 0 on error. */
 uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj);
 
 /* Copy the plan's tables into the caller-owned device workspace `ws`
- * (256-byte aligned, at least lora_plan_workspace_bytes(pl, max_proj)) and
- * reset its counters, on `stream`.  Every sgmv call with this plan then uses
- * `ws`; calls must be ordered after this upload on the same stream. */
+ * (256-byte aligned, at least lora_plan_workspace_bytes(pl, max_proj)), on
+ * `stream`.  Every sgmv call with this plan then uses `ws` (its tables, and
+ * scratch for the shrink's partial sums); calls must be ordered after this
+ * upload, and calls that share `ws` must not run concurrently. */
 lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
                              void *stream);
 
@@ -213,7 +214,8 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer,
 /* Fused shrink then expand: y = y_in + s_i * B_i,p (A_i,p x), with y_in = base
  * (base_out of the frozen layer, same column layout as y, [T][ldb]) when base
  * is non-NULL, else the current y.  Tokens without an adapter get y = base
- * (or are left untouched when base is NULL).  v lives in the workspace. */
+ * (or are left untouched when base is NULL).  v is never written to memory:
+ * the expand sums the shrink's partials itself. */
 lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
                        int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
                        const void *x, int64_t ldx, const void *base, int64_t ldb,
