@@ -125,6 +125,8 @@ def main():
                     help="layers of the CPU-oracle sample (-1: all, 0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=5,
                     help="event-timed passes for the per-kernel roofline")
+    ap.add_argument("--copy-mib", type=int, default=2048,
+                    help="size of the device-copy bandwidth reference (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -252,6 +254,25 @@ def main():
             "alg_bytes_per_launch": int(kern[dom]["alg_bytes_per_launch"])}
     log(f"[bench] kernels: {json.dumps(kern)}")
 
+    # device copy bandwidth: a second, measured denominator
+    copy_gbs = None
+    if args.copy_mib > 0:
+        nel = args.copy_mib * (1 << 20) // 2
+        src = torch.empty(nel, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for _ in range(5):
+                dst.copy_(src)
+            c1.record(stream)
+            torch.cuda.synchronize()
+        copy_gbs = 2 * nel * 2 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
+        log(f"[bench] device copy of {args.copy_mib} MiB: {copy_gbs:.1f} GB/s (read + write)")
+
     cpu = None
     if args.cpu_layers != 0 and keep:
         cpu = cpu_baseline(w, keep, cpu_layers, threads)
@@ -275,6 +296,7 @@ def main():
         "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"],
         "eager_ms_per_step": round(eager_ms, 5),
         "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},
+        "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

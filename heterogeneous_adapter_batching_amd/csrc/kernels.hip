@@ -6,7 +6,13 @@
 // bound by HBM: a decode group streams its adapter's A and B rows once, a
 // prefill group streams its token rows.  MFMA is used so that the arithmetic
 // costs nothing next to the loads for any group size, not to reach a matrix
-// throughput; the loads are 16-byte per lane and each wave streams whole rows.
+// throughput.
+//
+// Memory access: every global access is a buffer load or store through a
+// wave-uniform resource whose size bounds the access; masked lanes use an
+// out-of-range offset, which returns zero (loads) or is dropped (stores) by
+// the hardware without touching memory.  So no load sits behind a branch,
+// and each wave issues all of its streaming loads before it waits for any.
 //
 // MFMA operand layout used throughout (16x16 output tile): lane l = 16 q + n
 // holds row n of the left operand and column n of the right operand for the
@@ -29,18 +35,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int E = 8; };   // bf16 bit patterns
 template <> struct Elem<float> { static constexpr int E = 4; };
 
-__device__ __forceinline__ u32x4 ld16(const void *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
+// Buffer resources: raw (stride 0) with the byte size as the range.
+constexpr uint32_t kOOB = 0x80000000u;        // offset of a masked lane: out of range
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNT = 2;                        // non-temporal: streamed once
 
-__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
-    // adapter rows are read once per launch: do not keep them in the caches
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes),
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t off_or_oob(bool ok, uint32_t off) { return ok ? off : kOOB; }
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+}
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kNT);
 }
 
 // float -> bf16 bits, round to nearest even; NaN stays NaN.
@@ -76,8 +92,8 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-__device__ __forceinline__ uint64_t extent(const BlockDesc &b) {
-    return (uint64_t(b.ext_hi) << 32) | b.ext_lo;
+__device__ __forceinline__ uint64_t extent(uint32_t lo, uint32_t hi) {
+    return (uint64_t(hi) << 32) | lo;
 }
 
 // Workgroup g runs on XCD g % kXcds.  Give each XCD a contiguous range of
@@ -88,22 +104,12 @@ __device__ __forceinline__ int xcd_unit(int grid) {
     return (g % kXcds) * (grid / kXcds) + g / kXcds;
 }
 
-// unit -> block: the largest b with rt_prefix[b] <= key (rt_prefix[nb] > key)
-__device__ __forceinline__ int find_block(const int32_t *rt_prefix, int nb, int key) {
-    int lo = 0, hi = nb;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (rt_prefix[mid] <= key) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 // ---------------------------------------------------------------- shrink ----
 template <typename T, int TT>
 __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     constexpr int E = Elem<T>::E;        // elements per 16-byte fragment
     constexpr int SPAN = 4 * E;          // K covered by one fragment over 4 lane groups
-    constexpr int UNROLL = 4;
+    constexpr int F = shrink_frags<TT>();
     __shared__ f32x4 red[kWaves][TT][kWaveSize];
 
     const int u = xcd_unit(a.grid);
@@ -112,62 +118,62 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     const int w = wave_id();
     const int n = lane & 15, q = lane >> 4;
 
-    // unit -> (block, chunk, rank tile, projection)
+    // unit -> (rank tile, chunk, projection): the descriptor and the token
+    // rows of the tile load in parallel
     const int per = a.nproj * a.c0;
-    const int b = find_block(a.rt_prefix, a.nb, u / per);
-    const BlockDesc blk = a.blocks[b];
-    int rem = u - a.rt_prefix[b] * per;
-    const int p = rem % a.nproj;
-    rem /= a.nproj;
-    const int rt = rem % blk.rt;
-    const int c = rem / blk.rt;
+    const int key = u / per;
+    int trow[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) trow[tt] = a.tile_tok[key * kMaxBlockTokens + tt * kTile + n];
+    const TileDesc td = a.tiles[key];
+    const int rem = u - key * per;
+    const int c = rem / a.nproj, p = rem - (rem / a.nproj) * a.nproj;
 
-    // operands: rank row j of A (left), token rows (right)
-    const T *ablk = reinterpret_cast<const T *>(
-        a.slab + extent(blk) + uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]));
-    const int j = rt * kTile + n;
-    const bool jv = j < blk.r_pad;
-    const T *arow = ablk + int64_t(jv ? j : 0) * a.h_in;
-    const T *xrow[TT];
-    bool tv[TT];
+    // this wave's quarter of the chunk: at most F fragments
+    const int kw = a.kc / kWaves;
+    const int k_lo = c * a.kc + w * kw;
+    const int k_hi = min(min(a.h_in, (c + 1) * a.kc), k_lo + kw);
+
+    // A rows first: they depend on nothing but the descriptor
+    const rsrc_t ar = make_rsrc(
+        a.slab + extent(td.ext_lo, td.ext_hi) +
+            uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
+        uint32_t(td.r_pad) * uint32_t(a.h_in) * sizeof(T));
+    const int j = td.tile * kTile + n;
+    const bool jv = j < td.r_pad;
+    u32x4 af[F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const int k = k_lo + f * SPAN + q * E;
+        af[f] = bload16_nt(ar, off_or_oob(jv && k < k_hi,
+                                          (uint32_t(j) * uint32_t(a.h_in) + k) * sizeof(T)));
+    }
+
+    // then the token rows
+    const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const int ntiles = (td.n_tok + kTile - 1) / kTile;   // wave-uniform
+    u32x4 xf[TT][F];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-        const int ti = tt * kTile + n;
-        tv[tt] = ti < blk.n_tok;
-        const int t = tv[tt] ? a.tok[blk.tok_off + ti] : 0;
-        xrow[tt] = reinterpret_cast<const T *>(a.x) + int64_t(t) * a.ldx;
+        const int t = trow[tt];
+        const bool tv = tt < ntiles && t >= 0;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int k = k_lo + f * SPAN + q * E;
+            xf[tt][f] = bload16(xr, off_or_oob(tv && k < k_hi,
+                                               uint32_t(int64_t(t) * a.ldx + k) * sizeof(T)));
+        }
     }
-    const int ntiles = (blk.n_tok + kTile - 1) / kTile;   // wave-uniform
 
-    // this wave's quarter of the chunk
-    const int kw = a.kc / kWaves;
-    const int k_chunk_end = min(a.h_in, (c + 1) * a.kc);
-    const int k_lo = c * a.kc + w * kw;
-    const int k_hi = min(k_chunk_end, k_lo + kw);
     f32x4 acc[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb = k_lo; kb < k_hi; kb += SPAN * UNROLL) {
-        u32x4 af[UNROLL], xf[TT][UNROLL];
 #pragma unroll
-        for (int f = 0; f < UNROLL; ++f) {
-            const int k = kb + f * SPAN + q * E;
-            const bool kv = k < k_hi;
-            af[f] = u32x4{0u, 0u, 0u, 0u};
-            if (jv && kv) af[f] = ld16_stream(arow + k);
+    for (int f = 0; f < F; ++f) {
+        if (k_lo + f * SPAN >= k_hi) break;              // wave-uniform
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                xf[tt][f] = u32x4{0u, 0u, 0u, 0u};
-                if (tt < ntiles && tv[tt] && kv) xf[tt][f] = ld16(xrow[tt] + k);
-            }
-        }
-#pragma unroll
-        for (int f = 0; f < UNROLL; ++f) {
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                if (tt < ntiles) acc[tt] = mma<T>(af[f], xf[tt][f], acc[tt]);
-        }
+        for (int tt = 0; tt < TT; ++tt)
+            if (tt < ntiles) acc[tt] = mma<T>(af[f], xf[tt][f], acc[tt]);
     }
 
     // sum the 4 waves in a fixed order; lane holds ranks 4q..4q+3 of token n
@@ -182,6 +188,14 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     }
 }
 
+// partial tile of (rank tile, chunk, projection) for an adapter block
+__device__ __forceinline__ const float *partial_tile(const float *partial, int tt_tiles,
+                                                     int rt_before, int tile, int c, int p,
+                                                     int nproj, int c0) {
+    const int u = (rt_before + tile) * nproj * c0 + c * nproj + p;
+    return partial + size_t(u) * (tt_tiles * kTile * kTile);
+}
+
 // --------------------------------------------------------------- reduce -----
 // One workgroup per (adapter block, projection): v = sum of the chunk partials.
 template <int TT>
@@ -189,19 +203,15 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
     const int bp = blockIdx.x;
     const int b = bp / a.nproj, p = bp % a.nproj;
     const BlockDesc blk = a.blocks[b];
-    const int per = a.nproj * a.c0;
-    const int ubase = a.rt_prefix[b] * per;
     const int quads = a.r_max / 4;
     for (int i = threadIdx.x; i < blk.n_tok * quads; i += blockDim.x) {
         const int ti = i / quads, j = (i % quads) * 4;
         f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
         if (j < blk.r_pad) {
-            const int rt = j / kTile, jj = j % kTile;
-            for (int c = 0; c < a.c0; ++c) {
-                const int u = ubase + (c * blk.rt + rt) * a.nproj + p;
+            for (int c = 0; c < a.c0; ++c)
                 s4 += *reinterpret_cast<const f32x4 *>(
-                    a.partial + size_t(u) * (TT * kTile * kTile) + ti * kTile + jj);
-            }
+                    partial_tile(a.partial, TT, blk.rt_before, j / kTile, c, p, a.nproj, a.c0) +
+                    ti * kTile + j % kTile);
         }
         const int t = a.tok[blk.tok_off + ti];
         *reinterpret_cast<f32x4 *>(a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j) = s4;
@@ -244,41 +254,48 @@ template <> struct VOperand<float> {
     }
 };
 
-template <typename T> struct OutVec;
-template <> struct OutVec<uint16_t> {   // 4 bf16 = 8 bytes
-    static __device__ __forceinline__ void load(const void *p, float (&o)[4]) {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+// 4 consecutive outputs of one token: bf16 (8 bytes) or float32 (16 bytes)
+template <typename T> struct Out4;
+template <> struct Out4<uint16_t> {
+    typedef u32x2 raw;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0);
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, raw v) {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, 0);
+    }
+    static __device__ __forceinline__ void unpack(raw w, float (&o)[4]) {
         o[0] = __uint_as_float(w[0] << 16); o[1] = __uint_as_float(w[0] & 0xffff0000u);
         o[2] = __uint_as_float(w[1] << 16); o[3] = __uint_as_float(w[1] & 0xffff0000u);
     }
-    static __device__ __forceinline__ void store(void *p, const float (&o)[4]) {
-        const u32x2 w = u32x2{bf16_rne(o[0]) | (bf16_rne(o[1]) << 16),
-                              bf16_rne(o[2]) | (bf16_rne(o[3]) << 16)};
-        *reinterpret_cast<u32x2 *>(p) = w;
-    }
-    static __device__ __forceinline__ void copy(const void *src, void *dst) {
-        *reinterpret_cast<u32x2 *>(dst) = *reinterpret_cast<const u32x2 *>(src);
+    static __device__ __forceinline__ raw pack(const float (&o)[4]) {
+        return u32x2{bf16_rne(o[0]) | (bf16_rne(o[1]) << 16),
+                     bf16_rne(o[2]) | (bf16_rne(o[3]) << 16)};
     }
 };
-template <> struct OutVec<float> {      // 4 float = 16 bytes
-    static __device__ __forceinline__ void load(const void *p, float (&o)[4]) {
-        const f32x4 w = *reinterpret_cast<const f32x4 *>(p);
-        o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3];
+template <> struct Out4<float> {
+    typedef u32x4 raw;
+    static __device__ __forceinline__ raw load(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
     }
-    static __device__ __forceinline__ void store(void *p, const float (&o)[4]) {
-        *reinterpret_cast<f32x4 *>(p) = f32x4{o[0], o[1], o[2], o[3]};
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, raw v) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, 0);
     }
-    static __device__ __forceinline__ void copy(const void *src, void *dst) {
-        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+    static __device__ __forceinline__ void unpack(raw w, float (&o)[4]) {
+        o[0] = __uint_as_float(w[0]); o[1] = __uint_as_float(w[1]);
+        o[2] = __uint_as_float(w[2]); o[3] = __uint_as_float(w[3]);
+    }
+    static __device__ __forceinline__ raw pack(const float (&o)[4]) {
+        return u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                     __float_as_uint(o[3])};
     }
 };
 
-template <typename T, int TT>
+template <typename T, int TT, int KSM>
 __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int SPAN = 4 * E;                      // ranks per K-step
-    constexpr int KS = (LORA_MAX_RANK + SPAN - 1) / SPAN;
-    constexpr int OT = 2;                            // o-tiles per iteration
+    constexpr int OTW = expand_tiles(KSM);           // 16-row tiles per wave
     constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
     __shared__ float vs[TT * kTile][VS];
 
@@ -294,51 +311,89 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     int p = 0;
     while (rem >= a.oc_prefix[p + 1]) ++p;
     const int oc = rem - a.oc_prefix[p];
+    int trow[TT];                                    // token rows, -1 padded
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) trow[tt] = a.block_tok[b * kMaxBlockTokens + tt * kTile + n];
     const BlockDesc blk = a.blocks[b];
     const int h_out = a.h_out[p];
-    const int o_lo = min(h_out, (oc * kWaves + w) * a.ocw);
-    const int o_hi = min(h_out, o_lo + a.ocw);
-    const int ntiles = (blk.n_tok + kTile - 1) / kTile;
+    const int o_lo = min(h_out, (oc * kWaves + w) * (OTW * kTile));
+    const int o_hi = min(h_out, o_lo + OTW * kTile);
     const int yoff = a.y_off[p];
+    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;  // wave-uniform, <= KSM
 
-    int trow[TT];
+    // B rows of this wave first: they depend on nothing but the descriptor
+    const rsrc_t br = make_rsrc(
+        a.slab + extent(blk.ext_lo, blk.ext_hi) +
+            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
+        uint32_t(h_out) * uint32_t(blk.r_pad) * sizeof(T));
+    u32x4 bf[OTW][KSM];
+#pragma unroll
+    for (int ot = 0; ot < OTW; ++ot) {
+        const int orow = o_lo + ot * kTile + n;
+#pragma unroll
+        for (int ks = 0; ks < KSM; ++ks) {
+            const int j0 = ks * SPAN + q * E;
+            bf[ot][ks] = bload16_nt(br, off_or_oob(ks < ks_n && orow < o_hi && j0 < blk.r_pad,
+                                                   uint32_t(orow * blk.r_pad + j0) * sizeof(T)));
+        }
+    }
+
+    // then y_in (base, or y itself) of every output tile
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
+    const int64_t ld_in = a.base ? a.ldb : a.ldy;
+    const int ntiles = (blk.n_tok + kTile - 1) / kTile;
     bool tv[TT];
+    typename Out4<T>::raw yin[OTW][TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
-        const int ti = tt * kTile + n;
-        tv[tt] = ti < blk.n_tok;
-        trow[tt] = tv[tt] ? a.tok[blk.tok_off + ti] : 0;
+        tv[tt] = tt < ntiles && trow[tt] >= 0;
+#pragma unroll
+        for (int ot = 0; ot < OTW; ++ot) {
+            const int o = o_lo + ot * kTile + 4 * q;
+            yin[ot][tt] = Out4<T>::load(
+                inr, off_or_oob(tv[tt] && o < o_hi,
+                                uint32_t(int64_t(trow[tt]) * ld_in + yoff + o) * sizeof(T)));
+        }
     }
-    T *y = reinterpret_cast<T *>(a.y);
-    const T *base = reinterpret_cast<const T *>(a.base);
 
     if (blk.r_pad == 0) {            // tokens without an adapter: y = base
-        if (!base) return;
-        for (int o0 = o_lo; o0 < o_hi; o0 += kTile) {
-            const int o = o0 + 4 * q;
+        if (!a.base) return;
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt < ntiles && tv[tt] && o < o_hi)
-                    OutVec<T>::copy(base + int64_t(trow[tt]) * a.ldb + yoff + o,
-                                    y + int64_t(trow[tt]) * a.ldy + yoff + o);
+        for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+            for (int ot = 0; ot < OTW; ++ot) {
+                const int o = o_lo + ot * kTile + 4 * q;
+                Out4<T>::store(yr, off_or_oob(tv[tt] && o < o_hi,
+                                              uint32_t(int64_t(trow[tt]) * a.ldy + yoff + o) *
+                                                  sizeof(T)),
+                               yin[ot][tt]);
             }
         }
         return;
     }
 
-    // v of the block's tokens into LDS, once per workgroup
+    // v of the block's tokens into LDS, once per workgroup: the chunk partials
+    // of each (token, 4 ranks) are loaded 8 at a time, then summed in order
     const int quads = blk.r_pad / 4;
     if (a.partial) {
-        const int per = a.nproj * a.c0;
-        const int ubase = a.rt_prefix[b] * per;
+        const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
+        constexpr int G = 8;
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
             const int ti = i / quads, j = (i % quads) * 4;
-            const int rt = j / kTile, jj = j % kTile;
+            const uint32_t base_f = uint32_t((blk.rt_before + j / kTile) * a.nproj * a.c0 + p) *
+                                        (TT * kTile * kTile) + ti * kTile + j % kTile;
+            const uint32_t stride_f = uint32_t(a.nproj) * (TT * kTile * kTile);
             f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c = 0; c < a.c0; ++c) {
-                const int uu = ubase + (c * blk.rt + rt) * a.nproj + p;
-                s4 += *reinterpret_cast<const f32x4 *>(
-                    a.partial + size_t(uu) * (TT * kTile * kTile) + ti * kTile + jj);
+            for (int c0 = 0; c0 < a.c0; c0 += G) {
+                u32x4 part[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    part[g] = bload16(pr, off_or_oob(c0 + g < a.c0,
+                                                     (base_f + uint32_t(c0 + g) * stride_f) * 4));
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if (c0 + g < a.c0) s4 += __builtin_bit_cast(f32x4, part[g]);
             }
             *reinterpret_cast<f32x4 *>(&vs[ti][j]) = s4;
         }
@@ -354,69 +409,51 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     if (o_lo >= o_hi) return;
 
     // v operand per (token tile, K-step)
-    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;  // wave-uniform
-    VOperand<T> vop[TT][KS];
+    VOperand<T> vop[TT][KSM];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KSM; ++ks) {
             float f[E];
             const int j0 = ks * SPAN + q * E;
-            const bool ok = tt < ntiles && tv[tt] && ks < ks_n && j0 < blk.r_pad;
+            const bool ok = tv[tt] && ks < ks_n && j0 < blk.r_pad;
+            const int row = ok ? tt * kTile + n : 0;
+            const int col = ok ? j0 : 0;
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
-                f32x4 w4 = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (ok) w4 = *reinterpret_cast<const f32x4 *>(&vs[tt * kTile + n][j0 + e]);
-                f[e] = w4[0]; f[e + 1] = w4[1]; f[e + 2] = w4[2]; f[e + 3] = w4[3];
+                const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[row][col + e]);
+                f[e] = ok ? w4[0] : 0.f; f[e + 1] = ok ? w4[1] : 0.f;
+                f[e + 2] = ok ? w4[2] : 0.f; f[e + 3] = ok ? w4[3] : 0.f;
             }
             vop[tt][ks].set(f);
         }
     }
 
-    const T *bblk = reinterpret_cast<const T *>(
-        a.slab + extent(blk) + uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]));
     const float s = blk.scale;
-
-    for (int o0 = o_lo; o0 < o_hi; o0 += kTile * OT) {
-        u32x4 bf[OT][KS];
 #pragma unroll
-        for (int ot = 0; ot < OT; ++ot) {
-            const int orow = o0 + ot * kTile + n;
+    for (int ot = 0; ot < OTW; ++ot) {
+        const int obase = o_lo + ot * kTile;
+        if (obase >= o_hi) break;                    // wave-uniform
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int j0 = ks * SPAN + q * E;
-                bf[ot][ks] = u32x4{0u, 0u, 0u, 0u};
-                if (ks < ks_n && orow < o_hi && j0 < blk.r_pad)
-                    bf[ot][ks] = ld16_stream(bblk + int64_t(orow) * blk.r_pad + j0);
+        for (int tt = 0; tt < TT; ++tt) {
+            if (tt >= ntiles) continue;              // wave-uniform
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSM; ++ks) {
+                if (ks >= ks_n) continue;
+#pragma unroll
+                for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
+                    acc = mma<T>(bf[ot][ks], vop[tt][ks].piece[pc], acc);
             }
-        }
+            const int o = obase + 4 * q;             // 4 consecutive outputs of token n
+            float in[4], out[4];
+            Out4<T>::unpack(yin[ot][tt], in);
 #pragma unroll
-        for (int ot = 0; ot < OT; ++ot) {
-            const int obase = o0 + ot * kTile;
-            if (obase >= o_hi) break;
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt >= ntiles) continue;
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if (ks >= ks_n) continue;
-#pragma unroll
-                    for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
-                        acc = mma<T>(bf[ot][ks], vop[tt][ks].piece[pc], acc);
-                }
-                const int o = obase + 4 * q;     // 4 consecutive outputs of token n
-                if (tv[tt] && o < o_hi) {
-                    T *yp = y + int64_t(trow[tt]) * a.ldy + yoff + o;
-                    float in[4];
-                    if (base) OutVec<T>::load(base + int64_t(trow[tt]) * a.ldb + yoff + o, in);
-                    else OutVec<T>::load(yp, in);
-                    float out[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) out[i] = in[i] + s * acc[i];
-                    OutVec<T>::store(yp, out);
-                }
-            }
+            for (int i = 0; i < 4; ++i) out[i] = in[i] + s * acc[i];
+            Out4<T>::store(yr, off_or_oob(tv[tt] && o < o_hi,
+                                          uint32_t(int64_t(trow[tt]) * a.ldy + yoff + o) *
+                                              sizeof(T)),
+                           Out4<T>::pack(out));
         }
     }
 }
@@ -433,13 +470,13 @@ hipError_t shrink_dispatch(int tt, const ShrinkArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t expand_dispatch(int tt, const ExpandArgs &a, hipStream_t s) {
+template <typename T, int KSM>
+hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, hipStream_t s) {
     const dim3 grid(a.grid), block(kWaves * kWaveSize);
     switch (tt) {
-    case 1: hipLaunchKernelGGL((k_expand<T, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_expand<T, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_expand<T, 4>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_expand<T, 1, KSM>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_expand<T, 2, KSM>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_expand<T, 4, KSM>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -465,10 +502,17 @@ hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_expand(int dtype, int tt, const ExpandArgs &a, hipStream_t s) {
+hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
-    return dtype == LORA_BF16 ? expand_dispatch<uint16_t>(tt, a, s)
-                              : expand_dispatch<float>(tt, a, s);
+    if (dtype == LORA_BF16) {
+        if (ks == 1) return expand_dispatch_ks<uint16_t, 1>(tt, a, s);
+        if (ks == 2) return expand_dispatch_ks<uint16_t, 2>(tt, a, s);
+        return hipErrorInvalidValue;
+    }
+    if (ks == 1) return expand_dispatch_ks<float, 1>(tt, a, s);
+    if (ks == 2) return expand_dispatch_ks<float, 2>(tt, a, s);
+    if (ks == 4) return expand_dispatch_ks<float, 4>(tt, a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace lora

@@ -141,33 +141,53 @@ struct lora_plan {
     std::vector<int32_t> token_group;    // per token row
     std::vector<int32_t> group_adapter, group_rank;
     std::vector<BlockDesc> blocks;       // adapter blocks [0, nb_act), no-adapter blocks after
-    std::vector<int32_t> rt_prefix;      // over adapter blocks
-    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1;
+    std::vector<lora::TileDesc> tiles;   // rank tiles of the adapter blocks, in block order
+    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0;
 
     // device image in the caller's workspace
     void *ws = nullptr;
     uint64_t ws_bytes = 0;
     int32_t max_proj = 0;
-    uint64_t off_tok = 0, off_blocks = 0, off_rtp = 0, off_part = 0;
+    uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_part = 0;
     uint64_t image_bytes = 0, part_bytes = 0;
     void *staging = nullptr;
     uint64_t staging_bytes = 0;
     hipEvent_t staged = nullptr;
 
-    int32_t rt_total() const { return rt_prefix.empty() ? 0 : rt_prefix.back(); }
+    int32_t rt_total() const { return int32_t(tiles.size()); }
     int32_t nb_all() const { return int32_t(blocks.size()); }
 
     void layout(int32_t mp) {
         uint64_t o = 0;
         off_tok = o;     o = round_up(o + 4ull * std::max(T, 1), 256);
         off_blocks = o;  o = round_up(o + sizeof(BlockDesc) * std::max(nb_all(), 1), 256);
-        off_rtp = o;     o = round_up(o + 4ull * (nb_act + 1), 256);
+        off_tiles = o;   o = round_up(o + sizeof(lora::TileDesc) * std::max(rt_total(), 1), 256);
+        off_btok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(nb_all(), 1), 256);
+        off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(rt_total(), 1), 256);
         image_bytes = o;
-        // the k-chunk policy keeps shrink units <= kTargetGroups + nproj * rt_total
-        part_bytes = 4ull * (lora::kTargetGroups + uint64_t(mp) * rt_total()) * tt *
-                     lora::kTile * lora::kTile;
+        part_bytes = 4ull * max_shrink_units(mp) * tt * lora::kTile * lora::kTile;
         off_part = o;    o = round_up(o + part_bytes, 256);
         ws_bytes = o;
+    }
+
+    // Largest shrink launch (workgroups) of a call of up to mp projections
+    // under shrink_geometry: per_chunk * max(ceil(target / per_chunk),
+    // ceil(steps / frags)), where steps = fragments of 4 waves over h_in.
+    uint64_t max_shrink_units(int32_t mp) const {
+        const lora_pool_desc &d = pool->d;
+        const uint64_t span = 4ull * (16 / esize(d.dtype));
+        int32_t h_in_max = 0;
+        for (int i = 0; i < d.num_proj; ++i) h_in_max = std::max(h_in_max, d.h_in[i]);
+        const uint64_t steps = (h_in_max + lora::kWaves * span - 1) / (lora::kWaves * span);
+        const uint64_t frags = tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
+        const uint64_t by_frags = (steps + frags - 1) / frags;
+        uint64_t most = 0;
+        for (int32_t np = 1; np <= mp; ++np) {
+            const uint64_t per_chunk = uint64_t(np) * std::max(rt_total(), 1);
+            const uint64_t by_target = (lora::kTargetGroups + per_chunk - 1) / per_chunk;
+            most = std::max(most, per_chunk * std::max(by_target, by_frags));
+        }
+        return most;
     }
 };
 
@@ -391,10 +411,15 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
     for (int32_t t = 0; t < T; ++t)
         if (pl->token_group[t] < 0) idle.push_back(t);
 
-    // blocks: each group cut into near-equal blocks of at most kMaxBlockTokens
+    // blocks: each group cut into near-equal blocks of at most `bmax` tokens:
+    // 16 (one token tile) unless a group is long enough to be prefill-like
+    size_t longest = 0;
+    for (auto &m : members) longest = std::max(longest, m.size());
+    const int32_t bmax = longest >= size_t(lora::kLongGroup) ? lora::kMaxBlockTokens
+                                                             : lora::kDecodeBlockTokens;
     auto add_blocks = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
         const int32_t n = int32_t(toks.size());
-        const int32_t nblk = (n + lora::kMaxBlockTokens - 1) / lora::kMaxBlockTokens;
+        const int32_t nblk = (n + bmax - 1) / bmax;
         int32_t start = 0;
         for (int32_t i = 0; i < nblk; ++i) {
             const int32_t cnt = n / nblk + (i < n % nblk ? 1 : 0);
@@ -404,7 +429,8 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
             bd.r_pad = sl ? sl->r_pad : 0;
             bd.rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
             bd.scale = sl ? sl->scale : 0.f;
-            bd.group = g;
+            bd.rt_before = 0;
+            (void)g;
             bd.ext_lo = sl ? uint32_t(sl->off & 0xffffffffu) : 0u;
             bd.ext_hi = sl ? uint32_t(sl->off >> 32) : 0u;
             pl->blocks.push_back(bd);
@@ -419,9 +445,22 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
     pl->n_active = int32_t(pl->token_order.size());
     add_blocks(idle, -1, nullptr);
 
-    pl->rt_prefix.assign(pl->nb_act + 1, 0);
-    for (int32_t b = 0; b < pl->nb_act; ++b)
-        pl->rt_prefix[b + 1] = pl->rt_prefix[b] + pl->blocks[b].rt;
+    for (int32_t b = 0; b < pl->nb_act; ++b) {
+        BlockDesc &bd = pl->blocks[b];
+        bd.rt_before = int32_t(pl->tiles.size());
+        pl->max_rpad = std::max(pl->max_rpad, bd.r_pad);
+        for (int32_t i = 0; i < bd.rt; ++i) {
+            lora::TileDesc td{};
+            td.tok_off = bd.tok_off;
+            td.n_tok = bd.n_tok;
+            td.r_pad = bd.r_pad;
+            td.tile = i;
+            td.block = b;
+            td.ext_lo = bd.ext_lo;
+            td.ext_hi = bd.ext_hi;
+            pl->tiles.push_back(td);
+        }
+    }
     const int32_t tiles = (pl->max_block + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
     *out = pl;
@@ -445,7 +484,7 @@ uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj) {
     tmp.pool = pl->pool;
     tmp.T = pl->T;
     tmp.blocks = pl->blocks;
-    tmp.rt_prefix = pl->rt_prefix;
+    tmp.tiles = pl->tiles;
     tmp.nb_act = pl->nb_act;
     tmp.tt = pl->tt;
     tmp.layout(max_proj);
@@ -470,7 +509,7 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     }
     lora_plan probe = lora_plan();   // layout of the new image
     probe.pool = pl->pool; probe.T = pl->T; probe.blocks = pl->blocks;
-    probe.rt_prefix = pl->rt_prefix; probe.nb_act = pl->nb_act; probe.tt = pl->tt;
+    probe.tiles = pl->tiles; probe.nb_act = pl->nb_act; probe.tt = pl->tt;
     probe.layout(max_proj);
     if (pl->staging_bytes < probe.image_bytes) {
         void *buf = nullptr;
@@ -491,7 +530,22 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
     if (!pl->blocks.empty())
         std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
-    std::memcpy(img + pl->off_rtp, pl->rt_prefix.data(), 4ull * pl->rt_prefix.size());
+    if (!pl->tiles.empty())
+        std::memcpy(img + pl->off_tiles, pl->tiles.data(), sizeof(lora::TileDesc) * pl->tiles.size());
+    {   // token rows of each block and of each rank tile, -1 padded
+        int32_t *bt = reinterpret_cast<int32_t *>(img + pl->off_btok);
+        for (int32_t b = 0; b < pl->nb_all(); ++b) {
+            const BlockDesc &bd = pl->blocks[b];
+            for (int32_t i = 0; i < lora::kMaxBlockTokens; ++i)
+                bt[b * lora::kMaxBlockTokens + i] =
+                    i < bd.n_tok ? pl->token_order[bd.tok_off + i] : -1;
+        }
+        int32_t *tt = reinterpret_cast<int32_t *>(img + pl->off_ttok);
+        for (int32_t k = 0; k < pl->rt_total(); ++k)
+            std::memcpy(tt + k * lora::kMaxBlockTokens,
+                        bt + pl->tiles[k].block * lora::kMaxBlockTokens,
+                        4ull * lora::kMaxBlockTokens);
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     e = hipMemcpyAsync(ws, img, pl->image_bytes, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "plan upload");
@@ -529,6 +583,12 @@ namespace {
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
+// bytes spanned by T rows of width `width` at leading dimension ld
+uint64_t tensor_bytes(int32_t T, int64_t ld, int64_t width, int32_t es) {
+    if (T <= 0) return 0;
+    return (uint64_t(T - 1) * uint64_t(ld) + uint64_t(width)) * uint64_t(es);
+}
+
 struct CallCheck {
     int32_t h_in = 0;
     int32_t es = 0;
@@ -562,13 +622,16 @@ lora_status check_call(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     return LORA_OK;
 }
 
-lora_status check_y(const lora_pool *p, int32_t nproj, const int32_t *projs, const int32_t *yoff,
-                    const void *y, int64_t ldy, const char *name, const CallCheck &cc) {
+lora_status check_y(const lora_pool *p, int32_t T, int32_t nproj, const int32_t *projs,
+                    const int32_t *yoff, const void *y, int64_t ldy, const char *name,
+                    const CallCheck &cc) {
     if (!yoff) return fail(LORA_EINVAL, "null y_offsets");
     if (!y || !aligned16(y)) return fail(LORA_EINVAL, "%s must be non-null and 16-byte aligned", name);
     if (ldy < 1 || ldy % 8 || ldy % cc.vec)
         return fail(LORA_EINVAL, "ld of %s (%lld) must be a positive multiple of 8", name,
                     (long long)ldy);
+    if (tensor_bytes(T, ldy, ldy, cc.es) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "%s spans more than 2 GiB", name);
     for (int i = 0; i < nproj; ++i) {
         if (yoff[i] < 0 || yoff[i] % 8)
             return fail(LORA_EINVAL, "y_offsets[%d] = %d must be a non-negative multiple of 8", i,
@@ -579,16 +642,17 @@ lora_status check_y(const lora_pool *p, int32_t nproj, const int32_t *projs, con
     return LORA_OK;
 }
 
-// k-chunking of the shrink: about kTargetGroups workgroups per launch, never
-// more than kTargetGroups + nproj * rt_total (the workspace is sized for that);
-// every chunk is a multiple of 4 fragment spans so the 4 waves split it evenly.
+// k-chunking of the shrink: about kTargetGroups workgroups per launch, each
+// wave loading at most `frags` fragments (all issued up front); chunks are a
+// multiple of 4 fragment spans so the 4 waves split them evenly.
 void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
                      int32_t *kc, int32_t *c0) {
     const int64_t per_chunk = int64_t(nproj) * std::max(pl->rt_total(), 1);
+    const int32_t frags = pl->tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
     const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
     int64_t want = (lora::kTargetGroups + per_chunk - 1) / per_chunk;
     want = std::max<int64_t>(1, std::min<int64_t>(want, steps));
-    const int32_t sper = int32_t((steps + want - 1) / want);
+    const int32_t sper = std::min<int32_t>(frags, int32_t((steps + want - 1) / want));
     *kc = sper * lora::kWaves * span;
     *c0 = (h_in + *kc - 1) / *kc;
 }
@@ -605,19 +669,18 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     lora::ShrinkArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
-    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
-    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
-    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
+    a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->off_ttok);
+    a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->off_tiles);
     a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->off_part);
     a.x = x;
     a.ldx = ldx;
     for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
-    a.nb = pl->nb_act;
     a.nproj = nproj;
     a.h_in = cc.h_in;
     shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
     a.units = nproj * pl->rt_total() * a.c0;
     a.grid = grid_for(a.units);
+    a.x_bytes = uint32_t(tensor_bytes(pl->T, ldx, cc.h_in, cc.es));
     const uint64_t need = 4ull * uint64_t(a.units) * pl->tt * lora::kTile * lora::kTile;
     if (need > pl->part_bytes)
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
@@ -635,7 +698,6 @@ lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, i
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
-    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
     a.partial = reinterpret_cast<const float *>(ws + pl->off_part);
     a.v = v;
     a.ldv = ldv;
@@ -646,6 +708,14 @@ lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, i
     hipError_t e = lora::launch_reduce(pl->tt, a, st);
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
     return LORA_OK;
+}
+
+// K-steps of the largest padded rank in the plan (the expand kernels are
+// built for 1, 2 or 4)
+int32_t plan_ksteps(const lora_pool *p, const lora_plan *pl) {
+    const int32_t span = 4 * (16 / esize(p->d.dtype));
+    int32_t ks = std::max(1, (pl->max_rpad + span - 1) / span);
+    return ks == 3 ? 4 : ks;
 }
 
 // v source of the expand: the shrink partials of this call (c0 > 0), or a
@@ -660,9 +730,10 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
+    a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->off_btok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
-    a.rt_prefix = reinterpret_cast<const int32_t *>(ws + pl->off_rtp);
     a.partial = c0 > 0 ? reinterpret_cast<const float *>(ws + pl->off_part) : nullptr;
+    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->part_bytes, lora::kMaxTensorBytes));
     a.c0 = c0;
     a.v = v;
     a.y = y;
@@ -670,19 +741,15 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.ldv = ldv;
     a.ldy = ldy;
     a.ldb = ldb;
-    int64_t rows = 0;
     for (int i = 0; i < nproj; ++i) {
         a.coef_b[i] = p->coef_b(layer, projs[i]);
         a.h_out[i] = p->d.h_out[projs[i]];
         a.y_off[i] = yoff[i];
-        rows += a.h_out[i];
     }
-    // rows per wave: about kTargetGroups workgroups, 32 .. 512 rows per wave
-    int64_t ocw = (rows * nb + int64_t(lora::kTargetGroups) * lora::kWaves - 1) /
-                  (int64_t(lora::kTargetGroups) * lora::kWaves);
-    ocw = std::max<int64_t>(32, std::min<int64_t>(512, round_up(uint64_t(ocw), 32)));
-    a.ocw = int32_t(ocw);
-    const int32_t rows_per_group = a.ocw * lora::kWaves;
+    // K-steps of the largest padded rank fix the rows per wave (the wave
+    // keeps 8 B fragments); 4 waves per workgroup
+    const int32_t ks = plan_ksteps(p, pl);
+    const int32_t rows_per_group = 16 * lora::expand_tiles(ks) * lora::kWaves;
     a.oc_prefix[0] = 0;
     for (int i = 0; i < nproj; ++i)
         a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
@@ -692,7 +759,9 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.units = nb * a.oc_prefix[nproj];
     a.grid = grid_for(a.units);
     a.r_max = p->d.r_max;
-    hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, a, st);
+    a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
+    a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
+    hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, ks, a, st);
     if (e != hipSuccess) return hip_fail(e, "expand launch");
     return LORA_OK;
 }
@@ -711,6 +780,8 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
     if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
                                                (long long)ldx);
+    if (tensor_bytes(pl->T, ldx, cc.h_in, cc.es) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "x spans more than 2 GiB");
     if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
     if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
@@ -731,7 +802,7 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
     if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
-    st = check_y(p, nproj, projs, yoff, y, ldy, "y", cc);
+    st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
     return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,
                       static_cast<hipStream_t>(stream));
@@ -747,10 +818,12 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
     if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
                                                (long long)ldx);
-    st = check_y(p, nproj, projs, yoff, y, ldy, "y", cc);
+    if (tensor_bytes(pl->T, ldx, cc.h_in, cc.es) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "x spans more than 2 GiB");
+    st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
     if (base) {
-        st = check_y(p, nproj, projs, yoff, base, ldb, "base", cc);
+        st = check_y(p, pl->T, nproj, projs, yoff, base, ldb, "base", cc);
         if (st != LORA_OK) return st;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);

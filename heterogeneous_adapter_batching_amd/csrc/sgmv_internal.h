@@ -14,8 +14,13 @@ constexpr int kWaveSize = 64;
 constexpr int kWaves = 4;                    // waves per 256-thread workgroup
 constexpr int kTile = 16;                    // MFMA tile edge (rows, tokens)
 constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 token tiles
+constexpr int kDecodeBlockTokens = 16;       // block size when no group reaches kLongGroup
+constexpr int kLongGroup = 48;
 constexpr int kTargetGroups = 1024;          // workgroups aimed for per launch (4 per CU)
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
+// Activations and outputs are addressed through buffer resources whose
+// out-of-range offset is 2^31: each such tensor spans at most 2 GiB.
+constexpr uint64_t kMaxTensorBytes = 1ull << 31;
 
 // One token block of one adapter group (or of the tokens without an adapter).
 struct BlockDesc {
@@ -24,42 +29,58 @@ struct BlockDesc {
     int32_t r_pad;     // padded rank; 0 marks a block of tokens without an adapter
     int32_t rt;        // rank tiles of 16 rows: ceil(r_pad / 16)
     float scale;       // the adapter's scale
-    int32_t group;     // group index (-1 for tokens without an adapter)
+    int32_t rt_before; // rank tiles of the adapter blocks before this one
     uint32_t ext_lo;   // adapter extent byte offset in the slab, low and high words
     uint32_t ext_hi;
 };
 static_assert(sizeof(BlockDesc) == 32, "BlockDesc is 32 bytes");
 
-// Shrink: one workgroup per unit (block b, k-chunk c, rank tile rt,
-// projection i).  Units of a block are ordered with c outermost, so the units
-// that read the same x chunk are consecutive; consecutive units are placed on
-// one XCD.  The 4 waves split the chunk's K range and are summed through LDS
-// in a fixed order; the unit writes one float32 partial tile
-// [16 * TT token slots][16 ranks] at partial + unit * TT * 256.
+// One rank tile (16 rows of A) of one adapter block: the shrink's unit of
+// equal adapter bytes, whatever the adapter's rank.  tiles[rt_before + i] is
+// tile i of a block.
+struct TileDesc {
+    int32_t tok_off;
+    int32_t n_tok;
+    int32_t r_pad;
+    int32_t tile;      // rank tile index within the block
+    int32_t block;     // block index
+    int32_t pad1;
+    uint32_t ext_lo;
+    uint32_t ext_hi;
+};
+static_assert(sizeof(TileDesc) == 32, "TileDesc is 32 bytes");
+
+// Shrink: one workgroup per unit (rank tile, k-chunk c, projection i), unit
+// u = tile * nproj * c0 + c * nproj + i, so the projections that read the
+// same x chunk are consecutive; consecutive units are placed on one XCD.
+// The 4 waves split the chunk's K range and are summed through LDS in a fixed
+// order; the unit writes one float32 partial tile [16 * TT token slots][16
+// ranks] at partial + u * TT * 256.
 struct ShrinkArgs {
     const uint8_t *slab;
-    const int32_t *tok;          // plan token order
-    const BlockDesc *blocks;
-    const int32_t *rt_prefix;    // [nb + 1] prefix sums of BlockDesc::rt
+    const int32_t *tile_tok;     // [rt_total][kMaxBlockTokens] token rows, -1 padded
+    const TileDesc *tiles;       // [rt_total]
     float *partial;
     const void *x;
     int64_t ldx;
     int64_t coef_a[LORA_MAX_PROJ];  // A block offset = extent + r_pad * esize * coef_a[i]
-    int32_t nb;                  // adapter blocks
     int32_t nproj;
     int32_t h_in;
-    int32_t kc;                  // k-chunk (elements, multiple of 4 fragment spans)
+    int32_t kc;                  // k-chunk (elements): 4 waves x at most kShrinkFrags fragments
     int32_t c0;                  // number of k-chunks
     int32_t units;
     int32_t grid;                // workgroups launched: units rounded up to kXcds
+    uint32_t x_bytes;            // buffer range (at most kMaxTensorBytes)
 };
+
+// fragments (16 bytes per lane) a shrink wave loads up front
+template <int TT> constexpr int shrink_frags() { return TT <= 2 ? 8 : 4; }
 
 // v from the shrink's partials, for the standalone shrink:
 // v[t][i * r_max + j] = sum over chunks (j < r_pad), 0 for r_pad <= j < r_max.
 struct ReduceArgs {
     const int32_t *tok;
     const BlockDesc *blocks;
-    const int32_t *rt_prefix;
     const float *partial;
     float *v;
     int64_t ldv;
@@ -70,17 +91,18 @@ struct ReduceArgs {
 };
 
 // Expand: one workgroup per unit (block b, projection i, chunk of 4 * ocw
-// output rows).  The workgroup gathers its tokens' v into LDS once (summing
-// the shrink partials in a fixed order, or reading a caller's v), then each
-// wave streams the B rows of its ocw rows and writes y = y_in + s * (B v),
-// rounded once.
+// output rows; ocw = 16 * expand_tiles(ks)).  Each wave first issues the
+// loads of all its B rows, then the workgroup gathers its tokens' v into LDS
+// once (summing the shrink partials in a fixed order, or reading a caller's
+// v), and each wave writes y = y_in + s * (B v), rounded once.
 struct ExpandArgs {
     const uint8_t *slab;
-    const int32_t *tok;
+    const int32_t *tok;          // plan token order
+    const int32_t *block_tok;    // [nb][kMaxBlockTokens] token rows, -1 padded
     const BlockDesc *blocks;
-    const int32_t *rt_prefix;
     const float *partial;        // non-null: v = sum of partials
     const float *v;              // else: caller's v [T][ldv]
+    uint32_t partial_bytes;
     void *y;
     const void *base;            // nullable: y_in = base, else y_in = y
     int64_t ldv;
@@ -92,17 +114,23 @@ struct ExpandArgs {
     int32_t oc_prefix[LORA_MAX_PROJ + 1];  // row chunks of projections before i
     int32_t nb;                  // blocks launched over
     int32_t nproj;
-    int32_t ocw;                 // output rows per wave (multiple of 32)
     int32_t c0;                  // partial chunks (when partial != null)
     int32_t units;
     int32_t grid;
     int32_t r_max;
+    uint32_t y_bytes;            // buffer ranges (each at most kMaxTensorBytes)
+    uint32_t base_bytes;
 };
 
+// 16-row output tiles per expand wave, for kernels built for `ks` K-steps
+// (ranks / (4 fragment elements)) at most: the wave keeps 8 B fragments.
+constexpr int expand_tiles(int ks) { return ks >= 8 ? 1 : 8 / ks; }
+
 // Kernel launchers (kernels.hip).  dtype is a lora_dtype; tt is the number of
-// 16-token tiles of the largest block (1, 2 or 4).
+// 16-token tiles of the largest block (1, 2 or 4); ks the K-steps of the
+// largest padded rank (bf16: 1 or 2, f32: 1, 2 or 4).
 hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
-hipError_t launch_expand(int dtype, int tt, const ExpandArgs &a, hipStream_t s);
+hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s);
 
 }  // namespace lora

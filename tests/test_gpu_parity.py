@@ -179,19 +179,23 @@ def test_prefill_blocks(seed):
     check_workload(dw, tight=True, threads=4)
 
 
-def test_two_step_equals_fused():
-    """sgmv_shrink + sgmv_expand through a v buffer gives the same bits as sgmv_fused."""
-    for w in (config(1), multi_proj_case(3, has_base=True), config(0)):
-        log(f"[parity] two-step vs fused {w.name}")
+def test_two_step_path():
+    """sgmv_shrink + sgmv_expand through a caller's v buffer: the same delta,
+    within the float32 bound (it sums K in another order than sgmv_fused), and
+    deterministic."""
+    for w in (config(1), multi_proj_case(3, has_base=True), config(0),
+              random_case(71, T=150, h_in=512, h_out=256, max_seg=80, r_choices=[8, 24, 64])):
+        log(f"[parity] two-step {w.name}")
         dw = DeviceWorkload(w, threads=4)
-        dw.zero_outputs()
-        dw.run_fused()
-        fused = {k: from_device(v) for k, v in dw.y.items()}
-        dw.zero_outputs()
-        dw.run_two_step()
-        torch.cuda.synchronize()
-        for k, v in dw.y.items():
-            assert np.array_equal(from_device(v), fused[k]), k
+        outs = []
+        for _ in range(2):
+            dw.zero_outputs()
+            dw.run_two_step()
+            torch.cuda.synchronize()
+            outs.append({k: from_device(v) for k, v in dw.y.items()})
+        for k in outs[0]:
+            assert np.array_equal(outs[0][k], outs[1][k]), k
+        check_workload(dw, tight=True, threads=4)
 
 
 def test_shrink_output_layout():
