@@ -59,15 +59,16 @@ __device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kNT);
 }
 
-// float -> bf16 bits, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 bits (low half = a), rounded to nearest even by
+// the hardware conversion (v_cvt_pk_bf16_f32); NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <typename T> __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c);
 
@@ -96,12 +97,15 @@ __device__ __forceinline__ uint64_t extent(uint32_t lo, uint32_t hi) {
     return (uint64_t(hi) << 32) | lo;
 }
 
-// Workgroup g runs on XCD g % kXcds.  Give each XCD a contiguous range of
-// units, so units that share operands (the x chunk of one block, the partials
-// of one block) meet in one L2.
-__device__ __forceinline__ int xcd_unit(int grid) {
+// Workgroup g runs on XCD g % kXcds.  Units are dealt to the XCDs in groups
+// of `gs` consecutive units, round-robin: a group (e.g. the projections that
+// read one x chunk) shares one L2, while consecutive groups, whose work may
+// differ a lot (a popular adapter's block), spread over all XCDs and their
+// links.  `grid` is a multiple of kXcds * gs.
+__device__ __forceinline__ int xcd_unit(int gs) {
     const int g = blockIdx.x;
-    return (g % kXcds) * (grid / kXcds) + g / kXcds;
+    const int x = g % kXcds, i = g / kXcds;
+    return (i / gs) * (kXcds * gs) + x * gs + (i % gs);
 }
 
 // ---------------------------------------------------------------- shrink ----
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     constexpr int F = shrink_frags<TT>();
     __shared__ f32x4 red[kWaves][TT][kWaveSize];
 
-    const int u = xcd_unit(a.grid);
+    const int u = xcd_unit(a.nproj);
     if (u >= a.units) return;            // whole workgroup: no barrier is skipped
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
@@ -134,19 +138,22 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     const int k_lo = c * a.kc + w * kw;
     const int k_hi = min(min(a.h_in, (c + 1) * a.kc), k_lo + kw);
 
-    // A rows first: they depend on nothing but the descriptor
+    // A first: it depends on nothing but the descriptor.  A is K-blocked
+    // [h_in_pad / SPAN][r_pad][SPAN], so the 16 rows x SPAN columns of one
+    // fragment are one contiguous 1 KB (bf16) read.
     const rsrc_t ar = make_rsrc(
         a.slab + extent(td.ext_lo, td.ext_hi) +
             uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
-        uint32_t(td.r_pad) * uint32_t(a.h_in) * sizeof(T));
+        uint32_t(td.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
     const int j = td.tile * kTile + n;
     const bool jv = j < td.r_pad;
     u32x4 af[F];
 #pragma unroll
     for (int f = 0; f < F; ++f) {
         const int k = k_lo + f * SPAN + q * E;
+        const uint32_t kb = uint32_t(k_lo / SPAN + f);
         af[f] = bload16_nt(ar, off_or_oob(jv && k < k_hi,
-                                          (uint32_t(j) * uint32_t(a.h_in) + k) * sizeof(T)));
+                                          ((kb * td.r_pad + j) * SPAN + q * E) * sizeof(T)));
     }
 
     // then the token rows
@@ -226,22 +233,24 @@ template <typename T> struct VOperand;
 template <> struct VOperand<uint16_t> {
     static constexpr int kPieces = 3;
     u32x4 piece[3];
+    // v = h0 + h1 + h2 exactly: each residual is exact in float32 and the
+    // three 8-bit significands cover float32's 24.  Inf/NaN keep no residual.
     __device__ __forceinline__ void set(const float (&f)[8]) {
-        uint32_t h[3][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h0 = bf16_rne(f[e]);
-            const float r1 = f[e] - bf16_to_f32(h0);
-            const bool fin = (h0 & 0x7f80u) != 0x7f80u;   // Inf/NaN: no residual
-            const uint32_t h1 = fin ? bf16_rne(r1) : 0u;
-            const float r2 = r1 - bf16_to_f32(h1);
-            const uint32_t h2 = fin ? bf16_rne(r2) : 0u;
-            h[0][e] = h0; h[1][e] = h1; h[2][e] = h2;
+        for (int i = 0; i < 4; ++i) {
+            const float a = f[2 * i], b = f[2 * i + 1];
+            const uint32_t w0 = bf16x2_rne(a, b);
+            const float a1 = a - bf16_lo(w0), b1 = b - bf16_hi(w0);
+            const uint32_t w1 = bf16x2_rne(a1, b1);
+            const float a2 = a1 - bf16_lo(w1), b2 = b1 - bf16_hi(w1);
+            uint32_t w2 = bf16x2_rne(a2, b2);
+            uint32_t w1m = w1;
+            if ((w0 & 0x7f80u) == 0x7f80u) { w1m &= 0xffff0000u; w2 &= 0xffff0000u; }
+            if ((w0 & 0x7f800000u) == 0x7f800000u) { w1m &= 0xffffu; w2 &= 0xffffu; }
+            piece[0][i] = w0;
+            piece[1][i] = w1m;
+            piece[2][i] = w2;
         }
-#pragma unroll
-        for (int pc = 0; pc < 3; ++pc)
-            piece[pc] = u32x4{h[pc][0] | (h[pc][1] << 16), h[pc][2] | (h[pc][3] << 16),
-                              h[pc][4] | (h[pc][5] << 16), h[pc][6] | (h[pc][7] << 16)};
     }
 };
 
@@ -265,12 +274,11 @@ template <> struct Out4<uint16_t> {
         __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, 0);
     }
     static __device__ __forceinline__ void unpack(raw w, float (&o)[4]) {
-        o[0] = __uint_as_float(w[0] << 16); o[1] = __uint_as_float(w[0] & 0xffff0000u);
-        o[2] = __uint_as_float(w[1] << 16); o[3] = __uint_as_float(w[1] & 0xffff0000u);
+        o[0] = bf16_lo(w[0]); o[1] = bf16_hi(w[0]);
+        o[2] = bf16_lo(w[1]); o[3] = bf16_hi(w[1]);
     }
     static __device__ __forceinline__ raw pack(const float (&o)[4]) {
-        return u32x2{bf16_rne(o[0]) | (bf16_rne(o[1]) << 16),
-                     bf16_rne(o[2]) | (bf16_rne(o[3]) << 16)};
+        return u32x2{bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3])};
     }
 };
 template <> struct Out4<float> {
@@ -291,108 +299,58 @@ template <> struct Out4<float> {
     }
 };
 
-template <typename T, int TT, int KSM>
-__global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
-    constexpr int E = Elem<T>::E;
-    constexpr int SPAN = 4 * E;                      // ranks per K-step
-    constexpr int OTW = expand_tiles(KSM);           // 16-row tiles per wave
-    constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
-    __shared__ float vs[TT * kTile][VS];
+// The expand's per-workgroup context: the block, its token rows and the
+// wave's output rows.
+struct ExpandCtx {
+    int b, p, w, n, q;
+    int o_lo, o_hi, yoff, h_out, ks_n, ntiles;
+    float scale;
+};
 
-    const int u = xcd_unit(a.grid);
-    if (u >= a.units) return;                        // whole workgroup
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
-    const int n = lane & 15, q = lane >> 4;
-
-    const int upb = a.oc_prefix[a.nproj];
-    const int b = u / upb;
-    const int rem = u - b * upb;
-    int p = 0;
-    while (rem >= a.oc_prefix[p + 1]) ++p;
-    const int oc = rem - a.oc_prefix[p];
-    int trow[TT];                                    // token rows, -1 padded
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) trow[tt] = a.block_tok[b * kMaxBlockTokens + tt * kTile + n];
-    const BlockDesc blk = a.blocks[b];
-    const int h_out = a.h_out[p];
-    const int o_lo = min(h_out, (oc * kWaves + w) * (OTW * kTile));
-    const int o_hi = min(h_out, o_lo + OTW * kTile);
-    const int yoff = a.y_off[p];
-    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;  // wave-uniform, <= KSM
-
-    // B rows of this wave first: they depend on nothing but the descriptor
-    const rsrc_t br = make_rsrc(
-        a.slab + extent(blk.ext_lo, blk.ext_hi) +
-            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
-        uint32_t(h_out) * uint32_t(blk.r_pad) * sizeof(T));
-    u32x4 bf[OTW][KSM];
-#pragma unroll
-    for (int ot = 0; ot < OTW; ++ot) {
-        const int orow = o_lo + ot * kTile + n;
-#pragma unroll
-        for (int ks = 0; ks < KSM; ++ks) {
-            const int j0 = ks * SPAN + q * E;
-            bf[ot][ks] = bload16_nt(br, off_or_oob(ks < ks_n && orow < o_hi && j0 < blk.r_pad,
-                                                   uint32_t(orow * blk.r_pad + j0) * sizeof(T)));
-        }
+// One output element: bf16 (2 bytes) or float32 (4 bytes).
+template <typename T> struct Out1;
+template <> struct Out1<uint16_t> {
+    static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
+        return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, 0))
+                               << 16);
     }
-
-    // then y_in (base, or y itself) of every output tile
-    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
-    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
-    const int64_t ld_in = a.base ? a.ldb : a.ldy;
-    const int ntiles = (blk.n_tok + kTile - 1) / kTile;
-    bool tv[TT];
-    typename Out4<T>::raw yin[OTW][TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        tv[tt] = tt < ntiles && trow[tt] >= 0;
-#pragma unroll
-        for (int ot = 0; ot < OTW; ++ot) {
-            const int o = o_lo + ot * kTile + 4 * q;
-            yin[ot][tt] = Out4<T>::load(
-                inr, off_or_oob(tv[tt] && o < o_hi,
-                                uint32_t(int64_t(trow[tt]) * ld_in + yoff + o) * sizeof(T)));
-        }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(
+            (unsigned short)(bf16x2_rne(v, 0.f) & 0xffffu), r, int(off), 0, 0);
     }
-
-    if (blk.r_pad == 0) {            // tokens without an adapter: y = base
-        if (!a.base) return;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-            for (int ot = 0; ot < OTW; ++ot) {
-                const int o = o_lo + ot * kTile + 4 * q;
-                Out4<T>::store(yr, off_or_oob(tv[tt] && o < o_hi,
-                                              uint32_t(int64_t(trow[tt]) * a.ldy + yoff + o) *
-                                                  sizeof(T)),
-                               yin[ot][tt]);
-            }
-        }
-        return;
+};
+template <> struct Out1<float> {
+    static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
     }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, int(off), 0, 0);
+    }
+};
 
-    // v of the block's tokens into LDS, once per workgroup: the chunk partials
-    // of each (token, 4 ranks) are loaded 8 at a time, then summed in order
+// v of the block's tokens into LDS, once per workgroup: from the shrink's
+// chunk partials (loaded 8 at a time, summed in chunk order) or a caller's v.
+template <int TT>
+__device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &blk, int p,
+                                         float (*vs)[LORA_MAX_RANK + 4]) {
     const int quads = blk.r_pad / 4;
     if (a.partial) {
         const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
-        constexpr int G = 8;
+        constexpr int GP = 8;
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
             const int ti = i / quads, j = (i % quads) * 4;
             const uint32_t base_f = uint32_t((blk.rt_before + j / kTile) * a.nproj * a.c0 + p) *
                                         (TT * kTile * kTile) + ti * kTile + j % kTile;
             const uint32_t stride_f = uint32_t(a.nproj) * (TT * kTile * kTile);
             f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < a.c0; c0 += G) {
-                u32x4 part[G];
+            for (int c0 = 0; c0 < a.c0; c0 += GP) {
+                u32x4 part[GP];
 #pragma unroll
-                for (int g = 0; g < G; ++g)
+                for (int g = 0; g < GP; ++g)
                     part[g] = bload16(pr, off_or_oob(c0 + g < a.c0,
                                                      (base_f + uint32_t(c0 + g) * stride_f) * 4));
 #pragma unroll
-                for (int g = 0; g < G; ++g)
+                for (int g = 0; g < GP; ++g)
                     if (c0 + g < a.c0) s4 += __builtin_bit_cast(f32x4, part[g]);
             }
             *reinterpret_cast<f32x4 *>(&vs[ti][j]) = s4;
@@ -405,19 +363,204 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
                 a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j);
         }
     }
-    __syncthreads();
-    if (o_lo >= o_hi) return;
+}
 
-    // v operand per (token tile, K-step)
+// Decode expand on the vector ALUs (blocks of at most kValuTokens tokens):
+// each lane owns RPL output rows per step (rows lane + 64 i) and streams NV
+// 16-byte vectors of each (the B row: r_pad = NV * E values), dotting them
+// with every token's v (an LDS broadcast), in float32.  Every step issues
+// 8 B loads per lane (8 KB a wave) at once; other resident waves cover the
+// latency.
+template <typename T, int NV>
+__device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
+                                            const ExpandCtx &c, float (*vs)[LORA_MAX_RANK + 4]) {
+    constexpr int E = Elem<T>::E;
+    constexpr int RPL = NV >= 8 ? 1 : (NV >= 4 ? 2 : 4);   // rows per lane per step
+    constexpr int NT = kValuTokens;
+    constexpr int STEP = RPL * kWaveSize;                  // rows per step
+    const int lane = threadIdx.x & 63;
+    const int nv = blk.r_pad / E;                    // wave-uniform, <= NV
+    const int nt = blk.n_tok;                        // wave-uniform, <= NT
+    const rsrc_t br = make_rsrc(
+        a.slab + extent(blk.ext_lo, blk.ext_hi) +
+            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[c.p]),
+        uint32_t(c.h_out) * uint32_t(blk.r_pad) * sizeof(T));
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
+    const int64_t ld_in = a.base ? a.ldb : a.ldy;
+    const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
+    uint32_t in_row[NT], y_row[NT];                  // wave-uniform token rows (byte offsets)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int tr = a.block_tok[c.b * kMaxBlockTokens + t];
+        const bool ok = t < nt && tr >= 0;
+        in_row[t] = ok ? uint32_t((int64_t(tr) * ld_in + c.yoff) * sizeof(T)) : kOOB;
+        y_row[t] = ok ? uint32_t((int64_t(tr) * a.ldy + c.yoff) * sizeof(T)) : kOOB;
+    }
+
+    u32x4 bv[RPL][NV];
+    float yin[RPL][NT];
+    auto load = [&](int r0) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = r0 + i * kWaveSize + lane;
+            const bool rok = row < c.o_hi;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                bv[i][v] = bload16_nt(br, off_or_oob(rok && v < nv,
+                                                     uint32_t(row) * row_bytes + v * 16));
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+        }
+    };
+
+    load(c.o_lo);
+    gather_v<1>(a, blk, c.p, vs);
+    __syncthreads();
+    for (int r0 = c.o_lo; r0 < c.o_hi; r0 += STEP) {
+        if (r0 > c.o_lo) load(r0);
+        float d[RPL][NT];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            // a wave-uniform guard rather than a loop exit, so the loop
+            // unrolls fully and bv stays in registers
+            if (v < nv) {
+            // v is read from LDS per vector (a broadcast), not hoisted into
+            // NT * r_pad registers
+            asm volatile("" ::: "memory");
+            float w[NT][E];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + e]);
+                    w[t][e] = w4[0]; w[t][e + 1] = w4[1]; w[t][e + 2] = w4[2]; w[t][e + 3] = w4[3];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                float f[E];
+                if constexpr (E == 8) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        f[2 * k] = bf16_lo(bv[i][v][k]);
+                        f[2 * k + 1] = bf16_hi(bv[i][v][k]);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(bv[i][v][k]);
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    if (t < nt) {                    // wave-uniform
+#pragma unroll
+                        for (int e = 0; e < E; ++e)
+                            d[i][t] = __builtin_fmaf(f[e], w[t][e], d[i][t]);
+                    }
+            }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = r0 + i * kWaveSize + lane;
+            const bool rok = row < c.o_hi;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)           // y_row[t] is kOOB for t >= nt
+                Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
+                               yin[i][t] + c.scale * d[i][t]);
+        }
+    }
+}
+
+// Expand of one workgroup for blocks whose padded rank packs TPL row tiles
+// into one 16-byte load per lane (TPL = 4: r_pad = E / 2 ... see below), or
+// TPL = 1 (one tile per load and K-step).  Row chunks of OTW tiles are
+// double-buffered: the next chunk's B rows and y_in are in flight while the
+// current chunk is computed.
+//
+// Packing: a 16-row tile of B is 16 * r_pad elements.  With G = r_pad / E
+// 16-byte vectors per row and G in {1, 2}, one load of 64 lanes covers
+// TPL = 4 / G consecutive tiles: lane group q reads vector q % G of tile
+// q / G.  The MFMA of tile t then takes v only in the lane groups holding
+// tile t (zero elsewhere), which selects tile t's rows.
+template <typename T, int TT, int KSM, int TPL>
+__device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc &blk,
+                                            const ExpandCtx &c, const int (&trow)[TT],
+                                            const bool (&tv)[TT], float (*vs)[LORA_MAX_RANK + 4]) {
+    constexpr int E = Elem<T>::E;
+    constexpr int SPAN = 4 * E;
+    constexpr int OTW = expand_tiles(KSM);           // tiles per chunk
+    constexpr int NL = TPL == 1 ? OTW * KSM : OTW / TPL;   // loads per chunk
+    constexpr int CH = OTW * kTile;                  // rows per chunk
+    const int G = TPL == 1 ? 4 : 4 / TPL;            // vectors per row (packed)
+    typedef typename Out4<T>::raw raw;
+
+    const rsrc_t br = make_rsrc(
+        a.slab + extent(blk.ext_lo, blk.ext_hi) +
+            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[c.p]),
+        uint32_t(c.h_out) * uint32_t(blk.r_pad) * sizeof(T));
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
+    const int64_t ld_in = a.base ? a.ldb : a.ldy;
+
+    // Byte offsets hoisted out of the row loops: a masked token's row offset
+    // is already out of range (kOOB + o * size stays >= 2^31, below 2^32).
+    uint32_t in_row[TT], y_row[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        in_row[tt] = tv[tt] ? uint32_t((int64_t(trow[tt]) * ld_in + c.yoff) * sizeof(T)) : kOOB;
+        y_row[tt] = tv[tt] ? uint32_t((int64_t(trow[tt]) * a.ldy + c.yoff) * sizeof(T)) : kOOB;
+    }
+    const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
+    // this lane's row within a tile and element offset within the row
+    const int lane_tile = TPL == 1 ? 0 : c.q / G;
+    const uint32_t lane_b = uint32_t(lane_tile * kTile + c.n) * row_bytes +
+                            uint32_t(TPL == 1 ? c.q * E : (c.q % G) * E) * sizeof(T);
+
+    auto load = [&](int o0, u32x4 (&bf)[NL], raw (&yin)[OTW][TT]) {
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int t = TPL == 1 ? l / KSM : l * TPL;          // first tile of the load
+            const int ks = TPL == 1 ? l % KSM : 0;
+            const int row = o0 + (t + lane_tile) * kTile + c.n;
+            const bool ok = row < c.o_hi &&
+                            (TPL > 1 || (ks < c.ks_n && ks * SPAN + c.q * E < blk.r_pad));
+            bf[l] = bload16_nt(br, off_or_oob(ok, uint32_t(o0 + t * kTile) * row_bytes + lane_b +
+                                                      uint32_t(ks * SPAN) * sizeof(T)));
+        }
+#pragma unroll
+        for (int ot = 0; ot < OTW; ++ot) {
+            const int o = o0 + ot * kTile + 4 * c.q;
+            const uint32_t oo = uint32_t(o) * sizeof(T);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                yin[ot][tt] = Out4<T>::load(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
+        }
+    };
+
+    u32x4 bfA[NL], bfB[NL];
+    raw yinA[OTW][TT], yinB[OTW][TT];
+    load(c.o_lo, bfA, yinA);
+
+    gather_v<TT>(a, blk, c.p, vs);
+    __syncthreads();
+    if (c.o_lo >= c.o_hi) return;
+
+    // v operand per (token tile, K-step); packed blocks have one K-step
     VOperand<T> vop[TT][KSM];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
         for (int ks = 0; ks < KSM; ++ks) {
             float f[E];
-            const int j0 = ks * SPAN + q * E;
-            const bool ok = tv[tt] && ks < ks_n && j0 < blk.r_pad;
-            const int row = ok ? tt * kTile + n : 0;
+            const int j0 = TPL == 1 ? ks * SPAN + c.q * E : (c.q % G) * E;
+            const bool ok = tv[tt] && ks < c.ks_n && j0 < blk.r_pad;
+            const int row = ok ? tt * kTile + c.n : 0;
             const int col = ok ? j0 : 0;
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
@@ -429,33 +572,191 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
         }
     }
 
-    const float s = blk.scale;
+    auto compute = [&](int o0, const u32x4 (&bf)[NL], const raw (&yin)[OTW][TT]) {
 #pragma unroll
-    for (int ot = 0; ot < OTW; ++ot) {
-        const int obase = o_lo + ot * kTile;
-        if (obase >= o_hi) break;                    // wave-uniform
+        for (int ot = 0; ot < OTW; ++ot) {
+            const int obase = o0 + ot * kTile;
+            if (obase >= c.o_hi) break;              // wave-uniform
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            if (tt >= ntiles) continue;              // wave-uniform
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < TT; ++tt) {
+                if (tt >= c.ntiles) continue;        // wave-uniform
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (TPL == 1) {
 #pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) {
-                if (ks >= ks_n) continue;
+                    for (int ks = 0; ks < KSM; ++ks) {
+                        if (ks >= c.ks_n) continue;
 #pragma unroll
-                for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
-                    acc = mma<T>(bf[ot][ks], vop[tt][ks].piece[pc], acc);
+                        for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
+                            acc = mma<T>(bf[ot * KSM + ks], vop[tt][ks].piece[pc], acc);
+                    }
+                } else {
+                    const bool mine = c.q / G == ot % TPL;   // lane groups of this tile
+#pragma unroll
+                    for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc) {
+                        const u32x4 vp = vop[tt][0].piece[pc];
+                        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                        acc = mma<T>(bf[ot / TPL], mine ? vp : z, acc);
+                    }
+                }
+                const int o = obase + 4 * c.q;
+                float in[4], out[4];
+                Out4<T>::unpack(yin[ot][tt], in);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[i] = in[i] + c.scale * acc[i];
+                Out4<T>::store(yr, o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB,
+                               Out4<T>::pack(out));
             }
-            const int o = obase + 4 * q;             // 4 consecutive outputs of token n
-            float in[4], out[4];
-            Out4<T>::unpack(yin[ot][tt], in);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = in[i] + s * acc[i];
-            Out4<T>::store(yr, off_or_oob(tv[tt] && o < o_hi,
-                                          uint32_t(int64_t(trow[tt]) * a.ldy + yoff + o) *
-                                              sizeof(T)),
-                           Out4<T>::pack(out));
         }
+    };
+
+    for (int o0 = c.o_lo; o0 < c.o_hi; o0 += 2 * CH) {
+        if (o0 + CH < c.o_hi) load(o0 + CH, bfB, yinB);
+        compute(o0, bfA, yinA);
+        const int o1 = o0 + CH;
+        if (o1 >= c.o_hi) break;
+        if (o1 + CH < c.o_hi) load(o1 + CH, bfA, yinA);
+        compute(o1, bfB, yinB);
     }
+}
+
+// Decode expand: plans whose blocks hold at most kValuTokens tokens.  Same
+// units and row slices as k_expand; the B row length picks the vector count.
+template <typename T>
+__global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
+    constexpr int E = Elem<T>::E;
+    constexpr int VS = LORA_MAX_RANK + 4;
+    __shared__ float vs[kValuTokens][VS];
+
+    const int u = xcd_unit(1);
+    if (u >= a.units) return;                        // whole workgroup
+    const int lane = threadIdx.x & 63;
+    ExpandCtx c;
+    c.w = wave_id();
+    c.n = lane & 15;
+    c.q = lane >> 4;
+    const int upb = a.oc_prefix[a.nproj];
+    c.b = u / upb;
+    const int rem = u - c.b * upb;
+    c.p = 0;
+    while (rem >= a.oc_prefix[c.p + 1]) ++c.p;
+    const int oc = rem - a.oc_prefix[c.p];
+    const BlockDesc blk = a.blocks[c.b];
+    c.h_out = a.h_out[c.p];
+    const int rows_w = a.chunks * kDecodeRows;       // rows of this wave
+    c.o_lo = min(c.h_out, (oc * kWaves + c.w) * rows_w);
+    c.o_hi = min(c.h_out, c.o_lo + rows_w);
+    c.yoff = a.y_off[c.p];
+    c.scale = blk.scale;
+
+    if (blk.r_pad == 0) {            // tokens without an adapter: y = base, 4 outputs a lane
+        if (!a.base) return;
+        const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+        const rsrc_t br = make_rsrc(a.base, a.base_bytes);
+        for (int t = 0; t < blk.n_tok; ++t) {
+            const int tr = a.block_tok[c.b * kMaxBlockTokens + t];
+            for (int o = c.o_lo + 4 * lane; o < c.o_hi; o += 4 * kWaveSize) {
+                const auto v4 = Out4<T>::load(
+                    br, uint32_t((int64_t(tr) * a.ldb + c.yoff + o) * sizeof(T)));
+                Out4<T>::store(yr, uint32_t((int64_t(tr) * a.ldy + c.yoff + o) * sizeof(T)), v4);
+            }
+        }
+        return;
+    }
+    const int nv = blk.r_pad / E;
+    if (nv <= 1) return expand_valu<T, 1>(a, blk, c, vs);
+    if (nv <= 2) return expand_valu<T, 2>(a, blk, c, vs);
+    if (nv <= 4) return expand_valu<T, 4>(a, blk, c, vs);
+    if constexpr (E == 8) {
+        return expand_valu<T, 8>(a, blk, c, vs);
+    } else {
+        if (nv <= 8) return expand_valu<T, 8>(a, blk, c, vs);
+        return expand_valu<T, 16>(a, blk, c, vs);
+    }
+}
+
+template <typename T, int TT, int KSM>
+__global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
+    constexpr int E = Elem<T>::E;
+    constexpr int SPAN = 4 * E;
+    constexpr int OTW = expand_tiles(KSM);
+    constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
+    __shared__ float vs[TT * kTile][VS];
+
+    const int u = xcd_unit(1);
+    if (u >= a.units) return;                        // whole workgroup
+    const int lane = threadIdx.x & 63;
+    ExpandCtx c;
+    c.w = wave_id();
+    c.n = lane & 15;
+    c.q = lane >> 4;
+    const int upb = a.oc_prefix[a.nproj];
+    c.b = u / upb;
+    const int rem = u - c.b * upb;
+    c.p = 0;
+    while (rem >= a.oc_prefix[c.p + 1]) ++c.p;
+    const int oc = rem - a.oc_prefix[c.p];
+    int trow[TT];                                    // token rows, -1 padded
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+        trow[tt] = a.block_tok[c.b * kMaxBlockTokens + tt * kTile + c.n];
+    const BlockDesc blk = a.blocks[c.b];
+    c.h_out = a.h_out[c.p];
+    const int rows_w = a.chunks * OTW * kTile;       // rows of this wave
+    c.o_lo = min(c.h_out, (oc * kWaves + c.w) * rows_w);
+    c.o_hi = min(c.h_out, c.o_lo + rows_w);
+    c.yoff = a.y_off[c.p];
+    c.ks_n = (blk.r_pad + SPAN - 1) / SPAN;          // wave-uniform, <= KSM
+    c.ntiles = (blk.n_tok + kTile - 1) / kTile;
+    c.scale = blk.scale;
+    bool tv[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) tv[tt] = tt < c.ntiles && trow[tt] >= 0;
+
+    if (blk.r_pad == 0) {            // tokens without an adapter: y = base
+        if (!a.base) return;
+        const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+        const rsrc_t br = make_rsrc(a.base, a.base_bytes);
+        for (int o0 = c.o_lo; o0 < c.o_hi; o0 += kTile) {
+            const int o = o0 + 4 * c.q;
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const bool ok = tv[tt] && o < c.o_hi;
+                const auto v4 = Out4<T>::load(
+                    br, off_or_oob(ok, uint32_t(int64_t(trow[tt]) * a.ldb + c.yoff + o) * sizeof(T)));
+                Out4<T>::store(
+                    yr, off_or_oob(ok, uint32_t(int64_t(trow[tt]) * a.ldy + c.yoff + o) * sizeof(T)),
+                    v4);
+            }
+        }
+        return;
+    }
+
+    // rows of 16-byte vectors: 1 or 2 per row pack 4 or 2 tiles into one load
+    if constexpr (KSM == 1) {
+        const int g = blk.r_pad / E;
+        if (g == 1) return expand_body<T, TT, KSM, 4>(a, blk, c, trow, tv, vs);
+        if (g == 2) return expand_body<T, TT, KSM, 2>(a, blk, c, trow, tv, vs);
+    }
+    expand_body<T, TT, KSM, 1>(a, blk, c, trow, tv, vs);
+}
+
+// ----------------------------------------------------------------- pack ----
+// A [rank][h_in] (row-major, device) -> K-blocked [h_in_pad / SPAN][r_pad][SPAN]
+// with zeros in the pad rows and columns; one thread per 16-byte vector.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_a(const T *src, int rank, int h_in, T *dst,
+                                                int r_pad, int h_in_pad) {
+    constexpr int E = Elem<T>::E;
+    constexpr int SPAN = 4 * E;
+    const int vecs = h_in_pad / E * r_pad;             // 16-byte vectors of the block
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= vecs) return;
+    const int kb = i / (r_pad * 4), rem = i % (r_pad * 4);
+    const int j = rem / 4, c = (rem % 4) * E;
+    const int k = kb * SPAN + c;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (j < rank && k < h_in) v = *reinterpret_cast<const u32x4 *>(src + int64_t(j) * h_in + k);
+    *reinterpret_cast<u32x4 *>(dst + (int64_t(kb) * r_pad + j) * SPAN + c) = v;
 }
 
 template <typename T>
@@ -490,6 +791,21 @@ hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s) 
                               : shrink_dispatch<float>(tt, a, s);
 }
 
+hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
+                         int h_in_pad, hipStream_t s) {
+    const int e = dtype == LORA_BF16 ? 8 : 4;
+    const int vecs = h_in_pad / e * r_pad;
+    const dim3 grid((vecs + 255) / 256), block(256);
+    if (dtype == LORA_BF16)
+        hipLaunchKernelGGL(k_pack_a<uint16_t>, grid, block, 0, s,
+                           static_cast<const uint16_t *>(src), rank, h_in,
+                           static_cast<uint16_t *>(dst), r_pad, h_in_pad);
+    else
+        hipLaunchKernelGGL(k_pack_a<float>, grid, block, 0, s, static_cast<const float *>(src),
+                           rank, h_in, static_cast<float *>(dst), r_pad, h_in_pad);
+    return hipGetLastError();
+}
+
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
     if (a.nb <= 0) return hipSuccess;
     const dim3 grid(a.nb * a.nproj), block(kWaves * kWaveSize);
@@ -499,6 +815,14 @@ hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
     case 4: hipLaunchKernelGGL((k_reduce<4>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s) {
+    if (a.units <= 0) return hipSuccess;
+    const dim3 grid(a.grid), block(kWaves * kWaveSize);
+    if (dtype == LORA_BF16) hipLaunchKernelGGL(k_expand_decode<uint16_t>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_expand_decode<float>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 

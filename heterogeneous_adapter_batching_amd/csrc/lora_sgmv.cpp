@@ -73,6 +73,21 @@ int64_t row_elems(const lora_pool_desc *d) {
     return w;
 }
 
+// K elements of one 16-byte fragment over the 4 lane groups of an MFMA:
+// A is stored in blocks of this many columns (see lora_pool_create)
+int32_t kspan(int32_t dtype) { return dtype == LORA_BF16 ? 32 : 16; }
+
+int64_t h_in_pad(const lora_pool_desc *d, int p) {
+    return int64_t(round_up(uint64_t(d->h_in[p]), uint64_t(kspan(d->dtype))));
+}
+
+// the same sum with h_in padded to whole K-blocks: the stored layout
+int64_t stored_row_elems(const lora_pool_desc *d) {
+    int64_t w = 0;
+    for (int p = 0; p < d->num_proj; ++p) w += h_in_pad(d, p) + d->h_out[p];
+    return w;
+}
+
 int32_t pad_rank(const lora_pool_desc *d, int32_t r) {
     return int32_t(round_up(uint64_t(r), uint64_t(d->rank_granule)));
 }
@@ -94,13 +109,13 @@ struct lora_pool {
     std::unordered_map<int32_t, Slot> slots;
     std::map<uint64_t, uint64_t> free_list;  // offset -> bytes, coalesced
     uint64_t generation = 0;                  // bumped by unregister
-    int64_t W = 0;                            // row_elems(d)
-    int64_t pre[LORA_MAX_PROJ + 1] = {};      // prefix of (h_in + h_out) over projections
+    int64_t W = 0;                            // stored_row_elems(d)
+    int64_t pre[LORA_MAX_PROJ + 1] = {};      // prefix of (h_in_pad + h_out) over projections
 
     // element offset multipliers of the A and B blocks of (layer, proj), in
     // units of r_pad elements
     int64_t coef_a(int layer, int p) const { return int64_t(layer) * W + pre[p]; }
-    int64_t coef_b(int layer, int p) const { return coef_a(layer, p) + d.h_in[p]; }
+    int64_t coef_b(int layer, int p) const { return coef_a(layer, p) + h_in_pad(&d, p); }
 
     bool alloc(uint64_t bytes, uint64_t *off) {
         for (auto it = free_list.begin(); it != free_list.end(); ++it) {
@@ -204,7 +219,7 @@ uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank) {
 uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank) {
     if (check_desc(d) != LORA_OK || rank < 1 || rank > d->r_max) return 0;
     return round_up(uint64_t(pad_rank(d, rank)) * esize(d->dtype) * uint64_t(d->num_layers) *
-                    uint64_t(row_elems(d)), 256);
+                    uint64_t(stored_row_elems(d)), 256);
 }
 
 lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d, void *slab,
@@ -219,8 +234,8 @@ lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d, void *sla
     p->slab = static_cast<uint8_t *>(slab);
     p->slab_bytes = slab_bytes / 256 * 256;
     if (p->slab_bytes) p->free_list.emplace(0, p->slab_bytes);
-    p->W = row_elems(d);
-    for (int i = 0; i < d->num_proj; ++i) p->pre[i + 1] = p->pre[i] + d->h_in[i] + d->h_out[i];
+    p->W = stored_row_elems(d);
+    for (int i = 0; i < d->num_proj; ++i) p->pre[i + 1] = p->pre[i] + h_in_pad(d, i) + d->h_out[i];
     *out = p;
     return LORA_OK;
 }
@@ -258,20 +273,37 @@ lora_status lora_pool_upload(lora_pool *p, int32_t id, int32_t layer, int32_t pr
     if (proj < 0 || proj >= p->d.num_proj)
         return fail(LORA_EINVAL, "projection %d not in 0..%d", proj, p->d.num_proj - 1);
     if (!A || !B) return fail(LORA_EINVAL, "null weight pointer");
+    if (!src_on_host && ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15)))
+        return fail(LORA_EINVAL, "device weight sources must be 16-byte aligned");
     const Slot &s = it->second;
     const uint64_t es = esize(p->d.dtype);
     const uint64_t h_in = p->d.h_in[proj], h_out = p->d.h_out[proj];
+    const uint64_t span = kspan(p->d.dtype), hp = h_in_pad(&p->d, proj);
     uint8_t *a_dst = p->slab + s.off + uint64_t(s.r_pad) * es * p->coef_a(layer, proj);
     uint8_t *b_dst = p->slab + s.off + uint64_t(s.r_pad) * es * p->coef_b(layer, proj);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const hipMemcpyKind kind = src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
-    hipError_t e = hipMemcpyAsync(a_dst, A, uint64_t(s.rank) * h_in * es, kind, st);
-    if (e != hipSuccess) return hip_fail(e, "A upload");
-    if (s.r_pad > s.rank) {
-        e = hipMemsetAsync(a_dst + uint64_t(s.rank) * h_in * es, 0,
-                           uint64_t(s.r_pad - s.rank) * h_in * es, st);
-        if (e != hipSuccess) return hip_fail(e, "A pad rows");
+    // A goes K-blocked: [h_in_pad / span][r_pad][span], zero padded, so the 16
+    // rows x span columns one MFMA fragment reads are contiguous
+    const uint64_t a_bytes = uint64_t(s.r_pad) * hp * es;
+    hipError_t e;
+    std::vector<uint8_t> a_blk;
+    if (src_on_host) {
+        a_blk.assign(a_bytes, 0);
+        const uint8_t *src = static_cast<const uint8_t *>(A);
+        for (uint64_t kb = 0; kb < hp / span; ++kb) {
+            const uint64_t cols = std::min<uint64_t>(span, h_in - std::min(h_in, kb * span));
+            if (!cols) break;
+            for (uint64_t j = 0; j < uint64_t(s.rank); ++j)
+                std::memcpy(a_blk.data() + ((kb * s.r_pad + j) * span) * es,
+                            src + (j * h_in + kb * span) * es, cols * es);
+        }
+        e = hipMemcpyAsync(a_dst, a_blk.data(), a_bytes, kind, st);
+    } else {
+        e = lora::launch_pack_a(p->d.dtype, A, s.rank, int32_t(h_in), a_dst, s.r_pad,
+                                int32_t(hp), st);
     }
+    if (e != hipSuccess) return hip_fail(e, "A upload");
     const uint64_t b_bytes = h_out * uint64_t(s.r_pad) * es;
     std::vector<uint8_t> padded;   // host source with padding: widen rows on the host
     if (s.r_pad == s.rank) {
@@ -657,8 +689,9 @@ void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t s
     *c0 = (h_in + *kc - 1) / *kc;
 }
 
-int32_t grid_for(int32_t units) {
-    return int32_t(round_up(uint64_t(std::max(units, 0)), lora::kXcds));
+// workgroups launched for `units` dealt to the XCDs in groups of `gs`
+int32_t grid_for(int32_t units, int32_t gs) {
+    return int32_t(round_up(uint64_t(std::max(units, 0)), uint64_t(lora::kXcds) * gs));
 }
 
 lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
@@ -677,9 +710,10 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
     a.nproj = nproj;
     a.h_in = cc.h_in;
+    a.h_in_pad = int32_t(h_in_pad(&p->d, projs[0]));
     shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
     a.units = nproj * pl->rt_total() * a.c0;
-    a.grid = grid_for(a.units);
+    a.grid = grid_for(a.units, nproj);
     a.x_bytes = uint32_t(tensor_bytes(pl->T, ldx, cc.h_in, cc.es));
     const uint64_t need = 4ull * uint64_t(a.units) * pl->tt * lora::kTile * lora::kTile;
     if (need > pl->part_bytes)
@@ -749,7 +783,15 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     // K-steps of the largest padded rank fix the rows per wave (the wave
     // keeps 8 B fragments); 4 waves per workgroup
     const int32_t ks = plan_ksteps(p, pl);
-    const int32_t rows_per_group = 16 * lora::expand_tiles(ks) * lora::kWaves;
+    const bool decode = pl->max_block <= lora::kValuTokens;   // blocks of the decode expand
+    // row chunks per wave: about kTargetGroups workgroups per launch
+    const int64_t chunk_rows = int64_t(decode ? lora::kDecodeRows : 16 * lora::expand_tiles(ks)) *
+                               lora::kWaves;
+    int64_t rows = 0;
+    for (int i = 0; i < nproj; ++i) rows += a.h_out[i];
+    a.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
+        8, rows * nb / (chunk_rows * lora::kTargetGroups))));
+    const int32_t rows_per_group = int32_t(chunk_rows) * a.chunks;
     a.oc_prefix[0] = 0;
     for (int i = 0; i < nproj; ++i)
         a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
@@ -757,11 +799,12 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.nb = nb;
     a.nproj = nproj;
     a.units = nb * a.oc_prefix[nproj];
-    a.grid = grid_for(a.units);
+    a.grid = grid_for(a.units, 1);
     a.r_max = p->d.r_max;
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
-    hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, ks, a, st);
+    hipError_t e = decode ? lora::launch_expand_decode(p->d.dtype, a, st)
+                          : lora::launch_expand(p->d.dtype, pl->tt, ks, a, st);
     if (e != hipSuccess) return hip_fail(e, "expand launch");
     return LORA_OK;
 }

@@ -14,8 +14,14 @@ constexpr int kWaveSize = 64;
 constexpr int kWaves = 4;                    // waves per 256-thread workgroup
 constexpr int kTile = 16;                    // MFMA tile edge (rows, tokens)
 constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 token tiles
-constexpr int kDecodeBlockTokens = 16;       // block size when no group reaches kLongGroup
+// Decode plans (no group reaches kLongGroup tokens) cut groups into blocks of
+// at most kDecodeBlockTokens: every workgroup of a launch then moves about
+// the same bytes (a popular adapter's group becomes several blocks instead of
+// one heavy one), and the decode expand takes a whole block in one pass.
+constexpr int kDecodeBlockTokens = 4;
 constexpr int kLongGroup = 48;
+constexpr int kValuTokens = kDecodeBlockTokens;  // token slots of the decode expand
+constexpr int kDecodeRows = 256;             // decode expand: rows per wave per chunk
 constexpr int kTargetGroups = 1024;          // workgroups aimed for per launch (4 per CU)
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 // Activations and outputs are addressed through buffer resources whose
@@ -52,7 +58,7 @@ static_assert(sizeof(TileDesc) == 32, "TileDesc is 32 bytes");
 
 // Shrink: one workgroup per unit (rank tile, k-chunk c, projection i), unit
 // u = tile * nproj * c0 + c * nproj + i, so the projections that read the
-// same x chunk are consecutive; consecutive units are placed on one XCD.
+// same x chunk are consecutive and are placed on one XCD.
 // The 4 waves split the chunk's K range and are summed through LDS in a fixed
 // order; the unit writes one float32 partial tile [16 * TT token slots][16
 // ranks] at partial + u * TT * 256.
@@ -66,10 +72,11 @@ struct ShrinkArgs {
     int64_t coef_a[LORA_MAX_PROJ];  // A block offset = extent + r_pad * esize * coef_a[i]
     int32_t nproj;
     int32_t h_in;
+    int32_t h_in_pad;            // stored K: h_in rounded up to whole K-blocks
     int32_t kc;                  // k-chunk (elements): 4 waves x at most kShrinkFrags fragments
     int32_t c0;                  // number of k-chunks
     int32_t units;
-    int32_t grid;                // workgroups launched: units rounded up to kXcds
+    int32_t grid;                // workgroups launched: units rounded up to kXcds * nproj
     uint32_t x_bytes;            // buffer range (at most kMaxTensorBytes)
 };
 
@@ -90,8 +97,8 @@ struct ReduceArgs {
     int32_t r_max;
 };
 
-// Expand: one workgroup per unit (block b, projection i, chunk of 4 * ocw
-// output rows; ocw = 16 * expand_tiles(ks)).  Each wave first issues the
+// Expand: one workgroup per unit (block b, projection i, slice of 4 * ocw
+// output rows; ocw = chunks * 16 * expand_tiles(ks)).  Each wave first issues the
 // loads of all its B rows, then the workgroup gathers its tokens' v into LDS
 // once (summing the shrink partials in a fixed order, or reading a caller's
 // v), and each wave writes y = y_in + s * (B v), rounded once.
@@ -114,6 +121,7 @@ struct ExpandArgs {
     int32_t oc_prefix[LORA_MAX_PROJ + 1];  // row chunks of projections before i
     int32_t nb;                  // blocks launched over
     int32_t nproj;
+    int32_t chunks;              // row chunks per wave (16 * expand_tiles(ks) rows each)
     int32_t c0;                  // partial chunks (when partial != null)
     int32_t units;
     int32_t grid;
@@ -130,7 +138,12 @@ constexpr int expand_tiles(int ks) { return ks >= 8 ? 1 : 8 / ks; }
 // 16-token tiles of the largest block (1, 2 or 4); ks the K-steps of the
 // largest padded rank (bf16: 1 or 2, f32: 1, 2 or 4).
 hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s);
+// A [rank][h_in] row-major (device) -> K-blocked [h_in_pad / span][r_pad][span]
+hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
+                         int h_in_pad, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s);
+// decode expand (every block of the plan within one 16-token tile)
+hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s);
 
 }  // namespace lora

@@ -419,3 +419,28 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for k, v in dw.y.items():
             assert np.array_equal(from_device(v), eager[k]), (rep, k)
+
+
+def test_register_from_device_matches_host():
+    """lora_pool_register from device tensors (the K-blocking pack kernel) gives
+    the same pool, hence the same output bits, as uploads from host arrays."""
+    import heterogeneous_adapter_batching_amd as hab
+    from synth.device import to_device, host_weights
+    for dtype, h_in in (("bf16", 200), ("f32", 72), ("bf16", 4096)):
+        w = random_case(81, T=40, h_in=h_in, h_out=96, n_adapters=4, dtype=dtype,
+                        r_choices=[5, 16, 40, 64])
+        dw = DeviceWorkload(w, threads=2)
+        dw.run_fused()
+        ref = dw.output(0, 0)
+        pool2 = hab.Pool(1, [h_in], [96], w.r_max, dtype, max_slots=8,
+                         slab_bytes=dw.pool.slab.numel())
+        pool2.slab.fill_(0xFF)                   # NaN everywhere the pack must overwrite
+        for a in range(w.pool_size):
+            A, B = w.adapter_block(a, 0, 0)
+            pool2.register(a, int(w.ranks[a]), float(w.scales[a]),
+                           [to_device(A, dtype)[None]], [to_device(B, dtype)[None]])
+        plan2 = hab.Plan(pool2, w.num_tokens, w.seg_starts, w.seg_adapter).upload(1)
+        y2 = torch.zeros_like(dw.y[(0, 0)])
+        hab.sgmv_fused(pool2, plan2, 0, (0,), (0,), dw.x[(0, "x")], y2)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(y2), ref), dtype

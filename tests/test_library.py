@@ -190,8 +190,8 @@ def test_plan_matches_reference(seed):
     st = plan.stats()
     assert st["active_tokens"] == int((ref[1] >= 0).sum())
     sizes = np.bincount(ref[1][ref[1] >= 0], minlength=len(ref[2]))
-    # blocks of one 16-token tile, or of 64 tokens once some group has >= 48
-    bmax = 64 if len(sizes) and sizes.max() >= 48 else 16
+    # decode blocks of at most 4 tokens, or of 64 once some group has >= 48
+    bmax = 64 if len(sizes) and sizes.max() >= 48 else 4
     exp_blocks = int(sum(-(-n // bmax) for n in sizes)) + (-(-int((ref[1] < 0).sum()) // bmax))
     assert st["max_block_tokens"] <= bmax
     assert st["blocks"] == exp_blocks
