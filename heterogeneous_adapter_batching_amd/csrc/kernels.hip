@@ -195,31 +195,51 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     }
 }
 
-// partial tile of (rank tile, chunk, projection) for an adapter block
-__device__ __forceinline__ const float *partial_tile(const float *partial, int tt_tiles,
-                                                     int rt_before, int tile, int c, int p,
-                                                     int nproj, int c0) {
-    const int u = (rt_before + tile) * nproj * c0 + c * nproj + p;
-    return partial + size_t(u) * (tt_tiles * kTile * kTile);
+// Float offset of v entries (token slot `slot`, ranks j .. j + 3) of chunk 0
+// in the shrink's partials, and the stride between chunks.  Unit u = (rank
+// tile, chunk c, projection p) wrote tile u * ptt * 256: u = tile * nproj * c0
+// + c * nproj + p, token slot s and rank i at s * 16 + i.
+__device__ __forceinline__ uint32_t partial_off(int rt, int j, int slot, int p, int nproj, int c0,
+                                                int ptt) {
+    return uint32_t((rt + j / kTile) * nproj * c0 + p) * uint32_t(ptt * kTile * kTile) +
+           uint32_t(slot * kTile + j % kTile);
+}
+
+// The whole chunk sum in the one order: the ways, then ((s0 + s1) + s2) + s3.
+__device__ __forceinline__ f32x4 chunk_sum(rsrc_t pr, uint32_t off, uint32_t stride, int c0) {
+    f32x4 w[kSumWays];
+#pragma unroll
+    for (int k = 0; k < kSumWays; ++k) w[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < c0; c += 8) {
+        u32x4 part[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            part[g] = bload16(pr, off_or_oob(c + g < c0, (off + uint32_t(c + g) * stride) * 4));
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            if (c + g < c0) w[g % kSumWays] += __builtin_bit_cast(f32x4, part[g]);
+    }
+    f32x4 s = w[0];
+#pragma unroll
+    for (int k = 1; k < kSumWays; ++k) s += w[k];
+    return s;
 }
 
 // --------------------------------------------------------------- reduce -----
-// One workgroup per (adapter block, projection): v = sum of the chunk partials.
+// One workgroup per (expand block, projection): v = sum of the chunk partials.
 template <int TT>
 __global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
     const int bp = blockIdx.x;
     const int b = bp / a.nproj, p = bp % a.nproj;
     const BlockDesc blk = a.blocks[b];
+    const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
     const int quads = a.r_max / 4;
     for (int i = threadIdx.x; i < blk.n_tok * quads; i += blockDim.x) {
         const int ti = i / quads, j = (i % quads) * 4;
         f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (j < blk.r_pad) {
-            for (int c = 0; c < a.c0; ++c)
-                s4 += *reinterpret_cast<const f32x4 *>(
-                    partial_tile(a.partial, TT, blk.rt_before, j / kTile, c, p, a.nproj, a.c0) +
-                    ti * kTile + j % kTile);
-        }
+        if (j < blk.r_pad)
+            s4 = chunk_sum(pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, TT),
+                           uint32_t(a.nproj * TT * kTile * kTile), a.c0);
         const int t = a.tok[blk.tok_off + ti];
         *reinterpret_cast<f32x4 *>(a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j) = s4;
     }
@@ -329,31 +349,19 @@ template <> struct Out1<float> {
 };
 
 // v of the block's tokens into LDS, once per workgroup: from the shrink's
-// chunk partials (loaded 8 at a time, summed in chunk order) or a caller's v.
+// chunk partials (summed in the one chunk order) or a caller's v.
 template <int TT>
 __device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &blk, int p,
                                          float (*vs)[LORA_MAX_RANK + 4]) {
     const int quads = blk.r_pad / 4;
     if (a.partial) {
         const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
-        constexpr int GP = 8;
+        const uint32_t stride = uint32_t(a.nproj * TT * kTile * kTile);
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
             const int ti = i / quads, j = (i % quads) * 4;
-            const uint32_t base_f = uint32_t((blk.rt_before + j / kTile) * a.nproj * a.c0 + p) *
-                                        (TT * kTile * kTile) + ti * kTile + j % kTile;
-            const uint32_t stride_f = uint32_t(a.nproj) * (TT * kTile * kTile);
-            f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int c0 = 0; c0 < a.c0; c0 += GP) {
-                u32x4 part[GP];
-#pragma unroll
-                for (int g = 0; g < GP; ++g)
-                    part[g] = bload16(pr, off_or_oob(c0 + g < a.c0,
-                                                     (base_f + uint32_t(c0 + g) * stride_f) * 4));
-#pragma unroll
-                for (int g = 0; g < GP; ++g)
-                    if (c0 + g < a.c0) s4 += __builtin_bit_cast(f32x4, part[g]);
-            }
-            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = s4;
+            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = chunk_sum(
+                pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, TT), stride,
+                a.c0);
         }
     } else {
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
@@ -365,26 +373,111 @@ __device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &b
     }
 }
 
-// Decode expand on the vector ALUs (blocks of at most kValuTokens tokens):
-// each lane owns RPL output rows per step (rows lane + 64 i) and streams NV
-// 16-byte vectors of each (the B row: r_pad = NV * E values), dotting them
-// with every token's v (an LDS broadcast), in float32.  Every step issues
-// 8 B loads per lane (8 KB a wave) at once; other resident waves cover the
-// latency.
+// v of a decode block (at most kValuTokens tokens) into LDS, in two parts so
+// that its loads go out before the wave's B loads and its wait covers them
+// alone (a wave's loads complete in issue order).  From the shrink's
+// partials, thread (entry, way k) sums way k of the chunk sum of one v entry
+// (4 ranks of one token) and the ways are added in order through LDS: the
+// one chunk order.  Otherwise thread `entry` reads the entry from the
+// caller's v.
+struct VGather {
+    u32x4 part[4];       // chunks k, k + 4, k + 8, k + 12 of way k (or the caller's entry)
+    int e, k, ti, j;
+    bool on;
+};
+
+__device__ __forceinline__ void gather_issue(const ExpandArgs &a, const BlockDesc &blk,
+                                             const int (&tr)[kValuTokens], int p, VGather &g) {
+    const int quads = blk.r_pad / 4;                 // r_pad > 0
+    const int entries = blk.n_tok * quads;           // <= kValuTokens * 16 = 64
+    const int tid = int(threadIdx.x);
+    if (a.partial) {
+        g.k = tid % kSumWays;
+        g.e = tid / kSumWays;
+        g.on = g.e < entries;
+        g.ti = g.e / quads;
+        g.j = (g.e % quads) * 4;
+        const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
+        const uint32_t off = partial_off(blk.rt_before, g.j, blk.slot0 + g.ti, p, a.nproj, a.c0,
+                                         a.ptt);
+        const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = g.k + i * kSumWays;
+            g.part[i] = bload16(pr, off_or_oob(g.on && c < a.c0, (off + uint32_t(c) * stride) * 4));
+        }
+    } else {
+        g.k = 0;
+        g.e = tid;
+        g.on = tid < entries;
+        g.ti = g.on ? tid / quads : 0;
+        g.j = (tid % quads) * 4;
+        const rsrc_t vr = make_rsrc(a.v, a.v_bytes);
+        // the entry's token row by selects (an indexed private array would
+        // be placed in memory)
+        const int row = g.ti == 0 ? tr[0] : g.ti == 1 ? tr[1] : g.ti == 2 ? tr[2] : tr[3];
+        g.part[0] = bload16(vr, off_or_oob(g.on, uint32_t((int64_t(row) * a.ldv +
+                                                           int64_t(p) * a.r_max + g.j) * 4)));
+    }
+}
+
+__device__ __forceinline__ void gather_finish(const ExpandArgs &a, const BlockDesc &blk, int p,
+                                              const VGather &g, float (*vs)[LORA_MAX_RANK + 4],
+                                              f32x4 (*ways)[kSumWays]) {
+    const int quads = blk.r_pad / 4;
+    const int entries = blk.n_tok * quads;
+    const int tid = int(threadIdx.x);
+    if (a.partial) {
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (g.k + i * kSumWays < a.c0) s += __builtin_bit_cast(f32x4, g.part[i]);
+        if (a.c0 > 4 * kSumWays) {                   // the rest of the way, in order
+            const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
+            const uint32_t off = partial_off(blk.rt_before, g.j, blk.slot0 + g.ti, p, a.nproj,
+                                             a.c0, a.ptt);
+            const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
+            for (int c = g.k + 4 * kSumWays; c < a.c0; c += kSumWays)
+                s += __builtin_bit_cast(
+                    f32x4, bload16(pr, off_or_oob(g.on, (off + uint32_t(c) * stride) * 4)));
+        }
+        if (g.on) ways[g.e][g.k] = s;
+        __syncthreads();
+        if (tid < entries) {
+            const int ti = tid / quads, j = (tid % quads) * 4;
+            f32x4 s4 = ways[tid][0];
+#pragma unroll
+            for (int w = 1; w < kSumWays; ++w) s4 += ways[tid][w];
+            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = s4;
+        }
+    } else if (g.on) {
+        *reinterpret_cast<f32x4 *>(&vs[g.ti][g.j]) = __builtin_bit_cast(f32x4, g.part[0]);
+    }
+    __syncthreads();
+}
+
+// Decode expand on the vector ALUs, for one wave's slice [o_lo, o_hi) of a
+// unit: lane owns rows o_lo + lane + 64 i (i < RPL) and streams the NV
+// 16-byte vectors of each B row (r_pad = nv * E values, nv <= NV), dotting
+// them with every token's v (an LDS broadcast) in float32.  Loads go out in
+// the order they are used: the v gather, B vector by vector, then y_in; so
+// the dot products of the first vectors start while the rest arrive.
 template <typename T, int NV>
 __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
-                                            const ExpandCtx &c, float (*vs)[LORA_MAX_RANK + 4]) {
+                                            const int (&tr)[kValuTokens], int p, int o_lo,
+                                            int o_hi, float (*vs)[LORA_MAX_RANK + 4],
+                                            f32x4 (*ways)[kSumWays]) {
     constexpr int E = Elem<T>::E;
-    constexpr int RPL = NV >= 8 ? 1 : (NV >= 4 ? 2 : 4);   // rows per lane per step
+    constexpr int RPL = decode_rpl(NV);
     constexpr int NT = kValuTokens;
-    constexpr int STEP = RPL * kWaveSize;                  // rows per step
     const int lane = threadIdx.x & 63;
     const int nv = blk.r_pad / E;                    // wave-uniform, <= NV
     const int nt = blk.n_tok;                        // wave-uniform, <= NT
+    const int yoff = a.y_off[p];
     const rsrc_t br = make_rsrc(
         a.slab + extent(blk.ext_lo, blk.ext_hi) +
-            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[c.p]),
-        uint32_t(c.h_out) * uint32_t(blk.r_pad) * sizeof(T));
+            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
+        uint32_t(a.h_out[p]) * uint32_t(blk.r_pad) * sizeof(T));
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
     const int64_t ld_in = a.base ? a.ldb : a.ldy;
@@ -392,68 +485,66 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     uint32_t in_row[NT], y_row[NT];                  // wave-uniform token rows (byte offsets)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int tr = a.block_tok[c.b * kMaxBlockTokens + t];
-        const bool ok = t < nt && tr >= 0;
-        in_row[t] = ok ? uint32_t((int64_t(tr) * ld_in + c.yoff) * sizeof(T)) : kOOB;
-        y_row[t] = ok ? uint32_t((int64_t(tr) * a.ldy + c.yoff) * sizeof(T)) : kOOB;
+        const bool ok = t < nt && tr[t] >= 0;
+        in_row[t] = ok ? uint32_t((int64_t(tr[t]) * ld_in + yoff) * sizeof(T)) : kOOB;
+        y_row[t] = ok ? uint32_t((int64_t(tr[t]) * a.ldy + yoff) * sizeof(T)) : kOOB;
     }
 
-    u32x4 bv[RPL][NV];
-    float yin[RPL][NT];
-    auto load = [&](int r0) {
+    VGather g;
+    gather_issue(a, blk, tr, p, g);
+    u32x4 bv[NV][RPL];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            const int row = r0 + i * kWaveSize + lane;
-            const bool rok = row < c.o_hi;
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-                bv[i][v] = bload16_nt(br, off_or_oob(rok && v < nv,
-                                                     uint32_t(row) * row_bytes + v * 16));
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+            const int row = o_lo + i * kWaveSize + lane;
+            bv[v][i] = bload16_nt(br, off_or_oob(row < o_hi && v < nv,
+                                                 uint32_t(row) * row_bytes + v * 16));
         }
-    };
+    float yin[RPL][NT];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int row = o_lo + i * kWaveSize + lane;
+        const bool rok = row < o_hi;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+    }
+    gather_finish(a, blk, p, g, vs, ways);
 
-    load(c.o_lo);
-    gather_v<1>(a, blk, c.p, vs);
-    __syncthreads();
-    for (int r0 = c.o_lo; r0 < c.o_hi; r0 += STEP) {
-        if (r0 > c.o_lo) load(r0);
-        float d[RPL][NT];
+    float d[RPL][NT];
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
+    for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
+        for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            // a wave-uniform guard rather than a loop exit, so the loop
-            // unrolls fully and bv stays in registers
-            if (v < nv) {
-            // v is read from LDS per vector (a broadcast), not hoisted into
-            // NT * r_pad registers
+    for (int v = 0; v < NV; ++v) {
+        // a wave-uniform guard rather than a loop exit, so the loop unrolls
+        // fully and bv stays in registers
+        if (v < nv) {
+            // this vector's v of every token from LDS (broadcast reads, one
+            // wait), not all of v held in registers
             asm volatile("" ::: "memory");
             float w[NT][E];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int e = 0; e < E; e += 4) {
                     const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + e]);
                     w[t][e] = w4[0]; w[t][e + 1] = w4[1]; w[t][e + 2] = w4[2]; w[t][e + 3] = w4[3];
                 }
-            }
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 float f[E];
                 if constexpr (E == 8) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        f[2 * k] = bf16_lo(bv[i][v][k]);
-                        f[2 * k + 1] = bf16_hi(bv[i][v][k]);
+                        f[2 * k] = bf16_lo(bv[v][i][k]);
+                        f[2 * k + 1] = bf16_hi(bv[v][i][k]);
                     }
                 } else {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(bv[i][v][k]);
+                    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(bv[v][i][k]);
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
@@ -463,17 +554,17 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
                             d[i][t] = __builtin_fmaf(f[e], w[t][e], d[i][t]);
                     }
             }
-            }
         }
+    }
+    const float scale = blk.scale;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int row = r0 + i * kWaveSize + lane;
-            const bool rok = row < c.o_hi;
+    for (int i = 0; i < RPL; ++i) {
+        const int row = o_lo + i * kWaveSize + lane;
+        const bool rok = row < o_hi;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)           // y_row[t] is kOOB for t >= nt
-                Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
-                               yin[i][t] + c.scale * d[i][t]);
-        }
+        for (int t = 0; t < NT; ++t)                 // y_row[t] is kOOB for t >= nt
+            Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
+                           yin[i][t] + scale * d[i][t]);
     }
 }
 
@@ -619,58 +710,69 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
     }
 }
 
-// Decode expand: plans whose blocks hold at most kValuTokens tokens.  Same
-// units and row slices as k_expand; the B row length picks the vector count.
+// Decode expand: plans whose blocks hold at most kValuTokens tokens.  A
+// unit is (block, projection, kWaves slices of decode_wave_rows rows); the
+// blocks are ordered by padded rank, and a unit's rank class, block,
+// projection and slice follow from the kernel arguments alone, so the first
+// loads are the block's descriptor and token rows (one round trip).
 template <typename T>
 __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
-    constexpr int E = Elem<T>::E;
     constexpr int VS = LORA_MAX_RANK + 4;
     __shared__ float vs[kValuTokens][VS];
+    __shared__ f32x4 ways[kValuTokens * LORA_MAX_RANK / 4][kSumWays];
 
     const int u = xcd_unit(1);
     if (u >= a.units) return;                        // whole workgroup
-    const int lane = threadIdx.x & 63;
-    ExpandCtx c;
-    c.w = wave_id();
-    c.n = lane & 15;
-    c.q = lane >> 4;
-    const int upb = a.oc_prefix[a.nproj];
-    c.b = u / upb;
-    const int rem = u - c.b * upb;
-    c.p = 0;
-    while (rem >= a.oc_prefix[c.p + 1]) ++c.p;
-    const int oc = rem - a.oc_prefix[c.p];
-    const BlockDesc blk = a.blocks[c.b];
-    c.h_out = a.h_out[c.p];
-    const int rows_w = a.chunks * kDecodeRows;       // rows of this wave
-    c.o_lo = min(c.h_out, (oc * kWaves + c.w) * rows_w);
-    c.o_hi = min(c.h_out, c.o_lo + rows_w);
-    c.yoff = a.y_off[c.p];
-    c.scale = blk.scale;
+    int k = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxClasses; ++i) k += u >= a.cls_unit0[i];
+    const DecodeClass &dc = a.cls[k];                // kernel-argument loads, no copy
+    const int ur = u - a.cls_unit0[k];
+    const int upb = dc.upb;
+    const int b = dc.block0 + ur / upb;
+    const int rem = ur - (ur / upb) * upb;
+    int p = 0, first = 0;                            // projection and its first unit
+#pragma unroll
+    for (int i = 1; i < LORA_MAX_PROJ; ++i) {
+        const int pi = dc.prefix[i];
+        if (rem >= pi) { p = i; first = pi; }
+    }
+    const int slice = rem - first;
+    const int r_pad = dc.rpad;
 
-    if (blk.r_pad == 0) {            // tokens without an adapter: y = base, 4 outputs a lane
+    const BlockDesc blk = a.blocks[b];
+    const int4 bt4 = *reinterpret_cast<const int4 *>(a.block_tok + b * kMaxBlockTokens);
+    const int tr[kValuTokens] = {bt4.x, bt4.y, bt4.z, bt4.w};
+    static_assert(kValuTokens == 4, "token rows load as one int4");
+
+    const int h_out = a.h_out[p];
+    const int wrows = decode_wave_rows(r_pad, sizeof(T));
+    const int o_lo = min(h_out, (slice * kWaves + wave_id()) * wrows);
+    const int o_hi = min(h_out, o_lo + wrows);
+
+    if (r_pad == 0) {                // tokens without an adapter: y = base, 4 outputs a lane
         if (!a.base) return;
         const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
         const rsrc_t br = make_rsrc(a.base, a.base_bytes);
-        for (int t = 0; t < blk.n_tok; ++t) {
-            const int tr = a.block_tok[c.b * kMaxBlockTokens + t];
-            for (int o = c.o_lo + 4 * lane; o < c.o_hi; o += 4 * kWaveSize) {
-                const auto v4 = Out4<T>::load(
-                    br, uint32_t((int64_t(tr) * a.ldb + c.yoff + o) * sizeof(T)));
-                Out4<T>::store(yr, uint32_t((int64_t(tr) * a.ldy + c.yoff + o) * sizeof(T)), v4);
-            }
+        const int o = o_lo + 4 * (threadIdx.x & 63);
+        const int yoff = a.y_off[p];
+#pragma unroll
+        for (int t = 0; t < kValuTokens; ++t) {
+            const bool ok = t < blk.n_tok && o < o_hi;
+            const auto v4 = Out4<T>::load(
+                br, ok ? uint32_t((int64_t(tr[t]) * a.ldb + yoff + o) * sizeof(T)) : kOOB);
+            Out4<T>::store(yr, ok ? uint32_t((int64_t(tr[t]) * a.ldy + yoff + o) * sizeof(T)) : kOOB,
+                           v4);
         }
         return;
     }
-    const int nv = blk.r_pad / E;
-    if (nv <= 1) return expand_valu<T, 1>(a, blk, c, vs);
-    if (nv <= 2) return expand_valu<T, 2>(a, blk, c, vs);
-    if (nv <= 4) return expand_valu<T, 4>(a, blk, c, vs);
-    if constexpr (E == 8) {
-        return expand_valu<T, 8>(a, blk, c, vs);
-    } else {
-        if (nv <= 8) return expand_valu<T, 8>(a, blk, c, vs);
-        return expand_valu<T, 16>(a, blk, c, vs);
+    switch (decode_nvt(r_pad, sizeof(T))) {
+    case 1: return expand_valu<T, 1>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: return expand_valu<T, 2>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 4: return expand_valu<T, 4>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 8: return expand_valu<T, 8>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    default:
+        if constexpr (sizeof(T) == 4) return expand_valu<T, 16>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 

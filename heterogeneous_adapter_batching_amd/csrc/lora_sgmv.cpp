@@ -443,57 +443,79 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
     for (int32_t t = 0; t < T; ++t)
         if (pl->token_group[t] < 0) idle.push_back(t);
 
-    // blocks: each group cut into near-equal blocks of at most `bmax` tokens:
-    // 16 (one token tile) unless a group is long enough to be prefill-like
+    // Two levels of blocks.  Shrink blocks: each group cut into near-equal
+    // blocks of at most one 16-token tile (64 tokens, 4 tiles, once some
+    // group has kLongGroup tokens); the shrink reads the adapter's A once per
+    // shrink block and per 16-rank tile of it (the rank tiles are its units).
+    // Expand blocks: in a decode-like batch each shrink block is cut again
+    // into near-equal blocks of at most kDecodeBlockTokens tokens, so that
+    // the expand's units move about the same bytes whatever a group's size;
+    // otherwise they are the shrink blocks.  An expand block names its shrink
+    // block's first rank tile and its first token slot in it.
     size_t longest = 0;
     for (auto &m : members) longest = std::max(longest, m.size());
-    const int32_t bmax = longest >= size_t(lora::kLongGroup) ? lora::kMaxBlockTokens
-                                                             : lora::kDecodeBlockTokens;
-    auto add_blocks = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
-        const int32_t n = int32_t(toks.size());
-        const int32_t nblk = (n + bmax - 1) / bmax;
-        int32_t start = 0;
-        for (int32_t i = 0; i < nblk; ++i) {
-            const int32_t cnt = n / nblk + (i < n % nblk ? 1 : 0);
-            BlockDesc bd{};
-            bd.tok_off = int32_t(pl->token_order.size()) + start;
-            bd.n_tok = cnt;
-            bd.r_pad = sl ? sl->r_pad : 0;
-            bd.rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
-            bd.scale = sl ? sl->scale : 0.f;
-            bd.rt_before = 0;
-            (void)g;
-            bd.ext_lo = sl ? uint32_t(sl->off & 0xffffffffu) : 0u;
-            bd.ext_hi = sl ? uint32_t(sl->off >> 32) : 0u;
-            pl->blocks.push_back(bd);
-            pl->max_block = std::max(pl->max_block, cnt);
-            start += cnt;
+    const bool prefill = longest >= size_t(lora::kLongGroup);
+    const int32_t smax = prefill ? lora::kMaxBlockTokens : lora::kTile;
+    const int32_t emax = prefill ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
+    auto cut = [](int32_t n, int32_t m, std::vector<int32_t> *sizes) {
+        sizes->clear();
+        const int32_t k = (n + m - 1) / m;
+        for (int32_t i = 0; i < k; ++i) sizes->push_back(n / k + (i < n % k ? 1 : 0));
+    };
+    int32_t max_sblock = 0;
+    std::vector<int32_t> ssz, esz;
+    auto add_group = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
+        const int32_t base = int32_t(pl->token_order.size());
+        const int32_t rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
+        cut(int32_t(toks.size()), smax, &ssz);
+        int32_t s0 = 0;
+        for (int32_t sn : ssz) {
+            const int32_t rt_before = int32_t(pl->tiles.size());
+            for (int32_t i = 0; i < rt; ++i) {
+                lora::TileDesc td{};
+                td.tok_off = base + s0;
+                td.n_tok = sn;
+                td.r_pad = sl->r_pad;
+                td.tile = i;
+                td.block = g;
+                td.ext_lo = uint32_t(sl->off & 0xffffffffu);
+                td.ext_hi = uint32_t(sl->off >> 32);
+                pl->tiles.push_back(td);
+            }
+            max_sblock = std::max(max_sblock, sn);
+            cut(sn, emax, &esz);
+            int32_t e0 = 0;
+            for (int32_t en : esz) {
+                BlockDesc bd{};
+                bd.tok_off = base + s0 + e0;
+                bd.n_tok = en;
+                bd.r_pad = sl ? sl->r_pad : 0;
+                bd.slot0 = e0;
+                bd.scale = sl ? sl->scale : 0.f;
+                bd.rt_before = rt_before;
+                bd.ext_lo = sl ? uint32_t(sl->off & 0xffffffffu) : 0u;
+                bd.ext_hi = sl ? uint32_t(sl->off >> 32) : 0u;
+                pl->blocks.push_back(bd);
+                pl->max_block = std::max(pl->max_block, en);
+                e0 += en;
+            }
+            s0 += sn;
         }
         pl->token_order.insert(pl->token_order.end(), toks.begin(), toks.end());
     };
     for (int32_t g = 0; g < int32_t(members.size()); ++g)
-        add_blocks(members[g], g, &p->slots.at(pl->group_adapter[g]));
+        add_group(members[g], g, &p->slots.at(pl->group_adapter[g]));
     pl->nb_act = int32_t(pl->blocks.size());
     pl->n_active = int32_t(pl->token_order.size());
-    add_blocks(idle, -1, nullptr);
-
-    for (int32_t b = 0; b < pl->nb_act; ++b) {
-        BlockDesc &bd = pl->blocks[b];
-        bd.rt_before = int32_t(pl->tiles.size());
-        pl->max_rpad = std::max(pl->max_rpad, bd.r_pad);
-        for (int32_t i = 0; i < bd.rt; ++i) {
-            lora::TileDesc td{};
-            td.tok_off = bd.tok_off;
-            td.n_tok = bd.n_tok;
-            td.r_pad = bd.r_pad;
-            td.tile = i;
-            td.block = b;
-            td.ext_lo = bd.ext_lo;
-            td.ext_hi = bd.ext_hi;
-            pl->tiles.push_back(td);
-        }
-    }
-    const int32_t tiles = (pl->max_block + lora::kTile - 1) / lora::kTile;
+    add_group(idle, -1, nullptr);
+    // The expand visits the adapter blocks by padded rank, largest first
+    // (stable within a rank): its units are equal in bytes within a rank, the
+    // costliest are dealt first, and the rank is uniform over a range of units.
+    std::stable_sort(pl->blocks.begin(), pl->blocks.begin() + pl->nb_act,
+                     [](const BlockDesc &x, const BlockDesc &y) { return x.r_pad > y.r_pad; });
+    for (int32_t b = 0; b < pl->nb_act; ++b)
+        pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
+    const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
     *out = pl;
     return LORA_OK;
@@ -573,10 +595,12 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
                     i < bd.n_tok ? pl->token_order[bd.tok_off + i] : -1;
         }
         int32_t *tt = reinterpret_cast<int32_t *>(img + pl->off_ttok);
-        for (int32_t k = 0; k < pl->rt_total(); ++k)
-            std::memcpy(tt + k * lora::kMaxBlockTokens,
-                        bt + pl->tiles[k].block * lora::kMaxBlockTokens,
-                        4ull * lora::kMaxBlockTokens);
+        for (int32_t k = 0; k < pl->rt_total(); ++k) {
+            const lora::TileDesc &td = pl->tiles[k];
+            for (int32_t i = 0; i < lora::kMaxBlockTokens; ++i)
+                tt[k * lora::kMaxBlockTokens + i] =
+                    i < td.n_tok ? pl->token_order[td.tok_off + i] : -1;
+        }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     e = hipMemcpyAsync(ws, img, pl->image_bytes, hipMemcpyHostToDevice, st);
@@ -733,6 +757,7 @@ lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, i
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
     a.partial = reinterpret_cast<const float *>(ws + pl->off_part);
+    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->part_bytes, lora::kMaxTensorBytes));
     a.v = v;
     a.ldv = ldv;
     a.nb = pl->nb_act;
@@ -780,29 +805,62 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         a.h_out[i] = p->d.h_out[projs[i]];
         a.y_off[i] = yoff[i];
     }
-    // K-steps of the largest padded rank fix the rows per wave (the wave
-    // keeps 8 B fragments); 4 waves per workgroup
-    const int32_t ks = plan_ksteps(p, pl);
-    const bool decode = pl->max_block <= lora::kValuTokens;   // blocks of the decode expand
-    // row chunks per wave: about kTargetGroups workgroups per launch
-    const int64_t chunk_rows = int64_t(decode ? lora::kDecodeRows : 16 * lora::expand_tiles(ks)) *
-                               lora::kWaves;
-    int64_t rows = 0;
-    for (int i = 0; i < nproj; ++i) rows += a.h_out[i];
-    a.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
-        8, rows * nb / (chunk_rows * lora::kTargetGroups))));
-    const int32_t rows_per_group = int32_t(chunk_rows) * a.chunks;
-    a.oc_prefix[0] = 0;
-    for (int i = 0; i < nproj; ++i)
-        a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
-    for (int i = nproj; i < LORA_MAX_PROJ; ++i) a.oc_prefix[i + 1] = INT32_MAX;
     a.nb = nb;
     a.nproj = nproj;
-    a.units = nb * a.oc_prefix[nproj];
-    a.grid = grid_for(a.units, 1);
     a.r_max = p->d.r_max;
+    a.ptt = pl->tt;
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
+    a.v_bytes = v ? uint32_t(tensor_bytes(pl->T, ldv, ldv, 4)) : 0u;
+    const bool decode = pl->max_block <= lora::kValuTokens;   // blocks of the decode expand
+    const int32_t ks = plan_ksteps(p, pl);
+    if (decode) {
+        // rank classes: runs of equal padded rank in block order (adapter
+        // blocks by rank, largest first; then the blocks without an adapter)
+        for (int k = 0; k < lora::kMaxClasses; ++k) {
+            lora::DecodeClass &dc = a.cls[k];
+            dc.block0 = dc.upb = dc.rpad = INT32_MAX;
+            for (int i = 0; i <= LORA_MAX_PROJ; ++i) dc.prefix[i] = INT32_MAX;
+        }
+        int32_t ncls = 0, units = 0;
+        for (int32_t b = 0; b < nb;) {
+            const int32_t r = pl->blocks[b].r_pad;
+            int32_t e = b;
+            while (e < nb && pl->blocks[e].r_pad == r) ++e;
+            if (ncls == lora::kMaxClasses)
+                return fail(LORA_ESTATE, "more than %d rank classes", lora::kMaxClasses);
+            const int32_t rows = lora::kWaves * lora::decode_wave_rows(r, esize(p->d.dtype));
+            lora::DecodeClass &dc = a.cls[ncls];
+            dc.rpad = r;
+            dc.block0 = b;
+            dc.prefix[0] = 0;
+            for (int i = 0; i < nproj; ++i)
+                dc.prefix[i + 1] = dc.prefix[i] + (a.h_out[i] + rows - 1) / rows;
+            dc.upb = dc.prefix[nproj];
+            a.cls_unit0[ncls] = units;
+            units += (e - b) * dc.upb;
+            ++ncls;
+            b = e;
+        }
+        for (int k = ncls; k <= lora::kMaxClasses; ++k) a.cls_unit0[k] = k == ncls ? units : INT32_MAX;
+        a.units = units;
+    } else {
+        // K-steps of the largest padded rank fix the rows per wave (the wave
+        // keeps 8 B fragments); 4 waves per workgroup; row chunks per wave:
+        // about kTargetGroups workgroups per launch
+        const int64_t chunk_rows = int64_t(16 * lora::expand_tiles(ks)) * lora::kWaves;
+        int64_t rows = 0;
+        for (int i = 0; i < nproj; ++i) rows += a.h_out[i];
+        a.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
+            8, rows * nb / (chunk_rows * lora::kTargetGroups))));
+        const int32_t rows_per_group = int32_t(chunk_rows) * a.chunks;
+        a.oc_prefix[0] = 0;
+        for (int i = 0; i < nproj; ++i)
+            a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
+        for (int i = nproj; i < LORA_MAX_PROJ; ++i) a.oc_prefix[i + 1] = INT32_MAX;
+        a.units = nb * a.oc_prefix[nproj];
+    }
+    a.grid = grid_for(a.units, 1);
     hipError_t e = decode ? lora::launch_expand_decode(p->d.dtype, a, st)
                           : lora::launch_expand(p->d.dtype, pl->tt, ks, a, st);
     if (e != hipSuccess) return hip_fail(e, "expand launch");
@@ -845,6 +903,8 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
     if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
+    if (tensor_bytes(pl->T, ldv, ldv, 4) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "v spans more than 2 GiB");
     st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
     return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,

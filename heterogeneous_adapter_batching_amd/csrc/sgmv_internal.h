@@ -21,35 +21,42 @@ constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 toke
 constexpr int kDecodeBlockTokens = 4;
 constexpr int kLongGroup = 48;
 constexpr int kValuTokens = kDecodeBlockTokens;  // token slots of the decode expand
-constexpr int kDecodeRows = 256;             // decode expand: rows per wave per chunk
+// The shrink's chunk partials of one v entry are summed as kSumWays
+// interleaved running sums (chunk c into sum c % kSumWays, in increasing c),
+// then added in order: every kernel that sums them uses this one order.
+constexpr int kSumWays = 4;
+// rank classes of the decode expand: distinct padded ranks (multiples of 8)
+// of the blocks, and 0 for tokens without an adapter
+constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
 constexpr int kTargetGroups = 1024;          // workgroups aimed for per launch (4 per CU)
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 // Activations and outputs are addressed through buffer resources whose
 // out-of-range offset is 2^31: each such tensor spans at most 2 GiB.
 constexpr uint64_t kMaxTensorBytes = 1ull << 31;
 
-// One token block of one adapter group (or of the tokens without an adapter).
+// One expand block: tokens of one adapter group (or tokens without an
+// adapter) that share one pass over the adapter's B rows.
 struct BlockDesc {
     int32_t tok_off;   // first entry of the block in the plan's token order
     int32_t n_tok;     // 1 .. kMaxBlockTokens
     int32_t r_pad;     // padded rank; 0 marks a block of tokens without an adapter
-    int32_t rt;        // rank tiles of 16 rows: ceil(r_pad / 16)
+    int32_t slot0;     // token slot of its first token in its shrink block's partials
     float scale;       // the adapter's scale
-    int32_t rt_before; // rank tiles of the adapter blocks before this one
+    int32_t rt_before; // first rank tile of its shrink block (index into the tiles)
     uint32_t ext_lo;   // adapter extent byte offset in the slab, low and high words
     uint32_t ext_hi;
 };
 static_assert(sizeof(BlockDesc) == 32, "BlockDesc is 32 bytes");
 
-// One rank tile (16 rows of A) of one adapter block: the shrink's unit of
+// One rank tile (16 rows of A) of one shrink block: the shrink's unit of
 // equal adapter bytes, whatever the adapter's rank.  tiles[rt_before + i] is
-// tile i of a block.
+// tile i of a shrink block; its token rows are those of the shrink block.
 struct TileDesc {
     int32_t tok_off;
     int32_t n_tok;
     int32_t r_pad;
     int32_t tile;      // rank tile index within the block
-    int32_t block;     // block index
+    int32_t block;     // group index
     int32_t pad1;
     uint32_t ext_lo;
     uint32_t ext_hi;
@@ -89,6 +96,7 @@ struct ReduceArgs {
     const int32_t *tok;
     const BlockDesc *blocks;
     const float *partial;
+    uint32_t partial_bytes;
     float *v;
     int64_t ldv;
     int32_t nb;
@@ -96,6 +104,18 @@ struct ReduceArgs {
     int32_t c0;
     int32_t r_max;
 };
+
+// A rank class of the decode expand: blocks [block0, block0 + n) with padded
+// rank rpad; upb units per block, of which projection i of the call has
+// units [prefix[i], prefix[i + 1]) (prefix[0] = 0; entries past the call's
+// projections are INT32_MAX).  48 bytes: one scalar load.
+struct DecodeClass {
+    int32_t block0;
+    int32_t upb;
+    int32_t rpad;
+    int32_t prefix[LORA_MAX_PROJ + 1];
+};
+static_assert(sizeof(DecodeClass) == 48, "DecodeClass is 48 bytes");
 
 // Expand: one workgroup per unit (block b, projection i, slice of 4 * ocw
 // output rows; ocw = chunks * 16 * expand_tiles(ks)).  Each wave first issues the
@@ -123,12 +143,34 @@ struct ExpandArgs {
     int32_t nproj;
     int32_t chunks;              // row chunks per wave (16 * expand_tiles(ks) rows each)
     int32_t c0;                  // partial chunks (when partial != null)
+    int32_t ptt;                 // 16-token tiles per shrink partial tile
     int32_t units;
     int32_t grid;
     int32_t r_max;
     uint32_t y_bytes;            // buffer ranges (each at most kMaxTensorBytes)
     uint32_t base_bytes;
+    uint32_t v_bytes;            // range of a caller's v (when partial == null)
+    // Decode expand: units by rank class; class k has units [cls_unit0[k],
+    // cls_unit0[k + 1]) (unused entries INT32_MAX) and the record cls[k].
+    int32_t cls_unit0[kMaxClasses + 1];
+    DecodeClass cls[kMaxClasses];
 };
+
+// Decode expand geometry.  A B row of r_pad elements is nv 16-byte vectors;
+// the kernel is built for nvt = nv rounded up to a power of two, and a lane
+// owns decode_rpl(nvt) rows of a step, so that one step of a wave streams
+// about 8 KB of B whatever the rank (4 KB at the smallest rank).  A wave's slice of a unit is one step;
+// a unit is kWaves slices.  Tokens without an adapter (r_pad 0) are copied
+// 4 outputs a lane.
+constexpr int decode_nvt(int r_pad, int esize) {
+    int nv = (r_pad * esize + 15) / 16, t = 1;
+    while (t < nv) t *= 2;
+    return t;
+}
+constexpr int decode_rpl(int nvt) { return nvt >= 8 ? 1 : nvt >= 2 ? 8 / nvt : 4; }
+constexpr int decode_wave_rows(int r_pad, int esize) {
+    return r_pad == 0 ? 4 * kWaveSize : decode_rpl(decode_nvt(r_pad, esize)) * kWaveSize;
+}
 
 // 16-row output tiles per expand wave, for kernels built for `ks` K-steps
 // (ranks / (4 fragment elements)) at most: the wave keeps 8 B fragments.
@@ -143,7 +185,7 @@ hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *d
                          int h_in_pad, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s);
-// decode expand (every block of the plan within one 16-token tile)
+// decode expand (every block of the plan within kValuTokens tokens)
 hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s);
 
 }  // namespace lora

@@ -1,0 +1,155 @@
+"""Summaries of rocprofv3 output for the kernels of this library.
+
+Two jobs, both on CSV files that ``rocprofv3 --output-format csv`` writes:
+
+* ``stats``: the per-kernel table of a ``--kernel-trace --stats`` run
+  (``*_kernel_stats.csv``), reduced to a short text summary.
+* ``traffic``: HBM bytes per launch of one kernel from two ``--pmc`` runs,
+  one with ``FETCH_SIZE`` and one with ``WRITE_SIZE`` (both KiB per
+  dispatch).  Each counter is scaled by what it reads for a plain device copy
+  of known size in the same run (a copy of N bytes reads N and writes N), so
+  the figure is in the copy's bytes.  The result is stored with a hash of the
+  kernel sources; a reader that finds a different hash treats it as absent.
+
+Usage::
+
+    python -m heterogeneous_adapter_batching_amd.profiling stats CSV --command CMD --out TXT
+    python -m heterogeneous_adapter_batching_amd.profiling traffic --fetch CSV --write CSV \\
+        --workload NAME --kernel K --copy-bytes N --json OUT --out TXT --command CMD ...
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_SOURCES = ("kernels.hip", "lora_sgmv.cpp", "sgmv_internal.h")
+_COPY = re.compile(r"copyBuffer")
+
+
+def source_hash() -> str:
+    """Hash of the kernel and launcher sources the counters were taken on."""
+    h = hashlib.sha256()
+    for f in _SOURCES:
+        with open(os.path.join(ROOT, "heterogeneous_adapter_batching_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    """Kernel name without namespaces, arguments or template arguments."""
+    n = re.sub(r"lora::\(anonymous namespace\)::", "", name.replace("void ", ""))
+    n = re.sub(r"\(.*", "", n)
+    return n.strip()
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        rd = csv.DictReader(f)
+        for r in rd:
+            yield {k.strip().lower(): v for k, v in r.items() if k}
+
+
+def kernel_stats(path: str, command: str, limit: int = 12) -> str:
+    rows = list(_rows(path))
+    rows.sort(key=lambda r: -float(r.get("totaldurationns", 0)))
+    out = ["# rocprofv3 --kernel-trace --stats", f"command: {command}", "",
+           f"{'kernel':60s} {'calls':>6s} {'avg_us':>9s} {'min_us':>8s} {'max_us':>8s} {'pct':>6s}"]
+    for r in rows[:limit]:
+        out.append(f"{r['name'][:60]:60s} {int(r['calls']):6d} "
+                   f"{float(r['averagens']) / 1e3:9.2f} {float(r['minns']) / 1e3:8.2f} "
+                   f"{float(r['maxns']) / 1e3:8.2f} {float(r['percentage']):6.2f}")
+    return "\n".join(out) + "\n"
+
+
+def _counter(path: str, counter: str):
+    """{dispatch id: (kernel name, grid size, value)} for one counter."""
+    per = defaultdict(float)
+    meta = {}
+    for r in _rows(path):
+        if r.get("counter_name", "").strip() != counter:
+            continue
+        d = int(r["dispatch_id"])
+        per[d] += float(r["counter_value"])
+        meta[d] = (r["kernel_name"], int(r.get("grid_size", 0) or 0))
+    return {d: (meta[d][0], meta[d][1], v) for d, v in per.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int):
+    """Per-launch fetch and write bytes of `kernel` (short name; a '+' joins
+    kernels launched together, whose sums are added), scaled by the copy."""
+    res = {}
+    for tag, path, cname in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        disp = _counter(path, cname)
+        copies = [v for (n, g, v) in disp.values() if _COPY.search(n)]
+        # the calibration copy is the largest copy dispatch of the run
+        ref = max(copies) if copies else 0.0
+        factor = copy_bytes / (ref * 1024.0) if ref > 0 else None
+        total = 0.0
+        for part in kernel.split("+"):
+            vals = [v for (n, g, v) in disp.values() if short_name(n).split("<")[0] == part]
+            if not vals:
+                raise SystemExit(f"no dispatch of {part} in {path}")
+            total += sum(vals) / len(vals)
+        res[tag] = {"kib_per_launch": total, "copy_kib": ref, "factor": factor,
+                    "bytes_per_launch": total * 1024.0 * factor if factor else None,
+                    "dispatches": len([1 for (n, g, v) in disp.values()
+                                       if short_name(n).split("<")[0] in kernel.split("+")])}
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--kernel", action="append", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", action="append", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        with open(a.out, "w") as f:
+            f.write(kernel_stats(a.csv, a.command))
+        return
+    try:
+        with open(a.json) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    lines = ["# HBM traffic per launch from rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE)"]
+    lines += [f"command: {c}" for c in a.command]
+    lines.append(f"calibration: a device copy of {a.copy_bytes} bytes (reads and writes that many)")
+    for k in a.kernel:
+        r = traffic(a.fetch, a.write, k, a.copy_bytes)
+        fb, wb = r["fetch"]["bytes_per_launch"], r["write"]["bytes_per_launch"]
+        ent = {"bytes_per_launch": (fb + wb) if fb is not None and wb is not None else None,
+               "fetch_bytes": fb, "write_bytes": wb,
+               "fetch_factor": r["fetch"]["factor"], "write_factor": r["write"]["factor"],
+               "source_hash": source_hash()}
+        data.setdefault(a.workload, {})[k] = ent
+        lines.append(f"{a.workload} {k}: fetch {r['fetch']['kib_per_launch']:.1f} KiB x "
+                     f"{r['fetch']['factor']:.4f}, write {r['write']['kib_per_launch']:.1f} KiB x "
+                     f"{r['write']['factor']:.4f} -> {ent['bytes_per_launch'] / 1e6:.3f} MB per launch "
+                     f"({r['fetch']['dispatches']} dispatches; copy read {r['fetch']['copy_kib']:.0f} "
+                     f"KiB, wrote {r['write']['copy_kib']:.0f} KiB)")
+    with open(a.json, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -190,10 +190,22 @@ def test_plan_matches_reference(seed):
     st = plan.stats()
     assert st["active_tokens"] == int((ref[1] >= 0).sum())
     sizes = np.bincount(ref[1][ref[1] >= 0], minlength=len(ref[2]))
-    # decode blocks of at most 4 tokens, or of 64 once some group has >= 48
-    bmax = 64 if len(sizes) and sizes.max() >= 48 else 4
-    exp_blocks = int(sum(-(-n // bmax) for n in sizes)) + (-(-int((ref[1] < 0).sum()) // bmax))
-    assert st["max_block_tokens"] <= bmax
+    # shrink blocks: near-equal cuts of each group into at most 16 tokens,
+    # each cut again into near-equal expand blocks of at most 4 tokens; both
+    # levels 64 tokens once some group has >= 48
+    prefill = len(sizes) and sizes.max() >= 48
+    smax, emax = (64, 64) if prefill else (16, 4)
+
+    def cut(n, m):
+        k = -(-n // m)
+        return [n // k + (i < n % k) for i in range(k)]
+
+    def n_expand_blocks(n):
+        return sum(len(cut(sn, emax)) for sn in cut(n, smax)) if n else 0
+
+    exp_blocks = sum(n_expand_blocks(int(n)) for n in sizes) + n_expand_blocks(
+        int((ref[1] < 0).sum()))
+    assert st["max_block_tokens"] <= emax
     assert st["blocks"] == exp_blocks
 
 
