@@ -85,25 +85,30 @@ def traffic_from_profile(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(w, blocks, layers, threads):
-    """Time the oracle (as it is) on the host for the sampled layers."""
+def cpu_baseline(w, blocks, layers, threads, min_seconds):
+    """Time the oracle (as it is) on the host: whole passes over the sampled
+    layers, repeated until at least `min_seconds` of oracle time."""
     import oracle
-    t_total = 0.0
+    inputs = []
     for l in layers:
         for p, pr in enumerate(w.projs):
             adapters = {a: (blocks[(a, l, p)][0], blocks[(a, l, p)][1], float(w.scales[a]))
                         for a in w.touched()}
-            x = w.activation(l, pr.x_key)
-            y_in = w.base_out(l, p) if w.has_base else None
+            inputs.append((w.activation(l, pr.x_key), adapters,
+                           w.base_out(l, p) if w.has_base else None))
+    t_total, passes = 0.0, 0
+    while passes == 0 or t_total < min_seconds:
+        for x, adapters, y_in in inputs:
             t0 = time.perf_counter()
             oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, threads=threads)
             t_total += time.perf_counter() - t0
+        passes += 1
     frac = len(layers) / w.num_layers
-    return {"value": w.num_tokens * frac / t_total, "unit": "tokens/s", "cores": threads,
+    return {"value": passes * w.num_tokens * frac / t_total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(layers)} of {w.num_layers} layers x {len(w.projs)} projections, "
-                      f"all {w.num_tokens} tokens, float32 oracle, {threads} OpenMP threads, "
-                      f"{t_total:.2f} s"}
+            "sample": f"{passes} passes over {len(layers)} of {w.num_layers} layers x "
+                      f"{len(w.projs)} projections, all {w.num_tokens} tokens, float32 oracle, "
+                      f"{threads} OpenMP threads, {t_total:.2f} s"}
 
 
 def main():
@@ -117,6 +122,8 @@ def main():
                     help="layers of the CPU-oracle sample (-1: all, 0: skip)")
     ap.add_argument("--kernel-reps", type=int, default=5,
                     help="event-timed passes for the per-kernel roofline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum oracle time of the CPU baseline")
     ap.add_argument("--copy-mib", type=int, default=2048,
                     help="size of the device-copy bandwidth reference (0: skip)")
     args = ap.parse_args()
@@ -199,10 +206,12 @@ def main():
         torch.cuda.synchronize()
     eager_ms = e2.elapsed_time(e3) / max(3, args.steps // 5)
 
-    # per-kernel durations on the launch stream: every call's standalone
-    # expand (one kernel, reading v) launched back to back between two events,
-    # and likewise every call's standalone shrink (the shrink kernel plus the
-    # small kernel that sums its partials into v)
+    # per-kernel durations on the launch stream, each over every call's
+    # launches back to back between two events: the fused call (shrink
+    # kernel + expand kernel), the standalone expand (one kernel, reading v)
+    # and the standalone shrink (shrink kernel + the small kernel that sums
+    # its partials into v).  The shrink kernel's time is the fused call's
+    # less the expand's.
     v = torch.zeros((w.num_tokens, dw.max_proj * w.r_max), dtype=torch.float32, device="cuda")
     n_launch = len(dw.layers) * len(dw.calls)
 
@@ -210,14 +219,18 @@ def main():
         for l in dw.layers:
             for ci, c in enumerate(dw.calls):
                 vv = v[:, :len(c) * w.r_max]
-                if kind == "shrink":
-                    hab.sgmv_shrink(dw.pool, dw.plan, l, c, dw.x[(l, w.projs[c[0]].x_key)], vv)
+                x = dw.x[(l, w.projs[c[0]].x_key)]
+                if kind == "fused":
+                    hab.sgmv_fused(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x, dw.y[(l, ci)],
+                                   dw.base.get((l, ci)))
+                elif kind == "shrink+reduce":
+                    hab.sgmv_shrink(dw.pool, dw.plan, l, c, x, vv)
                 else:
                     hab.sgmv_expand(dw.pool, dw.plan, l, c, dw.y_offsets[ci], vv, dw.y[(l, ci)])
 
-    kern = {}
+    us = {}
     with torch.cuda.stream(stream):
-        for kind in ("shrink", "expand"):
+        for kind in ("fused", "shrink+reduce", "expand"):
             launch(kind)                                   # warm
             torch.cuda.synchronize()
             ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -226,15 +239,17 @@ def main():
                 launch(kind)
             eb.record(stream)
             torch.cuda.synchronize()
-            us = ea.elapsed_time(eb) * 1e3 / (args.kernel_reps * n_launch)
-            bpl = sum(kernel_bytes(w, c, kind) for c in dw.calls) / len(dw.calls)
-            kern[kind] = {"avg_us": us, "gbs": bpl / (us * 1e-6) / 1e9,
-                          "alg_bytes_per_launch": bpl}
-    # the expand is one kernel per call; the shrink figure spans two
+            us[kind] = ea.elapsed_time(eb) * 1e3 / (args.kernel_reps * n_launch)
+    us["shrink"] = us["fused"] - us["expand"]
+    kern = {}
+    for kind in ("shrink", "expand", "shrink+reduce", "fused"):
+        parts = ("shrink", "expand") if kind == "fused" else (kind.split("+")[0],)
+        bpl = sum(kernel_bytes(w, c, k) for c in dw.calls for k in parts) / len(dw.calls)
+        kern[kind] = {"avg_us": us[kind], "gbs": bpl / (us[kind] * 1e-6) / 1e9,
+                      "alg_bytes_per_launch": bpl}
     dom = "expand" if kern["expand"]["avg_us"] >= kern["shrink"]["avg_us"] else "shrink"
     decode = dw.plan.stats()["max_block_tokens"] <= 4
-    kname = {"shrink": "k_shrink+k_reduce",
-             "expand": "k_expand_decode" if decode else "k_expand"}[dom]
+    kname = {"shrink": "k_shrink", "expand": "k_expand_decode" if decode else "k_expand"}[dom]
     traffic = traffic_from_profile(kname, w.name)
     roof = {"bound": "hbm", "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
@@ -264,7 +279,7 @@ def main():
 
     cpu = None
     if args.cpu_layers != 0 and keep:
-        cpu = cpu_baseline(w, keep, cpu_layers, threads)
+        cpu = cpu_baseline(w, keep, cpu_layers, threads, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
 
     tok_s = w.num_tokens / (ms * 1e-3)

@@ -67,6 +67,24 @@ def kernel_stats(path: str, command: str, limit: int = 12) -> str:
     return "\n".join(out) + "\n"
 
 
+def launches_by_grid(path: str, limit: int = 12) -> str:
+    """Per (kernel, workgroups) durations from a ``*_kernel_trace.csv``: the
+    launches of one call shape (e.g. one projection set) share a grid."""
+    groups = defaultdict(list)
+    for r in _rows(path):
+        wg = int(r.get("workgroup_size_x") or r.get("workgroup_size") or 1)
+        g = int(r.get("grid_size_x") or r.get("grid_size") or 0) // max(wg, 1)
+        groups[(short_name(r["kernel_name"]), g)].append(
+            (int(r["end_timestamp"]) - int(r["start_timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    out = [f"{'kernel':40s} {'wgs':>6s} {'calls':>6s} {'avg_us':>8s} {'med_us':>8s} {'pct':>6s}"]
+    for (name, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:limit]:
+        v = sorted(v)
+        out.append(f"{name[:40]:40s} {g:6d} {len(v):6d} {sum(v) / len(v):8.2f} "
+                   f"{v[len(v) // 2]:8.2f} {100 * sum(v) / total:6.2f}")
+    return "\n".join(out) + "\n"
+
+
 def _counter(path: str, counter: str):
     """{dispatch id: (kernel name, grid size, value)} for one counter."""
     per = defaultdict(float)
@@ -108,6 +126,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    s.add_argument("--trace", help="the run's *_kernel_trace.csv: adds launches by grid")
+    s.add_argument("--note", action="append", default=[])
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
@@ -123,6 +143,11 @@ def main(argv=None):
     if a.cmd == "stats":
         with open(a.out, "w") as f:
             f.write(kernel_stats(a.csv, a.command))
+            if a.trace:
+                f.write("\nlaunches by kernel and grid (workgroups):\n")
+                f.write(launches_by_grid(a.trace))
+            for n in a.note:
+                f.write(f"\n{n}\n")
         return
     try:
         with open(a.json) as f:
