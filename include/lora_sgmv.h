@@ -100,16 +100,19 @@ const char *lora_last_error(void);
  * Multi-LoRA", section "Technical Foundation").  0 on a bad descriptor. */
 uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank);
 
-/* Bytes one adapter occupies in the slab: the same sum at the padded rank,
+/* Bytes one adapter occupies in the slab: the same sum at the padded rank
+ * with h_in rounded up to whole K-blocks (32 bf16 / 16 f32 elements),
  * rounded up to 256 bytes.  0 on a bad descriptor or rank. */
 uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank);
 
 /* Create a pool over a caller-owned device buffer `slab` of `slab_bytes`
  * (256-byte aligned).  Each adapter occupies one contiguous extent of the
- * slab; inside it, for layer l and projection p, the A block [r_pad][h_in_p]
- * is followed by the B block [h_out_p][r_pad], layers outermost.  Pad rows
- * of A and pad columns of B are zero.  The slab is not touched here and is
- * not freed by lora_pool_destroy. */
+ * slab; inside it, for layer l and projection p, the A block is followed by
+ * the B block, layers outermost.  A is stored K-blocked,
+ * [h_in_pad_p / S][r_pad][S] with S = 32 (bf16) or 16 (f32) and h_in_pad_p =
+ * h_in_p rounded up to S, so that 16 rank rows x S columns are one
+ * contiguous run; B is [h_out_p][r_pad] row-major.  Pad rows and columns are
+ * zero.  The slab is not touched here and is not freed by lora_pool_destroy. */
 lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d,
                              void *slab, uint64_t slab_bytes);
 lora_status lora_pool_destroy(lora_pool *p);
