@@ -45,6 +45,10 @@ template <> struct Elem<float> { static constexpr int E = 4; };
 constexpr uint32_t kOOB = 0x80000000u;        // offset of a masked lane: out of range
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kNT = 2;                        // non-temporal: streamed once
+// Outputs are stored at device scope (`sc1`, written through the L2): no
+// dirty output lines are left for the kernel boundary to write back, which
+// measured about 3% faster over the full stack than write-back stores.
+constexpr int kOut = 16;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes),
@@ -191,7 +195,9 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     for (int i = threadIdx.x; i < TT * kWaveSize; i += kWaves * kWaveSize) {
         const int tt = i / kWaveSize, ln = i % kWaveSize;
         const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
-        *reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4) = s4;
+        // partials are read once, by the next kernel
+        __builtin_nontemporal_store(
+            s4, reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4));
     }
 }
 
@@ -291,7 +297,7 @@ template <> struct Out4<uint16_t> {
         return __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0);
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, raw v) {
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, kOut);
     }
     static __device__ __forceinline__ void unpack(raw w, float (&o)[4]) {
         o[0] = bf16_lo(w[0]); o[1] = bf16_hi(w[0]);
@@ -307,7 +313,7 @@ template <> struct Out4<float> {
         return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, raw v) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, kOut);
     }
     static __device__ __forceinline__ void unpack(raw w, float (&o)[4]) {
         o[0] = __uint_as_float(w[0]); o[1] = __uint_as_float(w[1]);
@@ -336,7 +342,7 @@ template <> struct Out1<uint16_t> {
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
         __builtin_amdgcn_raw_buffer_store_b16(
-            (unsigned short)(bf16x2_rne(v, 0.f) & 0xffffu), r, int(off), 0, 0);
+            (unsigned short)(bf16x2_rne(v, 0.f) & 0xffffu), r, int(off), 0, kOut);
     }
 };
 template <> struct Out1<float> {
@@ -344,7 +350,7 @@ template <> struct Out1<float> {
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, int(off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, int(off), 0, kOut);
     }
 };
 

@@ -180,9 +180,10 @@ def test_prefill_blocks(seed):
 
 
 def test_two_step_path():
-    """sgmv_shrink + sgmv_expand through a caller's v buffer: the same delta,
-    within the float32 bound (it sums K in another order than sgmv_fused), and
-    deterministic."""
+    """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
+    float32 bound of the oracle, deterministic, and bit-identical to
+    sgmv_fused (every kernel sums the k-chunk partials in one order) on both
+    the decode path (one fused launch) and the prefill path."""
     for w in (config(1), multi_proj_case(3, has_base=True), config(0),
               random_case(71, T=150, h_in=512, h_out=256, max_seg=80, r_choices=[8, 24, 64])):
         log(f"[parity] two-step {w.name}")
@@ -196,6 +197,11 @@ def test_two_step_path():
         for k in outs[0]:
             assert np.array_equal(outs[0][k], outs[1][k]), k
         check_workload(dw, tight=True, threads=4)
+        dw.zero_outputs()
+        dw.run_fused()
+        torch.cuda.synchronize()
+        for k, v in dw.y.items():
+            assert np.array_equal(from_device(v).view(np.uint8), outs[0][k].view(np.uint8)), k
 
 
 def test_shrink_output_layout():
