@@ -32,11 +32,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _core_elems(w):
+    """float32 elements of one core: r_max^2 (full) or r_max (diag)."""
+    return w.r_max * (w.r_max if w.sigma_kind == "full" else 1)
+
+
+def _distinct_cores(w):
+    tok = w.token_adapter()
+    sig = np.full(w.num_tokens, -1)
+    for s in range(w.num_segs):
+        sig[w.seg_starts[s]:w.seg_starts[s + 1]] = w.seg_sigma[s]
+    return len({int(j) for j, a in zip(sig, tok) if j >= 0 and a >= 0})
+
+
 def algorithmic(w, layers=None):
     """Bytes and FLOPs the delta must move/do, each counted once: adapter
-    bytes of the distinct (adapter, layer, projection) triples at true rank,
-    each activation read once, y written once and its input (base_out or y)
-    read once."""
+    bytes of the distinct (adapter, layer, projection) triples at true rank
+    (for jointly compressed adapters: the shared bases plus the distinct
+    cores, float32), each activation read once, y written once and its input
+    (base_out or y) read once."""
     es = 2 if w.dtype == "bf16" else 4
     layers = range(w.num_layers) if layers is None else layers
     tok = w.token_adapter()
@@ -44,6 +58,8 @@ def algorithmic(w, layers=None):
     act = int((tok >= 0).sum())
     per_layer_adapter = sum(int(w.ranks[a]) * (p.h_in + p.h_out) for a in touched
                             for p in w.projs) * es
+    if w.sigma_kind:
+        per_layer_adapter += _distinct_cores(w) * len(w.projs) * _core_elems(w) * 4
     per_layer_x = sum(w.num_tokens * w.x_width(k) for k in w.x_keys()) * es
     per_layer_y = sum(w.num_tokens * p.h_out for p in w.projs) * es * 2
     flops = sum(2 * int(w.ranks[tok[t]]) * (p.h_in + p.h_out) for t in range(w.num_tokens)
@@ -66,7 +82,8 @@ def kernel_bytes(w, call, kind):
         h_in = w.projs[call[0]].h_in
         return r_sum * h_in * es * len(call) + act * h_in * es + v_bytes
     h_out = sum(w.projs[p].h_out for p in call)
-    return r_sum * h_out * es + v_bytes + 2 * w.num_tokens * h_out * es
+    cores = _distinct_cores(w) * len(call) * _core_elems(w) * 4 if w.sigma_kind else 0
+    return r_sum * h_out * es + v_bytes + 2 * w.num_tokens * h_out * es + cores
 
 
 def traffic_from_profile(kernel, workload):
@@ -90,17 +107,28 @@ def cpu_baseline(w, blocks, layers, threads, min_seconds):
     layers, repeated until at least `min_seconds` of oracle time."""
     import oracle
     inputs = []
+    used = sorted({int(j) for j in w.seg_sigma if j >= 0}) if w.sigma_kind else []
     for l in layers:
         for p, pr in enumerate(w.projs):
             adapters = {a: (blocks[(a, l, p)][0], blocks[(a, l, p)][1], float(w.scales[a]))
                         for a in w.touched()}
+            cores = None
+            if w.sigma_kind:
+                cores = np.zeros((w.n_cores,) + w.core(0, l, p).shape, np.float32)
+                for j in used:
+                    cores[j] = w.core(j, l, p)
             inputs.append((w.activation(l, pr.x_key), adapters,
-                           w.base_out(l, p) if w.has_base else None))
+                           w.base_out(l, p) if w.has_base else None, cores))
     t_total, passes = 0.0, 0
     while passes == 0 or t_total < min_seconds:
-        for x, adapters, y_in in inputs:
+        for x, adapters, y_in, cores in inputs:
             t0 = time.perf_counter()
-            oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, threads=threads)
+            if cores is not None:
+                oracle.lora_delta_sigma(x, w.seg_starts, w.seg_adapter, w.seg_sigma, adapters,
+                                        cores, w.sigma_kind, y_in, threads=threads)
+            else:
+                oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in,
+                                  threads=threads)
             t_total += time.perf_counter() - t0
         passes += 1
     frac = len(layers) / w.num_layers
@@ -116,7 +144,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=4, help="0..4 (default: the full stack)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="0..4 (default 4: the full stack); 5, 6: the full stack served from "
+                         "jointly compressed adapters with full / diagonal cores")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-layers", type=int, default=-1,
                     help="layers of the CPU-oracle sample (-1: all, 0: skip)")
@@ -140,7 +170,11 @@ def main():
 
     hab.load()
     torch.cuda.set_device(0)
-    w = config(args.workload)
+    if args.workload in (5, 6):
+        from synth import jd_full_stack
+        w = jd_full_stack("full" if args.workload == 5 else "diag")
+    else:
+        w = config(args.workload)
     threads = min(16, os.cpu_count() or 1)
     cpu_layers = list(range(w.num_layers)) if args.cpu_layers < 0 else list(
         range(min(args.cpu_layers, w.num_layers)))
@@ -221,10 +255,18 @@ def main():
                 vv = v[:, :len(c) * w.r_max]
                 x = dw.x[(l, w.projs[c[0]].x_key)]
                 if kind == "fused":
-                    hab.sgmv_fused(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x, dw.y[(l, ci)],
-                                   dw.base.get((l, ci)))
+                    if dw.sigma is not None:
+                        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
+                                             dw.sigma, w.sigma_kind, dw.y[(l, ci)],
+                                             dw.base.get((l, ci)))
+                    else:
+                        hab.sgmv_fused(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
+                                       dw.y[(l, ci)], dw.base.get((l, ci)))
                 elif kind == "shrink+reduce":
                     hab.sgmv_shrink(dw.pool, dw.plan, l, c, x, vv)
+                elif dw.sigma is not None:
+                    hab.sgmv_expand_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci], vv,
+                                          dw.sigma, w.sigma_kind, dw.y[(l, ci)])
                 else:
                     hab.sgmv_expand(dw.pool, dw.plan, l, c, dw.y_offsets[ci], vv, dw.y[(l, ci)])
 

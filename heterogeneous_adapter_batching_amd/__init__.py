@@ -11,11 +11,12 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     LIB_PATH, LoraError, PoolDesc, load, status_name, LORA_F32, LORA_BF16,
-    LORA_MAX_PROJ, LORA_MAX_RANK,
+    LORA_MAX_PROJ, LORA_MAX_RANK, LORA_SIGMA_DIAG, LORA_SIGMA_FULL,
 )
 from .api import (  # noqa: F401
-    Pool, Plan, sgmv_shrink, sgmv_expand, sgmv_fused, adapter_bytes, extent_bytes,
+    Pool, Plan, sgmv_shrink, sgmv_expand, sgmv_fused, sgmv_expand_sigma, sgmv_fused_sigma,
+    adapter_bytes, extent_bytes,
 )
 
-__all__ = ["Pool", "Plan", "sgmv_shrink", "sgmv_expand", "sgmv_fused", "adapter_bytes",
-           "extent_bytes", "LoraError", "load"]
+__all__ = ["Pool", "Plan", "sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_expand_sigma",
+           "sgmv_fused_sigma", "adapter_bytes", "extent_bytes", "LoraError", "load"]

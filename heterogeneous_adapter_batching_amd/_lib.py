@@ -62,7 +62,14 @@ SIGNATURES = {
     "sgmv_expand": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp]),
     "sgmv_fused": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp, _i64,
                           _vp]),
+    "lora_plan_create_sigma": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32p, _i32]),
+    "sgmv_expand_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
+                                 _vp, _i64, _vp]),
+    "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
+                                _vp, _i64, _vp, _i64, _vp]),
 }
+
+LORA_SIGMA_DIAG, LORA_SIGMA_FULL = 1, 2
 
 _lib = None
 

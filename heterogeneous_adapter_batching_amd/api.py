@@ -6,7 +6,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from ._lib import LORA_BF16, LORA_F32, LORA_MAX_PROJ, PoolDesc, check, load
+from ._lib import (LORA_BF16, LORA_F32, LORA_MAX_PROJ, LORA_SIGMA_DIAG, LORA_SIGMA_FULL, PoolDesc,
+                   check, load)
 
 _DTYPES = {"bf16": LORA_BF16, "f32": LORA_F32}
 
@@ -184,7 +185,9 @@ class Pool:
 class Plan:
     """The gather plan of one heterogeneous batch (built on the host)."""
 
-    def __init__(self, pool: Pool, num_tokens: int, seg_starts, seg_adapter):
+    def __init__(self, pool: Pool, num_tokens: int, seg_starts, seg_adapter, seg_sigma=None):
+        """seg_sigma: per-segment core index of jointly compressed adapters
+        (-1: none), or None for plain adapters."""
         self.lib = pool.lib
         self.pool = pool
         self.num_tokens = int(num_tokens)
@@ -194,9 +197,18 @@ class Plan:
             raise ValueError("seg_starts must have one more entry than seg_adapter")
         self._h = ctypes.c_void_p()
         i32p = ctypes.POINTER(ctypes.c_int32)
-        check(self.lib.lora_plan_create(ctypes.byref(self._h), pool.handle, self.num_tokens,
-                                        starts.ctypes.data_as(i32p), segs.ctypes.data_as(i32p),
-                                        int(segs.shape[0])))
+        if seg_sigma is None:
+            check(self.lib.lora_plan_create(ctypes.byref(self._h), pool.handle, self.num_tokens,
+                                            starts.ctypes.data_as(i32p),
+                                            segs.ctypes.data_as(i32p), int(segs.shape[0])))
+        else:
+            sig = np.ascontiguousarray(seg_sigma, dtype=np.int32)
+            if sig.shape != segs.shape:
+                raise ValueError("seg_sigma must have one entry per segment")
+            check(self.lib.lora_plan_create_sigma(ctypes.byref(self._h), pool.handle,
+                                                  self.num_tokens, starts.ctypes.data_as(i32p),
+                                                  segs.ctypes.data_as(i32p),
+                                                  sig.ctypes.data_as(i32p), int(segs.shape[0])))
         self.ws = None
         self.max_proj = 0
 
@@ -300,4 +312,63 @@ def sgmv_fused(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=
                               base.stride(0) if base is not None else 0,
                               ctypes.c_void_p(y.data_ptr()), y.stride(0),
                               _stream_handle(stream)))
+    return y
+
+
+def _sigma_kind(kind) -> int:
+    codes = {"diag": LORA_SIGMA_DIAG, "full": LORA_SIGMA_FULL}
+    if kind not in codes:
+        raise ValueError(f"core kind {kind!r} is neither 'diag' nor 'full'")
+    return codes[kind]
+
+
+def _check_cores(pool: Pool, sigma, kind):
+    torch = _torch()
+    _check_dev(sigma, "sigma", torch.float32, ndim=sigma.dim() if hasattr(sigma, "dim") else 2)
+    if not sigma.is_contiguous():
+        raise ValueError("sigma must be contiguous")
+    tail = (pool.num_layers, len(pool.h_in), pool.r_max) + ((pool.r_max,) if kind == "full" else ())
+    if tuple(sigma.shape[1:]) != tail:
+        raise ValueError(f"sigma must be [n]{list(tail)}, got {list(sigma.shape)}")
+    return int(sigma.shape[0])
+
+
+def sgmv_expand_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, v, sigma, kind, y,
+                      stream=None):
+    """y[:, off_i : off_i + h_out] += s * B_c,p (Sigma_k v_i): the B step of
+    jointly compressed adapters after their core step.  sigma: float32
+    [n][layers][proj][r_max][r_max] ("full") or [n][layers][proj][r_max] ("diag")."""
+    torch = _torch()
+    _check_dev(v, "v", torch.float32)
+    _check_dev(y, "y", _torch_dtype(pool.dtype))
+    n_sig = _check_cores(pool, sigma, kind)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_expand_sigma(pool.handle, plan.handle, layer, n, parr,
+                                     _i32_array(y_offsets),
+                                     ctypes.c_void_p(v.data_ptr()), v.stride(0),
+                                     ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), n_sig,
+                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                     _stream_handle(stream)))
+    return y
+
+
+def sgmv_fused_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, sigma, kind, y,
+                     base=None, stream=None):
+    """y = (base or y) + s * B_c (Sigma_k (A_c x)) for each listed projection's
+    slice of y: the three steps of jointly compressed adapters."""
+    dt = _torch_dtype(pool.dtype)
+    _check_dev(x, "x", dt)
+    _check_dev(y, "y", dt)
+    if base is not None:
+        _check_dev(base, "base", dt)
+    n_sig = _check_cores(pool, sigma, kind)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_fused_sigma(pool.handle, plan.handle, layer, n, parr,
+                                    _i32_array(y_offsets),
+                                    ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                                    ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), n_sig,
+                                    ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                    base.stride(0) if base is not None else 0,
+                                    ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                    _stream_handle(stream)))
     return y

@@ -379,6 +379,54 @@ __device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &b
     }
 }
 
+// The core step of jointly compressed adapters ("Compress then Serve",
+// rebuttal pseudocode of add_lora_slice_with_sigma, step 2): each token's v
+// (LDS rows [0, n_tok), ranks [0, r_pad)) becomes Sigma_j v with the token's
+// core j, in float32, k ascending; a token without a core keeps v.  Full
+// cores are r_max x r_max row-major, diagonal cores r_max values.  Up to
+// MAXI entries per thread.
+template <int MAXI>
+__device__ __forceinline__ void apply_sigma(const ExpandArgs &a, const BlockDesc &blk, int p,
+                                            float (*vs)[LORA_MAX_RANK + 4]) {
+    const int r = blk.r_pad;
+    const int entries = blk.n_tok * r;
+    float out[MAXI];
+#pragma unroll
+    for (int ii = 0; ii < MAXI; ++ii) {
+        const int i = int(threadIdx.x) + ii * kWaves * kWaveSize;
+        out[ii] = 0.f;
+        if (i < entries) {
+            const int ti = i / r, j = i - (i / r) * r;
+            const int sg = a.tok_sig[blk.tok_off + ti];
+            float o = vs[ti][j];
+            if (sg >= 0) {
+                const float *core = a.sigma + int64_t(sg) * a.sig_stride + a.sig_off[p];
+                if (a.sigma_kind == 1) {
+                    o = core[j] * vs[ti][j];
+                } else {
+                    const f32x4 *row = reinterpret_cast<const f32x4 *>(core + int64_t(j) * a.r_max);
+                    o = 0.f;
+                    for (int k = 0; k < r; k += 4) {
+                        const f32x4 c4 = row[k / 4];
+                        o = __builtin_fmaf(c4[0], vs[ti][k], o);
+                        o = __builtin_fmaf(c4[1], vs[ti][k + 1], o);
+                        o = __builtin_fmaf(c4[2], vs[ti][k + 2], o);
+                        o = __builtin_fmaf(c4[3], vs[ti][k + 3], o);
+                    }
+                }
+            }
+            out[ii] = o;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < MAXI; ++ii) {
+        const int i = int(threadIdx.x) + ii * kWaves * kWaveSize;
+        if (i < entries) vs[i / r][i - (i / r) * r] = out[ii];
+    }
+    __syncthreads();
+}
+
 // v of a decode block (at most kValuTokens tokens) into LDS, in two parts so
 // that its loads go out before the wave's B loads and its wait covers them
 // alone (a wave's loads complete in issue order).  From the shrink's
@@ -468,7 +516,7 @@ __device__ __forceinline__ void gather_finish(const ExpandArgs &a, const BlockDe
 // them with every token's v (an LDS broadcast) in float32.  Loads go out in
 // the order they are used: the v gather, B vector by vector, then y_in; so
 // the dot products of the first vectors start while the rest arrive.
-template <typename T, int NV>
+template <typename T, int NV, bool Sig>
 __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
                                             const int (&tr)[kValuTokens], int p, int o_lo,
                                             int o_hi, float (*vs)[LORA_MAX_RANK + 4],
@@ -517,6 +565,8 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
             yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
     }
     gather_finish(a, blk, p, g, vs, ways);
+    if constexpr (Sig)
+        apply_sigma<kValuTokens * LORA_MAX_RANK / (kWaves * kWaveSize)>(a, blk, p, vs);
 
     float d[RPL][NT];
 #pragma unroll
@@ -646,6 +696,8 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
 
     gather_v<TT>(a, blk, c.p, vs);
     __syncthreads();
+    if (a.sigma_kind)
+        apply_sigma<TT * kTile * LORA_MAX_RANK / (kWaves * kWaveSize)>(a, blk, c.p, vs);
     if (c.o_lo >= c.o_hi) return;
 
     // v operand per (token tile, K-step); packed blocks have one K-step
@@ -721,7 +773,9 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
 // blocks are ordered by padded rank, and a unit's rank class, block,
 // projection and slice follow from the kernel arguments alone, so the first
 // loads are the block's descriptor and token rows (one round trip).
-template <typename T>
+// Sig: the launch applies cores of jointly compressed adapters (a separate
+// build, so the plain kernel keeps its registers).
+template <typename T, bool Sig>
 __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     constexpr int VS = LORA_MAX_RANK + 4;
     __shared__ float vs[kValuTokens][VS];
@@ -773,12 +827,12 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
         return;
     }
     switch (decode_nvt(r_pad, sizeof(T))) {
-    case 1: return expand_valu<T, 1>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 2: return expand_valu<T, 2>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 4: return expand_valu<T, 4>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 8: return expand_valu<T, 8>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 1: return expand_valu<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 4: return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 8: return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     default:
-        if constexpr (sizeof(T) == 4) return expand_valu<T, 16>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+        if constexpr (sizeof(T) == 4) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 
@@ -929,8 +983,13 @@ hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
 hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
     const dim3 grid(a.grid), block(kWaves * kWaveSize);
-    if (dtype == LORA_BF16) hipLaunchKernelGGL(k_expand_decode<uint16_t>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(k_expand_decode<float>, grid, block, 0, s, a);
+    if (a.sigma_kind) {
+        if (dtype == LORA_BF16) hipLaunchKernelGGL((k_expand_decode<uint16_t, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_expand_decode<float, true>), grid, block, 0, s, a);
+    } else {
+        if (dtype == LORA_BF16) hipLaunchKernelGGL((k_expand_decode<uint16_t, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_expand_decode<float, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -153,6 +153,8 @@ struct lora_plan {
     uint64_t pool_generation = 0;
     int32_t T = 0;
     std::vector<int32_t> token_order;    // plan order: grouped adapter tokens, then the rest
+    std::vector<int32_t> token_sigma;    // core index per plan-order row (-1: none)
+    int32_t max_sigma = -1;              // largest core index named
     std::vector<int32_t> token_group;    // per token row
     std::vector<int32_t> group_adapter, group_rank;
     std::vector<BlockDesc> blocks;       // adapter blocks [0, nb_act), no-adapter blocks after
@@ -163,7 +165,8 @@ struct lora_plan {
     void *ws = nullptr;
     uint64_t ws_bytes = 0;
     int32_t max_proj = 0;
-    uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_part = 0;
+    uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
+             off_part = 0;
     uint64_t image_bytes = 0, part_bytes = 0;
     void *staging = nullptr;
     uint64_t staging_bytes = 0;
@@ -179,6 +182,7 @@ struct lora_plan {
         off_tiles = o;   o = round_up(o + sizeof(lora::TileDesc) * std::max(rt_total(), 1), 256);
         off_btok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(nb_all(), 1), 256);
         off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(rt_total(), 1), 256);
+        off_tsig = o;    o = round_up(o + 4ull * std::max(T, 1), 256);
         image_bytes = o;
         part_bytes = 4ull * max_shrink_units(mp) * tt * lora::kTile * lora::kTile;
         off_part = o;    o = round_up(o + part_bytes, 256);
@@ -393,8 +397,11 @@ lora_status lora_pool_stats(const lora_pool *p, int32_t *num, uint64_t *free_byt
 }
 
 // ------------------------------------------------------------------- plan ----
-lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
-                             const int32_t *seg_starts, const int32_t *seg_adapter, int32_t S) {
+}  // extern "C"
+
+namespace {
+lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const int32_t *seg_starts,
+                        const int32_t *seg_adapter, const int32_t *seg_sigma, int32_t S) {
     if (!out) return fail(LORA_EINVAL, "null output pointer");
     if (!p) return fail(LORA_EINVAL, "null pool");
     if (T < 0 || S < 0) return fail(LORA_ESEG, "negative token or segment count");
@@ -409,6 +416,8 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
         if (id < -1) return fail(LORA_ENOENT, "segment %d names adapter id %d", s, id);
         if (id >= 0 && !p->slots.count(id))
             return fail(LORA_ENOENT, "segment %d names unregistered adapter %d", s, id);
+        if (seg_sigma && seg_sigma[s] < -1)
+            return fail(LORA_EINVAL, "segment %d names core %d", s, seg_sigma[s]);
     }
 
     lora_plan *pl = new lora_plan();
@@ -517,8 +526,33 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
         pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
     const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
+    // each row's core, in plan order
+    std::vector<int32_t> row_sigma(T, -1);
+    if (seg_sigma)
+        for (int32_t s = 0; s < S; ++s)
+            for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) row_sigma[t] = seg_sigma[s];
+    pl->token_sigma.resize(T);
+    for (int32_t i = 0; i < T; ++i) {
+        pl->token_sigma[i] = row_sigma[pl->token_order[i]];
+        pl->max_sigma = std::max(pl->max_sigma, pl->token_sigma[i]);
+    }
     *out = pl;
     return LORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
+                             const int32_t *seg_starts, const int32_t *seg_adapter, int32_t S) {
+    return plan_create(out, p, T, seg_starts, seg_adapter, nullptr, S);
+}
+
+lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t T,
+                                   const int32_t *seg_starts, const int32_t *seg_adapter,
+                                   const int32_t *seg_sigma, int32_t S) {
+    if (S > 0 && !seg_sigma) return fail(LORA_EINVAL, "null core table");
+    return plan_create(out, p, T, seg_starts, seg_adapter, seg_sigma, S);
 }
 
 lora_status lora_plan_destroy(lora_plan *pl) {
@@ -582,6 +616,7 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     uint8_t *img = static_cast<uint8_t *>(pl->staging);
     std::memset(img, 0, pl->image_bytes);
     if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
+    if (pl->T) std::memcpy(img + pl->off_tsig, pl->token_sigma.data(), 4ull * pl->T);
     if (!pl->blocks.empty())
         std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
     if (!pl->tiles.empty())
@@ -777,12 +812,30 @@ int32_t plan_ksteps(const lora_pool *p, const lora_plan *pl) {
     return ks == 3 ? 4 : ks;
 }
 
+// Cores of jointly compressed adapters for one call (kind 0: none).
+struct Cores {
+    const float *sigma = nullptr;
+    int32_t kind = 0;
+    int32_t count = 0;
+};
+
+// Checks the core table of a call against the plan and pool.
+lora_status check_cores(const lora_plan *pl, const Cores &c) {
+    if (c.kind != LORA_SIGMA_DIAG && c.kind != LORA_SIGMA_FULL)
+        return fail(LORA_EINVAL, "core kind %d is neither diagonal nor full", c.kind);
+    if (!c.sigma || !aligned16(c.sigma))
+        return fail(LORA_EINVAL, "core table must be non-null and 16-byte aligned");
+    if (c.count < 0 || pl->max_sigma >= c.count)
+        return fail(LORA_EINVAL, "plan names core %d of a table of %d", pl->max_sigma, c.count);
+    return LORA_OK;
+}
+
 // v source of the expand: the shrink partials of this call (c0 > 0), or a
 // caller's v buffer
 lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
                        const int32_t *projs, const int32_t *yoff, int32_t c0, const float *v,
                        int64_t ldv, void *y, int64_t ldy, const void *base, int64_t ldb,
-                       hipStream_t st) {
+                       hipStream_t st, const Cores &cores = Cores()) {
     const int32_t nb = base ? pl->nb_all() : pl->nb_act;
     if (nb == 0) return LORA_OK;
     lora::ExpandArgs a{};
@@ -812,6 +865,16 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
     a.v_bytes = v ? uint32_t(tensor_bytes(pl->T, ldv, ldv, 4)) : 0u;
+    if (cores.kind) {
+        const int64_t per = cores.kind == LORA_SIGMA_FULL ? int64_t(p->d.r_max) * p->d.r_max
+                                                           : int64_t(p->d.r_max);
+        a.sigma = cores.sigma;
+        a.sigma_kind = cores.kind;
+        a.tok_sig = reinterpret_cast<const int32_t *>(ws + pl->off_tsig);
+        a.sig_stride = int64_t(p->d.num_layers) * p->d.num_proj * per;
+        for (int i = 0; i < nproj; ++i)
+            a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;
+    }
     const bool decode = pl->max_block <= lora::kValuTokens;   // blocks of the decode expand
     const int32_t ks = plan_ksteps(p, pl);
     if (decode) {
@@ -911,9 +974,40 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
                       static_cast<hipStream_t>(stream));
 }
 
+lora_status sgmv_expand_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                              int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                              const float *v, int64_t ldv, const float *sigma, int32_t sigma_kind,
+                              int32_t num_sigma, void *y, int64_t ldy, void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    const Cores cores{sigma, sigma_kind, num_sigma};
+    st = check_cores(pl, cores);
+    if (st != LORA_OK) return st;
+    if (pl->T == 0) return LORA_OK;
+    if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
+    if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)
+        return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
+    if (tensor_bytes(pl->T, ldv, ldv, 4) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "v spans more than 2 GiB");
+    st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
+    if (st != LORA_OK) return st;
+    return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,
+                      static_cast<hipStream_t>(stream), cores);
+}
+
 lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
                        const int32_t *projs, const int32_t *yoff, const void *x, int64_t ldx,
                        const void *base, int64_t ldb, void *y, int64_t ldy, void *stream) {
+    return sgmv_fused_sigma(p, pl, layer, nproj, projs, yoff, x, ldx, nullptr, 0, 0, base, ldb,
+                            y, ldy, stream);
+}
+
+lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                             int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                             const void *x, int64_t ldx, const float *sigma, int32_t sigma_kind,
+                             int32_t num_sigma, const void *base, int64_t ldb, void *y,
+                             int64_t ldy, void *stream) {
     CallCheck cc;
     lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
     if (st != LORA_OK) return st;
@@ -923,6 +1017,11 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, i
                                                (long long)ldx);
     if (tensor_bytes(pl->T, ldx, cc.h_in, cc.es) > lora::kMaxTensorBytes)
         return fail(LORA_EINVAL, "x spans more than 2 GiB");
+    const Cores cores{sigma, sigma_kind, num_sigma};
+    if (sigma_kind != 0 || sigma) {
+        st = check_cores(pl, cores);
+        if (st != LORA_OK) return st;
+    }
     st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
     if (base) {
@@ -933,7 +1032,8 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     int32_t c0 = 0;
     st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0);
     if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs);
+    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
+                      cores);
 }
 
 }  // extern "C"

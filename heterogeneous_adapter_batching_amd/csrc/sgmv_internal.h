@@ -150,6 +150,15 @@ struct ExpandArgs {
     uint32_t y_bytes;            // buffer ranges (each at most kMaxTensorBytes)
     uint32_t base_bytes;
     uint32_t v_bytes;            // range of a caller's v (when partial == null)
+    // Jointly compressed adapters: sigma_kind 0 = none, 1 = diagonal cores,
+    // 2 = full cores.  Token row tok_off + i of the plan order uses core
+    // tok_sig[tok_off + i] (-1: none); core j of projection i of the call
+    // starts at sigma + j * sig_stride + sig_off[i] (floats).
+    const float *sigma;
+    const int32_t *tok_sig;
+    int64_t sig_stride;
+    int64_t sig_off[LORA_MAX_PROJ];
+    int32_t sigma_kind;
     // Decode expand: units by rank class; class k has units [cls_unit0[k],
     // cls_unit0[k + 1]) (unused entries INT32_MAX) and the record cls[k].
     int32_t cls_unit0[kMaxClasses + 1];

@@ -71,6 +71,10 @@ typedef enum {
 
 typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 
+/* Core kinds of jointly compressed adapters ("Compress then Serve": JD-Diag
+ * keeps a diagonal core per adapter, JD-Full a full one). */
+typedef enum { LORA_SIGMA_DIAG = 1, LORA_SIGMA_FULL = 2 } lora_sigma_kind;
+
 #define LORA_MAX_PROJ 8   /* adapted projections per pool (q, k, v, o, gate, up, down, ...) */
 #define LORA_MAX_RANK 64  /* largest supported r_max */
 
@@ -156,12 +160,26 @@ lora_status lora_pool_stats(const lora_pool *p, int32_t *num_adapters, uint64_t 
  *   seg_starts[S] = T; seg_adapter[S] holds adapter ids, -1 = no adapter.
  *   Empty segments are allowed and ids may repeat.
  * Segments are grouped by adapter in first-appearance order (the segmented
- * gather), each group is cut into blocks of at most 64 tokens, and every id
- * is resolved to its slot, rank and scale.  Errors: LORA_ESEG, LORA_ENOENT.
+ * gather), each group is cut into blocks (at most 16 tokens, or 64 once a
+ * group reaches 48 tokens; a decode batch's blocks are cut again into
+ * blocks of at most 4 tokens for the expand), and every id is resolved to
+ * its slot, rank and scale.  Errors: LORA_ESEG, LORA_ENOENT.
  * The plan stays valid while its adapters stay registered. */
 lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_tokens,
                              const int32_t *seg_starts, const int32_t *seg_adapter,
                              int32_t num_segs);
+
+/* The same for jointly compressed adapters ("Compress then Serve", rebuttal
+ * pseudocode of add_lora_slice_with_sigma): seg_adapter names the pool entry
+ * that holds the segment's shared basis A, B (a cluster's), and
+ * seg_sigma[S] its core: an index into the core table passed to the
+ * *_sigma calls, or -1 for none (the identity: plain LoRA).  Segments of
+ * different cores share one group when they share a basis.
+ * Errors as lora_plan_create, and LORA_EINVAL for a core index < -1 (the
+ * upper bound is checked by each call against its table). */
+lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t num_tokens,
+                                   const int32_t *seg_starts, const int32_t *seg_adapter,
+                                   const int32_t *seg_sigma, int32_t num_segs);
 lora_status lora_plan_destroy(lora_plan *pl);   /* waits for its last upload */
 
 /* Device bytes the plan needs: its tables and the per-call partial sums of
@@ -223,6 +241,34 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
                        int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
                        const void *x, int64_t ldx, const void *base, int64_t ldb,
                        void *y, int64_t ldy, void *stream);
+
+/* The three-step delta of jointly compressed adapters ("Compress then
+ * Serve", rebuttal pseudocode of add_lora_slice_with_sigma: step 1 A into a
+ * float32 buffer, step 2 the core Sigma into a second float32 buffer, step 3
+ * B with the scale into the y slice):
+ *   y[t][y_offsets[i] + o] = y_in + s_c * sum_j B_c,p[o][j] (Sigma_k v)[j],
+ *   (Sigma_k v)[j] = sum_l Sigma_k,l,p[j][l] v[l]   (full, l ascending), or
+ *                  = Sigma_k,l,p[j] v[j]             (diagonal),
+ * with c the token's pool entry, k its core (plan_create_sigma), v = A_c,p x
+ * (fused) or the caller's v (expand), all in float32; a token without a
+ * core uses v itself.  sigma: device float32 table, 16-byte aligned,
+ * [num_sigma][num_layers][num_proj][r_max][r_max] (LORA_SIGMA_FULL) or
+ * [num_sigma][num_layers][num_proj][r_max] (LORA_SIGMA_DIAG); entries at or
+ * beyond an entry's padded rank are not read, entries between its rank and
+ * padded rank multiply zeros and must be finite.  Errors as the plain calls,
+ * and LORA_EINVAL for a bad kind, table pointer, or a plan naming a core
+ * >= num_sigma.  With a plan from lora_plan_create (no cores) these equal
+ * the plain calls bit for bit. */
+lora_status sgmv_expand_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                              int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                              const float *v, int64_t ldv, const float *sigma,
+                              int32_t sigma_kind, int32_t num_sigma, void *y, int64_t ldy,
+                              void *stream);
+lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                             int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                             const void *x, int64_t ldx, const float *sigma, int32_t sigma_kind,
+                             int32_t num_sigma, const void *base, int64_t ldb, void *y,
+                             int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

@@ -192,3 +192,159 @@ int oracle_delta_f64(int32_t T, int32_t h_in, int32_t h_out,
     free(tok_a);
     return 0;
 }
+
+/*
+ * Jointly compressed adapters: the three-step delta
+ *
+ *   y[t] = y_in[t] + s_i * B_c (Sigma_j (A_c x[t]))
+ *
+ * ("Compress then Serve", rebuttal pseudocode of add_lora_slice_with_sigma:
+ * step 1 applies A into the float32 buffer, step 2 transforms the buffer
+ * with the adapter's Sigma into a second float32 buffer, step 3 applies B
+ * with the scale and adds into the y slice).  A_c and B_c are the shared
+ * basis of the segment's entry c in the adapter table (a cluster, r x h_in
+ * and h_out x r); Sigma_j is the segment's core, r x r (kind 2, "JD-Full")
+ * or its diagonal of r values (kind 1, "JD-Diag"); seg_sigma[s] = -1 means
+ * no core (Sigma = identity), which is plain LoRA.  sigma[j] points at core
+ * j, row-major with row length sigma_ld (kind 2).  Same loops, order and
+ * error returns as oracle_delta_f32; also -1 for a core index out of range.
+ */
+int oracle_delta_sigma_f32(int32_t T, int32_t h_in, int32_t h_out,
+                           const float *x, int64_t ldx,
+                           int32_t S, const int32_t *seg_starts, const int32_t *seg_adapter,
+                           const int32_t *seg_sigma,
+                           int32_t n_adapters, const int32_t *adapter_ids,
+                           const int32_t *ranks, const float *scales,
+                           const float *const *A, const float *const *B,
+                           int32_t n_sigma, int32_t sigma_kind, const float *const *sigma,
+                           int64_t sigma_ld,
+                           const float *y_in, int64_t ld_in,
+                           float *y_out, int64_t ld_out, int32_t threads)
+{
+    if (sigma_kind != 1 && sigma_kind != 2) return -1;
+    int32_t *tok_a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    int32_t *tok_s = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    if (!tok_a || !tok_s) { free(tok_a); free(tok_s); return -1; }
+    if (token_adapters(T, S, seg_starts, seg_adapter, n_adapters, adapter_ids, tok_a)) {
+        free(tok_a); free(tok_s);
+        return -1;
+    }
+    for (int32_t s = 0; s < S; ++s) {
+        if (seg_sigma[s] < -1 || seg_sigma[s] >= n_sigma) { free(tok_a); free(tok_s); return -1; }
+        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) tok_s[t] = seg_sigma[s];
+    }
+    const int32_t r_big = max_rank(n_adapters, ranks);
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
+    for (int32_t t = 0; t < T; ++t) {
+        float v[r_big], vs[r_big];
+        float *yt = y_out + (int64_t)t * ld_out;
+        for (int32_t o = 0; o < h_out; ++o)
+            yt[o] = y_in ? y_in[(int64_t)t * ld_in + o] : 0.0f;
+        const int32_t a = tok_a[t];
+        if (a < 0) continue;
+        const int32_t r = ranks[a];
+        const float sc = scales[a];
+        const float *xt = x + (int64_t)t * ldx;
+        /* step 1: buffer = A_c x[t] */
+        for (int32_t j = 0; j < r; ++j) {
+            float acc = 0.0f;
+            const float *aj = A[a] + (int64_t)j * h_in;
+            for (int32_t k = 0; k < h_in; ++k) acc += aj[k] * xt[k];
+            v[j] = acc;
+        }
+        /* step 2: buffer_sigma = Sigma_j buffer */
+        const int32_t sj = tok_s[t];
+        for (int32_t j = 0; j < r; ++j) {
+            if (sj < 0) {
+                vs[j] = v[j];
+            } else if (sigma_kind == 1) {
+                vs[j] = sigma[sj][j] * v[j];
+            } else {
+                float acc = 0.0f;
+                const float *row = sigma[sj] + (int64_t)j * sigma_ld;
+                for (int32_t k = 0; k < r; ++k) acc += row[k] * v[k];
+                vs[j] = acc;
+            }
+        }
+        /* step 3: y[t] += s * (B_c buffer_sigma) */
+        for (int32_t o = 0; o < h_out; ++o) {
+            float d = 0.0f;
+            const float *bo = B[a] + (int64_t)o * r;
+            for (int32_t j = 0; j < r; ++j) d += bo[j] * vs[j];
+            yt[o] = yt[o] + sc * d;
+        }
+    }
+    free(tok_a);
+    free(tok_s);
+    return 0;
+}
+
+/* The same three steps with double accumulation; y_out is double. */
+int oracle_delta_sigma_f64(int32_t T, int32_t h_in, int32_t h_out,
+                           const float *x, int64_t ldx,
+                           int32_t S, const int32_t *seg_starts, const int32_t *seg_adapter,
+                           const int32_t *seg_sigma,
+                           int32_t n_adapters, const int32_t *adapter_ids,
+                           const int32_t *ranks, const float *scales,
+                           const float *const *A, const float *const *B,
+                           int32_t n_sigma, int32_t sigma_kind, const float *const *sigma,
+                           int64_t sigma_ld,
+                           const float *y_in, int64_t ld_in,
+                           double *y_out, int64_t ld_out, int32_t threads)
+{
+    if (sigma_kind != 1 && sigma_kind != 2) return -1;
+    int32_t *tok_a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    int32_t *tok_s = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+    if (!tok_a || !tok_s) { free(tok_a); free(tok_s); return -1; }
+    if (token_adapters(T, S, seg_starts, seg_adapter, n_adapters, adapter_ids, tok_a)) {
+        free(tok_a); free(tok_s);
+        return -1;
+    }
+    for (int32_t s = 0; s < S; ++s) {
+        if (seg_sigma[s] < -1 || seg_sigma[s] >= n_sigma) { free(tok_a); free(tok_s); return -1; }
+        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) tok_s[t] = seg_sigma[s];
+    }
+    const int32_t r_big = max_rank(n_adapters, ranks);
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
+    for (int32_t t = 0; t < T; ++t) {
+        double v[r_big], vs[r_big];
+        double *yt = y_out + (int64_t)t * ld_out;
+        for (int32_t o = 0; o < h_out; ++o)
+            yt[o] = y_in ? (double)y_in[(int64_t)t * ld_in + o] : 0.0;
+        const int32_t a = tok_a[t];
+        if (a < 0) continue;
+        const int32_t r = ranks[a];
+        const double sc = (double)scales[a];
+        const float *xt = x + (int64_t)t * ldx;
+        for (int32_t j = 0; j < r; ++j) {
+            double acc = 0.0;
+            const float *aj = A[a] + (int64_t)j * h_in;
+            for (int32_t k = 0; k < h_in; ++k) acc += (double)aj[k] * (double)xt[k];
+            v[j] = acc;
+        }
+        const int32_t sj = tok_s[t];
+        for (int32_t j = 0; j < r; ++j) {
+            if (sj < 0) {
+                vs[j] = v[j];
+            } else if (sigma_kind == 1) {
+                vs[j] = (double)sigma[sj][j] * v[j];
+            } else {
+                double acc = 0.0;
+                const float *row = sigma[sj] + (int64_t)j * sigma_ld;
+                for (int32_t k = 0; k < r; ++k) acc += (double)row[k] * v[k];
+                vs[j] = acc;
+            }
+        }
+        for (int32_t o = 0; o < h_out; ++o) {
+            double d = 0.0;
+            const float *bo = B[a] + (int64_t)o * r;
+            for (int32_t j = 0; j < r; ++j) d += (double)bo[j] * vs[j];
+            yt[o] = yt[o] + sc * d;
+        }
+    }
+    free(tok_a);
+    free(tok_s);
+    return 0;
+}

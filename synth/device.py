@@ -84,8 +84,22 @@ class DeviceWorkload:
 
         self.calls = [tuple(c) for c in w.calls]
         self.max_proj = max_proj or max(len(c) for c in self.calls)
-        self.plan = hab.Plan(self.pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+        self.plan = hab.Plan(self.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
+                             seg_sigma=w.seg_sigma if w.sigma_kind else None)
         self.plan.upload(self.max_proj)
+        # cores of jointly compressed adapters: [n][layers][proj][r_max]([r_max])
+        self.sigma = None
+        if w.sigma_kind:
+            used = sorted({int(j) for j in w.seg_sigma if j >= 0})
+            shape = (w.n_cores, w.num_layers, len(w.projs), w.r_max) + (
+                (w.r_max,) if w.sigma_kind == "full" else ())
+            self.sigma = torch.zeros(shape, dtype=torch.float32, device="cuda")
+            for j in used:                 # one copy per core
+                host = np.zeros(shape[1:], np.float32)
+                for l in self.layers:
+                    for p in range(len(w.projs)):
+                        host[l, p] = w.core(j, l, p)
+                self.sigma[j].copy_(torch.from_numpy(host))
         self.y_offsets = []
         for c in self.calls:
             offs, o = [], 0
@@ -118,8 +132,13 @@ class DeviceWorkload:
         for l in self.layers:
             for ci, c in enumerate(self.calls):
                 x = self.x[(l, w.projs[c[0]].x_key)]
-                hab.sgmv_fused(self.pool, self.plan, l, c, self.y_offsets[ci], x,
-                               self.y[(l, ci)], self.base.get((l, ci)), stream=stream)
+                if self.sigma is not None:
+                    hab.sgmv_fused_sigma(self.pool, self.plan, l, c, self.y_offsets[ci], x,
+                                         self.sigma, w.sigma_kind, self.y[(l, ci)],
+                                         self.base.get((l, ci)), stream=stream)
+                else:
+                    hab.sgmv_fused(self.pool, self.plan, l, c, self.y_offsets[ci], x,
+                                   self.y[(l, ci)], self.base.get((l, ci)), stream=stream)
 
     def run_two_step(self, stream=None):
         """The same pass as separate shrink and expand calls through a v buffer."""
@@ -134,8 +153,12 @@ class DeviceWorkload:
                 v = torch.zeros((w.num_tokens, len(c) * w.r_max), dtype=torch.float32,
                                 device="cuda")
                 hab.sgmv_shrink(self.pool, self.plan, l, c, x, v, stream=stream)
-                hab.sgmv_expand(self.pool, self.plan, l, c, self.y_offsets[ci], v, y,
-                                stream=stream)
+                if self.sigma is not None:
+                    hab.sgmv_expand_sigma(self.pool, self.plan, l, c, self.y_offsets[ci], v,
+                                          self.sigma, w.sigma_kind, y, stream=stream)
+                else:
+                    hab.sgmv_expand(self.pool, self.plan, l, c, self.y_offsets[ci], v, y,
+                                    stream=stream)
 
     def output(self, layer: int, p: int) -> np.ndarray:
         """y of projection p at ``layer`` as float32 on the host."""

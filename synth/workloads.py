@@ -32,7 +32,7 @@ import os
 import numpy as np
 
 # Tags that keep the per-block seed tuples of different kinds apart.
-_TAG_MAP, _TAG_RANK, _TAG_W, _TAG_X, _TAG_BASE = 1, 2, 7, 11, 13
+_TAG_MAP, _TAG_RANK, _TAG_W, _TAG_X, _TAG_BASE, _TAG_SIGMA = 1, 2, 7, 11, 13, 17
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -92,6 +92,12 @@ class Workload:
     # Adapter weights drawn for a pin instead of the random recipe:
     # {(adapter, layer, proj): (A, B)}.
     overrides: dict = field(default_factory=dict)
+    # Jointly compressed adapters: the pool entries are shared bases, and
+    # segment s also names core seg_sigma[s] (-1: none) of n_cores cores of
+    # kind sigma_kind ("full": r_max x r_max, "diag": r_max values).
+    seg_sigma: np.ndarray = None
+    n_cores: int = 0
+    sigma_kind: str = None
 
     # ---- derived facts about the draw (pure bookkeeping) ----
     @property
@@ -142,6 +148,23 @@ class Workload:
         a = (g.random((r, pr.h_in), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)) * bound
         b = g.standard_normal((pr.h_out, r), dtype=np.float32) * np.float32(0.02)
         return self._round(a), self._round(b)
+
+    def core(self, j: int, layer: int, p: int) -> np.ndarray:
+        """Core j of (layer, projection p), float32: full cores are the
+        identity plus N(0, 1/r_max) noise, diagonal cores U(0.5, 1.5)."""
+        g = _rng(self.seed, _TAG_SIGMA, j, layer, p)
+        r = self.r_max
+        if self.sigma_kind == "full":
+            c = np.eye(r, dtype=np.float32) + g.standard_normal((r, r), dtype=np.float32) * \
+                np.float32(1.0 / np.sqrt(r))
+            return c.astype(np.float32)
+        return (g.random(r, dtype=np.float32) + np.float32(0.5)).astype(np.float32)
+
+    def core_table(self) -> np.ndarray:
+        """All cores: [n_cores][layers][projections][r_max]([r_max])."""
+        return np.stack([np.stack([np.stack([self.core(j, l, p) for p in range(len(self.projs))])
+                                   for l in range(self.num_layers)])
+                         for j in range(self.n_cores)])
 
     def activation(self, layer: int, key: str) -> np.ndarray:
         """x [T][h_in] float32 for the activation ``key`` of ``layer``."""
@@ -301,3 +324,53 @@ def random_case(seed: int, *, T: int = None, h_in: int = None, h_out: int = None
         seg_starts=np.asarray(cuts, np.int32), seg_adapter=seg_adapter,
         pool_size=n_adapters, ranks=ranks, scales=scales, has_base=has_base,
         r_max=r_max, description="random small case")
+
+
+def jd_case(seed: int, *, kind: str, T: int = 96, h_in: int = 256, h_outs=(192, 64),
+            n_clusters: int = 3, n_cores: int = 6, r_choices=(16, 24, 32), r_max: int = 32,
+            dtype: str = "bf16", has_base: bool = True, max_seg: int = None,
+            num_layers: int = 2, no_core_frac: float = 0.15) -> Workload:
+    """Jointly compressed adapters: each pool entry is a cluster's shared basis
+    (A_c, B_c at the cluster's rank), each segment names a cluster and one of
+    n_cores cores (or -1), some segments no adapter at all.  Projections share
+    one x (a q/k-like pair)."""
+    g = _rng(seed, 97)
+    cuts = [0]
+    while cuts[-1] < T:
+        step = int(g.integers(0, (max_seg or max(2, T // 6)) + 1))
+        cuts.append(min(T, cuts[-1] + step))
+    S = len(cuts) - 1
+    seg_adapter = g.integers(0, n_clusters, S).astype(np.int32)
+    seg_adapter[g.random(S) < 0.1] = -1
+    seg_sigma = g.integers(0, n_cores, S).astype(np.int32)
+    seg_sigma[g.random(S) < no_core_frac] = -1
+    ranks = g.choice(np.asarray(r_choices), n_clusters).astype(np.int32)
+    scales = g.uniform(0.5, 2.0, n_clusters).astype(np.float32)
+    projs = tuple(Proj(f"p{i}", h_in, h, "x") for i, h in enumerate(h_outs))
+    return Workload(
+        name=f"jd_{kind}_{seed}", seed=2000 + seed, dtype=dtype, num_layers=num_layers,
+        projs=projs, calls=(tuple(range(len(projs))),), num_tokens=T,
+        seg_starts=np.asarray(cuts, np.int32), seg_adapter=seg_adapter,
+        pool_size=n_clusters, ranks=ranks, scales=scales, has_base=has_base, r_max=r_max,
+        description=f"jointly compressed adapters ({kind} cores)",
+        seg_sigma=seg_sigma, n_cores=n_cores, sigma_kind=kind)
+
+
+def jd_full_stack(kind: str = "full") -> Workload:
+    """The full Mistral-7B stack served from jointly compressed adapters:
+    1000 adapters in 10 clusters, each cluster one shared rank-32 basis per
+    (layer, projection), each adapter a core; 128 decode tokens whose adapters
+    follow the same bounded Zipf(1.1) draw as the plain full stack."""
+    seed = 5
+    base = config4()
+    ids = base.seg_adapter
+    clusters = (ids % 10).astype(np.int32)
+    return Workload(
+        name=f"jd_full_stack_{kind}", seed=seed, dtype="bf16", num_layers=LAYERS,
+        projs=MISTRAL_PROJS, calls=((0, 1, 2), (3,), (4, 5), (6,)), num_tokens=128,
+        seg_starts=_one_token_segments(128), seg_adapter=clusters,
+        pool_size=10, ranks=np.full(10, 32, np.int32), scales=np.full(10, 1.0, np.float32),
+        has_base=True, r_max=32, seg_sigma=ids.astype(np.int32), n_cores=1000,
+        sigma_kind=kind,
+        description=f"32 layers x 7 projections; 1000 adapters as {kind} cores over 10 shared "
+                    "rank-32 bases; T=S=128, Zipf(1.1); y = base_out + delta")

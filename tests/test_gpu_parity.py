@@ -450,3 +450,99 @@ def test_register_from_device_matches_host():
         hab.sgmv_fused(pool2, plan2, 0, (0,), (0,), dw.x[(0, "x")], y2)
         torch.cuda.synchronize()
         assert np.array_equal(from_device(y2), ref), dtype
+
+
+# ------------------------------------------- jointly compressed adapters ----
+def _jd_check(dw):
+    """Contract tolerance per output tensor, and the delta alone (y - y_in)
+    to a tolerance scaled by the delta plus the single rounding of y."""
+    w = dw.w
+    for l in dw.layers:
+        for p in range(len(w.projs)):
+            got = dw.output(l, p).astype(np.float64)
+            ref = oracle_ref(w, l, p, acc="f64")
+            contract_check(got, ref, f"{w.name} layer {l} proj {p}")
+            y_in = w.base_out(l, p).astype(np.float64) if w.has_base else 0.0
+            d_ref = ref - y_in
+            ulp = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+            lim = 1e-4 * np.abs(d_ref).max() + ulp * np.abs(ref) + 1e-30
+            assert np.all(np.abs((got - y_in) - d_ref) <= lim), f"{w.name} delta {l} {p}"
+
+
+@pytest.mark.parametrize("kind", ["full", "diag"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("prefill", [False, True])
+def test_sigma_parity(kind, dtype, prefill):
+    """The three steps A, Sigma, B ("Compress then Serve", rebuttal pseudocode
+    of add_lora_slice_with_sigma) against the oracle: mixed basis ranks,
+    segments without a core or an adapter, decode blocks or prefill blocks;
+    the fused call and shrink + expand_sigma through v are bit-identical."""
+    from synth import jd_case
+    seed = {("full", "bf16"): 1, ("full", "f32"): 2, ("diag", "bf16"): 3,
+            ("diag", "f32"): 4}[(kind, dtype)] + (10 if prefill else 0)
+    w = jd_case(seed, kind=kind, dtype=dtype, T=200 if prefill else 96,
+                max_seg=120 if prefill else 3)
+    log(f"[parity] {w.name} dtype {dtype} prefill {prefill}")
+    dw = DeviceWorkload(w, threads=4)
+    assert (dw.plan.stats()["max_block_tokens"] > 4) == prefill
+    dw.zero_outputs()
+    dw.run_fused()
+    torch.cuda.synchronize()
+    _jd_check(dw)
+    fused = {k: from_device(v) for k, v in dw.y.items()}
+    dw.zero_outputs()
+    dw.run_two_step()
+    torch.cuda.synchronize()
+    for k, v in dw.y.items():
+        assert np.array_equal(from_device(v).view(np.uint8), fused[k].view(np.uint8)), k
+
+
+def test_sigma_identity_equals_plain_bitexact():
+    """Identity cores (full and diagonal) and a plan without cores all give
+    the plain two-step delta with the shared basis, bit for bit."""
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import jd_case
+    for kind in ("full", "diag"):
+        w = jd_case(21, kind=kind, T=80, max_seg=4)
+        dw = DeviceWorkload(w, threads=4)
+        if kind == "full":
+            dw.sigma.copy_(torch.eye(w.r_max, device="cuda").expand_as(dw.sigma))
+        else:
+            dw.sigma.fill_(1.0)
+        dw.zero_outputs()
+        dw.run_fused()
+        torch.cuda.synchronize()
+        with_cores = {k: from_device(v) for k, v in dw.y.items()}
+        plain = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+        plain.upload(dw.max_proj)
+        for l in dw.layers:
+            for ci, c in enumerate(dw.calls):
+                y = torch.zeros_like(dw.y[(l, ci)])
+                hab.sgmv_fused(dw.pool, plain, l, c, dw.y_offsets[ci],
+                               dw.x[(l, w.projs[c[0]].x_key)], y, dw.base.get((l, ci)))
+                torch.cuda.synchronize()
+                assert np.array_equal(from_device(y).view(np.uint8),
+                                      with_cores[(l, ci)].view(np.uint8)), (kind, l, ci)
+
+
+def test_sigma_call_errors():
+    """A plan naming a core beyond the table, a bad kind, or a wrong table
+    shape is refused before anything runs; y is untouched."""
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import jd_case
+    w = jd_case(22, kind="full", T=40, max_seg=4)
+    dw = DeviceWorkload(w, threads=4)
+    l, c = dw.layers[0], dw.calls[0]
+    x = dw.x[(l, w.projs[c[0]].x_key)]
+    y = dw.y[(l, 0)]
+    y.fill_(3.0)
+    small = dw.sigma[: int(w.seg_sigma.max())].contiguous()       # one core short
+    with pytest.raises(hab.LoraError):
+        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[0], x, small, "full", y)
+    with pytest.raises(ValueError):
+        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[0], x, dw.sigma, "lower", y)
+    with pytest.raises(ValueError):
+        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[0], x, dw.sigma[..., 0].contiguous(),
+                             "full", y)
+    torch.cuda.synchronize()
+    assert bool((y == 3.0).all())

@@ -139,7 +139,97 @@ def pin_b_zero(lib=None, seed=11):
         assert np.array_equal(y, y_in)
 
 
-ALL_PINS = (pin_hand_example, pin_indicator_adapters, pin_merged_weight, pin_b_zero)
+def _sigma_case(seed, *, r=6, h_in=40, h_out=24, T=30, n_clusters=3, n_cores=5):
+    """A small batch of jointly compressed adapters: shared bases per cluster
+    (ids 10, 11, ...), cores 0..n_cores-1, segment (cluster, core) pairs,
+    some segments without an adapter or without a core."""
+    g = np.random.default_rng(seed)
+    bases = {10 + c: _rand_adapter(g, r, h_in, h_out) for c in range(n_clusters)}
+    cuts = np.sort(g.choice(np.arange(1, T), 7, replace=False))
+    starts = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    S = len(starts) - 1
+    segs = g.choice(list(bases) + [-1], S).astype(np.int32)
+    sig = g.integers(-1, n_cores, S).astype(np.int32)
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    return g, x, starts, segs, sig, bases
+
+
+def pin_sigma_identity(lib=None, seed=21):
+    """No core, and the identity core (full and diagonal), both reduce the
+    three steps to plain LoRA: the same values, bit for bit, as the two-step
+    delta with the shared basis as the adapter."""
+    g, x, starts, segs, sig, bases = _sigma_case(seed)
+    r = 6
+    y_in = g.standard_normal((x.shape[0], 24)).astype(np.float32)
+    for acc in ("f32", "f64"):
+        plain = _delta(x, starts, segs, bases, y_in, acc=acc, lib=lib)
+        none = oracle.lora_delta_sigma(x, starts, segs, np.full_like(sig, -1), bases,
+                                       np.zeros((1, r, r), np.float32), "full", y_in,
+                                       acc=acc, lib=lib)
+        eye = oracle.lora_delta_sigma(x, starts, segs, np.maximum(sig, 0), bases,
+                                      np.stack([np.eye(r, dtype=np.float32)] * 5), "full",
+                                      y_in, acc=acc, lib=lib)
+        ones = oracle.lora_delta_sigma(x, starts, segs, np.maximum(sig, 0), bases,
+                                       np.ones((5, r), np.float32), "diag", y_in, acc=acc,
+                                       lib=lib)
+        for got in (none, eye, ones):
+            assert np.array_equal(got, plain), acc
+
+
+def pin_sigma_diag_powers_of_two(lib=None, seed=23):
+    """A diagonal core of powers of two scales rank row j of v exactly, so
+    the three steps equal plain LoRA with A's row j scaled by the same power
+    of two, bit for bit (each segment's core applied to its own copy of A)."""
+    g, x, starts, segs, sig, bases = _sigma_case(seed)
+    r = 6
+    cores = (2.0 ** g.integers(-3, 4, (5, r))).astype(np.float32)
+    for acc in ("f32", "f64"):
+        got = oracle.lora_delta_sigma(x, starts, segs, sig, bases, cores, "diag",
+                                      acc=acc, lib=lib)
+        for si in range(len(segs)):
+            a0, b0 = starts[si], starts[si + 1]
+            if segs[si] < 0 or a0 == b0:
+                continue
+            a, b, s = bases[int(segs[si])]
+            if sig[si] >= 0:
+                a = (a * cores[sig[si]][:, None]).astype(np.float32)
+            ref = _delta(x[a0:b0], [0, b0 - a0], [7], {7: (a, b, s)}, acc=acc, lib=lib)
+            assert np.array_equal(got[a0:b0], ref), (acc, si)
+
+
+def pin_sigma_full_merged(lib=None, seed=29):
+    """A full core: the delta equals the merged product s (B Sigma A) x done
+    by numpy in float64, and a full core that is diagonal equals the
+    diagonal kind exactly."""
+    g, x, starts, segs, sig, bases = _sigma_case(seed)
+    r = 6
+    cores = g.standard_normal((5, r, r)).astype(np.float32)
+    y64 = oracle.lora_delta_sigma(x, starts, segs, sig, bases, cores, "full", acc="f64",
+                                  lib=lib)
+    y32 = oracle.lora_delta_sigma(x, starts, segs, sig, bases, cores, "full", acc="f32",
+                                  lib=lib)
+    ref = np.zeros_like(y64)
+    for si in range(len(segs)):
+        a0, b0 = starts[si], starts[si + 1]
+        if segs[si] < 0:
+            continue
+        a, b, s = (m.astype(np.float64) if isinstance(m, np.ndarray) else m
+                   for m in bases[int(segs[si])])
+        core = np.eye(r) if sig[si] < 0 else cores[sig[si]].astype(np.float64)
+        ref[a0:b0] = x[a0:b0].astype(np.float64) @ (s * b @ core @ a).T
+    scale = np.abs(ref).max()
+    assert np.abs(y64 - ref).max() <= 1e-12 * scale
+    assert np.abs(y32 - ref).max() <= 1e-5 * scale
+    d = g.standard_normal((5, r)).astype(np.float32)
+    full = np.stack([np.diag(v) for v in d]).astype(np.float32)
+    for acc in ("f32", "f64"):
+        assert np.array_equal(
+            oracle.lora_delta_sigma(x, starts, segs, sig, bases, full, "full", acc=acc, lib=lib),
+            oracle.lora_delta_sigma(x, starts, segs, sig, bases, d, "diag", acc=acc, lib=lib))
+
+
+ALL_PINS = (pin_hand_example, pin_indicator_adapters, pin_merged_weight, pin_b_zero,
+            pin_sigma_identity, pin_sigma_diag_powers_of_two, pin_sigma_full_merged)
 
 
 def test_hand_example():
@@ -294,6 +384,26 @@ def test_f32_within_rounding_bound():
             assert np.all(np.abs(y32[t] - y64[t]) <= bound), (w.name, t)
 
 
+def test_sigma_identity():
+    pin_sigma_identity()
+
+
+def test_sigma_diag_powers_of_two():
+    pin_sigma_diag_powers_of_two()
+
+
+def test_sigma_full_merged():
+    pin_sigma_full_merged()
+
+
+def test_sigma_errors():
+    g, x, starts, segs, sig, bases = _sigma_case(31)
+    bad = sig.copy()
+    bad[0] = 5                                            # core index out of range
+    with pytest.raises(oracle.OracleError):
+        oracle.lora_delta_sigma(x, starts, segs, bad, bases, np.ones((5, 6), np.float32), "diag")
+
+
 def test_errors():
     x = np.zeros((4, 8), np.float32)
     ad = {1: (np.zeros((2, 8), np.float32), np.zeros((8, 2), np.float32), 1.0)}
@@ -325,6 +435,14 @@ MUTATIONS = {
     "sign_flip": ("yt[o] = yt[o] + sc * d;", "yt[o] = yt[o] - sc * d;"),
     "no_adapter_uses_first": ("const int32_t a = tok_a[t];",
                               "const int32_t a = tok_a[t] < 0 ? 0 : tok_a[t];"),
+    "sigma_transposed": ("acc += row[k] * v[k];",
+                         "acc += sigma[sj][(int64_t)k * sigma_ld + j] * v[k];"),
+    "sigma_skipped": ("vs[j] = acc;", "vs[j] = v[j];"),
+    "sigma_diag_ignored": ("vs[j] = sigma[sj][j] * v[j];", "vs[j] = v[j];"),
+    "sigma_first_core": ("const int32_t sj = tok_s[t];",
+                         "const int32_t sj = tok_s[t] < 0 ? -1 : 0;"),
+    "sigma_b_reads_buffer": ("for (int32_t j = 0; j < r; ++j) d += bo[j] * vs[j];",
+                             "for (int32_t j = 0; j < r; ++j) d += bo[j] * v[j];"),
 }
 
 
