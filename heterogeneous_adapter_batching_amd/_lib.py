@@ -63,6 +63,8 @@ SIGNATURES = {
     "sgmv_fused": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp, _i64,
                           _vp]),
     "lora_plan_create_sigma": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32p, _i32]),
+    "lora_plan_create_weighted": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p,
+                                         ctypes.POINTER(_f32), _i32]),
     "sgmv_expand_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
                                  _vp, _i64, _vp]),
     "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,

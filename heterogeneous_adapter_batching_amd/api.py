@@ -185,9 +185,12 @@ class Pool:
 class Plan:
     """The gather plan of one heterogeneous batch (built on the host)."""
 
-    def __init__(self, pool: Pool, num_tokens: int, seg_starts, seg_adapter, seg_sigma=None):
+    def __init__(self, pool: Pool, num_tokens: int, seg_starts, seg_adapter, seg_sigma=None,
+                 seg_weight=None):
         """seg_sigma: per-segment core index of jointly compressed adapters
-        (-1: none), or None for plain adapters."""
+        (-1: none), or None for plain adapters.  seg_weight: per-segment
+        weight that scales each token's delta (one slot of a weighted merge),
+        or None."""
         self.lib = pool.lib
         self.pool = pool
         self.num_tokens = int(num_tokens)
@@ -197,7 +200,17 @@ class Plan:
             raise ValueError("seg_starts must have one more entry than seg_adapter")
         self._h = ctypes.c_void_p()
         i32p = ctypes.POINTER(ctypes.c_int32)
-        if seg_sigma is None:
+        if seg_sigma is not None and seg_weight is not None:
+            raise ValueError("a plan takes cores or weights, not both")
+        if seg_weight is not None:
+            wts = np.ascontiguousarray(seg_weight, dtype=np.float32)
+            if wts.shape != segs.shape:
+                raise ValueError("seg_weight must have one entry per segment")
+            check(self.lib.lora_plan_create_weighted(
+                ctypes.byref(self._h), pool.handle, self.num_tokens, starts.ctypes.data_as(i32p),
+                segs.ctypes.data_as(i32p), wts.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                int(segs.shape[0])))
+        elif seg_sigma is None:
             check(self.lib.lora_plan_create(ctypes.byref(self._h), pool.handle, self.num_tokens,
                                             starts.ctypes.data_as(i32p),
                                             segs.ctypes.data_as(i32p), int(segs.shape[0])))
@@ -371,4 +384,15 @@ def sgmv_fused_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, si
                                     base.stride(0) if base is not None else 0,
                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
                                     _stream_handle(stream)))
+    return y
+
+
+def merge_fused(pool: Pool, plans, layer: int, projs, y_offsets, x, y, base=None, stream=None):
+    """Weighted merge of several adapters per request: ``plans`` are weighted
+    plans over the same tokens, one per merge slot; the first is applied over
+    ``base`` (or y), the others add their weighted deltas into y in turn:
+    y = y_in + sum_k (w_k s_k) B_k (A_k x)."""
+    for k, pl in enumerate(plans):
+        sgmv_fused(pool, pl, layer, projs, y_offsets, x, y, base if k == 0 else None,
+                   stream=stream)
     return y

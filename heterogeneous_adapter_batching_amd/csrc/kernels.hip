@@ -331,6 +331,7 @@ struct ExpandCtx {
     int b, p, w, n, q;
     int o_lo, o_hi, yoff, h_out, ks_n, ntiles;
     float scale;
+    float tsc[4];     // the scale of this lane's token in each 16-token tile
 };
 
 // One output element: bf16 (2 bytes) or float32 (4 bytes).
@@ -612,7 +613,12 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
             }
         }
     }
-    const float scale = blk.scale;
+    // the delta's scale per token: the adapter's, times the token's weight
+    // in a weighted plan (one float32 product)
+    float sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        sc[t] = a.tok_w && t < nt ? blk.scale * a.tok_w[blk.tok_off + t] : blk.scale;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
         const int row = o_lo + i * kWaveSize + lane;
@@ -620,7 +626,7 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
 #pragma unroll
         for (int t = 0; t < NT; ++t)                 // y_row[t] is kOOB for t >= nt
             Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
-                           yin[i][t] + scale * d[i][t]);
+                           yin[i][t] + sc[t] * d[i][t]);
     }
 }
 
@@ -751,7 +757,7 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
                 float in[4], out[4];
                 Out4<T>::unpack(yin[ot][tt], in);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) out[i] = in[i] + c.scale * acc[i];
+                for (int i = 0; i < 4; ++i) out[i] = in[i] + c.tsc[tt] * acc[i];
                 Out4<T>::store(yr, o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB,
                                Out4<T>::pack(out));
             }
@@ -873,6 +879,12 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     bool tv[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) tv[tt] = tt < c.ntiles && trow[tt] >= 0;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int i = tt * kTile + c.n;
+        c.tsc[tt] = a.tok_w && tt < TT && i < blk.n_tok ? blk.scale * a.tok_w[blk.tok_off + i]
+                                                       : blk.scale;
+    }
 
     if (blk.r_pad == 0) {            // tokens without an adapter: y = base
         if (!a.base) return;

@@ -5,6 +5,7 @@
 // Nothing here allocates device memory.  Validation happens before anything
 // is enqueued, so an error leaves every object as it was.
 #include <algorithm>
+#include <cmath>
 #include <climits>
 #include <cstdint>
 #include <cstdarg>
@@ -154,6 +155,8 @@ struct lora_plan {
     int32_t T = 0;
     std::vector<int32_t> token_order;    // plan order: grouped adapter tokens, then the rest
     std::vector<int32_t> token_sigma;    // core index per plan-order row (-1: none)
+    std::vector<float> token_weight;     // weight per plan-order row (weighted plans)
+    bool weighted = false;
     int32_t max_sigma = -1;              // largest core index named
     std::vector<int32_t> token_group;    // per token row
     std::vector<int32_t> group_adapter, group_rank;
@@ -166,7 +169,7 @@ struct lora_plan {
     uint64_t ws_bytes = 0;
     int32_t max_proj = 0;
     uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
-             off_part = 0;
+             off_tw = 0, off_part = 0;
     uint64_t image_bytes = 0, part_bytes = 0;
     void *staging = nullptr;
     uint64_t staging_bytes = 0;
@@ -183,6 +186,7 @@ struct lora_plan {
         off_btok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(nb_all(), 1), 256);
         off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(rt_total(), 1), 256);
         off_tsig = o;    o = round_up(o + 4ull * std::max(T, 1), 256);
+        off_tw = o;      o = round_up(o + 4ull * std::max(T, 1), 256);
         image_bytes = o;
         part_bytes = 4ull * max_shrink_units(mp) * tt * lora::kTile * lora::kTile;
         off_part = o;    o = round_up(o + part_bytes, 256);
@@ -401,7 +405,8 @@ lora_status lora_pool_stats(const lora_pool *p, int32_t *num, uint64_t *free_byt
 
 namespace {
 lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const int32_t *seg_starts,
-                        const int32_t *seg_adapter, const int32_t *seg_sigma, int32_t S) {
+                        const int32_t *seg_adapter, const int32_t *seg_sigma,
+                        const float *seg_weight, int32_t S) {
     if (!out) return fail(LORA_EINVAL, "null output pointer");
     if (!p) return fail(LORA_EINVAL, "null pool");
     if (T < 0 || S < 0) return fail(LORA_ESEG, "negative token or segment count");
@@ -418,6 +423,8 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
             return fail(LORA_ENOENT, "segment %d names unregistered adapter %d", s, id);
         if (seg_sigma && seg_sigma[s] < -1)
             return fail(LORA_EINVAL, "segment %d names core %d", s, seg_sigma[s]);
+        if (seg_weight && !std::isfinite(seg_weight[s]))
+            return fail(LORA_EINVAL, "segment %d has a weight that is not finite", s);
     }
 
     lora_plan *pl = new lora_plan();
@@ -536,6 +543,15 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
         pl->token_sigma[i] = row_sigma[pl->token_order[i]];
         pl->max_sigma = std::max(pl->max_sigma, pl->token_sigma[i]);
     }
+    // and each row's weight, in plan order
+    if (seg_weight) {
+        std::vector<float> row_weight(T, 1.0f);
+        for (int32_t s = 0; s < S; ++s)
+            for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) row_weight[t] = seg_weight[s];
+        pl->weighted = true;
+        pl->token_weight.resize(T);
+        for (int32_t i = 0; i < T; ++i) pl->token_weight[i] = row_weight[pl->token_order[i]];
+    }
     *out = pl;
     return LORA_OK;
 }
@@ -545,14 +561,21 @@ extern "C" {
 
 lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t T,
                              const int32_t *seg_starts, const int32_t *seg_adapter, int32_t S) {
-    return plan_create(out, p, T, seg_starts, seg_adapter, nullptr, S);
+    return plan_create(out, p, T, seg_starts, seg_adapter, nullptr, nullptr, S);
+}
+
+lora_status lora_plan_create_weighted(lora_plan **out, const lora_pool *p, int32_t T,
+                                      const int32_t *seg_starts, const int32_t *seg_adapter,
+                                      const float *seg_weight, int32_t S) {
+    if (S > 0 && !seg_weight) return fail(LORA_EINVAL, "null weight table");
+    return plan_create(out, p, T, seg_starts, seg_adapter, nullptr, seg_weight, S);
 }
 
 lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t T,
                                    const int32_t *seg_starts, const int32_t *seg_adapter,
                                    const int32_t *seg_sigma, int32_t S) {
     if (S > 0 && !seg_sigma) return fail(LORA_EINVAL, "null core table");
-    return plan_create(out, p, T, seg_starts, seg_adapter, seg_sigma, S);
+    return plan_create(out, p, T, seg_starts, seg_adapter, seg_sigma, nullptr, S);
 }
 
 lora_status lora_plan_destroy(lora_plan *pl) {
@@ -617,6 +640,8 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     std::memset(img, 0, pl->image_bytes);
     if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
     if (pl->T) std::memcpy(img + pl->off_tsig, pl->token_sigma.data(), 4ull * pl->T);
+    if (pl->T && pl->weighted)
+        std::memcpy(img + pl->off_tw, pl->token_weight.data(), 4ull * pl->T);
     if (!pl->blocks.empty())
         std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
     if (!pl->tiles.empty())
@@ -865,6 +890,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
     a.v_bytes = v ? uint32_t(tensor_bytes(pl->T, ldv, ldv, 4)) : 0u;
+    if (pl->weighted) a.tok_w = reinterpret_cast<const float *>(ws + pl->off_tw);
     if (cores.kind) {
         const int64_t per = cores.kind == LORA_SIGMA_FULL ? int64_t(p->d.r_max) * p->d.r_max
                                                            : int64_t(p->d.r_max);

@@ -156,6 +156,9 @@ struct ExpandArgs {
     // starts at sigma + j * sig_stride + sig_off[i] (floats).
     const float *sigma;
     const int32_t *tok_sig;
+    // Weighted plans: token row tok_off + i of the plan order scales its
+    // delta by blk.scale * tok_w[tok_off + i] (null: by blk.scale).
+    const float *tok_w;
     int64_t sig_stride;
     int64_t sig_off[LORA_MAX_PROJ];
     int32_t sigma_kind;

@@ -169,6 +169,19 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_to
                              const int32_t *seg_starts, const int32_t *seg_adapter,
                              int32_t num_segs);
 
+/* The same with a weight per segment: every call with this plan scales a
+ * token's delta by its segment's weight (with the adapter's scale s: y = y_in
+ * + (w * s) * B (A x), the product w * s rounded to float32 once).  This is
+ * one slot of a weighted merge of adapters per request ("predibase/lorax":
+ * adapters merged per request into a weighted ensemble, read as the linear
+ * merge sum_k w_k s_k B_k A_k): a merge of K adapters is K weighted plans
+ * over the same segments, applied in turn (the first with base, the rest
+ * adding into y).  Errors as lora_plan_create, and LORA_EINVAL for a weight
+ * that is not finite. */
+lora_status lora_plan_create_weighted(lora_plan **out, const lora_pool *p, int32_t num_tokens,
+                                      const int32_t *seg_starts, const int32_t *seg_adapter,
+                                      const float *seg_weight, int32_t num_segs);
+
 /* The same for jointly compressed adapters ("Compress then Serve", rebuttal
  * pseudocode of add_lora_slice_with_sigma): seg_adapter names the pool entry
  * that holds the segment's shared basis A, B (a cluster's), and

@@ -54,6 +54,16 @@ def load_library(path):
                        ctypes.c_int32, ctypes.c_int32, _vpp, ctypes.c_int64,
                        _f32p, ctypes.c_int64,
                        yp, ctypes.c_int64, ctypes.c_int32]
+    for name, yp in (("oracle_delta_merge_f32", _f32p), ("oracle_delta_merge_f64", _f64p)):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                       _f32p, ctypes.c_int64,
+                       ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, _f32p,
+                       ctypes.c_int32, _i32p, _i32p, _f32p,
+                       _vpp, _vpp,
+                       _f32p, ctypes.c_int64,
+                       yp, ctypes.c_int64, ctypes.c_int32]
     return lib
 
 
@@ -197,6 +207,59 @@ def lora_delta_sigma(x, seg_starts, seg_adapter, seg_sigma, adapters, cores, kin
             yin_p, ld_in, yp, h_out, int(threads))
     if rc != 0:
         raise OracleError("malformed segment table, unknown adapter id or core index")
+    return y
+
+
+def lora_delta_merge(x, seg_starts, seg_adapters, seg_weights, adapters, y_in=None, *,
+                     acc="f32", threads=1, lib=None):
+    """Weighted merge of several adapters per request ("predibase/lorax":
+    adapters merged per request into a weighted ensemble):
+    y[t] = y_in[t] + sum_k (w_k s_k) B_k (A_k x[t]), slot by slot.
+
+    seg_adapters, seg_weights: [S][K] int32 / float32 (adapter -1: empty slot)
+    Other arguments as ``lora_delta``.
+    """
+    lib = lib or _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T, h_in = x.shape
+    seg_starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
+    seg_adapters = np.ascontiguousarray(seg_adapters, dtype=np.int32)
+    seg_weights = np.ascontiguousarray(seg_weights, dtype=np.float32)
+    if seg_adapters.ndim != 2 or seg_weights.shape != seg_adapters.shape:
+        raise ValueError("seg_adapters and seg_weights must both be [S][K]")
+    S, K = seg_adapters.shape
+    ids = np.asarray(sorted(adapters), dtype=np.int32)
+    mats = [(np.ascontiguousarray(adapters[i][0], dtype=np.float32),
+             np.ascontiguousarray(adapters[i][1], dtype=np.float32)) for i in ids]
+    if mats:
+        h_out = mats[0][1].shape[0]
+    elif y_in is not None:
+        h_out = np.asarray(y_in).shape[1]
+    else:
+        raise ValueError("h_out unknown: no adapters and no y_in")
+    ranks = np.asarray([a.shape[0] for a, _ in mats], dtype=np.int32)
+    scales = np.asarray([adapters[i][2] for i in ids], dtype=np.float32)
+    n = len(ids)
+    a_ptrs = (ctypes.c_void_p * max(n, 1))(*[m[0].ctypes.data for m in mats])
+    b_ptrs = (ctypes.c_void_p * max(n, 1))(*[m[1].ctypes.data for m in mats])
+    if y_in is not None:
+        y_in = np.ascontiguousarray(y_in, dtype=np.float32)
+        yin_p, ld_in = y_in.ctypes.data_as(_f32p), h_out
+    else:
+        yin_p, ld_in = None, 0
+    if acc == "f32":
+        y = np.empty((T, h_out), dtype=np.float32)
+        fn, yp = lib.oracle_delta_merge_f32, y.ctypes.data_as(_f32p)
+    else:
+        y = np.empty((T, h_out), dtype=np.float64)
+        fn, yp = lib.oracle_delta_merge_f64, y.ctypes.data_as(_f64p)
+    rc = fn(T, h_in, h_out, x.ctypes.data_as(_f32p), h_in, int(S),
+            seg_starts.ctypes.data_as(_i32p), int(K), seg_adapters.ctypes.data_as(_i32p),
+            seg_weights.ctypes.data_as(_f32p), n, ids.ctypes.data_as(_i32p),
+            ranks.ctypes.data_as(_i32p), scales.ctypes.data_as(_f32p), a_ptrs, b_ptrs,
+            yin_p, ld_in, yp, h_out, int(threads))
+    if rc != 0:
+        raise OracleError("malformed segment table or unknown adapter id")
     return y
 
 

@@ -348,3 +348,125 @@ int oracle_delta_sigma_f64(int32_t T, int32_t h_in, int32_t h_out,
     free(tok_s);
     return 0;
 }
+
+/*
+ * Weighted merging of adapters per request ("predibase/lorax" listing:
+ * adapters merged per request into a weighted ensemble): segment s carries
+ * K slots (adapter seg_adapters[s*K + k], weight seg_weights[s*K + k]), and
+ *
+ *   y[t] = y_in[t] + sum_k (w_k * s_k) * B_k (A_k x[t])
+ *
+ * summed slot by slot in k order (the product w_k * s_k rounded to float
+ * first), each slot's delta as in oracle_delta_f32.  Reading: the merge is
+ * linear in the adapters' deltas (the same as merging their low-rank
+ * updates B A with those weights); a slot with adapter -1 adds nothing.
+ * Returns -1 for a malformed segment table or an unknown adapter id.
+ */
+int oracle_delta_merge_f32(int32_t T, int32_t h_in, int32_t h_out,
+                           const float *x, int64_t ldx,
+                           int32_t S, const int32_t *seg_starts, int32_t K,
+                           const int32_t *seg_adapters, const float *seg_weights,
+                           int32_t n_adapters, const int32_t *adapter_ids,
+                           const int32_t *ranks, const float *scales,
+                           const float *const *A, const float *const *B,
+                           const float *y_in, int64_t ld_in,
+                           float *y_out, int64_t ld_out, int32_t threads)
+{
+    if (K < 1 || check_segments(T, S, seg_starts)) return -1;
+    int32_t *slot_a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S * K > 0 ? S * K : 1));
+    if (!slot_a) return -1;
+    for (int32_t i = 0; i < S * K; ++i) {
+        slot_a[i] = -1;
+        if (seg_adapters[i] != -1) {
+            slot_a[i] = find_adapter(n_adapters, adapter_ids, seg_adapters[i]);
+            if (slot_a[i] < 0) { free(slot_a); return -1; }
+        }
+    }
+    const int32_t r_big = max_rank(n_adapters, ranks);
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
+    for (int32_t s = 0; s < S; ++s) {
+        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) {
+            float v[r_big];
+            float *yt = y_out + (int64_t)t * ld_out;
+            for (int32_t o = 0; o < h_out; ++o)
+                yt[o] = y_in ? y_in[(int64_t)t * ld_in + o] : 0.0f;
+            const float *xt = x + (int64_t)t * ldx;
+            for (int32_t k = 0; k < K; ++k) {
+                const int32_t a = slot_a[s * K + k];
+                if (a < 0) continue;
+                const int32_t r = ranks[a];
+                const float sw = seg_weights[s * K + k] * scales[a];
+                for (int32_t j = 0; j < r; ++j) {
+                    float acc = 0.0f;
+                    const float *aj = A[a] + (int64_t)j * h_in;
+                    for (int32_t kk = 0; kk < h_in; ++kk) acc += aj[kk] * xt[kk];
+                    v[j] = acc;
+                }
+                for (int32_t o = 0; o < h_out; ++o) {
+                    float d = 0.0f;
+                    const float *bo = B[a] + (int64_t)o * r;
+                    for (int32_t j = 0; j < r; ++j) d += bo[j] * v[j];
+                    yt[o] = yt[o] + sw * d;
+                }
+            }
+        }
+    }
+    free(slot_a);
+    return 0;
+}
+
+/* The same merge with double accumulation; y_out is double. */
+int oracle_delta_merge_f64(int32_t T, int32_t h_in, int32_t h_out,
+                           const float *x, int64_t ldx,
+                           int32_t S, const int32_t *seg_starts, int32_t K,
+                           const int32_t *seg_adapters, const float *seg_weights,
+                           int32_t n_adapters, const int32_t *adapter_ids,
+                           const int32_t *ranks, const float *scales,
+                           const float *const *A, const float *const *B,
+                           const float *y_in, int64_t ld_in,
+                           double *y_out, int64_t ld_out, int32_t threads)
+{
+    if (K < 1 || check_segments(T, S, seg_starts)) return -1;
+    int32_t *slot_a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(S * K > 0 ? S * K : 1));
+    if (!slot_a) return -1;
+    for (int32_t i = 0; i < S * K; ++i) {
+        slot_a[i] = -1;
+        if (seg_adapters[i] != -1) {
+            slot_a[i] = find_adapter(n_adapters, adapter_ids, seg_adapters[i]);
+            if (slot_a[i] < 0) { free(slot_a); return -1; }
+        }
+    }
+    const int32_t r_big = max_rank(n_adapters, ranks);
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
+    for (int32_t s = 0; s < S; ++s) {
+        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) {
+            double v[r_big];
+            double *yt = y_out + (int64_t)t * ld_out;
+            for (int32_t o = 0; o < h_out; ++o)
+                yt[o] = y_in ? (double)y_in[(int64_t)t * ld_in + o] : 0.0;
+            const float *xt = x + (int64_t)t * ldx;
+            for (int32_t k = 0; k < K; ++k) {
+                const int32_t a = slot_a[s * K + k];
+                if (a < 0) continue;
+                const int32_t r = ranks[a];
+                const double sw = (double)seg_weights[s * K + k] * (double)scales[a];
+                for (int32_t j = 0; j < r; ++j) {
+                    double acc = 0.0;
+                    const float *aj = A[a] + (int64_t)j * h_in;
+                    for (int32_t kk = 0; kk < h_in; ++kk) acc += (double)aj[kk] * (double)xt[kk];
+                    v[j] = acc;
+                }
+                for (int32_t o = 0; o < h_out; ++o) {
+                    double d = 0.0;
+                    const float *bo = B[a] + (int64_t)o * r;
+                    for (int32_t j = 0; j < r; ++j) d += (double)bo[j] * v[j];
+                    yt[o] = yt[o] + sw * d;
+                }
+            }
+        }
+    }
+    free(slot_a);
+    return 0;
+}

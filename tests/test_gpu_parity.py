@@ -546,3 +546,97 @@ def test_sigma_call_errors():
                              "full", y)
     torch.cuda.synchronize()
     assert bool((y == 3.0).all())
+
+
+# ----------------------------------------------------------- weighted merge ----
+def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=5):
+    """A pool of n_adapters (mixed ranks) and K merge slots per segment: a
+    plain random batch gives the segments; each slot draws its own adapters
+    (or -1) and weights."""
+    import heterogeneous_adapter_batching_amd as hab
+    w = random_case(seed, T=T, h_in=h_in, h_out=h_out, n_adapters=n_adapters,
+                    r_choices=[8, 16, 32], dtype=dtype, max_seg=max_seg, has_base=True,
+                    r_max=32)
+    g = np.random.default_rng(seed)
+    S = w.num_segs
+    seg_ad = g.integers(-1, n_adapters, (S, K)).astype(np.int32)
+    seg_ad[:, 0] = w.seg_adapter                            # slot 0: the batch's own draw
+    seg_w = g.uniform(-1.0, 1.5, (S, K)).astype(np.float32)
+    dw = DeviceWorkload(w, upload=np.arange(n_adapters), threads=4)
+    plans = []
+    for k in range(K):
+        pl = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, seg_ad[:, k], seg_weight=seg_w[:, k])
+        pl.upload(1)
+        plans.append(pl)
+    return w, dw, plans, seg_ad, seg_w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("prefill", [False, True])
+def test_merge_parity(dtype, prefill):
+    """K = 3 adapters merged per request with weights (one weighted plan per
+    slot, applied in turn) against the oracle's merge."""
+    import heterogeneous_adapter_batching_amd as hab
+    seed = (31 if dtype == "bf16" else 32) + (10 if prefill else 0)
+    w, dw, plans, seg_ad, seg_w = _merge_setup(seed, K=3, dtype=dtype,
+                                               T=160 if prefill else 64,
+                                               max_seg=100 if prefill else 3)
+    log(f"[parity] merge {w.name} {dtype} prefill {prefill}")
+    assert (plans[0].stats()["max_block_tokens"] > 4) == prefill
+    x = dw.x[(0, "x")]
+    y = torch.zeros_like(dw.y[(0, 0)])
+    hab.merge_fused(dw.pool, plans, 0, (0,), [0], x, y, dw.base[(0, 0)])
+    torch.cuda.synchronize()
+    adapters = {}
+    for a in range(w.pool_size):
+        A, B = w.adapter_block(a, 0, 0)
+        adapters[a] = (A, B, float(w.scales[a]))
+    y_in = w.base_out(0, 0)
+    ref = oracle.lora_delta_merge(w.activation(0, "x"), w.seg_starts, seg_ad, seg_w, adapters,
+                                  y_in, acc="f64", threads=4)
+    got = from_device(y).astype(np.float64)
+    contract_check(got, ref, f"merge {w.name}")
+    # the delta alone: y is rounded to the output type once per slot, each
+    # rounding at most 2^-8 (bf16) or 2^-24 (f32) of the partial sum it
+    # rounds, which the oracle gives for slots 0..k
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    d_ref = ref - y_in
+    lim = 1e-4 * np.abs(d_ref).max() + 1e-30
+    for k in range(1, seg_ad.shape[1] + 1):
+        part = ref if k == seg_ad.shape[1] else oracle.lora_delta_merge(
+            w.activation(0, "x"), w.seg_starts, seg_ad[:, :k], seg_w[:, :k], adapters,
+            y_in, acc="f64", threads=4)
+        lim = lim + ulp * np.abs(part)
+    err = np.abs((got - y_in) - d_ref)
+    assert np.all(err <= lim), float((err / lim).max())
+
+
+def test_weight_one_equals_plain_bitexact():
+    """A weighted plan with every weight 1 gives the plain plan's output bit
+    for bit (decode and prefill blocks)."""
+    import heterogeneous_adapter_batching_amd as hab
+    for seed, max_seg in ((51, 3), (52, 100)):
+        w = random_case(seed, T=120, h_in=256, h_out=128, n_adapters=4, r_choices=[16, 32],
+                        has_base=True, max_seg=max_seg, r_max=32)
+        dw = DeviceWorkload(w, threads=4)
+        ones = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
+                        seg_weight=np.ones(w.num_segs, np.float32))
+        ones.upload(1)
+        x = dw.x[(0, "x")]
+        y1 = torch.zeros_like(dw.y[(0, 0)])
+        y2 = torch.zeros_like(dw.y[(0, 0)])
+        hab.sgmv_fused(dw.pool, dw.plan, 0, (0,), [0], x, y1, dw.base[(0, 0)])
+        hab.sgmv_fused(dw.pool, ones, 0, (0,), [0], x, y2, dw.base[(0, 0)])
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(y1).view(np.uint8), from_device(y2).view(np.uint8))
+
+
+def test_weight_errors():
+    """A weight that is not finite is refused when the plan is built."""
+    import heterogeneous_adapter_batching_amd as hab
+    w = random_case(53, T=20, h_in=64, h_out=32)
+    dw = DeviceWorkload(w, threads=4)
+    bad = np.ones(w.num_segs, np.float32)
+    bad[-1] = np.inf
+    with pytest.raises(hab.LoraError):
+        hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter, seg_weight=bad)

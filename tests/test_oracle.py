@@ -228,8 +228,84 @@ def pin_sigma_full_merged(lib=None, seed=29):
             oracle.lora_delta_sigma(x, starts, segs, sig, bases, d, "diag", acc=acc, lib=lib))
 
 
+def _merge_case(seed, *, K=3, T=36, h_in=40, h_out=24, n_adapters=5):
+    g = np.random.default_rng(seed)
+    adapters = {i: _rand_adapter(g, int(g.integers(1, 9)), h_in, h_out) for i in range(n_adapters)}
+    cuts = np.sort(g.choice(np.arange(1, T), 6, replace=False))
+    starts = np.concatenate([[0], cuts, [T]]).astype(np.int32)
+    S = len(starts) - 1
+    seg_ad = g.integers(-1, n_adapters, (S, K)).astype(np.int32)
+    seg_w = g.uniform(-1.5, 1.5, (S, K)).astype(np.float32)
+    x = g.standard_normal((T, h_in)).astype(np.float32)
+    y_in = g.standard_normal((T, h_out)).astype(np.float32)
+    return g, x, starts, seg_ad, seg_w, adapters, y_in
+
+
+def pin_merge_one_slot(lib=None, seed=41):
+    """One slot of weight 1 is the plain delta, bit for bit; a slot of weight
+    2^e equals the plain delta of that adapter with its scale times 2^e."""
+    g, x, starts, seg_ad, seg_w, adapters, y_in = _merge_case(seed, K=1)
+    for acc in ("f32", "f64"):
+        ones = np.ones_like(seg_w)
+        assert np.array_equal(
+            oracle.lora_delta_merge(x, starts, seg_ad, ones, adapters, y_in, acc=acc, lib=lib),
+            _delta(x, starts, seg_ad[:, 0], adapters, y_in, acc=acc, lib=lib))
+        e = int(g.integers(-3, 4))
+        pw = np.full_like(seg_w, 2.0 ** e)
+        scaled = {i: (a, b, s * 2.0 ** e) for i, (a, b, s) in adapters.items()}
+        assert np.array_equal(
+            oracle.lora_delta_merge(x, starts, seg_ad, pw, adapters, y_in, acc=acc, lib=lib),
+            _delta(x, starts, seg_ad[:, 0], scaled, y_in, acc=acc, lib=lib))
+
+
+def pin_merge_slots_in_order(lib=None, seed=43):
+    """K slots equal K plain deltas applied one after the other (each on the
+    previous result), with the scales times power-of-two weights: bit for bit."""
+    g, x, starts, seg_ad, seg_w, adapters, y_in = _merge_case(seed, K=3)
+    pw = (2.0 ** g.integers(-2, 3, seg_w.shape)).astype(np.float32)
+    for acc in ("f32",):
+        got = oracle.lora_delta_merge(x, starts, seg_ad, pw, adapters, y_in, acc=acc, lib=lib)
+        y = y_in
+        for k in range(seg_ad.shape[1]):
+            # per segment, the slot's adapter at its weighted scale: one
+            # adapter id per (segment, slot) pair
+            ad, segs = {}, []
+            for si in range(len(seg_ad)):
+                a = int(seg_ad[si, k])
+                if a < 0:
+                    segs.append(-1)
+                    continue
+                key = 1000 * si + a
+                A, B, s = adapters[a]
+                ad[key] = (A, B, float(np.float32(pw[si, k]) * np.float32(s)))
+                segs.append(key)
+            y = _delta(x, starts, segs, ad, y, acc=acc, lib=lib) if ad else y
+        assert np.array_equal(got, y)
+
+
+def pin_merge_merged_weight(lib=None, seed=47):
+    """The merge equals x (sum_k w_k s_k B_k A_k)^T per segment, by numpy in
+    float64; a weight of 0 leaves y_in."""
+    g, x, starts, seg_ad, seg_w, adapters, y_in = _merge_case(seed, K=3)
+    y64 = oracle.lora_delta_merge(x, starts, seg_ad, seg_w, adapters, y_in, acc="f64", lib=lib)
+    ref = y_in.astype(np.float64).copy()
+    for si in range(len(seg_ad)):
+        W = np.zeros((24, 40))
+        for k in range(seg_ad.shape[1]):
+            a = int(seg_ad[si, k])
+            if a >= 0:
+                A, B, s = adapters[a]
+                W += float(seg_w[si, k]) * s * (B.astype(np.float64) @ A.astype(np.float64))
+        ref[starts[si]:starts[si + 1]] += x[starts[si]:starts[si + 1]].astype(np.float64) @ W.T
+    assert np.abs(y64 - ref).max() <= 1e-12 * np.abs(ref).max()
+    zero = oracle.lora_delta_merge(x, starts, seg_ad, np.zeros_like(seg_w), adapters, y_in,
+                                   acc="f32", lib=lib)
+    assert np.all(zero == y_in)
+
+
 ALL_PINS = (pin_hand_example, pin_indicator_adapters, pin_merged_weight, pin_b_zero,
-            pin_sigma_identity, pin_sigma_diag_powers_of_two, pin_sigma_full_merged)
+            pin_sigma_identity, pin_sigma_diag_powers_of_two, pin_sigma_full_merged,
+            pin_merge_one_slot, pin_merge_slots_in_order, pin_merge_merged_weight)
 
 
 def test_hand_example():
@@ -396,6 +472,18 @@ def test_sigma_full_merged():
     pin_sigma_full_merged()
 
 
+def test_merge_one_slot():
+    pin_merge_one_slot()
+
+
+def test_merge_slots_in_order():
+    pin_merge_slots_in_order()
+
+
+def test_merge_merged_weight():
+    pin_merge_merged_weight()
+
+
 def test_sigma_errors():
     g, x, starts, segs, sig, bases = _sigma_case(31)
     bad = sig.copy()
@@ -443,6 +531,12 @@ MUTATIONS = {
                          "const int32_t sj = tok_s[t] < 0 ? -1 : 0;"),
     "sigma_b_reads_buffer": ("for (int32_t j = 0; j < r; ++j) d += bo[j] * vs[j];",
                              "for (int32_t j = 0; j < r; ++j) d += bo[j] * v[j];"),
+    "merge_weight_dropped": ("const float sw = seg_weights[s * K + k] * scales[a];",
+                             "const float sw = scales[a];"),
+    "merge_first_slot_only": ("for (int32_t k = 0; k < K; ++k) {\n                const int32_t a = slot_a",
+                              "for (int32_t k = 0; k < 1; ++k) {\n                const int32_t a = slot_a"),
+    "merge_y_in_per_slot": ("yt[o] = yt[o] + sw * d;",
+                            "yt[o] = (y_in ? y_in[(int64_t)t * ld_in + o] : 0.0f) + sw * d;"),
 }
 
 
