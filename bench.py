@@ -139,6 +139,129 @@ def cpu_baseline(w, blocks, layers, threads, min_seconds):
                       f"{threads} OpenMP threads, {t_total:.2f} s"}
 
 
+def _time_graph(fn, stream, warmup, steps):
+    """ms per call of fn, captured in a HIP graph and replayed on stream."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / steps
+
+
+def base_stack(w, stream, warmup, steps):
+    """The base model's own projections on the same tokens: per layer and
+    call, y = x W with W the call's (h_in, sum of h_out) bf16 weight, every
+    layer with weights of its own (so nothing is served from cache across
+    layers).  Returns (ms per pass, weight bytes)."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    mats, xs, ys, nbytes = [], {}, [], 0
+    for key in w.x_keys():
+        xs[key] = torch.randn((w.num_tokens, w.x_width(key)), generator=gen, device="cuda",
+                              dtype=torch.float32).to(dt)
+    for _ in range(w.num_layers):
+        for c in w.calls:
+            h_in = w.projs[c[0]].h_in
+            width = sum(w.projs[p].h_out for p in c)
+            wt = torch.empty((h_in, width), device="cuda", dtype=dt).normal_(
+                0.0, h_in ** -0.5, generator=gen)
+            mats.append((w.projs[c[0]].x_key, wt))
+            ys.append(torch.empty((w.num_tokens, width), device="cuda", dtype=dt))
+            nbytes += wt.numel() * wt.element_size()
+
+    def fn():
+        for (key, wt), y in zip(mats, ys):
+            torch.mm(xs[key], wt, out=y)
+
+    ms = _time_graph(fn, stream, warmup, steps)
+    del mats, xs, ys
+    torch.cuda.empty_cache()
+    return ms, nbytes
+
+
+def sweep(args):
+    """Delta time of the full stack against the number of distinct adapters
+    in the batch and against the skew of a Zipf draw, beside the base model's
+    own projection GEMMs on the same 128 decode tokens."""
+    import torch
+    import heterogeneous_adapter_batching_amd as hab
+    from dataclasses import replace
+    from synth import default_threads, sweep_assignments, sweep_stack
+    from synth.device import DeviceWorkload
+
+    hab.load()
+    torch.cuda.set_device(0)
+    w = sweep_stack(128)
+    t0 = time.perf_counter()
+    dw = DeviceWorkload(w, upload=np.arange(w.pool_size), threads=default_threads())
+    torch.cuda.synchronize()
+    log(f"[sweep] staged {w.name}: {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.Stream()
+    base_ms, base_bytes = base_stack(w, stream, args.warmup, args.steps)
+    log(f"[sweep] base projections: {base_ms:.4f} ms, {base_bytes / 1e9:.3f} GB of weights, "
+        f"{base_bytes / (base_ms * 1e-3) / 1e9:.1f} GB/s")
+    est_ms = base_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    points = []
+    for label, params, ids in sweep_assignments(w.num_tokens, w.pool_size):
+        wp = replace(w, seg_adapter=ids)
+        dw.plan = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, ids)
+        dw.plan.upload(dw.max_proj)
+        ms = _time_graph(dw.run_fused, stream, args.warmup, args.steps)
+        alg = algorithmic(wp)
+        st = dw.plan.stats()
+        pt = {"label": label, **params, "distinct": int(len(wp.touched())),
+              "active_tokens": alg["active_tokens"], "ms": round(ms, 5),
+              "vs_base": round(ms / base_ms, 4), "vs_base_estimate": round(ms / est_ms, 4),
+              "adapter_bytes": alg["adapter"], "bytes": alg["bytes"],
+              "gbs": round(alg["bytes"] / (ms * 1e-3) / 1e9, 1),
+              "groups": st["groups"], "max_block_tokens": st["max_block_tokens"]}
+        points.append(pt)
+        log(f"[sweep] {label:14s} distinct {pt['distinct']:4d}  {ms:.4f} ms  "
+            f"x{pt['vs_base']:.3f} of base  adapter {alg['adapter'] / 1e9:.3f} GB  "
+            f"{pt['gbs']:.0f} GB/s")
+    out = {"metric": "LoRA-delta ms per step vs distinct adapters and Zipf skew, 1 GPU",
+           "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "dtype": w.dtype, "data": "synthetic",
+           "config": {"workload": w.name, "description": w.description,
+                      "tokens": w.num_tokens, "layers": w.num_layers, "mode": "graph"},
+           "base": {"ms": round(base_ms, 5), "weight_bytes": base_bytes,
+                    "estimate_ms_at_peak": round(est_ms, 5)},
+           "points": points}
+    if args.sweep_out:
+        lines = ["# LoRA delta vs distinct adapters and Zipf skew (full stack, 128 decode tokens)",
+                 f"command: python bench.py --sweep --steps {args.steps} --warmup {args.warmup} "
+                 f"--sweep-out {args.sweep_out}",
+                 f"base projections (torch.mm, bf16, graph): {base_ms:.4f} ms for "
+                 f"{base_bytes / 1e9:.3f} GB of weights "
+                 f"({base_bytes / (base_ms * 1e-3) / 1e9:.0f} GB/s); at 8 TB/s: {est_ms:.4f} ms",
+                 "",
+                 f"{'point':14s} {'distinct':>8s} {'groups':>6s} {'ms':>8s} {'x base':>7s} "
+                 f"{'adapter GB':>10s} {'GB/s':>6s}"]
+        for p in points:
+            lines.append(f"{p['label']:14s} {p['distinct']:8d} {p['groups']:6d} {p['ms']:8.4f} "
+                         f"{p['vs_base']:7.3f} {p['adapter_bytes'] / 1e9:10.3f} {p['gbs']:6.0f}")
+        with open(args.sweep_out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,12 +279,17 @@ def main():
                     help="minimum oracle time of the CPU baseline")
     ap.add_argument("--copy-mib", type=int, default=2048,
                     help="size of the device-copy bandwidth reference (0: skip)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: delta time vs distinct adapters and Zipf skew")
+    ap.add_argument("--sweep-out", default=None, help="text summary of the sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the delta shards over GPUs by request without any exchange; see DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        return sweep(args)
 
     import torch
     import heterogeneous_adapter_batching_amd as hab

@@ -192,7 +192,8 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     for (int tt = 0; tt < TT; ++tt) red[w][tt][lane] = acc[tt];
     __syncthreads();
     float *pt = a.partial + size_t(u) * (TT * kTile * kTile);
-    for (int i = threadIdx.x; i < TT * kWaveSize; i += kWaves * kWaveSize) {
+    for (int i = threadIdx.x; i < ntiles * kWaveSize; i += kWaves * kWaveSize) {
+        // token tiles past the block's last are never read: not stored
         const int tt = i / kWaveSize, ln = i % kWaveSize;
         const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
         // partials are read once, by the next kernel

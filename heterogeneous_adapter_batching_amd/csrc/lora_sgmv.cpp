@@ -160,7 +160,10 @@ struct lora_plan {
     int32_t max_sigma = -1;              // largest core index named
     std::vector<int32_t> token_group;    // per token row
     std::vector<int32_t> group_adapter, group_rank;
-    std::vector<BlockDesc> blocks;       // adapter blocks [0, nb_act), no-adapter blocks after
+    // adapter blocks [0, nb_act): the long groups' [0, nb_long), then the
+    // short groups' by padded rank; no-adapter blocks after
+    std::vector<BlockDesc> blocks;
+    int32_t nb_long = 0;
     std::vector<lora::TileDesc> tiles;   // rank tiles of the adapter blocks, in block order
     int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0;
 
@@ -460,19 +463,19 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
         if (pl->token_group[t] < 0) idle.push_back(t);
 
     // Two levels of blocks.  Shrink blocks: each group cut into near-equal
-    // blocks of at most one 16-token tile (64 tokens, 4 tiles, once some
-    // group has kLongGroup tokens); the shrink reads the adapter's A once per
-    // shrink block and per 16-rank tile of it (the rank tiles are its units).
-    // Expand blocks: in a decode-like batch each shrink block is cut again
-    // into near-equal blocks of at most kDecodeBlockTokens tokens, so that
-    // the expand's units move about the same bytes whatever a group's size;
-    // otherwise they are the shrink blocks.  An expand block names its shrink
+    // blocks of at most one 16-token tile (64 tokens, 4 tiles, for a long
+    // group); the shrink reads the adapter's A once per shrink block and per
+    // 16-rank tile of it (the rank tiles are its units).  Expand blocks: a
+    // short group's shrink blocks are cut again into near-equal blocks of at
+    // most kDecodeBlockTokens tokens, so that the decode expand's units move
+    // about the same bytes whatever a group's size; a long group's are its
+    // shrink blocks, for the MFMA expand.  An expand block names its shrink
     // block's first rank tile and its first token slot in it.
-    size_t longest = 0;
-    for (auto &m : members) longest = std::max(longest, m.size());
-    const bool prefill = longest >= size_t(lora::kLongGroup);
-    const int32_t smax = prefill ? lora::kMaxBlockTokens : lora::kTile;
-    const int32_t emax = prefill ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
+    size_t long_tokens = 0;
+    for (auto &m : members)
+        if (m.size() >= size_t(lora::kLongGroup)) long_tokens += m.size();
+    const bool use_long = long_tokens >= size_t(lora::kMinLongTokens);
+    std::vector<BlockDesc> long_blocks, short_blocks;
     auto cut = [](int32_t n, int32_t m, std::vector<int32_t> *sizes) {
         sizes->clear();
         const int32_t k = (n + m - 1) / m;
@@ -483,6 +486,9 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
     auto add_group = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
         const int32_t base = int32_t(pl->token_order.size());
         const int32_t rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
+        const bool lg = sl && use_long && toks.size() >= size_t(lora::kLongGroup);
+        const int32_t smax = lg ? lora::kMaxBlockTokens : lora::kTile;
+        const int32_t emax = lg ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
         cut(int32_t(toks.size()), smax, &ssz);
         int32_t s0 = 0;
         for (int32_t sn : ssz) {
@@ -511,7 +517,7 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
                 bd.rt_before = rt_before;
                 bd.ext_lo = sl ? uint32_t(sl->off & 0xffffffffu) : 0u;
                 bd.ext_hi = sl ? uint32_t(sl->off >> 32) : 0u;
-                pl->blocks.push_back(bd);
+                (lg ? long_blocks : short_blocks).push_back(bd);
                 pl->max_block = std::max(pl->max_block, en);
                 e0 += en;
             }
@@ -521,14 +527,19 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
     };
     for (int32_t g = 0; g < int32_t(members.size()); ++g)
         add_group(members[g], g, &p->slots.at(pl->group_adapter[g]));
-    pl->nb_act = int32_t(pl->blocks.size());
-    pl->n_active = int32_t(pl->token_order.size());
-    add_group(idle, -1, nullptr);
-    // The expand visits the adapter blocks by padded rank, largest first
+    // The decode expand visits the short blocks by padded rank, largest first
     // (stable within a rank): its units are equal in bytes within a rank, the
     // costliest are dealt first, and the rank is uniform over a range of units.
-    std::stable_sort(pl->blocks.begin(), pl->blocks.begin() + pl->nb_act,
+    std::stable_sort(short_blocks.begin(), short_blocks.end(),
                      [](const BlockDesc &x, const BlockDesc &y) { return x.r_pad > y.r_pad; });
+    pl->blocks = long_blocks;
+    pl->blocks.insert(pl->blocks.end(), short_blocks.begin(), short_blocks.end());
+    pl->nb_long = int32_t(long_blocks.size());
+    pl->nb_act = int32_t(pl->blocks.size());
+    pl->n_active = int32_t(pl->token_order.size());
+    short_blocks.clear();
+    add_group(idle, -1, nullptr);
+    pl->blocks.insert(pl->blocks.end(), short_blocks.begin(), short_blocks.end());
     for (int32_t b = 0; b < pl->nb_act; ++b)
         pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
     const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
@@ -901,10 +912,34 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         for (int i = 0; i < nproj; ++i)
             a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;
     }
-    const bool decode = pl->max_block <= lora::kValuTokens;   // blocks of the decode expand
-    const int32_t ks = plan_ksteps(p, pl);
-    if (decode) {
-        // rank classes: runs of equal padded rank in block order (adapter
+    // The long groups' blocks [0, nb_long) go to the MFMA expand, the rest
+    // (short groups' blocks, then the blocks without an adapter) to the decode
+    // expand: two launches on the stream when a batch has both.
+    const int32_t nl = std::min(pl->nb_long, nb);
+    if (nl > 0) {
+        // K-steps of the largest padded rank fix the rows per wave (the wave
+        // keeps 8 B fragments); 4 waves per workgroup; row chunks per wave:
+        // about kTargetGroups workgroups per launch
+        lora::ExpandArgs m = a;
+        const int32_t ks = plan_ksteps(p, pl);
+        const int64_t chunk_rows = int64_t(16 * lora::expand_tiles(ks)) * lora::kWaves;
+        int64_t rows = 0;
+        for (int i = 0; i < nproj; ++i) rows += m.h_out[i];
+        m.nb = nl;
+        m.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
+            8, rows * nl / (chunk_rows * lora::kTargetGroups))));
+        const int32_t rows_per_group = int32_t(chunk_rows) * m.chunks;
+        m.oc_prefix[0] = 0;
+        for (int i = 0; i < nproj; ++i)
+            m.oc_prefix[i + 1] = m.oc_prefix[i] + (m.h_out[i] + rows_per_group - 1) / rows_per_group;
+        for (int i = nproj; i < LORA_MAX_PROJ; ++i) m.oc_prefix[i + 1] = INT32_MAX;
+        m.units = nl * m.oc_prefix[nproj];
+        m.grid = grid_for(m.units, 1);
+        const hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, ks, m, st);
+        if (e != hipSuccess) return hip_fail(e, "expand launch");
+    }
+    if (nb > nl) {
+        // rank classes: runs of equal padded rank in block order (short
         // blocks by rank, largest first; then the blocks without an adapter)
         for (int k = 0; k < lora::kMaxClasses; ++k) {
             lora::DecodeClass &dc = a.cls[k];
@@ -912,7 +947,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
             for (int i = 0; i <= LORA_MAX_PROJ; ++i) dc.prefix[i] = INT32_MAX;
         }
         int32_t ncls = 0, units = 0;
-        for (int32_t b = 0; b < nb;) {
+        for (int32_t b = nl; b < nb;) {
             const int32_t r = pl->blocks[b].r_pad;
             int32_t e = b;
             while (e < nb && pl->blocks[e].r_pad == r) ++e;
@@ -933,26 +968,10 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         }
         for (int k = ncls; k <= lora::kMaxClasses; ++k) a.cls_unit0[k] = k == ncls ? units : INT32_MAX;
         a.units = units;
-    } else {
-        // K-steps of the largest padded rank fix the rows per wave (the wave
-        // keeps 8 B fragments); 4 waves per workgroup; row chunks per wave:
-        // about kTargetGroups workgroups per launch
-        const int64_t chunk_rows = int64_t(16 * lora::expand_tiles(ks)) * lora::kWaves;
-        int64_t rows = 0;
-        for (int i = 0; i < nproj; ++i) rows += a.h_out[i];
-        a.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
-            8, rows * nb / (chunk_rows * lora::kTargetGroups))));
-        const int32_t rows_per_group = int32_t(chunk_rows) * a.chunks;
-        a.oc_prefix[0] = 0;
-        for (int i = 0; i < nproj; ++i)
-            a.oc_prefix[i + 1] = a.oc_prefix[i] + (a.h_out[i] + rows_per_group - 1) / rows_per_group;
-        for (int i = nproj; i < LORA_MAX_PROJ; ++i) a.oc_prefix[i + 1] = INT32_MAX;
-        a.units = nb * a.oc_prefix[nproj];
+        a.grid = grid_for(a.units, 1);
+        const hipError_t e = lora::launch_expand_decode(p->d.dtype, a, st);
+        if (e != hipSuccess) return hip_fail(e, "expand launch");
     }
-    a.grid = grid_for(a.units, 1);
-    hipError_t e = decode ? lora::launch_expand_decode(p->d.dtype, a, st)
-                          : lora::launch_expand(p->d.dtype, pl->tt, ks, a, st);
-    if (e != hipSuccess) return hip_fail(e, "expand launch");
     return LORA_OK;
 }
 

@@ -14,12 +14,20 @@ constexpr int kWaveSize = 64;
 constexpr int kWaves = 4;                    // waves per 256-thread workgroup
 constexpr int kTile = 16;                    // MFMA tile edge (rows, tokens)
 constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 token tiles
-// Decode plans (no group reaches kLongGroup tokens) cut groups into blocks of
-// at most kDecodeBlockTokens: every workgroup of a launch then moves about
-// the same bytes (a popular adapter's group becomes several blocks instead of
-// one heavy one), and the decode expand takes a whole block in one pass.
+// Short groups are cut into blocks of at most kDecodeBlockTokens for the
+// decode expand: every workgroup of its launch then moves about the same
+// bytes (a popular adapter's group becomes several blocks instead of one
+// heavy one), and it takes a whole block in one pass.  A group of at least
+// kLongGroup tokens is long, and takes kMaxBlockTokens-token blocks and the
+// MFMA expand, but only when the batch's long groups hold kMinLongTokens
+// tokens between them: fewer 64-token blocks leave most of the chip idle in
+// the MFMA expand's launch, and the decode cut does better.
 constexpr int kDecodeBlockTokens = 4;
 constexpr int kLongGroup = 48;
+#ifndef LORA_MIN_LONG_TOKENS
+#define LORA_MIN_LONG_TOKENS 1024
+#endif
+constexpr int kMinLongTokens = LORA_MIN_LONG_TOKENS;
 constexpr int kValuTokens = kDecodeBlockTokens;  // token slots of the decode expand
 // The shrink's chunk partials of one v entry are summed as kSumWays
 // interleaved running sums (chunk c into sum c % kSumWays, in increasing c),

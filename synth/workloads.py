@@ -287,6 +287,48 @@ def config4() -> Workload:
                     "Zipf(1.1) popularity; y = base_out + delta")
 
 
+def sweep_stack(n_adapters: int = 128) -> Workload:
+    """The full stack of the Zipf decode batch with a pool of n_adapters
+    rank-16 adapters, every one of them used by the first draw (token t takes
+    adapter t mod n_adapters).  Activations and base outputs are the same
+    draws as the Zipf batch's; only the assignment differs."""
+    w = config4()
+    T = w.num_tokens
+    w.name = "full_stack_sweep_bf16"
+    w.pool_size = n_adapters
+    w.ranks = np.full(n_adapters, 16, np.int32)
+    w.scales = np.full(n_adapters, 2.0, np.float32)
+    w.seg_adapter = (np.arange(T) % n_adapters).astype(np.int32)
+    w.description = (f"32 layers x {{q,k,v,o,gate,up,down}}; T=S={T}; pool {n_adapters} r=16; "
+                     "the assignment of tokens to adapters varies")
+    return w
+
+
+def sweep_assignments(T: int = 128, n_adapters: int = 128):
+    """Token-to-adapter assignments of the cost sweep, as (label, params,
+    ids[T]).  Adapter identity does not change the work, only how many
+    distinct adapters there are and how many tokens each takes, so every
+    draw is relabelled to ids 0, 1, ... in order of first appearance.
+
+    * ``distinct``: d distinct adapters, token t takes t mod d (d = 0: no
+      token is adapted); d runs over 0, 1, 2, 4, ..., T.
+    * ``zipf``: T ids drawn from a bounded Zipf(s) over 1000 adapters, for a
+      range of skews s (s = 0 is uniform)."""
+    out = []
+    d = 0
+    while d <= min(T, n_adapters):
+        ids = np.full(T, -1, np.int32) if d == 0 else (np.arange(T) % d).astype(np.int32)
+        out.append((f"distinct={d}", {"kind": "distinct", "d": d}, ids))
+        d = 1 if d == 0 else 2 * d
+    for k, s in enumerate((0.0, 0.5, 0.8, 1.1, 1.5, 2.0, 3.0)):
+        draw = _rng(4, _TAG_MAP, 1000 + k).choice(1000, size=T, p=zipf_probs(1000, s))
+        relabel = {}
+        ids = np.asarray([relabel.setdefault(int(a), len(relabel)) for a in draw], np.int32)
+        assert len(relabel) <= n_adapters
+        out.append((f"zipf={s}", {"kind": "zipf", "s": s}, ids))
+    return out
+
+
 CONFIGS = (config0, config1, config2, config3, config4)
 
 
@@ -324,6 +366,39 @@ def random_case(seed: int, *, T: int = None, h_in: int = None, h_out: int = None
         seg_starts=np.asarray(cuts, np.int32), seg_adapter=seg_adapter,
         pool_size=n_adapters, ranks=ranks, scales=scales, has_base=has_base,
         r_max=r_max, description="random small case")
+
+
+def mixed_case(seed: int, *, long_tokens: int = 1100, n_long: int = 2, n_short: int = 40,
+               short_max: int = 3, h_in: int = 256, h_out: int = 192,
+               r_choices=(8, 16, 32, 64), dtype: str = "bf16", has_base: bool = True,
+               no_adapter_frac: float = 0.1, r_max: int = 64) -> Workload:
+    """A continuous batch of prompts and decode steps: n_long adapters'
+    prompts of long_tokens tokens in all (each at least 48 tokens, ragged,
+    cut into one to three segments), interleaved in random order with n_short
+    requests of 1 .. short_max tokens, each naming an adapter of its own (a
+    fraction no_adapter_frac of them none)."""
+    g = _rng(seed, 95)
+    segs = []                                   # (adapter, tokens)
+    lens = g.multinomial(long_tokens - 48 * n_long, np.full(n_long, 1.0 / n_long)) + 48
+    for i, n in enumerate(lens):
+        k = int(g.integers(1, 4))
+        cuts = np.sort(g.choice(np.arange(1, n), k - 1, replace=False)) if k > 1 else []
+        for part in np.diff(np.concatenate([[0], cuts, [n]])):
+            segs.append((i, int(part)))
+    for j in range(n_short):
+        a = -1 if g.random() < no_adapter_frac else n_long + j
+        segs.append((a, int(g.integers(1, short_max + 1))))
+    segs = [segs[i] for i in g.permutation(len(segs))]
+    starts = np.concatenate([[0], np.cumsum([n for _, n in segs])]).astype(np.int32)
+    n_adapters = n_long + n_short
+    ranks = g.choice(np.asarray(r_choices), n_adapters).astype(np.int32)
+    scales = g.uniform(0.25, 4.0, n_adapters).astype(np.float32)
+    return Workload(
+        name=f"mixed_{seed}", seed=3000 + seed, dtype=dtype, num_layers=1,
+        projs=(Proj("p", h_in, h_out, "x"),), calls=((0,),), num_tokens=int(starts[-1]),
+        seg_starts=starts, seg_adapter=np.asarray([a for a, _ in segs], np.int32),
+        pool_size=n_adapters, ranks=ranks, scales=scales, has_base=has_base, r_max=r_max,
+        description="prompts and decode steps in one batch")
 
 
 def jd_case(seed: int, *, kind: str, T: int = 96, h_in: int = 256, h_outs=(192, 64),

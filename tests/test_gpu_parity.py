@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import config, random_case, Proj
+from synth import config, mixed_case, random_case, Proj
 from synth.device import DeviceWorkload, from_device
 
 pytestmark = pytest.mark.gpu
@@ -168,12 +168,33 @@ def test_random_heterogeneous(seed):
 
 @pytest.mark.parametrize("seed", range(4))
 def test_prefill_blocks(seed):
-    """Long same-adapter segments: several 64-token blocks per group, ragged tails."""
-    T = [65, 130, 200, 257][seed]
+    """Long same-adapter segments (over 1024 tokens in long groups, so the
+    MFMA expand runs): several 64-token blocks per group, ragged tails."""
+    T = [1030, 1100, 1300, 1601][seed]
     w = random_case(100 + seed, T=T, h_in=512, h_out=256, n_adapters=3, max_seg=T,
                     no_adapter_frac=0.0, r_choices=[8, 16, 32, 64])
     log(f"[parity] prefill {seed} T={T} segments={list(np.diff(w.seg_starts))}")
     dw = DeviceWorkload(w, threads=4)
+    assert dw.plan.stats()["max_block_tokens"] > 4
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("has_base", [True, False])
+def test_mixed_blocks(dtype, has_base):
+    """Prompts and decode steps in one batch: the long groups take 64-token
+    blocks (MFMA expand), the short groups and the tokens without an adapter
+    4-token blocks (decode expand), two expand launches per call."""
+    seed = {("bf16", True): 81, ("bf16", False): 82, ("f32", True): 83, ("f32", False): 84}[
+        (dtype, has_base)]
+    w = mixed_case(seed, dtype=dtype, has_base=has_base, h_in=384, h_out=264)
+    sizes = np.diff(w.seg_starts)
+    log(f"[parity] mixed {w.name} {dtype} base {has_base} T={w.num_tokens} S={w.num_segs}")
+    dw = DeviceWorkload(w, threads=4)
+    st = dw.plan.stats()
+    assert st["max_block_tokens"] > 4 and (sizes[w.seg_adapter >= 0] <= 3).any()
     dw.run_fused()
     torch.cuda.synchronize()
     check_workload(dw, tight=True, threads=4)
@@ -185,7 +206,7 @@ def test_two_step_path():
     sgmv_fused (every kernel sums the k-chunk partials in one order) on both
     the decode path (one fused launch) and the prefill path."""
     for w in (config(1), multi_proj_case(3, has_base=True), config(0),
-              random_case(71, T=150, h_in=512, h_out=256, max_seg=80, r_choices=[8, 24, 64])):
+              mixed_case(71, h_in=512, h_out=256, r_choices=[8, 24, 64])):
         log(f"[parity] two-step {w.name}")
         dw = DeviceWorkload(w, threads=4)
         outs = []
@@ -480,8 +501,8 @@ def test_sigma_parity(kind, dtype, prefill):
     from synth import jd_case
     seed = {("full", "bf16"): 1, ("full", "f32"): 2, ("diag", "bf16"): 3,
             ("diag", "f32"): 4}[(kind, dtype)] + (10 if prefill else 0)
-    w = jd_case(seed, kind=kind, dtype=dtype, T=200 if prefill else 96,
-                max_seg=120 if prefill else 3)
+    w = jd_case(seed, kind=kind, dtype=dtype, T=1500 if prefill else 96,
+                max_seg=500 if prefill else 3)
     log(f"[parity] {w.name} dtype {dtype} prefill {prefill}")
     dw = DeviceWorkload(w, threads=4)
     assert (dw.plan.stats()["max_block_tokens"] > 4) == prefill
@@ -579,8 +600,8 @@ def test_merge_parity(dtype, prefill):
     import heterogeneous_adapter_batching_amd as hab
     seed = (31 if dtype == "bf16" else 32) + (10 if prefill else 0)
     w, dw, plans, seg_ad, seg_w = _merge_setup(seed, K=3, dtype=dtype,
-                                               T=160 if prefill else 64,
-                                               max_seg=100 if prefill else 3)
+                                               T=1300 if prefill else 64,
+                                               max_seg=400 if prefill else 3)
     log(f"[parity] merge {w.name} {dtype} prefill {prefill}")
     assert (plans[0].stats()["max_block_tokens"] > 4) == prefill
     x = dw.x[(0, "x")]
@@ -615,8 +636,8 @@ def test_weight_one_equals_plain_bitexact():
     """A weighted plan with every weight 1 gives the plain plan's output bit
     for bit (decode and prefill blocks)."""
     import heterogeneous_adapter_batching_amd as hab
-    for seed, max_seg in ((51, 3), (52, 100)):
-        w = random_case(seed, T=120, h_in=256, h_out=128, n_adapters=4, r_choices=[16, 32],
+    for seed, T, max_seg in ((51, 120, 3), (52, 1300, 400)):
+        w = random_case(seed, T=T, h_in=256, h_out=128, n_adapters=4, r_choices=[16, 32],
                         has_base=True, max_seg=max_seg, r_max=32)
         dw = DeviceWorkload(w, threads=4)
         ones = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
