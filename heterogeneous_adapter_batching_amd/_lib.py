@@ -69,6 +69,20 @@ SIGNATURES = {
                                  _vp, _i64, _vp]),
     "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
                                 _vp, _i64, _vp, _i64, _vp]),
+    "lora_pack_adapter": (_i32, [ctypes.POINTER(PoolDesc), _i32, _pp, _pp, _vp, _u64]),
+    "lora_pool_upload_image": (_i32, [_vp, _i32, _vp, _i32, _vp]),
+    "lora_pool_register_image": (_i32, [_vp, _i32, _i32, _f32, _vp, _i32, _vp]),
+    "lora_pool_get_desc": (_i32, [_vp, ctypes.POINTER(PoolDesc)]),
+    "lora_cache_create": (_i32, [ctypes.POINTER(_vp), _vp, _vp]),
+    "lora_cache_destroy": (_i32, [_vp]),
+    "lora_cache_add": (_i32, [_vp, _i32, _i32, _f32, _vp]),
+    "lora_cache_acquire": (_i32, [_vp, _i32, _i32p, _vp, _i32p]),
+    "lora_cache_release": (_i32, [_vp, _vp]),
+    "lora_cache_prefetch": (_i32, [_vp, _i32, _i32p, _i32p]),
+    "lora_cache_query": (_i32, [_vp, _i32, _i32p, _i32p]),
+    "lora_cache_stats": (_i32, [_vp, _i32p, ctypes.POINTER(_u64), ctypes.POINTER(_u64),
+                                ctypes.POINTER(_u64), ctypes.POINTER(_u64),
+                                ctypes.POINTER(_u64)]),
 }
 
 LORA_SIGMA_DIAG, LORA_SIGMA_FULL = 1, 2

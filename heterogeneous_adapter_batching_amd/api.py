@@ -61,6 +61,27 @@ def extent_bytes(desc: PoolDesc, rank: int) -> int:
     return int(load().lora_pool_extent_bytes(ctypes.byref(desc), rank))
 
 
+def pack_adapter(desc: PoolDesc, rank: int, A: Sequence, B: Sequence, out=None) -> np.ndarray:
+    """The packed extent image of one adapter (host, no device call): A[p]
+    [L][rank][h_in_p], B[p] [L][h_out_p][rank] as host arrays of the pool
+    dtype (float32, or uint16 bf16 bits).  `out`: a writable host buffer of at
+    least extent_bytes(desc, rank) bytes (e.g. a pinned uint8 tensor's numpy
+    view); a new uint8 array otherwise."""
+    lib = load()
+    n = extent_bytes(desc, rank)
+    if out is None:
+        out = np.empty(n, np.uint8)
+    keep = [np.ascontiguousarray(a) for a in A] + [np.ascontiguousarray(b) for b in B]
+    np_ = desc.num_proj
+    arr_a = (ctypes.c_void_p * np_)(*[k.ctypes.data for k in keep[:np_]])
+    arr_b = (ctypes.c_void_p * np_)(*[k.ctypes.data for k in keep[np_:]])
+    ptr = out.ctypes.data if isinstance(out, np.ndarray) else out.data_ptr()
+    nbytes = out.nbytes if isinstance(out, np.ndarray) else out.numel() * out.element_size()
+    check(lib.lora_pack_adapter(ctypes.byref(desc), rank, arr_a, arr_b, ctypes.c_void_p(ptr),
+                                nbytes))
+    return out
+
+
 def _check_dev(t, name, dtype=None, ndim=2):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -169,6 +190,15 @@ class Pool:
     def unregister(self, adapter_id: int):
         check(self.lib.lora_pool_unregister(self._h, adapter_id))
 
+    def register_image(self, adapter_id: int, rank: int, scale: float, image, stream=None):
+        """Reserve and copy a packed image (``pack_adapter``): a host numpy
+        array or CPU tensor (pinned for an asynchronous copy), or a CUDA
+        tensor.  The image must stay alive until the stream passes the copy."""
+        ptr, on_host = _image_ptr(image)
+        check(self.lib.lora_pool_register_image(self._h, adapter_id, rank, ctypes.c_float(scale),
+                                                ctypes.c_void_p(ptr), int(on_host),
+                                                _stream_handle(stream)))
+
     def query(self, adapter_id: int):
         r, rp = ctypes.c_int32(), ctypes.c_int32()
         sc, off = ctypes.c_float(), ctypes.c_uint64()
@@ -180,6 +210,75 @@ class Pool:
         n, free = ctypes.c_int32(), ctypes.c_uint64()
         check(self.lib.lora_pool_stats(self._h, ctypes.byref(n), ctypes.byref(free)))
         return {"adapters": n.value, "free_bytes": free.value}
+
+
+def _image_ptr(image):
+    if isinstance(image, np.ndarray):
+        return image.ctypes.data, True
+    return image.data_ptr(), not image.is_cuda
+
+
+class Cache:
+    """Adapter exchange over a pool: host-resident packed adapters made
+    resident on demand on a copy stream, least recently used evicted (see
+    lora_cache_* in the C header).  Images are kept referenced here."""
+
+    def __init__(self, pool: Pool, copy_stream=None):
+        torch = _torch()
+        self.lib = pool.lib
+        self.pool = pool
+        self.copy_stream = copy_stream if copy_stream is not None else torch.cuda.Stream()
+        self._images = {}
+        self._h = ctypes.c_void_p()
+        check(self.lib.lora_cache_create(ctypes.byref(self._h), pool.handle,
+                                         ctypes.c_void_p(self.copy_stream.cuda_stream)))
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self.lib.lora_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, adapter_id: int, rank: int, scale: float, image):
+        ptr, on_host = _image_ptr(image)
+        if not on_host:
+            raise ValueError("cache images live in host memory")
+        check(self.lib.lora_cache_add(self._h, adapter_id, rank, ctypes.c_float(scale),
+                                      ctypes.c_void_p(ptr)))
+        self._images[adapter_id] = image
+
+    def acquire(self, ids, stream=None) -> int:
+        arr = _i32_array(ids)
+        up = ctypes.c_int32()
+        check(self.lib.lora_cache_acquire(self._h, len(list(ids)), arr, _stream_handle(stream),
+                                          ctypes.byref(up)))
+        return up.value
+
+    def release(self, stream=None):
+        check(self.lib.lora_cache_release(self._h, _stream_handle(stream)))
+
+    def prefetch(self, ids) -> int:
+        arr = _i32_array(ids)
+        up = ctypes.c_int32()
+        check(self.lib.lora_cache_prefetch(self._h, len(list(ids)), arr, ctypes.byref(up)))
+        return up.value
+
+    def query(self, adapter_id: int):
+        r, h = ctypes.c_int32(), ctypes.c_int32()
+        check(self.lib.lora_cache_query(self._h, adapter_id, ctypes.byref(r), ctypes.byref(h)))
+        return {"resident": bool(r.value), "held": bool(h.value)}
+
+    def stats(self):
+        n = ctypes.c_int32()
+        v = [ctypes.c_uint64() for _ in range(5)]
+        check(self.lib.lora_cache_stats(self._h, ctypes.byref(n), *[ctypes.byref(x) for x in v]))
+        return dict(zip(("resident", "hits", "misses", "prefetched", "evictions",
+                         "bytes_uploaded"), [n.value] + [x.value for x in v]))
 
 
 class Plan:

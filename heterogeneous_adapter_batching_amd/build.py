@@ -16,7 +16,8 @@ LIB = os.path.join(PKG, "libhab_lora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "lora_sgmv.cpp"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, "lora_sgmv.cpp"), os.path.join(CSRC, "exchange.cpp"),
+           os.path.join(CSRC, "kernels.hip")]
 
 # Packed float32 ALU ops are switched off for all device code; the compiler's
 # host pass warns that it does not know the feature, which is harmless.

@@ -217,6 +217,30 @@ struct lora_plan {
     }
 };
 
+namespace {
+
+// Host copy of one A block into its K-blocked place: A [rank][h_in] row-major
+// -> dst [h_in_pad / span][r_pad][span]; dst is zero already.
+void pack_a_host(const uint8_t *src, int32_t rank, uint64_t h_in, uint64_t hp, uint64_t span,
+                 int32_t r_pad, uint64_t es, uint8_t *dst) {
+    for (uint64_t kb = 0; kb < hp / span; ++kb) {
+        const uint64_t cols = std::min<uint64_t>(span, h_in - std::min(h_in, kb * span));
+        if (!cols) break;
+        for (uint64_t j = 0; j < uint64_t(rank); ++j)
+            std::memcpy(dst + ((kb * r_pad + j) * span) * es, src + (j * h_in + kb * span) * es,
+                        cols * es);
+    }
+}
+
+}  // namespace
+
+namespace lora {
+lora_status set_error(lora_status st, const char *msg) {
+    g_last_error = msg;
+    return st;
+}
+}  // namespace lora
+
 // ------------------------------------------------------------------ C ABI ----
 extern "C" {
 
@@ -301,14 +325,8 @@ lora_status lora_pool_upload(lora_pool *p, int32_t id, int32_t layer, int32_t pr
     std::vector<uint8_t> a_blk;
     if (src_on_host) {
         a_blk.assign(a_bytes, 0);
-        const uint8_t *src = static_cast<const uint8_t *>(A);
-        for (uint64_t kb = 0; kb < hp / span; ++kb) {
-            const uint64_t cols = std::min<uint64_t>(span, h_in - std::min(h_in, kb * span));
-            if (!cols) break;
-            for (uint64_t j = 0; j < uint64_t(s.rank); ++j)
-                std::memcpy(a_blk.data() + ((kb * s.r_pad + j) * span) * es,
-                            src + (j * h_in + kb * span) * es, cols * es);
-        }
+        pack_a_host(static_cast<const uint8_t *>(A), s.rank, h_in, hp, span, s.r_pad, es,
+                    a_blk.data());
         e = hipMemcpyAsync(a_dst, a_blk.data(), a_bytes, kind, st);
     } else {
         e = lora::launch_pack_a(p->d.dtype, A, s.rank, int32_t(h_in), a_dst, s.r_pad,
@@ -377,6 +395,80 @@ lora_status lora_pool_register(lora_pool *p, int32_t id, int32_t rank, float sca
             }
         }
     }
+    return LORA_OK;
+}
+
+lora_status lora_pack_adapter(const lora_pool_desc *d, int32_t rank, const void *const *A,
+                              const void *const *B, void *image, uint64_t image_bytes) {
+    lora_status st = check_desc(d);
+    if (st != LORA_OK) return st;
+    if (rank < 1 || rank > d->r_max)
+        return fail(LORA_ERANK, "rank %d not in 1..r_max=%d", rank, d->r_max);
+    if (!A || !B || !image) return fail(LORA_EINVAL, "null weight array or image");
+    for (int i = 0; i < d->num_proj; ++i)
+        if (!A[i] || !B[i]) return fail(LORA_EINVAL, "null weights for projection %d", i);
+    const uint64_t need = lora_pool_extent_bytes(d, rank);
+    if (image_bytes < need)
+        return fail(LORA_EINVAL, "image of %llu bytes < extent of %llu",
+                    (unsigned long long)image_bytes, (unsigned long long)need);
+    const uint64_t es = esize(d->dtype), span = kspan(d->dtype);
+    const int32_t r_pad = pad_rank(d, rank);
+    const uint64_t W = uint64_t(stored_row_elems(d));
+    uint8_t *img = static_cast<uint8_t *>(image);
+    std::memset(img, 0, need);
+    for (int l = 0; l < d->num_layers; ++l) {
+        uint64_t pre = 0;   // (h_in_pad + h_out) of the projections before p
+        for (int i = 0; i < d->num_proj; ++i) {
+            const uint64_t h_in = d->h_in[i], h_out = d->h_out[i], hp = h_in_pad(d, i);
+            uint8_t *a_dst = img + uint64_t(r_pad) * es * (uint64_t(l) * W + pre);
+            uint8_t *b_dst = a_dst + uint64_t(r_pad) * es * hp;
+            pack_a_host(static_cast<const uint8_t *>(A[i]) + uint64_t(l) * rank * h_in * es,
+                        rank, h_in, hp, span, r_pad, es, a_dst);
+            const uint8_t *b = static_cast<const uint8_t *>(B[i]) + uint64_t(l) * h_out * rank * es;
+            for (uint64_t o = 0; o < h_out; ++o)
+                std::memcpy(b_dst + o * r_pad * es, b + o * rank * es, rank * es);
+            pre += hp + h_out;
+        }
+    }
+    return LORA_OK;
+}
+
+lora_status lora_pool_upload_image(lora_pool *p, int32_t id, const void *image,
+                                   int32_t src_on_host, void *stream) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (!image) return fail(LORA_EINVAL, "null image");
+    auto it = p->slots.find(id);
+    if (it == p->slots.end()) return fail(LORA_ENOENT, "adapter %d not registered", id);
+    if (!src_on_host && (reinterpret_cast<uintptr_t>(image) & 15))
+        return fail(LORA_EINVAL, "device images must be 16-byte aligned");
+    const hipError_t e = hipMemcpyAsync(
+        p->slab + it->second.off, image, it->second.bytes,
+        src_on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "image upload");
+    return LORA_OK;
+}
+
+lora_status lora_pool_register_image(lora_pool *p, int32_t id, int32_t rank, float scale,
+                                     const void *image, int32_t src_on_host, void *stream) {
+    if (!p) return fail(LORA_EINVAL, "null pool");
+    if (!image) return fail(LORA_EINVAL, "null image");
+    lora_status st = lora_pool_reserve(p, id, rank, scale);
+    if (st != LORA_OK) return st;
+    st = lora_pool_upload_image(p, id, image, src_on_host, stream);
+    if (st != LORA_OK) {
+        std::string msg = g_last_error;
+        auto it = p->slots.find(id);   // undo the reservation (not a generation bump)
+        p->release(it->second.off, it->second.bytes);
+        p->slots.erase(it);
+        g_last_error = msg;
+    }
+    return st;
+}
+
+lora_status lora_pool_get_desc(const lora_pool *p, lora_pool_desc *d) {
+    if (!p || !d) return fail(LORA_EINVAL, "null pool or descriptor");
+    *d = p->d;
     return LORA_OK;
 }
 

@@ -196,6 +196,9 @@ constexpr int decode_wave_rows(int r_pad, int esize) {
 // (ranks / (4 fragment elements)) at most: the wave keeps 8 B fragments.
 constexpr int expand_tiles(int ks) { return ks >= 8 ? 1 : 8 / ks; }
 
+// Sets the thread's last-error message (lora_last_error) and returns st.
+lora_status set_error(lora_status st, const char *msg);
+
 // Kernel launchers (kernels.hip).  dtype is a lora_dtype; tt is the number of
 // 16-token tiles of the largest block (1, 2 or 4); ks the K-steps of the
 // largest padded rank (bf16: 1 or 2, f32: 1, 2 or 4).

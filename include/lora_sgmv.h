@@ -145,6 +145,33 @@ lora_status lora_pool_register(lora_pool *p, int32_t adapter_id, int32_t rank, f
  * adapter must not be launched afterwards. */
 lora_status lora_pool_unregister(lora_pool *p, int32_t adapter_id);
 
+/* Pack one adapter, on the host, into the byte image of its slab extent: the
+ * layout described at lora_pool_create, pad rows, pad columns and the
+ * 256-byte tail zero.  A[p] -> [L][rank][h_in_p] and B[p] -> [L][h_out_p][rank]
+ * (arrays of num_proj host pointers, pool dtype); `image` (host, caller-owned)
+ * holds at least lora_pool_extent_bytes(d, rank) bytes.  A packed image
+ * reaches the device as one contiguous copy (lora_pool_upload_image), the
+ * unit an adapter exchange moves.  No device call is made.
+ * Errors: LORA_EINVAL (null pointers, image too small), LORA_ERANK. */
+lora_status lora_pack_adapter(const lora_pool_desc *d, int32_t rank, const void *const *A,
+                              const void *const *B, void *image, uint64_t image_bytes);
+
+/* Copy a packed image into the extent of a reserved adapter: one copy of
+ * lora_pool_extent_bytes(rank) bytes enqueued on `stream`, from host memory
+ * (src_on_host = 1; pinned memory makes it asynchronous) or device memory
+ * (0, 16-byte aligned).  The image must stay valid until the stream has
+ * passed the copy.  Errors: LORA_EINVAL, LORA_ENOENT, LORA_EHIP. */
+lora_status lora_pool_upload_image(lora_pool *p, int32_t adapter_id, const void *image,
+                                   int32_t src_on_host, void *stream);
+
+/* lora_pool_reserve, then lora_pool_upload_image; on an upload error the
+ * reservation is released again. */
+lora_status lora_pool_register_image(lora_pool *p, int32_t adapter_id, int32_t rank, float scale,
+                                     const void *image, int32_t src_on_host, void *stream);
+
+/* The descriptor the pool was created with. */
+lora_status lora_pool_get_desc(const lora_pool *p, lora_pool_desc *d);
+
 /* Where an adapter lives: rank, padded rank, scale and extent byte offset in
  * the slab (any output pointer may be NULL).  LORA_ENOENT if absent. */
 lora_status lora_pool_query(const lora_pool *p, int32_t adapter_id, int32_t *rank,
@@ -152,6 +179,82 @@ lora_status lora_pool_query(const lora_pool *p, int32_t adapter_id, int32_t *ran
 
 /* Number of resident adapters and free slab bytes. */
 lora_status lora_pool_stats(const lora_pool *p, int32_t *num_adapters, uint64_t *free_bytes);
+
+/* ------------------------------------------------------------ exchange ---- */
+/* Adapter exchange: a residency cache over a pool.  Adapters stay packed in
+ * host memory (lora_pack_adapter images, caller-owned, pinned for overlap)
+ * and are made resident on demand by one image copy each on a copy stream,
+ * while earlier batches run on the compute stream; when the slab or the slot
+ * table is full, the least recently used adapter that the outstanding batch
+ * does not hold is evicted (its device copy dropped: adapters are read-only,
+ * nothing moves back).  This is the asynchronous prefetch and offload of
+ * adapters between CPU and GPU memory of the LoRAX pages ("Lorax" tool
+ * listing, "What is Lorax?": adapter exchange scheduling; "predibase/lorax"
+ * listing: adapter offloading, just-in-time weight loading; "how does this
+ * differ from s-Lora?": adapters loaded asynchronously during inference).
+ *
+ * Use per batch: lora_cache_acquire(ids) -> build the plan -> launch the
+ * batch's sgmv calls on the compute stream -> lora_cache_release(compute
+ * stream).  Ordering is by events, the host never waits:
+ *   - acquire makes the compute stream wait for every copy enqueued so far;
+ *   - a copy into an extent freed by an eviction waits for the release fence
+ *     of the last batch that read the evicted adapter.
+ * Evictions unregister adapters, so plans built before an acquire or a
+ * prefetch that evicted must not be launched afterwards (the launch reports
+ * LORA_ESTATE).  The cache manages only the adapters added to it; it is not
+ * thread-safe and is not for use under graph capture.  An error from acquire
+ * or prefetch may leave adapters it brought in resident (and not held); no
+ * other state changes. */
+typedef struct lora_cache lora_cache;
+
+/* A cache over pool `p`, copying on `copy_stream` (a hipStream_t). */
+lora_status lora_cache_create(lora_cache **out, lora_pool *p, void *copy_stream);
+
+/* Frees the cache's host state and events; resident adapters stay in the
+ * pool.  Call after the streams have passed the cache's work. */
+lora_status lora_cache_destroy(lora_cache *c);
+
+/* Adds a host-resident adapter: `image` is its packed extent image
+ * (lora_pack_adapter at `rank`), kept valid by the caller while the cache
+ * lives.  Errors: LORA_EINVAL, LORA_ERANK, LORA_EEXIST (added already, or
+ * registered in the pool by other means). */
+lora_status lora_cache_add(lora_cache *c, int32_t adapter_id, int32_t rank, float scale,
+                           const void *image);
+
+/* Makes the adapters `ids[0..n)` (-1 entries ignored, repeats allowed)
+ * resident and holds them until lora_cache_release: misses are copied on the
+ * copy stream in first-appearance order, evicting unheld adapters by least
+ * recent use; `compute_stream` is made to wait for the copies.
+ * *num_uploaded (may be NULL) = misses copied by this call.
+ * Errors: LORA_ESTATE (a batch is outstanding), LORA_ENOENT (id not added),
+ * LORA_ENOSPC (the batch's adapters do not fit the pool together, or the free
+ * space around those already brought in is too fragmented), LORA_EHIP. */
+lora_status lora_cache_acquire(lora_cache *c, int32_t n, const int32_t *ids, void *compute_stream,
+                               int32_t *num_uploaded);
+
+/* Ends the outstanding batch: records its fence on `compute_stream` (after
+ * the batch's launches) and lets its adapters be evicted again.
+ * Errors: LORA_ESTATE (no batch outstanding), LORA_EHIP. */
+lora_status lora_cache_release(lora_cache *c, void *compute_stream);
+
+/* Starts copies of the adapters of a coming batch (-1 ignored): each one not
+ * resident is copied on the copy stream, evicting unheld adapters by least
+ * recent use, until one does not fit (not an error).  Prefetched adapters
+ * count as just used.  *num_uploaded (may be NULL) = copies started. */
+lora_status lora_cache_prefetch(lora_cache *c, int32_t n, const int32_t *ids,
+                                int32_t *num_uploaded);
+
+/* Whether an added adapter is resident and whether the outstanding batch
+ * holds it.  LORA_ENOENT if it was not added. */
+lora_status lora_cache_query(const lora_cache *c, int32_t adapter_id, int32_t *resident,
+                             int32_t *held);
+
+/* Counters: resident adapters; ids found resident by acquire (hits) and
+ * copied by it (misses); copies started by prefetch; evictions; bytes
+ * copied in all.  Any output pointer may be NULL. */
+lora_status lora_cache_stats(const lora_cache *c, int32_t *resident, uint64_t *hits,
+                             uint64_t *misses, uint64_t *prefetched, uint64_t *evictions,
+                             uint64_t *bytes_uploaded);
 
 /* ---------------------------------------------------------------- plan ---- */
 

@@ -233,3 +233,59 @@ def test_plan_for_workloads():
         if expect_groups[i] is not None:
             assert st["groups"] == expect_groups[i]
         assert st["active_tokens"] == w.num_tokens
+
+
+def _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype):
+    """The extent image as the header lays it out, built with numpy: per layer
+    (outermost) and projection, A K-blocked [h_in_pad / span][r_pad][span],
+    then B [h_out][r_pad]; pads zero; the whole rounded up to 256 bytes."""
+    g = np.random.default_rng(rank * 7 + len(h_in))
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    A = [g.integers(1, 60000, (L, rank, hi)).astype(npdt) if dtype == "bf16"
+         else g.standard_normal((L, rank, hi)).astype(npdt) for hi in h_in]
+    B = [g.integers(1, 60000, (L, ho, rank)).astype(npdt) if dtype == "bf16"
+         else g.standard_normal((L, ho, rank)).astype(npdt) for ho in h_out]
+    parts = []
+    for l in range(L):
+        for p, (hi, ho) in enumerate(zip(h_in, h_out)):
+            hp = -(-hi // span) * span
+            a = np.zeros((r_pad, hp), npdt)
+            a[:rank, :hi] = A[p][l]
+            parts.append(a.reshape(r_pad, hp // span, span).transpose(1, 0, 2).ravel())
+            b = np.zeros((ho, r_pad), npdt)
+            b[:, :rank] = B[p][l]
+            parts.append(b.ravel())
+    raw = np.concatenate(parts).view(np.uint8)
+    img = np.zeros(-(-raw.size // 256) * 256, np.uint8)
+    img[:raw.size] = raw
+    return A, B, img
+
+
+@pytest.mark.parametrize("dtype,rank,granule", [("bf16", 5, 8), ("bf16", 16, 16),
+                                                 ("f32", 13, 8), ("f32", 32, 8)])
+def test_pack_adapter_layout(dtype, rank, granule):
+    """lora_pack_adapter writes the extent layout the header states, byte for
+    byte, with ragged h_in (not a multiple of the K-block) and padded ranks."""
+    h_in, h_out, L = [40, 96, 24], [24, 8, 64], 3
+    desc = make_desc(L, h_in, h_out, 32, dtype, rank_granule=granule)
+    r_pad = -(-rank // granule) * granule
+    span = 32 if dtype == "bf16" else 16
+    A, B, ref = _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype)
+    assert hab.extent_bytes(desc, rank) == ref.size
+    got = hab.pack_adapter(desc, rank, A, B)
+    assert np.array_equal(got, ref)
+    # a dirty output buffer is overwritten everywhere, tail included
+    out = np.full(ref.size + 64, 0xAB, np.uint8)
+    hab.pack_adapter(desc, rank, A, B, out=out)
+    assert np.array_equal(out[:ref.size], ref) and (out[ref.size:] == 0xAB).all()
+
+
+def test_pack_adapter_errors():
+    desc = make_desc(1, [16], [16], 16, "f32")
+    A, B = [np.zeros((1, 4, 16), np.float32)], [np.zeros((1, 16, 4), np.float32)]
+    with pytest.raises(hab.LoraError) as ei:
+        hab.pack_adapter(desc, 4, A, B, out=np.zeros(8, np.uint8))
+    assert ei.value.status == -1
+    with pytest.raises(hab.LoraError) as ei:
+        hab.pack_adapter(desc, 17, A, B)
+    assert ei.value.status == -4
