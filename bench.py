@@ -262,6 +262,227 @@ def sweep(args):
     print(json.dumps(out), flush=True)
 
 
+def exchange(args):
+    """Adapter exchange on the full stack (rank-16 adapters, 32 layers x 7
+    projections, about 84 MB packed each): the host-to-device rate of packed
+    images from pinned memory, how much of that copy the delta hides, and a
+    replay of a continuous decode batch whose requests come and go, served
+    from a pool smaller than the adapters it sees."""
+    import torch
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import config, default_threads, zipf_probs
+    from synth.device import host_weights, to_device
+    from concurrent.futures import ThreadPoolExecutor
+
+    hab.load()
+    torch.cuda.set_device(0)
+    w = config(4)
+    h_in, h_out = [p.h_in for p in w.projs], [p.h_out for p in w.projs]
+    desc = hab.api.make_desc(w.num_layers, h_in, h_out, w.r_max, w.dtype)
+    ext = hab.extent_bytes(desc, 16)
+    n_img = args.exchange_images
+
+    def image(aid):
+        A = [np.stack([host_weights(w.adapter_block(aid, l, p)[0], w.dtype)
+                       for l in range(w.num_layers)]) for p in range(len(w.projs))]
+        B = [np.stack([host_weights(w.adapter_block(aid, l, p)[1], w.dtype)
+                       for l in range(w.num_layers)]) for p in range(len(w.projs))]
+        img = torch.empty(ext, dtype=torch.uint8, pin_memory=True)
+        hab.pack_adapter(desc, 16, A, B, out=img.numpy())
+        return img
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(min(8, default_threads())) as ex:
+        images = list(ex.map(image, range(n_img)))
+    log(f"[exchange] {n_img} packed images of {ext / 1e6:.1f} MB in pinned memory: "
+        f"{time.perf_counter() - t0:.1f} s")
+
+    # activations and outputs of the stack
+    calls = [tuple(c) for c in w.calls]
+    y_offsets = []
+    for c in calls:
+        o, offs = 0, []
+        for p in c:
+            offs.append(o)
+            o += w.projs[p].h_out
+        y_offsets.append(offs)
+    x = {(l, k): to_device(w.activation(l, k), w.dtype) for l in range(w.num_layers)
+         for k in w.x_keys()}
+    base = {(l, ci): to_device(np.concatenate([w.base_out(l, p) for p in c], axis=1), w.dtype)
+            for l in range(w.num_layers) for ci, c in enumerate(calls)}
+    y = {k: torch.empty_like(v) for k, v in base.items()}
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def new_pool(slots):
+        return hab.Pool(w.num_layers, h_in, h_out, w.r_max, w.dtype, slab_bytes=slots * ext,
+                        max_slots=max(slots, 1))
+
+    def launch(pool, plan):
+        for l in range(w.num_layers):
+            for ci, c in enumerate(calls):
+                hab.sgmv_fused(pool, plan, l, c, y_offsets[ci], x[(l, w.projs[c[0]].x_key)],
+                               y[(l, ci)], base[(l, ci)], stream=comp)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = time.perf_counter()
+        e0.record(comp)
+        fn(n)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, (time.perf_counter() - t) * 1e3 / n
+
+    T = w.num_tokens
+    starts = np.arange(T + 1, dtype=np.int32)
+    out = {}
+
+    # 1. copy rate: packed images into a pool on the copy stream, nothing else running
+    pool = new_pool(n_img)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(copy)
+    for i in range(n_img):
+        pool.register_image(i, 16, 2.0, images[i], stream=copy)
+    c1.record(copy)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1)
+    h2d = n_img * ext / (copy_ms * 1e-3) / 1e9
+    out["h2d_gbs"] = round(h2d, 2)
+    out["copy_ms_per_adapter"] = round(copy_ms / n_img, 4)
+    log(f"[exchange] host-to-device: {n_img} images in {copy_ms:.2f} ms = {h2d:.1f} GB/s")
+
+    # 2. overlap: the step (a graph over 8 resident adapters) on the compute
+    # stream while the copy stream uploads packed images into another pool;
+    # both start from one event
+    ids0 = (np.arange(T, dtype=np.int32) % 8)
+    pool2 = new_pool(8)
+    for i in range(8):
+        pool2.register_image(i, 16, 2.0, images[i], stream=comp)
+    plan2 = hab.Plan(pool2, T, starts, ids0)
+    with torch.cuda.stream(comp):
+        plan2.upload(3, stream=comp)
+        launch(pool2, plan2)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=comp):
+        launch(pool2, plan2)
+    torch.cuda.synchronize()
+    n_steps = args.exchange_steps
+    step_ms = _time_graph(lambda: launch(pool2, plan2), comp, 3, n_steps)
+    n_copy = max(1, int(round(n_steps * step_ms / (copy_ms / n_img))))
+    sink = new_pool(4)
+    live = []                  # ids in the sink pool; copies on one stream reuse extents in order
+
+    def copies(n):
+        for i in range(n):
+            if len(live) == 4:
+                sink.unregister(live.pop(0))
+            live.append(1000 + i)
+            sink.register_image(live[-1], 16, 2.0, images[i % n_img], stream=copy)
+
+    def together(do_copy, do_comp):
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(comp)
+        copy.wait_event(ev[0])
+        if do_copy:
+            copies(n_copy)
+        ev[1].record(copy)
+        with torch.cuda.stream(comp):
+            if do_comp:
+                for _ in range(n_steps):
+                    graph.replay()
+        ev[2].record(comp)
+        torch.cuda.synchronize()
+        while live:
+            sink.unregister(live.pop(0))
+        return max(ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[2]))
+
+    t_c = together(False, True)
+    t_x = together(True, False)
+    t_o = together(True, True)
+    eff = (t_c + t_x - t_o) / min(t_c, t_x)
+    out["overlap"] = {"steps": n_steps, "copies": n_copy, "compute_ms": round(t_c, 3),
+                      "copy_ms": round(t_x, 3), "both_ms": round(t_o, 3),
+                      "efficiency": round(eff, 3),
+                      "step_ms_alone": round(t_c / n_steps, 4),
+                      "step_ms_with_copies": round(t_o / n_steps, 4)}
+    log(f"[exchange] overlap: {n_steps} steps {t_c:.2f} ms alone, {n_copy} copies "
+        f"{t_x:.2f} ms alone, {t_o:.2f} ms together (hidden {eff:.0%} of the shorter)")
+    del graph, plan2, pool2, sink
+    torch.cuda.synchronize()
+
+    # 3. replay: 128 decode slots, `churn` requests replaced each step by
+    # Zipf(1.1) draws over 1000 adapters (ids map onto the packed images)
+    g = np.random.default_rng(11)
+    p_zipf = zipf_probs(1000, 1.1)
+    for churn in args.exchange_churn:
+        seq, cur = [], g.choice(1000, T, p=p_zipf).astype(np.int32)
+        for k in range(n_steps + 4):
+            cur = cur.copy()
+            cur[g.choice(T, churn, replace=False)] = g.choice(1000, churn, p=p_zipf)
+            seq.append(cur)
+        distinct = len({int(a) for s in seq for a in s})
+        res = {}
+        for mode, slots in (("resident", distinct), ("exchange", args.exchange_slots),
+                            ("exchange_no_prefetch", args.exchange_slots)):
+            pool3 = new_pool(slots)
+            cache = hab.Cache(pool3, copy_stream=copy)
+            for a in sorted({int(a) for s in seq for a in s}):
+                cache.add(a, 16, 2.0, images[a % n_img])
+            if mode == "resident":
+                for k in range(len(seq)):
+                    cache.prefetch(seq[k])
+                torch.cuda.synchronize()
+
+            def run(n, start, mode=mode, cache=cache, pool3=pool3):
+                for k in range(start, start + n):
+                    cache.acquire(seq[k], stream=comp)
+                    # the next batch's adapters copy while this batch runs
+                    # (this batch's are held, so they stay)
+                    if mode == "exchange" and k + 1 < len(seq):
+                        cache.prefetch(seq[k + 1])
+                    plan = hab.Plan(pool3, T, starts, seq[k])
+                    plan.upload(3, stream=comp)
+                    launch(pool3, plan)
+                    cache.release(stream=comp)
+
+            run(4, 0)
+            before = cache.stats()
+            ms, wall = timed(lambda n: run(n, 4), n_steps)
+            st = cache.stats()
+            up = st["bytes_uploaded"] - before["bytes_uploaded"]
+            acq = (st["hits"] - before["hits"]) + (st["misses"] - before["misses"])
+            res[mode] = {"ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall, 4),
+                         "hit_rate": round((st["hits"] - before["hits"]) / max(acq, 1), 4),
+                         "uploaded_mb_per_step": round(up / n_steps / 1e6, 2),
+                         "evictions_per_step": round(
+                             (st["evictions"] - before["evictions"]) / n_steps, 3),
+                         "slots": slots}
+            log(f"[exchange] churn {churn}, {mode:20s}: {ms:.3f} ms/step, "
+                f"hit rate {res[mode]['hit_rate']:.3f}, "
+                f"{res[mode]['uploaded_mb_per_step']:.0f} MB uploaded per step")
+            del cache, pool3
+            torch.cuda.synchronize()
+        out[f"replay_churn_{churn}"] = {"distinct_adapters": distinct, **res}
+
+    line = {"metric": "adapter exchange: H2D GB/s, overlap efficiency, replay step time, 1 GPU",
+            "unit": "mixed", "n_gpus": 1, "steps": n_steps, "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": "full_stack_bf16 exchange", "adapter_mb": round(ext / 1e6, 2),
+                       "tokens": T, "layers": w.num_layers, "pool_slots": args.exchange_slots,
+                       "mode": "eager"},
+            **out}
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write("# Adapter exchange on the full stack (rank-16 adapters)\n")
+            f.write(f"command: python bench.py --exchange --exchange-steps {n_steps} "
+                    f"--sweep-out {args.sweep_out}\n\n")
+            f.write(json.dumps(line, indent=1) + "\n")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +503,15 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: delta time vs distinct adapters and Zipf skew")
     ap.add_argument("--sweep-out", default=None, help="text summary of the sweep")
+    ap.add_argument("--exchange", action="store_true",
+                    help="instead of the step: adapter exchange rates and a replay")
+    ap.add_argument("--exchange-images", type=int, default=24,
+                    help="distinct packed adapters in pinned host memory")
+    ap.add_argument("--exchange-steps", type=int, default=30)
+    ap.add_argument("--exchange-slots", type=int, default=96,
+                    help="pool capacity (adapters) of the replay")
+    ap.add_argument("--exchange-churn", type=int, nargs="+", default=[1, 4],
+                    help="requests replaced per step in the replay")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -290,6 +520,8 @@ def main():
         sys.exit(2)
     if args.sweep:
         return sweep(args)
+    if args.exchange:
+        return exchange(args)
 
     import torch
     import heterogeneous_adapter_batching_amd as hab

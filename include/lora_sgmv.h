@@ -193,9 +193,12 @@ lora_status lora_pool_stats(const lora_pool *p, int32_t *num_adapters, uint64_t 
  * listing: adapter offloading, just-in-time weight loading; "how does this
  * differ from s-Lora?": adapters loaded asynchronously during inference).
  *
- * Use per batch: lora_cache_acquire(ids) -> build the plan -> launch the
- * batch's sgmv calls on the compute stream -> lora_cache_release(compute
- * stream).  Ordering is by events, the host never waits:
+ * Use per batch: lora_cache_acquire(ids) -> lora_cache_prefetch(the next
+ * batch's ids, when known) -> build the plan -> launch the batch's sgmv calls
+ * on the compute stream -> lora_cache_release(compute stream).  Prefetching
+ * before the launches lets the copies run under this batch's kernels; the
+ * batch's own adapters are held and cannot be evicted by it.  Ordering is by
+ * events, the host never waits:
  *   - acquire makes the compute stream wait for every copy enqueued so far;
  *   - a copy into an extent freed by an eviction waits for the release fence
  *     of the last batch that read the evicted adapter.

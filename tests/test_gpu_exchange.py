@@ -95,7 +95,8 @@ class LruModel:
                 self.misses += 1
             self.res[a] = self.tick
 
-    def prefetch(self, ids):
+    def prefetch(self, ids, held=()):
+        """held: the outstanding batch's adapters, which are never evicted."""
         self.tick += 1
         keep = set()
         for a in (int(i) for i in ids):
@@ -105,7 +106,7 @@ class LruModel:
             if a in self.res:
                 self.res[a] = self.tick
                 continue
-            if not self._bring(a, keep):
+            if not self._bring(a, keep | set(held)):
                 break
             self.prefetched += 1
 
@@ -162,6 +163,10 @@ def _run_batches(hab, w, cache, pool, batches, *, prefetch_next=False, model=Non
             ups.append(cache.acquire(segs, stream=comp))
             if model:
                 model.acquire(segs)
+            if prefetch_next and bi + 1 < len(batches):     # copies under this batch
+                cache.prefetch(batches[bi + 1][1])
+                if model:
+                    model.prefetch(batches[bi + 1][1], held=set(int(i) for i in segs if i >= 0))
             plan = hab.Plan(pool, w.num_tokens, starts, segs)
             plan.upload(2, stream=comp)
             ys = {}
@@ -170,10 +175,6 @@ def _run_batches(hab, w, cache, pool, batches, *, prefetch_next=False, model=Non
                                     dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
                 hab.sgmv_fused(pool, plan, l, (0, 1), [0, 192], x[l], ys[l], base[l], stream=comp)
             cache.release(stream=comp)
-            if prefetch_next and bi + 1 < len(batches):
-                cache.prefetch(batches[bi + 1][1])
-                if model:
-                    model.prefetch(batches[bi + 1][1])
             outs.append(ys)
             plans.append(plan)
     torch.cuda.synchronize()
