@@ -33,10 +33,19 @@
  * (the token keeps y_in); an id that is not in the adapter table, or a
  * segment table that does not partition [0, T), is an error (return -1).
  *
+ * Two more functions follow the same loops: the three-step delta of jointly
+ * compressed adapters (oracle_delta_sigma_*: a shared basis and a per-
+ * segment core between the A and B steps) and the weighted merge of several
+ * adapters per request (oracle_delta_merge_*).
+ *
  * Parity pins: every function here is pinned by the tests listed in the
  * oracle's test module (B = 0 identity, merged-weight equality, rank-1
  * closed form, permutation and split invariance, padding invariance,
- * linearity, indicator adapters, a hand-computed example).
+ * linearity, indicator adapters, a hand-computed example; for the cores:
+ * identity cores give plain LoRA bit for bit, power-of-two diagonal cores
+ * equal scaled A rows bit for bit, full cores equal s (B Sigma A) x in
+ * float64; for merges: one slot is plain LoRA, slots apply in order, the
+ * merge equals x (sum_k w_k s_k B_k A_k)^T in float64).
  */
 #include <stdint.h>
 #include <stdlib.h>
