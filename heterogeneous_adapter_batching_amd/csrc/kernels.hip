@@ -112,6 +112,26 @@ __device__ __forceinline__ int xcd_unit(int gs) {
     return (i / gs) * (kXcds * gs) + x * gs + (i % gs);
 }
 
+// Brings the whole kernel-argument block into the scalar cache in one
+// round: one dword of every 32 bytes, loaded together and waited for once.
+// The unit decode then reads its arguments in several dependent steps, each
+// a scalar-cache hit instead of a trip to L2 or HBM (the arguments of a
+// graph's kernels live in device memory).
+template <typename Args>
+__device__ __forceinline__ void warm_args() {
+    typedef const __attribute__((address_space(4))) uint32_t *kptr;
+    const kptr kp = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+    constexpr int N = int(sizeof(Args) + 31) / 32;
+    static_assert(N <= 15, "at most 15 scalar loads in flight");
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = i < N ? kp[8 * i] : 0u;
+    // every value live at once: the loads go out together, one wait
+    asm volatile("" ::"s"(w[0]), "s"(w[1]), "s"(w[2]), "s"(w[3]), "s"(w[4]), "s"(w[5]),
+                 "s"(w[6]), "s"(w[7]), "s"(w[8]), "s"(w[9]), "s"(w[10]), "s"(w[11]),
+                 "s"(w[12]), "s"(w[13]), "s"(w[14]));
+}
+
 // ---------------------------------------------------------------- shrink ----
 template <typename T, int TT>
 __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
@@ -120,6 +140,7 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     constexpr int F = shrink_frags<TT>();
     __shared__ f32x4 red[kWaves][TT][kWaveSize];
 
+    warm_args<ShrinkArgs>();
     const int u = xcd_unit(a.nproj);
     if (u >= a.units) return;            // whole workgroup: no barrier is skipped
     const int lane = threadIdx.x & 63;
@@ -788,32 +809,48 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     __shared__ float vs[kValuTokens][VS];
     __shared__ f32x4 ways[kValuTokens * LORA_MAX_RANK / 4][kSumWays];
 
+    warm_args<ExpandArgs>();
     const int u = xcd_unit(1);
+    int cbase = 0, rb = a.cls_rb[0];
+#pragma unroll
+    for (int i = 1; i < kMaxClasses; ++i) {
+        const int u0 = a.cls_unit0[i];
+        if (u >= u0) { cbase = u0; rb = a.cls_rb[i]; }
+    }
+    const int nproj = a.nproj;
+    int hout[LORA_MAX_PROJ];
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_PROJ; ++i) hout[i] = a.h_out[i];
     if (u >= a.units) return;                        // whole workgroup
-    int k = 0;
+    const int r_pad = rb & 0xff;
+    const int lg = decode_unit_rows_log2(r_pad, sizeof(T));
+    int cnt[LORA_MAX_PROJ], upb = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxClasses; ++i) k += u >= a.cls_unit0[i];
-    const DecodeClass &dc = a.cls[k];                // kernel-argument loads, no copy
-    const int ur = u - a.cls_unit0[k];
-    const int upb = dc.upb;
-    const int b = dc.block0 + ur / upb;
-    const int rem = ur - (ur / upb) * upb;
-    int p = 0, first = 0;                            // projection and its first unit
+    for (int i = 0; i < LORA_MAX_PROJ; ++i) {
+        cnt[i] = i < nproj ? (hout[i] + (1 << lg) - 1) >> lg : 0;
+        upb += cnt[i];
+    }
+    const int ur = u - cbase;
+    const int bi = ur / upb;
+    const int rem = ur - bi * upb;
+    const int b = (rb >> 8) + bi;
+    int p = 0, first = 0, run = 0;                   // projection and its first unit
 #pragma unroll
-    for (int i = 1; i < LORA_MAX_PROJ; ++i) {
-        const int pi = dc.prefix[i];
-        if (rem >= pi) { p = i; first = pi; }
+    for (int i = 0; i < LORA_MAX_PROJ; ++i) {
+        if (i < nproj && rem >= run) { p = i; first = run; }
+        run += cnt[i];
     }
     const int slice = rem - first;
-    const int r_pad = dc.rpad;
 
     const BlockDesc blk = a.blocks[b];
     const int4 bt4 = *reinterpret_cast<const int4 *>(a.block_tok + b * kMaxBlockTokens);
     const int tr[kValuTokens] = {bt4.x, bt4.y, bt4.z, bt4.w};
     static_assert(kValuTokens == 4, "token rows load as one int4");
 
-    const int h_out = a.h_out[p];
-    const int wrows = decode_wave_rows(r_pad, sizeof(T));
+    int h_out = hout[0];
+#pragma unroll
+    for (int i = 1; i < LORA_MAX_PROJ; ++i) h_out = p == i ? hout[i] : h_out;
+    const int wrows = 1 << (lg - 2);                 // rows of one wave slice
     const int o_lo = min(h_out, (slice * kWaves + wave_id()) * wrows);
     const int o_hi = min(h_out, o_lo + wrows);
 
@@ -851,6 +888,7 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
     __shared__ float vs[TT * kTile][VS];
 
+    warm_args<ExpandArgs>();
     const int u = xcd_unit(1);
     if (u >= a.units) return;                        // whole workgroup
     const int lane = threadIdx.x & 63;

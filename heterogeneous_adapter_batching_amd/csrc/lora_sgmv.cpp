@@ -1033,11 +1033,8 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     if (nb > nl) {
         // rank classes: runs of equal padded rank in block order (short
         // blocks by rank, largest first; then the blocks without an adapter)
-        for (int k = 0; k < lora::kMaxClasses; ++k) {
-            lora::DecodeClass &dc = a.cls[k];
-            dc.block0 = dc.upb = dc.rpad = INT32_MAX;
-            for (int i = 0; i <= LORA_MAX_PROJ; ++i) dc.prefix[i] = INT32_MAX;
-        }
+        for (int k = 0; k < lora::kMaxClasses; ++k) a.cls_rb[k] = 0;
+        if (nb >= (1 << 23)) return fail(LORA_ESTATE, "%d blocks: more than 2^23", nb);
         int32_t ncls = 0, units = 0;
         for (int32_t b = nl; b < nb;) {
             const int32_t r = pl->blocks[b].r_pad;
@@ -1045,16 +1042,12 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
             while (e < nb && pl->blocks[e].r_pad == r) ++e;
             if (ncls == lora::kMaxClasses)
                 return fail(LORA_ESTATE, "more than %d rank classes", lora::kMaxClasses);
-            const int32_t rows = lora::kWaves * lora::decode_wave_rows(r, esize(p->d.dtype));
-            lora::DecodeClass &dc = a.cls[ncls];
-            dc.rpad = r;
-            dc.block0 = b;
-            dc.prefix[0] = 0;
-            for (int i = 0; i < nproj; ++i)
-                dc.prefix[i + 1] = dc.prefix[i] + (a.h_out[i] + rows - 1) / rows;
-            dc.upb = dc.prefix[nproj];
+            const int32_t lg = lora::decode_unit_rows_log2(r, esize(p->d.dtype));
+            int32_t upb = 0;
+            for (int i = 0; i < nproj; ++i) upb += (a.h_out[i] + (1 << lg) - 1) >> lg;
+            a.cls_rb[ncls] = (b << 8) | r;
             a.cls_unit0[ncls] = units;
-            units += (e - b) * dc.upb;
+            units += (e - b) * upb;
             ++ncls;
             b = e;
         }

@@ -113,17 +113,6 @@ struct ReduceArgs {
     int32_t r_max;
 };
 
-// A rank class of the decode expand: blocks [block0, block0 + n) with padded
-// rank rpad; upb units per block, of which projection i of the call has
-// units [prefix[i], prefix[i + 1]) (prefix[0] = 0; entries past the call's
-// projections are INT32_MAX).  48 bytes: one scalar load.
-struct DecodeClass {
-    int32_t block0;
-    int32_t upb;
-    int32_t rpad;
-    int32_t prefix[LORA_MAX_PROJ + 1];
-};
-static_assert(sizeof(DecodeClass) == 48, "DecodeClass is 48 bytes");
 
 // Expand: one workgroup per unit (block b, projection i, slice of 4 * ocw
 // output rows; ocw = chunks * 16 * expand_tiles(ks)).  Each wave first issues the
@@ -170,10 +159,13 @@ struct ExpandArgs {
     int64_t sig_stride;
     int64_t sig_off[LORA_MAX_PROJ];
     int32_t sigma_kind;
-    // Decode expand: units by rank class; class k has units [cls_unit0[k],
-    // cls_unit0[k + 1]) (unused entries INT32_MAX) and the record cls[k].
+    // Decode expand: units by rank class.  Class k has units [cls_unit0[k],
+    // cls_unit0[k + 1]) (unused entries INT32_MAX) over blocks from its first
+    // one with one padded rank: cls_rb[k] = (first block << 8) | padded rank.
+    // A block has, per projection i of the call, ceil(h_out[i] / rows) units
+    // of rows = 1 << decode_unit_rows_log2(padded rank) output rows.
     int32_t cls_unit0[kMaxClasses + 1];
-    DecodeClass cls[kMaxClasses];
+    int32_t cls_rb[kMaxClasses];
 };
 
 // Decode expand geometry.  A B row of r_pad elements is nv 16-byte vectors;
@@ -191,6 +183,20 @@ constexpr int decode_rpl(int nvt) { return nvt >= 8 ? 1 : nvt >= 2 ? 8 / nvt : 4
 constexpr int decode_wave_rows(int r_pad, int esize) {
     return r_pad == 0 ? 4 * kWaveSize : decode_rpl(decode_nvt(r_pad, esize)) * kWaveSize;
 }
+// log2 of a decode unit's rows, kWaves wave slices: 1024 rows (r_pad 0, or
+// nvt 1 and 2), 512 (nvt 4) or 256 (nvt 8 and 16); selects only, for the
+// kernels' unit decode
+constexpr int decode_unit_rows_log2(int r_pad, int esize) {
+    return r_pad == 0 ? 10 : decode_nvt(r_pad, esize) >= 8 ? 8
+         : decode_nvt(r_pad, esize) == 4 ? 9 : 10;
+}
+constexpr bool decode_rows_agree() {
+    for (int es = 2; es <= 4; es += 2)
+        for (int r = 0; r <= LORA_MAX_RANK; r += 8)
+            if ((1 << decode_unit_rows_log2(r, es)) != kWaves * decode_wave_rows(r, es)) return false;
+    return true;
+}
+static_assert(decode_rows_agree(), "decode unit rows are kWaves wave slices");
 
 // 16-row output tiles per expand wave, for kernels built for `ks` K-steps
 // (ranks / (4 fragment elements)) at most: the wave keeps 8 B fragments.
