@@ -170,25 +170,26 @@ struct ExpandArgs {
 
 // Decode expand geometry.  A B row of r_pad elements is nv 16-byte vectors;
 // the kernel is built for nvt = nv rounded up to a power of two, and a lane
-// owns decode_rpl(nvt) rows of a step, so that one step of a wave streams
-// about 8 KB of B whatever the rank (4 KB at the smallest rank).  A wave's slice of a unit is one step;
-// a unit is kWaves slices.  Tokens without an adapter (r_pad 0) are copied
-// 4 outputs a lane.
+// owns decode_rpl(nvt) rows of a step: 2 rows up to 64-byte rows, 1 row
+// beyond, so one step of a wave streams 2-8 KB of B.  A wave's slice of a
+// unit is one step; a unit is kWaves slices.  Units of 2 rows a lane beat
+// 4 (fewer, longer workgroups) on every call of the full stack: 0.6-0.7 us
+// less for the 4096-row projections, even for the 28672-row gate/up pair.
+// Tokens without an adapter (r_pad 0) are copied 4 outputs a lane.
 constexpr int decode_nvt(int r_pad, int esize) {
     int nv = (r_pad * esize + 15) / 16, t = 1;
     while (t < nv) t *= 2;
     return t;
 }
-constexpr int decode_rpl(int nvt) { return nvt >= 8 ? 1 : nvt >= 2 ? 8 / nvt : 4; }
+constexpr int decode_rpl(int nvt) { return nvt >= 8 ? 1 : 2; }
 constexpr int decode_wave_rows(int r_pad, int esize) {
     return r_pad == 0 ? 4 * kWaveSize : decode_rpl(decode_nvt(r_pad, esize)) * kWaveSize;
 }
-// log2 of a decode unit's rows, kWaves wave slices: 1024 rows (r_pad 0, or
-// nvt 1 and 2), 512 (nvt 4) or 256 (nvt 8 and 16); selects only, for the
-// kernels' unit decode
+// log2 of a decode unit's rows, kWaves wave slices of decode_rpl rows per
+// lane (1024 rows for r_pad 0); selects only, for the kernels' unit decode
 constexpr int decode_unit_rows_log2(int r_pad, int esize) {
-    return r_pad == 0 ? 10 : decode_nvt(r_pad, esize) >= 8 ? 8
-         : decode_nvt(r_pad, esize) == 4 ? 9 : 10;
+    return r_pad == 0 ? 10 : 8 + (decode_rpl(decode_nvt(r_pad, esize)) >= 4 ? 2
+                                  : decode_rpl(decode_nvt(r_pad, esize)) == 2 ? 1 : 0);
 }
 constexpr bool decode_rows_agree() {
     for (int es = 2; es <= 4; es += 2)
