@@ -210,7 +210,7 @@ struct lora_plan {
         uint64_t most = 0;
         for (int32_t np = 1; np <= mp; ++np) {
             const uint64_t per_chunk = uint64_t(np) * std::max(rt_total(), 1);
-            const uint64_t by_target = (lora::kTargetGroups + per_chunk - 1) / per_chunk;
+            const uint64_t by_target = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
             most = std::max(most, per_chunk * std::max(by_target, by_frags));
         }
         return most;
@@ -861,7 +861,7 @@ lora_status check_y(const lora_pool *p, int32_t T, int32_t nproj, const int32_t 
     return LORA_OK;
 }
 
-// k-chunking of the shrink: about kTargetGroups workgroups per launch, each
+// k-chunking of the shrink: about kShrinkTargetGroups workgroups per launch, each
 // wave loading at most `frags` fragments (all issued up front); chunks are a
 // multiple of 4 fragment spans so the 4 waves split them evenly.
 void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
@@ -869,7 +869,7 @@ void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t s
     const int64_t per_chunk = int64_t(nproj) * std::max(pl->rt_total(), 1);
     const int32_t frags = pl->tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
     const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
-    int64_t want = (lora::kTargetGroups + per_chunk - 1) / per_chunk;
+    int64_t want = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
     want = std::max<int64_t>(1, std::min<int64_t>(want, steps));
     const int32_t sper = std::min<int32_t>(frags, int32_t((steps + want - 1) / want));
     *kc = sper * lora::kWaves * span;

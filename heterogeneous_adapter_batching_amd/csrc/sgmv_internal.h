@@ -36,7 +36,12 @@ constexpr int kSumWays = 4;
 // rank classes of the decode expand: distinct padded ranks (multiples of 8)
 // of the blocks, and 0 for tokens without an adapter
 constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
-constexpr int kTargetGroups = 1024;          // workgroups aimed for per launch (4 per CU)
+constexpr int kTargetGroups = 1024;          // MFMA expand: workgroups aimed for per launch
+// Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
+// more, shorter ones here (the expand then also sums fewer partials):
+// measured on the full stack, 384 beat 1024 by 3.5% per step, and 256..512
+// were within 1% of each other.
+constexpr int kShrinkTargetGroups = 384;
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 // Activations and outputs are addressed through buffer resources whose
 // out-of-range offset is 2^31: each such tensor spans at most 2 GiB.
