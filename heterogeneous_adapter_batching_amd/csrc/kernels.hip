@@ -390,12 +390,12 @@ __device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &b
     const int quads = blk.r_pad / 4;
     if (a.partial) {
         const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
-        const uint32_t stride = uint32_t(a.nproj * TT * kTile * kTile);
+        const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
             const int ti = i / quads, j = (i % quads) * 4;
             *reinterpret_cast<f32x4 *>(&vs[ti][j]) = chunk_sum(
-                pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, TT), stride,
-                a.c0);
+                pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, a.ptt),
+                stride, a.c0);
         }
     } else {
         for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
@@ -901,17 +901,28 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     c.w = wave_id();
     c.n = lane & 15;
     c.q = lane >> 4;
+    // unit -> (block, token slice, projection, row chunk)
     const int upb = a.oc_prefix[a.nproj];
-    c.b = u / upb;
-    const int rem = u - c.b * upb;
+    const int per_block = a.tslices * upb;
+    c.b = u / per_block;
+    const int rs = u - c.b * per_block;
+    const int ts = rs / upb;
+    const int rem = rs - ts * upb;
     c.p = 0;
     while (rem >= a.oc_prefix[c.p + 1]) ++c.p;
     const int oc = rem - a.oc_prefix[c.p];
+    // the slice's tokens as a block of their own: its first token, its first
+    // slot in the shrink block and its token count
+    BlockDesc blk = a.blocks[c.b];
+    const int off = ts * TT * kTile;
+    if (off >= blk.n_tok) return;                    // whole workgroup: an empty slice
+    blk.tok_off += off;
+    blk.slot0 += off;
+    blk.n_tok = min(TT * kTile, blk.n_tok - off);
     int trow[TT];                                    // token rows, -1 padded
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
-        trow[tt] = a.block_tok[c.b * kMaxBlockTokens + tt * kTile + c.n];
-    const BlockDesc blk = a.blocks[c.b];
+        trow[tt] = a.block_tok[c.b * kMaxBlockTokens + off + tt * kTile + c.n];
     c.h_out = a.h_out[c.p];
     const int rows_w = a.chunks * OTW * kTile;       // rows of this wave
     c.o_lo = min(c.h_out, (oc * kWaves + c.w) * rows_w);

@@ -986,7 +986,6 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         a.h_out[i] = p->d.h_out[projs[i]];
         a.y_off[i] = yoff[i];
     }
-    a.nb = nb;
     a.nproj = nproj;
     a.r_max = p->d.r_max;
     a.ptt = pl->tt;
@@ -1015,19 +1014,21 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         lora::ExpandArgs m = a;
         const int32_t ks = plan_ksteps(p, pl);
         const int64_t chunk_rows = int64_t(16 * lora::expand_tiles(ks)) * lora::kWaves;
+        // token tiles per unit, and token slices per block
+        const int32_t ttu = std::min<int32_t>(pl->tt, lora::kExpandUnitTiles);
+        m.tslices = pl->tt / ttu;
         int64_t rows = 0;
         for (int i = 0; i < nproj; ++i) rows += m.h_out[i];
-        m.nb = nl;
         m.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
-            8, rows * nl / (chunk_rows * lora::kTargetGroups))));
+            8, rows * nl * m.tslices / (chunk_rows * lora::kTargetGroups))));
         const int32_t rows_per_group = int32_t(chunk_rows) * m.chunks;
         m.oc_prefix[0] = 0;
         for (int i = 0; i < nproj; ++i)
             m.oc_prefix[i + 1] = m.oc_prefix[i] + (m.h_out[i] + rows_per_group - 1) / rows_per_group;
         for (int i = nproj; i < LORA_MAX_PROJ; ++i) m.oc_prefix[i + 1] = INT32_MAX;
-        m.units = nl * m.oc_prefix[nproj];
+        m.units = nl * m.tslices * m.oc_prefix[nproj];
         m.grid = grid_for(m.units, 1);
-        const hipError_t e = lora::launch_expand(p->d.dtype, pl->tt, ks, m, st);
+        const hipError_t e = lora::launch_expand(p->d.dtype, ttu, ks, m, st);
         if (e != hipSuccess) return hip_fail(e, "expand launch");
     }
     if (nb > nl) {

@@ -37,6 +37,11 @@ constexpr int kSumWays = 4;
 // of the blocks, and 0 for tokens without an adapter
 constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
 constexpr int kTargetGroups = 1024;          // MFMA expand: workgroups aimed for per launch
+// MFMA expand: 16-token tiles of a block per unit (a 64-token block is
+// kMaxBlockTokens / (16 * kExpandUnitTiles) units over the same rows).  One
+// tile a unit keeps the kernel at 146 VGPRs (3 waves a SIMD) where 4 tiles
+// spilled into AGPRs at 1 wave: 4.5% faster per prefill step, 2 tiles 3.5%.
+constexpr int kExpandUnitTiles = 1;
 // Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
 // more, shorter ones here (the expand then also sums fewer partials):
 // measured on the full stack, 384 beat 1024 by 3.5% per step, and 256..512
@@ -141,7 +146,7 @@ struct ExpandArgs {
     int32_t h_out[LORA_MAX_PROJ];
     int32_t y_off[LORA_MAX_PROJ];
     int32_t oc_prefix[LORA_MAX_PROJ + 1];  // row chunks of projections before i
-    int32_t nb;                  // blocks launched over
+    int32_t tslices;             // MFMA expand: token slices of TT tiles per block
     int32_t nproj;
     int32_t chunks;              // row chunks per wave (16 * expand_tiles(ks) rows each)
     int32_t c0;                  // partial chunks (when partial != null)
