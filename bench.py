@@ -132,11 +132,36 @@ def cpu_baseline(w, blocks, layers, threads, min_seconds):
             t_total += time.perf_counter() - t0
         passes += 1
     frac = len(layers) / w.num_layers
+    # one thread, over the first layer's calls only (bounded)
+    first = inputs[:len(w.projs)]
+    t1 = 0.0
+    for x, adapters, y_in, cores in first:
+        t0 = time.perf_counter()
+        if cores is not None:
+            oracle.lora_delta_sigma(x, w.seg_starts, w.seg_adapter, w.seg_sigma, adapters,
+                                    cores, w.sigma_kind, y_in, threads=1)
+        else:
+            oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, threads=1)
+        t1 += time.perf_counter() - t0
     return {"value": passes * w.num_tokens * frac / t_total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{passes} passes over {len(layers)} of {w.num_layers} layers x "
                       f"{len(w.projs)} projections, all {w.num_tokens} tokens, float32 oracle, "
-                      f"{threads} OpenMP threads, {t_total:.2f} s"}
+                      f"{threads} OpenMP threads, {t_total:.2f} s",
+            "single_thread": {"value": w.num_tokens / (t1 * w.num_layers), "unit": "tokens/s",
+                              "sample": f"1 of {w.num_layers} layers, {t1:.2f} s"},
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _time_graph(fn, stream, warmup, steps):
@@ -589,6 +614,19 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {args.mode}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms)")
 
+    # the spread of single steps: each step between its own pair of events
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+    per_step = np.sort([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    quant = {q: round(float(np.quantile(per_step, v)), 5)
+             for q, v in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
+
     # eager step time for reference (Python + C launch path, no graph)
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
@@ -600,52 +638,48 @@ def main():
         torch.cuda.synchronize()
     eager_ms = e2.elapsed_time(e3) / max(3, args.steps // 5)
 
-    # per-kernel durations on the launch stream, each over every call's
-    # launches back to back between two events: the fused call (shrink
-    # kernel + expand kernel), the standalone expand (one kernel, reading v)
-    # and the standalone shrink (shrink kernel + the small kernel that sums
-    # its partials into v).  The shrink kernel's time is the fused call's
-    # less the expand's.
-    v = torch.zeros((w.num_tokens, dw.max_proj * w.r_max), dtype=torch.float32, device="cuda")
+    # Per-kernel durations of the step's two kernels, launched back to back
+    # (a full queue, as in the step): passes over every (layer, call) of the
+    # shrink alone, and of the shrink then the expand (the two kernels of
+    # sgmv_fused as separate calls, in the step's order), between two events
+    # on the launch stream.  The expand's duration is the pair's less the
+    # shrink's.
     n_launch = len(dw.layers) * len(dw.calls)
 
-    def launch(kind):
+    def one_pass(expand):
         for l in dw.layers:
             for ci, c in enumerate(dw.calls):
-                vv = v[:, :len(c) * w.r_max]
                 x = dw.x[(l, w.projs[c[0]].x_key)]
-                if kind == "fused":
-                    if dw.sigma is not None:
-                        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
-                                             dw.sigma, w.sigma_kind, dw.y[(l, ci)],
-                                             dw.base.get((l, ci)))
-                    else:
-                        hab.sgmv_fused(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
-                                       dw.y[(l, ci)], dw.base.get((l, ci)))
-                elif kind == "shrink+reduce":
-                    hab.sgmv_shrink(dw.pool, dw.plan, l, c, x, vv)
-                elif dw.sigma is not None:
-                    hab.sgmv_expand_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci], vv,
-                                          dw.sigma, w.sigma_kind, dw.y[(l, ci)])
+                hab.sgmv_shrink_partials(dw.pool, dw.plan, l, c, x, stream=stream)
+                if not expand:
+                    continue
+                if dw.sigma is not None:
+                    hab.sgmv_expand_partials_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci],
+                                                   dw.sigma, w.sigma_kind, dw.y[(l, ci)],
+                                                   dw.base.get((l, ci)), stream=stream)
                 else:
-                    hab.sgmv_expand(dw.pool, dw.plan, l, c, dw.y_offsets[ci], vv, dw.y[(l, ci)])
+                    hab.sgmv_expand_partials(dw.pool, dw.plan, l, c, dw.y_offsets[ci],
+                                             dw.y[(l, ci)], dw.base.get((l, ci)), stream=stream)
 
-    us = {}
+    tot = {}
     with torch.cuda.stream(stream):
-        for kind in ("fused", "shrink+reduce", "expand"):
-            launch(kind)                                   # warm
+        for kind, expand in (("shrink", False), ("pair", True)):
+            one_pass(expand)                                 # warm
             torch.cuda.synchronize()
             ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ea.record(stream)
             for _ in range(args.kernel_reps):
-                launch(kind)
+                one_pass(expand)
             eb.record(stream)
             torch.cuda.synchronize()
-            us[kind] = ea.elapsed_time(eb) * 1e3 / (args.kernel_reps * n_launch)
-    us["shrink"] = us["fused"] - us["expand"]
+            tot[kind] = ea.elapsed_time(eb)
+    tot["expand"] = tot["pair"] - tot["shrink"]
+    tot.pop("pair")
+    us = {kind: t * 1e3 / (args.kernel_reps * n_launch) for kind, t in tot.items()}
+    us["fused"] = us["shrink"] + us["expand"]
     kern = {}
-    for kind in ("shrink", "expand", "shrink+reduce", "fused"):
-        parts = ("shrink", "expand") if kind == "fused" else (kind.split("+")[0],)
+    for kind in ("shrink", "expand", "fused"):
+        parts = ("shrink", "expand") if kind == "fused" else (kind,)
         bpl = sum(kernel_bytes(w, c, k) for c in dw.calls for k in parts) / len(dw.calls)
         kern[kind] = {"avg_us": us[kind], "gbs": bpl / (us[kind] * 1e-6) / 1e9,
                       "alg_bytes_per_launch": bpl}
@@ -699,6 +733,13 @@ def main():
                    "distinct_adapters": int(len(w.touched())), "mode": args.mode},
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        # the attainable roof for the path's arithmetic intensity I (FLOP/B):
+        # min(MFMA peak, I x HBM peak); the step's TFLOP/s as a fraction of it
+        "attainable_tflops": round(min(BF16_PEAK_TFLOPS, alg["flops"] / alg["bytes"] *
+                                       HBM_PEAK_GBS / 1e3), 2),
+        "attainable_frac": round(tflops / min(BF16_PEAK_TFLOPS, alg["flops"] / alg["bytes"] *
+                                              HBM_PEAK_GBS / 1e3), 4),
+        "step_ms_quantiles": quant,
         "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"],
         "eager_ms_per_step": round(eager_ms, 5),
         "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},

@@ -15,9 +15,11 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     Pool, Plan, sgmv_shrink, sgmv_expand, sgmv_fused, sgmv_expand_sigma, sgmv_fused_sigma,
-    merge_fused, adapter_bytes, extent_bytes, pack_adapter, Cache,
+    merge_fused, adapter_bytes, extent_bytes, pack_adapter, Cache, sgmv_shrink_partials,
+    sgmv_expand_partials, sgmv_expand_partials_sigma,
 )
 
 __all__ = ["Pool", "Plan", "sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_expand_sigma",
-           "sgmv_fused_sigma", "merge_fused", "adapter_bytes", "extent_bytes", "pack_adapter",
-           "Cache", "LoraError", "load"]
+           "sgmv_fused_sigma", "sgmv_shrink_partials", "sgmv_expand_partials",
+           "sgmv_expand_partials_sigma", "merge_fused",
+           "adapter_bytes", "extent_bytes", "pack_adapter", "Cache", "LoraError", "load"]

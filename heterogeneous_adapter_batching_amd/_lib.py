@@ -69,6 +69,11 @@ SIGNATURES = {
                                  _vp, _i64, _vp]),
     "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
                                 _vp, _i64, _vp, _i64, _vp]),
+    "sgmv_shrink_partials": (_i32, [_vp, _vp, _i32, _i32, _i32p, _vp, _i64, _vp]),
+    "sgmv_expand_partials": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64,
+                                    _vp]),
+    "sgmv_expand_partials_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i32, _i32,
+                                          _vp, _i64, _vp, _i64, _vp]),
     "lora_pack_adapter": (_i32, [ctypes.POINTER(PoolDesc), _i32, _pp, _pp, _vp, _u64]),
     "lora_pool_upload_image": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "lora_pool_register_image": (_i32, [_vp, _i32, _i32, _f32, _vp, _i32, _vp]),

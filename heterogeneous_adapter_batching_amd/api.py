@@ -427,6 +427,52 @@ def sgmv_fused(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=
     return y
 
 
+def sgmv_shrink_partials(pool: Pool, plan: Plan, layer: int, projs, x, stream=None):
+    """The shrink of sgmv_fused alone: partial sums of v = A x left in the
+    plan's workspace for sgmv_expand_partials of the same call."""
+    _check_dev(x, "x", _torch_dtype(pool.dtype))
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_shrink_partials(pool.handle, plan.handle, layer, n, parr,
+                                        ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                                        _stream_handle(stream)))
+
+
+def sgmv_expand_partials(pool: Pool, plan: Plan, layer: int, projs, y_offsets, y, base=None,
+                         stream=None):
+    """The expand of sgmv_fused alone, from the partials of the plan's last
+    shrink (which must be this call's): y = (base or y) + s * B v."""
+    dt = _torch_dtype(pool.dtype)
+    _check_dev(y, "y", dt)
+    if base is not None:
+        _check_dev(base, "base", dt)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_expand_partials(pool.handle, plan.handle, layer, n, parr,
+                                        _i32_array(y_offsets),
+                                        ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                        base.stride(0) if base is not None else 0,
+                                        ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                        _stream_handle(stream)))
+    return y
+
+
+def sgmv_expand_partials_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, sigma, kind,
+                               y, base=None, stream=None):
+    """sgmv_expand_partials with the core step of jointly compressed adapters."""
+    dt = _torch_dtype(pool.dtype)
+    _check_dev(y, "y", dt)
+    if base is not None:
+        _check_dev(base, "base", dt)
+    _check_cores(pool, sigma, kind)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_expand_partials_sigma(
+        pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
+        ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), sigma.shape[0],
+        ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+        base.stride(0) if base is not None else 0, ctypes.c_void_p(y.data_ptr()), y.stride(0),
+        _stream_handle(stream)))
+    return y
+
+
 def _sigma_kind(kind) -> int:
     codes = {"diag": LORA_SIGMA_DIAG, "full": LORA_SIGMA_FULL}
     if kind not in codes:

@@ -177,6 +177,10 @@ struct lora_plan {
     void *staging = nullptr;
     uint64_t staging_bytes = 0;
     hipEvent_t staged = nullptr;
+    // the call whose shrink partials the workspace holds (sgmv_shrink_partials):
+    // layer, projections and k-chunks; part_layer -1 = none
+    mutable int32_t part_layer = -1, part_nproj = 0, part_c0 = 0;
+    mutable int32_t part_projs[LORA_MAX_PROJ] = {};
 
     int32_t rt_total() const { return int32_t(tiles.size()); }
     int32_t nb_all() const { return int32_t(blocks.size()); }
@@ -771,6 +775,7 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     e = hipEventRecord(pl->staged, st);
     if (e != hipSuccess) return hip_fail(e, "plan staging event record");
     pl->ws = ws;
+    pl->part_layer = -1;               // a new workspace holds no partials
     return LORA_OK;
 }
 
@@ -885,7 +890,18 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
                        const int32_t *projs, const void *x, int64_t ldx, const CallCheck &cc,
                        hipStream_t st, int32_t *c0_out) {
     *c0_out = 0;
-    if (pl->nb_act == 0) return LORA_OK;
+    // every shrink leaves its partials in the workspace: record whose they are
+    pl->part_layer = -1;
+    auto record = [&](int32_t c0) {
+        pl->part_layer = layer;
+        pl->part_nproj = nproj;
+        pl->part_c0 = c0;
+        for (int i = 0; i < nproj; ++i) pl->part_projs[i] = projs[i];
+    };
+    if (pl->nb_act == 0) {
+        record(0);
+        return LORA_OK;
+    }
     lora::ShrinkArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
@@ -909,6 +925,7 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
     *c0_out = a.c0;
+    record(a.c0);
     return LORA_OK;
 }
 
@@ -1165,6 +1182,68 @@ lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t la
     if (st != LORA_OK) return st;
     return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
                       cores);
+}
+
+lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                 int32_t nproj, const int32_t *projs, const void *x, int64_t ldx,
+                                 void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    if (pl->T > 0) {
+        if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
+        if (ldx < cc.h_in || ldx % 8)
+            return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8", (long long)ldx);
+        if (tensor_bytes(pl->T, ldx, cc.h_in, cc.es) > lora::kMaxTensorBytes)
+            return fail(LORA_EINVAL, "x spans more than 2 GiB");
+    }
+    int32_t c0 = 0;
+    if (pl->T == 0) {                  // empty batch: nothing to read; the record alone
+        pl->part_layer = layer;
+        pl->part_nproj = nproj;
+        pl->part_c0 = 0;
+        for (int i = 0; i < nproj; ++i) pl->part_projs[i] = projs[i];
+        return LORA_OK;
+    }
+    return run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, static_cast<hipStream_t>(stream),
+                      &c0);
+}
+
+lora_status sgmv_expand_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                 int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                                 const void *base, int64_t ldb, void *y, int64_t ldy,
+                                 void *stream) {
+    return sgmv_expand_partials_sigma(p, pl, layer, nproj, projs, yoff, nullptr, 0, 0, base, ldb,
+                                      y, ldy, stream);
+}
+
+lora_status sgmv_expand_partials_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                       int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                                       const float *sigma, int32_t sigma_kind, int32_t num_sigma,
+                                       const void *base, int64_t ldb, void *y, int64_t ldy,
+                                       void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    const Cores cores{sigma, sigma_kind, num_sigma};
+    if (sigma_kind != 0 || sigma) {
+        st = check_cores(pl, cores);
+        if (st != LORA_OK) return st;
+    }
+    bool same = pl->part_layer == layer && pl->part_nproj == nproj;
+    for (int i = 0; same && i < nproj; ++i) same = pl->part_projs[i] == projs[i];
+    if (!same)
+        return fail(LORA_ESTATE, "the plan's workspace holds no shrink partials of layer %d "
+                                 "and these projections", layer);
+    if (pl->T == 0) return LORA_OK;
+    st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
+    if (st != LORA_OK) return st;
+    if (base) {
+        st = check_y(p, pl->T, nproj, projs, yoff, base, ldb, "base", cc);
+        if (st != LORA_OK) return st;
+    }
+    return run_expand(p, pl, layer, nproj, projs, yoff, pl->part_c0, nullptr, 0, y, ldy, base,
+                      ldb, static_cast<hipStream_t>(stream), cores);
 }
 
 }  // extern "C"

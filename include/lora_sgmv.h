@@ -361,6 +361,31 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
                        const void *x, int64_t ldx, const void *base, int64_t ldb,
                        void *y, int64_t ldy, void *stream);
 
+/* sgmv_fused in two calls, each one kernel: the shrink (the A step, scale
+ * 1.0, "Compress then Serve" rebuttal pseudocode, step 1) leaves float32
+ * partial sums of v in the plan's workspace; the expand (step 3) sums them
+ * and writes y exactly as sgmv_fused does (the same bits).  The shrink needs
+ * only x, so a caller can run it beside the frozen layer's own product and
+ * the expand after it.  The workspace holds the partials of the last shrink
+ * run with the plan (this one, sgmv_fused's or sgmv_shrink's); the expand
+ * must name that call's layer and projections (LORA_ESTATE otherwise), and
+ * runs on a stream ordered after that shrink.  Arguments and errors as
+ * sgmv_fused. */
+lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                 int32_t nproj, const int32_t *projs, const void *x, int64_t ldx,
+                                 void *stream);
+lora_status sgmv_expand_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                 int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                                 const void *base, int64_t ldb, void *y, int64_t ldy,
+                                 void *stream);
+/* The same expand with the core step of jointly compressed adapters (the
+ * core table as for sgmv_fused_sigma). */
+lora_status sgmv_expand_partials_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                                       int32_t nproj, const int32_t *projs,
+                                       const int32_t *y_offsets, const float *sigma,
+                                       int32_t sigma_kind, int32_t num_sigma, const void *base,
+                                       int64_t ldb, void *y, int64_t ldy, void *stream);
+
 /* The three-step delta of jointly compressed adapters ("Compress then
  * Serve", rebuttal pseudocode of add_lora_slice_with_sigma: step 1 A into a
  * float32 buffer, step 2 the core Sigma into a second float32 buffer, step 3

@@ -661,3 +661,33 @@ def test_weight_errors():
     bad[-1] = np.inf
     with pytest.raises(hab.LoraError):
         hab.Plan(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter, seg_weight=bad)
+
+
+def test_split_fused_bitexact():
+    """sgmv_shrink_partials then sgmv_expand_partials give sgmv_fused's bits
+    (decode blocks, prefill blocks, a mixed batch; with and without base);
+    the expand refuses partials of another call."""
+    import heterogeneous_adapter_batching_amd as hab
+    cases = (random_case(61, T=100, h_in=384, h_out=256, n_adapters=6, has_base=True, max_seg=3),
+             random_case(62, T=1300, h_in=256, h_out=128, n_adapters=3, max_seg=600,
+                         no_adapter_frac=0.0),
+             mixed_case(63, h_in=256, h_out=192, has_base=False))
+    for w in cases:
+        log(f"[parity] split {w.name}")
+        dw = DeviceWorkload(w, threads=4)
+        x = dw.x[(0, "x")]
+        base = dw.base.get((0, 0))
+        y1 = torch.zeros_like(dw.y[(0, 0)])
+        y2 = torch.zeros_like(dw.y[(0, 0)])
+        hab.sgmv_fused(dw.pool, dw.plan, 0, (0,), [0], x, y1, base)
+        hab.sgmv_shrink_partials(dw.pool, dw.plan, 0, (0,), x)
+        hab.sgmv_expand_partials(dw.pool, dw.plan, 0, (0,), [0], y2, base)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(y1).view(np.uint8), from_device(y2).view(np.uint8))
+    with pytest.raises(hab.LoraError) as ei:     # partials of layer 0, expand of layer 1
+        w = random_case(64, T=20, h_in=64, h_out=32)
+        w = dataclasses.replace(w, num_layers=2)
+        dw = DeviceWorkload(w, threads=4)
+        hab.sgmv_shrink_partials(dw.pool, dw.plan, 0, (0,), dw.x[(0, "x")])
+        hab.sgmv_expand_partials(dw.pool, dw.plan, 1, (0,), [0], dw.y[(1, 0)])
+    assert ei.value.status == -9
