@@ -691,3 +691,24 @@ def test_split_fused_bitexact():
         hab.sgmv_shrink_partials(dw.pool, dw.plan, 0, (0,), dw.x[(0, "x")])
         hab.sgmv_expand_partials(dw.pool, dw.plan, 1, (0,), [0], dw.y[(1, 0)])
     assert ei.value.status == -9
+
+
+@pytest.mark.parametrize("kind", ["full", "diag"])
+def test_split_fused_sigma_bitexact(kind):
+    """The split form with cores gives sgmv_fused_sigma's bits."""
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import jd_case
+    w = jd_case(71 if kind == "full" else 72, kind=kind, T=96, max_seg=3)
+    log(f"[parity] split sigma {w.name}")
+    dw = DeviceWorkload(w, threads=4)
+    c = dw.calls[0]
+    x = dw.x[(0, w.projs[c[0]].x_key)]
+    base = dw.base.get((0, 0))
+    y1 = torch.zeros_like(dw.y[(0, 0)])
+    y2 = torch.zeros_like(dw.y[(0, 0)])
+    hab.sgmv_fused_sigma(dw.pool, dw.plan, 0, c, dw.y_offsets[0], x, dw.sigma, kind, y1, base)
+    hab.sgmv_shrink_partials(dw.pool, dw.plan, 0, c, x)
+    hab.sgmv_expand_partials_sigma(dw.pool, dw.plan, 0, c, dw.y_offsets[0], dw.sigma, kind, y2,
+                                   base)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device(y1).view(np.uint8), from_device(y2).view(np.uint8))
