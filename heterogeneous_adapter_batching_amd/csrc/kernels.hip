@@ -24,6 +24,8 @@
 // multiply exactly inside the bf16 MFMA and sum in float32.  For the B step
 // the float32 v is split into three bf16 pieces whose sum is v exactly, so
 // B (h0 + h1 + h2) is the float32 product B v summed in float32.
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "sgmv_internal.h"
@@ -697,34 +699,49 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
         y_row[tt] = tv[tt] ? uint32_t((int64_t(trow[tt]) * a.ldy + c.yoff) * sizeof(T)) : kOOB;
     }
     const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
-    // this lane's row within a tile and element offset within the row
+    // this lane's tile within a load and element offset within its B row
     const int lane_tile = TPL == 1 ? 0 : c.q / G;
-    const uint32_t lane_b = uint32_t(lane_tile * kTile + c.n) * row_bytes +
-                            uint32_t(TPL == 1 ? c.q * E : (c.q % G) * E) * sizeof(T);
+    const uint32_t lane_col = uint32_t(TPL == 1 ? c.q * E : (c.q % G) * E) * sizeof(T);
+    // bf16: within each pair of row tiles the B rows are taken in the order
+    // that leaves a lane 8 consecutive outputs (4 from each tile of the
+    // pair), so y_in and y move 16 bytes a lane: tile T's MFMA row n is
+    // output row 16 (T & ~1) + 8 (n / 4) + 4 (T & 1) + n % 4 of the chunk.
+    constexpr bool PAIR = sizeof(T) == 2;
+    static_assert(!PAIR || OTW % 2 == 0, "row tiles of a chunk come in pairs");
+    auto brow = [&](int tile, int n) {
+        return PAIR ? (tile & ~1) * kTile + 8 * (n >> 2) + 4 * (tile & 1) + (n & 3)
+                    : tile * kTile + n;
+    };
+    constexpr int NY = PAIR ? OTW / 2 : OTW;         // y_in loads per token tile and chunk
+    typedef typename std::conditional<PAIR, u32x4, raw>::type yraw;
 
-    auto load = [&](int o0, u32x4 (&bf)[NL], raw (&yin)[OTW][TT]) {
+    auto load = [&](int o0, u32x4 (&bf)[NL], yraw (&yin)[NY][TT]) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
             const int t = TPL == 1 ? l / KSM : l * TPL;          // first tile of the load
             const int ks = TPL == 1 ? l % KSM : 0;
-            const int row = o0 + (t + lane_tile) * kTile + c.n;
+            const int row = o0 + brow(t + lane_tile, c.n);
             const bool ok = row < c.o_hi &&
                             (TPL > 1 || (ks < c.ks_n && ks * SPAN + c.q * E < blk.r_pad));
-            bf[l] = bload16(br, off_or_oob(ok, uint32_t(o0 + t * kTile) * row_bytes + lane_b +
+            bf[l] = bload16(br, off_or_oob(ok, uint32_t(row) * row_bytes + lane_col +
                                                    uint32_t(ks * SPAN) * sizeof(T)));
         }
 #pragma unroll
-        for (int ot = 0; ot < OTW; ++ot) {
-            const int o = o0 + ot * kTile + 4 * c.q;
+        for (int oy = 0; oy < NY; ++oy) {
+            const int o = PAIR ? o0 + oy * 2 * kTile + 8 * c.q : o0 + oy * kTile + 4 * c.q;
             const uint32_t oo = uint32_t(o) * sizeof(T);
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt)
-                yin[ot][tt] = Out4<T>::load(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
+            for (int tt = 0; tt < TT; ++tt) {
+                if constexpr (PAIR)
+                    yin[oy][tt] = bload16(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
+                else
+                    yin[oy][tt] = Out4<T>::load(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
+            }
         }
     };
 
     u32x4 bfA[NL], bfB[NL];
-    raw yinA[OTW][TT], yinB[OTW][TT];
+    yraw yinA[NY][TT], yinB[NY][TT];
     load(c.o_lo, bfA, yinA);
 
     gather_v<TT>(a, blk, c.p, vs);
@@ -754,39 +771,66 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
         }
     }
 
-    auto compute = [&](int o0, const u32x4 (&bf)[NL], const raw (&yin)[OTW][TT]) {
+    // B v of row tile ot for token tile tt: D rows 4q .. 4q + 3 of the tile
+    auto tile_acc = [&](int ot, int tt, const u32x4 (&bf)[NL]) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (TPL == 1) {
 #pragma unroll
-        for (int ot = 0; ot < OTW; ++ot) {
-            const int obase = o0 + ot * kTile;
+            for (int ks = 0; ks < KSM; ++ks) {
+                if (ks >= c.ks_n) continue;
+#pragma unroll
+                for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
+                    acc = mma<T>(bf[ot * KSM + ks], vop[tt][ks].piece[pc], acc);
+            }
+        } else {
+            const bool mine = c.q / G == ot % TPL;   // lane groups of this tile
+#pragma unroll
+            for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc) {
+                const u32x4 vp = vop[tt][0].piece[pc];
+                const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                acc = mma<T>(bf[ot / TPL], mine ? vp : z, acc);
+            }
+        }
+        return acc;
+    };
+
+    auto compute = [&](int o0, const u32x4 (&bf)[NL], const yraw (&yin)[NY][TT]) {
+#pragma unroll
+        for (int oy = 0; oy < NY; ++oy) {
+            const int obase = o0 + oy * (PAIR ? 2 : 1) * kTile;
             if (obase >= c.o_hi) break;              // wave-uniform
 #pragma unroll
             for (int tt = 0; tt < TT; ++tt) {
                 if (tt >= c.ntiles) continue;        // wave-uniform
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (TPL == 1) {
+                if constexpr (PAIR) {
+                    // tiles 2 oy and 2 oy + 1: this lane's outputs 8 q .. 8 q + 7
+                    const f32x4 a0 = tile_acc(2 * oy, tt, bf);
+                    const f32x4 a1 = tile_acc(2 * oy + 1, tt, bf);
+                    const int o = obase + 8 * c.q;
+                    const u32x4 w = yin[oy][tt];
+                    float out[8];
 #pragma unroll
-                    for (int ks = 0; ks < KSM; ++ks) {
-                        if (ks >= c.ks_n) continue;
-#pragma unroll
-                        for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
-                            acc = mma<T>(bf[ot * KSM + ks], vop[tt][ks].piece[pc], acc);
+                    for (int i = 0; i < 2; ++i) {
+                        out[2 * i] = bf16_lo(w[i]) + c.tsc[tt] * a0[2 * i];
+                        out[2 * i + 1] = bf16_hi(w[i]) + c.tsc[tt] * a0[2 * i + 1];
+                        out[4 + 2 * i] = bf16_lo(w[2 + i]) + c.tsc[tt] * a1[2 * i];
+                        out[5 + 2 * i] = bf16_hi(w[2 + i]) + c.tsc[tt] * a1[2 * i + 1];
                     }
+                    const u32x4 pk = u32x4{bf16x2_rne(out[0], out[1]), bf16x2_rne(out[2], out[3]),
+                                           bf16x2_rne(out[4], out[5]), bf16x2_rne(out[6], out[7])};
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        pk, yr, int(o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB), 0,
+                        kOut);
                 } else {
-                    const bool mine = c.q / G == ot % TPL;   // lane groups of this tile
+                    const f32x4 acc = tile_acc(oy, tt, bf);
+                    const int o = obase + 4 * c.q;
+                    float in[4], out[4];
+                    Out4<T>::unpack(yin[oy][tt], in);
 #pragma unroll
-                    for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc) {
-                        const u32x4 vp = vop[tt][0].piece[pc];
-                        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-                        acc = mma<T>(bf[ot / TPL], mine ? vp : z, acc);
-                    }
+                    for (int i = 0; i < 4; ++i) out[i] = in[i] + c.tsc[tt] * acc[i];
+                    Out4<T>::store(yr, o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB,
+                                   Out4<T>::pack(out));
                 }
-                const int o = obase + 4 * c.q;
-                float in[4], out[4];
-                Out4<T>::unpack(yin[ot][tt], in);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) out[i] = in[i] + c.tsc[tt] * acc[i];
-                Out4<T>::store(yr, o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB,
-                               Out4<T>::pack(out));
             }
         }
     };
