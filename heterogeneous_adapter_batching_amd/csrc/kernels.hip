@@ -852,7 +852,10 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
 // loads are the block's descriptor and token rows (one round trip).
 // Sig: the launch applies cores of jointly compressed adapters (a separate
 // build, so the plain kernel keeps its registers).
-template <typename T, bool Sig>
+// NVM: the largest count of 16-byte vectors per B row among the launch's
+// rank classes; a build per bound, so that a batch of small ranks runs with
+// the registers (and occupancy) of its own class rather than of rank 64.
+template <typename T, bool Sig, int NVM>
 __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     constexpr int VS = LORA_MAX_RANK + 4;
     __shared__ float vs[kValuTokens][VS];
@@ -919,13 +922,16 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
         }
         return;
     }
-    switch (decode_nvt(r_pad, sizeof(T))) {
+    switch (decode_nvt(r_pad, sizeof(T))) {         // <= NVM for every class of the launch
     case 1: return expand_valu<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 2: return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 4: return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 8: return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+            return;
+    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+            return;
+    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+            return;
     default:
-        if constexpr (sizeof(T) == 4) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 
@@ -1091,15 +1097,26 @@ hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s) {
+template <typename T, bool Sig>
+void expand_decode_nvm(int nvm, dim3 grid, dim3 block, const ExpandArgs &a, hipStream_t s) {
+    if (nvm <= 1) hipLaunchKernelGGL((k_expand_decode<T, Sig, 1>), grid, block, 0, s, a);
+    else if (nvm <= 2) hipLaunchKernelGGL((k_expand_decode<T, Sig, 2>), grid, block, 0, s, a);
+    else if (nvm <= 4) hipLaunchKernelGGL((k_expand_decode<T, Sig, 4>), grid, block, 0, s, a);
+    else if (nvm <= 8) hipLaunchKernelGGL((k_expand_decode<T, Sig, 8>), grid, block, 0, s, a);
+    else if constexpr (sizeof(T) == 4) hipLaunchKernelGGL((k_expand_decode<T, Sig, 16>), grid, block, 0, s, a);
+}
+
+hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
     const dim3 grid(a.grid), block(kWaves * kWaveSize);
-    if (a.sigma_kind) {
-        if (dtype == LORA_BF16) hipLaunchKernelGGL((k_expand_decode<uint16_t, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_expand_decode<float, true>), grid, block, 0, s, a);
+    if (dtype == LORA_BF16) {
+        if (nvm > 8) return hipErrorInvalidValue;
+        if (a.sigma_kind) expand_decode_nvm<uint16_t, true>(nvm, grid, block, a, s);
+        else expand_decode_nvm<uint16_t, false>(nvm, grid, block, a, s);
     } else {
-        if (dtype == LORA_BF16) hipLaunchKernelGGL((k_expand_decode<uint16_t, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_expand_decode<float, false>), grid, block, 0, s, a);
+        if (nvm > 16) return hipErrorInvalidValue;
+        if (a.sigma_kind) expand_decode_nvm<float, true>(nvm, grid, block, a, s);
+        else expand_decode_nvm<float, false>(nvm, grid, block, a, s);
     }
     return hipGetLastError();
 }

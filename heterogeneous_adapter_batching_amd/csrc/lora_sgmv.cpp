@@ -1053,7 +1053,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         // blocks by rank, largest first; then the blocks without an adapter)
         for (int k = 0; k < lora::kMaxClasses; ++k) a.cls_rb[k] = 0;
         if (nb >= (1 << 23)) return fail(LORA_ESTATE, "%d blocks: more than 2^23", nb);
-        int32_t ncls = 0, units = 0;
+        int32_t ncls = 0, units = 0, nvm = 1;
         for (int32_t b = nl; b < nb;) {
             const int32_t r = pl->blocks[b].r_pad;
             int32_t e = b;
@@ -1063,6 +1063,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
             const int32_t lg = lora::decode_unit_rows_log2(r, esize(p->d.dtype));
             int32_t upb = 0;
             for (int i = 0; i < nproj; ++i) upb += (a.h_out[i] + (1 << lg) - 1) >> lg;
+            if (r > 0) nvm = std::max(nvm, lora::decode_nvt(r, esize(p->d.dtype)));
             a.cls_rb[ncls] = (b << 8) | r;
             a.cls_unit0[ncls] = units;
             units += (e - b) * upb;
@@ -1072,7 +1073,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         for (int k = ncls; k <= lora::kMaxClasses; ++k) a.cls_unit0[k] = k == ncls ? units : INT32_MAX;
         a.units = units;
         a.grid = grid_for(a.units, 1);
-        const hipError_t e = lora::launch_expand_decode(p->d.dtype, a, st);
+        const hipError_t e = lora::launch_expand_decode(p->d.dtype, nvm, a, st);
         if (e != hipSuccess) return hip_fail(e, "expand launch");
     }
     return LORA_OK;

@@ -226,6 +226,7 @@ hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *d
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s);
 // decode expand (every block of the plan within kValuTokens tokens)
-hipError_t launch_expand_decode(int dtype, const ExpandArgs &a, hipStream_t s);
+// nvm: the largest decode_nvt of the launch's rank classes
+hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s);
 
 }  // namespace lora

@@ -166,6 +166,29 @@ def test_random_heterogeneous(seed):
     check_workload(dw, tight=True, threads=4)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("r_top", [4, 8, 16, 32, 64])
+def test_decode_rank_bound(dtype, r_top):
+    """Decode batches whose largest rank is r_top: the decode expand is built
+    per bound on the B row width of the launch's rank classes, so each bound
+    (and the classes below it in one launch) is checked."""
+    seed = 200 + r_top + (1 if dtype == "f32" else 0)
+    w = random_case(seed, T=48, h_in=264, h_out=200, n_adapters=6, max_seg=3,
+                    r_choices=sorted({r_top, max(1, r_top // 2), max(1, r_top // 4), 1}),
+                    dtype=dtype, has_base=r_top % 16 == 0)
+    # adapter 0 has rank r_top and the first non-empty segment
+    first = int(np.flatnonzero(np.diff(w.seg_starts) > 0)[0])
+    w = dataclasses.replace(w, ranks=np.where(np.arange(w.pool_size) == 0, r_top, w.ranks)
+                            .astype(np.int32), seg_adapter=np.where(
+                                np.arange(w.num_segs) == first, 0, w.seg_adapter).astype(np.int32))
+    log(f"[parity] decode rank bound {r_top} {dtype} ranks={list(w.ranks)}")
+    dw = DeviceWorkload(w, threads=4)
+    assert dw.plan.stats()["max_block_tokens"] <= 4
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_prefill_blocks(seed):
     """Long same-adapter segments (over 1024 tokens in long groups, so the
