@@ -142,15 +142,22 @@ __device__ __forceinline__ void warm_args() {
 }
 
 // ---------------------------------------------------------------- shrink ----
-template <typename T, int TT>
+// NP > 1: a unit is (rank tile, k-chunk) and runs all NP projections of the
+// call (a.nproj == NP) over one load of its x fragments: the A fragments of
+// every projection, then x, all in flight together, then the projections'
+// MFMAs and partial tiles one after the other (the same tiles as the
+// per-projection units write).  For blocks of more than one 16-token tile,
+// where x is most of the shrink's loads.
+template <typename T, int TT, int NP>
 __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
+    constexpr bool MP = NP > 1;
     constexpr int E = Elem<T>::E;        // elements per 16-byte fragment
     constexpr int SPAN = 4 * E;          // K covered by one fragment over 4 lane groups
     constexpr int F = shrink_frags<TT>();
     __shared__ f32x4 red[kWaves][TT][kWaveSize];
 
     warm_args<ShrinkArgs>();
-    const int u = xcd_unit(a.nproj);
+    const int u = xcd_unit(MP ? 1 : a.nproj);
     if (u >= a.units) return;            // whole workgroup: no barrier is skipped
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
@@ -159,13 +166,20 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     // unit -> (rank tile, chunk, projection): the descriptor and the token
     // rows of the tile load in parallel
     const int per = a.nproj * a.c0;
-    const int key = u / per;
+    const int key = MP ? u / a.c0 : u / per;
     int trow[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) trow[tt] = a.tile_tok[key * kMaxBlockTokens + tt * kTile + n];
     const TileDesc td = a.tiles[key];
-    const int rem = u - key * per;
-    const int c = rem / a.nproj, p = rem - (rem / a.nproj) * a.nproj;
+    int c, p0;
+    if constexpr (MP) {
+        c = u - key * a.c0;
+        p0 = 0;
+    } else {
+        const int rem = u - key * per;
+        c = rem / a.nproj;
+        p0 = rem - (rem / a.nproj) * a.nproj;
+    }
 
     // this wave's quarter of the chunk: at most F fragments
     const int kw = a.kc / kWaves;
@@ -175,20 +189,24 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     // A first: it depends on nothing but the descriptor.  A is K-blocked
     // [h_in_pad / SPAN][r_pad][SPAN], so the 16 rows x SPAN columns of one
     // fragment are one contiguous 1 KB (bf16) read.
-    const rsrc_t ar = make_rsrc(
-        a.slab + extent(td.ext_lo, td.ext_hi) +
-            uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
-        uint32_t(td.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
     const int j = td.tile * kTile + n;
     const bool jv = j < td.r_pad;
-    u32x4 af[F];
+    auto load_a = [&](int p, u32x4 (&af)[F]) {
+        const rsrc_t ar = make_rsrc(
+            a.slab + extent(td.ext_lo, td.ext_hi) +
+                uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
+            uint32_t(td.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-        const int k = k_lo + f * SPAN + q * E;
-        const uint32_t kb = uint32_t(k_lo / SPAN + f);
-        af[f] = bload16_nt(ar, off_or_oob(jv && k < k_hi,
-                                          ((kb * td.r_pad + j) * SPAN + q * E) * sizeof(T)));
-    }
+        for (int f = 0; f < F; ++f) {
+            const int k = k_lo + f * SPAN + q * E;
+            const uint32_t kb = uint32_t(k_lo / SPAN + f);
+            af[f] = bload16_nt(ar, off_or_oob(jv && k < k_hi,
+                                              ((kb * td.r_pad + j) * SPAN + q * E) * sizeof(T)));
+        }
+    };
+    u32x4 af[NP][F];
+#pragma unroll
+    for (int pi = 0; pi < NP; ++pi) load_a(p0 + pi, af[pi]);
 
     // then the token rows
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
@@ -214,29 +232,36 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
         }
     }
 
-    f32x4 acc[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pi = 0; pi < NP; ++pi) {
+        f32x4 acc[TT];
 #pragma unroll
-    for (int f = 0; f < F; ++f) {
-        if (k_lo + f * SPAN >= k_hi) break;              // wave-uniform
+        for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-            if (tt < ntiles) acc[tt] = mma<T>(af[f], xf[tt][f], acc[tt]);
-    }
+        for (int f = 0; f < F; ++f) {
+            if (k_lo + f * SPAN >= k_hi) break;          // wave-uniform
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                if (tt < ntiles) acc[tt] = mma<T>(af[pi][f], xf[tt][f], acc[tt]);
+        }
 
-    // sum the 4 waves in a fixed order; lane holds ranks 4q..4q+3 of token n
+        // sum the 4 waves in a fixed order; lane holds ranks 4q..4q+3 of token n
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) red[w][tt][lane] = acc[tt];
-    __syncthreads();
-    float *pt = a.partial + size_t(u) * (TT * kTile * kTile);
-    for (int i = threadIdx.x; i < ntiles * kWaveSize; i += kWaves * kWaveSize) {
-        // token tiles past the block's last are never read: not stored
-        const int tt = i / kWaveSize, ln = i % kWaveSize;
-        const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
-        // partials are read once, by the next kernel
-        __builtin_nontemporal_store(
-            s4, reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4));
+        for (int tt = 0; tt < TT; ++tt) red[w][tt][lane] = acc[tt];
+        __syncthreads();
+        // the partial tile of (rank tile, chunk, projection), as per-projection
+        // units number them
+        const int uu = key * per + c * a.nproj + p0 + pi;
+        float *pt = a.partial + size_t(uu) * (TT * kTile * kTile);
+        for (int i = threadIdx.x; i < ntiles * kWaveSize; i += kWaves * kWaveSize) {
+            // token tiles past the block's last are never read: not stored
+            const int tt = i / kWaveSize, ln = i % kWaveSize;
+            const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
+            // partials are read once, by the next kernel
+            __builtin_nontemporal_store(
+                s4, reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4));
+        }
+        if (MP) __syncthreads();                     // red is written again
     }
 }
 
@@ -1049,12 +1074,17 @@ __global__ __launch_bounds__(256) void k_pack_a(const T *src, int rank, int h_in
 }
 
 template <typename T>
-hipError_t shrink_dispatch(int tt, const ShrinkArgs &a, hipStream_t s) {
+hipError_t shrink_dispatch(int tt, bool mp, const ShrinkArgs &a, hipStream_t s) {
     const dim3 grid(a.grid), block(kWaves * kWaveSize);
-    switch (tt) {
-    case 1: hipLaunchKernelGGL((k_shrink<T, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_shrink<T, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_shrink<T, 4>), grid, block, 0, s, a); break;
+    const int np = mp ? a.nproj : 1;
+    switch (tt * 4 + np) {
+    case 1 * 4 + 1: hipLaunchKernelGGL((k_shrink<T, 1, 1>), grid, block, 0, s, a); break;
+    case 2 * 4 + 1: hipLaunchKernelGGL((k_shrink<T, 2, 1>), grid, block, 0, s, a); break;
+    case 2 * 4 + 2: hipLaunchKernelGGL((k_shrink<T, 2, 2>), grid, block, 0, s, a); break;
+    case 2 * 4 + 3: hipLaunchKernelGGL((k_shrink<T, 2, 3>), grid, block, 0, s, a); break;
+    case 4 * 4 + 1: hipLaunchKernelGGL((k_shrink<T, 4, 1>), grid, block, 0, s, a); break;
+    case 4 * 4 + 2: hipLaunchKernelGGL((k_shrink<T, 4, 2>), grid, block, 0, s, a); break;
+    case 4 * 4 + 3: hipLaunchKernelGGL((k_shrink<T, 4, 3>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1074,10 +1104,10 @@ hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s) {
+hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
-    return dtype == LORA_BF16 ? shrink_dispatch<uint16_t>(tt, a, s)
-                              : shrink_dispatch<float>(tt, a, s);
+    return dtype == LORA_BF16 ? shrink_dispatch<uint16_t>(tt, mp, a, s)
+                              : shrink_dispatch<float>(tt, mp, a, s);
 }
 
 hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,

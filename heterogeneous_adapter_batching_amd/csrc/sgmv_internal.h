@@ -219,7 +219,9 @@ lora_status set_error(lora_status st, const char *msg);
 // Kernel launchers (kernels.hip).  dtype is a lora_dtype; tt is the number of
 // 16-token tiles of the largest block (1, 2 or 4); ks the K-steps of the
 // largest padded rank (bf16: 1 or 2, f32: 1, 2 or 4).
-hipError_t launch_shrink(int dtype, int tt, const ShrinkArgs &a, hipStream_t s);
+// mp: units of (rank tile, k-chunk) over every projection (tt 2 or 4, and
+// 2 or 3 projections, only)
+hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStream_t s);
 // A [rank][h_in] row-major (device) -> K-blocked [h_in_pad / span][r_pad][span]
 hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
                          int h_in_pad, hipStream_t s);
