@@ -643,38 +643,40 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
         // a wave-uniform guard rather than a loop exit, so the loop unrolls
         // fully and bv stays in registers
         if (v < nv) {
-            // this vector's v of every token from LDS (broadcast reads, one
-            // wait), not all of v held in registers
-            asm volatile("" ::: "memory");
-            float w[NT][E];
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int e = 0; e < E; e += 4) {
-                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + e]);
-                    w[t][e] = w4[0]; w[t][e + 1] = w4[1]; w[t][e + 2] = w4[2]; w[t][e + 3] = w4[3];
-                }
+            // this vector's v one token at a time from LDS (broadcast
+            // reads): E values live rather than every token's, which keeps
+            // the rank-16 build at 54 VGPRs (8 waves a SIMD; 68 and 7 with
+            // all tokens' values at once), 1.5% per full-stack step
+            float f[RPL][E];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                float f[E];
                 if constexpr (E == 8) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        f[2 * k] = bf16_lo(bv[v][i][k]);
-                        f[2 * k + 1] = bf16_hi(bv[v][i][k]);
+                        f[i][2 * k] = bf16_lo(bv[v][i][k]);
+                        f[i][2 * k + 1] = bf16_hi(bv[v][i][k]);
                     }
                 } else {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(bv[v][i][k]);
+                    for (int k = 0; k < 4; ++k) f[i][k] = __uint_as_float(bv[v][i][k]);
                 }
+            }
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    if (t < nt) {                    // wave-uniform
+            for (int t = 0; t < NT; ++t)
+                if (t < nt) {                        // wave-uniform
+                    asm volatile("" ::: "memory");
+                    float w[E];
+#pragma unroll
+                    for (int e = 0; e < E; e += 4) {
+                        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + e]);
+                        w[e] = w4[0]; w[e + 1] = w4[1]; w[e + 2] = w4[2]; w[e + 3] = w4[3];
+                    }
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i)
 #pragma unroll
                         for (int e = 0; e < E; ++e)
-                            d[i][t] = __builtin_fmaf(f[e], w[t][e], d[i][t]);
-                    }
-            }
+                            d[i][t] = __builtin_fmaf(f[i][e], w[e], d[i][t]);
+                }
         }
     }
     // the delta's scale per token: the adapter's, times the token's weight
