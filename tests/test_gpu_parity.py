@@ -204,6 +204,26 @@ def test_prefill_blocks(seed):
     check_workload(dw, tight=True, threads=4)
 
 
+@pytest.mark.parametrize("nproj,dtype", [(2, "bf16"), (3, "bf16"), (2, "f32"), (3, "f32")])
+def test_prefill_multi_projection(nproj, dtype):
+    """Calls of 2 and 3 projections over blocks of several token tiles: the
+    shrink runs one unit per (rank tile, k-chunk) over all of the call's
+    projections (x loaded once); ranks up to 64 (4 rank tiles), distinct
+    h_out per projection, ragged prompts beside decode steps."""
+    seed = {2: 91, 3: 92}[nproj] + (10 if dtype == "f32" else 0)
+    base = mixed_case(seed, dtype=dtype, has_base=nproj == 3, h_in=520, h_out=8)
+    g = np.random.default_rng(seed)
+    projs = tuple(Proj(f"p{i}", 520, int(g.integers(4, 40)) * 8, "x") for i in range(nproj))
+    w = dataclasses.replace(base, projs=projs, calls=(tuple(range(nproj)),))
+    log(f"[parity] prefill {nproj} projections {dtype} T={w.num_tokens} "
+        f"h_out={[p.h_out for p in projs]} ranks={sorted(set(w.ranks.tolist()))}")
+    dw = DeviceWorkload(w, threads=4)
+    assert dw.plan.stats()["max_block_tokens"] > 16
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("has_base", [True, False])
 def test_mixed_blocks(dtype, has_base):
@@ -227,7 +247,7 @@ def test_two_step_path():
     """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
     float32 bound of the oracle, deterministic, and bit-identical to
     sgmv_fused (every kernel sums the k-chunk partials in one order) on both
-    the decode path (one fused launch) and the prefill path."""
+    the decode path (shrink and decode expand) and the prefill path."""
     for w in (config(1), multi_proj_case(3, has_base=True), config(0),
               mixed_case(71, h_in=512, h_out=256, r_choices=[8, 24, 64])):
         log(f"[parity] two-step {w.name}")
