@@ -519,6 +519,10 @@ def main():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-layers", type=int, default=-1,
                     help="layers of the CPU-oracle sample (-1: all, 0: skip)")
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="MiB written between timed steps, outside the timed events, so that "
+                         "a step does not find the last step's data in the 256 MB Infinity "
+                         "Cache or the L2s; -1: 1024 when a step moves under 1 GiB, else 0")
     ap.add_argument("--kernel-reps", type=int, default=5,
                     help="event-timed passes for the per-kernel roofline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -601,29 +605,55 @@ def main():
         else:
             dw.run_fused()
 
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t_wall = time.perf_counter()
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {args.mode}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms)")
+    # A step that moves less than the caches hold would find the last step's
+    # data there: such steps are timed one by one, each after a flush write.
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (
+        1024 if alg["bytes"] < (1 << 30) else 0)
+    flush = (torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+             if flush_mib > 0 else None)
 
-    # the spread of single steps: each step between its own pair of events
-    with torch.cuda.stream(stream):
-        torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        evs[0].record(stream)
-        for i in range(args.steps):
-            step()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-    per_step = np.sort([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    def flush_caches(i):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+
+    if flush is None:
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t_wall = time.perf_counter()
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t_wall
+        ms = e0.elapsed_time(e1) / args.steps
+        log(f"[bench] {args.mode}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms)")
+
+        # the spread of single steps: each step between its own pair of events
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            evs[0].record(stream)
+            for i in range(args.steps):
+                step()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+        per_step = np.sort([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    else:
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.steps)]
+            for i, (ea, eb) in enumerate(pairs):
+                flush_caches(i)
+                ea.record(stream)
+                step()
+                eb.record(stream)
+            torch.cuda.synchronize()
+        per_step = np.sort([ea.elapsed_time(eb) for ea, eb in pairs])
+        ms = float(per_step.mean())
+        log(f"[bench] {args.mode}: {ms:.4f} ms/step, each step after a {flush_mib} MiB flush")
     quant = {q: round(float(np.quantile(per_step, v)), 5)
              for q, v in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
 
@@ -666,13 +696,24 @@ def main():
         for kind, expand in (("shrink", False), ("pair", True)):
             one_pass(expand)                                 # warm
             torch.cuda.synchronize()
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ea.record(stream)
-            for _ in range(args.kernel_reps):
-                one_pass(expand)
-            eb.record(stream)
-            torch.cuda.synchronize()
-            tot[kind] = ea.elapsed_time(eb)
+            if flush is None:
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ea.record(stream)
+                for _ in range(args.kernel_reps):
+                    one_pass(expand)
+                eb.record(stream)
+                torch.cuda.synchronize()
+                tot[kind] = ea.elapsed_time(eb)
+            else:                                            # each pass after a flush
+                pairs = [(torch.cuda.Event(enable_timing=True),
+                          torch.cuda.Event(enable_timing=True)) for _ in range(args.kernel_reps)]
+                for i, (ea, eb) in enumerate(pairs):
+                    flush_caches(i)
+                    ea.record(stream)
+                    one_pass(expand)
+                    eb.record(stream)
+                torch.cuda.synchronize()
+                tot[kind] = sum(ea.elapsed_time(eb) for ea, eb in pairs)
     tot["expand"] = tot["pair"] - tot["shrink"]
     tot.pop("pair")
     us = {kind: t * 1e3 / (args.kernel_reps * n_launch) for kind, t in tot.items()}
@@ -730,7 +771,8 @@ def main():
                    "tokens": w.num_tokens, "layers": w.num_layers,
                    "projections": [p.name for p in w.projs],
                    "calls_per_layer": len(dw.calls), "kernel_launches_per_step": launches,
-                   "distinct_adapters": int(len(w.touched())), "mode": args.mode},
+                   "distinct_adapters": int(len(w.touched())), "mode": args.mode,
+                   "flush_mib_between_steps": flush_mib},
         "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
         # the attainable roof for the path's arithmetic intensity I (FLOP/B):
