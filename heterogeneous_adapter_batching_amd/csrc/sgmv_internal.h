@@ -44,9 +44,9 @@ constexpr int kTargetGroups = 1024;          // MFMA expand: workgroups aimed fo
 constexpr int kExpandUnitTiles = 1;
 // Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
 // more, shorter ones here (the expand then also sums fewer partials):
-// measured on the full stack, 384 beat 1024 by 3.5% per step, and 256..512
-// were within 1% of each other.
-constexpr int kShrinkTargetGroups = 384;
+// measured on the full stack, 384 beat 1024 by 3.5% per step, and 256 beat
+// 384 by 0.5% (the o call's 6 k-chunks become 4; 128 measured the same).
+constexpr int kShrinkTargetGroups = 256;
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 // Activations and outputs are addressed through buffer resources whose
 // out-of-range offset is 2^31: each such tensor spans at most 2 GiB.
