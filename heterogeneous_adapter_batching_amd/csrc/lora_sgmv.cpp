@@ -939,6 +939,9 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.x_bytes = uint32_t(tensor_bytes(pl->T, ldx, cc.h_in, cc.es));
     const uint64_t need = 4ull * uint64_t(nproj) * pl->rt_total() * a.c0 * pl->tt * lora::kTile *
                           lora::kTile;
+    if (need > lora::kMaxTensorBytes)   // the expands address the partials within 2 GiB
+        return fail(LORA_EINVAL, "the call's shrink partials would span %llu bytes, more than "
+                    "2 GiB: split the batch", (unsigned long long)need);
     if (need > pl->part_bytes)
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
                     (unsigned long long)need, (unsigned long long)pl->part_bytes);

@@ -333,7 +333,11 @@ lora_status lora_plan_export(const lora_plan *pl, int32_t *token_order, int32_t 
  * column slice y[:, y_offsets[i] : y_offsets[i] + h_out] (the pseudocode's
  * y_offset and y_slice_size), and its v columns are
  * v[:, i * r_max : i * r_max + r_max].  With num_tokens = 0 the calls
- * validate the pool, plan and projection list and do nothing else. */
+ * validate the pool, plan and projection list and do nothing else.
+ * Every device tensor a call addresses (x, y, base, v) spans at most 2 GiB,
+ * and so do the shrink's partial sums of one call (rank tiles x k-chunks x
+ * projections x 1 KiB per 16-token tile): a larger call is refused with
+ * LORA_EINVAL before anything is enqueued (split the batch). */
 
 /* Shrink (the A step, scale 1.0): v[t][i*r_max + j] = sum_k A_i,p[j][k] x[t][k]
  * for every token with an adapter, j < r_max (columns j >= rank are zero).
