@@ -365,7 +365,8 @@ lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
                        const void *x, int64_t ldx, const void *base, int64_t ldb,
                        void *y, int64_t ldy, void *stream);
 
-/* sgmv_fused in two calls, each one kernel: the shrink (the A step, scale
+/* sgmv_fused in two calls, each one kernel (the expand two for a batch with
+ * both prompt and decode blocks): the shrink (the A step, scale
  * 1.0, "Compress then Serve" rebuttal pseudocode, step 1) leaves float32
  * partial sums of v in the plan's workspace; the expand (step 3) sums them
  * and writes y exactly as sgmv_fused does (the same bits).  The shrink needs
