@@ -247,9 +247,14 @@ def test_two_step_path():
     """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
     float32 bound of the oracle, deterministic, and bit-identical to
     sgmv_fused (every kernel sums the k-chunk partials in one order) on both
-    the decode path (shrink and decode expand) and the prefill path."""
+    the decode path (shrink and decode expand) and the prefill path, also
+    with the shrink's units over all three projections of a call."""
+    three = dataclasses.replace(
+        mixed_case(72, h_in=264, h_out=8, has_base=False),
+        projs=tuple(Proj(f"p{i}", 264, ho, "x") for i, ho in enumerate((96, 40, 136))),
+        calls=((0, 1, 2),))
     for w in (config(1), multi_proj_case(3, has_base=True), config(0),
-              mixed_case(71, h_in=512, h_out=256, r_choices=[8, 24, 64])):
+              mixed_case(71, h_in=512, h_out=256, r_choices=[8, 24, 64]), three):
         log(f"[parity] two-step {w.name}")
         dw = DeviceWorkload(w, threads=4)
         outs = []
