@@ -581,7 +581,7 @@ __device__ __forceinline__ void gather_finish(const ExpandArgs &a, const BlockDe
 // them with every token's v (an LDS broadcast) in float32.  Loads go out in
 // the order they are used: the v gather, B vector by vector, then y_in; so
 // the dot products of the first vectors start while the rest arrive.
-template <typename T, int NV, bool Sig>
+template <typename T, int NV, bool Sig, bool PRW>
 __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
                                             const int (&tr)[kValuTokens], int p, int o_lo,
                                             int o_hi, float (*vs)[LORA_MAX_RANK + 4],
@@ -609,6 +609,14 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
         y_row[t] = ok ? uint32_t((int64_t(tr[t]) * a.ldy + yoff) * sizeof(T)) : kOOB;
     }
 
+    // PR (builds for B rows of at most 2 vectors): a lane owns two adjacent
+    // rows, so y_in and y of a token move 4 bytes a lane (bf16) in one
+    // access instead of two of 2 bytes, and the kernel holds 48 VGPRs
+    // instead of 54: 1% per full-stack step.  Wider rows keep rows a wave
+    // apart (paired, their B loads would stride 128 bytes a lane; 1% slower
+    // on the multi-rank decode).
+    constexpr bool PR = PRW && RPL == 2;
+    auto row_of = [&](int i) { return PR ? o_lo + 2 * lane + i : o_lo + i * kWaveSize + lane; };
     VGather g;
     gather_issue(a, blk, tr, p, g);
     u32x4 bv[NV][RPL];
@@ -616,18 +624,36 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            const int row = o_lo + i * kWaveSize + lane;
+            const int row = row_of(i);
             bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
                                               uint32_t(row) * row_bytes + v * 16));
         }
     float yin[RPL][NT];
+    if constexpr (PR) {
+        const int row = row_of(0);
+        const bool rok = row < o_hi;                 // o_hi is even: the pair is in or out
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int row = o_lo + i * kWaveSize + lane;
-        const bool rok = row < o_hi;
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t off = rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB;
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(inr, int(off), 0, 0);
+                yin[0][t] = bf16_lo(w);
+                yin[1][t] = bf16_hi(w);
+            } else {
+                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(inr, int(off), 0, 0);
+                yin[0][t] = __uint_as_float(w[0]);
+                yin[1][t] = __uint_as_float(w[1]);
+            }
+        }
+    } else {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+        for (int i = 0; i < RPL; ++i) {
+            const int row = row_of(i);
+            const bool rok = row < o_hi;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+        }
     }
     gather_finish(a, blk, p, g, vs, ways);
     if constexpr (Sig)
@@ -685,14 +711,29 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         sc[t] = a.tok_w && t < nt ? blk.scale * a.tok_w[blk.tok_off + t] : blk.scale;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int row = o_lo + i * kWaveSize + lane;
+    if constexpr (PR) {
+        const int row = row_of(0);
         const bool rok = row < o_hi;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)                 // y_row[t] is kOOB for t >= nt
-            Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
-                           yin[i][t] + sc[t] * d[i][t]);
+        for (int t = 0; t < NT; ++t) {               // y_row[t] is kOOB for t >= nt
+            const uint32_t off = rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB;
+            const float o0 = yin[0][t] + sc[t] * d[0][t], o1 = yin[1][t] + sc[t] * d[1][t];
+            if constexpr (sizeof(T) == 2)
+                __builtin_amdgcn_raw_buffer_store_b32(bf16x2_rne(o0, o1), yr, int(off), 0, kOut);
+            else
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(o0), __float_as_uint(o1)},
+                                                      yr, int(off), 0, kOut);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = row_of(i);
+            const bool rok = row < o_hi;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)             // y_row[t] is kOOB for t >= nt
+                Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB,
+                               yin[i][t] + sc[t] * d[i][t]);
+        }
     }
 }
 
@@ -960,15 +1001,15 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
         return;
     }
     switch (decode_nvt(r_pad, sizeof(T))) {         // <= NVM for every class of the launch
-    case 1: return expand_valu<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 1: return expand_valu<T, 1, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
     default:
-        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 
