@@ -670,9 +670,9 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
         // fully and bv stays in registers
         if (v < nv) {
             // this vector's v one token at a time from LDS (broadcast
-            // reads): E values live rather than every token's, which keeps
-            // the rank-16 build at 54 VGPRs (8 waves a SIMD; 68 and 7 with
-            // all tokens' values at once), 1.5% per full-stack step
+            // reads): E values live rather than every token's, 14 VGPRs
+            // fewer (the rank-16 build at 8 waves a SIMD instead of 7),
+            // 1.5% per full-stack step
             float f[RPL][E];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {

@@ -39,7 +39,7 @@ constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
 constexpr int kTargetGroups = 1024;          // MFMA expand: workgroups aimed for per launch
 // MFMA expand: 16-token tiles of a block per unit (a 64-token block is
 // kMaxBlockTokens / (16 * kExpandUnitTiles) units over the same rows).  One
-// tile a unit keeps the kernel at 146 VGPRs (3 waves a SIMD) where 4 tiles
+// tile a unit keeps the kernel near 150 VGPRs (3 waves a SIMD) where 4 tiles
 // spilled into AGPRs at 1 wave: 4.5% faster per prefill step, 2 tiles 3.5%.
 constexpr int kExpandUnitTiles = 1;
 // Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
