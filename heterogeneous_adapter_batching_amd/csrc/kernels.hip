@@ -121,6 +121,27 @@ __device__ __forceinline__ int xcd_unit(int gs) {
     return (i / gs) * (kXcds * gs) + x * gs + (i % gs);
 }
 
+// Reads plan memory (descriptors, token rows) through the constant address
+// space, which promises that it stays unchanged for the whole dispatch: the
+// plan workspace is written only by host uploads between launches, and the
+// scalar cache is invalidated at each dispatch.  The dwords come in by
+// scalar loads into SGPRs, so the unit's buffer resources are built in
+// SGPRs (no loop around the buffer loads to make a VGPR descriptor
+// uniform), and their wait counts apart from the vector loads.  3% per
+// full-stack step against plain loads, which the compiler makes vector loads
+// once a kernel may write memory.
+template <typename D>
+__device__ __forceinline__ D load_invariant(const D *p) {
+    static_assert(sizeof(D) % 4 == 0, "whole dwords");
+    typedef const __attribute__((address_space(4))) uint32_t *cptr;
+    const cptr c = (cptr)p;
+    D d;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(&d);
+#pragma unroll
+    for (int i = 0; i < int(sizeof(D) / 4); ++i) dst[i] = c[i];
+    return d;
+}
+
 // Brings the whole kernel-argument block into the scalar cache in one
 // round: one dword of every 32 bytes, loaded together and waited for once.
 // The unit decode then reads its arguments in several dependent steps, each
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     int trow[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) trow[tt] = a.tile_tok[key * kMaxBlockTokens + tt * kTile + n];
-    const TileDesc td = a.tiles[key];
+    const TileDesc td = load_invariant(a.tiles + key);
     int c, p0;
     if constexpr (MP) {
         c = u - key * a.c0;
@@ -301,7 +322,7 @@ template <int TT>
 __global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
     const int bp = blockIdx.x;
     const int b = bp / a.nproj, p = bp % a.nproj;
-    const BlockDesc blk = a.blocks[b];
+    const BlockDesc blk = load_invariant(a.blocks + b);
     const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
     const int quads = a.r_max / 4;
     for (int i = threadIdx.x; i < blk.n_tok * quads; i += blockDim.x) {
@@ -972,8 +993,8 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     }
     const int slice = rem - first;
 
-    const BlockDesc blk = a.blocks[b];
-    const int4 bt4 = *reinterpret_cast<const int4 *>(a.block_tok + b * kMaxBlockTokens);
+    const BlockDesc blk = load_invariant(a.blocks + b);
+    const int4 bt4 = load_invariant(reinterpret_cast<const int4 *>(a.block_tok + b * kMaxBlockTokens));
     const int tr[kValuTokens] = {bt4.x, bt4.y, bt4.z, bt4.w};
     static_assert(kValuTokens == 4, "token rows load as one int4");
 
@@ -1041,7 +1062,7 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     const int oc = rem - a.oc_prefix[c.p];
     // the slice's tokens as a block of their own: its first token, its first
     // slot in the shrink block and its token count
-    BlockDesc blk = a.blocks[c.b];
+    BlockDesc blk = load_invariant(a.blocks + c.b);
     const int off = ts * TT * kTile;
     if (off >= blk.n_tok) return;                    // whole workgroup: an empty slice
     blk.tok_off += off;
