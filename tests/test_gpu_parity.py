@@ -496,6 +496,45 @@ def test_graph_replay_matches_eager():
             assert np.array_equal(from_device(v), eager[k]), (rep, k)
 
 
+@pytest.mark.parametrize("T", [40, 700])
+def test_plan_reupload_same_workspace(T):
+    """Plans uploaded in turn into one workspace: every launch sees the plan
+    uploaded before it.  The kernels read plan memory (descriptors, token
+    rows) by scalar loads, as memory that no launch changes while it runs;
+    a new upload between launches must still reach the next launch.  The
+    second plan gives each segment the adapter of the segment before it;
+    the third upload restores the first plan, whose output bits come back."""
+    import heterogeneous_adapter_batching_amd as hab
+    w1 = random_case(91, T=T, h_in=256, h_out=160, n_adapters=6, r_choices=[8, 16, 32])
+    ids = np.asarray(w1.seg_adapter)
+    w2 = dataclasses.replace(w1, seg_adapter=np.roll(ids, 1))
+    assert not np.array_equal(ids, np.asarray(w2.seg_adapter))
+    # the rotation can move an adapter off an empty segment: upload what either plan uses
+    both = sorted(set(w1.touched().tolist()) | set(w2.touched().tolist()))
+    dw = DeviceWorkload(w1, threads=2, upload=both)
+    mp = dw.max_proj
+    p1 = dw.plan
+    p2 = hab.Plan(dw.pool, w2.num_tokens, w2.seg_starts, w2.seg_adapter)
+    ws = torch.empty(max(p1.workspace_bytes(mp), p2.workspace_bytes(mp)), dtype=torch.uint8,
+                     device="cuda")
+    outs = []
+    for i, (plan, w) in enumerate(((p1, w1), (p2, w2), (p1, w1))):
+        plan.upload(mp, ws=ws)
+        dw.plan, dw.w = plan, w
+        dw.zero_outputs()
+        dw.run_fused()
+        torch.cuda.synchronize()
+        for k, v in dw.y.items():
+            bad = ~np.isfinite(from_device(v))
+            assert not bad.any(), (f"upload {i}: {int(bad.sum())} non-finite outputs in {k}, "
+                                   f"token rows {sorted(set(np.nonzero(bad)[0].tolist()))[:12]}")
+        check_workload(dw, threads=2)
+        outs.append({k: from_device(v) for k, v in dw.y.items()})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[2][k]), k
+        assert not np.array_equal(outs[0][k], outs[1][k]), k
+
+
 def test_register_from_device_matches_host():
     """lora_pool_register from device tensors (the K-blocking pack kernel) gives
     the same pool, hence the same output bits, as uploads from host arrays."""
