@@ -543,9 +543,9 @@ def main():
                     help="requests replaced per step in the replay")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the delta shards over GPUs by request without any exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the delta "
+              "shards over GPUs by request with no exchange between them, so one GPU's "
+              "throughput is the figure)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         return sweep(args)
