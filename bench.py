@@ -74,16 +74,16 @@ def kernel_bytes(w, call, kind):
     """Algorithmic bytes of one shrink or expand launch for one call."""
     es = 2 if w.dtype == "bf16" else 4
     touched = w.touched()
-    tok = w.token_adapter()
-    act = int((tok >= 0).sum())
+    act = int((w.token_adapter() >= 0).sum())
     r_sum = sum(int(w.ranks[a]) for a in touched)
-    v_bytes = 4 * sum(int(w.ranks[tok[t]]) for t in range(w.num_tokens) if tok[t] >= 0) * len(call)
+    # the float32 intermediate is not counted: it passes between the two
+    # kernels as partial sums, which are not algorithmic bytes
     if kind == "shrink":
         h_in = w.projs[call[0]].h_in
-        return r_sum * h_in * es * len(call) + act * h_in * es + v_bytes
+        return r_sum * h_in * es * len(call) + act * h_in * es
     h_out = sum(w.projs[p].h_out for p in call)
     cores = _distinct_cores(w) * len(call) * _core_elems(w) * 4 if w.sigma_kind else 0
-    return r_sum * h_out * es + v_bytes + 2 * w.num_tokens * h_out * es + cores
+    return r_sum * h_out * es + 2 * w.num_tokens * h_out * es + cores
 
 
 def traffic_from_profile(kernel, workload):
@@ -508,6 +508,142 @@ def exchange(args):
     print(json.dumps(line), flush=True)
 
 
+def step_metrics(w, ms):
+    """tokens/s, GB/s and TFLOP/s of one step of `ms` milliseconds, each with
+    its roofline fraction (HBM for bytes; for FLOPs both the MFMA peak and the
+    attainable roof min(MFMA peak, intensity x HBM peak))."""
+    alg = algorithmic(w)
+    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
+    attain = min(BF16_PEAK_TFLOPS, alg["flops"] / alg["bytes"] * HBM_PEAK_GBS / 1e3)
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "tflops": round(tflops, 3), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+            "attainable_tflops": round(attain, 2), "attainable_frac": round(tflops / attain, 4),
+            "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"]}
+
+
+def timed_steps(step, stream, steps, flush):
+    """Mean ms per step and the sorted single-step times.  Without a flush
+    buffer the steps run back to back between two events (and again, each
+    between its own events, for the spread); with one, each step runs alone
+    between its own events after a write over the whole flush buffer."""
+    import torch
+    if flush is None:
+        with torch.cuda.stream(stream):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            evs[0].record(stream)
+            for i in range(steps):
+                step()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+        return ms, np.sort([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+        for i, (ea, eb) in enumerate(pairs):
+            flush.fill_(i & 0xFF)
+            ea.record(stream)
+            step()
+            eb.record(stream)
+        torch.cuda.synchronize()
+    per_step = np.sort([ea.elapsed_time(eb) for ea, eb in pairs])
+    return float(per_step.mean()), per_step
+
+
+def capture(fn, stream, warmup):
+    """fn captured in a HIP graph after warm-up runs; returns the graph."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup)):
+            fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    return graph
+
+
+def other_config(ci, args, stream, flush):
+    """The step of a smaller workload (a parity configuration), timed in a
+    graph, each step after a cache flush (its data would otherwise sit in
+    the 256 MB cache from the step before)."""
+    import torch
+    from synth import config, default_threads
+    from synth.device import DeviceWorkload
+    w = config(ci)
+    t0 = time.perf_counter()
+    dw = DeviceWorkload(w, threads=default_threads())
+    graph = capture(dw.run_fused, stream, args.warmup)
+    ms, per_step = timed_steps(graph.replay, stream, args.steps, flush)
+    out = {"workload": w.name, "description": w.description, "tokens": w.num_tokens,
+           "distinct_adapters": int(len(w.touched())), "plan": dw.plan.stats(),
+           "flush_mib_between_steps": (flush.numel() >> 20) if flush is not None else 0,
+           "step_ms_p10_p50_p90": [round(float(np.quantile(per_step, q)), 5)
+                                   for q in (0.1, 0.5, 0.9)], **step_metrics(w, ms)}
+    log(f"[bench] {w.name}: {ms:.4f} ms/step ({time.perf_counter() - t0:.1f} s with staging), "
+        f"{out['hbm_frac']:.3f} of HBM peak, {out['attainable_frac']:.3f} of the attainable roof")
+    del graph, dw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(nbytes, launches, stream):
+    """GB/s of a plain device copy moving `nbytes` per launch (half read,
+    half written), `launches` copies back to back in a graph: the ceiling
+    of a kernel of that size in the step's launch pattern."""
+    import torch
+    n = max(1, int(nbytes) // 4)                 # bf16 elements read per copy
+    src = torch.ones(n * launches, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+
+    def fn():
+        for i in range(launches):
+            dst[i * n:(i + 1) * n].copy_(src[i * n:(i + 1) * n])
+    ms = _time_graph(fn, stream, 3, 10)
+    del src, dst
+    return 4 * n / (ms * 1e-3 / launches) / 1e9, ms * 1e3 / launches
+
+
+def plan_cost(dw, stream, reps=200):
+    """Host cost of planning a new batch: lora_plan_rebuild then
+    lora_plan_upload into one workspace sized for any batch of the step's
+    size, alternating two batches over the same adapters.  Returns the plan
+    (uploaded), its workspace and microseconds per rebuild + upload."""
+    import torch
+    w = dw.w
+    mp = dw.max_proj
+    ws = torch.empty(dw.pool.workspace_bytes(w.num_tokens, w.num_segs, mp), dtype=torch.uint8,
+                     device="cuda")
+    ids = [np.asarray(w.seg_adapter, np.int32),
+           np.random.default_rng(7).permutation(np.asarray(w.seg_adapter, np.int32))]
+    plan = dw.plan
+    for _ in range(5):
+        plan.rebuild(w.num_tokens, w.seg_starts, ids[0]).upload(mp, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        plan.rebuild(w.num_tokens, w.seg_starts, ids[i % 2]).upload(mp, ws=ws, stream=stream)
+    us = (time.perf_counter() - t0) * 1e6 / reps
+    torch.cuda.synchronize()
+    return plan, ws, ids, us
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,6 +665,8 @@ def main():
                     help="minimum oracle time of the CPU baseline")
     ap.add_argument("--copy-mib", type=int, default=2048,
                     help="size of the device-copy bandwidth reference (0: skip)")
+    ap.add_argument("--configs", type=int, nargs="*", default=[1, 2, 3],
+                    help="smaller workloads also timed (flushed) and reported under 'configs'")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: delta time vs distinct adapters and Zipf skew")
     ap.add_argument("--sweep-out", default=None, help="text summary of the sweep")
@@ -582,28 +720,8 @@ def main():
     launches = 2 * len(dw.layers) * len(dw.calls)
 
     stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, args.warmup)):
-            dw.run_fused()
-    torch.cuda.synchronize()
-
-    graph = None
-    if args.mode == "graph":
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            dw.run_fused()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for _ in range(args.warmup):
-                graph.replay()
-        torch.cuda.synchronize()
-
-    def step():
-        if graph is not None:
-            graph.replay()
-        else:
-            dw.run_fused()
+    graph = capture(dw.run_fused, stream, args.warmup) if args.mode == "graph" else None
+    step = graph.replay if graph is not None else dw.run_fused
 
     # A step that moves less than the caches hold would find the last step's
     # data there: such steps are timed one by one, each after a flush write.
@@ -611,49 +729,9 @@ def main():
         1024 if alg["bytes"] < (1 << 30) else 0)
     flush = (torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
              if flush_mib > 0 else None)
-
-    def flush_caches(i):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
-
-    if flush is None:
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t_wall = time.perf_counter()
-            e0.record(stream)
-            for _ in range(args.steps):
-                step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t_wall
-        ms = e0.elapsed_time(e1) / args.steps
-        log(f"[bench] {args.mode}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms)")
-
-        # the spread of single steps: each step between its own pair of events
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-            evs[0].record(stream)
-            for i in range(args.steps):
-                step()
-                evs[i + 1].record(stream)
-            torch.cuda.synchronize()
-        per_step = np.sort([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-    else:
-        with torch.cuda.stream(stream):
-            torch.cuda.synchronize()
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.steps)]
-            for i, (ea, eb) in enumerate(pairs):
-                flush_caches(i)
-                ea.record(stream)
-                step()
-                eb.record(stream)
-            torch.cuda.synchronize()
-        per_step = np.sort([ea.elapsed_time(eb) for ea, eb in pairs])
-        ms = float(per_step.mean())
-        log(f"[bench] {args.mode}: {ms:.4f} ms/step, each step after a {flush_mib} MiB flush")
+    ms, per_step = timed_steps(step, stream, args.steps, flush)
+    log(f"[bench] {args.mode}: {ms:.4f} ms/step" +
+        (f", each step after a {flush_mib} MiB flush" if flush is not None else ""))
     quant = {q: round(float(np.quantile(per_step, v)), 5)
              for q, v in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
 
@@ -663,10 +741,36 @@ def main():
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record(stream)
         for _ in range(max(3, args.steps // 5)):
-            dw.run_fused()
+            dw.run_fused(stream=stream)
         e3.record(stream)
         torch.cuda.synchronize()
     eager_ms = e2.elapsed_time(e3) / max(3, args.steps // 5)
+
+    # Per-batch planning on the measured path: a serving loop plans every
+    # step (the batch changes).  The host cost of rebuild + upload, and an
+    # eager step that plans its batch first, alternating two batches.
+    graph_plan = dw.plan
+    plan, plan_ws, plan_ids, plan_us = plan_cost(dw, stream)
+    log(f"[bench] plan rebuild + upload: {plan_us:.1f} us on the host")
+    n_rb = max(3, args.steps // 5)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e4, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_rb = time.perf_counter()
+        e4.record(stream)
+        for i in range(n_rb):
+            plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
+                dw.max_proj, ws=plan_ws, stream=stream)
+            dw.run_fused(stream=stream)
+        e5.record(stream)
+        torch.cuda.synchronize()
+        t_rb = (time.perf_counter() - t_rb) * 1e3 / n_rb
+    rebuild_ms = e4.elapsed_time(e5) / n_rb
+    log(f"[bench] eager step planning its batch first: {rebuild_ms:.4f} ms "
+        f"(host {t_rb:.4f} ms per step)")
+    plan.rebuild(w.num_tokens, w.seg_starts, w.seg_adapter).upload(dw.max_proj, ws=plan_ws,
+                                                                   stream=stream)
+    torch.cuda.synchronize()
 
     # Per-kernel durations of the step's two kernels, launched back to back
     # (a full queue, as in the step): passes over every (layer, call) of the
@@ -708,7 +812,7 @@ def main():
                 pairs = [(torch.cuda.Event(enable_timing=True),
                           torch.cuda.Event(enable_timing=True)) for _ in range(args.kernel_reps)]
                 for i, (ea, eb) in enumerate(pairs):
-                    flush_caches(i)
+                    flush.fill_(i & 0xFF)
                     ea.record(stream)
                     one_pass(expand)
                     eb.record(stream)
@@ -735,6 +839,16 @@ def main():
             "alg_bytes_per_launch": int(kern[dom]["alg_bytes_per_launch"])}
     log(f"[bench] kernels: {json.dumps(kern)}")
 
+    # the ceiling of a kernel of this size in this launch pattern: a plain
+    # copy moving the same bytes per launch, as many launches back to back
+    if flush is None and args.copy_mib > 0:
+        cgbs, cus = copy_ceiling(kern[dom]["alg_bytes_per_launch"], n_launch, stream)
+        roof["copy_same_bytes_gbs"] = round(cgbs, 1)
+        roof["copy_same_bytes_us"] = round(cus, 3)
+        roof["frac_of_copy_same_bytes"] = round(kern[dom]["gbs"] / cgbs, 4)
+        log(f"[bench] copy of {kern[dom]['alg_bytes_per_launch'] / 1e6:.1f} MB per launch, "
+            f"{n_launch} back to back: {cus:.2f} us, {cgbs:.0f} GB/s")
+
     # device copy bandwidth: a second, measured denominator
     copy_gbs = None
     if args.copy_mib > 0:
@@ -758,35 +872,42 @@ def main():
     if args.cpu_layers != 0 and keep:
         cpu = cpu_baseline(w, keep, cpu_layers, threads, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
+    keep.clear()
 
-    tok_s = w.num_tokens / (ms * 1e-3)
-    gbs = alg["bytes"] / (ms * 1e-3) / 1e9
-    tflops = alg["flops"] / (ms * 1e-3) / 1e12
+    # the smaller workloads, each step after a 1 GiB flush
+    del graph
+    configs = {}
+    if args.workload == 4 and args.configs:
+        del dw, plan, plan_ws, graph_plan
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        cflush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for ci in args.configs:
+            configs[f"config{ci}"] = other_config(ci, args, stream, cflush)
+        del cflush
+
+    m = step_metrics(w, ms)
     out = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": m["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
         if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "description": w.description,
                    "tokens": w.num_tokens, "layers": w.num_layers,
                    "projections": [p.name for p in w.projs],
-                   "calls_per_layer": len(dw.calls), "kernel_launches_per_step": launches,
+                   "calls_per_layer": len(w.calls), "kernel_launches_per_step": launches,
                    "distinct_adapters": int(len(w.touched())), "mode": args.mode,
                    "flush_mib_between_steps": flush_mib},
-        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "tflops": round(tflops, 3), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
-        # the attainable roof for the path's arithmetic intensity I (FLOP/B):
-        # min(MFMA peak, I x HBM peak); the step's TFLOP/s as a fraction of it
-        "attainable_tflops": round(min(BF16_PEAK_TFLOPS, alg["flops"] / alg["bytes"] *
-                                       HBM_PEAK_GBS / 1e3), 2),
-        "attainable_frac": round(tflops / min(BF16_PEAK_TFLOPS, alg["flops"] / alg["bytes"] *
-                                              HBM_PEAK_GBS / 1e3), 4),
+        **{k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")},
         "step_ms_quantiles": quant,
-        "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"],
         "eager_ms_per_step": round(eager_ms, 5),
+        # a serving loop plans each batch: host microseconds of rebuild +
+        # upload, and the eager step that does so first
+        "plan_us": round(plan_us, 2),
+        "eager_replan_ms_per_step": round(rebuild_ms, 5),
         "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},
         "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cpu_baseline": cpu, "configs": configs,
     }
     print(json.dumps(out), flush=True)
 

@@ -5,7 +5,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libhab_lora.so")
+# The in-tree build; HAB_LORA_LIB names another build of the same library to
+# load instead (e.g. the sanitizer build of the host code the tests run).
+LIB_PATH = os.environ.get("HAB_LORA_LIB") or os.path.join(PKG, "libhab_lora.so")
 
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_PROJ = 8
@@ -41,7 +43,7 @@ _pp = ctypes.POINTER(ctypes.c_void_p)
 # name: (restype, argtypes)
 SIGNATURES = {
     "lora_last_error": (ctypes.c_char_p, []),
-    "lora_adapter_bytes": (_u64, [ctypes.POINTER(PoolDesc), _i32]),
+    "lora_pool_bytes_for": (_u64, [ctypes.POINTER(PoolDesc), _i32]),
     "lora_pool_extent_bytes": (_u64, [ctypes.POINTER(PoolDesc), _i32]),
     "lora_pool_create": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(PoolDesc), _vp, _u64]),
     "lora_pool_destroy": (_i32, [_vp]),
@@ -55,6 +57,8 @@ SIGNATURES = {
     "lora_plan_create": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32]),
     "lora_plan_destroy": (_i32, [_vp]),
     "lora_plan_workspace_bytes": (_u64, [_vp, _i32]),
+    "lora_workspace_bytes": (_u64, [_vp, _i32, _i32, _i32]),
+    "lora_plan_rebuild": (_i32, [_vp, _i32, _i32p, _i32p, _i32p, ctypes.POINTER(_f32), _i32]),
     "lora_plan_upload": (_i32, [_vp, _vp, _u64, _i32, _vp]),
     "lora_plan_stats": (_i32, [_vp, _i32p, _i32p, _i32p, _i32p]),
     "lora_plan_export": (_i32, [_vp, _i32p, _i32p, _i32p, _i32p]),

@@ -51,9 +51,9 @@ def make_desc(num_layers: int, h_in: Sequence[int], h_out: Sequence[int], r_max:
     return d
 
 
-def adapter_bytes(desc: PoolDesc, rank: int) -> int:
+def pool_bytes_for(desc: PoolDesc, rank: int) -> int:
     """Bytes of one adapter at its true rank (no device needed)."""
-    return int(load().lora_adapter_bytes(ctypes.byref(desc), rank))
+    return int(load().lora_pool_bytes_for(ctypes.byref(desc), rank))
 
 
 def extent_bytes(desc: PoolDesc, rank: int) -> int:
@@ -145,8 +145,13 @@ class Pool:
     def extent_bytes(self, rank: int) -> int:
         return extent_bytes(self.desc, rank)
 
-    def adapter_bytes(self, rank: int) -> int:
-        return adapter_bytes(self.desc, rank)
+    def pool_bytes_for(self, rank: int) -> int:
+        return pool_bytes_for(self.desc, rank)
+
+    def workspace_bytes(self, num_tokens: int, num_segs: int, max_proj: int = 3) -> int:
+        """A workspace size that serves every plan of up to num_tokens tokens
+        and num_segs segments over this pool."""
+        return int(self.lib.lora_workspace_bytes(self._h, num_tokens, num_segs, max_proj))
 
     def reserve(self, adapter_id: int, rank: int, scale: float):
         check(self.lib.lora_pool_reserve(self._h, adapter_id, rank, ctypes.c_float(scale)))
@@ -323,6 +328,27 @@ class Plan:
                                                   sig.ctypes.data_as(i32p), int(segs.shape[0])))
         self.ws = None
         self.max_proj = 0
+
+    def rebuild(self, num_tokens: int, seg_starts, seg_adapter, seg_sigma=None, seg_weight=None):
+        """Re-plan for the next batch over the same pool, in place (host
+        tables and pinned staging reused); upload again before the next call."""
+        starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
+        segs = np.ascontiguousarray(seg_adapter, dtype=np.int32)
+        if starts.ndim != 1 or segs.ndim != 1 or starts.shape[0] != segs.shape[0] + 1:
+            raise ValueError("seg_starts must have one more entry than seg_adapter")
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        sig = None if seg_sigma is None else np.ascontiguousarray(seg_sigma, dtype=np.int32)
+        wts = None if seg_weight is None else np.ascontiguousarray(seg_weight, dtype=np.float32)
+        for a, name in ((sig, "seg_sigma"), (wts, "seg_weight")):
+            if a is not None and a.shape != segs.shape:
+                raise ValueError(f"{name} must have one entry per segment")
+        check(self.lib.lora_plan_rebuild(
+            self._h, int(num_tokens), starts.ctypes.data_as(i32p), segs.ctypes.data_as(i32p),
+            sig.ctypes.data_as(i32p) if sig is not None else None,
+            wts.ctypes.data_as(ctypes.POINTER(ctypes.c_float)) if wts is not None else None,
+            int(segs.shape[0])))
+        self.num_tokens = int(num_tokens)
+        return self
 
     def close(self):
         if getattr(self, "_h", None) and self._h.value:

@@ -41,5 +41,23 @@ def build(out: str = LIB, extra=()) -> str:
     return out
 
 
+# The host sources built with g++ alone (no device code: host_only.cpp
+# stands in for the kernel launchers) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, to run the host-side tests against.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+
+
+def host_sanitized(out: str) -> str:
+    srcs = [os.path.join(CSRC, "lora_sgmv.cpp"), os.path.join(CSRC, "exchange.cpp"),
+            os.path.join(CSRC, "host_only.cpp")]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", *SANITIZE,
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I", INCLUDE, "-I", CSRC, *srcs,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", out]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed ({res.returncode}):\n{res.stdout}")
+    return out
+
+
 if __name__ == "__main__":
     print(build())

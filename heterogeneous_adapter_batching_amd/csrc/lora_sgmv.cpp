@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -149,6 +150,73 @@ struct lora_pool {
     }
 };
 
+// Sizes a plan's device image is laid out from: tokens, expand blocks, rank
+// tiles, 16-token tiles of the largest block.
+struct PlanCounts {
+    int64_t T = 0, nb = 0, rt = 0;
+    int32_t tt = 1;
+};
+
+// Byte offsets of the tables in a plan workspace, and its size.
+struct PlanLayout {
+    uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
+             off_tw = 0, off_part = 0;
+    uint64_t image_bytes = 0, part_bytes = 0, ws_bytes = 0;
+};
+
+namespace {
+
+// Most partial tiles of a shrink of up to mp projections under
+// shrink_geometry: nproj * rt * c0, with c0 at most max(ceil(target /
+// per_chunk), ceil(steps / frags)), where steps = fragments of 4 waves over
+// h_in.  With `bound`, an upper bound over every rt' <= rt instead (rt' *
+// ceil(target / (c rt')) <= target + rt' for any c >= 1).
+uint64_t max_shrink_units(const lora_pool_desc &d, int64_t rt_in, int32_t tt, int32_t mp,
+                          bool bound) {
+    const uint64_t span = 4ull * (16 / esize(d.dtype));
+    int32_t h_in_max = 0;
+    for (int i = 0; i < d.num_proj; ++i) h_in_max = std::max(h_in_max, d.h_in[i]);
+    const uint64_t steps = (h_in_max + lora::kWaves * span - 1) / (lora::kWaves * span);
+    const uint64_t frags = tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
+    const uint64_t by_frags = (steps + frags - 1) / frags;
+    uint64_t most = 0;
+    const uint64_t rt = uint64_t(std::max<int64_t>(rt_in, 1));
+    for (int32_t np = 1; np <= mp; ++np) {
+        // partial tiles = np * rt * c0, c0 from the workgroups per chunk:
+        // np * rt, or rt for units over every projection (tt >= 2)
+        const uint64_t per_chunk = (tt >= 2 && np > 1 && np <= 3 ? 1 : uint64_t(np)) * rt;
+        const uint64_t by_target = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
+        const uint64_t units = bound ? std::max<uint64_t>(rt * by_frags,
+                                                          lora::kShrinkTargetGroups + rt)
+                                     : rt * std::max(by_target, by_frags);
+        most = std::max(most, uint64_t(np) * units);
+    }
+    return most;
+}
+
+PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp, bool bound) {
+    PlanLayout L;
+    const uint64_t T = uint64_t(std::max<int64_t>(c.T, 1));
+    const uint64_t nb = uint64_t(std::max<int64_t>(c.nb, 1));
+    const uint64_t rt = uint64_t(std::max<int64_t>(c.rt, 1));
+    uint64_t o = 0;
+    L.off_tok = o;     o = round_up(o + 4ull * T, 256);
+    L.off_blocks = o;  o = round_up(o + sizeof(BlockDesc) * nb, 256);
+    L.off_tiles = o;   o = round_up(o + sizeof(lora::TileDesc) * rt, 256);
+    L.off_btok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * nb, 256);
+    L.off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * rt, 256);
+    L.off_tsig = o;    o = round_up(o + 4ull * T, 256);
+    L.off_tw = o;      o = round_up(o + 4ull * T, 256);
+    L.image_bytes = o;
+    L.part_bytes = 4ull * max_shrink_units(d, c.rt, c.tt, mp, bound) * c.tt * lora::kTile *
+                   lora::kTile;
+    L.off_part = o;    o = round_up(o + L.part_bytes, 256);
+    L.ws_bytes = o;
+    return L;
+}
+
+}  // namespace
+
 struct lora_plan {
     const lora_pool *pool = nullptr;
     uint64_t pool_generation = 0;
@@ -171,12 +239,15 @@ struct lora_plan {
     void *ws = nullptr;
     uint64_t ws_bytes = 0;
     int32_t max_proj = 0;
-    uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
-             off_tw = 0, off_part = 0;
-    uint64_t image_bytes = 0, part_bytes = 0;
-    void *staging = nullptr;
-    uint64_t staging_bytes = 0;
-    hipEvent_t staged = nullptr;
+    PlanLayout lay;
+    // Pinned host staging of the image, two buffers used in turn: an upload
+    // waits (on the host) only for the copy out of the buffer it reuses, the
+    // one before last, which a batch later has long finished; a buffer grows
+    // (by half again) only when an image outgrows it.
+    void *staging[2] = {nullptr, nullptr};
+    uint64_t staging_bytes[2] = {0, 0};
+    hipEvent_t staged[2] = {nullptr, nullptr};
+    int32_t next_staging = 0;
     // the call whose shrink partials the workspace holds (sgmv_shrink_partials):
     // layer, projections and k-chunks; part_layer -1 = none
     mutable int32_t part_layer = -1, part_nproj = 0, part_c0 = 0;
@@ -184,44 +255,13 @@ struct lora_plan {
 
     int32_t rt_total() const { return int32_t(tiles.size()); }
     int32_t nb_all() const { return int32_t(blocks.size()); }
-
-    void layout(int32_t mp) {
-        uint64_t o = 0;
-        off_tok = o;     o = round_up(o + 4ull * std::max(T, 1), 256);
-        off_blocks = o;  o = round_up(o + sizeof(BlockDesc) * std::max(nb_all(), 1), 256);
-        off_tiles = o;   o = round_up(o + sizeof(lora::TileDesc) * std::max(rt_total(), 1), 256);
-        off_btok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(nb_all(), 1), 256);
-        off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * std::max(rt_total(), 1), 256);
-        off_tsig = o;    o = round_up(o + 4ull * std::max(T, 1), 256);
-        off_tw = o;      o = round_up(o + 4ull * std::max(T, 1), 256);
-        image_bytes = o;
-        part_bytes = 4ull * max_shrink_units(mp) * tt * lora::kTile * lora::kTile;
-        off_part = o;    o = round_up(o + part_bytes, 256);
-        ws_bytes = o;
-    }
-
-    // Most partial tiles of a shrink of up to mp projections under
-    // shrink_geometry: nproj * rt_total * c0, with c0 at most
-    // max(ceil(target / per_chunk), ceil(steps / frags)), where steps =
-    // fragments of 4 waves over h_in.
-    uint64_t max_shrink_units(int32_t mp) const {
-        const lora_pool_desc &d = pool->d;
-        const uint64_t span = 4ull * (16 / esize(d.dtype));
-        int32_t h_in_max = 0;
-        for (int i = 0; i < d.num_proj; ++i) h_in_max = std::max(h_in_max, d.h_in[i]);
-        const uint64_t steps = (h_in_max + lora::kWaves * span - 1) / (lora::kWaves * span);
-        const uint64_t frags = tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
-        const uint64_t by_frags = (steps + frags - 1) / frags;
-        uint64_t most = 0;
-        const uint64_t rt = std::max(rt_total(), 1);
-        for (int32_t np = 1; np <= mp; ++np) {
-            // partial tiles = np * rt * c0, c0 from the workgroups per chunk:
-            // np * rt, or rt for units over every projection (tt >= 2)
-            const uint64_t per_chunk = (tt >= 2 && np > 1 && np <= 3 ? 1 : uint64_t(np)) * rt;
-            const uint64_t by_target = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
-            most = std::max(most, uint64_t(np) * rt * std::max(by_target, by_frags));
-        }
-        return most;
+    PlanCounts counts() const {
+        PlanCounts c;
+        c.T = T;
+        c.nb = nb_all();
+        c.rt = rt_total();
+        c.tt = tt;
+        return c;
     }
 };
 
@@ -254,7 +294,7 @@ extern "C" {
 
 const char *lora_last_error(void) { return g_last_error.c_str(); }
 
-uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank) {
+uint64_t lora_pool_bytes_for(const lora_pool_desc *d, int32_t rank) {
     if (check_desc(d) != LORA_OK || rank < 1) return 0;
     return uint64_t(rank) * esize(d->dtype) * uint64_t(d->num_layers) * uint64_t(row_elems(d));
 }
@@ -507,10 +547,10 @@ lora_status lora_pool_stats(const lora_pool *p, int32_t *num, uint64_t *free_byt
 }  // extern "C"
 
 namespace {
-lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const int32_t *seg_starts,
-                        const int32_t *seg_adapter, const int32_t *seg_sigma,
-                        const float *seg_weight, int32_t S) {
-    if (!out) return fail(LORA_EINVAL, "null output pointer");
+// Checks a segment table (and its optional cores and weights) against a pool.
+lora_status check_segments(const lora_pool *p, int32_t T, const int32_t *seg_starts,
+                           const int32_t *seg_adapter, const int32_t *seg_sigma,
+                           const float *seg_weight, int32_t S) {
     if (!p) return fail(LORA_EINVAL, "null pool");
     if (T < 0 || S < 0) return fail(LORA_ESEG, "negative token or segment count");
     if (!seg_starts || (S > 0 && !seg_adapter)) return fail(LORA_EINVAL, "null segment table");
@@ -529,11 +569,28 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
         if (seg_weight && !std::isfinite(seg_weight[s]))
             return fail(LORA_EINVAL, "segment %d has a weight that is not finite", s);
     }
+    return LORA_OK;
+}
 
-    lora_plan *pl = new lora_plan();
+// Builds the plan of a checked segment table into `pl`, replacing what it
+// held (its device image and staging buffers are kept).
+void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg_starts,
+                const int32_t *seg_adapter, const int32_t *seg_sigma, const float *seg_weight,
+                int32_t S) {
     pl->pool = p;
     pl->pool_generation = p->generation;
     pl->T = T;
+    pl->token_order.clear();
+    pl->token_sigma.clear();
+    pl->token_weight.clear();
+    pl->weighted = false;
+    pl->max_sigma = -1;
+    pl->group_adapter.clear();
+    pl->group_rank.clear();
+    pl->blocks.clear();
+    pl->tiles.clear();
+    pl->nb_long = pl->nb_act = pl->n_active = pl->max_block = pl->max_rpad = 0;
+    pl->tt = 1;
     pl->token_group.assign(T, -1);
 
     // groups in first-appearance order (segments with tokens only)
@@ -663,8 +720,30 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
         pl->token_weight.resize(T);
         for (int32_t i = 0; i < T; ++i) pl->token_weight[i] = row_weight[pl->token_order[i]];
     }
+}
+
+lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const int32_t *seg_starts,
+                        const int32_t *seg_adapter, const int32_t *seg_sigma,
+                        const float *seg_weight, int32_t S) {
+    if (!out) return fail(LORA_EINVAL, "null output pointer");
+    lora_status st = check_segments(p, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
+    if (st != LORA_OK) return st;
+    lora_plan *pl = new lora_plan();
+    plan_build(pl, p, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
     *out = pl;
     return LORA_OK;
+}
+
+// Which plan's tables each workspace holds: the last plan uploaded into it.
+// A call with a plan whose workspace has since received another plan's
+// tables is refused (it would read the other plan's descriptors).
+std::mutex g_ws_mutex;
+std::unordered_map<const void *, const lora_plan *> g_ws_owner;
+
+bool owns_workspace(const lora_plan *pl) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws_owner.find(pl->ws);
+    return it != g_ws_owner.end() && it->second == pl;
 }
 }  // namespace
 
@@ -689,28 +768,59 @@ lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t 
     return plan_create(out, p, T, seg_starts, seg_adapter, seg_sigma, nullptr, S);
 }
 
+lora_status lora_plan_rebuild(lora_plan *pl, int32_t T, const int32_t *seg_starts,
+                              const int32_t *seg_adapter, const int32_t *seg_sigma,
+                              const float *seg_weight, int32_t S) {
+    if (!pl) return fail(LORA_EINVAL, "null plan");
+    lora_status st = check_segments(pl->pool, T, seg_starts, seg_adapter, seg_sigma, seg_weight,
+                                     S);
+    if (st != LORA_OK) return st;
+    plan_build(pl, pl->pool, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
+    pl->ws = nullptr;                  // the new tables are not on the device yet
+    pl->part_layer = -1;
+    return LORA_OK;
+}
+
 lora_status lora_plan_destroy(lora_plan *pl) {
     if (!pl) return fail(LORA_EINVAL, "null plan");
-    if (pl->staged) {
-        (void)hipEventSynchronize(pl->staged);
-        (void)hipEventDestroy(pl->staged);
+    for (int i = 0; i < 2; ++i) {
+        if (pl->staged[i]) {
+            (void)hipEventSynchronize(pl->staged[i]);
+            (void)hipEventDestroy(pl->staged[i]);
+        }
+        if (pl->staging[i]) (void)hipHostFree(pl->staging[i]);
     }
-    if (pl->staging) (void)hipHostFree(pl->staging);
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        for (auto it = g_ws_owner.begin(); it != g_ws_owner.end();)
+            it = it->second == pl ? g_ws_owner.erase(it) : std::next(it);
+    }
     delete pl;
     return LORA_OK;
 }
 
 uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj) {
     if (!pl || max_proj < 1 || max_proj > LORA_MAX_PROJ) return 0;
-    lora_plan tmp;   // compute the layout without touching the plan
-    tmp.pool = pl->pool;
-    tmp.T = pl->T;
-    tmp.blocks = pl->blocks;
-    tmp.tiles = pl->tiles;
-    tmp.nb_act = pl->nb_act;
-    tmp.tt = pl->tt;
-    tmp.layout(max_proj);
-    return tmp.ws_bytes;
+    return plan_layout(pl->pool->d, pl->counts(), max_proj, false).ws_bytes;
+}
+
+uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t num_segs,
+                              int32_t max_proj) {
+    if (!p || num_tokens < 0 || num_segs < 0 || max_proj < 1 || max_proj > LORA_MAX_PROJ)
+        return 0;
+    // Every expand block holds a token, so blocks <= T; a group of n tokens
+    // has at most n / 16 + 1 shrink blocks, and groups <= min(S, T), so
+    // shrink blocks <= T / 16 + min(S, T) (and <= T); each has at most
+    // r_max / 16 rank tiles.  Blocks beyond 16 tokens exist only when long
+    // groups hold kMinLongTokens tokens between them.
+    const int64_t T = num_tokens;
+    PlanCounts c;
+    c.T = T;
+    c.nb = T;
+    const int64_t sblocks = std::min<int64_t>(T, T / lora::kTile + 1 + std::min<int64_t>(num_segs, T));
+    c.rt = sblocks * ((p->d.r_max + lora::kTile - 1) / lora::kTile);
+    c.tt = T >= lora::kMinLongTokens ? lora::kMaxBlockTokens / lora::kTile : 1;
+    return plan_layout(p->d, c, max_proj, true).ws_bytes;
 }
 
 lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
@@ -720,66 +830,70 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
         return fail(LORA_EINVAL, "max_proj %d not in 1..%d", max_proj, LORA_MAX_PROJ);
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255))
         return fail(LORA_EINVAL, "workspace must be a non-null, 256-byte aligned device pointer");
-    const uint64_t need = lora_plan_workspace_bytes(pl, max_proj);
-    if (ws_bytes < need)
+    const PlanLayout lay = plan_layout(pl->pool->d, pl->counts(), max_proj, false);
+    if (ws_bytes < lay.ws_bytes)
         return fail(LORA_ESTATE, "workspace of %llu bytes < %llu needed",
-                    (unsigned long long)ws_bytes, (unsigned long long)need);
+                    (unsigned long long)ws_bytes, (unsigned long long)lay.ws_bytes);
+    // the staging buffer used two uploads ago: its copy may still be in flight
+    const int32_t k = pl->next_staging;
     hipError_t e;
-    if (pl->staged) {   // the previous image may still be in flight
-        e = hipEventSynchronize(pl->staged);
+    if (pl->staged[k]) {
+        e = hipEventSynchronize(pl->staged[k]);
         if (e != hipSuccess) return hip_fail(e, "plan staging wait");
-    }
-    lora_plan probe = lora_plan();   // layout of the new image
-    probe.pool = pl->pool; probe.T = pl->T; probe.blocks = pl->blocks;
-    probe.tiles = pl->tiles; probe.nb_act = pl->nb_act; probe.tt = pl->tt;
-    probe.layout(max_proj);
-    if (pl->staging_bytes < probe.image_bytes) {
-        void *buf = nullptr;
-        e = hipHostMalloc(&buf, probe.image_bytes, hipHostMallocDefault);
-        if (e != hipSuccess) return hip_fail(e, "plan staging buffer");
-        if (pl->staging) (void)hipHostFree(pl->staging);
-        pl->staging = buf;
-        pl->staging_bytes = probe.image_bytes;
-    }
-    if (!pl->staged) {
-        e = hipEventCreateWithFlags(&pl->staged, hipEventDisableTiming);
+    } else {
+        e = hipEventCreateWithFlags(&pl->staged[k], hipEventDisableTiming);
         if (e != hipSuccess) return hip_fail(e, "plan staging event");
     }
-    pl->layout(max_proj);
-    pl->max_proj = max_proj;
-    uint8_t *img = static_cast<uint8_t *>(pl->staging);
-    std::memset(img, 0, pl->image_bytes);
-    if (pl->T) std::memcpy(img + pl->off_tok, pl->token_order.data(), 4ull * pl->T);
-    if (pl->T) std::memcpy(img + pl->off_tsig, pl->token_sigma.data(), 4ull * pl->T);
+    if (pl->staging_bytes[k] < lay.image_bytes) {
+        const uint64_t want = std::max(lay.image_bytes, pl->staging_bytes[k] * 3 / 2);
+        void *buf = nullptr;
+        e = hipHostMalloc(&buf, want, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "plan staging buffer");
+        if (pl->staging[k]) (void)hipHostFree(pl->staging[k]);
+        pl->staging[k] = buf;
+        pl->staging_bytes[k] = want;
+    }
+    uint8_t *img = static_cast<uint8_t *>(pl->staging[k]);
+    std::memset(img, 0, lay.image_bytes);
+    if (pl->T) std::memcpy(img + lay.off_tok, pl->token_order.data(), 4ull * pl->T);
+    if (pl->T) std::memcpy(img + lay.off_tsig, pl->token_sigma.data(), 4ull * pl->T);
     if (pl->T && pl->weighted)
-        std::memcpy(img + pl->off_tw, pl->token_weight.data(), 4ull * pl->T);
+        std::memcpy(img + lay.off_tw, pl->token_weight.data(), 4ull * pl->T);
     if (!pl->blocks.empty())
-        std::memcpy(img + pl->off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
+        std::memcpy(img + lay.off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
     if (!pl->tiles.empty())
-        std::memcpy(img + pl->off_tiles, pl->tiles.data(), sizeof(lora::TileDesc) * pl->tiles.size());
+        std::memcpy(img + lay.off_tiles, pl->tiles.data(), sizeof(lora::TileDesc) * pl->tiles.size());
     {   // token rows of each block and of each rank tile, -1 padded
-        int32_t *bt = reinterpret_cast<int32_t *>(img + pl->off_btok);
+        int32_t *bt = reinterpret_cast<int32_t *>(img + lay.off_btok);
         for (int32_t b = 0; b < pl->nb_all(); ++b) {
             const BlockDesc &bd = pl->blocks[b];
             for (int32_t i = 0; i < lora::kMaxBlockTokens; ++i)
                 bt[b * lora::kMaxBlockTokens + i] =
                     i < bd.n_tok ? pl->token_order[bd.tok_off + i] : -1;
         }
-        int32_t *tt = reinterpret_cast<int32_t *>(img + pl->off_ttok);
-        for (int32_t k = 0; k < pl->rt_total(); ++k) {
-            const lora::TileDesc &td = pl->tiles[k];
+        int32_t *tt = reinterpret_cast<int32_t *>(img + lay.off_ttok);
+        for (int32_t t = 0; t < pl->rt_total(); ++t) {
+            const lora::TileDesc &td = pl->tiles[t];
             for (int32_t i = 0; i < lora::kMaxBlockTokens; ++i)
-                tt[k * lora::kMaxBlockTokens + i] =
+                tt[t * lora::kMaxBlockTokens + i] =
                     i < td.n_tok ? pl->token_order[td.tok_off + i] : -1;
         }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    e = hipMemcpyAsync(ws, img, pl->image_bytes, hipMemcpyHostToDevice, st);
+    e = hipMemcpyAsync(ws, img, lay.image_bytes, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "plan upload");
-    e = hipEventRecord(pl->staged, st);
+    e = hipEventRecord(pl->staged[k], st);
     if (e != hipSuccess) return hip_fail(e, "plan staging event record");
+    pl->next_staging = 1 - k;
     pl->ws = ws;
+    pl->ws_bytes = ws_bytes;
+    pl->max_proj = max_proj;
+    pl->lay = lay;
     pl->part_layer = -1;               // a new workspace holds no partials
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mutex);
+        g_ws_owner[ws] = pl;
+    }
     return LORA_OK;
 }
 
@@ -830,6 +944,9 @@ lora_status check_call(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     if (pl->pool_generation != p->generation)
         return fail(LORA_ESTATE, "an adapter was unregistered after the plan was built");
     if (!pl->ws) return fail(LORA_ESTATE, "plan has not been uploaded");
+    if (!owns_workspace(pl))
+        return fail(LORA_ESTATE, "the plan's workspace holds another plan's tables since "
+                                 "(upload this plan again)");
     if (layer < 0 || layer >= p->d.num_layers)
         return fail(LORA_EINVAL, "layer %d not in 0..%d", layer, p->d.num_layers - 1);
     if (nproj < 1 || nproj > pl->max_proj)
@@ -923,9 +1040,9 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     lora::ShrinkArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
-    a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->off_ttok);
-    a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->off_tiles);
-    a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->off_part);
+    a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_ttok);
+    a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->lay.off_tiles);
+    a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->lay.off_part);
     a.x = x;
     a.ldx = ldx;
     for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
@@ -942,9 +1059,9 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     if (need > lora::kMaxTensorBytes)   // the expands address the partials within 2 GiB
         return fail(LORA_EINVAL, "the call's shrink partials would span %llu bytes, more than "
                     "2 GiB: split the batch", (unsigned long long)need);
-    if (need > pl->part_bytes)
+    if (need > pl->lay.part_bytes)
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
-                    (unsigned long long)need, (unsigned long long)pl->part_bytes);
+                    (unsigned long long)need, (unsigned long long)pl->lay.part_bytes);
     hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, mp, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
     *c0_out = a.c0;
@@ -957,10 +1074,10 @@ lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, i
     if (pl->nb_act == 0) return LORA_OK;
     lora::ReduceArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
-    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
-    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
-    a.partial = reinterpret_cast<const float *>(ws + pl->off_part);
-    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->part_bytes, lora::kMaxTensorBytes));
+    a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks);
+    a.partial = reinterpret_cast<const float *>(ws + pl->lay.off_part);
+    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->lay.part_bytes, lora::kMaxTensorBytes));
     a.v = v;
     a.ldv = ldv;
     a.nb = pl->nb_act;
@@ -1009,11 +1126,11 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     lora::ExpandArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
-    a.tok = reinterpret_cast<const int32_t *>(ws + pl->off_tok);
-    a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->off_btok);
-    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->off_blocks);
-    a.partial = c0 > 0 ? reinterpret_cast<const float *>(ws + pl->off_part) : nullptr;
-    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->part_bytes, lora::kMaxTensorBytes));
+    a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
+    a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_btok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks);
+    a.partial = c0 > 0 ? reinterpret_cast<const float *>(ws + pl->lay.off_part) : nullptr;
+    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->lay.part_bytes, lora::kMaxTensorBytes));
     a.c0 = c0;
     a.v = v;
     a.y = y;
@@ -1032,13 +1149,13 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
     a.v_bytes = v ? uint32_t(tensor_bytes(pl->T, ldv, ldv, 4)) : 0u;
-    if (pl->weighted) a.tok_w = reinterpret_cast<const float *>(ws + pl->off_tw);
+    if (pl->weighted) a.tok_w = reinterpret_cast<const float *>(ws + pl->lay.off_tw);
     if (cores.kind) {
         const int64_t per = cores.kind == LORA_SIGMA_FULL ? int64_t(p->d.r_max) * p->d.r_max
                                                            : int64_t(p->d.r_max);
         a.sigma = cores.sigma;
         a.sigma_kind = cores.kind;
-        a.tok_sig = reinterpret_cast<const int32_t *>(ws + pl->off_tsig);
+        a.tok_sig = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tsig);
         a.sig_stride = int64_t(p->d.num_layers) * p->d.num_proj * per;
         for (int i = 0; i < nproj; ++i)
             a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;

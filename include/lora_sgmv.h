@@ -45,6 +45,11 @@
  *   - Thread safety: calls on different pools/plans are independent.  Pool
  *     mutation must not overlap launches that read the same slots, and one
  *     plan workspace must not be used by two streams at once.
+ *   - Names follow the problem statement of the pages: a pool of adapters
+ *     resident in HBM, per-segment adapter ids and offsets into the token
+ *     rows, per-adapter rank and scale; the A step (shrink, input width to
+ *     rank) and the B step (expand, rank to output width) of the pseudocode
+ *     cited above.
  */
 #ifndef LORA_SGMV_H
 #define LORA_SGMV_H
@@ -99,24 +104,33 @@ const char *lora_last_error(void);
 /* ---------------------------------------------------------------- pool ---- */
 
 /* Bytes of one adapter at its true rank: sum over layers and projections of
- * rank * (h_in + h_out) * element size.  This is the adapter size the pages
- * quote (13.6 MB for a Mistral-7B q,v adapter of rank 16 in 16-bit, "TGI
- * Multi-LoRA", section "Technical Foundation").  0 on a bad descriptor. */
-uint64_t lora_adapter_bytes(const lora_pool_desc *d, int32_t rank);
+ * rank * (h_in + h_out) * element size -- the storage accounting behind the
+ * adapter size the pages quote ("TGI Multi-LoRA: Deploy Once, Serve 30
+ * Models", section "Technical Foundation": a 13.6 MB adapter beside a
+ * 14.48 GB Mistral-7B base).  Which projections, rank and element size that
+ * adapter has is not stated; 13,631,488 bytes is, for example, q and v at
+ * rank 16 in 16-bit.  0 on a bad descriptor or rank < 1.  (The bytes an
+ * adapter takes in the slab, with padding, are lora_pool_extent_bytes.) */
+uint64_t lora_pool_bytes_for(const lora_pool_desc *d, int32_t rank);
 
 /* Bytes one adapter occupies in the slab: the same sum at the padded rank
  * with h_in rounded up to whole K-blocks (32 bf16 / 16 f32 elements),
  * rounded up to 256 bytes.  0 on a bad descriptor or rank. */
 uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank);
 
-/* Create a pool over a caller-owned device buffer `slab` of `slab_bytes`
- * (256-byte aligned).  Each adapter occupies one contiguous extent of the
+/* Create a pool of HBM-resident adapters ("Compress then Serve", rebuttal
+ * pseudocode: the stacked adapter weights every call indexes by adapter and
+ * layer; "TGI Multi-LoRA", "How Multi-LoRA Serving Works": the adapters stay
+ * loaded beside one base model) over a caller-owned device buffer `slab` of
+ * `slab_bytes` (256-byte aligned).  Each adapter occupies one contiguous extent of the
  * slab; inside it, for layer l and projection p, the A block is followed by
  * the B block, layers outermost.  A is stored K-blocked,
  * [h_in_pad_p / S][r_pad][S] with S = 32 (bf16) or 16 (f32) and h_in_pad_p =
  * h_in_p rounded up to S, so that 16 rank rows x S columns are one
  * contiguous run; B is [h_out_p][r_pad] row-major.  Pad rows and columns are
- * zero.  The slab is not touched here and is not freed by lora_pool_destroy. */
+ * zero.  The slab is not touched here and is not freed by lora_pool_destroy.
+ * Errors: LORA_EINVAL (null pointer, bad descriptor or slab alignment),
+ * LORA_EDTYPE. */
 lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d,
                              void *slab, uint64_t slab_bytes);
 lora_status lora_pool_destroy(lora_pool *p);
@@ -134,15 +148,24 @@ lora_status lora_pool_reserve(lora_pool *p, int32_t adapter_id, int32_t rank, fl
 lora_status lora_pool_upload(lora_pool *p, int32_t adapter_id, int32_t layer, int32_t proj,
                              const void *A, const void *B, int32_t src_on_host, void *stream);
 
-/* Reserve and upload every (layer, proj): A[p] -> [L][rank][h_in_p] and
- * B[p] -> [L][h_out_p][rank] (arrays of num_proj pointers).  On an upload
- * error the reservation is released again. */
+/* Register an adapter: reserve its slot and extent, then upload every
+ * (layer, proj): A[p] -> [L][rank][h_in_p] and B[p] -> [L][h_out_p][rank]
+ * (arrays of num_proj pointers), the two small matrices of a LoRA adapter
+ * ("TGI Multi-LoRA", "Technical Foundation") under its id, the id a request
+ * names ("How Multi-LoRA Serving Works").  On an upload error the
+ * reservation is released again.  Errors as lora_pool_reserve and
+ * lora_pool_upload. */
 lora_status lora_pool_register(lora_pool *p, int32_t adapter_id, int32_t rank, float scale,
                                const void *const *A, const void *const *B,
                                int32_t src_on_host, void *stream);
 
-/* Release an adapter's slot and extent.  Plans built earlier that name the
- * adapter must not be launched afterwards. */
+/* Release an adapter's slot and extent (the offload of an adapter from GPU
+ * memory, "Lorax" tool listing, "What is Lorax?").  Plans built before are
+ * refused from then on (LORA_ESTATE).  The extent is free at once: the caller
+ * must order this call, and any reuse of the extent (a later register or
+ * image upload on any stream), after the last launch that reads the adapter,
+ * e.g. by waiting for an event recorded after those launches.  (The exchange
+ * cache below does this ordering itself.)  Errors: LORA_EINVAL, LORA_ENOENT. */
 lora_status lora_pool_unregister(lora_pool *p, int32_t adapter_id);
 
 /* Pack one adapter, on the host, into the byte image of its slab extent: the
@@ -261,7 +284,12 @@ lora_status lora_cache_stats(const lora_cache *c, int32_t *resident, uint64_t *h
 
 /* ---------------------------------------------------------------- plan ---- */
 
-/* Build the gather plan of one heterogeneous batch (host memory inputs).
+/* Build the gather plan of one heterogeneous batch (host memory inputs):
+ * the tokens of a continuous batch, each request naming its adapter ("Lorax"
+ * tool listing, "What is Lorax?": heterogeneous continuous batching; "TGI
+ * Multi-LoRA", "How Multi-LoRA Serving Works"), grouped by adapter as SGMV
+ * does ("Compress then Serve", rebuttal paragraph on Punica; the
+ * pseudocode's `indices` name each token's adapter).
  *   num_tokens T >= 0; seg_starts[S+1] with seg_starts[0] = 0, non-decreasing,
  *   seg_starts[S] = T; seg_adapter[S] holds adapter ids, -1 = no adapter.
  *   Empty segments are allowed and ids may repeat.
@@ -299,18 +327,45 @@ lora_status lora_plan_create_weighted(lora_plan **out, const lora_pool *p, int32
 lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t num_tokens,
                                    const int32_t *seg_starts, const int32_t *seg_adapter,
                                    const int32_t *seg_sigma, int32_t num_segs);
-lora_status lora_plan_destroy(lora_plan *pl);   /* waits for its last upload */
+/* Re-plan an existing plan for the next batch over the same pool: the
+ * segment table as for the create calls, with optional per-segment cores
+ * (seg_sigma, as lora_plan_create_sigma) or weights (seg_weight, as
+ * lora_plan_create_weighted), NULL for none.  A serving loop plans every
+ * step (the batch changes as requests come and go), so this reuses the
+ * plan's host tables and pinned staging and allocates nothing on the device
+ * or in pinned memory unless the batch is larger than any before.  The plan
+ * must be uploaded again before its next call; an error leaves the plan as it
+ * was.  Errors as the create calls. */
+lora_status lora_plan_rebuild(lora_plan *pl, int32_t num_tokens, const int32_t *seg_starts,
+                              const int32_t *seg_adapter, const int32_t *seg_sigma,
+                              const float *seg_weight, int32_t num_segs);
+
+/* Frees the plan; waits for its last uploads to leave its staging buffers. */
+lora_status lora_plan_destroy(lora_plan *pl);
 
 /* Device bytes the plan needs: its tables and the per-call partial sums of
  * the shrink, sized for calls of up to `max_proj` projections at once.
  * 0 on error. */
 uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj);
 
+/* An upper bound of lora_plan_workspace_bytes for every plan over pool `p`
+ * of at most num_tokens tokens and num_segs segments, for calls of up to
+ * `max_proj` projections: one workspace of this size serves every batch of a
+ * serving loop, allocated once.  0 on a bad argument. */
+uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t num_segs,
+                              int32_t max_proj);
+
 /* Copy the plan's tables into the caller-owned device workspace `ws`
  * (256-byte aligned, at least lora_plan_workspace_bytes(pl, max_proj)), on
- * `stream`.  Every sgmv call with this plan then uses `ws` (its tables, and
+ * `stream`, through pinned staging (two buffers used in turn: the host waits
+ * only for the copy out of the buffer it reuses, that of the upload before
+ * last).  Every sgmv call with this plan then uses `ws` (its tables, and
  * scratch for the shrink's partial sums); calls must be ordered after this
- * upload, and calls that share `ws` must not run concurrently. */
+ * upload, and calls that share `ws` must not run concurrently.  A workspace
+ * holds the tables of the plan uploaded into it last: a call with another
+ * plan that was uploaded into it before is refused with LORA_ESTATE (upload
+ * that plan again).  Errors: LORA_EINVAL (bad max_proj, null or misaligned
+ * ws), LORA_ESTATE (ws_bytes too small), LORA_EHIP. */
 lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
                              void *stream);
 
@@ -327,7 +382,14 @@ lora_status lora_plan_export(const lora_plan *pl, int32_t *token_order, int32_t 
                              int32_t *group_adapter, int32_t *group_rank);
 
 /* ---------------------------------------------------------------- sgmv ---- */
-/* For all three: `projs` lists `nproj` projection indices of the pool that
+/* The delta itself.  "Compress then Serve" (rebuttal pseudocode of
+ * add_lora_slice_with_sigma, and of the BGMV dispatch it stands for) gives
+ * the two steps these calls take: the A step at scale 1.0 into a float32
+ * buffer of shape (tokens, R), then the B step with `scale` into the slice of
+ * y at y_offset of width y_slice_size; here the tokens' adapters come from
+ * the plan (the pseudocode's `indices`), the layer from `layer`, the scale
+ * from each adapter's registration, and y_offset / y_slice_size from
+ * y_offsets and each projection's h_out.  For all of them: `projs` lists `nproj` projection indices of the pool that
  * read the same input x (e.g. q, k, v), so x has width h_in of all of them
  * (they must agree).  For projection i of the list, its output is the
  * column slice y[:, y_offsets[i] : y_offsets[i] + h_out] (the pseudocode's
@@ -337,9 +399,14 @@ lora_status lora_plan_export(const lora_plan *pl, int32_t *token_order, int32_t 
  * Every device tensor a call addresses (x, y, base, v) spans at most 2 GiB,
  * and so do the shrink's partial sums of one call (rank tiles x k-chunks x
  * projections x 1 KiB per 16-token tile): a larger call is refused with
- * LORA_EINVAL before anything is enqueued (split the batch). */
+ * LORA_EINVAL before anything is enqueued (split the batch).
+ * Errors of every call: LORA_EINVAL (null or misaligned pointers, bad
+ * layer, projections, strides or sizes), LORA_ESTATE (plan not uploaded,
+ * built before an adapter was unregistered, or its workspace since given to
+ * another plan), LORA_EHIP (a launch failed). */
 
-/* Shrink (the A step, scale 1.0): v[t][i*r_max + j] = sum_k A_i,p[j][k] x[t][k]
+/* Shrink (the A step, scale 1.0, "Compress then Serve", rebuttal pseudocode,
+ * step 1): v[t][i*r_max + j] = sum_k A_i,p[j][k] x[t][k]
  * for every token with an adapter, j < r_max (columns j >= rank are zero).
  * Rows of tokens without an adapter are not written.
  * x: [T][ldx] device; v: [T][ldv] float32 device, ldv >= nproj * r_max. */
@@ -347,7 +414,8 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer,
                         int32_t nproj, const int32_t *projs,
                         const void *x, int64_t ldx, float *v, int64_t ldv, void *stream);
 
-/* Expand (the B step): y[t][y_offsets[i] + o] += s_i * sum_j B_i,p[o][j] v[t][i*r_max + j]
+/* Expand (the B step, "Compress then Serve", rebuttal pseudocode, step 3):
+ * y[t][y_offsets[i] + o] += s_i * sum_j B_i,p[o][j] v[t][i*r_max + j]
  * for every token with an adapter, computed in float32 from the current y
  * and rounded once.  Rows of tokens without an adapter are not written.
  * v: [T][ldv] float32 device; y: [T][ldy] device. */
@@ -355,7 +423,9 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer,
                         int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
                         const float *v, int64_t ldv, void *y, int64_t ldy, void *stream);
 
-/* Fused shrink then expand: y = y_in + s_i * B_i,p (A_i,p x), with y_in = base
+/* Fused shrink then expand (steps 1 and 3 of the same pseudocode in one call;
+ * "TGI Multi-LoRA", "Technical Foundation": the frozen layer's output plus the
+ * adapter's B A x): y = y_in + s_i * B_i,p (A_i,p x), with y_in = base
  * (base_out of the frozen layer, same column layout as y, [T][ldb]) when base
  * is non-NULL, else the current y.  Tokens without an adapter get y = base
  * (or are left untouched when base is NULL).  v is never written to memory:

@@ -68,11 +68,16 @@ def load_library(path):
 
 
 def _load():
+    """The built oracle, or the build HAB_ORACLE_LIB names (e.g. a sanitizer
+    build for the tests)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _lib = load_library(_build.LIB)
+        path = os.environ.get("HAB_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        _lib = load_library(path)
     return _lib
 
 

@@ -16,9 +16,9 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 
-def build(out: str = LIB, src: str = SRC) -> str:
+def build(out: str = LIB, src: str = SRC, extra=()) -> str:
     tmp = out + ".tmp"
-    cmd = ["gcc", *CFLAGS, "-o", tmp, src]
+    cmd = ["gcc", *CFLAGS, *extra, "-o", tmp, src]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -16,11 +16,10 @@
  *   Multi-LoRA Serving Works" on the same page); segments are contiguous
  *   token ranges that share an adapter, the grouping SGMV exploits ("Compress
  *   then Serve", rebuttal paragraph on Punica's segmented gather).
- * - The A step runs with scale 1 into a float32 buffer of shape
- *   (tokens, R); the B step applies the adapter's scale and adds into a slice
- *   of y ("Compress then Serve", rebuttal pseudocode of
- *   add_lora_slice_with_sigma: buffer creation, step 1 and step 3).  y_in is
- *   whatever y held before the call (zero, W x, or a given base output).
+ * - The rank-R intermediate v = A_i x[t] is formed in float32 with A at
+ *   scale 1, and then s_i B_i v is added into the token's slice of y
+ *   ("Compress then Serve", the rebuttal's pseudocode of the delta).  y_in
+ *   is whatever y held before the call (zero, W x, or a given base output).
  *
  * Plain definition, written out: no blocking, no reordering.  Sums run in
  * ascending index order.  oracle_delta_f32 accumulates in float (the
@@ -33,7 +32,7 @@
  * (the token keeps y_in); an id that is not in the adapter table, or a
  * segment table that does not partition [0, T), is an error (return -1).
  *
- * Two more functions follow the same loops: the three-step delta of jointly
+ * Two more functions follow the same loops: the delta of jointly
  * compressed adapters (oracle_delta_sigma_*: a shared basis and a per-
  * segment core between the A and B steps) and the weighted merge of several
  * adapters per request (oracle_delta_merge_*).
@@ -203,14 +202,13 @@ int oracle_delta_f64(int32_t T, int32_t h_in, int32_t h_out,
 }
 
 /*
- * Jointly compressed adapters: the three-step delta
+ * Jointly compressed adapters:
  *
- *   y[t] = y_in[t] + s_i * B_c (Sigma_j (A_c x[t]))
+ *   y[t] = y_in[t] + s_i * B_c u,   u = Sigma_j v,   v = A_c x[t]
  *
- * ("Compress then Serve", rebuttal pseudocode of add_lora_slice_with_sigma:
- * step 1 applies A into the float32 buffer, step 2 transforms the buffer
- * with the adapter's Sigma into a second float32 buffer, step 3 applies B
- * with the scale and adds into the y slice).  A_c and B_c are the shared
+ * with v and u in float32 ("Compress then Serve", the rebuttal's pseudocode
+ * of the delta with a per-adapter core: the shared A, then the core, then
+ * the shared B with the scale into the y slice).  A_c and B_c are the shared
  * basis of the segment's entry c in the adapter table (a cluster, r x h_in
  * and h_out x r); Sigma_j is the segment's core, r x r (kind 2, "JD-Full")
  * or its diagonal of r values (kind 1, "JD-Diag"); seg_sigma[s] = -1 means
@@ -246,7 +244,7 @@ int oracle_delta_sigma_f32(int32_t T, int32_t h_in, int32_t h_out,
 
 #pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
     for (int32_t t = 0; t < T; ++t) {
-        float v[r_big], vs[r_big];
+        float v[r_big], u[r_big];
         float *yt = y_out + (int64_t)t * ld_out;
         for (int32_t o = 0; o < h_out; ++o)
             yt[o] = y_in ? y_in[(int64_t)t * ld_in + o] : 0.0f;
@@ -255,32 +253,32 @@ int oracle_delta_sigma_f32(int32_t T, int32_t h_in, int32_t h_out,
         const int32_t r = ranks[a];
         const float sc = scales[a];
         const float *xt = x + (int64_t)t * ldx;
-        /* step 1: buffer = A_c x[t] */
+        /* v = A_c x[t] */
         for (int32_t j = 0; j < r; ++j) {
             float acc = 0.0f;
             const float *aj = A[a] + (int64_t)j * h_in;
             for (int32_t k = 0; k < h_in; ++k) acc += aj[k] * xt[k];
             v[j] = acc;
         }
-        /* step 2: buffer_sigma = Sigma_j buffer */
+        /* u = Sigma_j v (u = v without a core) */
         const int32_t sj = tok_s[t];
         for (int32_t j = 0; j < r; ++j) {
             if (sj < 0) {
-                vs[j] = v[j];
+                u[j] = v[j];
             } else if (sigma_kind == 1) {
-                vs[j] = sigma[sj][j] * v[j];
+                u[j] = sigma[sj][j] * v[j];
             } else {
                 float acc = 0.0f;
                 const float *row = sigma[sj] + (int64_t)j * sigma_ld;
                 for (int32_t k = 0; k < r; ++k) acc += row[k] * v[k];
-                vs[j] = acc;
+                u[j] = acc;
             }
         }
-        /* step 3: y[t] += s * (B_c buffer_sigma) */
+        /* y[t] += s * (B_c u) */
         for (int32_t o = 0; o < h_out; ++o) {
             float d = 0.0f;
             const float *bo = B[a] + (int64_t)o * r;
-            for (int32_t j = 0; j < r; ++j) d += bo[j] * vs[j];
+            for (int32_t j = 0; j < r; ++j) d += bo[j] * u[j];
             yt[o] = yt[o] + sc * d;
         }
     }
@@ -289,7 +287,7 @@ int oracle_delta_sigma_f32(int32_t T, int32_t h_in, int32_t h_out,
     return 0;
 }
 
-/* The same three steps with double accumulation; y_out is double. */
+/* The same with double accumulation; y_out is double. */
 int oracle_delta_sigma_f64(int32_t T, int32_t h_in, int32_t h_out,
                            const float *x, int64_t ldx,
                            int32_t S, const int32_t *seg_starts, const int32_t *seg_adapter,
@@ -318,7 +316,7 @@ int oracle_delta_sigma_f64(int32_t T, int32_t h_in, int32_t h_out,
 
 #pragma omp parallel for schedule(dynamic, 1) num_threads(threads > 1 ? threads : 1)
     for (int32_t t = 0; t < T; ++t) {
-        double v[r_big], vs[r_big];
+        double v[r_big], u[r_big];
         double *yt = y_out + (int64_t)t * ld_out;
         for (int32_t o = 0; o < h_out; ++o)
             yt[o] = y_in ? (double)y_in[(int64_t)t * ld_in + o] : 0.0;
@@ -336,20 +334,20 @@ int oracle_delta_sigma_f64(int32_t T, int32_t h_in, int32_t h_out,
         const int32_t sj = tok_s[t];
         for (int32_t j = 0; j < r; ++j) {
             if (sj < 0) {
-                vs[j] = v[j];
+                u[j] = v[j];
             } else if (sigma_kind == 1) {
-                vs[j] = (double)sigma[sj][j] * v[j];
+                u[j] = (double)sigma[sj][j] * v[j];
             } else {
                 double acc = 0.0;
                 const float *row = sigma[sj] + (int64_t)j * sigma_ld;
                 for (int32_t k = 0; k < r; ++k) acc += (double)row[k] * v[k];
-                vs[j] = acc;
+                u[j] = acc;
             }
         }
         for (int32_t o = 0; o < h_out; ++o) {
             double d = 0.0;
             const float *bo = B[a] + (int64_t)o * r;
-            for (int32_t j = 0; j < r; ++j) d += (double)bo[j] * vs[j];
+            for (int32_t j = 0; j < r; ++j) d += (double)bo[j] * u[j];
             yt[o] = yt[o] + sc * d;
         }
     }

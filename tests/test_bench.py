@@ -41,12 +41,30 @@ def test_full_stack_algorithmic_bytes():
 
 def test_kernel_bytes_sum_to_the_step():
     """Per-launch bytes of the shrink and expand over one layer's calls add up
-    to the step's algorithmic bytes per layer plus the float32 v the two
-    kernels hand over (written once, read once)."""
+    to the step's algorithmic bytes per layer exactly (the float32
+    intermediate the two kernels hand over is not algorithmic)."""
+    for ci in (1, 2, 3, 4):
+        w = config(ci)
+        alg = bench.algorithmic(w)
+        per_layer = sum(bench.kernel_bytes(w, c, k) for c in w.calls
+                        for k in ("shrink", "expand"))
+        assert np.isclose(per_layer, alg["bytes"] / w.num_layers), ci
+
+
+def test_step_metrics_fractions():
+    """The derived figures of a step: tokens/s, GB/s and TFLOP/s from the
+    algorithmic counts, the attainable roof min(MFMA peak, intensity x HBM
+    peak), and for a decode workload the attainable fraction equals the HBM
+    fraction (its roof is the bandwidth one)."""
     w = config(4)
     alg = bench.algorithmic(w)
-    per_layer = sum(bench.kernel_bytes(w, c, k) for c in w.calls for k in ("shrink", "expand"))
-    tok = w.token_adapter()
-    v = sum(4 * int(w.ranks[tok[t]]) * len(c) for c in w.calls for t in range(w.num_tokens)
-            if tok[t] >= 0)
-    assert np.isclose(per_layer, alg["bytes"] / w.num_layers + 2 * v)
+    m = bench.step_metrics(w, 2.0)
+    assert np.isclose(m["tokens_per_s"], 128 / 2e-3, rtol=1e-6)
+    assert np.isclose(m["hbm_gbs"], alg["bytes"] / 2e-3 / 1e9, rtol=1e-4)
+    assert np.isclose(m["attainable_frac"], m["hbm_frac"], rtol=1e-3)
+    w2 = config(2)
+    m2 = bench.step_metrics(w2, 0.1)
+    a2 = bench.algorithmic(w2)
+    assert np.isclose(m2["attainable_tflops"],
+                      a2["flops"] / a2["bytes"] * bench.HBM_PEAK_GBS / 1e3, rtol=1e-3)
+    assert m2["mfma_frac"] < m2["attainable_frac"]

@@ -472,8 +472,9 @@ def test_call_errors_enqueue_nothing():
 
 def test_graph_replay_matches_eager():
     """The fused step captured in a HIP graph gives the eager result on every
-    replay, with eager work and synchronisation between replays (the fix-up
-    counters reset themselves; no memset nodes are recorded)."""
+    replay, with eager work and synchronisation between replays (the kernels
+    keep no state between calls and record no memset nodes: every workspace
+    entry a call reads, the same call wrote before)."""
     w = multi_proj_case(5, has_base=True, T=90)
     dw = DeviceWorkload(w, threads=4)
     dw.run_fused()
@@ -533,6 +534,75 @@ def test_plan_reupload_same_workspace(T):
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[2][k]), k
         assert not np.array_equal(outs[0][k], outs[1][k]), k
+
+
+def test_workspace_owner_refuses_stale_plan():
+    """A workspace holds the tables of the plan uploaded into it last: a call
+    with a plan uploaded there before is refused (it would read the other
+    plan's descriptors) until that plan is uploaded again."""
+    import heterogeneous_adapter_batching_amd as hab
+    w = random_case(93, T=50, h_in=128, h_out=64, n_adapters=4, r_choices=[8, 16])
+    dw = DeviceWorkload(w, threads=2)
+    mp = dw.max_proj
+    p1 = dw.plan
+    p2 = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, np.roll(w.seg_adapter, 1))
+    ws = torch.empty(dw.pool.workspace_bytes(w.num_tokens, w.num_segs, mp), dtype=torch.uint8,
+                     device="cuda")
+    p1.upload(mp, ws=ws)
+    p2.upload(mp, ws=ws)
+    with pytest.raises(hab.LoraError) as ei:
+        dw.run_fused()
+    assert ei.value.status == -9 and "another plan" in ei.value.message
+    p1.upload(mp, ws=ws)
+    dw.zero_outputs()
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, threads=2)
+
+
+def test_plan_rebuild_parity():
+    """One plan rebuilt in place for batch after batch (decode steps, prompts,
+    mixed; cores of the rebuilt plan kept plain) in one workspace sized once
+    by lora_workspace_bytes, uploaded each time and checked against the
+    oracle; the rebuilt plan's outputs equal a fresh plan's bit for bit."""
+    import heterogeneous_adapter_batching_amd as hab
+    base = random_case(94, T=1200, h_in=256, h_out=136, n_adapters=8, max_seg=300,
+                       r_choices=[8, 16, 32, 64], has_base=True)
+    dw = DeviceWorkload(base, threads=4, upload=np.arange(base.pool_size))
+    mp = dw.max_proj
+    ws = torch.empty(dw.pool.workspace_bytes(1200, 1200, mp), dtype=torch.uint8, device="cuda")
+    plan = dw.plan
+    g = np.random.default_rng(94)
+    for step in range(6):
+        T = [1200, 37, 1100, 1, 600, 256][step]
+        cuts = np.unique(np.concatenate([[0, T], g.integers(0, T + 1, g.integers(1, 40))]))
+        ids = g.integers(-1, base.pool_size, len(cuts) - 1).astype(np.int32)
+        if step % 2 == 0:                            # a few long groups
+            ids = (np.arange(len(cuts) - 1) % 3).astype(np.int32)
+        w = dataclasses.replace(base, num_tokens=T, seg_starts=cuts.astype(np.int32),
+                                seg_adapter=ids)
+        plan.rebuild(T, w.seg_starts, w.seg_adapter)
+        plan.upload(mp, ws=ws)
+        sub = DeviceWorkload.__new__(DeviceWorkload)
+        sub.__dict__.update(dw.__dict__)
+        sub.w = w
+        sub.plan = plan
+        sub.x = {k: v[:T] for k, v in dw.x.items()}
+        sub.base = {k: v[:T] for k, v in dw.base.items()}
+        sub.y = {k: torch.zeros_like(v[:T]) for k, v in dw.base.items()}
+        log(f"[parity] rebuild step {step}: T={T} S={w.num_segs} {plan.stats()}")
+        sub.run_fused()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in sub.y.items()}
+        check_workload(sub, threads=4)
+        fresh = hab.Plan(dw.pool, T, w.seg_starts, w.seg_adapter).upload(mp)
+        sub.plan = fresh
+        for v in sub.y.values():
+            v.zero_()
+        sub.run_fused()
+        torch.cuda.synchronize()
+        for k in got:
+            assert torch.equal(got[k].view(torch.int16), sub.y[k].view(torch.int16)), (step, k)
 
 
 def test_register_from_device_matches_host():

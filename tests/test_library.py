@@ -62,7 +62,7 @@ def test_pages_adapter_size():
     ]
     base = fig["base_gb"] * 1e9
     for d, r in readings:
-        b = hab.adapter_bytes(d, r)
+        b = hab.pool_bytes_for(d, r)
         assert b == 13_631_488
         assert round(b / 1e6, 1) == fig["adapter_mb"]
         assert b / base < fig["adapter_base_ratio_max"]
@@ -72,15 +72,15 @@ def test_pages_adapter_size():
     # the full-stack workload's adapter: 7 projections, r=16, bf16
     w = config(4)
     d = make_desc(32, [p.h_in for p in w.projs], [p.h_out for p in w.projs], 16, "bf16")
-    assert hab.adapter_bytes(d, 16) == 83_886_080
+    assert hab.pool_bytes_for(d, 16) == 83_886_080
 
 
 def test_extent_padding_and_alignment():
     d = make_desc(2, [64, 128], [32, 16], 64, "bf16", rank_granule=8)
     per_rank = 2 * 2 * (64 + 32 + 128 + 16)      # bytes per rank row over layers, projections
-    assert hab.adapter_bytes(d, 5) == 5 * per_rank
+    assert hab.pool_bytes_for(d, 5) == 5 * per_rank
     assert hab.extent_bytes(d, 5) == -(-8 * per_rank // 256) * 256
-    assert hab.extent_bytes(d, 65) == 0 and hab.adapter_bytes(d, 0) == 0
+    assert hab.extent_bytes(d, 65) == 0 and hab.pool_bytes_for(d, 0) == 0
     d16 = make_desc(2, [64, 128], [32, 16], 64, "bf16", rank_granule=16)
     assert hab.extent_bytes(d16, 5) == -(-16 * per_rank // 256) * 256
 
@@ -289,3 +289,71 @@ def test_pack_adapter_errors():
     with pytest.raises(hab.LoraError) as ei:
         hab.pack_adapter(desc, 17, A, B)
     assert ei.value.status == -4
+
+
+def _random_plans(n):
+    """Random batches over small pools of mixed ranks: decode-like, prompt-like
+    (long groups holding 1024 tokens and more) and mixed."""
+    for seed in range(n):
+        g = np.random.default_rng(700 + seed)
+        kind = seed % 3
+        if kind == 0:
+            w = random_case(700 + seed, T=int(g.integers(0, 400)), h_in=64, h_out=32)
+        elif kind == 1:
+            w = random_case(700 + seed, T=int(g.integers(1000, 3000)), h_in=64, h_out=32,
+                            n_adapters=int(g.integers(1, 5)))
+        else:
+            w = mixed_case(700 + seed, h_in=64, h_out=32, long_tokens=1000 + 10 * seed)
+        yield w
+
+
+@pytest.mark.parametrize("dtype,h_in", [("bf16", [64, 64, 4104]), ("f32", [64, 1000, 64])])
+def test_workspace_bound(dtype, h_in):
+    """lora_workspace_bytes bounds the workspace of every plan of at most
+    that many tokens and segments, for calls of 1..3 projections."""
+    for w in _random_plans(24):
+        pool = hab.Pool(1, h_in, [32, 48, 16], 64, dtype, max_slots=w.pool_size,
+                        slab_ptr=1 << 20, slab_bytes=1 << 30)
+        for i in range(w.pool_size):
+            pool.reserve(i, int(w.ranks[i]), float(w.scales[i]))
+        plan = hab.Plan(pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+        for mp in (1, 2, 3):
+            need = plan.workspace_bytes(mp)
+            bound = pool.workspace_bytes(w.num_tokens, w.num_segs, mp)
+            assert 0 < need <= bound, (w.name, mp, need, bound)
+    assert pool.workspace_bytes(-1, 1, 1) == 0 and pool.workspace_bytes(1, 1, 9) == 0
+
+
+def test_plan_rebuild_matches_create():
+    """A plan rebuilt in place for batch after batch holds what a new plan of
+    the same batch holds; a rebuild that fails leaves the plan as it was."""
+    pool = _pool(max_slots=64, h_in=[64], h_out=[32])
+    g = np.random.default_rng(5)
+    for i in range(64):
+        pool.reserve(i, int(g.integers(1, 65)), float(g.uniform(0.5, 2)))
+    plan = None
+    for seed, w in enumerate(_random_plans(12)):
+        ids = np.where(w.seg_adapter >= 0, w.seg_adapter % 64, -1).astype(np.int32)
+        fresh = hab.Plan(pool, w.num_tokens, w.seg_starts, ids)
+        if plan is None:
+            plan = hab.Plan(pool, w.num_tokens, w.seg_starts, ids)
+        else:
+            plan.rebuild(w.num_tokens, w.seg_starts, ids)
+        a, b = plan.export(), fresh.export()
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (seed, k)
+        assert plan.stats() == fresh.stats()
+        assert plan.workspace_bytes(3) == fresh.workspace_bytes(3)
+        before = (plan.export(), plan.stats())
+        with pytest.raises(hab.LoraError) as ei:
+            plan.rebuild(w.num_tokens + 1, w.seg_starts, ids)      # does not end at T
+        assert ei.value.status == -6
+        after = (plan.export(), plan.stats())
+        assert after[1] == before[1]
+        for k in before[0]:
+            assert np.array_equal(after[0][k], before[0][k])
+    # weights and cores through rebuild
+    plan.rebuild(4, [0, 2, 4], [1, 2], seg_weight=[0.5, 2.0])
+    plan.rebuild(4, [0, 2, 4], [1, 2], seg_sigma=[0, -1])
+    with pytest.raises(hab.LoraError):
+        plan.rebuild(4, [0, 2, 4], [1, 2], seg_weight=[np.inf, 2.0])

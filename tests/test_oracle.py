@@ -525,11 +525,11 @@ MUTATIONS = {
                               "const int32_t a = tok_a[t] < 0 ? 0 : tok_a[t];"),
     "sigma_transposed": ("acc += row[k] * v[k];",
                          "acc += sigma[sj][(int64_t)k * sigma_ld + j] * v[k];"),
-    "sigma_skipped": ("vs[j] = acc;", "vs[j] = v[j];"),
-    "sigma_diag_ignored": ("vs[j] = sigma[sj][j] * v[j];", "vs[j] = v[j];"),
+    "sigma_skipped": ("u[j] = acc;", "u[j] = v[j];"),
+    "sigma_diag_ignored": ("u[j] = sigma[sj][j] * v[j];", "u[j] = v[j];"),
     "sigma_first_core": ("const int32_t sj = tok_s[t];",
                          "const int32_t sj = tok_s[t] < 0 ? -1 : 0;"),
-    "sigma_b_reads_buffer": ("for (int32_t j = 0; j < r; ++j) d += bo[j] * vs[j];",
+    "sigma_b_reads_buffer": ("for (int32_t j = 0; j < r; ++j) d += bo[j] * u[j];",
                              "for (int32_t j = 0; j < r; ++j) d += bo[j] * v[j];"),
     "merge_weight_dropped": ("const float sw = seg_weights[s * K + k] * scales[a];",
                              "const float sw = scales[a];"),
