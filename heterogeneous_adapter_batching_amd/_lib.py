@@ -12,6 +12,7 @@ LIB_PATH = os.environ.get("HAB_LORA_LIB") or os.path.join(PKG, "libhab_lora.so")
 LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_PROJ = 8
 LORA_MAX_RANK = 64
+LORA_STATIC_SCRATCH_MIB = 64
 
 STATUS = {0: "LORA_OK", -1: "LORA_EINVAL", -2: "LORA_ENOSPC", -3: "LORA_ENOENT",
           -4: "LORA_ERANK", -5: "LORA_EDTYPE", -6: "LORA_ESEG", -7: "LORA_EHIP",
@@ -73,6 +74,8 @@ SIGNATURES = {
                                  _vp, _i64, _vp]),
     "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
                                 _vp, _i64, _vp, _i64, _vp]),
+    "sgmv_fused_static": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64, _vp,
+                                 _i64, _vp]),
     "sgmv_shrink_partials": (_i32, [_vp, _vp, _i32, _i32, _i32p, _vp, _i64, _vp]),
     "sgmv_expand_partials": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i64,
                                     _vp]),

@@ -453,6 +453,26 @@ def sgmv_fused(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=
     return y
 
 
+def sgmv_fused_static(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=None,
+                      stream=None):
+    """sgmv_fused with the shrink partials in the library's static device
+    scratch: the call allocates nothing.  Calls on one GPU must not overlap."""
+    dt = _torch_dtype(pool.dtype)
+    _check_dev(x, "x", dt)
+    _check_dev(y, "y", dt)
+    if base is not None:
+        _check_dev(base, "base", dt)
+    n, parr = _projs(projs)
+    check(pool.lib.sgmv_fused_static(pool.handle, plan.handle, layer, n, parr,
+                                     _i32_array(y_offsets),
+                                     ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                                     ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                     base.stride(0) if base is not None else 0,
+                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                     _stream_handle(stream)))
+    return y
+
+
 def sgmv_shrink_partials(pool: Pool, plan: Plan, layer: int, projs, x, stream=None):
     """The shrink of sgmv_fused alone: partial sums of v = A x left in the
     plan's workspace for sgmv_expand_partials of the same call."""

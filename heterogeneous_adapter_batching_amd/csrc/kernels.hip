@@ -26,6 +26,7 @@
 // multiply exactly inside the bf16 MFMA and sum in float32.  For the B step
 // the float32 v is split into three bf16 pieces whose sum is v exactly, so
 // B (h0 + h1 + h2) is the float32 product B v summed in float32.
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_runtime.h>
@@ -1167,6 +1168,37 @@ hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Scratch for callers that cannot allocate (sgmv_fused_static): the shrink
+// partials of such a call.  Each device holds its own copy at its own address
+// until the process ends; host code must never pass the array's name to a
+// kernel or a copy (in host code it is a host-side stand-in), only the
+// address hipGetSymbolAddress gives for the current device, found once per
+// device and kept.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void **ptr, uint64_t *bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kStaticScratchBytes;
+    return hipSuccess;
+}
 
 hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;

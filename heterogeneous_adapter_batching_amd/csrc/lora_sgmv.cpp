@@ -1021,13 +1021,31 @@ int32_t grid_for(int32_t units, int32_t gs) {
     return int32_t(round_up(uint64_t(std::max(units, 0)), uint64_t(lora::kXcds) * gs));
 }
 
+// Where a call's shrink partials go: the plan workspace's partial region, or
+// the library's static device scratch (sgmv_fused_static).
+struct Partials {
+    float *ptr = nullptr;
+    uint64_t bytes = 0;
+    bool in_workspace = true;
+};
+
+Partials workspace_partials(const lora_plan *pl) {
+    Partials pt;
+    pt.ptr = reinterpret_cast<float *>(static_cast<uint8_t *>(pl->ws) + pl->lay.off_part);
+    pt.bytes = pl->lay.part_bytes;
+    return pt;
+}
+
 lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
                        const int32_t *projs, const void *x, int64_t ldx, const CallCheck &cc,
-                       hipStream_t st, int32_t *c0_out) {
+                       hipStream_t st, int32_t *c0_out, const Partials &pt) {
     *c0_out = 0;
-    // every shrink leaves its partials in the workspace: record whose they are
+    // a shrink into the workspace leaves its partials there: record whose
+    // they are (for sgmv_expand_partials); one into the static scratch
+    // leaves the workspace's partials unknown
     pl->part_layer = -1;
     auto record = [&](int32_t c0) {
+        if (!pt.in_workspace) return;
         pl->part_layer = layer;
         pl->part_nproj = nproj;
         pl->part_c0 = c0;
@@ -1042,7 +1060,7 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.slab = p->slab;
     a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_ttok);
     a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->lay.off_tiles);
-    a.partial = reinterpret_cast<float *>(const_cast<uint8_t *>(ws) + pl->lay.off_part);
+    a.partial = pt.ptr;
     a.x = x;
     a.ldx = ldx;
     for (int i = 0; i < nproj; ++i) a.coef_a[i] = p->coef_a(layer, projs[i]);
@@ -1059,9 +1077,14 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     if (need > lora::kMaxTensorBytes)   // the expands address the partials within 2 GiB
         return fail(LORA_EINVAL, "the call's shrink partials would span %llu bytes, more than "
                     "2 GiB: split the batch", (unsigned long long)need);
-    if (need > pl->lay.part_bytes)
+    if (need > pt.bytes) {
+        if (!pt.in_workspace)
+            return fail(LORA_EINVAL, "the call's shrink partials (%llu bytes) exceed the static "
+                        "scratch of %llu bytes: split the batch",
+                        (unsigned long long)need, (unsigned long long)pt.bytes);
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
-                    (unsigned long long)need, (unsigned long long)pl->lay.part_bytes);
+                    (unsigned long long)need, (unsigned long long)pt.bytes);
+    }
     hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, mp, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
     *c0_out = a.c0;
@@ -1120,7 +1143,8 @@ lora_status check_cores(const lora_plan *pl, const Cores &c) {
 lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
                        const int32_t *projs, const int32_t *yoff, int32_t c0, const float *v,
                        int64_t ldv, void *y, int64_t ldy, const void *base, int64_t ldb,
-                       hipStream_t st, const Cores &cores = Cores()) {
+                       hipStream_t st, const Cores &cores = Cores(),
+                       const Partials *pt = nullptr) {
     const int32_t nb = base ? pl->nb_all() : pl->nb_act;
     if (nb == 0) return LORA_OK;
     lora::ExpandArgs a{};
@@ -1129,8 +1153,9 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
     a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_btok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks);
-    a.partial = c0 > 0 ? reinterpret_cast<const float *>(ws + pl->lay.off_part) : nullptr;
-    a.partial_bytes = uint32_t(std::min<uint64_t>(pl->lay.part_bytes, lora::kMaxTensorBytes));
+    const Partials wpt = pt ? *pt : workspace_partials(pl);
+    a.partial = c0 > 0 ? wpt.ptr : nullptr;
+    a.partial_bytes = uint32_t(std::min<uint64_t>(wpt.bytes, lora::kMaxTensorBytes));
     a.c0 = c0;
     a.v = v;
     a.y = y;
@@ -1240,7 +1265,7 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, 
         return fail(LORA_EINVAL, "ldv %lld < nproj * r_max or not a multiple of 4", (long long)ldv);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int32_t c0 = 0;
-    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0);
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, workspace_partials(pl));
     if (st != LORA_OK) return st;
     return run_reduce(p, pl, nproj, c0, v, ldv, hs);
 }
@@ -1319,10 +1344,43 @@ lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t la
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int32_t c0 = 0;
-    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0);
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, workspace_partials(pl));
     if (st != LORA_OK) return st;
     return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
                       cores);
+}
+
+lora_status sgmv_fused_static(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                              int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                              const void *x, int64_t ldx, const void *base, int64_t ldb, void *y,
+                              int64_t ldy, void *stream) {
+    CallCheck cc;
+    lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
+    if (st != LORA_OK) return st;
+    if (pl->T == 0) return LORA_OK;
+    if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
+    if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
+                                               (long long)ldx);
+    if (tensor_bytes(pl->T, ldx, cc.h_in, cc.es) > lora::kMaxTensorBytes)
+        return fail(LORA_EINVAL, "x spans more than 2 GiB");
+    st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
+    if (st != LORA_OK) return st;
+    if (base) {
+        st = check_y(p, pl->T, nproj, projs, yoff, base, ldb, "base", cc);
+        if (st != LORA_OK) return st;
+    }
+    Partials pt;
+    pt.in_workspace = false;
+    void *ptr = nullptr;
+    const hipError_t e = lora::static_scratch(&ptr, &pt.bytes);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    pt.ptr = static_cast<float *>(ptr);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t c0 = 0;
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, pt);
+    if (st != LORA_OK) return st;
+    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
+                      Cores(), &pt);
 }
 
 lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
@@ -1347,7 +1405,7 @@ lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_
         return LORA_OK;
     }
     return run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, static_cast<hipStream_t>(stream),
-                      &c0);
+                      &c0, workspace_partials(pl));
 }
 
 lora_status sgmv_expand_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,

@@ -231,4 +231,9 @@ hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStre
 // nvm: the largest decode_nvt of the launch's rank classes
 hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s);
 
+// The library's static device scratch (sgmv_fused_static): the address of
+// the current device's copy, found once per device, and its size in bytes.
+constexpr uint64_t kStaticScratchBytes = uint64_t(LORA_STATIC_SCRATCH_MIB) << 20;
+hipError_t static_scratch(void **ptr, uint64_t *bytes);
+
 }  // namespace lora

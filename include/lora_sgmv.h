@@ -489,6 +489,28 @@ lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t la
                              int32_t num_sigma, const void *base, int64_t ldb, void *y,
                              int64_t ldy, void *stream);
 
+/* ------------------------------------------------------- no allocation ---- */
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): sgmv_fused
+ * with the shrink's partial sums in the library's static device scratch of
+ * LORA_STATIC_SCRATCH_MIB MiB instead of the plan workspace's partial region.
+ * The call makes no hipMalloc, hipFree or other allocating call; the caller
+ * still passes x, base and y and a plan uploaded before, whose tables the
+ * kernels read.  Each GPU has its own scratch, held from the first call on
+ * that GPU until the process ends, and every call on one GPU shares it:
+ * calls that overlap on one GPU (on different streams) race and give wrong
+ * results, so order them.  Nothing in the scratch needs clearing (every
+ * partial a call reads, the same call wrote before), and it keeps the last
+ * call's partials.  A call whose partials exceed the scratch is refused with
+ * LORA_EINVAL (split the batch).  Afterwards the plan's workspace holds no
+ * partials for sgmv_expand_partials.  Arguments, results (bit for bit) and
+ * other errors as sgmv_fused. */
+#define LORA_STATIC_SCRATCH_MIB 64
+lora_status sgmv_fused_static(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                              int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
+                              const void *x, int64_t ldx, const void *base, int64_t ldb,
+                              void *y, int64_t ldy, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
