@@ -15,11 +15,11 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     Pool, Plan, sgmv_shrink, sgmv_expand, sgmv_fused, sgmv_expand_sigma, sgmv_fused_sigma,
-    merge_fused, pool_bytes_for, extent_bytes, pack_adapter, Cache, sgmv_shrink_partials,
+    pool_bytes_for, extent_bytes, pack_adapter, Cache, sgmv_shrink_partials,
     sgmv_expand_partials, sgmv_expand_partials_sigma, sgmv_fused_static,
 )
 
 __all__ = ["Pool", "Plan", "sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_expand_sigma",
            "sgmv_fused_sigma", "sgmv_shrink_partials", "sgmv_expand_partials",
-           "sgmv_expand_partials_sigma", "sgmv_fused_static", "merge_fused",
+           "sgmv_expand_partials_sigma", "sgmv_fused_static",
            "pool_bytes_for", "extent_bytes", "pack_adapter", "Cache", "LoraError", "load"]

@@ -13,6 +13,7 @@ LORA_F32, LORA_BF16 = 0, 1
 LORA_MAX_PROJ = 8
 LORA_MAX_RANK = 64
 LORA_STATIC_SCRATCH_MIB = 64
+LORA_MAX_MERGE = 4
 
 STATUS = {0: "LORA_OK", -1: "LORA_EINVAL", -2: "LORA_ENOSPC", -3: "LORA_ENOENT",
           -4: "LORA_ERANK", -5: "LORA_EDTYPE", -6: "LORA_ESEG", -7: "LORA_EHIP",
@@ -70,6 +71,8 @@ SIGNATURES = {
     "lora_plan_create_sigma": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32p, _i32]),
     "lora_plan_create_weighted": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p,
                                          ctypes.POINTER(_f32), _i32]),
+    "lora_plan_create_merge": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32, _i32, _i32p,
+                                      ctypes.POINTER(_f32)]),
     "sgmv_expand_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,
                                  _vp, _i64, _vp]),
     "sgmv_fused_sigma": (_i32, [_vp, _vp, _i32, _i32, _i32p, _i32p, _vp, _i64, _vp, _i32, _i32,

@@ -329,6 +329,30 @@ class Plan:
         self.ws = None
         self.max_proj = 0
 
+    @classmethod
+    def merge(cls, pool: Pool, num_tokens: int, seg_starts, seg_adapters, seg_weights):
+        """A weighted merge of K adapters per request: seg_adapters and
+        seg_weights are [S][K] (adapter -1: an empty slot).  sgmv_fused with
+        this plan adds sum_k (w_k s_k) B_k (A_k x) in one pass."""
+        starts = np.ascontiguousarray(seg_starts, dtype=np.int32)
+        ads = np.ascontiguousarray(seg_adapters, dtype=np.int32)
+        wts = np.ascontiguousarray(seg_weights, dtype=np.float32)
+        if ads.ndim != 2 or wts.shape != ads.shape or starts.shape[0] != ads.shape[0] + 1:
+            raise ValueError("seg_adapters and seg_weights must be [S][K], seg_starts [S+1]")
+        self = cls.__new__(cls)
+        self.lib = pool.lib
+        self.pool = pool
+        self.num_tokens = int(num_tokens)
+        self._h = ctypes.c_void_p()
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        check(self.lib.lora_plan_create_merge(
+            ctypes.byref(self._h), pool.handle, self.num_tokens, starts.ctypes.data_as(i32p),
+            int(ads.shape[0]), int(ads.shape[1]), ads.ctypes.data_as(i32p),
+            wts.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+        self.ws = None
+        self.max_proj = 0
+        return self
+
     def rebuild(self, num_tokens: int, seg_starts, seg_adapter, seg_sigma=None, seg_weight=None):
         """Re-plan for the next batch over the same pool, in place (host
         tables and pinned staging reused); upload again before the next call."""
@@ -575,15 +599,4 @@ def sgmv_fused_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, si
                                     base.stride(0) if base is not None else 0,
                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
                                     _stream_handle(stream)))
-    return y
-
-
-def merge_fused(pool: Pool, plans, layer: int, projs, y_offsets, x, y, base=None, stream=None):
-    """Weighted merge of several adapters per request: ``plans`` are weighted
-    plans over the same tokens, one per merge slot; the first is applied over
-    ``base`` (or y), the others add their weighted deltas into y in turn:
-    y = y_in + sum_k (w_k s_k) B_k (A_k x)."""
-    for k, pl in enumerate(plans):
-        sgmv_fused(pool, pl, layer, projs, y_offsets, x, y, base if k == 0 else None,
-                   stream=stream)
     return y

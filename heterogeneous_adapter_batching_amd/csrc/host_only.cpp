@@ -19,5 +19,8 @@ hipError_t launch_expand(int, int, int, const ExpandArgs &, hipStream_t) {
 hipError_t launch_expand_decode(int, int, const ExpandArgs &, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t launch_expand_merge(int, int, const MergeArgs &, int, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 hipError_t static_scratch(void **, uint64_t *) { return hipErrorInvalidValue; }
 }  // namespace lora

@@ -1035,6 +1035,192 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     }
 }
 
+// Merge expand: y = y_in + sum_k (w_k s_k) B_k v_k for the tokens of a merge
+// block (at most kValuTokens tokens of one segment, so the same slot
+// adapters), slot by slot in order, in float32, rounded once.  A unit is
+// (block, projection, kWaves wave slices of rows) as in the decode expand;
+// lane owns rows o_lo + lane + 64 i (i < RPL).  For each slot the v of the
+// block's (token, slot) rows is gathered into LDS from the shrink's partials
+// (the one chunk order: thread (entry, way) sums one way, the ways are added
+// in order), the slot adapter's B rows stream in, and each lane adds the
+// slot's scaled dot products to its running outputs, which start at y_in.
+template <typename T, int NVM>
+__global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
+    constexpr int E = Elem<T>::E;
+    constexpr int RPL = decode_rpl(NVM);
+    constexpr int NT = kValuTokens;
+    constexpr int VS = LORA_MAX_RANK + 4;
+    __shared__ float vs[NT][VS];
+    __shared__ f32x4 ways[NT * LORA_MAX_RANK / 4][kSumWays];
+
+    warm_args<MergeArgs>();
+    const int u = xcd_unit(1);
+    if (u >= a.units) return;                        // whole workgroup
+    const int nproj = a.nproj;
+    const int lg = a.rows_log2;
+    int hout[LORA_MAX_PROJ], cnt[LORA_MAX_PROJ], upb = 0;
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_PROJ; ++i) {
+        hout[i] = a.h_out[i];
+        cnt[i] = i < nproj ? (hout[i] + (1 << lg) - 1) >> lg : 0;
+        upb += cnt[i];
+    }
+    const int b = u / upb;
+    const int rem = u - b * upb;
+    int p = 0, first = 0, run = 0;
+#pragma unroll
+    for (int i = 0; i < LORA_MAX_PROJ; ++i) {
+        if (i < nproj && rem >= run) { p = i; first = run; }
+        run += cnt[i];
+    }
+    const int slice = rem - first;
+    const MergeBlock mb = load_invariant(a.mblocks + b);
+    int h_out = hout[0];
+#pragma unroll
+    for (int i = 1; i < LORA_MAX_PROJ; ++i) h_out = p == i ? hout[i] : h_out;
+    const int wrows = 1 << (lg - 2);
+    const int o_lo = min(h_out, (slice * kWaves + wave_id()) * wrows);
+    const int o_hi = min(h_out, o_lo + wrows);
+    const int lane = threadIdx.x & 63;
+    const int tid = int(threadIdx.x);
+    const int yoff = a.y_off[p];
+
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
+    const int64_t ld_in = a.base ? a.ldb : a.ldy;
+    uint32_t in_row[NT], y_row[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const bool ok = t < mb.n_tok && mb.tok[t] >= 0;
+        in_row[t] = ok ? uint32_t((int64_t(mb.tok[t]) * ld_in + yoff) * sizeof(T)) : kOOB;
+        y_row[t] = ok ? uint32_t((int64_t(mb.tok[t]) * a.ldy + yoff) * sizeof(T)) : kOOB;
+    }
+    float acc[RPL][NT];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int row = o_lo + i * kWaveSize + lane;
+        const bool rok = row < o_hi;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+    }
+
+    const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
+    const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
+#pragma unroll
+    for (int k = 0; k < kMaxMerge; ++k) {
+        if (k >= mb.nslots) break;                   // wave-uniform
+        const MergeSlot sl = mb.slot[k];
+        if (sl.r_pad == 0) continue;                 // an empty slot: wave-uniform
+        // the v gather: thread (entry e, way kk), entry = 4 ranks of a token
+        const int quads = sl.r_pad / 4;
+        const int entries = mb.n_tok * quads;
+        const int kk = tid % kSumWays, e = tid / kSumWays;
+        const bool on = e < entries;
+        const int ti = on ? e / quads : 0;
+        const int j = on ? (e - ti * quads) * 4 : 0;
+        // the row's place in the partials, by selects (an indexed private
+        // array would be placed in memory)
+        const int rt = ti == 0 ? mb.rt[k][0] : ti == 1 ? mb.rt[k][1] : ti == 2 ? mb.rt[k][2]
+                                                                                : mb.rt[k][3];
+        const int ps = ti == 0 ? mb.ps[k][0] : ti == 1 ? mb.ps[k][1] : ti == 2 ? mb.ps[k][2]
+                                                                                : mb.ps[k][3];
+        const uint32_t off = on ? partial_off(rt, j, ps, p, a.nproj, a.c0, a.ptt) : 0u;
+        u32x4 part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = kk + i * kSumWays;
+            part[i] = bload16(pr, off_or_oob(on && c < a.c0, (off + uint32_t(c) * stride) * 4));
+        }
+        // the slot adapter's B rows
+        const uint32_t row_bytes = uint32_t(sl.r_pad) * sizeof(T);
+        const rsrc_t br = make_rsrc(a.slab + extent(sl.ext_lo, sl.ext_hi) +
+                                        uint64_t(sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
+                                    uint32_t(h_out) * row_bytes);
+        const int nv = sl.r_pad / E;
+        u32x4 bv[NVM][RPL];
+#pragma unroll
+        for (int v = 0; v < NVM; ++v)
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const int row = o_lo + i * kWaveSize + lane;
+                bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
+                                                  uint32_t(row) * row_bytes + v * 16));
+            }
+        // finish the gather in the one chunk order
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (kk + i * kSumWays < a.c0) s4 += __builtin_bit_cast(f32x4, part[i]);
+        for (int c = kk + 4 * kSumWays; c < a.c0; c += kSumWays)
+            s4 += __builtin_bit_cast(
+                f32x4, bload16(pr, off_or_oob(on, (off + uint32_t(c) * stride) * 4)));
+        if (on) ways[e][kk] = s4;
+        __syncthreads();
+        if (tid < entries) {
+            const int t2 = tid / quads, j2 = (tid - (tid / quads) * quads) * 4;
+            f32x4 w4 = ways[tid][0];
+#pragma unroll
+            for (int w = 1; w < kSumWays; ++w) w4 += ways[tid][w];
+            *reinterpret_cast<f32x4 *>(&vs[t2][j2]) = w4;
+        }
+        __syncthreads();
+        // this slot's dot products, added to the running outputs
+        float d[RPL][NT];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NVM; ++v) {
+            if (v < nv) {                            // wave-uniform
+                float f[RPL][E];
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    if constexpr (E == 8) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            f[i][2 * q] = bf16_lo(bv[v][i][q]);
+                            f[i][2 * q + 1] = bf16_hi(bv[v][i][q]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) f[i][q] = __uint_as_float(bv[v][i][q]);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    if (t < mb.n_tok) {              // wave-uniform
+                        float wv[E];
+#pragma unroll
+                        for (int q = 0; q < E; q += 4) {
+                            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + q]);
+                            wv[q] = w4[0]; wv[q + 1] = w4[1]; wv[q + 2] = w4[2]; wv[q + 3] = w4[3];
+                        }
+#pragma unroll
+                        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                            for (int q = 0; q < E; ++q)
+                                d[i][t] = __builtin_fmaf(f[i][q], wv[q], d[i][t]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[i][t] = acc[i][t] + sl.scale * d[i][t];
+        __syncthreads();                             // vs and ways are written again
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int row = o_lo + i * kWaveSize + lane;
+        const bool rok = row < o_hi;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)                 // y_row[t] is kOOB for absent tokens
+            Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB, acc[i][t]);
+    }
+}
+
 template <typename T, int TT, int KSM>
 __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     constexpr int E = Elem<T>::E;
@@ -1255,6 +1441,27 @@ hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStre
         else expand_decode_nvm<float, false>(nvm, grid, block, a, s);
     }
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t expand_merge_t(int nvm, dim3 grid, dim3 block, const MergeArgs &a, hipStream_t s) {
+    if (nvm <= 1) hipLaunchKernelGGL((k_expand_merge<T, 1>), grid, block, 0, s, a);
+    else if (nvm <= 2) hipLaunchKernelGGL((k_expand_merge<T, 2>), grid, block, 0, s, a);
+    else if (nvm <= 4) hipLaunchKernelGGL((k_expand_merge<T, 4>), grid, block, 0, s, a);
+    else if (nvm <= 8) hipLaunchKernelGGL((k_expand_merge<T, 8>), grid, block, 0, s, a);
+    else if constexpr (sizeof(T) == 4) hipLaunchKernelGGL((k_expand_merge<T, 16>), grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid, hipStream_t s) {
+    if (a.units <= 0) return hipSuccess;
+    const dim3 g(grid), block(kWaves * kWaveSize);
+    if (dtype == LORA_BF16) {
+        if (nvm > 8) return hipErrorInvalidValue;
+        return expand_merge_t<uint16_t>(nvm, g, block, a, s);
+    }
+    if (nvm > 16) return hipErrorInvalidValue;
+    return expand_merge_t<float>(nvm, g, block, a, s);
 }
 
 hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s) {

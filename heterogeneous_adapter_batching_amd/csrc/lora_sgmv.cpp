@@ -44,6 +44,13 @@ lora_status hip_fail(hipError_t e, const char *what) {
 
 uint64_t round_up(uint64_t v, uint64_t m) { return (v + m - 1) / m * m; }
 
+// n items cut into ceil(n / m) near-equal parts (the first n % k one larger)
+void cut_sizes(int32_t n, int32_t m, std::vector<int32_t> *sizes) {
+    sizes->clear();
+    const int32_t k = (n + m - 1) / m;
+    for (int32_t i = 0; i < k; ++i) sizes->push_back(n / k + (i < n % k ? 1 : 0));
+}
+
 int32_t esize(int32_t dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 
 lora_status check_desc(const lora_pool_desc *d) {
@@ -153,14 +160,14 @@ struct lora_pool {
 // Sizes a plan's device image is laid out from: tokens, expand blocks, rank
 // tiles, 16-token tiles of the largest block.
 struct PlanCounts {
-    int64_t T = 0, nb = 0, rt = 0;
-    int32_t tt = 1;
+    int64_t T = 0, nb = 0, rt = 0, mb = 0;   // rows (tokens, or (token, slot) rows), blocks,
+    int32_t tt = 1;                          // rank tiles, merge blocks; tiles per block
 };
 
 // Byte offsets of the tables in a plan workspace, and its size.
 struct PlanLayout {
     uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
-             off_tw = 0, off_part = 0;
+             off_tw = 0, off_mblocks = 0, off_part = 0;
     uint64_t image_bytes = 0, part_bytes = 0, ws_bytes = 0;
 };
 
@@ -207,6 +214,7 @@ PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp,
     L.off_ttok = o;    o = round_up(o + 4ull * lora::kMaxBlockTokens * rt, 256);
     L.off_tsig = o;    o = round_up(o + 4ull * T, 256);
     L.off_tw = o;      o = round_up(o + 4ull * T, 256);
+    L.off_mblocks = o; o = round_up(o + sizeof(lora::MergeBlock) * uint64_t(c.mb), 256);
     L.image_bytes = o;
     L.part_bytes = 4ull * max_shrink_units(d, c.rt, c.tt, mp, bound) * c.tt * lora::kTile *
                    lora::kTile;
@@ -224,7 +232,10 @@ struct lora_plan {
     std::vector<int32_t> token_order;    // plan order: grouped adapter tokens, then the rest
     std::vector<int32_t> token_sigma;    // core index per plan-order row (-1: none)
     std::vector<float> token_weight;     // weight per plan-order row (weighted plans)
+    std::vector<int32_t> token_slot;     // merge slot per plan-order row (-1: none)
     bool weighted = false;
+    int32_t merge_k = 0;                 // slots per segment of a merge plan (0: not one)
+    std::vector<lora::MergeBlock> mblocks;
     int32_t max_sigma = -1;              // largest core index named
     std::vector<int32_t> token_group;    // per token row
     std::vector<int32_t> group_adapter, group_rank;
@@ -255,9 +266,11 @@ struct lora_plan {
 
     int32_t rt_total() const { return int32_t(tiles.size()); }
     int32_t nb_all() const { return int32_t(blocks.size()); }
+    int32_t rows() const { return int32_t(token_order.size()); }
     PlanCounts counts() const {
         PlanCounts c;
-        c.T = T;
+        c.T = rows();
+        c.mb = int64_t(mblocks.size());
         c.nb = nb_all();
         c.rt = rt_total();
         c.tt = tt;
@@ -572,52 +585,64 @@ lora_status check_segments(const lora_pool *p, int32_t T, const int32_t *seg_sta
     return LORA_OK;
 }
 
-// Builds the plan of a checked segment table into `pl`, replacing what it
-// held (its device image and staging buffers are kept).
-void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg_starts,
-                const int32_t *seg_adapter, const int32_t *seg_sigma, const float *seg_weight,
-                int32_t S) {
+// One run of token rows [start, end) under one adapter: a segment of a plain
+// plan, or one (segment, slot) of a merge plan.  Rows of several runs may
+// coincide in a merge plan (a token's rows of different slots).
+struct Run {
+    int32_t start, end, adapter, slot, sigma;
+    float weight;
+};
+
+// Builds the plan of checked runs into `pl`, replacing what it held (its
+// device image and staging buffers are kept).  `weighted`: the runs carry
+// weights (else every weight is 1 and the plan has none).
+void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<Run> &runs,
+                bool weighted) {
     pl->pool = p;
     pl->pool_generation = p->generation;
     pl->T = T;
     pl->token_order.clear();
     pl->token_sigma.clear();
     pl->token_weight.clear();
+    pl->token_slot.clear();
     pl->weighted = false;
     pl->max_sigma = -1;
     pl->group_adapter.clear();
     pl->group_rank.clear();
     pl->blocks.clear();
     pl->tiles.clear();
+    pl->mblocks.clear();
+    pl->merge_k = 0;
     pl->nb_long = pl->nb_act = pl->n_active = pl->max_block = pl->max_rpad = 0;
     pl->tt = 1;
     pl->token_group.assign(T, -1);
 
-    // groups in first-appearance order (segments with tokens only)
+    // groups in first-appearance order (runs with rows only); a member is a
+    // (row, run) pair
     std::unordered_map<int32_t, int32_t> gidx;
-    std::vector<std::vector<int32_t>> members;
-    for (int32_t s = 0; s < S; ++s) {
-        const int32_t id = seg_adapter[s];
-        if (id < 0 || seg_starts[s + 1] == seg_starts[s]) continue;
-        auto it = gidx.find(id);
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> members;
+    for (int32_t r = 0; r < int32_t(runs.size()); ++r) {
+        const Run &rn = runs[r];
+        if (rn.adapter < 0 || rn.end == rn.start) continue;
+        auto it = gidx.find(rn.adapter);
         int32_t g;
         if (it == gidx.end()) {
             g = int32_t(members.size());
-            gidx.emplace(id, g);
+            gidx.emplace(rn.adapter, g);
             members.emplace_back();
-            pl->group_adapter.push_back(id);
-            pl->group_rank.push_back(p->slots.at(id).rank);
+            pl->group_adapter.push_back(rn.adapter);
+            pl->group_rank.push_back(p->slots.at(rn.adapter).rank);
         } else {
             g = it->second;
         }
-        for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) {
-            members[g].push_back(t);
-            pl->token_group[t] = g;
+        for (int32_t t = rn.start; t < rn.end; ++t) {
+            members[g].emplace_back(t, r);
+            if (pl->token_group[t] < 0) pl->token_group[t] = g;
         }
     }
-    std::vector<int32_t> idle;
+    std::vector<std::pair<int32_t, int32_t>> idle;
     for (int32_t t = 0; t < T; ++t)
-        if (pl->token_group[t] < 0) idle.push_back(t);
+        if (pl->token_group[t] < 0) idle.emplace_back(t, -1);
 
     // Two levels of blocks.  Shrink blocks: each group cut into near-equal
     // blocks of at most one 16-token tile (64 tokens, 4 tiles, for a long
@@ -633,20 +658,16 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg
         if (m.size() >= size_t(lora::kLongGroup)) long_tokens += m.size();
     const bool use_long = long_tokens >= size_t(lora::kMinLongTokens);
     std::vector<BlockDesc> long_blocks, short_blocks;
-    auto cut = [](int32_t n, int32_t m, std::vector<int32_t> *sizes) {
-        sizes->clear();
-        const int32_t k = (n + m - 1) / m;
-        for (int32_t i = 0; i < k; ++i) sizes->push_back(n / k + (i < n % k ? 1 : 0));
-    };
     int32_t max_sblock = 0;
     std::vector<int32_t> ssz, esz;
-    auto add_group = [&](const std::vector<int32_t> &toks, int32_t g, const Slot *sl) {
+    auto add_group = [&](const std::vector<std::pair<int32_t, int32_t>> &rows, int32_t g,
+                         const Slot *sl) {
         const int32_t base = int32_t(pl->token_order.size());
         const int32_t rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
-        const bool lg = sl && use_long && toks.size() >= size_t(lora::kLongGroup);
+        const bool lg = sl && use_long && rows.size() >= size_t(lora::kLongGroup);
         const int32_t smax = lg ? lora::kMaxBlockTokens : lora::kTile;
         const int32_t emax = lg ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
-        cut(int32_t(toks.size()), smax, &ssz);
+        cut_sizes(int32_t(rows.size()), smax, &ssz);
         int32_t s0 = 0;
         for (int32_t sn : ssz) {
             const int32_t rt_before = int32_t(pl->tiles.size());
@@ -662,7 +683,7 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg
                 pl->tiles.push_back(td);
             }
             max_sblock = std::max(max_sblock, sn);
-            cut(sn, emax, &esz);
+            cut_sizes(sn, emax, &esz);
             int32_t e0 = 0;
             for (int32_t en : esz) {
                 BlockDesc bd{};
@@ -680,7 +701,14 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg
             }
             s0 += sn;
         }
-        pl->token_order.insert(pl->token_order.end(), toks.begin(), toks.end());
+        for (const auto &m : rows) {
+            pl->token_order.push_back(m.first);
+            const Run *rn = m.second >= 0 ? &runs[m.second] : nullptr;
+            pl->token_sigma.push_back(rn ? rn->sigma : -1);
+            pl->token_weight.push_back(rn ? rn->weight : 1.0f);
+            pl->token_slot.push_back(rn ? rn->slot : -1);
+            if (rn) pl->max_sigma = std::max(pl->max_sigma, rn->sigma);
+        }
     };
     for (int32_t g = 0; g < int32_t(members.size()); ++g)
         add_group(members[g], g, &p->slots.at(pl->group_adapter[g]));
@@ -701,24 +729,71 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg
         pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
     const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
-    // each row's core, in plan order
-    std::vector<int32_t> row_sigma(T, -1);
-    if (seg_sigma)
-        for (int32_t s = 0; s < S; ++s)
-            for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) row_sigma[t] = seg_sigma[s];
-    pl->token_sigma.resize(T);
-    for (int32_t i = 0; i < T; ++i) {
-        pl->token_sigma[i] = row_sigma[pl->token_order[i]];
-        pl->max_sigma = std::max(pl->max_sigma, pl->token_sigma[i]);
+    pl->weighted = weighted;
+    if (!weighted) pl->token_weight.clear();
+}
+
+// The runs of a plain segment table (optional cores and weights).
+std::vector<Run> segment_runs(const int32_t *seg_starts, const int32_t *seg_adapter,
+                              const int32_t *seg_sigma, const float *seg_weight, int32_t S) {
+    std::vector<Run> runs(S);
+    for (int32_t s = 0; s < S; ++s)
+        runs[s] = Run{seg_starts[s], seg_starts[s + 1], seg_adapter[s], -1,
+                      seg_sigma ? seg_sigma[s] : -1, seg_weight ? seg_weight[s] : 1.0f};
+    return runs;
+}
+
+// The merge blocks of a merge plan built from `runs` (segment s, slot k is run
+// s * K + k): each segment cut into blocks of at most kValuTokens tokens,
+// each (token, slot) row located in the shrink's partials.
+void build_merge_blocks(lora_plan *pl, const lora_pool *p, int32_t T, const int32_t *seg_starts,
+                        int32_t S, int32_t K, const std::vector<Run> &runs) {
+    pl->merge_k = K;
+    // row (t, k) -> (first rank tile of its shrink block, slot in the block)
+    std::vector<int32_t> loc_rt(size_t(T) * K, -1), loc_ps(size_t(T) * K, 0);
+    for (int32_t ti = 0; ti < pl->rt_total(); ++ti) {
+        const lora::TileDesc &td = pl->tiles[ti];
+        if (td.tile != 0) continue;                  // the first tile names the block
+        for (int32_t j = 0; j < td.n_tok; ++j) {
+            const int32_t q = td.tok_off + j;
+            const size_t key = size_t(pl->token_order[q]) * K + pl->token_slot[q];
+            loc_rt[key] = ti;
+            loc_ps[key] = j;
+        }
     }
-    // and each row's weight, in plan order
-    if (seg_weight) {
-        std::vector<float> row_weight(T, 1.0f);
-        for (int32_t s = 0; s < S; ++s)
-            for (int32_t t = seg_starts[s]; t < seg_starts[s + 1]; ++t) row_weight[t] = seg_weight[s];
-        pl->weighted = true;
-        pl->token_weight.resize(T);
-        for (int32_t i = 0; i < T; ++i) pl->token_weight[i] = row_weight[pl->token_order[i]];
+    std::vector<int32_t> sizes;
+    for (int32_t s = 0; s < S; ++s) {
+        const int32_t n = seg_starts[s + 1] - seg_starts[s];
+        if (n == 0) continue;
+        lora::MergeBlock proto{};
+        proto.nslots = K;
+        for (int32_t k = 0; k < K; ++k) {
+            const Run &rn = runs[size_t(s) * K + k];
+            lora::MergeSlot &ms = proto.slot[k];
+            if (rn.adapter < 0) continue;            // r_pad 0: empty
+            const Slot &sl = p->slots.at(rn.adapter);
+            ms.ext_lo = uint32_t(sl.off & 0xffffffffu);
+            ms.ext_hi = uint32_t(sl.off >> 32);
+            ms.r_pad = sl.r_pad;
+            ms.scale = rn.weight * sl.scale;
+            pl->max_rpad = std::max(pl->max_rpad, sl.r_pad);
+        }
+        cut_sizes(n, lora::kValuTokens, &sizes);
+        int32_t t0 = seg_starts[s];
+        for (int32_t sz : sizes) {
+            lora::MergeBlock mb = proto;
+            mb.n_tok = sz;
+            for (int32_t i = 0; i < lora::kValuTokens; ++i) {
+                mb.tok[i] = i < sz ? t0 + i : -1;
+                for (int32_t k = 0; k < lora::kMaxMerge; ++k) {
+                    const bool live = i < sz && k < K && mb.slot[k].r_pad > 0;
+                    mb.rt[k][i] = live ? loc_rt[size_t(t0 + i) * K + k] : 0;
+                    mb.ps[k][i] = live ? loc_ps[size_t(t0 + i) * K + k] : 0;
+                }
+            }
+            pl->mblocks.push_back(mb);
+            t0 += sz;
+        }
     }
 }
 
@@ -729,7 +804,8 @@ lora_status plan_create(lora_plan **out, const lora_pool *p, int32_t T, const in
     lora_status st = check_segments(p, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
     if (st != LORA_OK) return st;
     lora_plan *pl = new lora_plan();
-    plan_build(pl, p, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
+    plan_build(pl, p, T, segment_runs(seg_starts, seg_adapter, seg_sigma, seg_weight, S),
+               seg_weight != nullptr);
     *out = pl;
     return LORA_OK;
 }
@@ -768,6 +844,39 @@ lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t 
     return plan_create(out, p, T, seg_starts, seg_adapter, seg_sigma, nullptr, S);
 }
 
+lora_status lora_plan_create_merge(lora_plan **out, const lora_pool *p, int32_t T,
+                                   const int32_t *seg_starts, int32_t S, int32_t K,
+                                   const int32_t *seg_adapters, const float *seg_weights) {
+    if (!out) return fail(LORA_EINVAL, "null output pointer");
+    if (K < 1 || K > LORA_MAX_MERGE)
+        return fail(LORA_EINVAL, "%d slots per segment not in 1..%d", K, LORA_MAX_MERGE);
+    if (S > 0 && (!seg_adapters || !seg_weights))
+        return fail(LORA_EINVAL, "null slot table");
+    if (S < 0) return fail(LORA_ESEG, "negative segment count");
+    // each slot's column checked as a segment table of its own
+    std::vector<int32_t> col_a(std::max(S, 1));
+    std::vector<float> col_w(std::max(S, 1));
+    for (int32_t k = 0; k < K; ++k) {
+        for (int32_t s2 = 0; s2 < S; ++s2) {
+            col_a[s2] = seg_adapters[size_t(s2) * K + k];
+            col_w[s2] = seg_weights[size_t(s2) * K + k];
+        }
+        lora_status st = check_segments(p, T, seg_starts, col_a.data(), nullptr, col_w.data(), S);
+        if (st != LORA_OK) return st;
+    }
+    std::vector<Run> runs(size_t(S) * K);
+    for (int32_t s2 = 0; s2 < S; ++s2)
+        for (int32_t k = 0; k < K; ++k)
+            runs[size_t(s2) * K + k] = Run{seg_starts[s2], seg_starts[s2 + 1],
+                                           seg_adapters[size_t(s2) * K + k], k, -1,
+                                           seg_weights[size_t(s2) * K + k]};
+    lora_plan *pl = new lora_plan();
+    plan_build(pl, p, T, runs, true);
+    build_merge_blocks(pl, p, T, seg_starts, S, K, runs);
+    *out = pl;
+    return LORA_OK;
+}
+
 lora_status lora_plan_rebuild(lora_plan *pl, int32_t T, const int32_t *seg_starts,
                               const int32_t *seg_adapter, const int32_t *seg_sigma,
                               const float *seg_weight, int32_t S) {
@@ -775,7 +884,8 @@ lora_status lora_plan_rebuild(lora_plan *pl, int32_t T, const int32_t *seg_start
     lora_status st = check_segments(pl->pool, T, seg_starts, seg_adapter, seg_sigma, seg_weight,
                                      S);
     if (st != LORA_OK) return st;
-    plan_build(pl, pl->pool, T, seg_starts, seg_adapter, seg_sigma, seg_weight, S);
+    plan_build(pl, pl->pool, T, segment_runs(seg_starts, seg_adapter, seg_sigma, seg_weight, S),
+               seg_weight != nullptr);
     pl->ws = nullptr;                  // the new tables are not on the device yet
     pl->part_layer = -1;
     return LORA_OK;
@@ -855,10 +965,13 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
     }
     uint8_t *img = static_cast<uint8_t *>(pl->staging[k]);
     std::memset(img, 0, lay.image_bytes);
-    if (pl->T) std::memcpy(img + lay.off_tok, pl->token_order.data(), 4ull * pl->T);
-    if (pl->T) std::memcpy(img + lay.off_tsig, pl->token_sigma.data(), 4ull * pl->T);
-    if (pl->T && pl->weighted)
-        std::memcpy(img + lay.off_tw, pl->token_weight.data(), 4ull * pl->T);
+    const uint64_t R = uint64_t(pl->rows());
+    if (R) std::memcpy(img + lay.off_tok, pl->token_order.data(), 4ull * R);
+    if (R) std::memcpy(img + lay.off_tsig, pl->token_sigma.data(), 4ull * R);
+    if (R && pl->weighted) std::memcpy(img + lay.off_tw, pl->token_weight.data(), 4ull * R);
+    if (!pl->mblocks.empty())
+        std::memcpy(img + lay.off_mblocks, pl->mblocks.data(),
+                    sizeof(lora::MergeBlock) * pl->mblocks.size());
     if (!pl->blocks.empty())
         std::memcpy(img + lay.off_blocks, pl->blocks.data(), sizeof(BlockDesc) * pl->blocks.size());
     if (!pl->tiles.empty())
@@ -910,6 +1023,7 @@ lora_status lora_plan_stats(const lora_plan *pl, int32_t *ng, int32_t *nb, int32
 lora_status lora_plan_export(const lora_plan *pl, int32_t *order, int32_t *tgroup,
                              int32_t *gad, int32_t *grank) {
     if (!pl) return fail(LORA_EINVAL, "null plan");
+    if (pl->merge_k) return fail(LORA_EINVAL, "a merge plan has a row per (token, slot): no export");
     if (order && pl->T) std::memcpy(order, pl->token_order.data(), 4ull * pl->T);
     if (tgroup && pl->T) std::memcpy(tgroup, pl->token_group.data(), 4ull * pl->T);
     const size_t G = pl->group_adapter.size();
@@ -1129,12 +1243,55 @@ struct Cores {
 
 // Checks the core table of a call against the plan and pool.
 lora_status check_cores(const lora_plan *pl, const Cores &c) {
+    if (pl->merge_k) return fail(LORA_EINVAL, "a merge plan takes no cores");
     if (c.kind != LORA_SIGMA_DIAG && c.kind != LORA_SIGMA_FULL)
         return fail(LORA_EINVAL, "core kind %d is neither diagonal nor full", c.kind);
     if (!c.sigma || !aligned16(c.sigma))
         return fail(LORA_EINVAL, "core table must be non-null and 16-byte aligned");
     if (c.count < 0 || pl->max_sigma >= c.count)
         return fail(LORA_EINVAL, "plan names core %d of a table of %d", pl->max_sigma, c.count);
+    return LORA_OK;
+}
+
+// The merge expand of a merge plan: y = y_in + sum_k (w_k s_k) B_k v_k per
+// token, one launch over the merge blocks (decode geometry for the plan's
+// largest padded rank).
+lora_status run_expand_merge(const lora_pool *p, const lora_plan *pl, int32_t layer,
+                             int32_t nproj, const int32_t *projs, const int32_t *yoff,
+                             int32_t c0, void *y, int64_t ldy, const void *base, int64_t ldb,
+                             hipStream_t st, const Partials &pt) {
+    if (pl->mblocks.empty()) return LORA_OK;
+    lora::MergeArgs a{};
+    const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
+    const int32_t es = esize(p->d.dtype);
+    a.slab = p->slab;
+    a.mblocks = reinterpret_cast<const lora::MergeBlock *>(ws + pl->lay.off_mblocks);
+    a.partial = pt.ptr;
+    a.partial_bytes = uint32_t(std::min<uint64_t>(pt.bytes, lora::kMaxTensorBytes));
+    a.y = y;
+    a.base = base;
+    a.ldy = ldy;
+    a.ldb = ldb;
+    for (int i = 0; i < nproj; ++i) {
+        a.coef_b[i] = p->coef_b(layer, projs[i]);
+        a.h_out[i] = p->d.h_out[projs[i]];
+        a.y_off[i] = yoff[i];
+    }
+    a.nproj = nproj;
+    a.c0 = c0;
+    a.ptt = pl->tt;
+    const int32_t rmax = std::max(pl->max_rpad, 8);
+    a.rows_log2 = lora::decode_unit_rows_log2(rmax, es);
+    int32_t upb = 0;
+    for (int i = 0; i < nproj; ++i) upb += (a.h_out[i] + (1 << a.rows_log2) - 1) >> a.rows_log2;
+    const int64_t units = int64_t(pl->mblocks.size()) * upb;
+    if (units > INT32_MAX / 2) return fail(LORA_EINVAL, "merge call too large: split the batch");
+    a.units = int32_t(units);
+    a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, es));
+    a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, es)) : 0u;
+    const hipError_t e = lora::launch_expand_merge(p->d.dtype, lora::decode_nvt(rmax, es), a,
+                                                   grid_for(a.units, 1), st);
+    if (e != hipSuccess) return hip_fail(e, "merge expand launch");
     return LORA_OK;
 }
 
@@ -1145,6 +1302,8 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
                        int64_t ldv, void *y, int64_t ldy, const void *base, int64_t ldb,
                        hipStream_t st, const Cores &cores = Cores(),
                        const Partials *pt = nullptr) {
+    if (pl->merge_k) return run_expand_merge(p, pl, layer, nproj, projs, yoff, c0, y, ldy, base,
+                                             ldb, st, pt ? *pt : workspace_partials(pl));
     const int32_t nb = base ? pl->nb_all() : pl->nb_act;
     if (nb == 0) return LORA_OK;
     lora::ExpandArgs a{};
@@ -1254,6 +1413,9 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     CallCheck cc;
     lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
     if (st != LORA_OK) return st;
+    if (pl->merge_k)
+        return fail(LORA_EINVAL, "a merge plan's v has a row per (token, slot): use sgmv_fused "
+                                 "or the partials calls");
     if (pl->T == 0) return LORA_OK;   // empty batch: nothing to read or write
     if (!x || !aligned16(x)) return fail(LORA_EINVAL, "x must be non-null and 16-byte aligned");
     if (ldx < cc.h_in || ldx % 8) return fail(LORA_EINVAL, "ldx %lld < h_in or not a multiple of 8",
@@ -1276,6 +1438,9 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     CallCheck cc;
     lora_status st = check_call(p, pl, layer, nproj, projs, &cc);
     if (st != LORA_OK) return st;
+    if (pl->merge_k)
+        return fail(LORA_EINVAL, "a merge plan's v has a row per (token, slot): use sgmv_fused "
+                                 "or the partials calls");
     if (pl->T == 0) return LORA_OK;   // empty batch: nothing to read or write
     if (!v || !aligned16(v)) return fail(LORA_EINVAL, "v must be non-null and 16-byte aligned");
     if (ldv < int64_t(nproj) * p->d.r_max || ldv % 4)

@@ -178,6 +178,54 @@ struct ExpandArgs {
     int32_t cls_rb[kMaxClasses];
 };
 
+// Weighted merge of several adapters per request, in one pass: the shrink
+// runs over every (token, slot) row as over the tokens of a plain plan (a
+// row is the token's x row, grouped under its slot's adapter); the merge
+// expand takes blocks of at most kValuTokens tokens of one segment (so the
+// same slot adapters) and forms y = y_in + sum_k (w_k s_k) B_k v_k in float32,
+// slot by slot in order, rounding y once.
+constexpr int kMaxMerge = LORA_MAX_MERGE;
+
+struct MergeSlot {
+    uint32_t ext_lo, ext_hi;   // the slot adapter's extent
+    int32_t r_pad;             // its padded rank; 0: an empty slot
+    float scale;               // w * s, rounded to float32 once
+};
+
+struct MergeBlock {
+    int32_t tok[kValuTokens];  // token rows, -1 padded
+    int32_t n_tok;
+    int32_t nslots;            // slots of the block's segment (<= kMaxMerge)
+    int32_t pad[2];
+    MergeSlot slot[kMaxMerge];
+    // where row (token i, slot k) sits in the shrink's partials: the first
+    // rank tile of its shrink block and its token slot in that block
+    int32_t rt[kMaxMerge][kValuTokens];
+    int32_t ps[kMaxMerge][kValuTokens];
+};
+static_assert(sizeof(MergeBlock) == 224, "MergeBlock is 224 bytes");
+
+struct MergeArgs {
+    const uint8_t *slab;
+    const MergeBlock *mblocks;
+    const float *partial;
+    void *y;
+    const void *base;            // nullable: y_in = base, else y_in = y
+    int64_t ldy;
+    int64_t ldb;
+    int64_t coef_b[LORA_MAX_PROJ];
+    int32_t h_out[LORA_MAX_PROJ];
+    int32_t y_off[LORA_MAX_PROJ];
+    int32_t nproj;
+    int32_t c0;
+    int32_t ptt;
+    int32_t units;
+    int32_t rows_log2;           // output rows of a unit (kWaves wave slices)
+    uint32_t partial_bytes;
+    uint32_t y_bytes;
+    uint32_t base_bytes;
+};
+
 // Decode expand geometry.  A B row of r_pad elements is nv 16-byte vectors;
 // the kernel is built for nvt = nv rounded up to a power of two, and a lane
 // owns decode_rpl(nvt) rows of a step: 2 rows up to 64-byte rows, 1 row
@@ -230,6 +278,8 @@ hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStre
 // decode expand (every block of the plan within kValuTokens tokens)
 // nvm: the largest decode_nvt of the launch's rank classes
 hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s);
+// merge expand; nvm: the largest decode_nvt of the plan's slot adapters
+hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid, hipStream_t s);
 
 // The library's static device scratch (sgmv_fused_static): the address of
 // the current device's copy, found once per device, and its size in bytes.

@@ -82,6 +82,7 @@ typedef enum { LORA_SIGMA_DIAG = 1, LORA_SIGMA_FULL = 2 } lora_sigma_kind;
 
 #define LORA_MAX_PROJ 8   /* adapted projections per pool (q, k, v, o, gate, up, down, ...) */
 #define LORA_MAX_RANK 64  /* largest supported r_max */
+#define LORA_MAX_MERGE 4  /* adapters merged per request (lora_plan_create_merge) */
 
 /* Shape of a pool: every adapter carries A and B for each (layer, projection). */
 typedef struct {
@@ -305,16 +306,33 @@ lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_to
 
 /* The same with a weight per segment: every call with this plan scales a
  * token's delta by its segment's weight (with the adapter's scale s: y = y_in
- * + (w * s) * B (A x), the product w * s rounded to float32 once).  This is
- * one slot of a weighted merge of adapters per request ("predibase/lorax":
- * adapters merged per request into a weighted ensemble, read as the linear
- * merge sum_k w_k s_k B_k A_k): a merge of K adapters is K weighted plans
- * over the same segments, applied in turn (the first with base, the rest
- * adding into y).  Errors as lora_plan_create, and LORA_EINVAL for a weight
- * that is not finite. */
+ * + (w * s) * B (A x), the product w * s rounded to float32 once): one
+ * weighted adapter per request.  Errors as lora_plan_create, and LORA_EINVAL
+ * for a weight that is not finite. */
 lora_status lora_plan_create_weighted(lora_plan **out, const lora_pool *p, int32_t num_tokens,
                                       const int32_t *seg_starts, const int32_t *seg_adapter,
                                       const float *seg_weight, int32_t num_segs);
+
+/* A weighted merge of several adapters per request ("predibase/lorax"
+ * repository listing, feature list: adapters merged per request with
+ * weighted merge strategies; "Lorax" tool listing, pros: per-request merges
+ * into ensembles), read as the linear merge
+ *     y = y_in + sum_k (w_k s_k) B_k (A_k x)
+ * (the pages name no other strategy).  Segment s carries num_slots (K <=
+ * LORA_MAX_MERGE) slots: adapter seg_adapters[s * K + k] (-1: an empty slot)
+ * with weight seg_weights[s * K + k]; w_k s_k is rounded to float32 once.
+ * sgmv_fused, sgmv_fused_static and the partials calls run it in one pass:
+ * one shrink over every (token, slot) row, grouped by adapter, then one
+ * expand that sums the K weighted deltas of each token in float32, slot by
+ * slot in order, onto y_in, and rounds y once (y is read and written once).
+ * A token whose slots are all empty keeps y_in.  The calls through a
+ * caller's v (sgmv_shrink, sgmv_expand) and the core calls refuse a merge
+ * plan (LORA_EINVAL), and so does lora_plan_export.  Errors as
+ * lora_plan_create, and LORA_EINVAL for K out of range or a weight that is
+ * not finite. */
+lora_status lora_plan_create_merge(lora_plan **out, const lora_pool *p, int32_t num_tokens,
+                                   const int32_t *seg_starts, int32_t num_segs, int32_t num_slots,
+                                   const int32_t *seg_adapters, const float *seg_weights);
 
 /* The same for jointly compressed adapters ("Compress then Serve", rebuttal
  * pseudocode of add_lora_slice_with_sigma): seg_adapter names the pool entry
@@ -351,7 +369,9 @@ uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj);
 /* An upper bound of lora_plan_workspace_bytes for every plan over pool `p`
  * of at most num_tokens tokens and num_segs segments, for calls of up to
  * `max_proj` projections: one workspace of this size serves every batch of a
- * serving loop, allocated once.  0 on a bad argument. */
+ * serving loop, allocated once.  (For a merge plan count a token per
+ * (token, non-empty slot) and a segment per (segment, slot).)  0 on a bad
+ * argument. */
 uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t num_segs,
                               int32_t max_proj);
 

@@ -741,29 +741,30 @@ def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=
     seg_ad[:, 0] = w.seg_adapter                            # slot 0: the batch's own draw
     seg_w = g.uniform(-1.0, 1.5, (S, K)).astype(np.float32)
     dw = DeviceWorkload(w, upload=np.arange(n_adapters), threads=4)
-    plans = []
-    for k in range(K):
-        pl = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, seg_ad[:, k], seg_weight=seg_w[:, k])
-        pl.upload(1)
-        plans.append(pl)
-    return w, dw, plans, seg_ad, seg_w
+    plan = hab.Plan.merge(dw.pool, w.num_tokens, w.seg_starts, seg_ad, seg_w).upload(1)
+    return w, dw, plan, seg_ad, seg_w
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("prefill", [False, True])
-def test_merge_parity(dtype, prefill):
-    """K = 3 adapters merged per request with weights (one weighted plan per
-    slot, applied in turn) against the oracle's merge."""
+@pytest.mark.parametrize("K", [3, 4])
+def test_merge_parity(dtype, prefill, K):
+    """K adapters merged per request with weights, in one pass (one shrink
+    over every (token, slot) row, one expand that sums the weighted deltas
+    and rounds y once), against the oracle's merge: the contract tolerance,
+    and the delta within the float32 accumulation bound plus a single
+    rounding of y; the fused, static-scratch and split calls agree bit for
+    bit."""
     import heterogeneous_adapter_batching_amd as hab
-    seed = (31 if dtype == "bf16" else 32) + (10 if prefill else 0)
-    w, dw, plans, seg_ad, seg_w = _merge_setup(seed, K=3, dtype=dtype,
-                                               T=1300 if prefill else 64,
-                                               max_seg=400 if prefill else 3)
-    log(f"[parity] merge {w.name} {dtype} prefill {prefill}")
-    assert (plans[0].stats()["max_block_tokens"] > 4) == prefill
+    seed = (31 if dtype == "bf16" else 32) + (10 if prefill else 0) + 100 * (K - 3)
+    w, dw, plan, seg_ad, seg_w = _merge_setup(seed, K=K, dtype=dtype,
+                                              T=1300 if prefill else 64,
+                                              max_seg=400 if prefill else 3)
+    log(f"[parity] merge {w.name} K={K} {dtype} prefill {prefill} {plan.stats()}")
+    assert (plan.stats()["max_block_tokens"] > 4) == prefill
     x = dw.x[(0, "x")]
     y = torch.zeros_like(dw.y[(0, 0)])
-    hab.merge_fused(dw.pool, plans, 0, (0,), [0], x, y, dw.base[(0, 0)])
+    hab.sgmv_fused(dw.pool, plan, 0, (0,), [0], x, y, dw.base[(0, 0)])
     torch.cuda.synchronize()
     adapters = {}
     for a in range(w.pool_size):
@@ -774,19 +775,53 @@ def test_merge_parity(dtype, prefill):
                                   y_in, acc="f64", threads=4)
     got = from_device(y).astype(np.float64)
     contract_check(got, ref, f"merge {w.name}")
-    # the delta alone: y is rounded to the output type once per slot, each
-    # rounding at most 2^-8 (bf16) or 2^-24 (f32) of the partial sum it
-    # rounds, which the oracle gives for slots 0..k
     ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
     d_ref = ref - y_in
-    lim = 1e-4 * np.abs(d_ref).max() + 1e-30
-    for k in range(1, seg_ad.shape[1] + 1):
-        part = ref if k == seg_ad.shape[1] else oracle.lora_delta_merge(
-            w.activation(0, "x"), w.seg_starts, seg_ad[:, :k], seg_w[:, :k], adapters,
-            y_in, acc="f64", threads=4)
-        lim = lim + ulp * np.abs(part)
-    err = np.abs((got - y_in) - d_ref)
+    lim = 1e-4 * np.abs(d_ref).max() + ulp * np.abs(ref) + 1e-30
+    err = np.abs(got - ref)
     assert np.all(err <= lim), float((err / lim).max())
+    # the same bits from the other entry points
+    y2 = torch.zeros_like(y)
+    hab.sgmv_fused_static(dw.pool, plan, 0, (0,), [0], x, y2, dw.base[(0, 0)])
+    y3 = torch.zeros_like(y)
+    hab.sgmv_shrink_partials(dw.pool, plan, 0, (0,), x)
+    hab.sgmv_expand_partials(dw.pool, plan, 0, (0,), [0], y3, dw.base[(0, 0)])
+    torch.cuda.synchronize()
+    for other in (y2, y3):
+        assert np.array_equal(from_device(y).view(np.uint8), from_device(other).view(np.uint8))
+
+
+def test_merge_one_slot_equals_plain_bitexact():
+    """A decode batch merged from one slot of weight 1 gives the plain plan's
+    output bit for bit (the merge expand forms the same float32 sums); with
+    base and without (y accumulated in place)."""
+    import heterogeneous_adapter_batching_amd as hab
+    for has_base in (True, False):
+        w = random_case(57 + has_base, T=90, h_in=264, h_out=200, n_adapters=5,
+                        r_choices=[8, 16, 32, 64], has_base=has_base, max_seg=3)
+        dw = DeviceWorkload(w, threads=4)
+        merge = hab.Plan.merge(dw.pool, w.num_tokens, w.seg_starts, w.seg_adapter[:, None],
+                               np.ones((w.num_segs, 1), np.float32)).upload(1)
+        x = dw.x[(0, "x")]
+        y1 = torch.randn(dw.y[(0, 0)].shape, device="cuda").to(dw.y[(0, 0)].dtype)
+        y2 = y1.clone()
+        hab.sgmv_fused(dw.pool, dw.plan, 0, (0,), [0], x, y1, dw.base.get((0, 0)))
+        hab.sgmv_fused(dw.pool, merge, 0, (0,), [0], x, y2, dw.base.get((0, 0)))
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(y1).view(np.uint8), from_device(y2).view(np.uint8))
+
+
+def test_merge_refused_calls():
+    """The calls through a caller's v and the core calls refuse a merge plan."""
+    import heterogeneous_adapter_batching_amd as hab
+    w, dw, plan, seg_ad, seg_w = _merge_setup(58, K=2, dtype="bf16", T=20, max_seg=3)
+    x = dw.x[(0, "x")]
+    v = torch.zeros((w.num_tokens, w.r_max), dtype=torch.float32, device="cuda")
+    y = torch.zeros_like(dw.y[(0, 0)])
+    with pytest.raises(hab.LoraError):
+        hab.sgmv_shrink(dw.pool, plan, 0, (0,), x, v)
+    with pytest.raises(hab.LoraError):
+        hab.sgmv_expand(dw.pool, plan, 0, (0,), [0], v, y)
 
 
 def test_weight_one_equals_plain_bitexact():

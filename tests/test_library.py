@@ -357,3 +357,34 @@ def test_plan_rebuild_matches_create():
     plan.rebuild(4, [0, 2, 4], [1, 2], seg_sigma=[0, -1])
     with pytest.raises(hab.LoraError):
         plan.rebuild(4, [0, 2, 4], [1, 2], seg_weight=[np.inf, 2.0])
+
+
+def test_merge_plan_validation():
+    """lora_plan_create_merge: slot counts outside 1..LORA_MAX_MERGE, a bad
+    segment table, an unknown slot adapter and a weight that is not finite
+    are refused; a valid plan has a row per (token, non-empty slot), its
+    workspace within the bound for that many rows, and no export."""
+    pool = _pool(max_slots=8)
+    for i in range(4):
+        pool.reserve(i, 8 * (i + 1), 1.0)
+    starts = [0, 3, 5]
+    ads = np.array([[0, 1, -1], [2, 2, 3]], np.int32)
+    wts = np.array([[1.0, 0.5, 2.0], [0.25, -1.0, 3.0]], np.float32)
+    plan = hab.Plan.merge(pool, 5, starts, ads, wts)
+    st = plan.stats()
+    assert st["active_tokens"] == 3 * 2 + 2 * 3               # rows of non-empty slots
+    assert st["groups"] == 4
+    assert 0 < plan.workspace_bytes(1) <= pool.workspace_bytes(st["active_tokens"], 6, 1)
+    with pytest.raises(hab.LoraError):
+        plan.export()
+    bad = [(np.zeros((2, 0), np.int32), np.zeros((2, 0), np.float32), -1),     # K = 0
+           (np.zeros((2, 5), np.int32), np.ones((2, 5), np.float32), -1),      # K = 5
+           (np.array([[0], [7]], np.int32), np.ones((2, 1), np.float32), -3),  # unknown id
+           (np.array([[0], [1]], np.int32), np.array([[1.0], [np.nan]], np.float32), -1)]
+    for a, w_, code in bad:
+        with pytest.raises(hab.LoraError) as ei:
+            hab.Plan.merge(pool, 5, starts, a, w_)
+        assert ei.value.status == code, (a.shape, code)
+    with pytest.raises(hab.LoraError) as ei:
+        hab.Plan.merge(pool, 6, starts, ads, wts)               # does not end at T
+    assert ei.value.status == -6
