@@ -523,11 +523,37 @@ def step_metrics(w, ms):
             "algorithmic_bytes_per_step": alg["bytes"], "flops_per_step": alg["flops"]}
 
 
+def make_flush(mib):
+    """A buffer that evicts the caches when read: written once here, so that
+    reading it before a step leaves the 256 MB memory-side cache and the L2s
+    holding its clean lines and none of the step's data.  (Writing it before
+    each step instead would leave them full of dirty lines, whose write-back
+    the step would pay: a cold 32 MB read runs at 2.2 TB/s after a 1 GiB
+    write and at 3.8 TB/s after a 1 GiB read.)"""
+    import torch
+    if mib <= 0:
+        return None
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    torch.cuda.synchronize()
+    return buf
+
+
+def clear_caches(flush):
+    """Read the whole flush buffer (a reduction to one value)."""
+    flush.view(torch_int32()).max()
+
+
+def torch_int32():
+    import torch
+    return torch.int32
+
+
 def timed_steps(step, stream, steps, flush):
     """Mean ms per step and the sorted single-step times.  Without a flush
     buffer the steps run back to back between two events (and again, each
     between its own events, for the spread); with one, each step runs alone
-    between its own events after a write over the whole flush buffer."""
+    between its own events after a read of the whole flush buffer."""
     import torch
     if flush is None:
         with torch.cuda.stream(stream):
@@ -550,8 +576,8 @@ def timed_steps(step, stream, steps, flush):
         torch.cuda.synchronize()
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(steps)]
-        for i, (ea, eb) in enumerate(pairs):
-            flush.fill_(i & 0xFF)
+        for ea, eb in pairs:
+            clear_caches(flush)
             ea.record(stream)
             step()
             eb.record(stream)
@@ -593,6 +619,7 @@ def other_config(ci, args, stream, flush):
     out = {"workload": w.name, "description": w.description, "tokens": w.num_tokens,
            "distinct_adapters": int(len(w.touched())), "plan": dw.plan.stats(),
            "flush_mib_between_steps": (flush.numel() >> 20) if flush is not None else 0,
+           "flush": "read",
            "step_ms_p10_p50_p90": [round(float(np.quantile(per_step, q)), 5)
                                    for q in (0.1, 0.5, 0.9)], **step_metrics(w, ms)}
     log(f"[bench] {w.name}: {ms:.4f} ms/step ({time.perf_counter() - t0:.1f} s with staging), "
@@ -727,8 +754,7 @@ def main():
     # data there: such steps are timed one by one, each after a flush write.
     flush_mib = args.flush_mib if args.flush_mib >= 0 else (
         1024 if alg["bytes"] < (1 << 30) else 0)
-    flush = (torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
-             if flush_mib > 0 else None)
+    flush = make_flush(flush_mib)
     ms, per_step = timed_steps(step, stream, args.steps, flush)
     log(f"[bench] {args.mode}: {ms:.4f} ms/step" +
         (f", each step after a {flush_mib} MiB flush" if flush is not None else ""))
@@ -811,8 +837,8 @@ def main():
             else:                                            # each pass after a flush
                 pairs = [(torch.cuda.Event(enable_timing=True),
                           torch.cuda.Event(enable_timing=True)) for _ in range(args.kernel_reps)]
-                for i, (ea, eb) in enumerate(pairs):
-                    flush.fill_(i & 0xFF)
+                for ea, eb in pairs:
+                    clear_caches(flush)
                     ea.record(stream)
                     one_pass(expand)
                     eb.record(stream)
@@ -881,7 +907,7 @@ def main():
         del dw, plan, plan_ws, graph_plan
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        cflush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cflush = make_flush(1024)
         for ci in args.configs:
             configs[f"config{ci}"] = other_config(ci, args, stream, cflush)
         del cflush
@@ -897,7 +923,7 @@ def main():
                    "projections": [p.name for p in w.projs],
                    "calls_per_layer": len(w.calls), "kernel_launches_per_step": launches,
                    "distinct_adapters": int(len(w.touched())), "mode": args.mode,
-                   "flush_mib_between_steps": flush_mib},
+                   "flush_mib_between_steps": flush_mib, "flush": "read"},
         **{k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")},
         "step_ms_quantiles": quant,
         "eager_ms_per_step": round(eager_ms, 5),
