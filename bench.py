@@ -647,6 +647,26 @@ def copy_ceiling(nbytes, launches, stream):
     return 4 * n / (ms * 1e-3 / launches) / 1e9, ms * 1e3 / launches
 
 
+def copy_step(sizes, stream):
+    """ms of a graph of plain device copies, one per kernel launch of the
+    step, each moving that launch's algorithmic bytes (half read, half
+    written), in the step's order: the step's ceiling if every kernel ran
+    at the speed of a copy of its size in this launch pattern."""
+    import torch
+    halves = [max(1, int(b) // 4) for b in sizes]     # bf16 elements read per copy
+    total = sum(halves)
+    src = torch.ones(total, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    offs = np.concatenate([[0], np.cumsum(halves)])
+
+    def fn():
+        for i in range(len(halves)):
+            dst[offs[i]:offs[i + 1]].copy_(src[offs[i]:offs[i + 1]])
+    ms = _time_graph(fn, stream, 3, 10)
+    del src, dst
+    return ms
+
+
 def plan_cost(dw, stream, reps=200):
     """Host cost of planning a new batch: lora_plan_rebuild then
     lora_plan_upload into one workspace sized for any batch of the step's
@@ -875,6 +895,16 @@ def main():
         log(f"[bench] copy of {kern[dom]['alg_bytes_per_launch'] / 1e6:.1f} MB per launch, "
             f"{n_launch} back to back: {cus:.2f} us, {cgbs:.0f} GB/s")
 
+    # the step as copies: every launch of the step replaced by a copy of its
+    # algorithmic bytes, in the same order, in a graph
+    copy_step_ms = None
+    if flush is None and args.copy_mib > 0:
+        sizes = [kernel_bytes(w, c, k) for _ in dw.layers for c in dw.calls
+                 for k in ("shrink", "expand")]
+        copy_step_ms = copy_step(sizes, stream)
+        log(f"[bench] the step as {len(sizes)} copies of its launches' bytes: "
+            f"{copy_step_ms:.4f} ms ({alg['bytes'] / (copy_step_ms * 1e-3) / 1e9:.0f} GB/s)")
+
     # device copy bandwidth: a second, measured denominator
     copy_gbs = None
     if args.copy_mib > 0:
@@ -933,6 +963,9 @@ def main():
         "eager_replan_ms_per_step": round(rebuild_ms, 5),
         "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},
         "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
+        # the same bytes per launch moved by plain copies in the same order
+        "copy_step_ms": round(copy_step_ms, 5) if copy_step_ms else None,
+        "frac_of_copy_step": round(copy_step_ms / ms, 4) if copy_step_ms else None,
         "roofline": roof, "cpu_baseline": cpu, "configs": configs,
     }
     print(json.dumps(out), flush=True)

@@ -122,6 +122,19 @@ __device__ __forceinline__ int xcd_unit(int gs) {
     return (i / gs) * (kXcds * gs) + x * gs + (i % gs);
 }
 
+// Workgroup g runs on XCD g % kXcds; here each XCD takes one contiguous range
+// of ceil(units / kXcds) units, in order.  For the MFMA expand, whose units
+// run block by block (token slices, then projections and row chunks), the
+// units that read one token tile's shrink partials then share an L2, and so
+// do the blocks of one adapter, which read the same B rows: with units dealt
+// round-robin, a tile's partials were fetched once per XCD its units ran on
+// (the prefill q/k/v expand fetched 1.4x its bytes).  Indices past `units`
+// (at most kXcds - 1 of them, on the last XCDs) are idle.
+__device__ __forceinline__ int xcd_range_unit(int units) {
+    const int g = blockIdx.x;
+    return (g % kXcds) * ((units + kXcds - 1) / kXcds) + g / kXcds;
+}
+
 // Reads plan memory (descriptors, token rows) through the constant address
 // space, which promises that it stays unchanged for the whole dispatch: the
 // plan workspace is written only by host uploads between launches, and the
@@ -1230,7 +1243,7 @@ __global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
     __shared__ float vs[TT * kTile][VS];
 
     warm_args<ExpandArgs>();
-    const int u = xcd_unit(1);
+    const int u = xcd_range_unit(a.units);
     if (u >= a.units) return;                        // whole workgroup
     const int lane = threadIdx.x & 63;
     ExpandCtx c;
@@ -1342,8 +1355,8 @@ hipError_t shrink_dispatch(int tt, bool mp, const ShrinkArgs &a, hipStream_t s) 
 }
 
 template <typename T, int KSM>
-hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, hipStream_t s) {
-    const dim3 grid(a.grid), block(kWaves * kWaveSize);
+hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, int g, hipStream_t s) {
+    const dim3 grid(g), block(kWaves * kWaveSize);
     switch (tt) {
     case 1: hipLaunchKernelGGL((k_expand<T, 1, KSM>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_expand<T, 2, KSM>), grid, block, 0, s, a); break;
@@ -1428,9 +1441,9 @@ void expand_decode_nvm(int nvm, dim3 grid, dim3 block, const ExpandArgs &a, hipS
     else if constexpr (sizeof(T) == 4) hipLaunchKernelGGL((k_expand_decode<T, Sig, 16>), grid, block, 0, s, a);
 }
 
-hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s) {
+hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int g, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
-    const dim3 grid(a.grid), block(kWaves * kWaveSize);
+    const dim3 grid(g), block(kWaves * kWaveSize);
     if (dtype == LORA_BF16) {
         if (nvm > 8) return hipErrorInvalidValue;
         if (a.sigma_kind) expand_decode_nvm<uint16_t, true>(nvm, grid, block, a, s);
@@ -1464,16 +1477,16 @@ hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid,
     return expand_merge_t<float>(nvm, g, block, a, s);
 }
 
-hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s) {
+hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, int g, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
     if (dtype == LORA_BF16) {
-        if (ks == 1) return expand_dispatch_ks<uint16_t, 1>(tt, a, s);
-        if (ks == 2) return expand_dispatch_ks<uint16_t, 2>(tt, a, s);
+        if (ks == 1) return expand_dispatch_ks<uint16_t, 1>(tt, a, g, s);
+        if (ks == 2) return expand_dispatch_ks<uint16_t, 2>(tt, a, g, s);
         return hipErrorInvalidValue;
     }
-    if (ks == 1) return expand_dispatch_ks<float, 1>(tt, a, s);
-    if (ks == 2) return expand_dispatch_ks<float, 2>(tt, a, s);
-    if (ks == 4) return expand_dispatch_ks<float, 4>(tt, a, s);
+    if (ks == 1) return expand_dispatch_ks<float, 1>(tt, a, g, s);
+    if (ks == 2) return expand_dispatch_ks<float, 2>(tt, a, g, s);
+    if (ks == 4) return expand_dispatch_ks<float, 4>(tt, a, g, s);
     return hipErrorInvalidValue;
 }
 

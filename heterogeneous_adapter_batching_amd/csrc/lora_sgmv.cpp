@@ -1368,8 +1368,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
             m.oc_prefix[i + 1] = m.oc_prefix[i] + (m.h_out[i] + rows_per_group - 1) / rows_per_group;
         for (int i = nproj; i < LORA_MAX_PROJ; ++i) m.oc_prefix[i + 1] = INT32_MAX;
         m.units = nl * m.tslices * m.oc_prefix[nproj];
-        m.grid = grid_for(m.units, 1);
-        const hipError_t e = lora::launch_expand(p->d.dtype, ttu, ks, m, st);
+        const hipError_t e = lora::launch_expand(p->d.dtype, ttu, ks, m, grid_for(m.units, 1), st);
         if (e != hipSuccess) return hip_fail(e, "expand launch");
     }
     if (nb > nl) {
@@ -1396,8 +1395,8 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         }
         for (int k = ncls; k <= lora::kMaxClasses; ++k) a.cls_unit0[k] = k == ncls ? units : INT32_MAX;
         a.units = units;
-        a.grid = grid_for(a.units, 1);
-        const hipError_t e = lora::launch_expand_decode(p->d.dtype, nvm, a, st);
+        const hipError_t e =
+            lora::launch_expand_decode(p->d.dtype, nvm, a, grid_for(a.units, 1), st);
         if (e != hipSuccess) return hip_fail(e, "expand launch");
     }
     return LORA_OK;

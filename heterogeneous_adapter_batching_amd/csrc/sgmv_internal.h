@@ -136,7 +136,6 @@ struct ExpandArgs {
     const BlockDesc *blocks;
     const float *partial;        // non-null: v = sum of partials
     const float *v;              // else: caller's v [T][ldv]
-    uint32_t partial_bytes;
     void *y;
     const void *base;            // nullable: y_in = base, else y_in = y
     int64_t ldv;
@@ -151,12 +150,12 @@ struct ExpandArgs {
     int32_t chunks;              // row chunks per wave (16 * expand_tiles(ks) rows each)
     int32_t c0;                  // partial chunks (when partial != null)
     int32_t ptt;                 // 16-token tiles per shrink partial tile
-    int32_t units;
-    int32_t grid;
+    int32_t units;               // (the grid is units rounded up to kXcds)
     int32_t r_max;
     uint32_t y_bytes;            // buffer ranges (each at most kMaxTensorBytes)
     uint32_t base_bytes;
     uint32_t v_bytes;            // range of a caller's v (when partial == null)
+    uint32_t partial_bytes;
     // Jointly compressed adapters: sigma_kind 0 = none, 1 = diagonal cores,
     // 2 = full cores.  Token row tok_off + i of the plan order uses core
     // tok_sig[tok_off + i] (-1: none); core j of projection i of the call
@@ -274,10 +273,12 @@ hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStr
 hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
                          int h_in_pad, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
-hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, hipStream_t s);
+hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, int grid,
+                         hipStream_t s);
 // decode expand (every block of the plan within kValuTokens tokens)
 // nvm: the largest decode_nvt of the launch's rank classes
-hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, hipStream_t s);
+hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int grid,
+                                hipStream_t s);
 // merge expand; nvm: the largest decode_nvt of the plan's slot adapters
 hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid, hipStream_t s);
 
