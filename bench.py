@@ -461,16 +461,27 @@ def exchange(args):
                     cache.prefetch(seq[k])
                 torch.cuda.synchronize()
 
-            def run(n, start, mode=mode, cache=cache, pool3=pool3):
+            # one plan re-planned in place for every batch, one workspace
+            # sized for any batch of T tokens: nothing is allocated per step
+            ws = torch.empty(pool3.workspace_bytes(T, T, 3), dtype=torch.uint8, device="cuda")
+            plan_box = [None]
+
+            def run(n, start, mode=mode, cache=cache, pool3=pool3, ws=ws, plan_box=plan_box):
                 for k in range(start, start + n):
                     cache.acquire(seq[k], stream=comp)
                     # the next batch's adapters copy while this batch runs
                     # (this batch's are held, so they stay)
                     if mode == "exchange" and k + 1 < len(seq):
                         cache.prefetch(seq[k + 1])
-                    plan = hab.Plan(pool3, T, starts, seq[k])
-                    plan.upload(3, stream=comp)
-                    launch(pool3, plan)
+                    # re-planning takes the pool as it is now, evictions
+                    # included, so the rebuilt plan is current
+                    pl = plan_box[0]
+                    if pl is None:
+                        pl = plan_box[0] = hab.Plan(pool3, T, starts, seq[k])
+                    else:
+                        pl.rebuild(T, starts, seq[k])
+                    pl.upload(3, ws=ws, stream=comp)
+                    launch(pool3, pl)
                     cache.release(stream=comp)
 
             run(4, 0)
@@ -501,10 +512,24 @@ def exchange(args):
             **out}
     if args.sweep_out:
         with open(args.sweep_out, "w") as f:
-            f.write("# Adapter exchange on the full stack (rank-16 adapters)\n")
+            f.write(f"# Adapter exchange on the full stack (rank-16 adapters, {ext / 1e6:.1f} MB "
+                    f"packed each; {T} decode tokens)\n")
             f.write(f"command: python bench.py --exchange --exchange-steps {n_steps} "
                     f"--sweep-out {args.sweep_out}\n\n")
-            f.write(json.dumps(line, indent=1) + "\n")
+            f.write(f"host-to-device, packed images from pinned memory: {out['h2d_gbs']} GB/s "
+                    f"({out['copy_ms_per_adapter']} ms per adapter)\n")
+            f.write("overlap (the step captured in a graph over 8 resident adapters, on the "
+                    "compute stream; image copies on the copy stream; both start from one "
+                    "event):\n")
+            f.write(f"  {json.dumps(out['overlap'])}\n")
+            f.write(f"replay ({T} decode slots, `churn` requests replaced per step by Zipf(1.1) "
+                    f"draws over 1000 adapters; eager launches; one plan rebuilt in place per "
+                    f"batch into one workspace; pool of {args.exchange_slots} adapters):\n")
+            for churn in args.exchange_churn:
+                r = out[f"replay_churn_{churn}"]
+                f.write(f"  replay_churn_{churn}: distinct adapters {r['distinct_adapters']}\n")
+                for mode in ("resident", "exchange", "exchange_no_prefetch"):
+                    f.write(f"    {mode:22s} {json.dumps(r[mode])}\n")
     print(json.dumps(line), flush=True)
 
 
@@ -798,8 +823,12 @@ def main():
     graph_plan = dw.plan
     plan, plan_ws, plan_ids, plan_us = plan_cost(dw, stream)
     log(f"[bench] plan rebuild + upload: {plan_us:.1f} us on the host")
-    n_rb = max(3, args.steps // 5)
+    n_rb = max(10, args.steps // 2)
     with torch.cuda.stream(stream):
+        for i in range(3):   # untimed: the first re-planned steps of the process
+            plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
+                dw.max_proj, ws=plan_ws, stream=stream)
+            dw.run_fused(stream=stream)
         torch.cuda.synchronize()
         e4, e5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_rb = time.perf_counter()

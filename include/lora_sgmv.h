@@ -353,7 +353,9 @@ lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t 
  * plan's host tables and pinned staging and allocates nothing on the device
  * or in pinned memory unless the batch is larger than any before.  The plan
  * must be uploaded again before its next call; an error leaves the plan as it
- * was.  Errors as the create calls. */
+ * was.  The plan is made against the pool as it is at the rebuild, so a plan
+ * that an unregister (or an exchange eviction) left stale is current again.
+ * Errors as the create calls. */
 lora_status lora_plan_rebuild(lora_plan *pl, int32_t num_tokens, const int32_t *seg_starts,
                               const int32_t *seg_adapter, const int32_t *seg_sigma,
                               const float *seg_weight, int32_t num_segs);

@@ -92,3 +92,63 @@ def test_traffic_file_and_source_hash(runs, tmp_path, monkeypatch):
     monkeypatch.setattr(profiling, "source_hash", lambda: "another")
     assert bench.traffic_from_profile("k_expand_decode", "wl") is None
     assert bench.traffic_from_profile("k_shrink", "wl") is None
+
+
+def test_mfma_use_per_launch_shape(tmp_path):
+    """MFMA use groups dispatches by (kernel, workgroups): the busy ratio is
+    averaged over a dispatch's rows, the FLOP summed, and the rate uses the
+    kernel trace's average duration for that same shape."""
+    cpath = tmp_path / "c.csv"
+    with open(cpath, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size",
+                    "Counter_Name", "Counter_Value"])
+        # two dispatches of the shrink on 64 workgroups, one on 128
+        for d, grid, util, fl in ((1, 64 * 256, 10.0, 2e9), (2, 64 * 256, 20.0, 4e9),
+                                  (3, 128 * 256, 5.0, 1e9)):
+            w.writerow([d, SHRINK, grid, 256, "MfmaUtil", util])
+            w.writerow([d, SHRINK, grid, 256, "MfmaFlopsBF16", fl / 2])
+            w.writerow([d, SHRINK, grid, 256, "MfmaFlopsBF16", fl / 2])
+        w.writerow([4, OTHER, 256, 256, "MfmaUtil", 99.0])
+    tpath = tmp_path / "t.csv"
+    with open(tpath, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp",
+                    "Workgroup_Size_X", "Grid_Size_X"])
+        w.writerow([SHRINK, 0, 10_000, 256, 64 * 256])
+        w.writerow([SHRINK, 0, 20_000, 256, 64 * 256])
+        w.writerow([SHRINK, 0, 4_000, 256, 128 * 256])
+    res = profiling.mfma_use(str(cpath), str(tpath), ["k_shrink"])
+    assert set(res) == {("k_shrink", 64), ("k_shrink", 128)}
+    a = res[("k_shrink", 64)]
+    assert a["util"] == pytest.approx(15.0)
+    assert a["gflop"] == pytest.approx(3.0)
+    assert a["us"] == pytest.approx(15.0)
+    assert a["launches"] == 2
+    txt = profiling.mfma_summary(str(cpath), str(tpath), ["k_shrink"], ["cmd"])
+    # 3 GFLOP in 15 us = 200 TFLOP/s = 0.08 of the bf16 peak
+    assert "200.00" in txt and "0.0800" in txt
+
+
+def test_copy_overlap_split(tmp_path):
+    """A launch is "with a copy" when any copy interval overlaps it, also a
+    copy that began long before it; touching endpoints do not count."""
+    t = tmp_path / "t.csv"
+    with open(t, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp",
+                    "Workgroup_Size_X", "Grid_Size_X"])
+        for s0, s1 in ((0, 1000), (1000, 3000), (5000, 6000), (9000, 9500), (20000, 22000)):
+            w.writerow([EXPAND, s0, s1, 256, 64 * 256])
+        w.writerow([OTHER, 5000, 6000, 256, 256])
+    c = tmp_path / "c.csv"
+    with open(c, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kind", "Start_Timestamp", "End_Timestamp"])
+        w.writerow(["MEMORY_COPY", 3000, 5500])     # overlaps the third, touches the second
+        w.writerow(["MEMORY_COPY", 8000, 30000])    # covers the fourth and fifth
+    res = profiling.copy_overlap(str(t), str(c), ["k_expand_decode"])
+    alone, na, with_copy, nb = res[("k_expand_decode", 64)]
+    assert (na, nb) == (2, 3)
+    assert alone == pytest.approx((1.0 + 2.0) / 2)
+    assert with_copy == pytest.approx((1.0 + 0.5 + 2.0) / 3)
