@@ -789,7 +789,10 @@ def main():
     log(f"[bench] staged {w.name}: {time.perf_counter() - t0:.1f} s, "
         f"plan {dw.plan.stats()}")
     alg = algorithmic(w)
-    launches = 2 * len(dw.layers) * len(dw.calls)
+    # a call is one prefill launch for a batch of long groups only, else a
+    # shrink and an expand launch
+    launches = (1 if dw.plan.stats()["max_block_tokens"] > 16 else 2) * len(dw.layers) * \
+        len(dw.calls)
 
     stream = torch.cuda.Stream()
     graph = capture(dw.run_fused, stream, args.warmup) if args.mode == "graph" else None
@@ -847,20 +850,31 @@ def main():
                                                                    stream=stream)
     torch.cuda.synchronize()
 
-    # Per-kernel durations of the step's two kernels, launched back to back
-    # (a full queue, as in the step): passes over every (layer, call) of the
-    # shrink alone, and of the shrink then the expand (the two kernels of
-    # sgmv_fused as separate calls, in the step's order), between two events
-    # on the launch stream.  The expand's duration is the pair's less the
-    # shrink's.
+    # Per-kernel durations, launched back to back (a full queue, as in the
+    # step), between two events on the launch stream.  Decode: the step's
+    # two kernels, as passes over every (layer, call) of the shrink alone
+    # and of the shrink then the expand (sgmv_fused's two kernels as separate
+    # calls, in the step's order); the expand's duration is the pair's less
+    # the shrink's.  A batch of long groups only: each call is one launch of
+    # the prefill kernel, timed as passes of sgmv_fused.
     n_launch = len(dw.layers) * len(dw.calls)
+    prefill = dw.plan.stats()["max_block_tokens"] > 16
 
-    def one_pass(expand):
+    def one_pass(kind):
         for l in dw.layers:
             for ci, c in enumerate(dw.calls):
                 x = dw.x[(l, w.projs[c[0]].x_key)]
+                if kind == "prefill":
+                    if dw.sigma is not None:
+                        hab.sgmv_fused_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
+                                             dw.sigma, w.sigma_kind, dw.y[(l, ci)],
+                                             dw.base.get((l, ci)), stream=stream)
+                    else:
+                        hab.sgmv_fused(dw.pool, dw.plan, l, c, dw.y_offsets[ci], x,
+                                       dw.y[(l, ci)], dw.base.get((l, ci)), stream=stream)
+                    continue
                 hab.sgmv_shrink_partials(dw.pool, dw.plan, l, c, x, stream=stream)
-                if not expand:
+                if kind == "shrink":
                     continue
                 if dw.sigma is not None:
                     hab.sgmv_expand_partials_sigma(dw.pool, dw.plan, l, c, dw.y_offsets[ci],
@@ -872,14 +886,14 @@ def main():
 
     tot = {}
     with torch.cuda.stream(stream):
-        for kind, expand in (("shrink", False), ("pair", True)):
-            one_pass(expand)                                 # warm
+        for kind in (("prefill",) if prefill else ("shrink", "pair")):
+            one_pass(kind)                                   # warm
             torch.cuda.synchronize()
             if flush is None:
                 ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ea.record(stream)
                 for _ in range(args.kernel_reps):
-                    one_pass(expand)
+                    one_pass(kind)
                 eb.record(stream)
                 torch.cuda.synchronize()
                 tot[kind] = ea.elapsed_time(eb)
@@ -889,23 +903,28 @@ def main():
                 for ea, eb in pairs:
                     clear_caches(flush)
                     ea.record(stream)
-                    one_pass(expand)
+                    one_pass(kind)
                     eb.record(stream)
                 torch.cuda.synchronize()
                 tot[kind] = sum(ea.elapsed_time(eb) for ea, eb in pairs)
-    tot["expand"] = tot["pair"] - tot["shrink"]
-    tot.pop("pair")
+    if not prefill:
+        tot["expand"] = tot["pair"] - tot["shrink"]
+        tot.pop("pair")
     us = {kind: t * 1e3 / (args.kernel_reps * n_launch) for kind, t in tot.items()}
-    us["fused"] = us["shrink"] + us["expand"]
     kern = {}
-    for kind in ("shrink", "expand", "fused"):
-        parts = ("shrink", "expand") if kind == "fused" else (kind,)
+    kinds = ("prefill",) if prefill else ("shrink", "expand", "fused")
+    if not prefill:
+        us["fused"] = us["shrink"] + us["expand"]
+    for kind in kinds:
+        parts = ("shrink", "expand") if kind in ("fused", "prefill") else (kind,)
         bpl = sum(kernel_bytes(w, c, k) for c in dw.calls for k in parts) / len(dw.calls)
         kern[kind] = {"avg_us": us[kind], "gbs": bpl / (us[kind] * 1e-6) / 1e9,
                       "alg_bytes_per_launch": bpl}
-    dom = "expand" if kern["expand"]["avg_us"] >= kern["shrink"]["avg_us"] else "shrink"
-    decode = dw.plan.stats()["max_block_tokens"] <= 4
-    kname = {"shrink": "k_shrink", "expand": "k_expand_decode" if decode else "k_expand"}[dom]
+    if prefill:
+        dom, kname = "prefill", "k_prefill"
+    else:
+        dom = "expand" if kern["expand"]["avg_us"] >= kern["shrink"]["avg_us"] else "shrink"
+        kname = {"shrink": "k_shrink", "expand": "k_expand_decode"}[dom]
     traffic = traffic_from_profile(kname, w.name)
     roof = {"bound": "hbm", "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),

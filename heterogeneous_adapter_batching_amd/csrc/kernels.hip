@@ -484,16 +484,16 @@ __device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &b
 // (LDS rows [0, n_tok), ranks [0, r_pad)) becomes Sigma_j v with the token's
 // core j, in float32, k ascending; a token without a core keeps v.  Full
 // cores are r_max x r_max row-major, diagonal cores r_max values.  Up to
-// MAXI entries per thread.
-template <int MAXI>
-__device__ __forceinline__ void apply_sigma(const ExpandArgs &a, const BlockDesc &blk, int p,
+// MAXI entries per thread of NT threads.
+template <int MAXI, int NT = kWaves * kWaveSize, typename Args>
+__device__ __forceinline__ void apply_sigma(const Args &a, const BlockDesc &blk, int p,
                                             float (*vs)[LORA_MAX_RANK + 4]) {
     const int r = blk.r_pad;
     const int entries = blk.n_tok * r;
     float out[MAXI];
 #pragma unroll
     for (int ii = 0; ii < MAXI; ++ii) {
-        const int i = int(threadIdx.x) + ii * kWaves * kWaveSize;
+        const int i = int(threadIdx.x) + ii * NT;
         out[ii] = 0.f;
         if (i < entries) {
             const int ti = i / r, j = i - (i / r) * r;
@@ -521,7 +521,7 @@ __device__ __forceinline__ void apply_sigma(const ExpandArgs &a, const BlockDesc
     __syncthreads();
 #pragma unroll
     for (int ii = 0; ii < MAXI; ++ii) {
-        const int i = int(threadIdx.x) + ii * kWaves * kWaveSize;
+        const int i = int(threadIdx.x) + ii * NT;
         if (i < entries) vs[i / r][i - (i / r) * r] = out[ii];
     }
     __syncthreads();
@@ -783,13 +783,14 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
 // TPL = 4 / G consecutive tiles: lane group q reads vector q % G of tile
 // q / G.  The MFMA of tile t then takes v only in the lane groups holding
 // tile t (zero elsewhere), which selects tile t's rows.
-template <typename T, int TT, int KSM, int TPL>
-__device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc &blk,
+template <typename T, int TT, int KSM, int TPL, bool GATHER = true, typename Args = ExpandArgs,
+          int OTWC = expand_tiles(KSM)>
+__device__ __forceinline__ void expand_body(const Args &a, const BlockDesc &blk,
                                             const ExpandCtx &c, const int (&trow)[TT],
                                             const bool (&tv)[TT], float (*vs)[LORA_MAX_RANK + 4]) {
     constexpr int E = Elem<T>::E;
     constexpr int SPAN = 4 * E;
-    constexpr int OTW = expand_tiles(KSM);           // tiles per chunk
+    constexpr int OTW = OTWC;                        // tiles per chunk
     constexpr int NL = TPL == 1 ? OTW * KSM : OTW / TPL;   // loads per chunk
     constexpr int CH = OTW * kTile;                  // rows per chunk
     const int G = TPL == 1 ? 4 : 4 / TPL;            // vectors per row (packed)
@@ -857,10 +858,12 @@ __device__ __forceinline__ void expand_body(const ExpandArgs &a, const BlockDesc
     yraw yinA[NY][TT], yinB[NY][TT];
     load(c.o_lo, bfA, yinA);
 
-    gather_v<TT>(a, blk, c.p, vs);
-    __syncthreads();
-    if (a.sigma_kind)
-        apply_sigma<TT * kTile * LORA_MAX_RANK / (kWaves * kWaveSize)>(a, blk, c.p, vs);
+    if constexpr (GATHER) {      // else v (cores applied) is in LDS already
+        gather_v<TT>(a, blk, c.p, vs);
+        __syncthreads();
+        if (a.sigma_kind)
+            apply_sigma<TT * kTile * LORA_MAX_RANK / (kWaves * kWaveSize)>(a, blk, c.p, vs);
+    }
     if (c.o_lo >= c.o_hi) return;
 
     // v operand per (token tile, K-step); packed blocks have one K-step
@@ -1234,88 +1237,242 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
     }
 }
 
-template <typename T, int TT, int KSM>
-__global__ __launch_bounds__(256) void k_expand(const ExpandArgs a) {
+// --------------------------------------------------------------- prefill ----
+// The whole delta of one 16-token tile of a long group's block in one
+// workgroup of kPrefillWaves waves, with nothing handed between kernels:
+//
+//  1. v = A x for each of the call's projections (the A step at scale 1.0,
+//     "Compress then Serve", rebuttal pseudocode, step 1): the waves split
+//     K into equal runs of K-blocks; each wave chains its MFMAs in K order,
+//     loading the next batch of x and A fragments while it multiplies the
+//     current one, and the waves' tiles are added in wave order through LDS.
+//     v stays float32 in LDS.
+//  2. y = y_in + s B v over every output row of the call's projections (step
+//     3): the rows are split among the waves (and among the workgroups of a
+//     tile when a launch has few tiles); each wave runs the MFMA expand's row
+//     loop on its rows.
+//
+// A tile's x rows are read once from HBM and its y rows once each way, the
+// adapter's A and B come from L2 (a group's tiles are consecutive units and
+// xcd_range_unit keeps them on one XCD), and v never reaches memory.  MODE
+// runs step 1 alone (v written to memory, the standalone shrink) or step 2
+// alone (v read from memory), with the same arithmetic as the fused form.
+//
+// K-blocks per batch of the shrink step, for `pairs` (projection, rank tile)
+// accumulators: a batch is FB x fragments and FB x pairs A fragments; two
+// batches in flight stay within about 72 VGPRs.
+constexpr int prefill_kbatch(int pairs) { return pairs <= 1 ? 4 : pairs <= 3 ? 2 : 1; }
+constexpr int prefill_ksm(int rtm, int e) {
+    return (rtm * kTile + 4 * e - 1) / (4 * e) == 3 ? 4 : (rtm * kTile + 4 * e - 1) / (4 * e);
+}
+// Row tiles per chunk of the expand step: half the decode geometry's, so two
+// chunks in flight fit the 128 VGPRs of a 16-wave workgroup (whole pairs in
+// bf16).
+constexpr int prefill_otw(int ksm, int esize) {
+    return esize == 2 ? (expand_tiles(ksm) / 2 < 2 ? 2 : expand_tiles(ksm) / 2)
+                      : (expand_tiles(ksm) / 2 < 1 ? 1 : expand_tiles(ksm) / 2);
+}
+
+template <typename T, int NP, int RTM, int MODE>
+__global__ __launch_bounds__(kPrefillWaves * kWaveSize) void k_prefill(const PrefillArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int SPAN = 4 * E;
-    constexpr int OTW = expand_tiles(KSM);
-    constexpr int VS = LORA_MAX_RANK + 4;            // LDS row stride of v (floats)
-    __shared__ float vs[TT * kTile][VS];
+    constexpr int W = kPrefillWaves;
+    constexpr int NT = W * kWaveSize;
+    constexpr int VS = LORA_MAX_RANK + 4;
+    constexpr int PAIRS = NP * RTM;
+    constexpr int FB = prefill_kbatch(PAIRS);
+    constexpr bool DB = PAIRS <= 8;
+    constexpr int KSM = prefill_ksm(RTM, E);
+    constexpr int OTW = prefill_otw(KSM, int(sizeof(T)));
+    __shared__ float vs[NP][kTile][VS];
+    __shared__ f32x4 red[MODE == kPrefillExpand ? 1 : 2][W][kWaveSize];
 
-    warm_args<ExpandArgs>();
+    warm_args<PrefillArgs>();
     const int u = xcd_range_unit(a.units);
     if (u >= a.units) return;                        // whole workgroup
     const int lane = threadIdx.x & 63;
-    ExpandCtx c;
-    c.w = wave_id();
-    c.n = lane & 15;
-    c.q = lane >> 4;
-    // unit -> (block, token slice, projection, row chunk)
-    const int upb = a.oc_prefix[a.nproj];
-    const int per_block = a.tslices * upb;
-    c.b = u / per_block;
-    const int rs = u - c.b * per_block;
-    const int ts = rs / upb;
-    const int rem = rs - ts * upb;
-    c.p = 0;
-    while (rem >= a.oc_prefix[c.p + 1]) ++c.p;
-    const int oc = rem - a.oc_prefix[c.p];
-    // the slice's tokens as a block of their own: its first token, its first
-    // slot in the shrink block and its token count
-    BlockDesc blk = load_invariant(a.blocks + c.b);
-    const int off = ts * TT * kTile;
-    if (off >= blk.n_tok) return;                    // whole workgroup: an empty slice
+    const int w = wave_id();
+    const int n = lane & 15, q = lane >> 4;
+    // unit -> (block, token tile, row part)
+    const int part = u % a.osplit;
+    const int bt = u / a.osplit;
+    const int b = bt / kPrefillTiles, tile = bt % kPrefillTiles;
+    BlockDesc blk = load_invariant(a.blocks + b);
+    const int off = tile * kTile;
+    if (off >= blk.n_tok) return;                    // whole workgroup: an empty tile
     blk.tok_off += off;
     blk.slot0 += off;
-    blk.n_tok = min(TT * kTile, blk.n_tok - off);
-    int trow[TT];                                    // token rows, -1 padded
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-        trow[tt] = a.block_tok[c.b * kMaxBlockTokens + off + tt * kTile + c.n];
-    c.h_out = a.h_out[c.p];
-    const int rows_w = a.chunks * OTW * kTile;       // rows of this wave
-    c.o_lo = min(c.h_out, (oc * kWaves + c.w) * rows_w);
-    c.o_hi = min(c.h_out, c.o_lo + rows_w);
-    c.yoff = a.y_off[c.p];
-    c.ks_n = (blk.r_pad + SPAN - 1) / SPAN;          // wave-uniform, <= KSM
-    c.ntiles = (blk.n_tok + kTile - 1) / kTile;
-    c.scale = blk.scale;
-    bool tv[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) tv[tt] = tt < c.ntiles && trow[tt] >= 0;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int i = tt * kTile + c.n;
-        c.tsc[tt] = a.tok_w && tt < TT && i < blk.n_tok ? blk.scale * a.tok_w[blk.tok_off + i]
-                                                       : blk.scale;
-    }
+    blk.n_tok = min(kTile, blk.n_tok - off);
+    const int trow = a.block_tok[b * kMaxBlockTokens + off + n];   // -1 past n_tok
 
-    if (blk.r_pad == 0) {            // tokens without an adapter: y = base
-        if (!a.base) return;
-        const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
-        const rsrc_t br = make_rsrc(a.base, a.base_bytes);
-        for (int o0 = c.o_lo; o0 < c.o_hi; o0 += kTile) {
-            const int o = o0 + 4 * c.q;
+    if constexpr (MODE != kPrefillExpand) {
+        // ---- step 1: v = A x, K split over the waves
+        const int nkb = (a.h_in + SPAN - 1) / SPAN;
+        const int per_w = (nkb + W - 1) / W;
+        const int kb0 = min(nkb, w * per_w), kb1 = min(nkb, kb0 + per_w);
+        const int rtn = (blk.r_pad + kTile - 1) / kTile;   // rank tiles, <= RTM
+        const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+        // an absent token's row offset is out of range already (kOOB + k
+        // bytes stays at or above 2^31)
+        const uint32_t xrow = trow >= 0 ? uint32_t(int64_t(trow) * a.ldx * sizeof(T)) : kOOB;
+        rsrc_t ar[NP];
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const bool ok = tv[tt] && o < c.o_hi;
-                const auto v4 = Out4<T>::load(
-                    br, off_or_oob(ok, uint32_t(int64_t(trow[tt]) * a.ldb + c.yoff + o) * sizeof(T)));
-                Out4<T>::store(
-                    yr, off_or_oob(ok, uint32_t(int64_t(trow[tt]) * a.ldy + c.yoff + o) * sizeof(T)),
-                    v4);
+        for (int p = 0; p < NP; ++p)
+            ar[p] = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
+                                  uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
+                              uint32_t(blk.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
+        f32x4 acc[NP][RTM];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int rt = 0; rt < RTM; ++rt) acc[p][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // a batch: K-blocks kb .. kb + FB - 1 (masked past kb1, so the loads
+        // need no branch); A is K-blocked [h_in_pad / SPAN][r_pad][SPAN]
+        auto load = [&](int kb, u32x4 (&xf)[FB], u32x4 (&af)[NP][RTM][FB]) {
+#pragma unroll
+            for (int f = 0; f < FB; ++f) {
+                const bool ok = kb + f < kb1;
+                const int k = (kb + f) * SPAN + q * E;
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+#pragma unroll
+                    for (int rt = 0; rt < RTM; ++rt) {
+                        const int j = rt * kTile + n;
+                        af[p][rt][f] = bload16(
+                            ar[p], off_or_oob(ok && j < blk.r_pad,
+                                              uint32_t(((kb + f) * blk.r_pad + j) * SPAN + q * E) *
+                                                  sizeof(T)));
+                    }
+                xf[f] = bload16_nt(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
+            }
+        };
+        auto mult = [&](int kb, const u32x4 (&xf)[FB], const u32x4 (&af)[NP][RTM][FB]) {
+#pragma unroll
+            for (int f = 0; f < FB; ++f) {
+                if (kb + f >= kb1) break;            // wave-uniform
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+#pragma unroll
+                    for (int rt = 0; rt < RTM; ++rt)
+                        if (rt < rtn) acc[p][rt] = mma<T>(af[p][rt][f], xf[f], acc[p][rt]);
+            }
+        };
+        u32x4 xa[FB], aa[NP][RTM][FB];
+        if constexpr (DB) {
+            u32x4 xb[FB], ab[NP][RTM][FB];
+            load(kb0, xa, aa);
+            for (int kb = kb0; kb < kb1; kb += 2 * FB) {
+                load(kb + FB, xb, ab);
+                mult(kb, xa, aa);
+                if (kb + FB >= kb1) break;
+                load(kb + 2 * FB, xa, aa);
+                mult(kb + FB, xb, ab);
+            }
+        } else {
+            for (int kb = kb0; kb < kb1; kb += FB) {
+                load(kb, xa, aa);
+                mult(kb, xa, aa);
             }
         }
-        return;
+
+        // the waves' tiles added in wave order: lane (n, q) holds ranks
+        // 4 q .. 4 q + 3 of token n; two LDS buffers in turn, one barrier a pair
+        int k = 0;
+#pragma unroll
+        for (int pr = 0; pr < PAIRS; ++pr) {
+            const int p = pr / RTM, rt = pr % RTM;
+            if (rt >= rtn) continue;                 // uniform over the workgroup
+            red[k & 1][w][lane] = acc[p][rt];
+            __syncthreads();
+            if (threadIdx.x < kTile * kTile) {
+                const int ln = threadIdx.x >> 2, e = threadIdx.x & 3;
+                float s = red[k & 1][0][ln][e];
+#pragma unroll
+                for (int ww = 1; ww < W; ++ww) s += red[k & 1][ww][ln][e];
+                vs[p][ln & 15][rt * kTile + 4 * (ln >> 4) + e] = s;
+            }
+            ++k;
+        }
+        __syncthreads();
+
+        if constexpr (MODE == kPrefillShrink) {
+            // v rows of the tile's tokens: r_max entries per projection,
+            // zero past the padded rank
+            const int quads = a.r_max / 4;
+            for (int i = threadIdx.x; i < blk.n_tok * NP * quads; i += NT) {
+                const int ti = i / (NP * quads), rem = i - ti * (NP * quads);
+                const int p = rem / quads, j = (rem - p * quads) * 4;
+                const f32x4 s4 = j < blk.r_pad ? *reinterpret_cast<const f32x4 *>(&vs[p][ti][j])
+                                               : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
+                                               : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
+                *reinterpret_cast<f32x4 *>(a.v + row * a.ldv + int64_t(p) * a.r_max + j) = s4;
+            }
+            return;
+        }
+    } else {
+        // v of the tile's tokens from memory
+        const int quads = blk.r_pad / 4;
+        for (int i = threadIdx.x; i < blk.n_tok * NP * quads; i += NT) {
+            const int ti = i / (NP * quads), rem = i - ti * (NP * quads);
+            const int p = rem / quads, j = (rem - p * quads) * 4;
+            const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
+                                           : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
+            *reinterpret_cast<f32x4 *>(&vs[p][ti][j]) = *reinterpret_cast<const f32x4 *>(
+                a.v + row * a.ldv + int64_t(p) * a.r_max + j);
+        }
+        __syncthreads();
     }
 
-    // rows of 16-byte vectors: 1 or 2 per row pack 4 or 2 tiles into one load
-    if constexpr (KSM == 1) {
-        const int g = blk.r_pad / E;
-        if (g == 1) return expand_body<T, TT, KSM, 4>(a, blk, c, trow, tv, vs);
-        if (g == 2) return expand_body<T, TT, KSM, 2>(a, blk, c, trow, tv, vs);
+    if constexpr (MODE != kPrefillShrink) {
+        // ---- step 2: y = y_in + s B v (cores applied to v first)
+        if (a.sigma_kind) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                apply_sigma<kTile * LORA_MAX_RANK / NT, NT>(a, blk, p, vs[p]);
+        }
+        ExpandCtx c;
+        c.b = b;
+        c.w = w;
+        c.n = n;
+        c.q = q;
+        c.ntiles = 1;
+        c.ks_n = (blk.r_pad + SPAN - 1) / SPAN;      // wave-uniform, <= KSM
+        c.scale = blk.scale;
+        c.tsc[0] = a.tok_w && n < blk.n_tok ? blk.scale * a.tok_w[blk.tok_off + n] : blk.scale;
+        c.tsc[1] = c.tsc[2] = c.tsc[3] = blk.scale;
+        const int trows[1] = {trow};
+        const bool tv[1] = {trow >= 0};
+        const int g = blk.r_pad / E;                 // 16-byte vectors per B row
+        // each projection's rows in kPrefillWaves * osplit shares of whole
+        // 32-row pairs; share part * W + w is this wave's
+        const int shares = W * a.osplit, share = part * W + w;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            c.p = p;
+            c.h_out = a.h_out[p];
+            c.yoff = a.y_off[p];
+            const int rw = ((c.h_out + shares - 1) / shares + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+            c.o_lo = min(c.h_out, share * rw);
+            c.o_hi = min(c.h_out, c.o_lo + rw);
+            if (c.o_lo >= c.o_hi) continue;          // wave-uniform
+            if constexpr (KSM == 1) {
+                if (g == 1) {
+                    expand_body<T, 1, KSM, 4, false, PrefillArgs, OTW>(a, blk, c, trows, tv,
+                                                                       vs[p]);
+                    continue;
+                }
+                if (g == 2) {
+                    expand_body<T, 1, KSM, 2, false, PrefillArgs, OTW>(a, blk, c, trows, tv,
+                                                                       vs[p]);
+                    continue;
+                }
+            }
+            expand_body<T, 1, KSM, 1, false, PrefillArgs, OTW>(a, blk, c, trows, tv, vs[p]);
+        }
     }
-    expand_body<T, TT, KSM, 1>(a, blk, c, trow, tv, vs);
 }
 
 // ----------------------------------------------------------------- pack ----
@@ -1354,16 +1511,29 @@ hipError_t shrink_dispatch(int tt, bool mp, const ShrinkArgs &a, hipStream_t s) 
     return hipGetLastError();
 }
 
-template <typename T, int KSM>
-hipError_t expand_dispatch_ks(int tt, const ExpandArgs &a, int g, hipStream_t s) {
-    const dim3 grid(g), block(kWaves * kWaveSize);
-    switch (tt) {
-    case 1: hipLaunchKernelGGL((k_expand<T, 1, KSM>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_expand<T, 2, KSM>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_expand<T, 4, KSM>), grid, block, 0, s, a); break;
+template <typename T, int MODE>
+hipError_t prefill_dispatch(int np, int rtm, const PrefillArgs &a, int g, hipStream_t s) {
+    const dim3 grid(g), block(kPrefillWaves * kWaveSize);
+    switch (np * 8 + rtm) {
+#define LORA_PREFILL(NP, RTM) \
+    case NP * 8 + RTM: hipLaunchKernelGGL((k_prefill<T, NP, RTM, MODE>), grid, block, 0, s, a); break;
+    LORA_PREFILL(1, 1) LORA_PREFILL(1, 2) LORA_PREFILL(1, 4)
+    LORA_PREFILL(2, 1) LORA_PREFILL(2, 2) LORA_PREFILL(2, 4)
+    LORA_PREFILL(3, 1) LORA_PREFILL(3, 2) LORA_PREFILL(3, 4)
+#undef LORA_PREFILL
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t prefill_modes(int mode, int np, int rtm, const PrefillArgs &a, int g, hipStream_t s) {
+    switch (mode) {
+    case kPrefillFused: return prefill_dispatch<T, kPrefillFused>(np, rtm, a, g, s);
+    case kPrefillShrink: return prefill_dispatch<T, kPrefillShrink>(np, rtm, a, g, s);
+    case kPrefillExpand: return prefill_dispatch<T, kPrefillExpand>(np, rtm, a, g, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -1477,17 +1647,11 @@ hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid,
     return expand_merge_t<float>(nvm, g, block, a, s);
 }
 
-hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, int g, hipStream_t s) {
+hipError_t launch_prefill(int dtype, int mode, int np, int rtm, const PrefillArgs &a, int grid,
+                          hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
-    if (dtype == LORA_BF16) {
-        if (ks == 1) return expand_dispatch_ks<uint16_t, 1>(tt, a, g, s);
-        if (ks == 2) return expand_dispatch_ks<uint16_t, 2>(tt, a, g, s);
-        return hipErrorInvalidValue;
-    }
-    if (ks == 1) return expand_dispatch_ks<float, 1>(tt, a, g, s);
-    if (ks == 2) return expand_dispatch_ks<float, 2>(tt, a, g, s);
-    if (ks == 4) return expand_dispatch_ks<float, 4>(tt, a, g, s);
-    return hipErrorInvalidValue;
+    return dtype == LORA_BF16 ? prefill_modes<uint16_t>(mode, np, rtm, a, grid, s)
+                              : prefill_modes<float>(mode, np, rtm, a, grid, s);
 }
 
 }  // namespace lora

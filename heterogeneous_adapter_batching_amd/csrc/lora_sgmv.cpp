@@ -162,12 +162,16 @@ struct lora_pool {
 struct PlanCounts {
     int64_t T = 0, nb = 0, rt = 0, mb = 0;   // rows (tokens, or (token, slot) rows), blocks,
     int32_t tt = 1;                          // rank tiles, merge blocks; tiles per block
+    bool merge = false;                      // a merge plan (its shrink covers every tile)
+    int64_t rt_long = 0;                     // a plain plan: rank tiles of long groups
+    int64_t long_rows = 0;                   // ... and rows of the long groups' v region
 };
 
 // Byte offsets of the tables in a plan workspace, and its size.
 struct PlanLayout {
     uint64_t off_tok = 0, off_blocks = 0, off_tiles = 0, off_btok = 0, off_ttok = 0, off_tsig = 0,
              off_tw = 0, off_mblocks = 0, off_part = 0;
+    uint64_t off_lv = 0;   // long groups' v rows, from off_part (plain plans)
     uint64_t image_bytes = 0, part_bytes = 0, ws_bytes = 0;
 };
 
@@ -216,8 +220,19 @@ PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp,
     L.off_tw = o;      o = round_up(o + 4ull * T, 256);
     L.off_mblocks = o; o = round_up(o + sizeof(lora::MergeBlock) * uint64_t(c.mb), 256);
     L.image_bytes = o;
-    L.part_bytes = 4ull * max_shrink_units(d, c.rt, c.tt, mp, bound) * c.tt * lora::kTile *
-                   lora::kTile;
+    // the shrink's partial tiles: every rank tile at the plan's tiles per
+    // block (a merge plan), or the short groups' tiles at one 16-token tile
+    // each followed by the long groups' v rows (a plain plan: [rows][mp][r_max]
+    // float32, written by sgmv_shrink_partials for sgmv_expand_partials);
+    // a bound covers both kinds
+    const uint64_t tile_bytes = 4ull * lora::kTile * lora::kTile;
+    const uint64_t merge_part = max_shrink_units(d, c.rt, c.tt, mp, bound) * c.tt * tile_bytes;
+    const uint64_t short_part = round_up(max_shrink_units(d, c.rt - c.rt_long, 1, mp, bound) *
+                                         tile_bytes, 256);
+    const uint64_t long_part = 4ull * uint64_t(c.long_rows) * uint64_t(mp) * uint64_t(d.r_max);
+    L.off_lv = short_part;
+    L.part_bytes = bound ? std::max(merge_part, short_part + long_part)
+                         : c.merge ? merge_part : short_part + long_part;
     L.off_part = o;    o = round_up(o + L.part_bytes, 256);
     L.ws_bytes = o;
     return L;
@@ -243,8 +258,11 @@ struct lora_plan {
     // short groups' by padded rank; no-adapter blocks after
     std::vector<BlockDesc> blocks;
     int32_t nb_long = 0;
-    std::vector<lora::TileDesc> tiles;   // rank tiles of the adapter blocks, in block order
-    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0;
+    // rank tiles of the adapter blocks: the long groups' [0, rt_long), then
+    // the short groups', each kind in group order
+    std::vector<lora::TileDesc> tiles;
+    int32_t rt_long = 0;
+    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0, max_rpad_long = 0;
 
     // device image in the caller's workspace
     void *ws = nullptr;
@@ -263,6 +281,14 @@ struct lora_plan {
     // layer, projections and k-chunks; part_layer -1 = none
     mutable int32_t part_layer = -1, part_nproj = 0, part_c0 = 0;
     mutable int32_t part_projs[LORA_MAX_PROJ] = {};
+    // ... and whether it also holds the long groups' v rows (only
+    // sgmv_shrink_partials writes them; the fused call keeps v in the kernel)
+    mutable bool part_long = false;
+
+    // a plain plan's long groups' blocks run in the prefill kernel, their
+    // rank tiles outside the shrink; a merge plan's run in the shrink
+    bool prefill() const { return !merge_k && nb_long > 0; }
+    int32_t rt_short() const { return rt_total() - (merge_k ? 0 : rt_long); }
 
     int32_t rt_total() const { return int32_t(tiles.size()); }
     int32_t nb_all() const { return int32_t(blocks.size()); }
@@ -274,6 +300,9 @@ struct lora_plan {
         c.nb = nb_all();
         c.rt = rt_total();
         c.tt = tt;
+        c.merge = merge_k > 0;
+        c.rt_long = rt_long;
+        c.long_rows = nb_long > 0 ? rows() : 0;
         return c;
     }
 };
@@ -613,7 +642,8 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     pl->tiles.clear();
     pl->mblocks.clear();
     pl->merge_k = 0;
-    pl->nb_long = pl->nb_act = pl->n_active = pl->max_block = pl->max_rpad = 0;
+    pl->nb_long = pl->nb_act = pl->n_active = pl->max_block = pl->max_rpad = pl->rt_long = 0;
+    pl->max_rpad_long = 0;
     pl->tt = 1;
     pl->token_group.assign(T, -1);
 
@@ -658,6 +688,10 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
         if (m.size() >= size_t(lora::kLongGroup)) long_tokens += m.size();
     const bool use_long = long_tokens >= size_t(lora::kMinLongTokens);
     std::vector<BlockDesc> long_blocks, short_blocks;
+    // rank tiles: the long groups' first (the prefill kernel runs their
+    // whole delta; a plain plan's shrink covers the short tiles alone), a
+    // block's rt_before counting within its own kind
+    std::vector<lora::TileDesc> long_tiles, short_tiles;
     int32_t max_sblock = 0;
     std::vector<int32_t> ssz, esz;
     auto add_group = [&](const std::vector<std::pair<int32_t, int32_t>> &rows, int32_t g,
@@ -669,8 +703,9 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
         const int32_t emax = lg ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
         cut_sizes(int32_t(rows.size()), smax, &ssz);
         int32_t s0 = 0;
+        std::vector<lora::TileDesc> &tiles = lg ? long_tiles : short_tiles;
         for (int32_t sn : ssz) {
-            const int32_t rt_before = int32_t(pl->tiles.size());
+            const int32_t rt_before = int32_t(tiles.size());
             for (int32_t i = 0; i < rt; ++i) {
                 lora::TileDesc td{};
                 td.tok_off = base + s0;
@@ -680,7 +715,7 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
                 td.block = g;
                 td.ext_lo = uint32_t(sl->off & 0xffffffffu);
                 td.ext_hi = uint32_t(sl->off >> 32);
-                pl->tiles.push_back(td);
+                tiles.push_back(td);
             }
             max_sblock = std::max(max_sblock, sn);
             cut_sizes(sn, emax, &esz);
@@ -720,6 +755,9 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     pl->blocks = long_blocks;
     pl->blocks.insert(pl->blocks.end(), short_blocks.begin(), short_blocks.end());
     pl->nb_long = int32_t(long_blocks.size());
+    pl->tiles = long_tiles;
+    pl->tiles.insert(pl->tiles.end(), short_tiles.begin(), short_tiles.end());
+    pl->rt_long = int32_t(long_tiles.size());
     pl->nb_act = int32_t(pl->blocks.size());
     pl->n_active = int32_t(pl->token_order.size());
     short_blocks.clear();
@@ -727,6 +765,8 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     pl->blocks.insert(pl->blocks.end(), short_blocks.begin(), short_blocks.end());
     for (int32_t b = 0; b < pl->nb_act; ++b)
         pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
+    for (int32_t b = 0; b < pl->nb_long; ++b)
+        pl->max_rpad_long = std::max(pl->max_rpad_long, pl->blocks[b].r_pad);
     const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
     pl->weighted = weighted;
@@ -930,6 +970,7 @@ uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t nu
     const int64_t sblocks = std::min<int64_t>(T, T / lora::kTile + 1 + std::min<int64_t>(num_segs, T));
     c.rt = sblocks * ((p->d.r_max + lora::kTile - 1) / lora::kTile);
     c.tt = T >= lora::kMinLongTokens ? lora::kMaxBlockTokens / lora::kTile : 1;
+    c.long_rows = T >= lora::kMinLongTokens ? T : 0;
     return plan_layout(p->d, c, max_proj, true).ws_bytes;
 }
 
@@ -1108,20 +1149,32 @@ lora_status check_y(const lora_pool *p, int32_t T, int32_t nproj, const int32_t 
 // average call went from 14.1 to 12.4 us.  Decode blocks (one tile) keep a
 // unit per projection.
 constexpr int32_t kShrinkMaxUnitProj = 3;
-bool shrink_mp(const lora_plan *pl, int32_t nproj) {
-    return pl->tt >= 2 && nproj > 1 && nproj <= kShrinkMaxUnitProj;
+bool shrink_mp(int32_t tt, int32_t nproj) {
+    return tt >= 2 && nproj > 1 && nproj <= kShrinkMaxUnitProj;
+}
+
+// The shrink's share of a plan: the rank tiles [first, first + count) at tt
+// 16-token tiles each.  A merge plan's shrink covers all of its tiles; a
+// plain plan's the short groups' (the prefill kernel runs the long groups'
+// delta whole), one 16-token tile each.
+struct ShrinkShare {
+    int32_t first, count, tt;
+};
+ShrinkShare shrink_share(const lora_plan *pl) {
+    if (pl->merge_k) return ShrinkShare{0, pl->rt_total(), pl->tt};
+    return ShrinkShare{pl->rt_long, pl->rt_short(), 1};
 }
 
 // k-chunking of the shrink: about kShrinkTargetGroups workgroups per launch, each
 // wave loading at most `frags` fragments (all issued up front); chunks are a
 // multiple of 4 fragment spans so the 4 waves split them evenly.
-void shrink_geometry(const lora_plan *pl, int32_t nproj, int32_t h_in, int32_t span,
+void shrink_geometry(const ShrinkShare &sh, int32_t nproj, int32_t h_in, int32_t span,
                      int32_t *kc, int32_t *c0) {
     // workgroups per k-chunk: one per rank tile and projection, or one per
     // rank tile for units over every projection
-    const int64_t per_chunk = int64_t(shrink_mp(pl, nproj) ? 1 : nproj) *
-                              std::max(pl->rt_total(), 1);
-    const int32_t frags = pl->tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
+    const int64_t per_chunk = int64_t(shrink_mp(sh.tt, nproj) ? 1 : nproj) *
+                              std::max(sh.count, 1);
+    const int32_t frags = sh.tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
     const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
     int64_t want = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
     want = std::max<int64_t>(1, std::min<int64_t>(want, steps));
@@ -1165,15 +1218,17 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         pl->part_c0 = c0;
         for (int i = 0; i < nproj; ++i) pl->part_projs[i] = projs[i];
     };
-    if (pl->nb_act == 0) {
+    const ShrinkShare sh = shrink_share(pl);
+    if (sh.count == 0) {
         record(0);
         return LORA_OK;
     }
     lora::ShrinkArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
-    a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_ttok);
-    a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->lay.off_tiles);
+    a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_ttok) +
+                 int64_t(sh.first) * lora::kMaxBlockTokens;
+    a.tiles = reinterpret_cast<const lora::TileDesc *>(ws + pl->lay.off_tiles) + sh.first;
     a.partial = pt.ptr;
     a.x = x;
     a.ldx = ldx;
@@ -1181,57 +1236,53 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.nproj = nproj;
     a.h_in = cc.h_in;
     a.h_in_pad = int32_t(h_in_pad(&p->d, projs[0]));
-    shrink_geometry(pl, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
-    const bool mp = shrink_mp(pl, nproj);
-    a.units = (mp ? 1 : nproj) * pl->rt_total() * a.c0;
+    shrink_geometry(sh, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
+    const bool mp = shrink_mp(sh.tt, nproj);
+    a.units = (mp ? 1 : nproj) * sh.count * a.c0;
     a.grid = grid_for(a.units, mp ? 1 : nproj);
     a.x_bytes = uint32_t(tensor_bytes(pl->T, ldx, cc.h_in, cc.es));
-    const uint64_t need = 4ull * uint64_t(nproj) * pl->rt_total() * a.c0 * pl->tt * lora::kTile *
+    const uint64_t need = 4ull * uint64_t(nproj) * sh.count * a.c0 * sh.tt * lora::kTile *
                           lora::kTile;
     if (need > lora::kMaxTensorBytes)   // the expands address the partials within 2 GiB
         return fail(LORA_EINVAL, "the call's shrink partials would span %llu bytes, more than "
                     "2 GiB: split the batch", (unsigned long long)need);
-    if (need > pt.bytes) {
+    const uint64_t room = pt.in_workspace && !pl->merge_k ? std::min(pt.bytes, pl->lay.off_lv)
+                                                          : pt.bytes;
+    if (need > room) {
         if (!pt.in_workspace)
             return fail(LORA_EINVAL, "the call's shrink partials (%llu bytes) exceed the static "
                         "scratch of %llu bytes: split the batch",
                         (unsigned long long)need, (unsigned long long)pt.bytes);
         return fail(LORA_ESTATE, "partial buffer too small (%llu > %llu)",
-                    (unsigned long long)need, (unsigned long long)pt.bytes);
+                    (unsigned long long)need, (unsigned long long)room);
     }
-    hipError_t e = lora::launch_shrink(p->d.dtype, pl->tt, mp, a, st);
+    hipError_t e = lora::launch_shrink(p->d.dtype, sh.tt, mp, a, st);
     if (e != hipSuccess) return hip_fail(e, "shrink launch");
     *c0_out = a.c0;
     record(a.c0);
     return LORA_OK;
 }
 
+// v of the short groups' blocks from the shrink's partials (the long
+// groups' v comes from the prefill kernel).
 lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, int32_t c0,
                        float *v, int64_t ldv, hipStream_t st) {
-    if (pl->nb_act == 0) return LORA_OK;
+    if (pl->nb_act == pl->nb_long) return LORA_OK;
     lora::ReduceArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
-    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks) + pl->nb_long;
     a.partial = reinterpret_cast<const float *>(ws + pl->lay.off_part);
     a.partial_bytes = uint32_t(std::min<uint64_t>(pl->lay.part_bytes, lora::kMaxTensorBytes));
     a.v = v;
     a.ldv = ldv;
-    a.nb = pl->nb_act;
+    a.nb = pl->nb_act - pl->nb_long;
     a.nproj = nproj;
     a.c0 = c0;
     a.r_max = p->d.r_max;
-    hipError_t e = lora::launch_reduce(pl->tt, a, st);
+    hipError_t e = lora::launch_reduce(1, a, st);
     if (e != hipSuccess) return hip_fail(e, "reduce launch");
     return LORA_OK;
-}
-
-// K-steps of the largest padded rank in the plan (the expand kernels are
-// built for 1, 2 or 4)
-int32_t plan_ksteps(const lora_pool *p, const lora_plan *pl) {
-    const int32_t span = 4 * (16 / esize(p->d.dtype));
-    int32_t ks = std::max(1, (pl->max_rpad + span - 1) / span);
-    return ks == 3 ? 4 : ks;
 }
 
 // Cores of jointly compressed adapters for one call (kind 0: none).
@@ -1304,8 +1355,11 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
                        const Partials *pt = nullptr) {
     if (pl->merge_k) return run_expand_merge(p, pl, layer, nproj, projs, yoff, c0, y, ldy, base,
                                              ldb, st, pt ? *pt : workspace_partials(pl));
+    // the short groups' blocks, then the blocks without an adapter (the long
+    // groups' blocks [0, nb_long) run in the prefill kernel)
     const int32_t nb = base ? pl->nb_all() : pl->nb_act;
-    if (nb == 0) return LORA_OK;
+    const int32_t nl = pl->nb_long;
+    if (nb == nl) return LORA_OK;
     lora::ExpandArgs a{};
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
@@ -1329,7 +1383,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     }
     a.nproj = nproj;
     a.r_max = p->d.r_max;
-    a.ptt = pl->tt;
+    a.ptt = 1;
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, esize(p->d.dtype)));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, esize(p->d.dtype))) : 0u;
     a.v_bytes = v ? uint32_t(tensor_bytes(pl->T, ldv, ldv, 4)) : 0u;
@@ -1344,34 +1398,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         for (int i = 0; i < nproj; ++i)
             a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;
     }
-    // The long groups' blocks [0, nb_long) go to the MFMA expand, the rest
-    // (short groups' blocks, then the blocks without an adapter) to the decode
-    // expand: two launches on the stream when a batch has both.
-    const int32_t nl = std::min(pl->nb_long, nb);
-    if (nl > 0) {
-        // K-steps of the largest padded rank fix the rows per wave (the wave
-        // keeps 8 B fragments); 4 waves per workgroup; row chunks per wave:
-        // about kTargetGroups workgroups per launch
-        lora::ExpandArgs m = a;
-        const int32_t ks = plan_ksteps(p, pl);
-        const int64_t chunk_rows = int64_t(16 * lora::expand_tiles(ks)) * lora::kWaves;
-        // token tiles per unit, and token slices per block
-        const int32_t ttu = std::min<int32_t>(pl->tt, lora::kExpandUnitTiles);
-        m.tslices = pl->tt / ttu;
-        int64_t rows = 0;
-        for (int i = 0; i < nproj; ++i) rows += m.h_out[i];
-        m.chunks = int32_t(std::max<int64_t>(1, std::min<int64_t>(
-            8, rows * nl * m.tslices / (chunk_rows * lora::kTargetGroups))));
-        const int32_t rows_per_group = int32_t(chunk_rows) * m.chunks;
-        m.oc_prefix[0] = 0;
-        for (int i = 0; i < nproj; ++i)
-            m.oc_prefix[i + 1] = m.oc_prefix[i] + (m.h_out[i] + rows_per_group - 1) / rows_per_group;
-        for (int i = nproj; i < LORA_MAX_PROJ; ++i) m.oc_prefix[i + 1] = INT32_MAX;
-        m.units = nl * m.tslices * m.oc_prefix[nproj];
-        const hipError_t e = lora::launch_expand(p->d.dtype, ttu, ks, m, grid_for(m.units, 1), st);
-        if (e != hipSuccess) return hip_fail(e, "expand launch");
-    }
-    if (nb > nl) {
+    {
         // rank classes: runs of equal padded rank in block order (short
         // blocks by rank, largest first; then the blocks without an adapter)
         for (int k = 0; k < lora::kMaxClasses; ++k) a.cls_rb[k] = 0;
@@ -1402,6 +1429,132 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     return LORA_OK;
 }
 
+// The long groups' blocks of a plain plan in the prefill kernel: the whole
+// delta (mode kPrefillFused: x in, y out), the A step alone (kPrefillShrink:
+// v rows out) or the B step alone (kPrefillExpand: v rows in).  v rows are a
+// caller's v by token row (v_by_pos false) or the workspace's long region
+// by plan position.
+struct PrefillIO {
+    int32_t mode = lora::kPrefillFused;
+    const void *x = nullptr;
+    int64_t ldx = 0;
+    float *v = nullptr;
+    int64_t ldv = 0;
+    bool v_by_pos = false;
+    void *y = nullptr;
+    int64_t ldy = 0;
+    const void *base = nullptr;
+    int64_t ldb = 0;
+};
+
+lora_status run_prefill(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                        const int32_t *projs, const int32_t *yoff, const CallCheck &cc,
+                        const PrefillIO &io, hipStream_t st, const Cores &cores = Cores()) {
+    if (!pl->prefill()) return LORA_OK;
+    lora::PrefillArgs a{};
+    const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
+    a.slab = p->slab;
+    a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_btok);
+    a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks);
+    a.x = io.x;
+    a.ldx = io.ldx;
+    a.y = io.y;
+    a.ldy = io.ldy;
+    a.base = io.base;
+    a.ldb = io.ldb;
+    a.v = io.v;
+    a.ldv = io.ldv;
+    a.v_by_pos = io.v_by_pos ? 1 : 0;
+    for (int i = 0; i < nproj; ++i) {
+        a.coef_a[i] = p->coef_a(layer, projs[i]);
+        a.coef_b[i] = p->coef_b(layer, projs[i]);
+        a.h_out[i] = p->d.h_out[projs[i]];
+        a.y_off[i] = yoff ? yoff[i] : 0;
+    }
+    a.h_in = cc.h_in;
+    a.h_in_pad = int32_t(h_in_pad(&p->d, projs[0]));
+    a.r_max = p->d.r_max;
+    a.x_bytes = io.x ? uint32_t(tensor_bytes(pl->T, io.ldx, cc.h_in, cc.es)) : 0u;
+    a.y_bytes = io.y ? uint32_t(tensor_bytes(pl->T, io.ldy, io.ldy, cc.es)) : 0u;
+    a.base_bytes = io.base ? uint32_t(tensor_bytes(pl->T, io.ldb, io.ldb, cc.es)) : 0u;
+    if (pl->weighted) a.tok_w = reinterpret_cast<const float *>(ws + pl->lay.off_tw);
+    if (cores.kind && io.mode != lora::kPrefillShrink) {
+        const int64_t per = cores.kind == LORA_SIGMA_FULL ? int64_t(p->d.r_max) * p->d.r_max
+                                                           : int64_t(p->d.r_max);
+        a.sigma = cores.sigma;
+        a.sigma_kind = cores.kind;
+        a.tok_sig = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tsig);
+        a.sig_stride = int64_t(p->d.num_layers) * p->d.num_proj * per;
+        for (int i = 0; i < nproj; ++i)
+            a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;
+    }
+    // units: (block, token tile, row part); a launch of few tiles splits the
+    // tiles' output rows so that it still has about kPrefillTargetGroups
+    // workgroups (the shrink step alone has no rows to split)
+    const int64_t tiles = int64_t(pl->nb_long) * lora::kPrefillTiles;
+    int32_t split = 1;
+    if (io.mode != lora::kPrefillShrink)
+        while (split < lora::kPrefillMaxSplit && tiles * split < lora::kPrefillTargetGroups)
+            split *= 2;
+    if (tiles * split >= (int64_t(1) << 30)) return fail(LORA_ESTATE, "too many prefill tiles");
+    a.osplit = split;
+    a.units = int32_t(tiles * split);
+    const int32_t rtiles = (pl->max_rpad_long + lora::kTile - 1) / lora::kTile;
+    const int32_t rtm = rtiles <= 1 ? 1 : rtiles == 2 ? 2 : 4;
+    const hipError_t e = lora::launch_prefill(p->d.dtype, io.mode, nproj, rtm, a,
+                                              grid_for(a.units, 1), st);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return LORA_OK;
+}
+
+// The workspace's region of the long groups' v rows ([rows][max_proj][r_max]).
+float *long_v(const lora_plan *pl) {
+    return reinterpret_cast<float *>(static_cast<uint8_t *>(pl->ws) + pl->lay.off_part +
+                                     pl->lay.off_lv);
+}
+
+// The B step from a caller's v: the short groups' blocks in the decode
+// expand, the long groups' in the prefill kernel.
+lora_status expand_from_v(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                          const int32_t *projs, const int32_t *yoff, const CallCheck &cc,
+                          const float *v, int64_t ldv, void *y, int64_t ldy, hipStream_t st,
+                          const Cores &cores) {
+    lora_status s = run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0, st,
+                               cores);
+    if (s != LORA_OK) return s;
+    PrefillIO io;
+    io.mode = lora::kPrefillExpand;
+    io.v = const_cast<float *>(v);
+    io.ldv = ldv;
+    io.y = y;
+    io.ldy = ldy;
+    return run_prefill(p, pl, layer, nproj, projs, yoff, cc, io, st, cores);
+}
+
+// The fused delta: the short groups' shrink into `pt`, the long groups'
+// whole delta in the prefill kernel, then the short groups' expand.
+lora_status fused_body(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
+                       const int32_t *projs, const int32_t *yoff, const CallCheck &cc,
+                       const void *x, int64_t ldx, const void *base, int64_t ldb, void *y,
+                       int64_t ldy, hipStream_t st, const Cores &cores, const Partials &pt) {
+    int32_t c0 = 0;
+    lora_status s = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, st, &c0, pt);
+    if (s != LORA_OK) return s;
+    if (pt.in_workspace) pl->part_long = false;
+    PrefillIO io;
+    io.mode = lora::kPrefillFused;
+    io.x = x;
+    io.ldx = ldx;
+    io.y = y;
+    io.ldy = ldy;
+    io.base = base;
+    io.ldb = ldb;
+    s = run_prefill(p, pl, layer, nproj, projs, yoff, cc, io, st, cores);
+    if (s != LORA_OK) return s;
+    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, st,
+                      cores, &pt);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1428,7 +1581,16 @@ lora_status sgmv_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     int32_t c0 = 0;
     st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, workspace_partials(pl));
     if (st != LORA_OK) return st;
-    return run_reduce(p, pl, nproj, c0, v, ldv, hs);
+    pl->part_long = false;
+    st = run_reduce(p, pl, nproj, c0, v, ldv, hs);
+    if (st != LORA_OK) return st;
+    PrefillIO io;
+    io.mode = lora::kPrefillShrink;
+    io.x = x;
+    io.ldx = ldx;
+    io.v = v;
+    io.ldv = ldv;
+    return run_prefill(p, pl, layer, nproj, projs, nullptr, cc, io, hs);
 }
 
 lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
@@ -1448,8 +1610,8 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, 
         return fail(LORA_EINVAL, "v spans more than 2 GiB");
     st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,
-                      static_cast<hipStream_t>(stream));
+    return expand_from_v(p, pl, layer, nproj, projs, yoff, cc, v, ldv, y, ldy,
+                         static_cast<hipStream_t>(stream), Cores());
 }
 
 lora_status sgmv_expand_sigma(const lora_pool *p, const lora_plan *pl, int32_t layer,
@@ -1470,8 +1632,8 @@ lora_status sgmv_expand_sigma(const lora_pool *p, const lora_plan *pl, int32_t l
         return fail(LORA_EINVAL, "v spans more than 2 GiB");
     st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, 0, v, ldv, y, ldy, nullptr, 0,
-                      static_cast<hipStream_t>(stream), cores);
+    return expand_from_v(p, pl, layer, nproj, projs, yoff, cc, v, ldv, y, ldy,
+                         static_cast<hipStream_t>(stream), cores);
 }
 
 lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
@@ -1506,12 +1668,8 @@ lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t la
         st = check_y(p, pl->T, nproj, projs, yoff, base, ldb, "base", cc);
         if (st != LORA_OK) return st;
     }
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    int32_t c0 = 0;
-    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, workspace_partials(pl));
-    if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
-                      cores);
+    return fused_body(p, pl, layer, nproj, projs, yoff, cc, x, ldx, base, ldb, y, ldy,
+                      static_cast<hipStream_t>(stream), cores, workspace_partials(pl));
 }
 
 lora_status sgmv_fused_static(const lora_pool *p, const lora_plan *pl, int32_t layer,
@@ -1539,12 +1697,8 @@ lora_status sgmv_fused_static(const lora_pool *p, const lora_plan *pl, int32_t l
     const hipError_t e = lora::static_scratch(&ptr, &pt.bytes);
     if (e != hipSuccess) return hip_fail(e, "static scratch address");
     pt.ptr = static_cast<float *>(ptr);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    int32_t c0 = 0;
-    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, pt);
-    if (st != LORA_OK) return st;
-    return run_expand(p, pl, layer, nproj, projs, yoff, c0, nullptr, 0, y, ldy, base, ldb, hs,
-                      Cores(), &pt);
+    return fused_body(p, pl, layer, nproj, projs, yoff, cc, x, ldx, base, ldb, y, ldy,
+                      static_cast<hipStream_t>(stream), Cores(), pt);
 }
 
 lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
@@ -1566,10 +1720,24 @@ lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_
         pl->part_nproj = nproj;
         pl->part_c0 = 0;
         for (int i = 0; i < nproj; ++i) pl->part_projs[i] = projs[i];
+        pl->part_long = true;
         return LORA_OK;
     }
-    return run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, static_cast<hipStream_t>(stream),
-                      &c0, workspace_partials(pl));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = run_shrink(p, pl, layer, nproj, projs, x, ldx, cc, hs, &c0, workspace_partials(pl));
+    if (st != LORA_OK) return st;
+    // the long groups' v rows (their A step) into the workspace's long region
+    PrefillIO io;
+    io.mode = lora::kPrefillShrink;
+    io.x = x;
+    io.ldx = ldx;
+    io.v = pl->prefill() ? long_v(pl) : nullptr;
+    io.ldv = int64_t(pl->max_proj) * p->d.r_max;
+    io.v_by_pos = true;
+    st = run_prefill(p, pl, layer, nproj, projs, nullptr, cc, io, hs);
+    if (st != LORA_OK) return st;
+    pl->part_long = true;
+    return LORA_OK;
 }
 
 lora_status sgmv_expand_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
@@ -1598,6 +1766,9 @@ lora_status sgmv_expand_partials_sigma(const lora_pool *p, const lora_plan *pl, 
     if (!same)
         return fail(LORA_ESTATE, "the plan's workspace holds no shrink partials of layer %d "
                                  "and these projections", layer);
+    if (pl->prefill() && !pl->part_long)
+        return fail(LORA_ESTATE, "the plan's workspace holds no v rows of its long groups: "
+                                 "the last shrink was not sgmv_shrink_partials");
     if (pl->T == 0) return LORA_OK;
     st = check_y(p, pl->T, nproj, projs, yoff, y, ldy, "y", cc);
     if (st != LORA_OK) return st;
@@ -1605,8 +1776,20 @@ lora_status sgmv_expand_partials_sigma(const lora_pool *p, const lora_plan *pl, 
         st = check_y(p, pl->T, nproj, projs, yoff, base, ldb, "base", cc);
         if (st != LORA_OK) return st;
     }
-    return run_expand(p, pl, layer, nproj, projs, yoff, pl->part_c0, nullptr, 0, y, ldy, base,
-                      ldb, static_cast<hipStream_t>(stream), cores);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = run_expand(p, pl, layer, nproj, projs, yoff, pl->part_c0, nullptr, 0, y, ldy, base, ldb,
+                    hs, cores);
+    if (st != LORA_OK) return st;
+    PrefillIO io;
+    io.mode = lora::kPrefillExpand;
+    io.v = pl->prefill() ? long_v(pl) : nullptr;
+    io.ldv = int64_t(pl->max_proj) * p->d.r_max;
+    io.v_by_pos = true;
+    io.y = y;
+    io.ldy = ldy;
+    io.base = base;
+    io.ldb = ldb;
+    return run_prefill(p, pl, layer, nproj, projs, yoff, cc, io, hs, cores);
 }
 
 }  // extern "C"

@@ -36,12 +36,18 @@ constexpr int kSumWays = 4;
 // rank classes of the decode expand: distinct padded ranks (multiples of 8)
 // of the blocks, and 0 for tokens without an adapter
 constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
-constexpr int kTargetGroups = 1024;          // MFMA expand: workgroups aimed for per launch
-// MFMA expand: 16-token tiles of a block per unit (a 64-token block is
-// kMaxBlockTokens / (16 * kExpandUnitTiles) units over the same rows).  One
-// tile a unit keeps the kernel near 150 VGPRs (3 waves a SIMD) where 4 tiles
-// spilled into AGPRs at 1 wave: 4.5% faster per prefill step, 2 tiles 3.5%.
-constexpr int kExpandUnitTiles = 1;
+// Prefill (long groups' blocks): one workgroup of kPrefillWaves waves per
+// 16-token tile of a block, kPrefillTiles tiles per block, runs the whole
+// delta of its tokens (see k_prefill).  16 waves fill a CU's 4 SIMDs with
+// one workgroup.
+constexpr int kPrefillWaves = 16;
+constexpr int kPrefillTiles = kMaxBlockTokens / kTile;
+// Prefill launches aim for this many workgroups at least: a launch with
+// fewer tiles splits each tile's output rows over up to kPrefillMaxSplit
+// workgroups (each then runs the A step of its tile itself).
+constexpr int kPrefillTargetGroups = 256;
+constexpr int kPrefillMaxSplit = 4;
+enum { kPrefillFused = 0, kPrefillShrink = 1, kPrefillExpand = 2 };
 // Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
 // more, shorter ones here (the expand then also sums fewer partials):
 // measured on the full stack, 384 beat 1024 by 3.5% per step, and 256 beat
@@ -124,11 +130,11 @@ struct ReduceArgs {
 };
 
 
-// Expand: one workgroup per unit (block b, projection i, slice of 4 * ocw
-// output rows; ocw = chunks * 16 * expand_tiles(ks)).  Each wave first issues the
-// loads of all its B rows, then the workgroup gathers its tokens' v into LDS
-// once (summing the shrink partials in a fixed order, or reading a caller's
-// v), and each wave writes y = y_in + s * (B v), rounded once.
+// Decode expand: one workgroup per unit (see launch_expand_decode).  Each
+// wave first issues the loads of its B rows, then the workgroup gathers its
+// tokens' v into LDS once (summing the shrink partials in a fixed order, or
+// reading a caller's v), and each wave writes y = y_in + s * (B v), rounded
+// once.
 struct ExpandArgs {
     const uint8_t *slab;
     const int32_t *tok;          // plan token order
@@ -144,10 +150,7 @@ struct ExpandArgs {
     int64_t coef_b[LORA_MAX_PROJ];  // B block offset = extent + r_pad * esize * coef_b[i]
     int32_t h_out[LORA_MAX_PROJ];
     int32_t y_off[LORA_MAX_PROJ];
-    int32_t oc_prefix[LORA_MAX_PROJ + 1];  // row chunks of projections before i
-    int32_t tslices;             // MFMA expand: token slices of TT tiles per block
     int32_t nproj;
-    int32_t chunks;              // row chunks per wave (16 * expand_tiles(ks) rows each)
     int32_t c0;                  // partial chunks (when partial != null)
     int32_t ptt;                 // 16-token tiles per shrink partial tile
     int32_t units;               // (the grid is units rounded up to kXcds)
@@ -175,6 +178,44 @@ struct ExpandArgs {
     // of rows = 1 << decode_unit_rows_log2(padded rank) output rows.
     int32_t cls_unit0[kMaxClasses + 1];
     int32_t cls_rb[kMaxClasses];
+};
+
+// Prefill: units are (long block, token tile, row part), unit u = (b *
+// kPrefillTiles + tile) * osplit + part; the blocks [0, units / (kPrefillTiles
+// * osplit)) of the plan are the long groups' blocks.  v rows (the shrink
+// step's output, the expand step's input when it runs alone) are token rows
+// of a caller's v, or plan positions (tok_off + i) of the workspace's region.
+struct PrefillArgs {
+    const uint8_t *slab;
+    const int32_t *block_tok;    // [nb][kMaxBlockTokens] token rows, -1 padded
+    const BlockDesc *blocks;
+    const void *x;               // the shrink step's activations [T][ldx]
+    void *y;                     // the expand step's output [T][ldy]
+    const void *base;            // nullable: y_in = base, else y_in = y
+    float *v;                    // v rows when a step runs alone
+    const float *tok_w;          // weighted plans: per plan position (null: none)
+    const float *sigma;          // cores of jointly compressed adapters
+    const int32_t *tok_sig;      // core per plan position (-1: none)
+    int64_t ldx;
+    int64_t ldy;
+    int64_t ldb;
+    int64_t ldv;
+    int64_t coef_a[LORA_MAX_PROJ];  // A block offset = extent + r_pad * esize * coef_a[i]
+    int64_t coef_b[LORA_MAX_PROJ];  // B block offset = extent + r_pad * esize * coef_b[i]
+    int64_t sig_stride;
+    int64_t sig_off[LORA_MAX_PROJ];
+    int32_t h_out[LORA_MAX_PROJ];
+    int32_t y_off[LORA_MAX_PROJ];
+    int32_t h_in;
+    int32_t h_in_pad;            // stored K of A: h_in rounded up to whole K-blocks
+    int32_t r_max;
+    int32_t units;               // (the grid is units rounded up to kXcds)
+    int32_t osplit;              // workgroups sharing a tile's output rows
+    int32_t v_by_pos;            // v rows: plan positions (1) or token rows (0)
+    int32_t sigma_kind;          // 0 none, 1 diagonal, 2 full (as ExpandArgs)
+    uint32_t x_bytes;            // buffer ranges (each at most kMaxTensorBytes)
+    uint32_t y_bytes;
+    uint32_t base_bytes;
 };
 
 // Weighted merge of several adapters per request, in one pass: the shrink
@@ -256,8 +297,9 @@ constexpr bool decode_rows_agree() {
 }
 static_assert(decode_rows_agree(), "decode unit rows are kWaves wave slices");
 
-// 16-row output tiles per expand wave, for kernels built for `ks` K-steps
-// (ranks / (4 fragment elements)) at most: the wave keeps 8 B fragments.
+// 16-row output tiles per chunk of the MFMA expand step, for kernels built
+// for `ks` K-steps (ranks / (4 fragment elements)) at most: the wave keeps 8 B
+// fragments.
 constexpr int expand_tiles(int ks) { return ks >= 8 ? 1 : 8 / ks; }
 
 // Sets the thread's last-error message (lora_last_error) and returns st.
@@ -273,8 +315,10 @@ hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStr
 hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
                          int h_in_pad, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
-hipError_t launch_expand(int dtype, int tt, int ks, const ExpandArgs &a, int grid,
-                         hipStream_t s);
+// prefill: mode kPrefillFused / kPrefillShrink / kPrefillExpand; np the
+// call's projections (1..3); rtm the launch's largest rank tiles (1, 2 or 4)
+hipError_t launch_prefill(int dtype, int mode, int np, int rtm, const PrefillArgs &a, int grid,
+                          hipStream_t s);
 // decode expand (every block of the plan within kValuTokens tokens)
 // nvm: the largest decode_nvt of the launch's rank classes
 hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int grid,

@@ -189,11 +189,13 @@ def test_decode_rank_bound(dtype, r_top):
     check_workload(dw, tight=True, threads=4)
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(6))
 def test_prefill_blocks(seed):
     """Long same-adapter segments (over 1024 tokens in long groups, so the
-    MFMA expand runs): several 64-token blocks per group, ragged tails."""
-    T = [1030, 1100, 1300, 1601][seed]
+    prefill kernel runs): several 64-token blocks per group, ragged tails;
+    launches of few tiles split each tile's output rows over 4 and 2
+    workgroups (T up to 1601, and 2600), or not at all (4100)."""
+    T = [1030, 1100, 1300, 1601, 2600, 4100][seed]
     w = random_case(100 + seed, T=T, h_in=512, h_out=256, n_adapters=3, max_seg=T,
                     no_adapter_frac=0.0, r_choices=[8, 16, 32, 64])
     log(f"[parity] prefill {seed} T={T} segments={list(np.diff(w.seg_starts))}")
@@ -207,9 +209,9 @@ def test_prefill_blocks(seed):
 @pytest.mark.parametrize("nproj,dtype", [(2, "bf16"), (3, "bf16"), (2, "f32"), (3, "f32")])
 def test_prefill_multi_projection(nproj, dtype):
     """Calls of 2 and 3 projections over blocks of several token tiles: the
-    shrink runs one unit per (rank tile, k-chunk) over all of the call's
-    projections (x loaded once); ranks up to 64 (4 rank tiles), distinct
-    h_out per projection, ragged prompts beside decode steps."""
+    prefill kernel forms every projection's v from one load of x per K-block
+    and expands each; ranks up to 64 (4 rank tiles), distinct h_out per
+    projection, ragged prompts beside decode steps."""
     seed = {2: 91, 3: 92}[nproj] + (10 if dtype == "f32" else 0)
     base = mixed_case(seed, dtype=dtype, has_base=nproj == 3, h_in=520, h_out=8)
     g = np.random.default_rng(seed)
@@ -228,8 +230,8 @@ def test_prefill_multi_projection(nproj, dtype):
 @pytest.mark.parametrize("has_base", [True, False])
 def test_mixed_blocks(dtype, has_base):
     """Prompts and decode steps in one batch: the long groups take 64-token
-    blocks (MFMA expand), the short groups and the tokens without an adapter
-    4-token blocks (decode expand), two expand launches per call."""
+    blocks (the prefill kernel), the short groups and the tokens without an
+    adapter 4-token blocks (shrink and decode expand): three launches a call."""
     seed = {("bf16", True): 81, ("bf16", False): 82, ("f32", True): 83, ("f32", False): 84}[
         (dtype, has_base)]
     w = mixed_case(seed, dtype=dtype, has_base=has_base, h_in=384, h_out=264)
@@ -246,9 +248,10 @@ def test_mixed_blocks(dtype, has_base):
 def test_two_step_path():
     """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
     float32 bound of the oracle, deterministic, and bit-identical to
-    sgmv_fused (every kernel sums the k-chunk partials in one order) on both
-    the decode path (shrink and decode expand) and the prefill path, also
-    with the shrink's units over all three projections of a call."""
+    sgmv_fused on both the decode path (every kernel sums the k-chunk
+    partials in one order) and the prefill path (the prefill kernel's A step
+    and B step alone form v and y as its fused form does), also over all
+    three projections of a call."""
     three = dataclasses.replace(
         mixed_case(72, h_in=264, h_out=8, has_base=False),
         projs=tuple(Proj(f"p{i}", 264, ho, "x") for i, ho in enumerate((96, 40, 136))),
@@ -273,13 +276,23 @@ def test_two_step_path():
             assert np.array_equal(from_device(v).view(np.uint8), outs[0][k].view(np.uint8)), k
 
 
-def test_shrink_output_layout():
+@pytest.mark.parametrize("prefill", [False, True])
+def test_shrink_output_layout(prefill):
     """v holds A x in columns [i*r_max, i*r_max + rank) and zeros up to r_max;
-    rows of tokens without an adapter are left as they were."""
+    rows of tokens without an adapter are left as they were.  Decode blocks
+    (shrink and reduce) and a batch with long groups (the prefill kernel's A
+    step) over three projections."""
     import heterogeneous_adapter_batching_amd as hab
-    w = multi_proj_case(7, T=40, r_max=32)
+    if prefill:
+        base = mixed_case(74, h_in=264, h_out=8, r_choices=(8, 16, 24, 32), r_max=32)
+        w = dataclasses.replace(
+            base, projs=tuple(Proj(f"p{i}", 264, ho, "x") for i, ho in enumerate((96, 40, 136))),
+            calls=((0, 1, 2),))
+    else:
+        w = multi_proj_case(7, T=40, r_max=32)
     w = dataclasses.replace(w, ranks=np.minimum(w.ranks, 32))
     dw = DeviceWorkload(w, threads=4)
+    assert (dw.plan.stats()["max_block_tokens"] > 16) == prefill
     n = len(w.projs)
     v = torch.full((w.num_tokens, n * 32 + 8), 7.0, device="cuda")
     hab.sgmv_shrink(dw.pool, dw.plan, 0, tuple(range(n)), dw.x[(0, "x")], v)
@@ -858,7 +871,9 @@ def test_weight_errors():
 def test_split_fused_bitexact():
     """sgmv_shrink_partials then sgmv_expand_partials give sgmv_fused's bits
     (decode blocks, prefill blocks, a mixed batch; with and without base);
-    the expand refuses partials of another call."""
+    the expand refuses partials of another call, and, for a plan with long
+    groups, a workspace whose last shrink was the fused call's (whose long
+    groups' v never left the prefill kernel)."""
     import heterogeneous_adapter_batching_amd as hab
     cases = (random_case(61, T=100, h_in=384, h_out=256, n_adapters=6, has_base=True, max_seg=3),
              random_case(62, T=1300, h_in=256, h_out=128, n_adapters=3, max_seg=600,
@@ -872,6 +887,10 @@ def test_split_fused_bitexact():
         y1 = torch.zeros_like(dw.y[(0, 0)])
         y2 = torch.zeros_like(dw.y[(0, 0)])
         hab.sgmv_fused(dw.pool, dw.plan, 0, (0,), [0], x, y1, base)
+        if dw.plan.stats()["max_block_tokens"] > 16:
+            with pytest.raises(hab.LoraError) as ei:
+                hab.sgmv_expand_partials(dw.pool, dw.plan, 0, (0,), [0], y2, base)
+            assert ei.value.status == -9
         hab.sgmv_shrink_partials(dw.pool, dw.plan, 0, (0,), x)
         hab.sgmv_expand_partials(dw.pool, dw.plan, 0, (0,), [0], y2, base)
         torch.cuda.synchronize()

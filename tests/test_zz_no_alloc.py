@@ -61,15 +61,18 @@ def test_static_scratch_matches_fused():
 
 
 def test_static_scratch_too_small_refused():
-    """A prefill call whose partials exceed the scratch: LORA_EINVAL, and the
-    output is untouched (nothing was enqueued)."""
+    """A call whose shrink partials exceed the scratch (a merge plan of two
+    slots over 16384 tokens, rank 64, three projections: its long groups'
+    rows run in the shrink at 64-token blocks): LORA_EINVAL, and the output
+    is untouched (nothing was enqueued)."""
     import heterogeneous_adapter_batching_amd as hab
     T, h = 16384, 4096
     pool = hab.Pool(1, [h, h, h], [h, h, h], 64, "bf16", slab_bytes=4 * (64 * 8 * h * 2 + 256),
                     max_slots=4)
     for a in range(2):
         pool.reserve(a, 64, 1.0)
-    plan = hab.Plan(pool, T, [0, T // 2, T], [0, 1]).upload(3)
+    plan = hab.Plan.merge(pool, T, [0, T // 2, T], np.array([[0, 1], [1, 0]], np.int32),
+                          np.ones((2, 2), np.float32)).upload(3)
     x = torch.zeros((T, h), dtype=torch.bfloat16, device="cuda")
     y = torch.full((T, 3 * h), 7.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(hab.LoraError) as ei:
