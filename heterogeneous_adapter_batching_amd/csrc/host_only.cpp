@@ -13,7 +13,7 @@ hipError_t launch_pack_a(int, const void *, int, int, void *, int, int, hipStrea
     return hipErrorInvalidValue;
 }
 hipError_t launch_reduce(int, const ReduceArgs &, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_prefill(int, int, int, int, const PrefillArgs &, int, hipStream_t) {
+hipError_t launch_prefill(int, int, int, int, int, const PrefillArgs &, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
 hipError_t launch_expand_decode(int, int, const ExpandArgs &, int, hipStream_t) {

@@ -1261,6 +1261,12 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
 // K-blocks per batch of the shrink step, for `pairs` (projection, rank tile)
 // accumulators: a batch is FB x fragments and FB x pairs A fragments; two
 // batches in flight stay within about 72 VGPRs.
+#ifndef LORA_PREFILL_X_NT
+#define LORA_PREFILL_X_NT 1
+#endif
+#ifndef LORA_PREFILL_EARLY
+#define LORA_PREFILL_EARLY 1
+#endif
 constexpr int prefill_kbatch(int pairs) { return pairs <= 1 ? 4 : pairs <= 3 ? 2 : 1; }
 constexpr int prefill_ksm(int rtm, int e) {
     return (rtm * kTile + 4 * e - 1) / (4 * e) == 3 ? 4 : (rtm * kTile + 4 * e - 1) / (4 * e);
@@ -1273,8 +1279,251 @@ constexpr int prefill_otw(int ksm, int esize) {
                       : (expand_tiles(ksm) / 2 < 1 ? 1 : expand_tiles(ksm) / 2);
 }
 
-template <typename T, int NP, int RTM, int MODE>
-__global__ __launch_bounds__(kPrefillWaves * kWaveSize) void k_prefill(const PrefillArgs a) {
+// The B step of a prefill workgroup for one wave: output rows of every
+// projection of the call, this wave's share of each (whole 32-row pairs),
+// visited as one run of OTW-tile chunks across the projections, so that two
+// chunks are in flight at every step, also where one projection's rows end
+// and the next one's begin.  Per chunk: the B rows (OTW 16-row tiles, TPL
+// tiles per 16-byte load when r_pad packs them) and y_in of the tile's
+// tokens, then the MFMAs against v (from LDS, in three bf16 pieces) and
+// y = y_in + s B v, rounded once.  bf16 rows come in the pair order of the
+// MFMA expand (a lane stores 8 consecutive outputs).
+template <typename T, int NP, int KSM, int TPL, int OTW, int NBUF, bool EARLY, typename Before>
+__device__ __forceinline__ void prefill_rows(const PrefillArgs &a, const BlockDesc &blk,
+                                             int share, int shares, int n, int q, int trow,
+                                             const int (&lrow)[2], float tsc,
+                                             float (*vs)[kTile][LORA_MAX_RANK + 4],
+                                             u32x4 *stage, Before before) {
+    constexpr int E = Elem<T>::E;
+    constexpr int SPAN = 4 * E;
+    constexpr int NL = TPL == 1 ? OTW * KSM : OTW / TPL;   // B loads per chunk
+    constexpr int CH = OTW * kTile;                  // rows per chunk
+    constexpr bool PAIR = sizeof(T) == 2;
+    static_assert(!PAIR || OTW % 2 == 0, "row tiles of a chunk come in pairs");
+    constexpr int NY = PAIR ? OTW / 2 : OTW;         // y_in loads per chunk
+    // bf16 chunks of 4 row tiles: a token's 64 outputs are one 128-byte
+    // line, so y_in and y move 8 tokens' whole lines per instruction (lane l:
+    // token 8 j + l / 8 of instruction j, bytes 16 (l % 8)) and pass through
+    // the wave's LDS rows (stage, 9 16-byte units a token: no bank
+    // conflicts) to and from the MFMA layout; otherwise 16 tokens x 64 bytes
+    // per instruction straight from the MFMA layout
+    constexpr bool STAGE = PAIR && OTW == 4;
+    constexpr int SROW = 9;                          // 16-byte units per staged token row
+    typedef typename Out4<T>::raw raw;
+    typedef typename std::conditional<PAIR, u32x4, raw>::type yraw;
+    const int G = TPL == 1 ? 4 : 4 / TPL;            // vectors per row (packed)
+    const int ks_n = (blk.r_pad + SPAN - 1) / SPAN;  // <= KSM
+
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
+    const int64_t ld_in = a.base ? a.ldb : a.ldy;
+    const bool tv = trow >= 0;
+    // an absent token's row offsets are out of range already
+    const uint32_t in_row = tv ? uint32_t(int64_t(trow) * ld_in * sizeof(T)) : kOOB;
+    const uint32_t y_row = tv ? uint32_t(int64_t(trow) * a.ldy * sizeof(T)) : kOOB;
+    const int lane = n + kTile * q;
+    uint32_t in_line[2], y_line[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        in_line[j] = lrow[j] >= 0 ? uint32_t(int64_t(lrow[j]) * ld_in * sizeof(T)) : kOOB;
+        y_line[j] = lrow[j] >= 0 ? uint32_t(int64_t(lrow[j]) * a.ldy * sizeof(T)) : kOOB;
+    }
+    const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
+    const int lane_tile = TPL == 1 ? 0 : q / G;
+    const uint32_t lane_col = uint32_t(TPL == 1 ? q * E : (q % G) * E) * sizeof(T);
+    auto brow = [&](int tile, int nn) {
+        return PAIR ? (tile & ~1) * kTile + 8 * (nn >> 2) + 4 * (tile & 1) + (nn & 3)
+                    : tile * kTile + nn;
+    };
+
+    // per-projection values by selects (an indexed array would be placed in
+    // memory)
+    auto sel = [](int p, auto v0, auto v1, auto v2) {
+        return NP == 1 || p == 0 ? v0 : NP == 2 || p == 1 ? v1 : v2;
+    };
+    // this wave's rows [lo, hi) of each projection, in chunks
+    int lo[NP], hi[NP], nch[NP];
+    int total = 0;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int h = a.h_out[p];
+        const int rw = ((h + shares - 1) / shares + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+        lo[p] = min(h, share * rw);
+        hi[p] = min(h, lo[p] + rw);
+        nch[p] = (hi[p] - lo[p] + CH - 1) / CH;
+        total += nch[p];
+    }
+    // chunk i -> (projection, first row); past the last chunk: past hi
+    auto where = [&](int i, int &p, int &o0) {
+        p = 0;
+#pragma unroll
+        for (int k = 0; k < NP - 1; ++k)
+            if (p == k && i >= nch[k]) {
+                i -= nch[k];
+                p = k + 1;
+            }
+        o0 = sel(p, lo[0], lo[NP > 1 ? 1 : 0], lo[NP > 2 ? 2 : 0]) + i * CH;
+    };
+
+    auto load = [&](int i, u32x4 (&bf)[NL], yraw (&yin)[NY]) {
+        int p, o0;
+        where(i, p, o0);
+        const int h = sel(p, a.h_out[0], a.h_out[1], a.h_out[2]);
+        const int top = sel(p, hi[0], hi[NP > 1 ? 1 : 0], hi[NP > 2 ? 2 : 0]);
+        const rsrc_t br = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
+                                        uint64_t(blk.r_pad) * sizeof(T) *
+                                            uint64_t(sel(p, a.coef_b[0], a.coef_b[1], a.coef_b[2])),
+                                    uint32_t(h) * uint32_t(blk.r_pad) * sizeof(T));
+        const uint32_t yoff = uint32_t(sel(p, a.y_off[0], a.y_off[1], a.y_off[2])) * sizeof(T);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int t = TPL == 1 ? l / KSM : l * TPL;
+            const int ks = TPL == 1 ? l % KSM : 0;
+            const int row = o0 + brow(t + lane_tile, n);
+            const bool ok = i < total && row < top &&
+                            (TPL > 1 || (ks < ks_n && ks * SPAN + q * E < blk.r_pad));
+            bf[l] = bload16(br, off_or_oob(ok, uint32_t(row) * row_bytes + lane_col +
+                                                   uint32_t(ks * SPAN) * sizeof(T)));
+        }
+#pragma unroll
+        for (int oy = 0; oy < NY; ++oy) {
+            if constexpr (STAGE) {
+                const int o = o0 + 8 * (lane & 7);
+                yin[oy] = bload16(inr, i < total && o < top
+                                           ? in_line[oy] + yoff + uint32_t(o) * sizeof(T) : kOOB);
+            } else {
+                const int o = PAIR ? o0 + oy * 2 * kTile + 8 * q : o0 + oy * kTile + 4 * q;
+                const uint32_t off =
+                    i < total && o < top ? in_row + yoff + uint32_t(o) * sizeof(T) : kOOB;
+                if constexpr (PAIR) yin[oy] = bload16(inr, off);
+                else yin[oy] = Out4<T>::load(inr, off);
+            }
+        }
+    };
+
+    VOperand<T> vop[KSM];
+    int vp = -1;                                     // projection whose v vop holds
+    auto compute = [&](int i, const u32x4 (&bf)[NL], const yraw (&yin)[NY]) {
+        int p, o0;
+        where(i, p, o0);
+        const int top = sel(p, hi[0], hi[NP > 1 ? 1 : 0], hi[NP > 2 ? 2 : 0]);
+        const uint32_t yoff = uint32_t(sel(p, a.y_off[0], a.y_off[1], a.y_off[2])) * sizeof(T);
+        if (p != vp) {                               // wave-uniform: v of projection p
+            vp = p;
+#pragma unroll
+            for (int ks = 0; ks < KSM; ++ks) {
+                float f[E];
+                const int j0 = TPL == 1 ? ks * SPAN + q * E : (q % G) * E;
+                const bool ok = tv && ks < ks_n && j0 < blk.r_pad;
+                const int row = ok ? n : 0, col = ok ? j0 : 0;
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[p][row][col + e]);
+                    f[e] = ok ? w4[0] : 0.f; f[e + 1] = ok ? w4[1] : 0.f;
+                    f[e + 2] = ok ? w4[2] : 0.f; f[e + 3] = ok ? w4[3] : 0.f;
+                }
+                vop[ks].set(f);
+            }
+        }
+        // B v of row tile ot: D rows 4 q .. 4 q + 3 of the tile
+        auto tile_acc = [&](int ot) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (TPL == 1) {
+#pragma unroll
+                for (int ks = 0; ks < KSM; ++ks) {
+                    if (ks >= ks_n) continue;
+#pragma unroll
+                    for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
+                        acc = mma<T>(bf[ot * KSM + ks], vop[ks].piece[pc], acc);
+                }
+            } else {
+                const bool mine = q / G == ot % TPL;     // lane groups of this tile
+#pragma unroll
+                for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc) {
+                    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                    acc = mma<T>(bf[ot / TPL], mine ? vop[0].piece[pc] : z, acc);
+                }
+            }
+            return acc;
+        };
+        if constexpr (STAGE) {                       // y_in rows into the MFMA layout
+#pragma unroll
+            for (int j = 0; j < NY; ++j) stage[(8 * j + (lane >> 3)) * SROW + (lane & 7)] = yin[j];
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int oy = 0; oy < NY; ++oy) {
+            const int obase = o0 + oy * (PAIR ? 2 : 1) * kTile;
+            if (!STAGE && obase >= top) break;       // wave-uniform
+            if constexpr (PAIR) {
+                const f32x4 a0 = tile_acc(2 * oy), a1 = tile_acc(2 * oy + 1);
+                const int o = obase + 8 * q;
+                const u32x4 wv = STAGE ? stage[n * SROW + 4 * oy + q] : yin[oy];
+                float out[8];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    out[2 * k] = bf16_lo(wv[k]) + tsc * a0[2 * k];
+                    out[2 * k + 1] = bf16_hi(wv[k]) + tsc * a0[2 * k + 1];
+                    out[4 + 2 * k] = bf16_lo(wv[2 + k]) + tsc * a1[2 * k];
+                    out[5 + 2 * k] = bf16_hi(wv[2 + k]) + tsc * a1[2 * k + 1];
+                }
+                const u32x4 pk = u32x4{bf16x2_rne(out[0], out[1]), bf16x2_rne(out[2], out[3]),
+                                       bf16x2_rne(out[4], out[5]), bf16x2_rne(out[6], out[7])};
+                if constexpr (STAGE)
+                    stage[n * SROW + 4 * oy + q] = pk;
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        pk, yr, int(o < top ? y_row + yoff + uint32_t(o) * sizeof(T) : kOOB), 0,
+                        kOut);
+            } else {
+                const f32x4 acc = tile_acc(oy);
+                const int o = obase + 4 * q;
+                float in[4], out[4];
+                Out4<T>::unpack(yin[oy], in);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) out[k] = in[k] + tsc * acc[k];
+                Out4<T>::store(yr, o < top ? y_row + yoff + uint32_t(o) * sizeof(T) : kOOB,
+                               Out4<T>::pack(out));
+            }
+        }
+        if constexpr (STAGE) {                       // y rows out of the MFMA layout
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < NY; ++j) {
+                const int o = o0 + 8 * (lane & 7);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    stage[(8 * j + (lane >> 3)) * SROW + (lane & 7)], yr,
+                    int(o < top ? y_line[j] + yoff + uint32_t(o) * sizeof(T) : kOOB), 0, kOut);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+
+    // a ring of NBUF chunks: the loads of NBUF - 1 chunks ahead are in flight
+    // while a chunk is computed (loads past the last chunk are masked)
+    u32x4 bf[NBUF][NL];
+    yraw yin[NBUF][NY];
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k) load(k, bf[k], yin[k]);
+        before();                                    // v into LDS meanwhile
+    } else {
+        before();
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k) load(k, bf[k], yin[k]);
+    }
+    for (int i = 0; i < total; i += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k) {
+            if (i + k >= total) break;               // wave-uniform
+            load(i + k + NBUF - 1, bf[(k + NBUF - 1) % NBUF], yin[(k + NBUF - 1) % NBUF]);
+            compute(i + k, bf[k], yin[k]);
+        }
+    }
+}
+
+template <typename T, int NP, int RTM, int MODE, int TPLK>
+__global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const PrefillArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int SPAN = 4 * E;
     constexpr int W = kPrefillWaves;
@@ -1285,8 +1534,15 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void k_prefill(const Pre
     constexpr bool DB = PAIRS <= 8;
     constexpr int KSM = prefill_ksm(RTM, E);
     constexpr int OTW = prefill_otw(KSM, int(sizeof(T)));
+#ifndef LORA_PREFILL_NBUF
+#define LORA_PREFILL_NBUF 2
+#endif
+    constexpr int NBUF = sizeof(T) == 2 && KSM == 1 ? LORA_PREFILL_NBUF : 2;
     __shared__ float vs[NP][kTile][VS];
     __shared__ f32x4 red[MODE == kPrefillExpand ? 1 : 2][W][kWaveSize];
+    // per wave: 16 staged token rows of 9 16-byte units (the expand step's
+    // bf16 y_in and y lines)
+    __shared__ u32x4 stage[MODE == kPrefillShrink ? 1 : W][kTile * 9];
 
     warm_args<PrefillArgs>();
     const int u = xcd_range_unit(a.units);
@@ -1304,174 +1560,172 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize) void k_prefill(const Pre
     blk.tok_off += off;
     blk.slot0 += off;
     blk.n_tok = min(kTile, blk.n_tok - off);
-    const int trow = a.block_tok[b * kMaxBlockTokens + off + n];   // -1 past n_tok
+    // the tile's 16 token rows (-1 past n_tok) by scalar loads, which go out
+    // with the descriptor's; each lane then picks its own row by selects, so
+    // no vector round trip precedes the first loads
+    struct Rows { int32_t r[kTile]; };
+    const Rows rows = load_invariant(reinterpret_cast<const Rows *>(a.block_tok) +
+                                     (b * kMaxBlockTokens + off) / kTile);
+    int trow = rows.r[0];
+#pragma unroll
+    for (int k = 1; k < kTile; ++k) trow = n == k ? rows.r[k] : trow;
 
-    if constexpr (MODE != kPrefillExpand) {
-        // ---- step 1: v = A x, K split over the waves
-        const int nkb = (a.h_in + SPAN - 1) / SPAN;
-        const int per_w = (nkb + W - 1) / W;
-        const int kb0 = min(nkb, w * per_w), kb1 = min(nkb, kb0 + per_w);
-        const int rtn = (blk.r_pad + kTile - 1) / kTile;   // rank tiles, <= RTM
-        const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
-        // an absent token's row offset is out of range already (kOOB + k
-        // bytes stays at or above 2^31)
-        const uint32_t xrow = trow >= 0 ? uint32_t(int64_t(trow) * a.ldx * sizeof(T)) : kOOB;
-        rsrc_t ar[NP];
+    // step 1 (v = A x into LDS), for the fused and shrink-only forms
+    auto step1 = [&]() {
+        if constexpr (MODE != kPrefillExpand) {
+            // ---- step 1: v = A x, K split over the waves
+            const int nkb = (a.h_in + SPAN - 1) / SPAN;
+            const int per_w = (nkb + W - 1) / W;
+            const int kb0 = min(nkb, w * per_w), kb1 = min(nkb, kb0 + per_w);
+            const int rtn = (blk.r_pad + kTile - 1) / kTile;   // rank tiles, <= RTM
+            const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+            // an absent token's row offset is out of range already (kOOB + k
+            // bytes stays at or above 2^31)
+            const uint32_t xrow = trow >= 0 ? uint32_t(int64_t(trow) * a.ldx * sizeof(T)) : kOOB;
+            rsrc_t ar[NP];
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-            ar[p] = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
-                                  uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
-                              uint32_t(blk.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
-        f32x4 acc[NP][RTM];
+            for (int p = 0; p < NP; ++p)
+                ar[p] = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
+                                      uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
+                                  uint32_t(blk.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
+            f32x4 acc[NP][RTM];
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
+            for (int p = 0; p < NP; ++p)
 #pragma unroll
-            for (int rt = 0; rt < RTM; ++rt) acc[p][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int rt = 0; rt < RTM; ++rt) acc[p][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // a batch: K-blocks kb .. kb + FB - 1 (masked past kb1, so the loads
-        // need no branch); A is K-blocked [h_in_pad / SPAN][r_pad][SPAN]
-        auto load = [&](int kb, u32x4 (&xf)[FB], u32x4 (&af)[NP][RTM][FB]) {
+            // a batch: K-blocks kb .. kb + FB - 1 (masked past kb1, so the loads
+            // need no branch); A is K-blocked [h_in_pad / SPAN][r_pad][SPAN]
+            auto load = [&](int kb, u32x4 (&xf)[FB], u32x4 (&af)[NP][RTM][FB]) {
 #pragma unroll
-            for (int f = 0; f < FB; ++f) {
-                const bool ok = kb + f < kb1;
-                const int k = (kb + f) * SPAN + q * E;
+                for (int f = 0; f < FB; ++f) {
+                    const bool ok = kb + f < kb1;
+                    const int k = (kb + f) * SPAN + q * E;
 #pragma unroll
-                for (int p = 0; p < NP; ++p)
+                    for (int p = 0; p < NP; ++p)
 #pragma unroll
-                    for (int rt = 0; rt < RTM; ++rt) {
-                        const int j = rt * kTile + n;
-                        af[p][rt][f] = bload16(
-                            ar[p], off_or_oob(ok && j < blk.r_pad,
-                                              uint32_t(((kb + f) * blk.r_pad + j) * SPAN + q * E) *
-                                                  sizeof(T)));
-                    }
-                xf[f] = bload16_nt(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
+                        for (int rt = 0; rt < RTM; ++rt) {
+                            const int j = rt * kTile + n;
+                            af[p][rt][f] = bload16(
+                                ar[p], off_or_oob(ok && j < blk.r_pad,
+                                                  uint32_t(((kb + f) * blk.r_pad + j) * SPAN + q * E) *
+                                                      sizeof(T)));
+                        }
+    #if LORA_PREFILL_X_NT
+                    xf[f] = bload16_nt(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
+    #else
+                    xf[f] = bload16(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
+    #endif
+                }
+            };
+            auto mult = [&](int kb, const u32x4 (&xf)[FB], const u32x4 (&af)[NP][RTM][FB]) {
+#pragma unroll
+                for (int f = 0; f < FB; ++f) {
+                    if (kb + f >= kb1) break;            // wave-uniform
+#pragma unroll
+                    for (int p = 0; p < NP; ++p)
+#pragma unroll
+                        for (int rt = 0; rt < RTM; ++rt)
+                            if (rt < rtn) acc[p][rt] = mma<T>(af[p][rt][f], xf[f], acc[p][rt]);
+                }
+            };
+            u32x4 xa[FB], aa[NP][RTM][FB];
+            if constexpr (DB) {
+                u32x4 xb[FB], ab[NP][RTM][FB];
+                load(kb0, xa, aa);
+                for (int kb = kb0; kb < kb1; kb += 2 * FB) {
+                    load(kb + FB, xb, ab);
+                    mult(kb, xa, aa);
+                    if (kb + FB >= kb1) break;
+                    load(kb + 2 * FB, xa, aa);
+                    mult(kb + FB, xb, ab);
+                }
+            } else {
+                for (int kb = kb0; kb < kb1; kb += FB) {
+                    load(kb, xa, aa);
+                    mult(kb, xa, aa);
+                }
             }
-        };
-        auto mult = [&](int kb, const u32x4 (&xf)[FB], const u32x4 (&af)[NP][RTM][FB]) {
-#pragma unroll
-            for (int f = 0; f < FB; ++f) {
-                if (kb + f >= kb1) break;            // wave-uniform
-#pragma unroll
-                for (int p = 0; p < NP; ++p)
-#pragma unroll
-                    for (int rt = 0; rt < RTM; ++rt)
-                        if (rt < rtn) acc[p][rt] = mma<T>(af[p][rt][f], xf[f], acc[p][rt]);
-            }
-        };
-        u32x4 xa[FB], aa[NP][RTM][FB];
-        if constexpr (DB) {
-            u32x4 xb[FB], ab[NP][RTM][FB];
-            load(kb0, xa, aa);
-            for (int kb = kb0; kb < kb1; kb += 2 * FB) {
-                load(kb + FB, xb, ab);
-                mult(kb, xa, aa);
-                if (kb + FB >= kb1) break;
-                load(kb + 2 * FB, xa, aa);
-                mult(kb + FB, xb, ab);
-            }
-        } else {
-            for (int kb = kb0; kb < kb1; kb += FB) {
-                load(kb, xa, aa);
-                mult(kb, xa, aa);
-            }
-        }
 
-        // the waves' tiles added in wave order: lane (n, q) holds ranks
-        // 4 q .. 4 q + 3 of token n; two LDS buffers in turn, one barrier a pair
-        int k = 0;
+            // the waves' tiles added in wave order: lane (n, q) holds ranks
+            // 4 q .. 4 q + 3 of token n; two LDS buffers in turn, one barrier a pair
+            int k = 0;
 #pragma unroll
-        for (int pr = 0; pr < PAIRS; ++pr) {
-            const int p = pr / RTM, rt = pr % RTM;
-            if (rt >= rtn) continue;                 // uniform over the workgroup
-            red[k & 1][w][lane] = acc[p][rt];
+            for (int pr = 0; pr < PAIRS; ++pr) {
+                const int p = pr / RTM, rt = pr % RTM;
+                if (rt >= rtn) continue;                 // uniform over the workgroup
+                red[k & 1][w][lane] = acc[p][rt];
+                __syncthreads();
+                if (threadIdx.x < kTile * kTile) {
+                    const int ln = threadIdx.x >> 2, e = threadIdx.x & 3;
+                    float s = red[k & 1][0][ln][e];
+#pragma unroll
+                    for (int ww = 1; ww < W; ++ww) s += red[k & 1][ww][ln][e];
+                    vs[p][ln & 15][rt * kTile + 4 * (ln >> 4) + e] = s;
+                }
+                ++k;
+            }
             __syncthreads();
-            if (threadIdx.x < kTile * kTile) {
-                const int ln = threadIdx.x >> 2, e = threadIdx.x & 3;
-                float s = red[k & 1][0][ln][e];
-#pragma unroll
-                for (int ww = 1; ww < W; ++ww) s += red[k & 1][ww][ln][e];
-                vs[p][ln & 15][rt * kTile + 4 * (ln >> 4) + e] = s;
-            }
-            ++k;
         }
-        __syncthreads();
-
-        if constexpr (MODE == kPrefillShrink) {
-            // v rows of the tile's tokens: r_max entries per projection,
-            // zero past the padded rank
-            const int quads = a.r_max / 4;
-            for (int i = threadIdx.x; i < blk.n_tok * NP * quads; i += NT) {
-                const int ti = i / (NP * quads), rem = i - ti * (NP * quads);
-                const int p = rem / quads, j = (rem - p * quads) * 4;
-                const f32x4 s4 = j < blk.r_pad ? *reinterpret_cast<const f32x4 *>(&vs[p][ti][j])
-                                               : f32x4{0.f, 0.f, 0.f, 0.f};
-                const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
-                                               : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
-                *reinterpret_cast<f32x4 *>(a.v + row * a.ldv + int64_t(p) * a.r_max + j) = s4;
-            }
-            return;
-        }
-    } else {
-        // v of the tile's tokens from memory
-        const int quads = blk.r_pad / 4;
+    };
+    if constexpr (MODE == kPrefillShrink) {
+        step1();
+        // v rows of the tile's tokens: r_max entries per projection,
+        // zero past the padded rank
+        const int quads = a.r_max / 4;
         for (int i = threadIdx.x; i < blk.n_tok * NP * quads; i += NT) {
             const int ti = i / (NP * quads), rem = i - ti * (NP * quads);
             const int p = rem / quads, j = (rem - p * quads) * 4;
+            const f32x4 s4 = j < blk.r_pad ? *reinterpret_cast<const f32x4 *>(&vs[p][ti][j])
+                                           : f32x4{0.f, 0.f, 0.f, 0.f};
             const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
                                            : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
-            *reinterpret_cast<f32x4 *>(&vs[p][ti][j]) = *reinterpret_cast<const f32x4 *>(
-                a.v + row * a.ldv + int64_t(p) * a.r_max + j);
+            *reinterpret_cast<f32x4 *>(a.v + row * a.ldv + int64_t(p) * a.r_max + j) = s4;
         }
-        __syncthreads();
-    }
-
-    if constexpr (MODE != kPrefillShrink) {
-        // ---- step 2: y = y_in + s B v (cores applied to v first)
-        if (a.sigma_kind) {
+    } else {
+        // v in LDS (step 1, or the tile's v rows from memory), cores applied;
+        // run by the expand step once its first loads are out
+        auto before = [&]() {
+            if constexpr (MODE == kPrefillFused) {
+                step1();
+            } else {
+                // v of the tile's tokens from memory
+                const int quads = blk.r_pad / 4;
+                for (int i = threadIdx.x; i < blk.n_tok * NP * quads; i += NT) {
+                    const int ti = i / (NP * quads), rem = i - ti * (NP * quads);
+                    const int p = rem / quads, j = (rem - p * quads) * 4;
+                    const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
+                                                   : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
+                    *reinterpret_cast<f32x4 *>(&vs[p][ti][j]) = *reinterpret_cast<const f32x4 *>(
+                        a.v + row * a.ldv + int64_t(p) * a.r_max + j);
+                }
+                __syncthreads();
+            }
+            if (a.sigma_kind) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p)
-                apply_sigma<kTile * LORA_MAX_RANK / NT, NT>(a, blk, p, vs[p]);
-        }
-        ExpandCtx c;
-        c.b = b;
-        c.w = w;
-        c.n = n;
-        c.q = q;
-        c.ntiles = 1;
-        c.ks_n = (blk.r_pad + SPAN - 1) / SPAN;      // wave-uniform, <= KSM
-        c.scale = blk.scale;
-        c.tsc[0] = a.tok_w && n < blk.n_tok ? blk.scale * a.tok_w[blk.tok_off + n] : blk.scale;
-        c.tsc[1] = c.tsc[2] = c.tsc[3] = blk.scale;
-        const int trows[1] = {trow};
-        const bool tv[1] = {trow >= 0};
-        const int g = blk.r_pad / E;                 // 16-byte vectors per B row
+                for (int p = 0; p < NP; ++p)
+                    apply_sigma<kTile * LORA_MAX_RANK / NT, NT>(a, blk, p, vs[p]);
+            }
+        };
+        const float tsc =
+            a.tok_w && n < blk.n_tok ? blk.scale * a.tok_w[blk.tok_off + n] : blk.scale;
         // each projection's rows in kPrefillWaves * osplit shares of whole
         // 32-row pairs; share part * W + w is this wave's
         const int shares = W * a.osplit, share = part * W + w;
+        // token rows of the lines layout: token 8 j + lane / 8 for j = 0, 1
+        int lrow[2];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            c.p = p;
-            c.h_out = a.h_out[p];
-            c.yoff = a.y_off[p];
-            const int rw = ((c.h_out + shares - 1) / shares + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
-            c.o_lo = min(c.h_out, share * rw);
-            c.o_hi = min(c.h_out, c.o_lo + rw);
-            if (c.o_lo >= c.o_hi) continue;          // wave-uniform
-            if constexpr (KSM == 1) {
-                if (g == 1) {
-                    expand_body<T, 1, KSM, 4, false, PrefillArgs, OTW>(a, blk, c, trows, tv,
-                                                                       vs[p]);
-                    continue;
-                }
-                if (g == 2) {
-                    expand_body<T, 1, KSM, 2, false, PrefillArgs, OTW>(a, blk, c, trows, tv,
-                                                                       vs[p]);
-                    continue;
-                }
-            }
-            expand_body<T, 1, KSM, 1, false, PrefillArgs, OTW>(a, blk, c, trows, tv, vs[p]);
+        for (int j = 0; j < 2; ++j) {
+            const int t = 8 * j + (lane >> 3);
+            lrow[j] = rows.r[0];
+#pragma unroll
+            for (int k = 1; k < kTile; ++k) lrow[j] = t == k ? rows.r[k] : lrow[j];
         }
+        // the first chunks' loads go out before step 1 where the registers
+        // allow (up to 4 accumulator tiles)
+        constexpr bool EARLY = LORA_PREFILL_EARLY && PAIRS <= 4;
+        prefill_rows<T, NP, KSM, TPLK, OTW, NBUF, EARLY>(a, blk, share, shares, n, q, trow, lrow,
+                                                         tsc, vs, stage[w], before);
     }
 }
 
@@ -1511,27 +1765,46 @@ hipError_t shrink_dispatch(int tt, bool mp, const ShrinkArgs &a, hipStream_t s) 
     return hipGetLastError();
 }
 
-template <typename T, int MODE>
-hipError_t prefill_dispatch(int np, int rtm, const PrefillArgs &a, int g, hipStream_t s) {
+// kernels built: TPL (B rows packed per load) 2 or 4 only for launches whose
+// long blocks all have one padded rank of 1 or 2 vectors (RTM 1), and only
+// for the modes with an expand step
+template <typename T, int MODE, int TPL>
+hipError_t prefill_np(int np, int rtm, const PrefillArgs &a, int g, hipStream_t s) {
     const dim3 grid(g), block(kPrefillWaves * kWaveSize);
-    switch (np * 8 + rtm) {
-#define LORA_PREFILL(NP, RTM) \
-    case NP * 8 + RTM: hipLaunchKernelGGL((k_prefill<T, NP, RTM, MODE>), grid, block, 0, s, a); break;
-    LORA_PREFILL(1, 1) LORA_PREFILL(1, 2) LORA_PREFILL(1, 4)
-    LORA_PREFILL(2, 1) LORA_PREFILL(2, 2) LORA_PREFILL(2, 4)
-    LORA_PREFILL(3, 1) LORA_PREFILL(3, 2) LORA_PREFILL(3, 4)
-#undef LORA_PREFILL
-    default: return hipErrorInvalidValue;
+#define LORA_PREFILL(NP, RTM)                                                                      \
+    case NP * 8 + RTM:                                                                            \
+        hipLaunchKernelGGL((k_prefill<T, NP, RTM, MODE, TPL>), grid, block, 0, s, a);             \
+        break;
+    if constexpr (TPL == 1) {
+        switch (np * 8 + rtm) {
+            LORA_PREFILL(1, 1) LORA_PREFILL(1, 2) LORA_PREFILL(1, 4)
+            LORA_PREFILL(2, 1) LORA_PREFILL(2, 2) LORA_PREFILL(2, 4)
+            LORA_PREFILL(3, 1) LORA_PREFILL(3, 2) LORA_PREFILL(3, 4)
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (np * 8 + rtm) {
+            LORA_PREFILL(1, 1) LORA_PREFILL(2, 1) LORA_PREFILL(3, 1)
+        default: return hipErrorInvalidValue;
+        }
     }
+#undef LORA_PREFILL
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t prefill_modes(int mode, int np, int rtm, const PrefillArgs &a, int g, hipStream_t s) {
-    switch (mode) {
-    case kPrefillFused: return prefill_dispatch<T, kPrefillFused>(np, rtm, a, g, s);
-    case kPrefillShrink: return prefill_dispatch<T, kPrefillShrink>(np, rtm, a, g, s);
-    case kPrefillExpand: return prefill_dispatch<T, kPrefillExpand>(np, rtm, a, g, s);
+hipError_t prefill_modes(int mode, int np, int rtm, int tpl, const PrefillArgs &a, int g,
+                         hipStream_t s) {
+    if (mode == kPrefillShrink) return prefill_np<T, kPrefillShrink, 1>(np, rtm, a, g, s);
+    if (mode != kPrefillFused && mode != kPrefillExpand) return hipErrorInvalidValue;
+    const bool fused = mode == kPrefillFused;
+    switch (tpl) {
+    case 1: return fused ? prefill_np<T, kPrefillFused, 1>(np, rtm, a, g, s)
+                         : prefill_np<T, kPrefillExpand, 1>(np, rtm, a, g, s);
+    case 2: return fused ? prefill_np<T, kPrefillFused, 2>(np, rtm, a, g, s)
+                         : prefill_np<T, kPrefillExpand, 2>(np, rtm, a, g, s);
+    case 4: return fused ? prefill_np<T, kPrefillFused, 4>(np, rtm, a, g, s)
+                         : prefill_np<T, kPrefillExpand, 4>(np, rtm, a, g, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1647,11 +1920,12 @@ hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid,
     return expand_merge_t<float>(nvm, g, block, a, s);
 }
 
-hipError_t launch_prefill(int dtype, int mode, int np, int rtm, const PrefillArgs &a, int grid,
-                          hipStream_t s) {
+hipError_t launch_prefill(int dtype, int mode, int np, int rtm, int tpl, const PrefillArgs &a,
+                          int grid, hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
-    return dtype == LORA_BF16 ? prefill_modes<uint16_t>(mode, np, rtm, a, grid, s)
-                              : prefill_modes<float>(mode, np, rtm, a, grid, s);
+    if (tpl != 1 && rtm != 1) return hipErrorInvalidValue;
+    return dtype == LORA_BF16 ? prefill_modes<uint16_t>(mode, np, rtm, tpl, a, grid, s)
+                              : prefill_modes<float>(mode, np, rtm, tpl, a, grid, s);
 }
 
 }  // namespace lora

@@ -262,7 +262,8 @@ struct lora_plan {
     // the short groups', each kind in group order
     std::vector<lora::TileDesc> tiles;
     int32_t rt_long = 0;
-    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0, max_rpad_long = 0;
+    int32_t nb_act = 0, n_active = 0, max_block = 0, tt = 1, max_rpad = 0;
+    int32_t max_rpad_long = 0, min_rpad_long = 0;   // padded ranks of the long groups' blocks
 
     // device image in the caller's workspace
     void *ws = nullptr;
@@ -643,7 +644,7 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     pl->mblocks.clear();
     pl->merge_k = 0;
     pl->nb_long = pl->nb_act = pl->n_active = pl->max_block = pl->max_rpad = pl->rt_long = 0;
-    pl->max_rpad_long = 0;
+    pl->max_rpad_long = pl->min_rpad_long = 0;
     pl->tt = 1;
     pl->token_group.assign(T, -1);
 
@@ -765,8 +766,11 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     pl->blocks.insert(pl->blocks.end(), short_blocks.begin(), short_blocks.end());
     for (int32_t b = 0; b < pl->nb_act; ++b)
         pl->max_rpad = std::max(pl->max_rpad, pl->blocks[b].r_pad);
-    for (int32_t b = 0; b < pl->nb_long; ++b)
+    for (int32_t b = 0; b < pl->nb_long; ++b) {
         pl->max_rpad_long = std::max(pl->max_rpad_long, pl->blocks[b].r_pad);
+        pl->min_rpad_long = b == 0 ? pl->blocks[b].r_pad
+                                   : std::min(pl->min_rpad_long, pl->blocks[b].r_pad);
+    }
     const int32_t tiles = (std::max(max_sblock, pl->max_block) + lora::kTile - 1) / lora::kTile;
     pl->tt = tiles <= 1 ? 1 : tiles == 2 ? 2 : 4;
     pl->weighted = weighted;
@@ -1501,7 +1505,14 @@ lora_status run_prefill(const lora_pool *p, const lora_plan *pl, int32_t layer, 
     a.units = int32_t(tiles * split);
     const int32_t rtiles = (pl->max_rpad_long + lora::kTile - 1) / lora::kTile;
     const int32_t rtm = rtiles <= 1 ? 1 : rtiles == 2 ? 2 : 4;
-    const hipError_t e = lora::launch_prefill(p->d.dtype, io.mode, nproj, rtm, a,
+    // B rows of one or two 16-byte vectors pack 4 or 2 row tiles into a load
+    // when every long block has that one padded rank
+    int32_t tpl = 1;
+    if (rtm == 1 && pl->min_rpad_long == pl->max_rpad_long) {
+        const int32_t g = pl->max_rpad_long * cc.es / 16;
+        tpl = g == 1 ? 4 : g == 2 ? 2 : 1;
+    }
+    const hipError_t e = lora::launch_prefill(p->d.dtype, io.mode, nproj, rtm, tpl, a,
                                               grid_for(a.units, 1), st);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return LORA_OK;

@@ -40,12 +40,18 @@ constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
 // 16-token tile of a block, kPrefillTiles tiles per block, runs the whole
 // delta of its tokens (see k_prefill).  16 waves fill a CU's 4 SIMDs with
 // one workgroup.
-constexpr int kPrefillWaves = 16;
+#ifndef LORA_PREFILL_WAVES
+#define LORA_PREFILL_WAVES 16
+#endif
+#ifndef LORA_PREFILL_TARGET
+#define LORA_PREFILL_TARGET 256
+#endif
+constexpr int kPrefillWaves = LORA_PREFILL_WAVES;
 constexpr int kPrefillTiles = kMaxBlockTokens / kTile;
 // Prefill launches aim for this many workgroups at least: a launch with
 // fewer tiles splits each tile's output rows over up to kPrefillMaxSplit
 // workgroups (each then runs the A step of its tile itself).
-constexpr int kPrefillTargetGroups = 256;
+constexpr int kPrefillTargetGroups = LORA_PREFILL_TARGET;
 constexpr int kPrefillMaxSplit = 4;
 enum { kPrefillFused = 0, kPrefillShrink = 1, kPrefillExpand = 2 };
 // Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
@@ -316,9 +322,11 @@ hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *d
                          int h_in_pad, hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 // prefill: mode kPrefillFused / kPrefillShrink / kPrefillExpand; np the
-// call's projections (1..3); rtm the launch's largest rank tiles (1, 2 or 4)
-hipError_t launch_prefill(int dtype, int mode, int np, int rtm, const PrefillArgs &a, int grid,
-                          hipStream_t s);
+// call's projections (1..3); rtm the launch's largest rank tiles (1, 2 or 4);
+// tpl the B row tiles per 16-byte load of the expand step: 4 or 2 when every
+// long block's B row is one or two 16-byte vectors (rtm 1), else 1
+hipError_t launch_prefill(int dtype, int mode, int np, int rtm, int tpl, const PrefillArgs &a,
+                          int grid, hipStream_t s);
 // decode expand (every block of the plan within kValuTokens tokens)
 // nvm: the largest decode_nvt of the launch's rank classes
 hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int grid,
