@@ -1261,11 +1261,8 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
 // K-blocks per batch of the shrink step, for `pairs` (projection, rank tile)
 // accumulators: a batch is FB x fragments and FB x pairs A fragments; two
 // batches in flight stay within about 72 VGPRs.
-#ifndef LORA_PREFILL_X_NT
-#define LORA_PREFILL_X_NT 1
-#endif
 #ifndef LORA_PREFILL_EARLY
-#define LORA_PREFILL_EARLY 1
+#define LORA_PREFILL_EARLY 0
 #endif
 constexpr int prefill_kbatch(int pairs) { return pairs <= 1 ? 4 : pairs <= 3 ? 2 : 1; }
 constexpr int prefill_ksm(int rtm, int e) {
@@ -1540,9 +1537,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
     constexpr int NBUF = sizeof(T) == 2 && KSM == 1 ? LORA_PREFILL_NBUF : 2;
     __shared__ float vs[NP][kTile][VS];
     __shared__ f32x4 red[MODE == kPrefillExpand ? 1 : 2][W][kWaveSize];
-    // per wave: 16 staged token rows of 9 16-byte units (the expand step's
-    // bf16 y_in and y lines)
-    __shared__ u32x4 stage[MODE == kPrefillShrink ? 1 : W][kTile * 9];
+    // per wave: 16 staged token rows of 9 16-byte units (bf16 x lines of the
+    // A step, y_in and y lines of the B step)
+    __shared__ u32x4 stage[W][kTile * 9];
 
     warm_args<PrefillArgs>();
     const int u = xcd_range_unit(a.units);
@@ -1569,6 +1566,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
     int trow = rows.r[0];
 #pragma unroll
     for (int k = 1; k < kTile; ++k) trow = n == k ? rows.r[k] : trow;
+    // token rows of the lines layout (staged loads and stores): token
+    // 8 j + lane / 8 of instruction j = 0, 1
+    int lrow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = 8 * j + (lane >> 3);
+        lrow[j] = rows.r[0];
+#pragma unroll
+        for (int k = 1; k < kTile; ++k) lrow[j] = t == k ? rows.r[k] : lrow[j];
+    }
 
     // step 1 (v = A x into LDS), for the fused and shrink-only forms
     auto step1 = [&]() {
@@ -1594,6 +1601,16 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
 #pragma unroll
                 for (int rt = 0; rt < RTM; ++rt) acc[p][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+            // bf16 batches of whole K-block pairs: x moves as 8 tokens' 128-byte
+            // lines per instruction (two K-blocks of a token) and passes through
+            // the wave's LDS rows into the MFMA layout, instead of 16 tokens x
+            // 64 bytes per instruction
+            constexpr bool STAGEX = sizeof(T) == 2 && FB % 2 == 0;
+            uint32_t xline[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                xline[j] = lrow[j] >= 0 ? uint32_t(int64_t(lrow[j]) * a.ldx * sizeof(T)) : kOOB;
+            u32x4 *xs = stage[w];
             // a batch: K-blocks kb .. kb + FB - 1 (masked past kb1, so the loads
             // need no branch); A is K-blocked [h_in_pad / SPAN][r_pad][SPAN]
             auto load = [&](int kb, u32x4 (&xf)[FB], u32x4 (&af)[NP][RTM][FB]) {
@@ -1611,14 +1628,38 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
                                                   uint32_t(((kb + f) * blk.r_pad + j) * SPAN + q * E) *
                                                       sizeof(T)));
                         }
-    #if LORA_PREFILL_X_NT
-                    xf[f] = bload16_nt(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
-    #else
-                    xf[f] = bload16(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T) : kOOB);
-    #endif
+                    if constexpr (STAGEX) {
+                        // instruction f: K-blocks kb + 2 (f / 2) and the next,
+                        // tokens 8 (f % 2) .. + 7, 16 bytes at 16 (lane % 8)
+                        const int b2 = kb + 2 * (f / 2);
+                        const int kk = b2 * SPAN + 8 * (lane & 7);
+                        const bool okl = b2 + ((lane & 7) >> 2) < kb1 && kk < a.h_in;
+                        xf[f] = bload16_nt(xr, okl ? xline[f % 2] + uint32_t(kk) * sizeof(T)
+                                                   : kOOB);
+                    } else {
+                        xf[f] = bload16_nt(xr, ok && k < a.h_in ? xrow + uint32_t(k) * sizeof(T)
+                                                                : kOOB);
+                    }
                 }
             };
-            auto mult = [&](int kb, const u32x4 (&xf)[FB], const u32x4 (&af)[NP][RTM][FB]) {
+            auto mult = [&](int kb, const u32x4 (&xl)[FB], const u32x4 (&af)[NP][RTM][FB]) {
+                u32x4 xf[FB];
+                if constexpr (STAGEX) {
+                    // lines into the MFMA layout: token n, K-block kb + f, the
+                    // 16 bytes of lane group q
+#pragma unroll
+                    for (int f2 = 0; f2 < FB; f2 += 2) {
+                        xs[(lane >> 3) * 9 + (lane & 7)] = xl[f2];
+                        xs[(8 + (lane >> 3)) * 9 + (lane & 7)] = xl[f2 + 1];
+                        __builtin_amdgcn_wave_barrier();
+                        xf[f2] = xs[n * 9 + q];
+                        xf[f2 + 1] = xs[n * 9 + 4 + q];
+                        __builtin_amdgcn_wave_barrier();
+                    }
+                } else {
+#pragma unroll
+                    for (int f = 0; f < FB; ++f) xf[f] = xl[f];
+                }
 #pragma unroll
                 for (int f = 0; f < FB; ++f) {
                     if (kb + f >= kb1) break;            // wave-uniform
@@ -1712,15 +1753,6 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
         // each projection's rows in kPrefillWaves * osplit shares of whole
         // 32-row pairs; share part * W + w is this wave's
         const int shares = W * a.osplit, share = part * W + w;
-        // token rows of the lines layout: token 8 j + lane / 8 for j = 0, 1
-        int lrow[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = 8 * j + (lane >> 3);
-            lrow[j] = rows.r[0];
-#pragma unroll
-            for (int k = 1; k < kTile; ++k) lrow[j] = t == k ? rows.r[k] : lrow[j];
-        }
         // the first chunks' loads go out before step 1 where the registers
         // allow (up to 4 accumulator tiles)
         constexpr bool EARLY = LORA_PREFILL_EARLY && PAIRS <= 4;
