@@ -451,21 +451,25 @@ lora_status sgmv_expand(const lora_pool *p, const lora_plan *pl, int32_t layer,
  * (base_out of the frozen layer, same column layout as y, [T][ldb]) when base
  * is non-NULL, else the current y.  Tokens without an adapter get y = base
  * (or are left untouched when base is NULL).  v is never written to memory:
- * the expand sums the shrink's partials itself. */
+ * for short groups (decode steps) the expand sums the shrink's partials
+ * itself; a long group's (a prompt's, once the batch's long groups hold 1024
+ * tokens) whole delta runs in one kernel whose workgroups keep v in LDS. */
 lora_status sgmv_fused(const lora_pool *p, const lora_plan *pl, int32_t layer,
                        int32_t nproj, const int32_t *projs, const int32_t *y_offsets,
                        const void *x, int64_t ldx, const void *base, int64_t ldb,
                        void *y, int64_t ldy, void *stream);
 
-/* sgmv_fused in two calls, each one kernel (the expand two for a batch with
- * both prompt and decode blocks): the shrink (the A step, scale
- * 1.0, "Compress then Serve" rebuttal pseudocode, step 1) leaves float32
- * partial sums of v in the plan's workspace; the expand (step 3) sums them
- * and writes y exactly as sgmv_fused does (the same bits).  The shrink needs
+/* sgmv_fused in two calls (the A step, scale 1.0, "Compress then Serve"
+ * rebuttal pseudocode, step 1; then step 3): the shrink leaves float32
+ * partial sums of v for the plan's short groups and the v rows of its long
+ * groups (prompts) in the plan's workspace; the expand reads them and
+ * writes y exactly as sgmv_fused does (the same bits).  The shrink needs
  * only x, so a caller can run it beside the frozen layer's own product and
  * the expand after it.  The workspace holds the partials of the last shrink
- * run with the plan (this one, sgmv_fused's or sgmv_shrink's); the expand
- * must name that call's layer and projections (LORA_ESTATE otherwise), and
+ * run with the plan (this one, sgmv_fused's or sgmv_shrink's; the long
+ * groups' v rows only this one's: sgmv_fused keeps them inside its kernel);
+ * the expand must name that call's layer and projections and, for a plan
+ * with long groups, follow sgmv_shrink_partials (LORA_ESTATE otherwise), and
  * runs on a stream ordered after that shrink.  Arguments and errors as
  * sgmv_fused. */
 lora_status sgmv_shrink_partials(const lora_pool *p, const lora_plan *pl, int32_t layer,
