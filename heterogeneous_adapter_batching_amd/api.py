@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import ctypes
+import functools
 from typing import Optional, Sequence
 
 import numpy as np
@@ -17,21 +18,35 @@ def _torch():
     return torch
 
 
+_TORCH_DTYPES = {}
+
+
 def _torch_dtype(dtype: str):
-    torch = _torch()
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    if dtype not in _TORCH_DTYPES:
+        torch = _torch()
+        _TORCH_DTYPES[dtype] = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return _TORCH_DTYPES[dtype]
 
 
-def _stream_handle(stream) -> ctypes.c_void_p:
-    torch = _torch()
+def _stream_handle(stream) -> int:
+    """The hipStream_t of a torch stream (the current one for None), as the
+    integer the c_void_p arguments take."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+        stream = _torch().cuda.current_stream()
+    return stream.cuda_stream
 
 
 def _i32_array(values) -> ctypes.Array:
     vals = [int(v) for v in values]
     return (ctypes.c_int32 * max(len(vals), 1))(*vals)
+
+
+@functools.lru_cache(maxsize=256)
+def _i32_const(values: tuple) -> ctypes.Array:
+    """A read-only int32 argument array, built once per distinct tuple: the
+    per-call projection and y-offset lists of the sgmv calls (the library
+    only reads them)."""
+    return _i32_array(values)
 
 
 def make_desc(num_layers: int, h_in: Sequence[int], h_out: Sequence[int], r_max: int,
@@ -427,8 +442,12 @@ class Plan:
 
 
 def _projs(projs):
-    projs = [int(p) for p in projs]
-    return len(projs), _i32_array(projs)
+    t = tuple(int(p) for p in projs)
+    return len(t), _i32_const(t)
+
+
+def _offsets(y_offsets):
+    return _i32_const(tuple(int(o) for o in y_offsets))
 
 
 def sgmv_shrink(pool: Pool, plan: Plan, layer: int, projs, x, v=None, stream=None):
@@ -440,8 +459,8 @@ def sgmv_shrink(pool: Pool, plan: Plan, layer: int, projs, x, v=None, stream=Non
         v = torch.zeros((x.shape[0], n * pool.r_max), dtype=torch.float32, device=x.device)
     _check_dev(v, "v", torch.float32)
     check(pool.lib.sgmv_shrink(pool.handle, plan.handle, layer, n, parr,
-                               ctypes.c_void_p(x.data_ptr()), x.stride(0),
-                               ctypes.c_void_p(v.data_ptr()), v.stride(0),
+                               x.data_ptr(), x.stride(0),
+                               v.data_ptr(), v.stride(0),
                                _stream_handle(stream)))
     return v
 
@@ -452,9 +471,9 @@ def sgmv_expand(pool: Pool, plan: Plan, layer: int, projs, y_offsets, v, y, stre
     _check_dev(v, "v", torch.float32)
     _check_dev(y, "y", _torch_dtype(pool.dtype))
     n, parr = _projs(projs)
-    check(pool.lib.sgmv_expand(pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
-                               ctypes.c_void_p(v.data_ptr()), v.stride(0),
-                               ctypes.c_void_p(y.data_ptr()), y.stride(0),
+    check(pool.lib.sgmv_expand(pool.handle, plan.handle, layer, n, parr, _offsets(y_offsets),
+                               v.data_ptr(), v.stride(0),
+                               y.data_ptr(), y.stride(0),
                                _stream_handle(stream)))
     return y
 
@@ -468,11 +487,11 @@ def sgmv_fused(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y, base=
     if base is not None:
         _check_dev(base, "base", dt)
     n, parr = _projs(projs)
-    check(pool.lib.sgmv_fused(pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
-                              ctypes.c_void_p(x.data_ptr()), x.stride(0),
-                              ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+    check(pool.lib.sgmv_fused(pool.handle, plan.handle, layer, n, parr, _offsets(y_offsets),
+                              x.data_ptr(), x.stride(0),
+                              (base.data_ptr() if base is not None else 0),
                               base.stride(0) if base is not None else 0,
-                              ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                              y.data_ptr(), y.stride(0),
                               _stream_handle(stream)))
     return y
 
@@ -488,11 +507,11 @@ def sgmv_fused_static(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, y
         _check_dev(base, "base", dt)
     n, parr = _projs(projs)
     check(pool.lib.sgmv_fused_static(pool.handle, plan.handle, layer, n, parr,
-                                     _i32_array(y_offsets),
-                                     ctypes.c_void_p(x.data_ptr()), x.stride(0),
-                                     ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                     _offsets(y_offsets),
+                                     x.data_ptr(), x.stride(0),
+                                     (base.data_ptr() if base is not None else 0),
                                      base.stride(0) if base is not None else 0,
-                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                     y.data_ptr(), y.stride(0),
                                      _stream_handle(stream)))
     return y
 
@@ -503,7 +522,7 @@ def sgmv_shrink_partials(pool: Pool, plan: Plan, layer: int, projs, x, stream=No
     _check_dev(x, "x", _torch_dtype(pool.dtype))
     n, parr = _projs(projs)
     check(pool.lib.sgmv_shrink_partials(pool.handle, plan.handle, layer, n, parr,
-                                        ctypes.c_void_p(x.data_ptr()), x.stride(0),
+                                        x.data_ptr(), x.stride(0),
                                         _stream_handle(stream)))
 
 
@@ -517,10 +536,10 @@ def sgmv_expand_partials(pool: Pool, plan: Plan, layer: int, projs, y_offsets, y
         _check_dev(base, "base", dt)
     n, parr = _projs(projs)
     check(pool.lib.sgmv_expand_partials(pool.handle, plan.handle, layer, n, parr,
-                                        _i32_array(y_offsets),
-                                        ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                        _offsets(y_offsets),
+                                        (base.data_ptr() if base is not None else 0),
                                         base.stride(0) if base is not None else 0,
-                                        ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                        y.data_ptr(), y.stride(0),
                                         _stream_handle(stream)))
     return y
 
@@ -535,10 +554,10 @@ def sgmv_expand_partials_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offs
     _check_cores(pool, sigma, kind)
     n, parr = _projs(projs)
     check(pool.lib.sgmv_expand_partials_sigma(
-        pool.handle, plan.handle, layer, n, parr, _i32_array(y_offsets),
-        ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), sigma.shape[0],
-        ctypes.c_void_p(base.data_ptr() if base is not None else 0),
-        base.stride(0) if base is not None else 0, ctypes.c_void_p(y.data_ptr()), y.stride(0),
+        pool.handle, plan.handle, layer, n, parr, _offsets(y_offsets),
+        sigma.data_ptr(), _sigma_kind(kind), sigma.shape[0],
+        (base.data_ptr() if base is not None else 0),
+        base.stride(0) if base is not None else 0, y.data_ptr(), y.stride(0),
         _stream_handle(stream)))
     return y
 
@@ -572,10 +591,10 @@ def sgmv_expand_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, v, s
     n_sig = _check_cores(pool, sigma, kind)
     n, parr = _projs(projs)
     check(pool.lib.sgmv_expand_sigma(pool.handle, plan.handle, layer, n, parr,
-                                     _i32_array(y_offsets),
-                                     ctypes.c_void_p(v.data_ptr()), v.stride(0),
-                                     ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), n_sig,
-                                     ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                     _offsets(y_offsets),
+                                     v.data_ptr(), v.stride(0),
+                                     sigma.data_ptr(), _sigma_kind(kind), n_sig,
+                                     y.data_ptr(), y.stride(0),
                                      _stream_handle(stream)))
     return y
 
@@ -592,11 +611,11 @@ def sgmv_fused_sigma(pool: Pool, plan: Plan, layer: int, projs, y_offsets, x, si
     n_sig = _check_cores(pool, sigma, kind)
     n, parr = _projs(projs)
     check(pool.lib.sgmv_fused_sigma(pool.handle, plan.handle, layer, n, parr,
-                                    _i32_array(y_offsets),
-                                    ctypes.c_void_p(x.data_ptr()), x.stride(0),
-                                    ctypes.c_void_p(sigma.data_ptr()), _sigma_kind(kind), n_sig,
-                                    ctypes.c_void_p(base.data_ptr() if base is not None else 0),
+                                    _offsets(y_offsets),
+                                    x.data_ptr(), x.stride(0),
+                                    sigma.data_ptr(), _sigma_kind(kind), n_sig,
+                                    (base.data_ptr() if base is not None else 0),
                                     base.stride(0) if base is not None else 0,
-                                    ctypes.c_void_p(y.data_ptr()), y.stride(0),
+                                    y.data_ptr(), y.stride(0),
                                     _stream_handle(stream)))
     return y
