@@ -236,7 +236,8 @@ def sweep(args):
     torch.cuda.set_device(0)
     w = sweep_stack(128)
     t0 = time.perf_counter()
-    dw = DeviceWorkload(w, upload=np.arange(w.pool_size), threads=default_threads())
+    dw = DeviceWorkload(w, upload=np.arange(w.pool_size), threads=default_threads(),
+                        plan_opts=plan_opts(args))
     torch.cuda.synchronize()
     log(f"[sweep] staged {w.name}: {time.perf_counter() - t0:.1f} s")
     stream = torch.cuda.Stream()
@@ -630,6 +631,14 @@ def capture(fn, stream, warmup):
     return graph
 
 
+def plan_opts(args):
+    """The plan options given on the command line (the library's defaults
+    for the others)."""
+    return {k: v for k, v in (("long_group", args.long_group), ("long_batch", args.long_batch),
+                              ("shrink_groups", args.shrink_groups),
+                              ("prefill_groups", args.prefill_groups)) if v is not None}
+
+
 def other_config(ci, args, stream, flush):
     """The step of a smaller workload (a parity configuration), timed in a
     graph, each step after a cache flush (its data would otherwise sit in
@@ -639,7 +648,7 @@ def other_config(ci, args, stream, flush):
     from synth.device import DeviceWorkload
     w = config(ci)
     t0 = time.perf_counter()
-    dw = DeviceWorkload(w, threads=default_threads())
+    dw = DeviceWorkload(w, threads=default_threads(), plan_opts=plan_opts(args))
     graph = capture(dw.run_fused, stream, args.warmup)
     ms, per_step = timed_steps(graph.replay, stream, args.steps, flush)
     out = {"workload": w.name, "description": w.description, "tokens": w.num_tokens,
@@ -740,6 +749,12 @@ def main():
                     help="size of the device-copy bandwidth reference (0: skip)")
     ap.add_argument("--configs", type=int, nargs="*", default=[1, 2, 3],
                     help="smaller workloads also timed (flushed) and reported under 'configs'")
+    for opt, what in (("long-group", "tokens that make a group long (the prompt kernel)"),
+                      ("long-batch", "long groups' tokens a batch needs to use the prompt kernel"),
+                      ("shrink-groups", "workgroups a decode shrink launch aims for"),
+                      ("prefill-groups", "workgroups a prompt launch aims for")):
+        ap.add_argument(f"--{opt}", type=int, default=None,
+                        help=f"plan option: {what} (default: the library's)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: delta time vs distinct adapters and Zipf skew")
     ap.add_argument("--sweep-out", default=None, help="text summary of the sweep")
@@ -785,7 +800,8 @@ def main():
             keep[(aid, l, p)] = (a, b)
 
     t0 = time.perf_counter()
-    dw = DeviceWorkload(w, on_block=on_block, threads=default_threads())
+    dw = DeviceWorkload(w, on_block=on_block, threads=default_threads(),
+                        plan_opts=plan_opts(args))
     torch.cuda.synchronize()
     log(f"[bench] staged {w.name}: {time.perf_counter() - t0:.1f} s, "
         f"plan {dw.plan.stats()}")
@@ -1015,7 +1031,8 @@ def main():
                    "projections": [p.name for p in w.projs],
                    "calls_per_layer": len(w.calls), "kernel_launches_per_step": launches,
                    "distinct_adapters": int(len(w.touched())), "mode": args.mode,
-                   "flush_mib_between_steps": flush_mib, "flush": "read"},
+                   "flush_mib_between_steps": flush_mib, "flush": "read",
+                   "plan_opts": dw.plan.opts()},
         **{k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")},
         "step_ms_quantiles": quant,
         "eager_ms_per_step": round(eager_ms, 5),

@@ -10,16 +10,17 @@ missing or fails to load, importing the binding's entry points raises.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    LIB_PATH, LoraError, PoolDesc, load, status_name, LORA_F32, LORA_BF16,
+    LIB_PATH, LoraError, PlanOpts, PoolDesc, load, status_name, LORA_F32, LORA_BF16,
     LORA_MAX_PROJ, LORA_MAX_RANK, LORA_SIGMA_DIAG, LORA_SIGMA_FULL,
 )
 from .api import (  # noqa: F401
     Pool, Plan, sgmv_shrink, sgmv_expand, sgmv_fused, sgmv_expand_sigma, sgmv_fused_sigma,
     pool_bytes_for, extent_bytes, pack_adapter, Cache, sgmv_shrink_partials,
-    sgmv_expand_partials, sgmv_expand_partials_sigma, sgmv_fused_static,
+    sgmv_expand_partials, sgmv_expand_partials_sigma, sgmv_fused_static, plan_opts_default,
 )
 
 __all__ = ["Pool", "Plan", "sgmv_shrink", "sgmv_expand", "sgmv_fused", "sgmv_expand_sigma",
            "sgmv_fused_sigma", "sgmv_shrink_partials", "sgmv_expand_partials",
            "sgmv_expand_partials_sigma", "sgmv_fused_static",
-           "pool_bytes_for", "extent_bytes", "pack_adapter", "Cache", "LoraError", "load"]
+           "pool_bytes_for", "extent_bytes", "pack_adapter", "Cache", "LoraError", "load",
+           "plan_opts_default"]

@@ -38,6 +38,11 @@ class PoolDesc(ctypes.Structure):
                 ("max_slots", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("long_group", ctypes.c_int32), ("long_batch", ctypes.c_int32),
+                ("shrink_groups", ctypes.c_int32), ("prefill_groups", ctypes.c_int32)]
+
+
 _i32, _i64, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 _vp, _i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
 _pp = ctypes.POINTER(ctypes.c_void_p)
@@ -58,6 +63,10 @@ SIGNATURES = {
     "lora_pool_stats": (_i32, [_vp, _i32p, ctypes.POINTER(_u64)]),
     "lora_plan_create": (_i32, [ctypes.POINTER(_vp), _vp, _i32, _i32p, _i32p, _i32]),
     "lora_plan_destroy": (_i32, [_vp]),
+    "lora_plan_opts_default": (None, [ctypes.POINTER(PlanOpts)]),
+    "lora_pool_set_plan_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
+    "lora_pool_get_plan_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
+    "lora_plan_get_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
     "lora_plan_workspace_bytes": (_u64, [_vp, _i32]),
     "lora_workspace_bytes": (_u64, [_vp, _i32, _i32, _i32]),
     "lora_plan_rebuild": (_i32, [_vp, _i32, _i32p, _i32p, _i32p, ctypes.POINTER(_f32), _i32]),

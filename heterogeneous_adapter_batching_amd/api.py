@@ -7,8 +7,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from ._lib import (LORA_BF16, LORA_F32, LORA_MAX_PROJ, LORA_SIGMA_DIAG, LORA_SIGMA_FULL, PoolDesc,
-                   check, load)
+from ._lib import (LORA_BF16, LORA_F32, LORA_MAX_PROJ, LORA_SIGMA_DIAG, LORA_SIGMA_FULL, PlanOpts,
+                   PoolDesc, check, load)
 
 _DTYPES = {"bf16": LORA_BF16, "f32": LORA_F32}
 
@@ -162,6 +162,23 @@ class Pool:
 
     def pool_bytes_for(self, rank: int) -> int:
         return pool_bytes_for(self.desc, rank)
+
+    def plan_opts(self) -> dict:
+        """The plan options plans built from this pool take (lora_plan_opts)."""
+        o = PlanOpts()
+        check(self.lib.lora_pool_get_plan_opts(self._h, ctypes.byref(o)))
+        return _opts_dict(o)
+
+    def set_plan_opts(self, **opts):
+        """Set some of long_group, long_batch, shrink_groups, prefill_groups
+        for plans built afterwards; the others keep their current values."""
+        o = PlanOpts()
+        check(self.lib.lora_pool_get_plan_opts(self._h, ctypes.byref(o)))
+        for k, v in opts.items():
+            if k not in _OPT_FIELDS:
+                raise ValueError(f"unknown plan option {k!r}")
+            setattr(o, k, int(v))
+        check(self.lib.lora_pool_set_plan_opts(self._h, ctypes.byref(o)))
 
     def workspace_bytes(self, num_tokens: int, num_segs: int, max_proj: int = 3) -> int:
         """A workspace size that serves every plan of up to num_tokens tokens
@@ -426,6 +443,12 @@ class Plan:
         return dict(zip(("groups", "blocks", "active_tokens", "max_block_tokens"),
                         [v.value for v in vals]))
 
+    def opts(self) -> dict:
+        """The plan options this plan was built with (its pool's at the time)."""
+        o = PlanOpts()
+        check(self.lib.lora_plan_get_opts(self._h, ctypes.byref(o)))
+        return _opts_dict(o)
+
     def export(self):
         st = self.stats()
         T, G = self.num_tokens, st["groups"]
@@ -439,6 +462,20 @@ class Plan:
                                         grank.ctypes.data_as(i32p)))
         return {"token_order": order[:T], "token_group": tgroup[:T],
                 "group_adapter": gad[:G], "group_rank": grank[:G]}
+
+
+_OPT_FIELDS = tuple(f[0] for f in PlanOpts._fields_)
+
+
+def _opts_dict(o) -> dict:
+    return {k: int(getattr(o, k)) for k in _OPT_FIELDS}
+
+
+def plan_opts_default() -> dict:
+    """The library's default plan options."""
+    o = PlanOpts()
+    load().lora_plan_opts_default(ctypes.byref(o))
+    return _opts_dict(o)
 
 
 def _projs(projs):

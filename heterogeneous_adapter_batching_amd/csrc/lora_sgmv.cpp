@@ -118,6 +118,7 @@ struct lora_pool {
     std::unordered_map<int32_t, Slot> slots;
     std::map<uint64_t, uint64_t> free_list;  // offset -> bytes, coalesced
     uint64_t generation = 0;                  // bumped by unregister
+    lora_plan_opts opts{};                    // taken by plans built afterwards
     int64_t W = 0;                            // stored_row_elems(d)
     int64_t pre[LORA_MAX_PROJ + 1] = {};      // prefix of (h_in_pad + h_out) over projections
 
@@ -178,12 +179,13 @@ struct PlanLayout {
 namespace {
 
 // Most partial tiles of a shrink of up to mp projections under
-// shrink_geometry: nproj * rt * c0, with c0 at most max(ceil(target /
-// per_chunk), ceil(steps / frags)), where steps = fragments of 4 waves over
-// h_in.  With `bound`, an upper bound over every rt' <= rt instead (rt' *
-// ceil(target / (c rt')) <= target + rt' for any c >= 1).
+// shrink_geometry with launch target `target`: nproj * rt * c0, with c0 at
+// most max(ceil(target / per_chunk), ceil(steps / frags)) and at most steps,
+// where steps = fragments of 4 waves over h_in.  With `bound`, an upper bound
+// over every rt' <= rt instead (rt' * ceil(target / (c rt')) <= target + rt'
+// for any c >= 1).
 uint64_t max_shrink_units(const lora_pool_desc &d, int64_t rt_in, int32_t tt, int32_t mp,
-                          bool bound) {
+                          bool bound, int32_t target) {
     const uint64_t span = 4ull * (16 / esize(d.dtype));
     int32_t h_in_max = 0;
     for (int i = 0; i < d.num_proj; ++i) h_in_max = std::max(h_in_max, d.h_in[i]);
@@ -196,16 +198,16 @@ uint64_t max_shrink_units(const lora_pool_desc &d, int64_t rt_in, int32_t tt, in
         // partial tiles = np * rt * c0, c0 from the workgroups per chunk:
         // np * rt, or rt for units over every projection (tt >= 2)
         const uint64_t per_chunk = (tt >= 2 && np > 1 && np <= 3 ? 1 : uint64_t(np)) * rt;
-        const uint64_t by_target = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
-        const uint64_t units = bound ? std::max<uint64_t>(rt * by_frags,
-                                                          lora::kShrinkTargetGroups + rt)
+        const uint64_t by_target = (uint64_t(target) + per_chunk - 1) / per_chunk;
+        const uint64_t units = bound ? std::max<uint64_t>(rt * by_frags, uint64_t(target) + rt)
                                      : rt * std::max(by_target, by_frags);
-        most = std::max(most, uint64_t(np) * units);
+        most = std::max(most, uint64_t(np) * std::min(units, rt * steps));
     }
     return most;
 }
 
-PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp, bool bound) {
+PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp, bool bound,
+                       int32_t target) {
     PlanLayout L;
     const uint64_t T = uint64_t(std::max<int64_t>(c.T, 1));
     const uint64_t nb = uint64_t(std::max<int64_t>(c.nb, 1));
@@ -226,9 +228,10 @@ PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp,
     // float32, written by sgmv_shrink_partials for sgmv_expand_partials);
     // a bound covers both kinds
     const uint64_t tile_bytes = 4ull * lora::kTile * lora::kTile;
-    const uint64_t merge_part = max_shrink_units(d, c.rt, c.tt, mp, bound) * c.tt * tile_bytes;
-    const uint64_t short_part = round_up(max_shrink_units(d, c.rt - c.rt_long, 1, mp, bound) *
-                                         tile_bytes, 256);
+    const uint64_t merge_part = max_shrink_units(d, c.rt, c.tt, mp, bound, target) * c.tt *
+                                tile_bytes;
+    const uint64_t short_part = round_up(max_shrink_units(d, c.rt - c.rt_long, 1, mp, bound,
+                                                          target) * tile_bytes, 256);
     const uint64_t long_part = 4ull * uint64_t(c.long_rows) * uint64_t(mp) * uint64_t(d.r_max);
     L.off_lv = short_part;
     L.part_bytes = bound ? std::max(merge_part, short_part + long_part)
@@ -243,6 +246,7 @@ PlanLayout plan_layout(const lora_pool_desc &d, const PlanCounts &c, int32_t mp,
 struct lora_plan {
     const lora_pool *pool = nullptr;
     uint64_t pool_generation = 0;
+    lora_plan_opts opts{};               // the pool's plan options when it was built
     int32_t T = 0;
     std::vector<int32_t> token_order;    // plan order: grouped adapter tokens, then the rest
     std::vector<int32_t> token_sigma;    // core index per plan-order row (-1: none)
@@ -362,7 +366,35 @@ lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d, void *sla
     if (p->slab_bytes) p->free_list.emplace(0, p->slab_bytes);
     p->W = stored_row_elems(d);
     for (int i = 0; i < d->num_proj; ++i) p->pre[i + 1] = p->pre[i] + h_in_pad(d, i) + d->h_out[i];
+    lora_plan_opts_default(&p->opts);
     *out = p;
+    return LORA_OK;
+}
+
+void lora_plan_opts_default(lora_plan_opts *o) {
+    if (!o) return;
+    o->long_group = lora::kDefaultLongGroup;
+    o->long_batch = lora::kDefaultLongBatch;
+    o->shrink_groups = lora::kDefaultShrinkGroups;
+    o->prefill_groups = lora::kDefaultPrefillGroups;
+}
+
+lora_status lora_pool_set_plan_opts(lora_pool *p, const lora_plan_opts *o) {
+    if (!p || !o) return fail(LORA_EINVAL, "null pointer");
+    if (o->long_group < 1 || o->long_batch < 1)
+        return fail(LORA_EINVAL, "long_group %d and long_batch %d must be at least 1",
+                    o->long_group, o->long_batch);
+    if (o->shrink_groups < 1 || o->shrink_groups > lora::kMaxLaunchTarget ||
+        o->prefill_groups < 1 || o->prefill_groups > lora::kMaxLaunchTarget)
+        return fail(LORA_EINVAL, "shrink_groups %d and prefill_groups %d must be in 1..%d",
+                    o->shrink_groups, o->prefill_groups, lora::kMaxLaunchTarget);
+    p->opts = *o;
+    return LORA_OK;
+}
+
+lora_status lora_pool_get_plan_opts(const lora_pool *p, lora_plan_opts *o) {
+    if (!p || !o) return fail(LORA_EINVAL, "null pointer");
+    *o = p->opts;
     return LORA_OK;
 }
 
@@ -630,6 +662,7 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
                 bool weighted) {
     pl->pool = p;
     pl->pool_generation = p->generation;
+    pl->opts = p->opts;
     pl->T = T;
     pl->token_order.clear();
     pl->token_sigma.clear();
@@ -684,10 +717,11 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
     // about the same bytes whatever a group's size; a long group's are its
     // shrink blocks, for the MFMA expand.  An expand block names its shrink
     // block's first rank tile and its first token slot in it.
+    const size_t long_group = size_t(pl->opts.long_group);
     size_t long_tokens = 0;
     for (auto &m : members)
-        if (m.size() >= size_t(lora::kLongGroup)) long_tokens += m.size();
-    const bool use_long = long_tokens >= size_t(lora::kMinLongTokens);
+        if (m.size() >= long_group) long_tokens += m.size();
+    const bool use_long = long_tokens >= size_t(pl->opts.long_batch);
     std::vector<BlockDesc> long_blocks, short_blocks;
     // rank tiles: the long groups' first (the prefill kernel runs their
     // whole delta; a plain plan's shrink covers the short tiles alone), a
@@ -699,7 +733,7 @@ void plan_build(lora_plan *pl, const lora_pool *p, int32_t T, const std::vector<
                          const Slot *sl) {
         const int32_t base = int32_t(pl->token_order.size());
         const int32_t rt = sl ? (sl->r_pad + lora::kTile - 1) / lora::kTile : 0;
-        const bool lg = sl && use_long && rows.size() >= size_t(lora::kLongGroup);
+        const bool lg = sl && use_long && rows.size() >= long_group;
         const int32_t smax = lg ? lora::kMaxBlockTokens : lora::kTile;
         const int32_t emax = lg ? lora::kMaxBlockTokens : lora::kDecodeBlockTokens;
         cut_sizes(int32_t(rows.size()), smax, &ssz);
@@ -953,9 +987,16 @@ lora_status lora_plan_destroy(lora_plan *pl) {
     return LORA_OK;
 }
 
+lora_status lora_plan_get_opts(const lora_plan *pl, lora_plan_opts *o) {
+    if (!pl || !o) return fail(LORA_EINVAL, "null pointer");
+    *o = pl->opts;
+    return LORA_OK;
+}
+
 uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj) {
     if (!pl || max_proj < 1 || max_proj > LORA_MAX_PROJ) return 0;
-    return plan_layout(pl->pool->d, pl->counts(), max_proj, false).ws_bytes;
+    return plan_layout(pl->pool->d, pl->counts(), max_proj, false, pl->opts.shrink_groups)
+        .ws_bytes;
 }
 
 uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t num_segs,
@@ -966,16 +1007,18 @@ uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t nu
     // has at most n / 16 + 1 shrink blocks, and groups <= min(S, T), so
     // shrink blocks <= T / 16 + min(S, T) (and <= T); each has at most
     // r_max / 16 rank tiles.  Blocks beyond 16 tokens exist only when long
-    // groups hold kMinLongTokens tokens between them.
+    // groups (of long_group tokens or more) hold long_batch tokens between
+    // them.
     const int64_t T = num_tokens;
+    const bool long_ok = T >= std::max(p->opts.long_group, p->opts.long_batch);
     PlanCounts c;
     c.T = T;
     c.nb = T;
     const int64_t sblocks = std::min<int64_t>(T, T / lora::kTile + 1 + std::min<int64_t>(num_segs, T));
     c.rt = sblocks * ((p->d.r_max + lora::kTile - 1) / lora::kTile);
-    c.tt = T >= lora::kMinLongTokens ? lora::kMaxBlockTokens / lora::kTile : 1;
-    c.long_rows = T >= lora::kMinLongTokens ? T : 0;
-    return plan_layout(p->d, c, max_proj, true).ws_bytes;
+    c.tt = long_ok ? lora::kMaxBlockTokens / lora::kTile : 1;
+    c.long_rows = long_ok ? T : 0;
+    return plan_layout(p->d, c, max_proj, true, p->opts.shrink_groups).ws_bytes;
 }
 
 lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
@@ -985,7 +1028,8 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
         return fail(LORA_EINVAL, "max_proj %d not in 1..%d", max_proj, LORA_MAX_PROJ);
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255))
         return fail(LORA_EINVAL, "workspace must be a non-null, 256-byte aligned device pointer");
-    const PlanLayout lay = plan_layout(pl->pool->d, pl->counts(), max_proj, false);
+    const PlanLayout lay = plan_layout(pl->pool->d, pl->counts(), max_proj, false,
+                                       pl->opts.shrink_groups);
     if (ws_bytes < lay.ws_bytes)
         return fail(LORA_ESTATE, "workspace of %llu bytes < %llu needed",
                     (unsigned long long)ws_bytes, (unsigned long long)lay.ws_bytes);
@@ -1169,18 +1213,18 @@ ShrinkShare shrink_share(const lora_plan *pl) {
     return ShrinkShare{pl->rt_long, pl->rt_short(), 1};
 }
 
-// k-chunking of the shrink: about kShrinkTargetGroups workgroups per launch, each
+// k-chunking of the shrink: about `target` workgroups per launch, each
 // wave loading at most `frags` fragments (all issued up front); chunks are a
 // multiple of 4 fragment spans so the 4 waves split them evenly.
 void shrink_geometry(const ShrinkShare &sh, int32_t nproj, int32_t h_in, int32_t span,
-                     int32_t *kc, int32_t *c0) {
+                     int32_t target, int32_t *kc, int32_t *c0) {
     // workgroups per k-chunk: one per rank tile and projection, or one per
     // rank tile for units over every projection
     const int64_t per_chunk = int64_t(shrink_mp(sh.tt, nproj) ? 1 : nproj) *
                               std::max(sh.count, 1);
     const int32_t frags = sh.tt <= 2 ? lora::shrink_frags<1>() : lora::shrink_frags<4>();
     const int32_t steps = (h_in + lora::kWaves * span - 1) / (lora::kWaves * span);
-    int64_t want = (lora::kShrinkTargetGroups + per_chunk - 1) / per_chunk;
+    int64_t want = (target + per_chunk - 1) / per_chunk;
     want = std::max<int64_t>(1, std::min<int64_t>(want, steps));
     const int32_t sper = std::min<int32_t>(frags, int32_t((steps + want - 1) / want));
     *kc = sper * lora::kWaves * span;
@@ -1240,7 +1284,7 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     a.nproj = nproj;
     a.h_in = cc.h_in;
     a.h_in_pad = int32_t(h_in_pad(&p->d, projs[0]));
-    shrink_geometry(sh, nproj, cc.h_in, 4 * cc.vec, &a.kc, &a.c0);
+    shrink_geometry(sh, nproj, cc.h_in, 4 * cc.vec, pl->opts.shrink_groups, &a.kc, &a.c0);
     const bool mp = shrink_mp(sh.tt, nproj);
     a.units = (mp ? 1 : nproj) * sh.count * a.c0;
     a.grid = grid_for(a.units, mp ? 1 : nproj);
@@ -1493,12 +1537,12 @@ lora_status run_prefill(const lora_pool *p, const lora_plan *pl, int32_t layer, 
             a.sig_off[i] = (int64_t(layer) * p->d.num_proj + projs[i]) * per;
     }
     // units: (block, token tile, row part); a launch of few tiles splits the
-    // tiles' output rows so that it still has about kPrefillTargetGroups
+    // tiles' output rows so that it still has about the plan's prefill_groups
     // workgroups (the shrink step alone has no rows to split)
     const int64_t tiles = int64_t(pl->nb_long) * lora::kPrefillTiles;
     int32_t split = 1;
     if (io.mode != lora::kPrefillShrink)
-        while (split < lora::kPrefillMaxSplit && tiles * split < lora::kPrefillTargetGroups)
+        while (split < lora::kPrefillMaxSplit && tiles * split < pl->opts.prefill_groups)
             split *= 2;
     if (tiles * split >= (int64_t(1) << 30)) return fail(LORA_ESTATE, "too many prefill tiles");
     a.osplit = split;

@@ -18,16 +18,14 @@ constexpr int kMaxBlockTokens = 64;          // tokens per block: at most 4 toke
 // decode expand: every workgroup of its launch then moves about the same
 // bytes (a popular adapter's group becomes several blocks instead of one
 // heavy one), and it takes a whole block in one pass.  A group of at least
-// kLongGroup tokens is long, and takes kMaxBlockTokens-token blocks and the
-// MFMA expand, but only when the batch's long groups hold kMinLongTokens
-// tokens between them: fewer 64-token blocks leave most of the chip idle in
-// the MFMA expand's launch, and the decode cut does better.
+// kDefaultLongGroup tokens is long, and takes kMaxBlockTokens-token blocks
+// and the prefill kernel, but only when the batch's long groups hold
+// kDefaultLongBatch tokens between them: fewer 64-token blocks leave most
+// of the chip idle in the prefill kernel's launch, and the decode cut does
+// better.  Both are defaults of a pool's plan options (lora_plan_opts).
 constexpr int kDecodeBlockTokens = 4;
-constexpr int kLongGroup = 48;
-#ifndef LORA_MIN_LONG_TOKENS
-#define LORA_MIN_LONG_TOKENS 1024
-#endif
-constexpr int kMinLongTokens = LORA_MIN_LONG_TOKENS;
+constexpr int kDefaultLongGroup = 48;
+constexpr int kDefaultLongBatch = 1024;
 constexpr int kValuTokens = kDecodeBlockTokens;  // token slots of the decode expand
 // The shrink's chunk partials of one v entry are summed as kSumWays
 // interleaved running sums (chunk c into sum c % kSumWays, in increasing c),
@@ -43,22 +41,22 @@ constexpr int kMaxClasses = LORA_MAX_RANK / 8 + 1;
 #ifndef LORA_PREFILL_WAVES
 #define LORA_PREFILL_WAVES 16
 #endif
-#ifndef LORA_PREFILL_TARGET
-#define LORA_PREFILL_TARGET 256
-#endif
 constexpr int kPrefillWaves = LORA_PREFILL_WAVES;
 constexpr int kPrefillTiles = kMaxBlockTokens / kTile;
-// Prefill launches aim for this many workgroups at least: a launch with
-// fewer tiles splits each tile's output rows over up to kPrefillMaxSplit
-// workgroups (each then runs the A step of its tile itself).
-constexpr int kPrefillTargetGroups = LORA_PREFILL_TARGET;
+// Prefill launches aim for this many workgroups at least (by default): a
+// launch with fewer tiles splits each tile's output rows over up to
+// kPrefillMaxSplit workgroups (each then runs the A step of its tile itself).
+constexpr int kDefaultPrefillGroups = 256;
 constexpr int kPrefillMaxSplit = 4;
 enum { kPrefillFused = 0, kPrefillShrink = 1, kPrefillExpand = 2 };
-// Shrink: workgroups aimed for per launch.  Fewer, longer k-chunks win over
-// more, shorter ones here (the expand then also sums fewer partials):
-// measured on the full stack, 384 beat 1024 by 3.5% per step, and 256 beat
-// 384 by 0.5% (the o call's 6 k-chunks become 4; 128 measured the same).
-constexpr int kShrinkTargetGroups = 256;
+// Shrink: workgroups aimed for per launch (by default).  Fewer, longer
+// k-chunks win over more, shorter ones here (the expand then also sums fewer
+// partials): measured on the full stack, 384 beat 1024 by 3.5% per step, and
+// 256 beat 384 by 0.5% (the o call's 6 k-chunks become 4; 128 measured the
+// same).
+constexpr int kDefaultShrinkGroups = 256;
+// upper limits of the launch targets a pool's plan options may set
+constexpr int kMaxLaunchTarget = 1 << 16;
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8
 // Activations and outputs are addressed through buffer resources whose
 // out-of-range offset is 2^31: each such tensor spans at most 2 GiB.

@@ -295,10 +295,11 @@ lora_status lora_cache_stats(const lora_cache *c, int32_t *resident, uint64_t *h
  *   seg_starts[S] = T; seg_adapter[S] holds adapter ids, -1 = no adapter.
  *   Empty segments are allowed and ids may repeat.
  * Segments are grouped by adapter in first-appearance order (the segmented
- * gather), each group is cut into blocks (at most 16 tokens, or 64 once a
- * group reaches 48 tokens; a decode batch's blocks are cut again into
+ * gather), each group is cut into blocks (at most 16 tokens, or 64 for a
+ * long group: see lora_plan_opts; a decode batch's blocks are cut again into
  * blocks of at most 4 tokens for the expand), and every id is resolved to
- * its slot, rank and scale.  Errors: LORA_ESEG, LORA_ENOENT.
+ * its slot, rank and scale.  The plan takes the pool's plan options.
+ * Errors: LORA_ESEG, LORA_ENOENT.
  * The plan stays valid while its adapters stay registered. */
 lora_status lora_plan_create(lora_plan **out, const lora_pool *p, int32_t num_tokens,
                              const int32_t *seg_starts, const int32_t *seg_adapter,
@@ -369,9 +370,10 @@ lora_status lora_plan_destroy(lora_plan *pl);
 uint64_t lora_plan_workspace_bytes(const lora_plan *pl, int32_t max_proj);
 
 /* An upper bound of lora_plan_workspace_bytes for every plan over pool `p`
- * of at most num_tokens tokens and num_segs segments, for calls of up to
- * `max_proj` projections: one workspace of this size serves every batch of a
- * serving loop, allocated once.  (For a merge plan count a token per
+ * of at most num_tokens tokens and num_segs segments, built with the pool's
+ * current plan options, for calls of up to `max_proj` projections: one
+ * workspace of this size serves every batch of a serving loop, allocated
+ * once.  (For a merge plan count a token per
  * (token, non-empty slot) and a segment per (segment, slot).)  0 on a bad
  * argument. */
 uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t num_segs,
@@ -390,6 +392,47 @@ uint64_t lora_workspace_bytes(const lora_pool *p, int32_t num_tokens, int32_t nu
  * ws), LORA_ESTATE (ws_bytes too small), LORA_EHIP. */
 lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t max_proj,
                              void *stream);
+
+/* Tunables of the grouping and of the launch geometry, held by a pool.
+ * SGMV groups a batch's requests by adapter ("Compress then Serve",
+ * rebuttal paragraph on Punica); how a group is then cut and launched is a
+ * GPU choice that these set.  A plan copies its pool's options when it is
+ * built (created or rebuilt), so its tables, workspace size and launches
+ * follow the options it was built with, whatever the pool holds later.
+ *   long_group      a group of at least this many tokens is long: 64-token
+ *                   blocks run by the one-launch prompt kernel ...
+ *   long_batch      ... once the batch's long groups hold at least this many
+ *                   tokens between them (otherwise every group takes the
+ *                   decode cut: shrink blocks of 16 tokens, expand blocks of 4)
+ *   shrink_groups   workgroups a decode shrink launch aims for: it sets the
+ *                   launch's k-chunks (more chunks: more workgroups, more
+ *                   partial sums for the expand to add)
+ *   prefill_groups  workgroups a prompt launch aims for: a launch of fewer
+ *                   16-token tiles splits each tile's output rows over up to
+ *                   4 workgroups
+ * Defaults (lora_plan_opts_default): 48, 1024, 256, 256, the values measured
+ * best on MI355X for decode batches of 64-256 tokens and a 4096-token prompt
+ * batch of Mistral-7B shapes. */
+typedef struct lora_plan_opts {
+    int32_t long_group;
+    int32_t long_batch;
+    int32_t shrink_groups;
+    int32_t prefill_groups;
+} lora_plan_opts;
+
+/* Fills `o` with the defaults. */
+void lora_plan_opts_default(lora_plan_opts *o);
+
+/* Sets the options plans built from `p` afterwards take; lora_workspace_bytes
+ * bounds workspaces for them.  Errors: LORA_EINVAL (null pointer, long_group
+ * or long_batch < 1, shrink_groups or prefill_groups not in 1..65536); the
+ * pool's options are then unchanged. */
+lora_status lora_pool_set_plan_opts(lora_pool *p, const lora_plan_opts *o);
+
+/* The pool's current options, and the options a plan was built with.
+ * Errors: LORA_EINVAL (null pointer). */
+lora_status lora_pool_get_plan_opts(const lora_pool *p, lora_plan_opts *o);
+lora_status lora_plan_get_opts(const lora_plan *pl, lora_plan_opts *o);
 
 /* Plan summary: groups, blocks, tokens with an adapter, largest block. */
 lora_status lora_plan_stats(const lora_plan *pl, int32_t *num_groups, int32_t *num_blocks,

@@ -41,10 +41,12 @@ class DeviceWorkload:
     slab_fill: byte value written over the whole slab before uploading (e.g.
                0xFF = bf16/f32 NaN, to prove untouched extents are never read)
     on_block:  callback(aid, layer, proj, A, B) with each uploaded float32 block
+    plan_opts: plan options set on the pool before the plan is built
     """
 
     def __init__(self, w: Workload, *, hab=None, pool_ids=None, upload=None, slab_fill=None,
-                 on_block=None, threads: int = 0, max_proj: int = None, layers=None):
+                 on_block=None, threads: int = 0, max_proj: int = None, layers=None,
+                 plan_opts=None):
         import torch
         if hab is None:
             import heterogeneous_adapter_batching_amd as hab
@@ -84,6 +86,8 @@ class DeviceWorkload:
 
         self.calls = [tuple(c) for c in w.calls]
         self.max_proj = max_proj or max(len(c) for c in self.calls)
+        if plan_opts:
+            self.pool.set_plan_opts(**plan_opts)
         self.plan = hab.Plan(self.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
                              seg_sigma=w.seg_sigma if w.sigma_kind else None)
         self.plan.upload(self.max_proj)

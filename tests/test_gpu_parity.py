@@ -245,6 +245,32 @@ def test_mixed_blocks(dtype, has_base):
     check_workload(dw, tight=True, threads=4)
 
 
+@pytest.mark.parametrize("case,opts", [
+    ("decode", dict(long_group=1, long_batch=1)),
+    ("decode", dict(shrink_groups=16)),
+    ("decode", dict(shrink_groups=4096)),
+    ("mixed", dict(long_group=200, long_batch=1)),
+    ("mixed", dict(long_group=1, long_batch=1, prefill_groups=1)),
+    ("mixed", dict(prefill_groups=65536, shrink_groups=384)),
+])
+def test_plan_opts_parity(case, opts):
+    """Plans built under other plan options (groups moved between the decode
+    cut and the prompt kernel, other k-chunkings and row splits) give the
+    delta within the float32 bound of the oracle."""
+    if case == "decode":
+        w = random_case(95, T=200, h_in=1024, h_out=520, n_adapters=40, max_seg=6,
+                        r_choices=[8, 16, 32, 64], has_base=True)
+    else:
+        w = mixed_case(96, h_in=384, h_out=264, r_choices=[8, 16, 24, 64])
+    log(f"[parity] plan options {case} {opts} T={w.num_tokens} S={w.num_segs}")
+    dw = DeviceWorkload(w, threads=4, plan_opts=opts)
+    assert {k: dw.plan.opts()[k] for k in opts} == opts
+    dw.zero_outputs()
+    dw.run_fused()
+    torch.cuda.synchronize()
+    check_workload(dw, tight=True, threads=4)
+
+
 def test_two_step_path():
     """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
     float32 bound of the oracle, deterministic, and bit-identical to

@@ -195,26 +195,93 @@ def test_plan_matches_reference(seed):
         assert np.array_equal(got[k], r), k
     st = plan.stats()
     assert st["active_tokens"] == int((ref[1] >= 0).sum())
-    sizes = np.bincount(ref[1][ref[1] >= 0], minlength=len(ref[2]))
-    # shrink blocks: near-equal cuts of each group into at most 16 tokens,
-    # each cut again into near-equal expand blocks of at most 4 tokens; both
-    # levels 64 tokens for a group of >= 48 tokens, once such groups hold
-    # >= 1024 tokens between them
-    use_long = sizes[sizes >= 48].sum() >= 1024
+    check_blocks(st, ref)
 
-    def cut(n, m):
-        k = -(-n // m)
-        return [n // k + (i < n % k) for i in range(k)]
+
+def _cut(n, m):
+    k = -(-n // m)
+    return [n // k + (i < n % k) for i in range(k)]
+
+
+def check_blocks(st, ref, long_group=48, long_batch=1024):
+    """The plan's block counts from the reference grouping: shrink blocks are
+    near-equal cuts of each group into at most 16 tokens, each cut again into
+    near-equal expand blocks of at most 4 tokens; both levels 64 tokens for a
+    group of >= long_group tokens, once such groups hold >= long_batch tokens
+    between them."""
+    sizes = np.bincount(ref[1][ref[1] >= 0], minlength=len(ref[2]))
+    use_long = sizes[sizes >= long_group].sum() >= long_batch
 
     def n_expand_blocks(n, long):
         smax, emax = (64, 64) if long else (16, 4)
-        return sum(len(cut(sn, emax)) for sn in cut(n, smax)) if n else 0
+        return sum(len(_cut(sn, emax)) for sn in _cut(n, smax)) if n else 0
 
-    exp_blocks = sum(n_expand_blocks(int(n), use_long and n >= 48) for n in sizes) + \
+    exp_blocks = sum(n_expand_blocks(int(n), use_long and n >= long_group) for n in sizes) + \
         n_expand_blocks(int((ref[1] < 0).sum()), False)
+    long_sizes = sizes[sizes >= long_group] if use_long else sizes[:0]
     assert st["max_block_tokens"] <= (64 if use_long else 4)
-    assert (st["max_block_tokens"] > 4) == bool(use_long)
+    assert (st["max_block_tokens"] > 4) == bool(use_long and (long_sizes > 4).any())
     assert st["blocks"] == exp_blocks
+
+
+def test_plan_opts_defaults_and_validation():
+    """lora_plan_opts: the defaults, a pool's options set and read back, and
+    out-of-range values refused with LORA_EINVAL, the pool's options then
+    unchanged."""
+    assert hab.plan_opts_default() == dict(long_group=48, long_batch=1024, shrink_groups=256,
+                                           prefill_groups=256)
+    pool = _pool()
+    assert pool.plan_opts() == hab.plan_opts_default()
+    pool.set_plan_opts(long_group=5, long_batch=7, shrink_groups=384, prefill_groups=65536)
+    want = dict(long_group=5, long_batch=7, shrink_groups=384, prefill_groups=65536)
+    assert pool.plan_opts() == want
+    for bad in (dict(long_group=0), dict(long_batch=-3), dict(shrink_groups=0),
+                dict(shrink_groups=65537), dict(prefill_groups=0), dict(prefill_groups=1 << 20)):
+        with pytest.raises(hab.LoraError) as ei:
+            pool.set_plan_opts(**bad)
+        assert ei.value.status == -1, bad
+        assert pool.plan_opts() == want
+    lib = hab.load()
+    o = hab.PlanOpts()
+    assert lib.lora_pool_set_plan_opts(None, ctypes.byref(o)) == -1
+    assert lib.lora_pool_set_plan_opts(pool.handle, None) == -1
+    assert lib.lora_pool_get_plan_opts(pool.handle, None) == -1
+    assert lib.lora_plan_get_opts(None, ctypes.byref(o)) == -1
+    with pytest.raises(ValueError):
+        pool.set_plan_opts(tile_tokens=8)
+
+
+@pytest.mark.parametrize("long_group,long_batch", [(1, 1), (3, 40), (48, 1024), (200, 1)])
+def test_plan_opts_grouping(long_group, long_batch):
+    """A plan cuts its groups by the long-group thresholds of the options it
+    was built with (the pool's when it was built), against the reference."""
+    for seed in (3, 11, 14):
+        if seed < 10:
+            w = random_case(seed, T=250, h_in=64, h_out=32)
+        elif seed < 13:
+            w = random_case(seed, T=1500, h_in=64, h_out=32, n_adapters=4)
+        else:
+            w = mixed_case(seed, h_in=64, h_out=32, long_tokens=1200)
+        pool = _pool(max_slots=w.pool_size)
+        for i in range(w.pool_size):
+            pool.reserve(i, int(w.ranks[i]), float(w.scales[i]))
+        pool.set_plan_opts(long_group=long_group, long_batch=long_batch)
+        plan = hab.Plan(pool, w.num_tokens, w.seg_starts, w.seg_adapter)
+        assert plan.opts()["long_group"] == long_group
+        ref = reference_plan(w.num_tokens, w.seg_starts, w.seg_adapter, w.ranks)
+        got = plan.export()
+        for k, r in zip(("token_order", "token_group", "group_adapter", "group_rank"), ref):
+            assert np.array_equal(got[k], r), k
+        check_blocks(plan.stats(), ref, long_group, long_batch)
+        # the plan keeps its options when the pool's change; a rebuild takes
+        # the pool's new ones
+        before = (plan.stats(), plan.workspace_bytes(3))
+        pool.set_plan_opts(long_group=48, long_batch=1024, shrink_groups=1024)
+        assert (plan.stats(), plan.workspace_bytes(3)) == before
+        assert plan.opts()["long_group"] == long_group
+        plan.rebuild(w.num_tokens, w.seg_starts, w.seg_adapter)
+        assert plan.opts() == pool.plan_opts()
+        check_blocks(plan.stats(), ref)
 
 
 def test_plan_for_workloads():
@@ -307,13 +374,19 @@ def _random_plans(n):
         yield w
 
 
-@pytest.mark.parametrize("dtype,h_in", [("bf16", [64, 64, 4104]), ("f32", [64, 1000, 64])])
-def test_workspace_bound(dtype, h_in):
+@pytest.mark.parametrize("dtype,h_in,opts", [
+    ("bf16", [64, 64, 4104], {}), ("f32", [64, 1000, 64], {}),
+    ("bf16", [64, 64, 4104], dict(long_group=1, long_batch=1, shrink_groups=1024)),
+    ("bf16", [4096, 64, 14336], dict(long_group=20, long_batch=100, shrink_groups=7)),
+    ("f32", [64, 1000, 64], dict(long_batch=1, shrink_groups=65536))])
+def test_workspace_bound(dtype, h_in, opts):
     """lora_workspace_bytes bounds the workspace of every plan of at most
-    that many tokens and segments, for calls of 1..3 projections."""
-    for w in _random_plans(24):
+    that many tokens and segments, for calls of 1..3 projections, under the
+    pool's plan options."""
+    for w in _random_plans(24 if not opts else 12):
         pool = hab.Pool(1, h_in, [32, 48, 16], 64, dtype, max_slots=w.pool_size,
                         slab_ptr=1 << 20, slab_bytes=1 << 30)
+        pool.set_plan_opts(**opts)
         for i in range(w.pool_size):
             pool.reserve(i, int(w.ranks[i]), float(w.scales[i]))
         plan = hab.Plan(pool, w.num_tokens, w.seg_starts, w.seg_adapter)
