@@ -424,15 +424,6 @@ template <> struct Out4<float> {
     }
 };
 
-// The expand's per-workgroup context: the block, its token rows and the
-// wave's output rows.
-struct ExpandCtx {
-    int b, p, w, n, q;
-    int o_lo, o_hi, yoff, h_out, ks_n, ntiles;
-    float scale;
-    float tsc[4];     // the scale of this lane's token in each 16-token tile
-};
-
 // One output element: bf16 (2 bytes) or float32 (4 bytes).
 template <typename T> struct Out1;
 template <> struct Out1<uint16_t> {
@@ -772,195 +763,6 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     }
 }
 
-// Expand of one workgroup for blocks whose padded rank packs TPL row tiles
-// into one 16-byte load per lane (TPL = 4: r_pad = E / 2 ... see below), or
-// TPL = 1 (one tile per load and K-step).  Row chunks of OTW tiles are
-// double-buffered: the next chunk's B rows and y_in are in flight while the
-// current chunk is computed.
-//
-// Packing: a 16-row tile of B is 16 * r_pad elements.  With G = r_pad / E
-// 16-byte vectors per row and G in {1, 2}, one load of 64 lanes covers
-// TPL = 4 / G consecutive tiles: lane group q reads vector q % G of tile
-// q / G.  The MFMA of tile t then takes v only in the lane groups holding
-// tile t (zero elsewhere), which selects tile t's rows.
-template <typename T, int TT, int KSM, int TPL, bool GATHER = true, typename Args = ExpandArgs,
-          int OTWC = expand_tiles(KSM)>
-__device__ __forceinline__ void expand_body(const Args &a, const BlockDesc &blk,
-                                            const ExpandCtx &c, const int (&trow)[TT],
-                                            const bool (&tv)[TT], float (*vs)[LORA_MAX_RANK + 4]) {
-    constexpr int E = Elem<T>::E;
-    constexpr int SPAN = 4 * E;
-    constexpr int OTW = OTWC;                        // tiles per chunk
-    constexpr int NL = TPL == 1 ? OTW * KSM : OTW / TPL;   // loads per chunk
-    constexpr int CH = OTW * kTile;                  // rows per chunk
-    const int G = TPL == 1 ? 4 : 4 / TPL;            // vectors per row (packed)
-    typedef typename Out4<T>::raw raw;
-
-    const rsrc_t br = make_rsrc(
-        a.slab + extent(blk.ext_lo, blk.ext_hi) +
-            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[c.p]),
-        uint32_t(c.h_out) * uint32_t(blk.r_pad) * sizeof(T));
-    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
-    const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
-    const int64_t ld_in = a.base ? a.ldb : a.ldy;
-
-    // Byte offsets hoisted out of the row loops: a masked token's row offset
-    // is already out of range (kOOB + o * size stays >= 2^31, below 2^32).
-    uint32_t in_row[TT], y_row[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        in_row[tt] = tv[tt] ? uint32_t((int64_t(trow[tt]) * ld_in + c.yoff) * sizeof(T)) : kOOB;
-        y_row[tt] = tv[tt] ? uint32_t((int64_t(trow[tt]) * a.ldy + c.yoff) * sizeof(T)) : kOOB;
-    }
-    const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
-    // this lane's tile within a load and element offset within its B row
-    const int lane_tile = TPL == 1 ? 0 : c.q / G;
-    const uint32_t lane_col = uint32_t(TPL == 1 ? c.q * E : (c.q % G) * E) * sizeof(T);
-    // bf16: within each pair of row tiles the B rows are taken in the order
-    // that leaves a lane 8 consecutive outputs (4 from each tile of the
-    // pair), so y_in and y move 16 bytes a lane: tile T's MFMA row n is
-    // output row 16 (T & ~1) + 8 (n / 4) + 4 (T & 1) + n % 4 of the chunk.
-    constexpr bool PAIR = sizeof(T) == 2;
-    static_assert(!PAIR || OTW % 2 == 0, "row tiles of a chunk come in pairs");
-    auto brow = [&](int tile, int n) {
-        return PAIR ? (tile & ~1) * kTile + 8 * (n >> 2) + 4 * (tile & 1) + (n & 3)
-                    : tile * kTile + n;
-    };
-    constexpr int NY = PAIR ? OTW / 2 : OTW;         // y_in loads per token tile and chunk
-    typedef typename std::conditional<PAIR, u32x4, raw>::type yraw;
-
-    auto load = [&](int o0, u32x4 (&bf)[NL], yraw (&yin)[NY][TT]) {
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-            const int t = TPL == 1 ? l / KSM : l * TPL;          // first tile of the load
-            const int ks = TPL == 1 ? l % KSM : 0;
-            const int row = o0 + brow(t + lane_tile, c.n);
-            const bool ok = row < c.o_hi &&
-                            (TPL > 1 || (ks < c.ks_n && ks * SPAN + c.q * E < blk.r_pad));
-            bf[l] = bload16(br, off_or_oob(ok, uint32_t(row) * row_bytes + lane_col +
-                                                   uint32_t(ks * SPAN) * sizeof(T)));
-        }
-#pragma unroll
-        for (int oy = 0; oy < NY; ++oy) {
-            const int o = PAIR ? o0 + oy * 2 * kTile + 8 * c.q : o0 + oy * kTile + 4 * c.q;
-            const uint32_t oo = uint32_t(o) * sizeof(T);
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if constexpr (PAIR)
-                    yin[oy][tt] = bload16(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
-                else
-                    yin[oy][tt] = Out4<T>::load(inr, o < c.o_hi ? in_row[tt] + oo : kOOB);
-            }
-        }
-    };
-
-    u32x4 bfA[NL], bfB[NL];
-    yraw yinA[NY][TT], yinB[NY][TT];
-    load(c.o_lo, bfA, yinA);
-
-    if constexpr (GATHER) {      // else v (cores applied) is in LDS already
-        gather_v<TT>(a, blk, c.p, vs);
-        __syncthreads();
-        if (a.sigma_kind)
-            apply_sigma<TT * kTile * LORA_MAX_RANK / (kWaves * kWaveSize)>(a, blk, c.p, vs);
-    }
-    if (c.o_lo >= c.o_hi) return;
-
-    // v operand per (token tile, K-step); packed blocks have one K-step
-    VOperand<T> vop[TT][KSM];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-        for (int ks = 0; ks < KSM; ++ks) {
-            float f[E];
-            const int j0 = TPL == 1 ? ks * SPAN + c.q * E : (c.q % G) * E;
-            const bool ok = tv[tt] && ks < c.ks_n && j0 < blk.r_pad;
-            const int row = ok ? tt * kTile + c.n : 0;
-            const int col = ok ? j0 : 0;
-#pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[row][col + e]);
-                f[e] = ok ? w4[0] : 0.f; f[e + 1] = ok ? w4[1] : 0.f;
-                f[e + 2] = ok ? w4[2] : 0.f; f[e + 3] = ok ? w4[3] : 0.f;
-            }
-            vop[tt][ks].set(f);
-        }
-    }
-
-    // B v of row tile ot for token tile tt: D rows 4q .. 4q + 3 of the tile
-    auto tile_acc = [&](int ot, int tt, const u32x4 (&bf)[NL]) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (TPL == 1) {
-#pragma unroll
-            for (int ks = 0; ks < KSM; ++ks) {
-                if (ks >= c.ks_n) continue;
-#pragma unroll
-                for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc)
-                    acc = mma<T>(bf[ot * KSM + ks], vop[tt][ks].piece[pc], acc);
-            }
-        } else {
-            const bool mine = c.q / G == ot % TPL;   // lane groups of this tile
-#pragma unroll
-            for (int pc = VOperand<T>::kPieces - 1; pc >= 0; --pc) {
-                const u32x4 vp = vop[tt][0].piece[pc];
-                const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-                acc = mma<T>(bf[ot / TPL], mine ? vp : z, acc);
-            }
-        }
-        return acc;
-    };
-
-    auto compute = [&](int o0, const u32x4 (&bf)[NL], const yraw (&yin)[NY][TT]) {
-#pragma unroll
-        for (int oy = 0; oy < NY; ++oy) {
-            const int obase = o0 + oy * (PAIR ? 2 : 1) * kTile;
-            if (obase >= c.o_hi) break;              // wave-uniform
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (tt >= c.ntiles) continue;        // wave-uniform
-                if constexpr (PAIR) {
-                    // tiles 2 oy and 2 oy + 1: this lane's outputs 8 q .. 8 q + 7
-                    const f32x4 a0 = tile_acc(2 * oy, tt, bf);
-                    const f32x4 a1 = tile_acc(2 * oy + 1, tt, bf);
-                    const int o = obase + 8 * c.q;
-                    const u32x4 w = yin[oy][tt];
-                    float out[8];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        out[2 * i] = bf16_lo(w[i]) + c.tsc[tt] * a0[2 * i];
-                        out[2 * i + 1] = bf16_hi(w[i]) + c.tsc[tt] * a0[2 * i + 1];
-                        out[4 + 2 * i] = bf16_lo(w[2 + i]) + c.tsc[tt] * a1[2 * i];
-                        out[5 + 2 * i] = bf16_hi(w[2 + i]) + c.tsc[tt] * a1[2 * i + 1];
-                    }
-                    const u32x4 pk = u32x4{bf16x2_rne(out[0], out[1]), bf16x2_rne(out[2], out[3]),
-                                           bf16x2_rne(out[4], out[5]), bf16x2_rne(out[6], out[7])};
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        pk, yr, int(o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB), 0,
-                        kOut);
-                } else {
-                    const f32x4 acc = tile_acc(oy, tt, bf);
-                    const int o = obase + 4 * c.q;
-                    float in[4], out[4];
-                    Out4<T>::unpack(yin[oy][tt], in);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) out[i] = in[i] + c.tsc[tt] * acc[i];
-                    Out4<T>::store(yr, o < c.o_hi ? y_row[tt] + uint32_t(o) * sizeof(T) : kOOB,
-                                   Out4<T>::pack(out));
-                }
-            }
-        }
-    };
-
-    for (int o0 = c.o_lo; o0 < c.o_hi; o0 += 2 * CH) {
-        if (o0 + CH < c.o_hi) load(o0 + CH, bfB, yinB);
-        compute(o0, bfA, yinA);
-        const int o1 = o0 + CH;
-        if (o1 >= c.o_hi) break;
-        if (o1 + CH < c.o_hi) load(o1 + CH, bfA, yinA);
-        compute(o1, bfB, yinB);
-    }
-}
-
 // Decode expand: plans whose blocks hold at most kValuTokens tokens.  A
 // unit is (block, projection, kWaves slices of decode_wave_rows rows); the
 // blocks are ordered by padded rank, and a unit's rank class, block,
@@ -1268,12 +1070,12 @@ constexpr int prefill_kbatch(int pairs) { return pairs <= 1 ? 4 : pairs <= 3 ? 2
 constexpr int prefill_ksm(int rtm, int e) {
     return (rtm * kTile + 4 * e - 1) / (4 * e) == 3 ? 4 : (rtm * kTile + 4 * e - 1) / (4 * e);
 }
-// Row tiles per chunk of the expand step: half the decode geometry's, so two
-// chunks in flight fit the 128 VGPRs of a 16-wave workgroup (whole pairs in
-// bf16).
+// Row tiles per chunk of the expand step: a wave holds B fragments for 8 /
+// ksm row tiles of ksm K-steps each, halved so that two chunks in flight fit
+// the 128 VGPRs of a 16-wave workgroup (whole pairs of tiles in bf16).
 constexpr int prefill_otw(int ksm, int esize) {
-    return esize == 2 ? (expand_tiles(ksm) / 2 < 2 ? 2 : expand_tiles(ksm) / 2)
-                      : (expand_tiles(ksm) / 2 < 1 ? 1 : expand_tiles(ksm) / 2);
+    const int half = (ksm >= 8 ? 1 : 8 / ksm) / 2;
+    return esize == 2 ? (half < 2 ? 2 : half) : (half < 1 ? 1 : half);
 }
 
 // The B step of a prefill workgroup for one wave: output rows of every

@@ -301,10 +301,6 @@ constexpr bool decode_rows_agree() {
 }
 static_assert(decode_rows_agree(), "decode unit rows are kWaves wave slices");
 
-// 16-row output tiles per chunk of the MFMA expand step, for kernels built
-// for `ks` K-steps (ranks / (4 fragment elements)) at most: the wave keeps 8 B
-// fragments.
-constexpr int expand_tiles(int ks) { return ks >= 8 ? 1 : 8 / ks; }
 
 // Sets the thread's last-error message (lora_last_error) and returns st.
 lora_status set_error(lora_status st, const char *msg);
