@@ -14,6 +14,7 @@ LORA_MAX_PROJ = 8
 LORA_MAX_RANK = 64
 LORA_STATIC_SCRATCH_MIB = 64
 LORA_MAX_MERGE = 4
+LORA_DEBUG_SLAB, LORA_DEBUG_TOKEN, LORA_DEBUG_ROW = 1, 2, 4
 
 STATUS = {0: "LORA_OK", -1: "LORA_EINVAL", -2: "LORA_ENOSPC", -3: "LORA_ENOENT",
           -4: "LORA_ERANK", -5: "LORA_EDTYPE", -6: "LORA_ESEG", -7: "LORA_EHIP",
@@ -67,6 +68,7 @@ SIGNATURES = {
     "lora_pool_set_plan_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
     "lora_pool_get_plan_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
     "lora_plan_get_opts": (_i32, [_vp, ctypes.POINTER(PlanOpts)]),
+    "lora_debug_checks": (_i32, [_i32p, ctypes.POINTER(ctypes.c_uint32), _i32]),
     "lora_plan_workspace_bytes": (_u64, [_vp, _i32]),
     "lora_workspace_bytes": (_u64, [_vp, _i32, _i32, _i32]),
     "lora_plan_rebuild": (_i32, [_vp, _i32, _i32p, _i32p, _i32p, ctypes.POINTER(_f32), _i32]),

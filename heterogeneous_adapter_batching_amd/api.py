@@ -478,6 +478,16 @@ def plan_opts_default() -> dict:
     return _opts_dict(o)
 
 
+def debug_checks(clear: bool = False):
+    """(enabled, errors): whether the loaded library is the bounds-checked
+    debug build, and the LORA_DEBUG_* bits its kernels set on the current
+    device since the last clear (waits for the device; 0 in the release
+    build); `clear` resets them."""
+    en, bits = ctypes.c_int32(), ctypes.c_uint32()
+    check(load().lora_debug_checks(ctypes.byref(en), ctypes.byref(bits), int(bool(clear))))
+    return bool(en.value), int(bits.value)
+
+
 def _projs(projs):
     t = tuple(int(p) for p in projs)
     return len(t), _i32_const(t)

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhab_lora.so")
+# the same library with the kernels' bounds checks compiled in (LORA_SGMV_DEBUG)
+DEBUG_LIB = os.path.join(PKG, "libhab_lora_debug.so")
+DEBUG_FLAGS = ["-DLORA_SGMV_DEBUG"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -27,18 +30,31 @@ FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
          "-I", INCLUDE, "-I", CSRC]
 
 
-def build(out: str = LIB, extra=()) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SOURCES]
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+def _start(out: str, extra):
+    cmd = [HIPCC, *FLAGS, *extra, "-o", out + ".tmp", *SOURCES]
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _finish(proc, out: str) -> str:
+    text = proc.communicate()[0]
     noise = "is not a recognized feature for this target"
-    log = "\n".join(l for l in res.stdout.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{log}")
+    log = "\n".join(l for l in text.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{log}")
     if log.strip():
         print(log, file=sys.stderr)
-    os.replace(tmp, out)
+    os.replace(out + ".tmp", out)
     return out
+
+
+def build(out: str = LIB, extra=()) -> str:
+    return _finish(_start(out, extra), out)
+
+
+def build_all() -> list:
+    """The library and its debug build, compiled side by side."""
+    jobs = [(LIB, _start(LIB, ())), (DEBUG_LIB, _start(DEBUG_LIB, DEBUG_FLAGS))]
+    return [_finish(proc, out) for out, proc in jobs]
 
 
 # The host sources built with g++ alone (no device code: host_only.cpp
@@ -60,4 +76,4 @@ def host_sanitized(out: str) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build_all())

@@ -23,4 +23,6 @@ hipError_t launch_expand_merge(int, int, const MergeArgs &, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
 hipError_t static_scratch(void **, uint64_t *) { return hipErrorInvalidValue; }
+bool debug_build() { return false; }
+hipError_t debug_errors(uint32_t *, bool) { return hipErrorInvalidValue; }
 }  // namespace lora

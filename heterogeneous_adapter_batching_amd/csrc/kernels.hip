@@ -111,6 +111,56 @@ __device__ __forceinline__ uint64_t extent(uint32_t lo, uint32_t hi) {
     return (uint64_t(hi) << 32) | lo;
 }
 
+// Debug build (LORA_SGMV_DEBUG): a unit checks every adapter block it
+// addresses against the slab and every token row and plan position it reads
+// against the batch; a failed check sets a bit of g_debug_errors and switches
+// the access off (a zero-sized resource: the block reads as zeros; an absent
+// row), so nothing outside the slab or the tensors is touched.  The release
+// build compiles the checks out.
+#ifdef LORA_SGMV_DEBUG
+constexpr bool kDebug = true;
+#else
+constexpr bool kDebug = false;
+#endif
+__device__ uint32_t g_debug_errors;
+
+// The byte range of the adapter block at slab offset `off`: `bytes`, or 0
+// when it would leave the slab (debug build).
+__device__ __forceinline__ uint32_t dbg_block(const DebugBounds &d, uint64_t off,
+                                              uint64_t bytes) {
+    if constexpr (kDebug) {
+        if (off + bytes > d.slab_bytes) {
+            atomicOr(&g_debug_errors, kDbgSlab);
+            return 0u;
+        }
+    }
+    return uint32_t(bytes);
+}
+
+// A token row from the plan: r, or -1 (absent) when it is outside [-1, T)
+// (debug build).
+__device__ __forceinline__ int dbg_token(const DebugBounds &d, int r) {
+    if constexpr (kDebug) {
+        if (r < -1 || r >= d.num_tokens) {
+            atomicOr(&g_debug_errors, kDbgToken);
+            return -1;
+        }
+    }
+    return r;
+}
+
+// The token count of a descriptor whose rows [off, off + n) index per-row
+// tables of the plan: n, or 0 when they leave the plan (debug build).
+__device__ __forceinline__ int dbg_rows(const DebugBounds &d, int off, int n) {
+    if constexpr (kDebug) {
+        if (off < 0 || n < 0 || off + n > d.num_rows) {
+            atomicOr(&g_debug_errors, kDbgRow);
+            return 0;
+        }
+    }
+    return n;
+}
+
 // Workgroup g runs on XCD g % kXcds.  Units are dealt to the XCDs in groups
 // of `gs` consecutive units, round-robin: a group (e.g. the projections that
 // read one x chunk) shares one L2, while consecutive groups, whose work may
@@ -204,8 +254,11 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     const int key = MP ? u / a.c0 : u / per;
     int trow[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) trow[tt] = a.tile_tok[key * kMaxBlockTokens + tt * kTile + n];
-    const TileDesc td = load_invariant(a.tiles + key);
+    for (int tt = 0; tt < TT; ++tt)
+        trow[tt] = dbg_token(a.dbg, a.tile_tok[key * kMaxBlockTokens + tt * kTile + n]);
+    TileDesc td = load_invariant(a.tiles + key);
+    if constexpr (kDebug)            // the tile's rows: inside the plan, at most TT tiles
+        td.n_tok = min(dbg_rows(a.dbg, td.tok_off, td.n_tok), TT * kTile);
     int c, p0;
     if constexpr (MP) {
         c = u - key * a.c0;
@@ -227,10 +280,11 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
     const int j = td.tile * kTile + n;
     const bool jv = j < td.r_pad;
     auto load_a = [&](int p, u32x4 (&af)[F]) {
+        const uint64_t off = extent(td.ext_lo, td.ext_hi) +
+                             uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]);
         const rsrc_t ar = make_rsrc(
-            a.slab + extent(td.ext_lo, td.ext_hi) +
-                uint64_t(td.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
-            uint32_t(td.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
+            a.slab + off,
+            dbg_block(a.dbg, off, uint64_t(td.r_pad) * uint64_t(a.h_in_pad) * sizeof(T)));
 #pragma unroll
         for (int f = 0; f < F; ++f) {
             const int k = k_lo + f * SPAN + q * E;
@@ -336,7 +390,9 @@ template <int TT>
 __global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
     const int bp = blockIdx.x;
     const int b = bp / a.nproj, p = bp % a.nproj;
-    const BlockDesc blk = load_invariant(a.blocks + b);
+    BlockDesc blk = load_invariant(a.blocks + b);
+    if constexpr (kDebug)
+        blk.n_tok = min(dbg_rows(a.dbg, blk.tok_off, blk.n_tok), kMaxBlockTokens);
     const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
     const int quads = a.r_max / 4;
     for (int i = threadIdx.x; i < blk.n_tok * quads; i += blockDim.x) {
@@ -345,7 +401,8 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceArgs a) {
         if (j < blk.r_pad)
             s4 = chunk_sum(pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, TT),
                            uint32_t(a.nproj * TT * kTile * kTile), a.c0);
-        const int t = a.tok[blk.tok_off + ti];
+        const int t = dbg_token(a.dbg, a.tok[blk.tok_off + ti]);
+        if (kDebug && t < 0) continue;
         *reinterpret_cast<f32x4 *>(a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j) = s4;
     }
 }
@@ -444,31 +501,6 @@ template <> struct Out1<float> {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, int(off), 0, kOut);
     }
 };
-
-// v of the block's tokens into LDS, once per workgroup: from the shrink's
-// chunk partials (summed in the one chunk order) or a caller's v.
-template <int TT>
-__device__ __forceinline__ void gather_v(const ExpandArgs &a, const BlockDesc &blk, int p,
-                                         float (*vs)[LORA_MAX_RANK + 4]) {
-    const int quads = blk.r_pad / 4;
-    if (a.partial) {
-        const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
-        const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
-        for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
-            const int ti = i / quads, j = (i % quads) * 4;
-            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = chunk_sum(
-                pr, partial_off(blk.rt_before, j, blk.slot0 + ti, p, a.nproj, a.c0, a.ptt),
-                stride, a.c0);
-        }
-    } else {
-        for (int i = threadIdx.x; i < blk.n_tok * quads; i += kWaves * kWaveSize) {
-            const int ti = i / quads, j = (i % quads) * 4;
-            const int t = a.tok[blk.tok_off + ti];
-            *reinterpret_cast<f32x4 *>(&vs[ti][j]) = *reinterpret_cast<const f32x4 *>(
-                a.v + int64_t(t) * a.ldv + int64_t(p) * a.r_max + j);
-        }
-    }
-}
 
 // The core step of jointly compressed adapters ("Compress then Serve",
 // rebuttal pseudocode of add_lora_slice_with_sigma, step 2): each token's v
@@ -619,10 +651,11 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     const int nv = blk.r_pad / E;                    // wave-uniform, <= NV
     const int nt = blk.n_tok;                        // wave-uniform, <= NT
     const int yoff = a.y_off[p];
+    const uint64_t boff = extent(blk.ext_lo, blk.ext_hi) +
+                          uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]);
     const rsrc_t br = make_rsrc(
-        a.slab + extent(blk.ext_lo, blk.ext_hi) +
-            uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
-        uint32_t(a.h_out[p]) * uint32_t(blk.r_pad) * sizeof(T));
+        a.slab + boff,
+        dbg_block(a.dbg, boff, uint64_t(a.h_out[p]) * uint64_t(blk.r_pad) * sizeof(T)));
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
     const int64_t ld_in = a.base ? a.ldb : a.ldy;
@@ -812,10 +845,13 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
     }
     const int slice = rem - first;
 
-    const BlockDesc blk = load_invariant(a.blocks + b);
+    BlockDesc blk = load_invariant(a.blocks + b);
     const int4 bt4 = load_invariant(reinterpret_cast<const int4 *>(a.block_tok + b * kMaxBlockTokens));
-    const int tr[kValuTokens] = {bt4.x, bt4.y, bt4.z, bt4.w};
+    const int tr[kValuTokens] = {dbg_token(a.dbg, bt4.x), dbg_token(a.dbg, bt4.y),
+                                 dbg_token(a.dbg, bt4.z), dbg_token(a.dbg, bt4.w)};
     static_assert(kValuTokens == 4, "token rows load as one int4");
+    if constexpr (kDebug)            // the block's rows: inside the plan, at most 4
+        blk.n_tok = min(dbg_rows(a.dbg, blk.tok_off, blk.n_tok), kValuTokens);
 
     int h_out = hout[0];
 #pragma unroll
@@ -892,7 +928,12 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         run += cnt[i];
     }
     const int slice = rem - first;
-    const MergeBlock mb = load_invariant(a.mblocks + b);
+    MergeBlock mb = load_invariant(a.mblocks + b);
+    if constexpr (kDebug) {          // token rows inside the batch, at most 4 of them
+        mb.n_tok = min(max(mb.n_tok, 0), kValuTokens);
+#pragma unroll
+        for (int t = 0; t < kValuTokens; ++t) mb.tok[t] = dbg_token(a.dbg, mb.tok[t]);
+    }
     int h_out = hout[0];
 #pragma unroll
     for (int i = 1; i < LORA_MAX_PROJ; ++i) h_out = p == i ? hout[i] : h_out;
@@ -952,9 +993,10 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         }
         // the slot adapter's B rows
         const uint32_t row_bytes = uint32_t(sl.r_pad) * sizeof(T);
-        const rsrc_t br = make_rsrc(a.slab + extent(sl.ext_lo, sl.ext_hi) +
-                                        uint64_t(sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]),
-                                    uint32_t(h_out) * row_bytes);
+        const uint64_t boff = extent(sl.ext_lo, sl.ext_hi) +
+                              uint64_t(sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]);
+        const rsrc_t br = make_rsrc(a.slab + boff,
+                                    dbg_block(a.dbg, boff, uint64_t(h_out) * row_bytes));
         const int nv = sl.r_pad / E;
         u32x4 bv[NVM][RPL];
 #pragma unroll
@@ -1169,10 +1211,12 @@ __device__ __forceinline__ void prefill_rows(const PrefillArgs &a, const BlockDe
         where(i, p, o0);
         const int h = sel(p, a.h_out[0], a.h_out[1], a.h_out[2]);
         const int top = sel(p, hi[0], hi[NP > 1 ? 1 : 0], hi[NP > 2 ? 2 : 0]);
-        const rsrc_t br = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
-                                        uint64_t(blk.r_pad) * sizeof(T) *
-                                            uint64_t(sel(p, a.coef_b[0], a.coef_b[1], a.coef_b[2])),
-                                    uint32_t(h) * uint32_t(blk.r_pad) * sizeof(T));
+        const uint64_t boff = extent(blk.ext_lo, blk.ext_hi) +
+                              uint64_t(blk.r_pad) * sizeof(T) *
+                                  uint64_t(sel(p, a.coef_b[0], a.coef_b[1], a.coef_b[2]));
+        const rsrc_t br = make_rsrc(a.slab + boff,
+                                    dbg_block(a.dbg, boff, uint64_t(h) * uint64_t(blk.r_pad) *
+                                                               sizeof(T)));
         const uint32_t yoff = uint32_t(sel(p, a.y_off[0], a.y_off[1], a.y_off[2])) * sizeof(T);
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
@@ -1354,6 +1398,8 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
     const int bt = u / a.osplit;
     const int b = bt / kPrefillTiles, tile = bt % kPrefillTiles;
     BlockDesc blk = load_invariant(a.blocks + b);
+    if constexpr (kDebug)            // the block's rows: inside the plan, at most one block
+        blk.n_tok = min(dbg_rows(a.dbg, blk.tok_off, blk.n_tok), kMaxBlockTokens);
     const int off = tile * kTile;
     if (off >= blk.n_tok) return;                    // whole workgroup: an empty tile
     blk.tok_off += off;
@@ -1363,8 +1409,12 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
     // with the descriptor's; each lane then picks its own row by selects, so
     // no vector round trip precedes the first loads
     struct Rows { int32_t r[kTile]; };
-    const Rows rows = load_invariant(reinterpret_cast<const Rows *>(a.block_tok) +
-                                     (b * kMaxBlockTokens + off) / kTile);
+    Rows rows = load_invariant(reinterpret_cast<const Rows *>(a.block_tok) +
+                               (b * kMaxBlockTokens + off) / kTile);
+    if constexpr (kDebug) {
+#pragma unroll
+        for (int k = 0; k < kTile; ++k) rows.r[k] = dbg_token(a.dbg, rows.r[k]);
+    }
     int trow = rows.r[0];
 #pragma unroll
     for (int k = 1; k < kTile; ++k) trow = n == k ? rows.r[k] : trow;
@@ -1393,10 +1443,13 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
             const uint32_t xrow = trow >= 0 ? uint32_t(int64_t(trow) * a.ldx * sizeof(T)) : kOOB;
             rsrc_t ar[NP];
 #pragma unroll
-            for (int p = 0; p < NP; ++p)
-                ar[p] = make_rsrc(a.slab + extent(blk.ext_lo, blk.ext_hi) +
-                                      uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]),
-                                  uint32_t(blk.r_pad) * uint32_t(a.h_in_pad) * sizeof(T));
+            for (int p = 0; p < NP; ++p) {
+                const uint64_t aoff = extent(blk.ext_lo, blk.ext_hi) +
+                                      uint64_t(blk.r_pad) * sizeof(T) * uint64_t(a.coef_a[p]);
+                ar[p] = make_rsrc(a.slab + aoff,
+                                  dbg_block(a.dbg, aoff, uint64_t(blk.r_pad) *
+                                                             uint64_t(a.h_in_pad) * sizeof(T)));
+            }
             f32x4 acc[NP][RTM];
 #pragma unroll
             for (int p = 0; p < NP; ++p)
@@ -1523,6 +1576,9 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
                                            : f32x4{0.f, 0.f, 0.f, 0.f};
             const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
                                            : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
+            if (kDebug && (a.v_by_pos ? dbg_rows(a.dbg, int(row), 1) == 0
+                                      : dbg_token(a.dbg, int(row)) < 0))
+                continue;
             *reinterpret_cast<f32x4 *>(a.v + row * a.ldv + int64_t(p) * a.r_max + j) = s4;
         }
     } else {
@@ -1539,6 +1595,11 @@ __global__ __launch_bounds__(kPrefillWaves * kWaveSize, 4) void k_prefill(const 
                     const int p = rem / quads, j = (rem - p * quads) * 4;
                     const int64_t row = a.v_by_pos ? int64_t(blk.tok_off + ti)
                                                    : int64_t(a.block_tok[b * kMaxBlockTokens + off + ti]);
+                    if (kDebug && (a.v_by_pos ? dbg_rows(a.dbg, int(row), 1) == 0
+                                              : dbg_token(a.dbg, int(row)) < 0)) {
+                        *reinterpret_cast<f32x4 *>(&vs[p][ti][j]) = f32x4{0.f, 0.f, 0.f, 0.f};
+                        continue;
+                    }
                     *reinterpret_cast<f32x4 *>(&vs[p][ti][j]) = *reinterpret_cast<const f32x4 *>(
                         a.v + row * a.ldv + int64_t(p) * a.r_max + j);
                 }
@@ -1673,6 +1734,24 @@ hipError_t static_scratch(void **ptr, uint64_t *bytes) {
     }
     *ptr = g_scratch_ptr[dev];
     *bytes = kStaticScratchBytes;
+    return hipSuccess;
+}
+
+bool debug_build() { return kDebug; }
+
+hipError_t debug_errors(uint32_t *bits, bool clear) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    uint32_t v = 0;
+    e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_errors), sizeof(v), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    if (clear) {
+        const uint32_t zero = 0;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_debug_errors), &zero, sizeof(zero), 0,
+                              hipMemcpyHostToDevice);
+        if (e != hipSuccess) return e;
+    }
+    *bits = v;
     return hipSuccess;
 }
 

@@ -987,6 +987,18 @@ lora_status lora_plan_destroy(lora_plan *pl) {
     return LORA_OK;
 }
 
+lora_status lora_debug_checks(int32_t *enabled, uint32_t *errors, int32_t clear) {
+    const bool dbg = lora::debug_build();
+    if (enabled) *enabled = dbg ? 1 : 0;
+    uint32_t bits = 0;
+    if (dbg && (errors || clear)) {
+        const hipError_t e = lora::debug_errors(&bits, clear != 0);
+        if (e != hipSuccess) return hip_fail(e, "debug error word");
+    }
+    if (errors) *errors = bits;
+    return LORA_OK;
+}
+
 lora_status lora_plan_get_opts(const lora_plan *pl, lora_plan_opts *o) {
     if (!pl || !o) return fail(LORA_EINVAL, "null pointer");
     *o = pl->opts;
@@ -1251,6 +1263,12 @@ Partials workspace_partials(const lora_plan *pl) {
     return pt;
 }
 
+// What the debug build checks each unit against (nothing in the release
+// build): the slab's bytes, the batch's tokens and the plan's rows.
+lora::DebugBounds debug_bounds(const lora_pool *p, const lora_plan *pl) {
+    return lora::DebugBounds{p->slab_bytes, pl->T, pl->rows()};
+}
+
 lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, int32_t nproj,
                        const int32_t *projs, const void *x, int64_t ldx, const CallCheck &cc,
                        hipStream_t st, int32_t *c0_out, const Partials &pt) {
@@ -1272,6 +1290,7 @@ lora_status run_shrink(const lora_pool *p, const lora_plan *pl, int32_t layer, i
         return LORA_OK;
     }
     lora::ShrinkArgs a{};
+    a.dbg = debug_bounds(p, pl);
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
     a.tile_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_ttok) +
@@ -1317,6 +1336,7 @@ lora_status run_reduce(const lora_pool *p, const lora_plan *pl, int32_t nproj, i
                        float *v, int64_t ldv, hipStream_t st) {
     if (pl->nb_act == pl->nb_long) return LORA_OK;
     lora::ReduceArgs a{};
+    a.dbg = debug_bounds(p, pl);
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
     a.blocks = reinterpret_cast<const BlockDesc *>(ws + pl->lay.off_blocks) + pl->nb_long;
@@ -1361,6 +1381,7 @@ lora_status run_expand_merge(const lora_pool *p, const lora_plan *pl, int32_t la
                              hipStream_t st, const Partials &pt) {
     if (pl->mblocks.empty()) return LORA_OK;
     lora::MergeArgs a{};
+    a.dbg = debug_bounds(p, pl);
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     const int32_t es = esize(p->d.dtype);
     a.slab = p->slab;
@@ -1409,6 +1430,7 @@ lora_status run_expand(const lora_pool *p, const lora_plan *pl, int32_t layer, i
     const int32_t nl = pl->nb_long;
     if (nb == nl) return LORA_OK;
     lora::ExpandArgs a{};
+    a.dbg = debug_bounds(p, pl);
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
     a.tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_tok);
@@ -1500,6 +1522,7 @@ lora_status run_prefill(const lora_pool *p, const lora_plan *pl, int32_t layer, 
                         const PrefillIO &io, hipStream_t st, const Cores &cores = Cores()) {
     if (!pl->prefill()) return LORA_OK;
     lora::PrefillArgs a{};
+    a.dbg = debug_bounds(p, pl);
     const uint8_t *ws = static_cast<const uint8_t *>(pl->ws);
     a.slab = p->slab;
     a.block_tok = reinterpret_cast<const int32_t *>(ws + pl->lay.off_btok);

@@ -91,6 +91,20 @@ struct TileDesc {
 };
 static_assert(sizeof(TileDesc) == 32, "TileDesc is 32 bytes");
 
+// What the debug build checks every unit against (see LORA_SGMV_DEBUG in
+// kernels.hip): the slab's bytes (every adapter block a unit addresses lies
+// inside), the tokens of the batch (every token row read from the plan lies
+// in [0, num_tokens), -1 where a row may be absent) and the plan's rows
+// (plan positions that index per-row tables lie in [0, num_rows)).
+struct DebugBounds {
+    uint64_t slab_bytes;
+    int32_t num_tokens;
+    int32_t num_rows;
+};
+// bits of the debug build's error word (lora_debug_checks)
+enum : uint32_t { kDbgSlab = LORA_DEBUG_SLAB, kDbgToken = LORA_DEBUG_TOKEN,
+                  kDbgRow = LORA_DEBUG_ROW };
+
 // Shrink: one workgroup per unit (rank tile, k-chunk c, projection i), unit
 // u = tile * nproj * c0 + c * nproj + i, so the projections that read the
 // same x chunk are consecutive and are placed on one XCD.
@@ -113,6 +127,7 @@ struct ShrinkArgs {
     int32_t units;
     int32_t grid;                // workgroups launched: units rounded up to kXcds * nproj
     uint32_t x_bytes;            // buffer range (at most kMaxTensorBytes)
+    DebugBounds dbg;             // checked by the debug build only
 };
 
 // fragments (16 bytes per lane) a shrink wave loads up front
@@ -131,6 +146,7 @@ struct ReduceArgs {
     int32_t nproj;
     int32_t c0;
     int32_t r_max;
+    DebugBounds dbg;             // checked by the debug build only
 };
 
 
@@ -182,6 +198,7 @@ struct ExpandArgs {
     // of rows = 1 << decode_unit_rows_log2(padded rank) output rows.
     int32_t cls_unit0[kMaxClasses + 1];
     int32_t cls_rb[kMaxClasses];
+    DebugBounds dbg;             // checked by the debug build only
 };
 
 // Prefill: units are (long block, token tile, row part), unit u = (b *
@@ -220,6 +237,7 @@ struct PrefillArgs {
     uint32_t x_bytes;            // buffer ranges (each at most kMaxTensorBytes)
     uint32_t y_bytes;
     uint32_t base_bytes;
+    DebugBounds dbg;             // checked by the debug build only
 };
 
 // Weighted merge of several adapters per request, in one pass: the shrink
@@ -268,6 +286,7 @@ struct MergeArgs {
     uint32_t partial_bytes;
     uint32_t y_bytes;
     uint32_t base_bytes;
+    DebugBounds dbg;             // checked by the debug build only
 };
 
 // Decode expand geometry.  A B row of r_pad elements is nv 16-byte vectors;
@@ -332,5 +351,10 @@ hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid,
 // the current device's copy, found once per device, and its size in bytes.
 constexpr uint64_t kStaticScratchBytes = uint64_t(LORA_STATIC_SCRATCH_MIB) << 20;
 hipError_t static_scratch(void **ptr, uint64_t *bytes);
+
+// Whether the kernels were built with LORA_SGMV_DEBUG, and the current
+// device's debug error bits (after waiting for the device), cleared on request.
+bool debug_build();
+hipError_t debug_errors(uint32_t *bits, bool clear);
 
 }  // namespace lora

@@ -558,6 +558,28 @@ lora_status sgmv_fused_sigma(const lora_pool *p, const lora_plan *pl, int32_t la
                              int32_t num_sigma, const void *base, int64_t ldb, void *y,
                              int64_t ldy, void *stream);
 
+/* --------------------------------------------------------------- debug ---- */
+/* The library built with LORA_SGMV_DEBUG (libhab_lora_debug.so, for
+ * debugging the kernels or a caller's plan memory) checks in every work unit
+ * that each adapter block it addresses lies inside the pool's slab
+ * (LORA_DEBUG_SLAB), that each token row it reads from the plan lies in
+ * [0, num_tokens) or is the -1 of an absent row (LORA_DEBUG_TOKEN), and that
+ * each plan position it indexes a per-row table with lies inside the plan
+ * (LORA_DEBUG_ROW).  A failed check sets its bit in a device-wide error word
+ * and switches that access off (the block reads as zeros, the row is taken
+ * as absent), so the launch ends normally with a wrong result instead of
+ * reading outside the slab or the caller's tensors.  The release build
+ * compiles the checks out.
+ * lora_debug_checks reports whether the loaded build checks (*enabled, 1 or
+ * 0) and the error bits set on the current device since the last clear
+ * (*errors; always 0 in the release build), and with `clear` resets them.
+ * It waits for the current device to finish its work.  Either pointer may be
+ * NULL.  Errors: LORA_EHIP. */
+#define LORA_DEBUG_SLAB 1u
+#define LORA_DEBUG_TOKEN 2u
+#define LORA_DEBUG_ROW 4u
+lora_status lora_debug_checks(int32_t *enabled, uint32_t *errors, int32_t clear);
+
 /* ------------------------------------------------------- no allocation ---- */
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): sgmv_fused

@@ -42,11 +42,13 @@ class DeviceWorkload:
                0xFF = bf16/f32 NaN, to prove untouched extents are never read)
     on_block:  callback(aid, layer, proj, A, B) with each uploaded float32 block
     plan_opts: plan options set on the pool before the plan is built
+    slab_margin: bytes allocated past the pool's slab (the pool sees only its
+               own bytes; reads a little past them stay inside the allocation)
     """
 
     def __init__(self, w: Workload, *, hab=None, pool_ids=None, upload=None, slab_fill=None,
                  on_block=None, threads: int = 0, max_proj: int = None, layers=None,
-                 plan_opts=None):
+                 plan_opts=None, slab_margin: int = 0):
         import torch
         if hab is None:
             import heterogeneous_adapter_batching_amd as hab
@@ -60,9 +62,10 @@ class DeviceWorkload:
         from heterogeneous_adapter_batching_amd.api import make_desc
         desc = make_desc(w.num_layers, h_in, h_out, w.r_max, w.dtype)
         slab_bytes = sum(hab.extent_bytes(desc, int(w.ranks[i])) for i in pool_ids)
-        slab = torch.empty(max(slab_bytes, 256), dtype=torch.uint8, device="cuda")
+        slab = torch.empty(max(slab_bytes, 256) + slab_margin, dtype=torch.uint8, device="cuda")
         if slab_fill is not None:
             slab.fill_(slab_fill)
+        slab = slab[:max(slab_bytes, 256)]
         self.pool = hab.Pool(w.num_layers, h_in, h_out, w.r_max, w.dtype,
                              max_slots=max(len(pool_ids), 1), slab=slab)
         for i in pool_ids:

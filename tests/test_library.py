@@ -36,12 +36,32 @@ def header_functions():
 def test_header_symbols_exported():
     names = header_functions()
     assert len(names) >= 18, names
-    lib = ctypes.CDLL(hab.LIB_PATH)
-    missing = [n for n in names if not hasattr(lib, n)]
-    assert not missing, missing
+    from heterogeneous_adapter_batching_amd import build
+    for path in (hab.LIB_PATH, build.DEBUG_LIB):
+        lib = ctypes.CDLL(path)
+        missing = [n for n in names if not hasattr(lib, n)]
+        assert not missing, (path, missing)
     # and the binding declares every one of them
     from heterogeneous_adapter_batching_amd._lib import SIGNATURES
     assert sorted(SIGNATURES) == names
+
+
+def test_debug_checks_flag():
+    """lora_debug_checks: the release build reports no checks and no errors
+    without touching a device; the debug build reports its checks (asked for
+    the flag alone, it touches no device either)."""
+    from heterogeneous_adapter_batching_amd import build
+    assert hab.debug_checks() == (False, 0)
+    assert hab.debug_checks(clear=True) == (False, 0)
+    dbg = ctypes.CDLL(build.DEBUG_LIB)
+    dbg.lora_debug_checks.argtypes = [ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]
+    en = ctypes.c_int32(-1)
+    assert dbg.lora_debug_checks(ctypes.byref(en), None, 0) == 0
+    assert en.value == 1
+    rel = hab.load()
+    en = ctypes.c_int32(-1)
+    assert rel.lora_debug_checks(ctypes.byref(en), None, 1) == 0 and en.value == 0
 
 
 def _pool(**kw):
