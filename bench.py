@@ -1010,6 +1010,7 @@ def main():
 
     # the smaller workloads, each step after a 1 GiB flush
     del graph
+    step_opts = dw.plan.opts()
     configs = {}
     if args.workload == 4 and args.configs:
         del dw, plan, plan_ws, graph_plan
@@ -1032,7 +1033,7 @@ def main():
                    "calls_per_layer": len(w.calls), "kernel_launches_per_step": launches,
                    "distinct_adapters": int(len(w.touched())), "mode": args.mode,
                    "flush_mib_between_steps": flush_mib, "flush": "read",
-                   "plan_opts": dw.plan.opts()},
+                   "plan_opts": step_opts},
         **{k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")},
         "step_ms_quantiles": quant,
         "eager_ms_per_step": round(eager_ms, 5),
