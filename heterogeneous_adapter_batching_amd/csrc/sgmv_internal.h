@@ -51,10 +51,12 @@ constexpr int kPrefillMaxSplit = 4;
 enum { kPrefillFused = 0, kPrefillShrink = 1, kPrefillExpand = 2 };
 // Shrink: workgroups aimed for per launch (by default).  Fewer, longer
 // k-chunks win over more, shorter ones here (the expand then also sums fewer
-// partials): measured on the full stack, 384 beat 1024 by 3.5% per step, and
-// 256 beat 384 by 0.5% (the o call's 6 k-chunks become 4; 128 measured the
-// same).
-constexpr int kDefaultShrinkGroups = 256;
+// partials): on the full stack 384 beat 1024 by 3.5% per step and 256 beat
+// 384 by 0.5%; over the cost sweep (the full stack with 0-128 distinct
+// adapters, and Zipf draws) 128 beat 256 by 7-8.5% for 1-8 distinct adapters
+// and 1-2% for Zipf skews of 1.1-3, was never slower, and gives the full
+// stack's calls the same k-chunks; 96, 64 and 32 lay between.
+constexpr int kDefaultShrinkGroups = 128;
 // upper limits of the launch targets a pool's plan options may set
 constexpr int kMaxLaunchTarget = 1 << 16;
 constexpr int kXcds = 8;                     // workgroup g runs on XCD g % 8

@@ -410,7 +410,7 @@ lora_status lora_plan_upload(lora_plan *pl, void *ws, uint64_t ws_bytes, int32_t
  *   prefill_groups  workgroups a prompt launch aims for: a launch of fewer
  *                   16-token tiles splits each tile's output rows over up to
  *                   4 workgroups
- * Defaults (lora_plan_opts_default): 48, 1024, 256, 256, the values measured
+ * Defaults (lora_plan_opts_default): 48, 1024, 128, 256, the values measured
  * best on MI355X for decode batches of 64-256 tokens and a 4096-token prompt
  * batch of Mistral-7B shapes. */
 typedef struct lora_plan_opts {

@@ -248,7 +248,7 @@ def test_plan_opts_defaults_and_validation():
     """lora_plan_opts: the defaults, a pool's options set and read back, and
     out-of-range values refused with LORA_EINVAL, the pool's options then
     unchanged."""
-    assert hab.plan_opts_default() == dict(long_group=48, long_batch=1024, shrink_groups=256,
+    assert hab.plan_opts_default() == dict(long_group=48, long_batch=1024, shrink_groups=128,
                                            prefill_groups=256)
     pool = _pool()
     assert pool.plan_opts() == hab.plan_opts_default()
