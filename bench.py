@@ -665,6 +665,36 @@ def other_config(ci, args, stream, flush):
     return out
 
 
+def cost_floor(args, stream):
+    """The flat part of the cost sweep: the full stack's 128 decode tokens
+    served from 1 and from 16 distinct rank-16 adapters (token t takes t mod
+    d), graph-timed back to back, beside no adapter at all (the launches and
+    the copy of base_out into y)."""
+    import torch
+    import heterogeneous_adapter_batching_amd as hab
+    from synth import default_threads, sweep_stack
+    from synth.device import DeviceWorkload
+    w = sweep_stack(16)
+    t0 = time.perf_counter()
+    dw = DeviceWorkload(w, upload=np.arange(w.pool_size), threads=default_threads(),
+                        plan_opts=plan_opts(args))
+    out = {"workload": w.name, "steps": args.steps}
+    for d in (0, 1, 16):
+        ids = np.full(w.num_tokens, -1, np.int32) if d == 0 else \
+            (np.arange(w.num_tokens) % d).astype(np.int32)
+        dw.plan = hab.Plan(dw.pool, w.num_tokens, w.seg_starts, ids)
+        dw.plan.upload(dw.max_proj)
+        out[f"distinct_{d}_ms"] = round(_time_graph(dw.run_fused, stream, args.warmup,
+                                                     args.steps), 5)
+    log(f"[bench] cost floor (0, 1, 16 distinct adapters): {out['distinct_0_ms']:.4f}, "
+        f"{out['distinct_1_ms']:.4f}, {out['distinct_16_ms']:.4f} ms per step "
+        f"({time.perf_counter() - t0:.1f} s with staging)")
+    del dw
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_ceiling(nbytes, launches, stream):
     """GB/s of a plain device copy moving `nbytes` per launch (half read,
     half written), `launches` copies back to back in a graph: the ceiling
@@ -749,6 +779,9 @@ def main():
                     help="size of the device-copy bandwidth reference (0: skip)")
     ap.add_argument("--configs", type=int, nargs="*", default=[1, 2, 3],
                     help="smaller workloads also timed (flushed) and reported under 'configs'")
+    ap.add_argument("--cost-floor", type=int, default=1,
+                    help="with the full stack, also time it from 0, 1 and 16 distinct adapters "
+                         "(the flat part of the cost sweep) under 'cost_floor' (0: skip)")
     for opt, what in (("long-group", "tokens that make a group long (the prompt kernel)"),
                       ("long-batch", "long groups' tokens a batch needs to use the prompt kernel"),
                       ("shrink-groups", "workgroups a decode shrink launch aims for"),
@@ -1020,6 +1053,7 @@ def main():
         for ci in args.configs:
             configs[f"config{ci}"] = other_config(ci, args, stream, cflush)
         del cflush
+    floor = cost_floor(args, stream) if args.workload == 4 and args.cost_floor else None
 
     m = step_metrics(w, ms)
     out = {
@@ -1046,7 +1080,7 @@ def main():
         # the same bytes per launch moved by plain copies in the same order
         "copy_step_ms": round(copy_step_ms, 5) if copy_step_ms else None,
         "frac_of_copy_step": round(copy_step_ms / ms, 4) if copy_step_ms else None,
-        "roofline": roof, "cpu_baseline": cpu, "configs": configs,
+        "roofline": roof, "cpu_baseline": cpu, "configs": configs, "cost_floor": floor,
     }
     print(json.dumps(out), flush=True)
 
