@@ -271,6 +271,23 @@ def test_plan_opts_parity(case, opts):
     check_workload(dw, tight=True, threads=4)
 
 
+@pytest.mark.parametrize("kind,dtype,opts", [
+    ("sigma-full", "bf16", dict(long_group=1, long_batch=1)),
+    ("sigma-diag", "f32", dict(long_group=1, long_batch=1, prefill_groups=1)),
+    ("sigma-full", "f32", dict(shrink_groups=4096)),
+    ("merge", "bf16", dict(long_group=1, long_batch=1)),
+    ("merge", "f32", dict(shrink_groups=7, prefill_groups=1)),
+])
+def test_plan_opts_other_plans(kind, dtype, opts):
+    """Jointly compressed and merge plans under other plan options (every
+    group through the prompt kernel, other k-chunkings and row splits): the
+    same checks as their own parity tests."""
+    if kind == "merge":
+        test_merge_parity(dtype, False, 3, plan_opts=opts)
+    else:
+        test_sigma_parity(kind.split("-")[1], dtype, False, plan_opts=opts)
+
+
 def test_two_step_path():
     """sgmv_shrink + sgmv_expand through a caller's v buffer: within the
     float32 bound of the oracle, deterministic, and bit-identical to
@@ -689,7 +706,7 @@ def _jd_check(dw):
 @pytest.mark.parametrize("kind", ["full", "diag"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("prefill", [False, True])
-def test_sigma_parity(kind, dtype, prefill):
+def test_sigma_parity(kind, dtype, prefill, plan_opts=None):
     """The three steps A, Sigma, B ("Compress then Serve", rebuttal pseudocode
     of add_lora_slice_with_sigma) against the oracle: mixed basis ranks,
     segments without a core or an adapter, decode blocks or prefill blocks;
@@ -699,9 +716,10 @@ def test_sigma_parity(kind, dtype, prefill):
             ("diag", "f32"): 4}[(kind, dtype)] + (10 if prefill else 0)
     w = jd_case(seed, kind=kind, dtype=dtype, T=1500 if prefill else 96,
                 max_seg=500 if prefill else 3)
-    log(f"[parity] {w.name} dtype {dtype} prefill {prefill}")
-    dw = DeviceWorkload(w, threads=4)
-    assert (dw.plan.stats()["max_block_tokens"] > 4) == prefill
+    log(f"[parity] {w.name} dtype {dtype} prefill {prefill} {plan_opts or ''}")
+    dw = DeviceWorkload(w, threads=4, plan_opts=plan_opts)
+    if plan_opts is None:
+        assert (dw.plan.stats()["max_block_tokens"] > 4) == prefill
     dw.zero_outputs()
     dw.run_fused()
     torch.cuda.synchronize()
@@ -766,10 +784,11 @@ def test_sigma_call_errors():
 
 
 # ----------------------------------------------------------- weighted merge ----
-def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=5):
+def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=5,
+                 plan_opts=None):
     """A pool of n_adapters (mixed ranks) and K merge slots per segment: a
     plain random batch gives the segments; each slot draws its own adapters
-    (or -1) and weights."""
+    (or -1) and weights; plan_opts are set on the pool before the plan."""
     import heterogeneous_adapter_batching_amd as hab
     w = random_case(seed, T=T, h_in=h_in, h_out=h_out, n_adapters=n_adapters,
                     r_choices=[8, 16, 32], dtype=dtype, max_seg=max_seg, has_base=True,
@@ -780,6 +799,8 @@ def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=
     seg_ad[:, 0] = w.seg_adapter                            # slot 0: the batch's own draw
     seg_w = g.uniform(-1.0, 1.5, (S, K)).astype(np.float32)
     dw = DeviceWorkload(w, upload=np.arange(n_adapters), threads=4)
+    if plan_opts:
+        dw.pool.set_plan_opts(**plan_opts)
     plan = hab.Plan.merge(dw.pool, w.num_tokens, w.seg_starts, seg_ad, seg_w).upload(1)
     return w, dw, plan, seg_ad, seg_w
 
@@ -787,7 +808,7 @@ def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("prefill", [False, True])
 @pytest.mark.parametrize("K", [3, 4])
-def test_merge_parity(dtype, prefill, K):
+def test_merge_parity(dtype, prefill, K, plan_opts=None):
     """K adapters merged per request with weights, in one pass (one shrink
     over every (token, slot) row, one expand that sums the weighted deltas
     and rounds y once), against the oracle's merge: the contract tolerance,
@@ -798,9 +819,12 @@ def test_merge_parity(dtype, prefill, K):
     seed = (31 if dtype == "bf16" else 32) + (10 if prefill else 0) + 100 * (K - 3)
     w, dw, plan, seg_ad, seg_w = _merge_setup(seed, K=K, dtype=dtype,
                                               T=1300 if prefill else 64,
-                                              max_seg=400 if prefill else 3)
-    log(f"[parity] merge {w.name} K={K} {dtype} prefill {prefill} {plan.stats()}")
-    assert (plan.stats()["max_block_tokens"] > 4) == prefill
+                                              max_seg=400 if prefill else 3,
+                                              plan_opts=plan_opts)
+    log(f"[parity] merge {w.name} K={K} {dtype} prefill {prefill} {plan.stats()} "
+        f"{plan_opts or ''}")
+    if plan_opts is None:
+        assert (plan.stats()["max_block_tokens"] > 4) == prefill
     x = dw.x[(0, "x")]
     y = torch.zeros_like(dw.y[(0, 0)])
     hab.sgmv_fused(dw.pool, plan, 0, (0,), [0], x, y, dw.base[(0, 0)])
