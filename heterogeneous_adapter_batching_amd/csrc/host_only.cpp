@@ -12,6 +12,9 @@ hipError_t launch_shrink(int, int, bool, const ShrinkArgs &, hipStream_t) {
 hipError_t launch_pack_a(int, const void *, int, int, void *, int, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t launch_pack_b(int, const void *, int, int, void *, int, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 hipError_t launch_reduce(int, const ReduceArgs &, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_prefill(int, int, int, int, int, const PrefillArgs &, int, hipStream_t) {
     return hipErrorInvalidValue;

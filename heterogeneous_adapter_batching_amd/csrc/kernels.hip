@@ -634,12 +634,14 @@ __device__ __forceinline__ void gather_finish(const ExpandArgs &a, const BlockDe
 }
 
 // Decode expand on the vector ALUs, for one wave's slice [o_lo, o_hi) of a
-// unit: lane owns rows o_lo + lane + 64 i (i < RPL) and streams the NV
-// 16-byte vectors of each B row (r_pad = nv * E values, nv <= NV), dotting
-// them with every token's v (an LDS broadcast) in float32.  Loads go out in
-// the order they are used: the v gather, B vector by vector, then y_in; so
-// the dot products of the first vectors start while the rest arrive.
-template <typename T, int NV, bool Sig, bool PRW>
+// unit (one slice of the B block layout): lane owns rows o_lo + RPL * lane +
+// i (i < RPL) and streams the NV 16-byte vectors of each B row (r_pad = nv *
+// E values, nv <= NV), dotting them with every token's v (an LDS broadcast)
+// in float32.  In the slab's B layout each (i, v) load of the wave is one
+// contiguous run.  Loads go out in the order they are used: the v gather, B
+// vector by vector, then y_in; so the dot products of the first vectors
+// start while the rest arrive.
+template <typename T, int NV, bool Sig>
 __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
                                             const int (&tr)[kValuTokens], int p, int o_lo,
                                             int o_hi, float (*vs)[LORA_MAX_RANK + 4],
@@ -668,25 +670,24 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
         y_row[t] = ok ? uint32_t((int64_t(tr[t]) * a.ldy + yoff) * sizeof(T)) : kOOB;
     }
 
-    // PR (builds for B rows of at most 2 vectors): a lane owns two adjacent
-    // rows, so y_in and y of a token move 4 bytes a lane (bf16) in one
-    // access instead of two of 2 bytes, and the kernel holds 48 VGPRs
-    // instead of 54: 1% per full-stack step.  Wider rows keep rows a wave
-    // apart (paired, their B loads would stride 128 bytes a lane; 1% slower
-    // on the multi-rank decode).
-    constexpr bool PR = PRW && RPL == 2;
-    auto row_of = [&](int i) { return PR ? o_lo + 2 * lane + i : o_lo + i * kWaveSize + lane; };
+    // PR (rows of at most 4 vectors, two rows a lane): a lane owns two
+    // adjacent rows, so y_in and y of a token move 4 bytes a lane (bf16) in
+    // one access instead of two of 2 bytes (1% per full-stack step).
+    constexpr bool PR = RPL == 2;
+    auto row_of = [&](int i) { return o_lo + RPL * lane + i; };
     VGather g;
     gather_issue(a, blk, tr, p, g);
+    // the slice's vectors run (i, v, lane): vector v of the lane's row i at
+    // ((i * nv + v) * lanes + lane) * 16 past the slice's first row
+    const int lanes = (o_hi - o_lo) / RPL;          // o_hi - o_lo is a multiple of 8
     u32x4 bv[NV][RPL];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int row = row_of(i);
-            bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
-                                              uint32_t(row) * row_bytes + v * 16));
-        }
+        for (int i = 0; i < RPL; ++i)
+            bv[v][i] = bload16(br, off_or_oob(lane < lanes && v < nv,
+                                              uint32_t(o_lo) * row_bytes +
+                                                  uint32_t(((i * nv + v) * lanes + lane) * 16)));
     float yin[RPL][NT];
     if constexpr (PR) {
         const int row = row_of(0);
@@ -877,15 +878,15 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
         return;
     }
     switch (decode_nvt(r_pad, sizeof(T))) {         // <= NVM for every class of the launch
-    case 1: return expand_valu<T, 1, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 1: return expand_valu<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
     default:
-        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig, (NVM <= 2)>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 
@@ -998,6 +999,7 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         const rsrc_t br = make_rsrc(a.slab + boff,
                                     dbg_block(a.dbg, boff, uint64_t(h_out) * row_bytes));
         const int nv = sl.r_pad / E;
+        const BLayout bl = b_layout(sl.r_pad, sizeof(T));   // the slot's B layout
         u32x4 bv[NVM][RPL];
 #pragma unroll
         for (int v = 0; v < NVM; ++v)
@@ -1005,7 +1007,7 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
             for (int i = 0; i < RPL; ++i) {
                 const int row = o_lo + i * kWaveSize + lane;
                 bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
-                                                  uint32_t(row) * row_bytes + v * 16));
+                                                  b_vec_off(bl, row, v, h_out)));
             }
         // finish the gather in the one chunk order
         f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1169,9 +1171,9 @@ __device__ __forceinline__ void prefill_rows(const PrefillArgs &a, const BlockDe
         in_line[j] = lrow[j] >= 0 ? uint32_t(int64_t(lrow[j]) * ld_in * sizeof(T)) : kOOB;
         y_line[j] = lrow[j] >= 0 ? uint32_t(int64_t(lrow[j]) * a.ldy * sizeof(T)) : kOOB;
     }
-    const uint32_t row_bytes = uint32_t(blk.r_pad) * sizeof(T);
     const int lane_tile = TPL == 1 ? 0 : q / G;
-    const uint32_t lane_col = uint32_t(TPL == 1 ? q * E : (q % G) * E) * sizeof(T);
+    const int lane_vec = TPL == 1 ? q : q % G;       // the lane's 16-byte vector of a B row
+    const BLayout bl = b_layout(blk.r_pad, sizeof(T));
     auto brow = [&](int tile, int nn) {
         return PAIR ? (tile & ~1) * kTile + 8 * (nn >> 2) + 4 * (tile & 1) + (nn & 3)
                     : tile * kTile + nn;
@@ -1225,8 +1227,7 @@ __device__ __forceinline__ void prefill_rows(const PrefillArgs &a, const BlockDe
             const int row = o0 + brow(t + lane_tile, n);
             const bool ok = i < total && row < top &&
                             (TPL > 1 || (ks < ks_n && ks * SPAN + q * E < blk.r_pad));
-            bf[l] = bload16(br, off_or_oob(ok, uint32_t(row) * row_bytes + lane_col +
-                                                   uint32_t(ks * SPAN) * sizeof(T)));
+            bf[l] = bload16(br, off_or_oob(ok, b_vec_off(bl, row, lane_vec + ks * (SPAN / E), h)));
         }
 #pragma unroll
         for (int oy = 0; oy < NY; ++oy) {
@@ -1643,6 +1644,29 @@ __global__ __launch_bounds__(256) void k_pack_a(const T *src, int rank, int h_in
     *reinterpret_cast<u32x4 *>(dst + (int64_t(kb) * r_pad + j) * SPAN + c) = v;
 }
 
+// B [h_out][rank] (row-major, device) -> the slab's B block layout (row
+// slices of permuted 16-byte vectors, b_vec_off) with zeros in the pad
+// columns; one thread per 16-byte vector, read element by element (rank
+// need not fill whole vectors).
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_b(const T *src, int rank, int h_out, T *dst,
+                                                int r_pad) {
+    constexpr int E = Elem<T>::E;
+    const BLayout bl = b_layout(r_pad, sizeof(T));
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= h_out * bl.nv) return;
+    const int o = i / bl.nv, v = i % bl.nv;
+    T e[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+        const int j = v * E + k;
+        e[k] = j < rank ? src[int64_t(o) * rank + j] : T(0);
+    }
+    u32x4 w;
+    __builtin_memcpy(&w, e, sizeof w);
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(dst) + b_vec_off(bl, o, v, h_out)) = w;
+}
+
 template <typename T>
 hipError_t shrink_dispatch(int tt, bool mp, const ShrinkArgs &a, hipStream_t s) {
     const dim3 grid(a.grid), block(kWaves * kWaveSize);
@@ -1773,6 +1797,21 @@ hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *d
     else
         hipLaunchKernelGGL(k_pack_a<float>, grid, block, 0, s, static_cast<const float *>(src),
                            rank, h_in, static_cast<float *>(dst), r_pad, h_in_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_b(int dtype, const void *src, int rank, int h_out, void *dst, int r_pad,
+                         hipStream_t s) {
+    const int es = dtype == LORA_BF16 ? 2 : 4;
+    const int vecs = h_out * (r_pad * es / 16);
+    const dim3 grid((vecs + 255) / 256), block(256);
+    if (dtype == LORA_BF16)
+        hipLaunchKernelGGL(k_pack_b<uint16_t>, grid, block, 0, s,
+                           static_cast<const uint16_t *>(src), rank, h_out,
+                           static_cast<uint16_t *>(dst), r_pad);
+    else
+        hipLaunchKernelGGL(k_pack_b<float>, grid, block, 0, s, static_cast<const float *>(src),
+                           rank, h_out, static_cast<float *>(dst), r_pad);
     return hipGetLastError();
 }
 

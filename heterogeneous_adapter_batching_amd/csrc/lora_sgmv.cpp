@@ -327,6 +327,23 @@ void pack_a_host(const uint8_t *src, int32_t rank, uint64_t h_in, uint64_t hp, u
     }
 }
 
+// B [h_out][rank] (host) -> the B block layout (lora::b_vec_off): row o's
+// elements go, 16 bytes at a time, to the positions of its vectors; pad
+// columns stay as dst holds them (zero).
+void pack_b_host(const uint8_t *src, int32_t rank, uint64_t h_out, int32_t r_pad, uint64_t es,
+                 uint8_t *dst) {
+    const lora::BLayout bl = lora::b_layout(r_pad, int(es));
+    const uint64_t per_vec = 16 / es;
+    for (uint64_t o = 0; o < h_out; ++o)
+        for (int v = 0; v < bl.nv; ++v) {
+            const uint64_t j0 = uint64_t(v) * per_vec;
+            if (j0 >= uint64_t(rank)) break;
+            const uint64_t n = std::min<uint64_t>(per_vec, uint64_t(rank) - j0);
+            std::memcpy(dst + lora::b_vec_off(bl, int(o), v, int(h_out)),
+                        src + (o * uint64_t(rank) + j0) * es, n * es);
+        }
+}
+
 }  // namespace
 
 namespace lora {
@@ -456,22 +473,16 @@ lora_status lora_pool_upload(lora_pool *p, int32_t id, int32_t layer, int32_t pr
                                 int32_t(hp), st);
     }
     if (e != hipSuccess) return hip_fail(e, "A upload");
+    // B goes in the B block layout: rows in slices of permuted 16-byte
+    // vectors (lora::b_vec_off), pad columns zero
     const uint64_t b_bytes = h_out * uint64_t(s.r_pad) * es;
-    std::vector<uint8_t> padded;   // host source with padding: widen rows on the host
-    if (s.r_pad == s.rank) {
-        e = hipMemcpyAsync(b_dst, B, b_bytes, kind, st);
-    } else if (src_on_host) {
-        padded.assign(b_bytes, 0);
-        const uint8_t *src = static_cast<const uint8_t *>(B);
-        for (uint64_t o = 0; o < h_out; ++o)
-            std::memcpy(padded.data() + o * s.r_pad * es, src + o * s.rank * es, s.rank * es);
-        e = hipMemcpyAsync(b_dst, padded.data(), b_bytes, kind, st);
+    std::vector<uint8_t> b_blk;
+    if (src_on_host) {
+        b_blk.assign(b_bytes, 0);
+        pack_b_host(static_cast<const uint8_t *>(B), s.rank, h_out, s.r_pad, es, b_blk.data());
+        e = hipMemcpyAsync(b_dst, b_blk.data(), b_bytes, kind, st);
     } else {
-        e = hipMemset2DAsync(b_dst + uint64_t(s.rank) * es, uint64_t(s.r_pad) * es, 0,
-                             uint64_t(s.r_pad - s.rank) * es, h_out, st);
-        if (e != hipSuccess) return hip_fail(e, "B pad columns");
-        e = hipMemcpy2DAsync(b_dst, uint64_t(s.r_pad) * es, B, uint64_t(s.rank) * es,
-                             uint64_t(s.rank) * es, h_out, kind, st);
+        e = lora::launch_pack_b(p->d.dtype, B, s.rank, int32_t(h_out), b_dst, s.r_pad, st);
     }
     if (e != hipSuccess) return hip_fail(e, "B upload");
     if (src_on_host) {
@@ -547,9 +558,8 @@ lora_status lora_pack_adapter(const lora_pool_desc *d, int32_t rank, const void 
             uint8_t *b_dst = a_dst + uint64_t(r_pad) * es * hp;
             pack_a_host(static_cast<const uint8_t *>(A[i]) + uint64_t(l) * rank * h_in * es,
                         rank, h_in, hp, span, r_pad, es, a_dst);
-            const uint8_t *b = static_cast<const uint8_t *>(B[i]) + uint64_t(l) * h_out * rank * es;
-            for (uint64_t o = 0; o < h_out; ++o)
-                std::memcpy(b_dst + o * r_pad * es, b + o * rank * es, rank * es);
+            pack_b_host(static_cast<const uint8_t *>(B[i]) + uint64_t(l) * h_out * rank * es,
+                        rank, h_out, r_pad, es, b_dst);
             pre += hp + h_out;
         }
     }

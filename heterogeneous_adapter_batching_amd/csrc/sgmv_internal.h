@@ -322,6 +322,31 @@ constexpr bool decode_rows_agree() {
 }
 static_assert(decode_rows_agree(), "decode unit rows are kWaves wave slices");
 
+// Layout of a B block in the slab: h_out rows of r_pad elements, each row nv
+// = r_pad * esize / 16 vectors of 16 bytes, permuted within slices of the
+// decode expand's wave rows (64 * rpl rows, rpl = decode_rpl of the row's
+// vector count; the last slice shorter).  In a slice of n rows the vectors
+// run (i, v, l) with i < rpl, v < nv and l < n / rpl, vector v of row
+// base + rpl * l + i at position (i * nv + v) * (n / rpl) + l: lane l of a
+// wave holds rows base + rpl * l + i, so each of the wave's B loads (one i,
+// one v) reads one contiguous run of n / rpl vectors.  The block's size is
+// that of [h_out][r_pad].  sh = log2 rpl.
+struct BLayout {
+    int nv;
+    int sh;
+};
+constexpr BLayout b_layout(int r_pad, int esize) {
+    return BLayout{r_pad * esize / 16, decode_rpl(decode_nvt(r_pad, esize)) == 2 ? 1 : 0};
+}
+// byte offset of vector v of row o (o < h_out, v < nv) in its B block
+constexpr uint32_t b_vec_off(BLayout b, int o, int v, int h_out) {
+    const int base = o >> (6 + b.sh) << (6 + b.sh);
+    const int n = h_out - base < (64 << b.sh) ? h_out - base : (64 << b.sh);
+    const int q = o - base;
+    return (uint32_t(base) * uint32_t(b.nv) +
+            uint32_t(((q & b.sh) * b.nv + v) * (n >> b.sh) + (q >> b.sh))) * 16u;
+}
+
 
 // Sets the thread's last-error message (lora_last_error) and returns st.
 lora_status set_error(lora_status st, const char *msg);
@@ -335,6 +360,10 @@ hipError_t launch_shrink(int dtype, int tt, bool mp, const ShrinkArgs &a, hipStr
 // A [rank][h_in] row-major (device) -> K-blocked [h_in_pad / span][r_pad][span]
 hipError_t launch_pack_a(int dtype, const void *src, int rank, int h_in, void *dst, int r_pad,
                          int h_in_pad, hipStream_t s);
+// B [h_out][rank] row-major (device) -> the B block layout
+// (b_vec_off), pad columns zero
+hipError_t launch_pack_b(int dtype, const void *src, int rank, int h_out, void *dst, int r_pad,
+                         hipStream_t s);
 hipError_t launch_reduce(int tt, const ReduceArgs &a, hipStream_t s);
 // prefill: mode kPrefillFused / kPrefillShrink / kPrefillExpand; np the
 // call's projections (1..3); rtm the launch's largest rank tiles (1, 2 or 4);

@@ -128,8 +128,14 @@ uint64_t lora_pool_extent_bytes(const lora_pool_desc *d, int32_t rank);
  * the B block, layers outermost.  A is stored K-blocked,
  * [h_in_pad_p / S][r_pad][S] with S = 32 (bf16) or 16 (f32) and h_in_pad_p =
  * h_in_p rounded up to S, so that 16 rank rows x S columns are one
- * contiguous run; B is [h_out_p][r_pad] row-major.  Pad rows and columns are
- * zero.  The slab is not touched here and is not freed by lora_pool_destroy.
+ * contiguous run.  B holds h_out_p rows of r_pad elements (nv = r_pad * e / 16
+ * vectors of 16 bytes a row, e the element size) in row slices of 64 * rpl
+ * rows, rpl = 1 when nv rounded up to a power of two is 8 or more, else 2
+ * (the last slice shorter): in a slice of n rows from row `base`, vector v of
+ * row base + rpl * l + i (i < rpl, l < n / rpl) is the slice's 16-byte vector
+ * number (i * nv + v) * (n / rpl) + l, so that the rows a 64-lane wave
+ * streams arrive as whole contiguous runs; the block is h_out_p * r_pad
+ * elements, as row-major would be.  Pad rows and columns are zero.  The slab is not touched here and is not freed by lora_pool_destroy.
  * Errors: LORA_EINVAL (null pointer, bad descriptor or slab alignment),
  * LORA_EDTYPE. */
 lora_status lora_pool_create(lora_pool **out, const lora_pool_desc *d,

@@ -662,8 +662,10 @@ def test_plan_rebuild_parity():
 
 
 def test_register_from_device_matches_host():
-    """lora_pool_register from device tensors (the K-blocking pack kernel) gives
-    the same pool, hence the same output bits, as uploads from host arrays."""
+    """lora_pool_register from device tensors (the pack kernels: A K-blocked,
+    B in row slices of permuted vectors) writes the same extent bytes as
+    uploads from host arrays, hence the same output bits; ranks of 1, 2, 5
+    and 8 vectors a bf16 row, h_out 96 (a ragged B slice either way)."""
     import heterogeneous_adapter_batching_amd as hab
     from synth.device import to_device, host_weights
     for dtype, h_in in (("bf16", 200), ("f32", 72), ("bf16", 4096)):
@@ -679,6 +681,14 @@ def test_register_from_device_matches_host():
             A, B = w.adapter_block(a, 0, 0)
             pool2.register(a, int(w.ranks[a]), float(w.scales[a]),
                            [to_device(A, dtype)[None]], [to_device(B, dtype)[None]])
+        es = 2 if dtype == "bf16" else 4
+        span = 32 if dtype == "bf16" else 16
+        for a in w.touched():
+            q1, q2 = dw.pool.query(int(a)), pool2.query(int(a))
+            n = q1["r_pad"] * es * (-(-h_in // span) * span + 96)   # less the 256-byte tail
+            s1 = dw.pool.slab[q1["offset"]:q1["offset"] + n].cpu().numpy()
+            s2 = pool2.slab[q2["offset"]:q2["offset"] + n].cpu().numpy()
+            assert np.array_equal(s1, s2), (dtype, int(a))
         plan2 = hab.Plan(pool2, w.num_tokens, w.seg_starts, w.seg_adapter).upload(1)
         y2 = torch.zeros_like(dw.y[(0, 0)])
         hab.sgmv_fused(pool2, plan2, 0, (0,), (0,), dw.x[(0, "x")], y2)

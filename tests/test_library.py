@@ -322,10 +322,29 @@ def test_plan_for_workloads():
         assert st["active_tokens"] == w.num_tokens
 
 
+def _b_block(b, dtype):
+    """B [h_out][r_pad] (pads included) in the header's B layout: rows in
+    slices of 64 * rpl, each slice's 16-byte vectors ordered (i, v, l) for
+    row base + rpl * l + i, vector v; built by index arithmetic on a
+    [slice rows][vectors][elements] view."""
+    h_out, r_pad = b.shape
+    per = 8 if dtype == "bf16" else 4                    # elements of a 16-byte vector
+    nv = r_pad // per
+    nvt = 1 << (nv - 1).bit_length()
+    rpl = 1 if nvt >= 8 else 2
+    out = []
+    for base in range(0, h_out, 64 * rpl):
+        n = min(64 * rpl, h_out - base)
+        sl = b[base:base + n].reshape(n // rpl, rpl, nv, per)   # [l][i][v][e]
+        out.append(sl.transpose(1, 2, 0, 3).ravel())            # [i][v][l][e]
+    return np.concatenate(out)
+
+
 def _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype):
     """The extent image as the header lays it out, built with numpy: per layer
     (outermost) and projection, A K-blocked [h_in_pad / span][r_pad][span],
-    then B [h_out][r_pad]; pads zero; the whole rounded up to 256 bytes."""
+    then the B block (_b_block); pads zero; the whole rounded up to 256
+    bytes."""
     g = np.random.default_rng(rank * 7 + len(h_in))
     npdt = np.uint16 if dtype == "bf16" else np.float32
     A = [g.integers(1, 60000, (L, rank, hi)).astype(npdt) if dtype == "bf16"
@@ -341,7 +360,7 @@ def _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype):
             parts.append(a.reshape(r_pad, hp // span, span).transpose(1, 0, 2).ravel())
             b = np.zeros((ho, r_pad), npdt)
             b[:, :rank] = B[p][l]
-            parts.append(b.ravel())
+            parts.append(_b_block(b, dtype))
     raw = np.concatenate(parts).view(np.uint8)
     img = np.zeros(-(-raw.size // 256) * 256, np.uint8)
     img[:raw.size] = raw
@@ -349,12 +368,15 @@ def _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype):
 
 
 @pytest.mark.parametrize("dtype,rank,granule", [("bf16", 5, 8), ("bf16", 16, 16),
+                                                 ("bf16", 27, 8), ("bf16", 64, 8),
                                                  ("f32", 13, 8), ("f32", 32, 8)])
 def test_pack_adapter_layout(dtype, rank, granule):
     """lora_pack_adapter writes the extent layout the header states, byte for
-    byte, with ragged h_in (not a multiple of the K-block) and padded ranks."""
-    h_in, h_out, L = [40, 96, 24], [24, 8, 64], 3
-    desc = make_desc(L, h_in, h_out, 32, dtype, rank_granule=granule)
+    byte, with ragged h_in (not a multiple of the K-block), padded ranks and
+    B blocks of one, several and ragged row slices (rows of 1 to 8 vectors:
+    two rows a lane and one)."""
+    h_in, h_out, L = [40, 96, 24], [24, 8, 328], 3
+    desc = make_desc(L, h_in, h_out, 64, dtype, rank_granule=granule)
     r_pad = -(-rank // granule) * granule
     span = 32 if dtype == "bf16" else 16
     A, B, ref = _pack_reference(L, h_in, h_out, rank, r_pad, span, dtype)
