@@ -49,11 +49,17 @@ template <> struct Elem<float> { static constexpr int E = 4; };
 // Buffer resources: raw (stride 0) with the byte size as the range.
 constexpr uint32_t kOOB = 0x80000000u;        // offset of a masked lane: out of range
 constexpr int kRsrcWord3 = 0x00020000;
-// Non-temporal loads (early eviction from L2) for the shrink's A only.  The
-// expands load B with the default policy: the blocks of one adapter read the
-// same B rows at about the same time on one XCD, and keeping the lines in L2
-// measured 3.8% faster per decode step (2% per prefill step) than streaming
-// them; for A the default policy was about 3% slower.
+// Non-temporal loads (early eviction from L2) for the shrink's A and the
+// decode expand's B and y_in: each line is read whole by one instruction (the
+// K-blocked A, the B block's row slices) and once; streaming B measured 2.7%
+// faster per full-stack step and 5% on the multi-rank decode than the default
+// policy, y_in 0.7% more on the full stack.  The shrink's partial sums keep
+// the default policy (each is read by every unit of its block: 4.8% slower
+// streamed).
+// (While B rows were read 16 bytes a lane across 8 instructions the default
+// policy was the faster one: the lines had to stay in L2 between the
+// instructions.)  The prompt kernel reads B with the default policy: every
+// token tile re-reads it from L2.
 constexpr int kNT = 2;
 // Outputs are stored at device scope (`sc1`, written through the L2): no
 // dirty output lines are left for the kernel boundary to write back, which
@@ -484,8 +490,9 @@ template <> struct Out4<float> {
 // One output element: bf16 (2 bytes) or float32 (4 bytes).
 template <typename T> struct Out1;
 template <> struct Out1<uint16_t> {
+    template <int AUX = 0>
     static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
-        return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, 0))
+        return __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, AUX))
                                << 16);
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
@@ -494,8 +501,9 @@ template <> struct Out1<uint16_t> {
     }
 };
 template <> struct Out1<float> {
+    template <int AUX = 0>
     static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, AUX));
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, float v) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, int(off), 0, kOut);
@@ -685,9 +693,9 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
-            bv[v][i] = bload16(br, off_or_oob(lane < lanes && v < nv,
-                                              uint32_t(o_lo) * row_bytes +
-                                                  uint32_t(((i * nv + v) * lanes + lane) * 16)));
+            bv[v][i] = bload16_nt(br, off_or_oob(lane < lanes && v < nv,
+                                                 uint32_t(o_lo) * row_bytes +
+                                                     uint32_t(((i * nv + v) * lanes + lane) * 16)));
     float yin[RPL][NT];
     if constexpr (PR) {
         const int row = row_of(0);
@@ -696,11 +704,11 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
         for (int t = 0; t < NT; ++t) {
             const uint32_t off = rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB;
             if constexpr (sizeof(T) == 2) {
-                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(inr, int(off), 0, 0);
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(inr, int(off), 0, kNT);
                 yin[0][t] = bf16_lo(w);
                 yin[1][t] = bf16_hi(w);
             } else {
-                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(inr, int(off), 0, 0);
+                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(inr, int(off), 0, kNT);
                 yin[0][t] = __uint_as_float(w[0]);
                 yin[1][t] = __uint_as_float(w[1]);
             }
@@ -712,7 +720,8 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
             const bool rok = row < o_hi;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                yin[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+                yin[i][t] =
+                    Out1<T>::template load<kNT>(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
         }
     }
     gather_finish(a, blk, p, g, vs, ways);
