@@ -54,17 +54,17 @@ def algorithmic(w, layers=None):
     (base_out or y) read once."""
     es = 2 if w.dtype == "bf16" else 4
     layers = range(w.num_layers) if layers is None else layers
-    tok = w.token_adapter()
+    slots = w.token_slots()                          # [T][K]: a merge's K adapters a token
     touched = w.touched()
-    act = int((tok >= 0).sum())
+    act = int((slots >= 0).any(axis=1).sum())
     per_layer_adapter = sum(int(w.ranks[a]) * (p.h_in + p.h_out) for a in touched
                             for p in w.projs) * es
     if w.sigma_kind:
         per_layer_adapter += _distinct_cores(w) * len(w.projs) * _core_elems(w) * 4
     per_layer_x = sum(w.num_tokens * w.x_width(k) for k in w.x_keys()) * es
     per_layer_y = sum(w.num_tokens * p.h_out for p in w.projs) * es * 2
-    flops = sum(2 * int(w.ranks[tok[t]]) * (p.h_in + p.h_out) for t in range(w.num_tokens)
-                if tok[t] >= 0 for p in w.projs)
+    flops = sum(2 * int(w.ranks[a]) * (p.h_in + p.h_out) for a in slots.ravel() if a >= 0
+                for p in w.projs)
     n = len(list(layers))
     return {"adapter": per_layer_adapter * n, "x": per_layer_x * n, "y": per_layer_y * n,
             "bytes": (per_layer_adapter + per_layer_x + per_layer_y) * n, "flops": flops * n,
@@ -75,7 +75,7 @@ def kernel_bytes(w, call, kind):
     """Algorithmic bytes of one shrink or expand launch for one call."""
     es = 2 if w.dtype == "bf16" else 4
     touched = w.touched()
-    act = int((w.token_adapter() >= 0).sum())
+    act = int((w.token_slots() >= 0).any(axis=1).sum())
     r_sum = sum(int(w.ranks[a]) for a in touched)
     # the float32 intermediate is not counted: it passes between the two
     # kernels as partial sums, which are not algorithmic bytes
@@ -127,6 +127,9 @@ def cpu_baseline(w, blocks, layers, threads, min_seconds):
             if cores is not None:
                 oracle.lora_delta_sigma(x, w.seg_starts, w.seg_adapter, w.seg_sigma, adapters,
                                         cores, w.sigma_kind, y_in, threads=threads)
+            elif w.merge_ids is not None:
+                oracle.lora_delta_merge(x, w.seg_starts, w.merge_ids, w.merge_w, adapters, y_in,
+                                        threads=threads)
             else:
                 oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in,
                                   threads=threads)
@@ -141,6 +144,9 @@ def cpu_baseline(w, blocks, layers, threads, min_seconds):
         if cores is not None:
             oracle.lora_delta_sigma(x, w.seg_starts, w.seg_adapter, w.seg_sigma, adapters,
                                     cores, w.sigma_kind, y_in, threads=1)
+        elif w.merge_ids is not None:
+            oracle.lora_delta_merge(x, w.seg_starts, w.merge_ids, w.merge_w, adapters, y_in,
+                                    threads=1)
         else:
             oracle.lora_delta(x, w.seg_starts, w.seg_adapter, adapters, y_in, threads=1)
         t1 += time.perf_counter() - t0
@@ -763,7 +769,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4,
                     help="0..4 (default 4: the full stack); 5, 6: the full stack served from "
-                         "jointly compressed adapters with full / diagonal cores")
+                         "jointly compressed adapters with full / diagonal cores; 7: the full "
+                         "stack with each request merging 2 adapters")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-layers", type=int, default=-1,
                     help="layers of the CPU-oracle sample (-1: all, 0: skip)")
@@ -821,6 +828,9 @@ def main():
     if args.workload in (5, 6):
         from synth import jd_full_stack
         w = jd_full_stack("full" if args.workload == 5 else "diag")
+    elif args.workload == 7:
+        from synth import merge_full_stack
+        w = merge_full_stack(2)
     else:
         w = config(args.workload)
     threads = min(16, os.cpu_count() or 1)
@@ -873,45 +883,47 @@ def main():
     # Per-batch planning on the measured path: a serving loop plans every
     # step (the batch changes).  The host cost of rebuild + upload, and an
     # eager step that plans its batch first, alternating two batches.
-    graph_plan = dw.plan
-    plan, plan_ws, plan_ids, plan_us = plan_cost(dw, stream)
-    log(f"[bench] plan rebuild + upload: {plan_us:.1f} us on the host")
-    # three timed runs of n_rb re-planned steps, the median reported; the
-    # garbage collector is held off meanwhile, as the host enqueues the
-    # step's launches from Python
-    n_rb = max(10, args.steps // 2)
-    runs = []
-    with torch.cuda.stream(stream):
-        for i in range(3):   # untimed: the first re-planned steps of the process
-            plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
-                dw.max_proj, ws=plan_ws, stream=stream)
-            dw.run_fused(stream=stream)
+    plan_us = rebuild_ms = None
+    if w.merge_ids is None:             # a merge plan is built, not rebuilt in place
+        graph_plan = dw.plan
+        plan, plan_ws, plan_ids, plan_us = plan_cost(dw, stream)
+        log(f"[bench] plan rebuild + upload: {plan_us:.1f} us on the host")
+        # three timed runs of n_rb re-planned steps, the median reported; the
+        # garbage collector is held off meanwhile, as the host enqueues the
+        # step's launches from Python
+        n_rb = max(10, args.steps // 2)
+        runs = []
+        with torch.cuda.stream(stream):
+            for i in range(3):   # untimed: the first re-planned steps of the process
+                plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
+                    dw.max_proj, ws=plan_ws, stream=stream)
+                dw.run_fused(stream=stream)
+            torch.cuda.synchronize()
+            gc_was = gc.isenabled()
+            gc.disable()
+            try:
+                for _ in range(3):
+                    e4, e5 = (torch.cuda.Event(enable_timing=True),
+                              torch.cuda.Event(enable_timing=True))
+                    t_rb = time.perf_counter()
+                    e4.record(stream)
+                    for i in range(n_rb):
+                        plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
+                            dw.max_proj, ws=plan_ws, stream=stream)
+                        dw.run_fused(stream=stream)
+                    e5.record(stream)
+                    torch.cuda.synchronize()
+                    runs.append((e4.elapsed_time(e5) / n_rb,
+                                 (time.perf_counter() - t_rb) * 1e3 / n_rb))
+            finally:
+                if gc_was:
+                    gc.enable()
+        rebuild_ms, t_rb = sorted(runs)[1]
+        log(f"[bench] eager step planning its batch first: {rebuild_ms:.4f} ms "
+            f"(host {t_rb:.4f} ms per step)")
+        plan.rebuild(w.num_tokens, w.seg_starts, w.seg_adapter).upload(dw.max_proj, ws=plan_ws,
+                                                                       stream=stream)
         torch.cuda.synchronize()
-        gc_was = gc.isenabled()
-        gc.disable()
-        try:
-            for _ in range(3):
-                e4, e5 = (torch.cuda.Event(enable_timing=True),
-                          torch.cuda.Event(enable_timing=True))
-                t_rb = time.perf_counter()
-                e4.record(stream)
-                for i in range(n_rb):
-                    plan.rebuild(w.num_tokens, w.seg_starts, plan_ids[i % 2]).upload(
-                        dw.max_proj, ws=plan_ws, stream=stream)
-                    dw.run_fused(stream=stream)
-                e5.record(stream)
-                torch.cuda.synchronize()
-                runs.append((e4.elapsed_time(e5) / n_rb,
-                             (time.perf_counter() - t_rb) * 1e3 / n_rb))
-        finally:
-            if gc_was:
-                gc.enable()
-    rebuild_ms, t_rb = sorted(runs)[1]
-    log(f"[bench] eager step planning its batch first: {rebuild_ms:.4f} ms "
-        f"(host {t_rb:.4f} ms per step)")
-    plan.rebuild(w.num_tokens, w.seg_starts, w.seg_adapter).upload(dw.max_proj, ws=plan_ws,
-                                                                   stream=stream)
-    torch.cuda.synchronize()
 
     # Per-kernel durations, launched back to back (a full queue, as in the
     # step), between two events on the launch stream.  Decode: the step's
@@ -987,7 +999,8 @@ def main():
         dom, kname = "prefill", "k_prefill"
     else:
         dom = "expand" if kern["expand"]["avg_us"] >= kern["shrink"]["avg_us"] else "shrink"
-        kname = {"shrink": "k_shrink", "expand": "k_expand_decode"}[dom]
+        kname = {"shrink": "k_shrink",
+                 "expand": "k_expand_merge" if w.merge_ids is not None else "k_expand_decode"}[dom]
     traffic = traffic_from_profile(kname, w.name)
     roof = {"bound": "hbm", "achieved": round(kern[dom]["gbs"], 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
@@ -1073,8 +1086,8 @@ def main():
         "eager_ms_per_step": round(eager_ms, 5),
         # a serving loop plans each batch: host microseconds of rebuild +
         # upload, and the eager step that does so first
-        "plan_us": round(plan_us, 2),
-        "eager_replan_ms_per_step": round(rebuild_ms, 5),
+        "plan_us": None if plan_us is None else round(plan_us, 2),
+        "eager_replan_ms_per_step": None if rebuild_ms is None else round(rebuild_ms, 5),
         "kernels": {k: {kk: round(vv, 3) for kk, vv in d.items()} for k, d in kern.items()},
         "copy_gbs": round(copy_gbs, 1) if copy_gbs else None,
         # the same bytes per launch moved by plain copies in the same order

@@ -938,7 +938,11 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         run += cnt[i];
     }
     const int slice = rem - first;
-    MergeBlock mb = load_invariant(a.mblocks + b);
+    // the block's head (token rows and counts) as a private copy; the slot
+    // entries are read from the plan at each slot (a private copy of the
+    // whole block, indexed by the slot, would live in scratch memory)
+    const MergeBlock *mbp = a.mblocks + b;
+    MergeHead mb = load_invariant(reinterpret_cast<const MergeHead *>(mbp));
     if constexpr (kDebug) {          // token rows inside the batch, at most 4 of them
         mb.n_tok = min(max(mb.n_tok, 0), kValuTokens);
 #pragma unroll
@@ -979,7 +983,7 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxMerge; ++k) {
         if (k >= mb.nslots) break;                   // wave-uniform
-        const MergeSlot sl = mb.slot[k];
+        const MergeSlot sl = load_invariant(&mbp->slot[k]);
         if (sl.r_pad == 0) continue;                 // an empty slot: wave-uniform
         // the v gather: thread (entry e, way kk), entry = 4 ranks of a token
         const int quads = sl.r_pad / 4;
@@ -990,10 +994,11 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         const int j = on ? (e - ti * quads) * 4 : 0;
         // the row's place in the partials, by selects (an indexed private
         // array would be placed in memory)
-        const int rt = ti == 0 ? mb.rt[k][0] : ti == 1 ? mb.rt[k][1] : ti == 2 ? mb.rt[k][2]
-                                                                                : mb.rt[k][3];
-        const int ps = ti == 0 ? mb.ps[k][0] : ti == 1 ? mb.ps[k][1] : ti == 2 ? mb.ps[k][2]
-                                                                                : mb.ps[k][3];
+        static_assert(kValuTokens == 4, "a slot's partial places load as one int4 each");
+        const int4 rt4 = load_invariant(reinterpret_cast<const int4 *>(mbp->rt[k]));
+        const int4 ps4 = load_invariant(reinterpret_cast<const int4 *>(mbp->ps[k]));
+        const int rt = ti == 0 ? rt4.x : ti == 1 ? rt4.y : ti == 2 ? rt4.z : rt4.w;
+        const int ps = ti == 0 ? ps4.x : ti == 1 ? ps4.y : ti == 2 ? ps4.z : ps4.w;
         const uint32_t off = on ? partial_off(rt, j, ps, p, a.nproj, a.c0, a.ptt) : 0u;
         u32x4 part[4];
 #pragma unroll

@@ -2,6 +2,7 @@
 // gfx950 kernels.  Not installed; the public interface is include/lora_sgmv.h.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -268,6 +269,16 @@ struct MergeBlock {
     int32_t ps[kMaxMerge][kValuTokens];
 };
 static_assert(sizeof(MergeBlock) == 224, "MergeBlock is 224 bytes");
+// the leading fields of a MergeBlock, which the merge expand copies whole
+struct MergeHead {
+    int32_t tok[kValuTokens];
+    int32_t n_tok;
+    int32_t nslots;
+    int32_t pad[2];
+};
+static_assert(sizeof(MergeHead) == offsetof(MergeBlock, slot) &&
+                  offsetof(MergeHead, nslots) == offsetof(MergeBlock, nslots),
+              "MergeHead is the head of MergeBlock");
 
 struct MergeArgs {
     const uint8_t *slab;

@@ -91,8 +91,12 @@ class DeviceWorkload:
         self.max_proj = max_proj or max(len(c) for c in self.calls)
         if plan_opts:
             self.pool.set_plan_opts(**plan_opts)
-        self.plan = hab.Plan(self.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
-                             seg_sigma=w.seg_sigma if w.sigma_kind else None)
+        if w.merge_ids is not None:
+            self.plan = hab.Plan.merge(self.pool, w.num_tokens, w.seg_starts, w.merge_ids,
+                                       w.merge_w)
+        else:
+            self.plan = hab.Plan(self.pool, w.num_tokens, w.seg_starts, w.seg_adapter,
+                                 seg_sigma=w.seg_sigma if w.sigma_kind else None)
         self.plan.upload(self.max_proj)
         # cores of jointly compressed adapters: [n][layers][proj][r_max]([r_max])
         self.sigma = None

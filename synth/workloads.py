@@ -98,6 +98,10 @@ class Workload:
     seg_sigma: np.ndarray = None
     n_cores: int = 0
     sigma_kind: str = None
+    # Weighted merging: segment s merges the adapters merge_ids[s] (K slots,
+    # -1: an empty slot) with weights merge_w[s]; seg_adapter is then slot 0.
+    merge_ids: np.ndarray = None
+    merge_w: np.ndarray = None
 
     # ---- derived facts about the draw (pure bookkeeping) ----
     @property
@@ -112,14 +116,26 @@ class Workload:
         return ids
 
     def touched(self) -> np.ndarray:
-        """Distinct adapter ids the batch uses, in first-appearance order."""
+        """Distinct adapter ids the batch uses (every merge slot included), in
+        first-appearance order."""
         out, seen = [], set()
         for s in range(self.num_segs):
-            a = int(self.seg_adapter[s])
-            if a >= 0 and self.seg_starts[s + 1] > self.seg_starts[s] and a not in seen:
-                seen.add(a)
-                out.append(a)
+            slots = self.merge_ids[s] if self.merge_ids is not None else (self.seg_adapter[s],)
+            for a in slots:
+                a = int(a)
+                if a >= 0 and self.seg_starts[s + 1] > self.seg_starts[s] and a not in seen:
+                    seen.add(a)
+                    out.append(a)
         return np.asarray(out, dtype=np.int32)
+
+    def token_slots(self) -> np.ndarray:
+        """Adapter ids of every token row's slots, [T][K] (K = 1 without
+        merging; -1: none)."""
+        ids = self.merge_ids if self.merge_ids is not None else self.seg_adapter[:, None]
+        out = np.full((self.num_tokens, ids.shape[1]), -1, dtype=np.int32)
+        for s in range(self.num_segs):
+            out[self.seg_starts[s]:self.seg_starts[s + 1]] = ids[s]
+        return out
 
     def x_keys(self) -> list:
         keys = []
@@ -285,6 +301,33 @@ def config4() -> Workload:
         scales=np.full(1000, 2.0, np.float32), has_base=True, r_max=16,
         description="32 layers x {q,k,v,o,gate,up,down}; T=S=128; pool 1000 r=16; "
                     "Zipf(1.1) popularity; y = base_out + delta")
+
+
+def merge_full_stack(K: int = 2) -> Workload:
+    """The full stack with every decode request merging K adapters: slot 0
+    is the plain full stack's Zipf(1.1) draw, slots 1..K-1 independent draws
+    of the same law, weights U(0.2, 1.0) per (request, slot)."""
+    seed = 7
+    w = config4()
+    S = w.num_segs
+    ids = np.empty((S, K), np.int32)
+    ids[:, 0] = w.seg_adapter
+    p = zipf_probs(1000, 1.1)
+    for k in range(1, K):
+        g = _rng(seed, _TAG_MAP, k)
+        for s in range(S):                  # K distinct adapters a request
+            a = int(g.choice(1000, p=p))
+            while a in ids[s, :k]:
+                a = int(g.choice(1000, p=p))
+            ids[s, k] = a
+    wts = (_rng(seed, _TAG_MAP, 100).random((S, K), dtype=np.float32) * np.float32(0.8) +
+           np.float32(0.2)).astype(np.float32)
+    w.name = f"full_stack_merge{K}_bf16"
+    w.merge_ids, w.merge_w = ids, wts
+    w.description = (f"32 layers x {{q,k,v,o,gate,up,down}}; T=S=128; pool 1000 r=16; "
+                     f"each request merges {K} adapters (Zipf(1.1) draws, weights "
+                     "U(0.2, 1)); y = base_out + sum_k w_k delta_k")
+    return w
 
 
 def sweep_stack(n_adapters: int = 128) -> Workload:

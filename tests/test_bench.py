@@ -39,6 +39,28 @@ def test_full_stack_algorithmic_bytes():
     assert alg["flops"] == flops
 
 
+def test_merge_stack_algorithmic_bytes():
+    """The merged full stack (2 adapters a request): adapter bytes over the
+    distinct adapters of both slots, activations once (every token has an
+    adapter), y read and written once, FLOPs for both slots of every token;
+    the two slots of a request name different adapters."""
+    from synth import merge_full_stack
+    w = merge_full_stack(2)
+    assert w.merge_ids.shape == (128, 2) and (w.merge_ids[:, 0] != w.merge_ids[:, 1]).all()
+    assert (w.merge_ids[:, 0] == config(4).seg_adapter).all()
+    assert ((w.merge_w >= 0.2) & (w.merge_w < 1.0)).all()
+    alg = bench.algorithmic(w)
+    distinct = len({int(a) for a in w.merge_ids.ravel()})
+    per_adapter = 83_886_080
+    x = 32 * 128 * (4096 + 4096 + 4096 + 14336) * 2
+    y = 32 * 128 * sum(p.h_out for p in w.projs) * 2 * 2
+    assert alg["adapter"] == distinct * per_adapter
+    assert alg["bytes"] == distinct * per_adapter + x + y
+    assert alg["flops"] == 2 * 32 * 128 * sum(2 * 16 * (p.h_in + p.h_out) for p in w.projs)
+    per_layer = sum(bench.kernel_bytes(w, c, k) for c in w.calls for k in ("shrink", "expand"))
+    assert np.isclose(per_layer, alg["bytes"] / w.num_layers)
+
+
 def test_kernel_bytes_sum_to_the_step():
     """Per-launch bytes of the shrink and expand over one layer's calls add up
     to the step's algorithmic bytes per layer exactly (the float32

@@ -143,6 +143,41 @@ def test_full_stack_parity():
     log(f"[parity] full stack worst err/tol {worst:.3f}")
 
 
+def test_merge_full_stack_parity():
+    """The full stack with every request merging 2 adapters (the merged
+    workload the benchmark times: one shrink over every (token, slot) row and
+    one merge expand per call), every output of the 32 layers x 7
+    projections against the oracle's merge."""
+    from synth import merge_full_stack
+    w = merge_full_stack(2)
+    log("[parity] merged full stack (2 adapters a request)")
+    refs, pending = {}, {}
+    touched = w.touched()
+
+    def on_block(aid, l, p, a, b):
+        pending.setdefault((l, p), {})[aid] = (a, b, float(w.scales[aid]))
+        if len(pending[(l, p)]) == len(touched):
+            pr = w.projs[p]
+            refs[(l, p)] = oracle.lora_delta_merge(w.activation(l, pr.x_key), w.seg_starts,
+                                                   w.merge_ids, w.merge_w, pending.pop((l, p)),
+                                                   w.base_out(l, p), threads=16)
+
+    dw = DeviceWorkload(w, on_block=on_block)
+    assert dw.plan.stats()["max_block_tokens"] <= 4
+    dw.run_fused()
+    torch.cuda.synchronize()
+    worst = 0.0
+    for (l, p), ref in refs.items():
+        got = dw.output(l, p)
+        err, tol = contract_check(got, ref, f"merged layer {l} proj {w.projs[p].name}")
+        d_ref = ref - w.base_out(l, p)
+        lim = 1e-2 * np.abs(d_ref).max() + 1e-3 + 2.0 ** -8 * np.abs(ref)
+        assert np.all(np.abs(got - ref) <= lim), f"delta check layer {l} proj {p}"
+        worst = max(worst, err / tol)
+    assert len(refs) == 32 * 7
+    log(f"[parity] merged full stack worst err/tol {worst:.3f}")
+
+
 # ---------------------------------------------------------- random cases ----
 def multi_proj_case(seed, dtype="bf16", has_base=False, T=None, r_max=64):
     g = np.random.default_rng(seed)
