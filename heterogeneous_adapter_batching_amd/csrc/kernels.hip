@@ -902,18 +902,33 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
 // Merge expand: y = y_in + sum_k (w_k s_k) B_k v_k for the tokens of a merge
 // block (at most kValuTokens tokens of one segment, so the same slot
 // adapters), slot by slot in order, in float32, rounded once.  A unit is
-// (block, projection, kWaves wave slices of rows) as in the decode expand;
-// lane owns rows o_lo + lane + 64 i (i < RPL).  For each slot the v of the
-// block's (token, slot) rows is gathered into LDS from the shrink's partials
-// (the one chunk order: thread (entry, way) sums one way, the ways are added
-// in order), the slot adapter's B rows stream in, and each lane adds the
-// slot's scaled dot products to its running outputs, which start at y_in.
+// (block, projection, kWaves wave slices of rows) as in the decode expand,
+// and a lane owns the same rows o_lo + RPL * lane + i (i < RPL).  For each
+// slot the v of the block's (token, slot) rows is gathered into LDS from the
+// shrink's partials (the one chunk order: thread (entry, way) sums one way,
+// the ways are added in order), the slot adapter's B rows stream in, and
+// each lane adds the slot's scaled dot products to its running outputs,
+// which start at y_in.  B keeps the default cache policy here: a block is
+// one request, so a popular adapter's B rows are read by many blocks
+// (streaming them was 2.4% slower per merged full-stack step).  Issuing slot
+// k + 1's loads before slot k's gather and dot products held 96 VGPRs
+// instead of 60, 5 waves a SIMD instead of 8, and was 6% slower.
+template <typename T, int NVM> struct MergeLoads {
+    static constexpr int RPL = decode_rpl(NVM);
+    MergeSlot sl;
+    u32x4 part[4];                // chunks kk, kk + 4, kk + 8, kk + 12 of the thread's way
+    u32x4 bv[NVM][RPL];           // the lane's B rows, vector by vector
+    uint32_t off;                 // the thread's v entry in the partials
+    bool live;                    // a slot with an adapter
+};
+
 template <typename T, int NVM>
 __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int RPL = decode_rpl(NVM);
     constexpr int NT = kValuTokens;
     constexpr int VS = LORA_MAX_RANK + 4;
+    constexpr bool PR = RPL == 2;                    // two adjacent rows a lane
     __shared__ float vs[NT][VS];
     __shared__ f32x4 ways[NT * LORA_MAX_RANK / 4][kSumWays];
 
@@ -957,6 +972,7 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const int tid = int(threadIdx.x);
     const int yoff = a.y_off[p];
+    auto row_of = [&](int i) { return o_lo + RPL * lane + i; };
 
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const rsrc_t inr = a.base ? make_rsrc(a.base, a.base_bytes) : yr;
@@ -968,28 +984,19 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         in_row[t] = ok ? uint32_t((int64_t(mb.tok[t]) * ld_in + yoff) * sizeof(T)) : kOOB;
         y_row[t] = ok ? uint32_t((int64_t(mb.tok[t]) * a.ldy + yoff) * sizeof(T)) : kOOB;
     }
-    float acc[RPL][NT];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int row = o_lo + i * kWaveSize + lane;
-        const bool rok = row < o_hi;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            acc[i][t] = Out1<T>::load(inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
-    }
 
     const rsrc_t pr = make_rsrc(a.partial, a.partial_bytes);
     const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
-#pragma unroll
-    for (int k = 0; k < kMaxMerge; ++k) {
-        if (k >= mb.nslots) break;                   // wave-uniform
-        const MergeSlot sl = load_invariant(&mbp->slot[k]);
-        if (sl.r_pad == 0) continue;                 // an empty slot: wave-uniform
-        // the v gather: thread (entry e, way kk), entry = 4 ranks of a token
-        const int quads = sl.r_pad / 4;
-        const int entries = mb.n_tok * quads;
-        const int kk = tid % kSumWays, e = tid / kSumWays;
-        const bool on = e < entries;
+    const int kk = tid % kSumWays, e = tid / kSumWays;   // the thread's (entry, way)
+    // the loads of slot k: its plan entry, its partials and its B rows
+    auto issue = [&](int k, MergeLoads<T, NVM> &ld) {
+        ld.live = false;
+        if (k >= mb.nslots) return;                  // wave-uniform
+        ld.sl = load_invariant(&mbp->slot[k]);
+        if (ld.sl.r_pad == 0) return;                // an empty slot: wave-uniform
+        ld.live = true;
+        const int quads = ld.sl.r_pad / 4;
+        const bool on = e < mb.n_tok * quads;
         const int ti = on ? e / quads : 0;
         const int j = on ? (e - ti * quads) * 4 : 0;
         // the row's place in the partials, by selects (an indexed private
@@ -999,101 +1006,156 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         const int4 ps4 = load_invariant(reinterpret_cast<const int4 *>(mbp->ps[k]));
         const int rt = ti == 0 ? rt4.x : ti == 1 ? rt4.y : ti == 2 ? rt4.z : rt4.w;
         const int ps = ti == 0 ? ps4.x : ti == 1 ? ps4.y : ti == 2 ? ps4.z : ps4.w;
-        const uint32_t off = on ? partial_off(rt, j, ps, p, a.nproj, a.c0, a.ptt) : 0u;
-        u32x4 part[4];
+        ld.off = on ? partial_off(rt, j, ps, p, a.nproj, a.c0, a.ptt) : kOOB / 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = kk + i * kSumWays;
-            part[i] = bload16(pr, off_or_oob(on && c < a.c0, (off + uint32_t(c) * stride) * 4));
+            ld.part[i] = bload16(pr, off_or_oob(on && c < a.c0, (ld.off + uint32_t(c) * stride) * 4));
         }
-        // the slot adapter's B rows
-        const uint32_t row_bytes = uint32_t(sl.r_pad) * sizeof(T);
-        const uint64_t boff = extent(sl.ext_lo, sl.ext_hi) +
-                              uint64_t(sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]);
+        const uint64_t boff = extent(ld.sl.ext_lo, ld.sl.ext_hi) +
+                              uint64_t(ld.sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]);
         const rsrc_t br = make_rsrc(a.slab + boff,
-                                    dbg_block(a.dbg, boff, uint64_t(h_out) * row_bytes));
-        const int nv = sl.r_pad / E;
-        const BLayout bl = b_layout(sl.r_pad, sizeof(T));   // the slot's B layout
-        u32x4 bv[NVM][RPL];
+                                    dbg_block(a.dbg, boff, uint64_t(h_out) * uint64_t(ld.sl.r_pad) *
+                                                               sizeof(T)));
+        const int nv = ld.sl.r_pad / E;
+        const BLayout bl = b_layout(ld.sl.r_pad, sizeof(T));   // the slot's B layout
 #pragma unroll
         for (int v = 0; v < NVM; ++v)
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                const int row = o_lo + i * kWaveSize + lane;
-                bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
-                                                  b_vec_off(bl, row, v, h_out)));
+                const int row = row_of(i);
+                ld.bv[v][i] = bload16(br, off_or_oob(row < o_hi && v < nv,
+                                                     b_vec_off(bl, row, v, h_out)));
             }
-        // finish the gather in the one chunk order
-        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    MergeLoads<T, NVM> cur;
+    float acc[RPL][NT];                              // y_in, then the running outputs
+    if constexpr (PR) {
+        const int row = row_of(0);
+        const bool rok = row < o_hi;                 // o_hi is even: the pair is in or out
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (kk + i * kSumWays < a.c0) s4 += __builtin_bit_cast(f32x4, part[i]);
-        for (int c = kk + 4 * kSumWays; c < a.c0; c += kSumWays)
-            s4 += __builtin_bit_cast(
-                f32x4, bload16(pr, off_or_oob(on, (off + uint32_t(c) * stride) * 4)));
-        if (on) ways[e][kk] = s4;
-        __syncthreads();
-        if (tid < entries) {
-            const int t2 = tid / quads, j2 = (tid - (tid / quads) * quads) * 4;
-            f32x4 w4 = ways[tid][0];
-#pragma unroll
-            for (int w = 1; w < kSumWays; ++w) w4 += ways[tid][w];
-            *reinterpret_cast<f32x4 *>(&vs[t2][j2]) = w4;
-        }
-        __syncthreads();
-        // this slot's dot products, added to the running outputs
-        float d[RPL][NT];
-#pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
-#pragma unroll
-        for (int v = 0; v < NVM; ++v) {
-            if (v < nv) {                            // wave-uniform
-                float f[RPL][E];
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) {
-                    if constexpr (E == 8) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            f[i][2 * q] = bf16_lo(bv[v][i][q]);
-                            f[i][2 * q + 1] = bf16_hi(bv[v][i][q]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) f[i][q] = __uint_as_float(bv[v][i][q]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    if (t < mb.n_tok) {              // wave-uniform
-                        float wv[E];
-#pragma unroll
-                        for (int q = 0; q < E; q += 4) {
-                            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + q]);
-                            wv[q] = w4[0]; wv[q + 1] = w4[1]; wv[q + 2] = w4[2]; wv[q + 3] = w4[3];
-                        }
-#pragma unroll
-                        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-                            for (int q = 0; q < E; ++q)
-                                d[i][t] = __builtin_fmaf(f[i][q], wv[q], d[i][t]);
-                    }
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t off = rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB;
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(inr, int(off), 0, kNT);
+                acc[0][t] = bf16_lo(w);
+                acc[1][t] = bf16_hi(w);
+            } else {
+                const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(inr, int(off), 0, kNT);
+                acc[0][t] = __uint_as_float(w[0]);
+                acc[1][t] = __uint_as_float(w[1]);
             }
         }
+    } else {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
+        for (int i = 0; i < RPL; ++i) {
+            const int row = row_of(i);
+            const bool rok = row < o_hi;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[i][t] = acc[i][t] + sl.scale * d[i][t];
-        __syncthreads();                             // vs and ways are written again
+            for (int t = 0; t < NT; ++t)
+                acc[i][t] = Out1<T>::template load<kNT>(
+                    inr, rok ? in_row[t] + uint32_t(row) * sizeof(T) : kOOB);
+        }
     }
+
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int row = o_lo + i * kWaveSize + lane;
+    for (int k = 0; k < kMaxMerge; ++k) {
+        if (k >= mb.nslots) break;                   // wave-uniform
+        issue(k, cur);
+        if (cur.live) {                              // wave-uniform
+            const int quads = cur.sl.r_pad / 4;
+            const int entries = mb.n_tok * quads;
+            const bool on = e < entries;
+            // finish the gather in the one chunk order
+            f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (kk + i * kSumWays < a.c0) s4 += __builtin_bit_cast(f32x4, cur.part[i]);
+            for (int c = kk + 4 * kSumWays; c < a.c0; c += kSumWays)
+                s4 += __builtin_bit_cast(
+                    f32x4, bload16(pr, off_or_oob(on, (cur.off + uint32_t(c) * stride) * 4)));
+            if (on) ways[e][kk] = s4;
+            __syncthreads();
+            if (tid < entries) {
+                const int t2 = tid / quads, j2 = (tid - (tid / quads) * quads) * 4;
+                f32x4 w4 = ways[tid][0];
+#pragma unroll
+                for (int w = 1; w < kSumWays; ++w) w4 += ways[tid][w];
+                *reinterpret_cast<f32x4 *>(&vs[t2][j2]) = w4;
+            }
+            __syncthreads();
+            // this slot's dot products, added to the running outputs
+            const int nv = cur.sl.r_pad / E;
+            float d[RPL][NT];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) d[i][t] = 0.f;
+#pragma unroll
+            for (int v = 0; v < NVM; ++v) {
+                if (v < nv) {                        // wave-uniform
+                    float f[RPL][E];
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        if constexpr (E == 8) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                f[i][2 * q] = bf16_lo(cur.bv[v][i][q]);
+                                f[i][2 * q + 1] = bf16_hi(cur.bv[v][i][q]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) f[i][q] = __uint_as_float(cur.bv[v][i][q]);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        if (t < mb.n_tok) {          // wave-uniform
+                            float wv[E];
+#pragma unroll
+                            for (int q = 0; q < E; q += 4) {
+                                const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&vs[t][v * E + q]);
+                                wv[q] = w4[0]; wv[q + 1] = w4[1]; wv[q + 2] = w4[2]; wv[q + 3] = w4[3];
+                            }
+#pragma unroll
+                            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                                for (int q = 0; q < E; ++q)
+                                    d[i][t] = __builtin_fmaf(f[i][q], wv[q], d[i][t]);
+                        }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[i][t] = acc[i][t] + cur.sl.scale * d[i][t];
+            __syncthreads();                         // vs and ways are written again
+        }
+    }
+    if constexpr (PR) {
+        const int row = row_of(0);
         const bool rok = row < o_hi;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)                 // y_row[t] is kOOB for absent tokens
-            Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB, acc[i][t]);
+        for (int t = 0; t < NT; ++t) {               // y_row[t] is kOOB for absent tokens
+            const uint32_t off = rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB;
+            if constexpr (sizeof(T) == 2)
+                __builtin_amdgcn_raw_buffer_store_b32(bf16x2_rne(acc[0][t], acc[1][t]), yr,
+                                                      int(off), 0, kOut);
+            else
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{__float_as_uint(acc[0][t]), __float_as_uint(acc[1][t])}, yr, int(off), 0,
+                    kOut);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = row_of(i);
+            const bool rok = row < o_hi;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)             // y_row[t] is kOOB for absent tokens
+                Out1<T>::store(yr, rok ? y_row[t] + uint32_t(row) * sizeof(T) : kOOB, acc[i][t]);
+        }
     }
 }
 
