@@ -648,15 +648,17 @@ __device__ __forceinline__ void gather_finish(const ExpandArgs &a, const BlockDe
 // in float32.  In the slab's B layout each (i, v) load of the wave is one
 // contiguous run.  Loads go out in the order they are used: the v gather, B
 // vector by vector, then y_in; so the dot products of the first vectors
-// start while the rest arrive.
-template <typename T, int NV, bool Sig>
+// start while the rest arrive.  NT: the token slots the code is built for
+// (the block's token count, or kValuTokens for a block of none), so that
+// no y_in load or y store is issued for an absent slot.
+template <typename T, int NV, bool Sig, int NT>
 __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc &blk,
                                             const int (&tr)[kValuTokens], int p, int o_lo,
                                             int o_hi, float (*vs)[LORA_MAX_RANK + 4],
                                             f32x4 (*ways)[kSumWays]) {
+    static_assert(NT >= 1 && NT <= kValuTokens, "token slots of a decode block");
     constexpr int E = Elem<T>::E;
     constexpr int RPL = decode_rpl(NV);
-    constexpr int NT = kValuTokens;
     const int lane = threadIdx.x & 63;
     const int nv = blk.r_pad / E;                    // wave-uniform, <= NV
     const int nt = blk.n_tok;                        // wave-uniform, <= NT
@@ -806,6 +808,31 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     }
 }
 
+// expand_valu built for the block's token count (a wave-uniform branch):
+// a block of fewer tokens issues its y_in loads and y stores for those
+// tokens only, instead of kValuTokens slots with the absent ones masked out
+// of range (most decode blocks hold one token): 3.7% per full-stack step,
+// 2.4% on the multi-rank decode.  Rows of 1-2 vectors only: below 4 tokens
+// the builds for wider rows raise the kernel to 89-127 VGPRs (against
+// 63-96, fewer waves a SIMD), and a single-token build for bf16 rows of 4
+// vectors, which keeps 63, gave back the multi-rank gain.  The core step's
+// build keeps one.
+template <typename T, int NV, bool Sig>
+__device__ __forceinline__ void expand_valu_nt(const ExpandArgs &a, const BlockDesc &blk,
+                                               const int (&tr)[kValuTokens], int p, int o_lo,
+                                               int o_hi, float (*vs)[LORA_MAX_RANK + 4],
+                                               f32x4 (*ways)[kSumWays]) {
+    static_assert(kValuTokens == 4 && NV <= 2, "builds per token count 1..4, rows of 1-2 vectors");
+    if constexpr (Sig)
+        return expand_valu<T, NV, Sig, kValuTokens>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    switch (blk.n_tok) {
+    case 1: return expand_valu<T, NV, Sig, 1>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: return expand_valu<T, NV, Sig, 2>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 3: return expand_valu<T, NV, Sig, 3>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    default: return expand_valu<T, NV, Sig, kValuTokens>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    }
+}
+
 // Decode expand: plans whose blocks hold at most kValuTokens tokens.  A
 // unit is (block, projection, kWaves slices of decode_wave_rows rows); the
 // blocks are ordered by padded rank, and a unit's rank class, block,
@@ -887,15 +914,15 @@ __global__ __launch_bounds__(256) void k_expand_decode(const ExpandArgs a) {
         return;
     }
     switch (decode_nvt(r_pad, sizeof(T))) {         // <= NVM for every class of the launch
-    case 1: return expand_valu<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
-    case 2: if constexpr (NVM >= 2) return expand_valu<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 1: return expand_valu_nt<T, 1, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 2: if constexpr (NVM >= 2) return expand_valu_nt<T, 2, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 4: if constexpr (NVM >= 4) return expand_valu<T, 4, Sig, kValuTokens>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
-    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+    case 8: if constexpr (NVM >= 8) return expand_valu<T, 8, Sig, kValuTokens>(a, blk, tr, p, o_lo, o_hi, vs, ways);
             return;
     default:
-        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig>(a, blk, tr, p, o_lo, o_hi, vs, ways);
+        if constexpr (sizeof(T) == 4 && NVM >= 16) return expand_valu<T, 16, Sig, kValuTokens>(a, blk, tr, p, o_lo, o_hi, vs, ways);
     }
 }
 
