@@ -571,6 +571,7 @@ struct VGather {
     bool on;
 };
 
+template <bool Skip>
 __device__ __forceinline__ void gather_issue(const ExpandArgs &a, const BlockDesc &blk,
                                              const int (&tr)[kValuTokens], int p, VGather &g) {
     const int quads = blk.r_pad / 4;                 // r_pad > 0
@@ -586,10 +587,22 @@ __device__ __forceinline__ void gather_issue(const ExpandArgs &a, const BlockDes
         const uint32_t off = partial_off(blk.rt_before, g.j, blk.slot0 + g.ti, p, a.nproj, a.c0,
                                          a.ptt);
         const uint32_t stride = uint32_t(a.nproj * a.ptt * kTile * kTile);
+        // Skip: a wave with no live entry (waves 1-3 of a block of at most
+        // 16 entries) issues no load at all, by one wave-uniform branch, as a
+        // masked lane still costs the address path.  These are the unit's
+        // first loads, so the waits for the loads after them do not change.
+        // 3-4.5% per full-stack expand; for wider rows (the rank-32 and -64
+        // build) the multi-rank gate/up expand measured 0.9% slower, and a
+        // branch per round of chunks as well raised that build past 64 VGPRs.
+        if (!Skip || wave_id() * kWaveSize < entries * kSumWays) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = g.k + i * kSumWays;
-            g.part[i] = bload16(pr, off_or_oob(g.on && c < a.c0, (off + uint32_t(c) * stride) * 4));
+            for (int i = 0; i < 4; ++i) {
+                const int c = g.k + i * kSumWays;
+                g.part[i] = bload16(pr, off_or_oob(g.on && c < a.c0, (off + uint32_t(c) * stride) * 4));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g.part[i] = u32x4{0u, 0u, 0u, 0u};
         }
     } else {
         g.k = 0;
@@ -686,7 +699,7 @@ __device__ __forceinline__ void expand_valu(const ExpandArgs &a, const BlockDesc
     constexpr bool PR = RPL == 2;
     auto row_of = [&](int i) { return o_lo + RPL * lane + i; };
     VGather g;
-    gather_issue(a, blk, tr, p, g);
+    gather_issue<(NV <= 2)>(a, blk, tr, p, g);
     // the slice's vectors run (i, v, lane): vector v of the lane's row i at
     // ((i * nv + v) * lanes + lane) * 16 past the slice's first row
     const int lanes = (o_hi - o_lo) / RPL;          // o_hi - o_lo is a multiple of 8
