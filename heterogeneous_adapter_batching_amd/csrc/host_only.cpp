@@ -22,7 +22,7 @@ hipError_t launch_prefill(int, int, int, int, int, const PrefillArgs &, int, hip
 hipError_t launch_expand_decode(int, int, const ExpandArgs &, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
-hipError_t launch_expand_merge(int, int, const MergeArgs &, int, hipStream_t) {
+hipError_t launch_expand_merge(int, int, int, const MergeArgs &, int, hipStream_t) {
     return hipErrorInvalidValue;
 }
 hipError_t static_scratch(void **, uint64_t *) { return hipErrorInvalidValue; }

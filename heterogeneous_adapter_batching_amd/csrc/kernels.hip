@@ -962,11 +962,14 @@ template <typename T, int NVM> struct MergeLoads {
     bool live;                    // a slot with an adapter
 };
 
-template <typename T, int NVM>
+// NT: the token slots of the launch's blocks, 1 when every merge block of
+// the plan holds one token (a decode batch: one request, one token), so
+// that no y_in load, y store or LDS row is spent on absent slots.
+template <typename T, int NVM, int NT>
 __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
+    static_assert(NT == 1 || NT == kValuTokens, "merge builds for 1 or kValuTokens tokens");
     constexpr int E = Elem<T>::E;
     constexpr int RPL = decode_rpl(NVM);
-    constexpr int NT = kValuTokens;
     constexpr int VS = LORA_MAX_RANK + 4;
     constexpr bool PR = RPL == 2;                    // two adjacent rows a lane
     __shared__ float vs[NT][VS];
@@ -1003,6 +1006,8 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
 #pragma unroll
         for (int t = 0; t < kValuTokens; ++t) mb.tok[t] = dbg_token(a.dbg, mb.tok[t]);
     }
+    if constexpr (NT < kValuTokens)  // the host launches this build for blocks of NT tokens
+        mb.n_tok = min(mb.n_tok, NT);
     int h_out = hout[0];
 #pragma unroll
     for (int i = 1; i < LORA_MAX_PROJ; ++i) h_out = p == i ? hout[i] : h_out;
@@ -1967,25 +1972,30 @@ hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int g, 
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int NT>
 hipError_t expand_merge_t(int nvm, dim3 grid, dim3 block, const MergeArgs &a, hipStream_t s) {
-    if (nvm <= 1) hipLaunchKernelGGL((k_expand_merge<T, 1>), grid, block, 0, s, a);
-    else if (nvm <= 2) hipLaunchKernelGGL((k_expand_merge<T, 2>), grid, block, 0, s, a);
-    else if (nvm <= 4) hipLaunchKernelGGL((k_expand_merge<T, 4>), grid, block, 0, s, a);
-    else if (nvm <= 8) hipLaunchKernelGGL((k_expand_merge<T, 8>), grid, block, 0, s, a);
-    else if constexpr (sizeof(T) == 4) hipLaunchKernelGGL((k_expand_merge<T, 16>), grid, block, 0, s, a);
+    if (nvm <= 1) hipLaunchKernelGGL((k_expand_merge<T, 1, NT>), grid, block, 0, s, a);
+    else if (nvm <= 2) hipLaunchKernelGGL((k_expand_merge<T, 2, NT>), grid, block, 0, s, a);
+    else if (nvm <= 4) hipLaunchKernelGGL((k_expand_merge<T, 4, NT>), grid, block, 0, s, a);
+    else if (nvm <= 8) hipLaunchKernelGGL((k_expand_merge<T, 8, NT>), grid, block, 0, s, a);
+    else if constexpr (sizeof(T) == 4) hipLaunchKernelGGL((k_expand_merge<T, 16, NT>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid, hipStream_t s) {
+hipError_t launch_expand_merge(int dtype, int nvm, int max_tok, const MergeArgs &a, int grid,
+                               hipStream_t s) {
     if (a.units <= 0) return hipSuccess;
+    if (max_tok < 1 || max_tok > kValuTokens) return hipErrorInvalidValue;
     const dim3 g(grid), block(kWaves * kWaveSize);
+    const bool one = max_tok == 1;
     if (dtype == LORA_BF16) {
         if (nvm > 8) return hipErrorInvalidValue;
-        return expand_merge_t<uint16_t>(nvm, g, block, a, s);
+        return one ? expand_merge_t<uint16_t, 1>(nvm, g, block, a, s)
+                   : expand_merge_t<uint16_t, kValuTokens>(nvm, g, block, a, s);
     }
     if (nvm > 16) return hipErrorInvalidValue;
-    return expand_merge_t<float>(nvm, g, block, a, s);
+    return one ? expand_merge_t<float, 1>(nvm, g, block, a, s)
+               : expand_merge_t<float, kValuTokens>(nvm, g, block, a, s);
 }
 
 hipError_t launch_prefill(int dtype, int mode, int np, int rtm, int tpl, const PrefillArgs &a,

@@ -1419,8 +1419,10 @@ lora_status run_expand_merge(const lora_pool *p, const lora_plan *pl, int32_t la
     a.units = int32_t(units);
     a.y_bytes = uint32_t(tensor_bytes(pl->T, ldy, ldy, es));
     a.base_bytes = base ? uint32_t(tensor_bytes(pl->T, ldb, ldb, es)) : 0u;
-    const hipError_t e = lora::launch_expand_merge(p->d.dtype, lora::decode_nvt(rmax, es), a,
-                                                   grid_for(a.units, 1), st);
+    int32_t max_tok = 1;             // a decode batch's merge blocks hold one token each
+    for (const lora::MergeBlock &mb : pl->mblocks) max_tok = std::max(max_tok, mb.n_tok);
+    const hipError_t e = lora::launch_expand_merge(p->d.dtype, lora::decode_nvt(rmax, es),
+                                                   max_tok, a, grid_for(a.units, 1), st);
     if (e != hipSuccess) return hip_fail(e, "merge expand launch");
     return LORA_OK;
 }

@@ -387,7 +387,9 @@ hipError_t launch_prefill(int dtype, int mode, int np, int rtm, int tpl, const P
 hipError_t launch_expand_decode(int dtype, int nvm, const ExpandArgs &a, int grid,
                                 hipStream_t s);
 // merge expand; nvm: the largest decode_nvt of the plan's slot adapters
-hipError_t launch_expand_merge(int dtype, int nvm, const MergeArgs &a, int grid, hipStream_t s);
+// max_tok: the most tokens in one of the plan's merge blocks (1..kValuTokens)
+hipError_t launch_expand_merge(int dtype, int nvm, int max_tok, const MergeArgs &a, int grid,
+                               hipStream_t s);
 
 // The library's static device scratch (sgmv_fused_static): the address of
 // the current device's copy, found once per device, and its size in bytes.

@@ -830,14 +830,14 @@ def test_sigma_call_errors():
 
 # ----------------------------------------------------------- weighted merge ----
 def _merge_setup(seed, *, K, dtype, T, max_seg, h_in=256, h_out=192, n_adapters=5,
-                 plan_opts=None):
+                 plan_opts=None, r_choices=(8, 16, 32)):
     """A pool of n_adapters (mixed ranks) and K merge slots per segment: a
     plain random batch gives the segments; each slot draws its own adapters
     (or -1) and weights; plan_opts are set on the pool before the plan."""
     import heterogeneous_adapter_batching_amd as hab
     w = random_case(seed, T=T, h_in=h_in, h_out=h_out, n_adapters=n_adapters,
-                    r_choices=[8, 16, 32], dtype=dtype, max_seg=max_seg, has_base=True,
-                    r_max=32)
+                    r_choices=list(r_choices), dtype=dtype, max_seg=max_seg, has_base=True,
+                    r_max=max(r_choices))
     g = np.random.default_rng(seed)
     S = w.num_segs
     seg_ad = g.integers(-1, n_adapters, (S, K)).astype(np.int32)
@@ -870,6 +870,14 @@ def test_merge_parity(dtype, prefill, K, plan_opts=None):
         f"{plan_opts or ''}")
     if plan_opts is None:
         assert (plan.stats()["max_block_tokens"] > 4) == prefill
+    _check_merge(w, dw, plan, seg_ad, seg_w, dtype)
+
+
+def _check_merge(w, dw, plan, seg_ad, seg_w, dtype):
+    """A merge plan's fused call against the oracle's merge (the contract
+    tolerance, and the delta within the float32 accumulation bound plus one
+    rounding of y); the static-scratch and split calls give the same bits."""
+    import heterogeneous_adapter_batching_amd as hab
     x = dw.x[(0, "x")]
     y = torch.zeros_like(dw.y[(0, 0)])
     hab.sgmv_fused(dw.pool, plan, 0, (0,), [0], x, y, dw.base[(0, 0)])
@@ -897,6 +905,23 @@ def test_merge_parity(dtype, prefill, K, plan_opts=None):
     torch.cuda.synchronize()
     for other in (y2, y3):
         assert np.array_equal(from_device(y).view(np.uint8), from_device(other).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("K", [2, 3])
+def test_merge_decode_parity(dtype, K):
+    """Decode merges: every segment one token (or empty), so every merge
+    block holds one token and the merge expand runs its single-token build;
+    ranks 8-64 (B rows of 1-8 vectors in bf16, 2-16 in float32) against the
+    oracle's merge at the bounds of the merge parity test, and the three
+    entry points bit for bit."""
+    seed = (61 if dtype == "bf16" else 62) + 10 * K
+    w, dw, plan, seg_ad, seg_w = _merge_setup(seed, K=K, dtype=dtype, T=150, max_seg=1,
+                                              n_adapters=8, r_choices=(8, 16, 32, 64))
+    lens = np.diff(np.asarray(w.seg_starts))
+    assert lens.max() == 1 and (lens == 1).sum() > 100
+    log(f"[parity] decode merge {w.name} K={K} {dtype} {plan.stats()}")
+    _check_merge(w, dw, plan, seg_ad, seg_w, dtype)
 
 
 def test_merge_one_slot_equals_plain_bitexact():
