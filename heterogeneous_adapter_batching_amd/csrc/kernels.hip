@@ -1052,10 +1052,18 @@ __global__ __launch_bounds__(256) void k_expand_merge(const MergeArgs a) {
         const int rt = ti == 0 ? rt4.x : ti == 1 ? rt4.y : ti == 2 ? rt4.z : rt4.w;
         const int ps = ti == 0 ? ps4.x : ti == 1 ? ps4.y : ti == 2 ? ps4.z : ps4.w;
         ld.off = on ? partial_off(rt, j, ps, p, a.nproj, a.c0, a.ptt) : kOOB / 4;
+        // one token: at most 16 entries, all in wave 0; waves 1-3 issue no
+        // partial-sum load (a wave-uniform branch; a masked lane still costs
+        // the address path)
+        if (NT > 1 || wave_id() == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = kk + i * kSumWays;
-            ld.part[i] = bload16(pr, off_or_oob(on && c < a.c0, (ld.off + uint32_t(c) * stride) * 4));
+            for (int i = 0; i < 4; ++i) {
+                const int c = kk + i * kSumWays;
+                ld.part[i] = bload16(pr, off_or_oob(on && c < a.c0, (ld.off + uint32_t(c) * stride) * 4));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ld.part[i] = u32x4{0u, 0u, 0u, 0u};
         }
         const uint64_t boff = extent(ld.sl.ext_lo, ld.sl.ext_hi) +
                               uint64_t(ld.sl.r_pad) * sizeof(T) * uint64_t(a.coef_b[p]);
