@@ -348,13 +348,27 @@ __global__ __launch_bounds__(256) void k_shrink(const ShrinkArgs a) {
         // units number them
         const int uu = key * per + c * a.nproj + p0 + pi;
         float *pt = a.partial + size_t(uu) * (TT * kTile * kTile);
-        for (int i = threadIdx.x; i < ntiles * kWaveSize; i += kWaves * kWaveSize) {
-            // token tiles past the block's last are never read: not stored
-            const int tt = i / kWaveSize, ln = i % kWaveSize;
-            const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
-            // partials are read once, by the next kernel
-            __builtin_nontemporal_store(
-                s4, reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4));
+        if constexpr (TT == 1) {
+            // one token tile (decode blocks): wave 0 stores it, token slot n a
+            // lane group; absent rows (a decode block fills 1-16 of the 16
+            // slots) are never read, so their lanes are switched off (the
+            // builds for 2-4 tiles keep the plain loop: this form held 4-6
+            // more VGPRs there, one wave a SIMD fewer)
+            if (w == 0 && ntiles > 0 && trow[0] >= 0) {
+                const f32x4 s4 = red[0][0][lane] + red[1][0][lane] + red[2][0][lane] +
+                                 red[3][0][lane];
+                // partials are read once, by the next kernel
+                __builtin_nontemporal_store(s4, reinterpret_cast<f32x4 *>(pt + n * kTile + q * 4));
+            }
+        } else {
+            for (int i = threadIdx.x; i < ntiles * kWaveSize; i += kWaves * kWaveSize) {
+                // token tiles past the block's last are never read: not stored
+                const int tt = i / kWaveSize, ln = i % kWaveSize;
+                const f32x4 s4 = red[0][tt][ln] + red[1][tt][ln] + red[2][tt][ln] + red[3][tt][ln];
+                // partials are read once, by the next kernel
+                __builtin_nontemporal_store(
+                    s4, reinterpret_cast<f32x4 *>(pt + (tt * kTile + (ln & 15)) * kTile + (ln >> 4) * 4));
+            }
         }
         if (MP) __syncthreads();                     // red is written again
     }
