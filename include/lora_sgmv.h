@@ -362,6 +362,10 @@ lora_status lora_plan_create_sigma(lora_plan **out, const lora_pool *p, int32_t 
  * must be uploaded again before its next call; an error leaves the plan as it
  * was.  The plan is made against the pool as it is at the rebuild, so a plan
  * that an unregister (or an exchange eviction) left stale is current again.
+ * Each call fixes its launches from the plan as it then is (grids, unit
+ * counts, and the kernel build chosen for the batch's blocks), so a HIP
+ * graph captured from calls on the plan before a rebuild must not be
+ * replayed after it: capture again, or call eagerly.
  * Errors as the create calls. */
 lora_status lora_plan_rebuild(lora_plan *pl, int32_t num_tokens, const int32_t *seg_starts,
                               const int32_t *seg_adapter, const int32_t *seg_sigma,
